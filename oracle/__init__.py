@@ -1,0 +1,104 @@
+"""CPU oracle for the chunkwise gated linear attention forward (fp64).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline may import this package; the GPU library and its Python binding never
+do, and nothing here imports them.
+
+``gla_reference`` runs the token-by-token recurrence of ``gla_oracle.c``
+(S_t = diag(exp(g_t)) S_{t-1} + k_t v_t^T, o_t = scale q_t^T S_t, per sequence
+and head, in double precision) on float32 inputs.  The definition and its
+sources are stated in the C file's header.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gla_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libgla_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.gla_oracle_fwd.argtypes = [i64, p, i64, i64, i64, p, p, p, p, p,
+                                       ctypes.c_double, p, p, ctypes.c_int]
+        lib.gla_oracle_fwd.restype = ctypes.c_int
+        lib.gla_oracle_max_threads.argtypes = []
+        lib.gla_oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().gla_oracle_max_threads())
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def gla_reference(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray,
+                  h0: Optional[np.ndarray] = None, cu_seqlens: Optional[np.ndarray] = None,
+                  scale: Optional[float] = None, output_final_state: bool = True,
+                  threads: int = 0) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """Token-by-token fp64 recurrence.
+
+    q, k, g: [B, T, H, K]; v: [B, T, H, V] (any float dtype; converted to float32,
+    which is exact for bf16 and fp32 data).  h0: [N, H, K, V] or None.
+    cu_seqlens: [N+1] offsets into the packed token axis (requires B == 1) or None.
+    scale: None means K ** -0.5.
+    Returns o [B, T, H, V] float64 and ht [N, H, K, V] float64 (or None).
+    """
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if k.shape != (B, T, H, K) or g.shape != (B, T, H, K) or v.shape != (B, T, H, V):
+        raise ValueError("shape mismatch")
+    if scale is None:
+        scale = K ** -0.5
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("packed sequences need a batch of one")
+        offsets = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+        if offsets[0] != 0 or offsets[-1] != T or np.any(np.diff(offsets) < 0):
+            raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+    else:
+        offsets = np.arange(B + 1, dtype=np.int64) * T
+    N = len(offsets) - 1
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    qf, kf, vf, gf = f32(q), f32(k), f32(v), f32(g)
+    hf = None
+    if h0 is not None:
+        if h0.shape != (N, H, K, V):
+            raise ValueError(f"h0 must be [{N}, {H}, {K}, {V}]")
+        hf = np.ascontiguousarray(h0, dtype=np.float64)
+    o = np.zeros((B, T, H, V), dtype=np.float64)
+    ht = np.zeros((N, H, K, V), dtype=np.float64) if output_final_state else None
+    rc = _load().gla_oracle_fwd(N, _ptr(offsets), H, K, V, _ptr(qf), _ptr(kf), _ptr(vf),
+                                _ptr(gf), _ptr(hf), float(scale), _ptr(o), _ptr(ht),
+                                int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle failed")
+    return o, ht

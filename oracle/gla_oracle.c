@@ -1,0 +1,117 @@
+/*
+ * CPU oracle for the chunkwise gated linear attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark do.  It shares no source with the GPU library.
+ *
+ * What it computes is the plain definition of the method, not the chunked
+ * algorithm: for every sequence n and head h it runs the gated linear
+ * attention recurrence token by token in double precision,
+ *
+ *     S_0 = h0[n,h]  (or 0)                     S is a K x V matrix
+ *     S_t = diag(exp(g_t)) S_{t-1} + k_t v_t^T   (decay first, then add)
+ *     o_t = scale * q_t^T S_t                    (the updated state)
+ *     ht[n,h] = S_T
+ *
+ * Sources (page "fla/ops/gla/fused_chunk.py"):
+ *   - fused_chunk_gla_fwd_kernel: the state is decayed row-wise by exp of the
+ *     chunk's log decay and then receives k^T v; h0 enters before the first
+ *     chunk and ht is the state after the last one, kept in fp32.
+ *   - prepare_qg_kg and fwd_inner_chunk: within a chunk, with G the inclusive
+ *     cumulative sum of g, the query is weighted by exp(G_i), a key entering
+ *     the carried state by exp(G_last - G_j), and the in-chunk score of key j
+ *     for query i by exp(G_i - G_j) under a causal mask that keeps j <= i
+ *     (diagonal included).  These weights make the chunked form equal, term
+ *     by term, to the token recurrence above with the output read after the
+ *     update.
+ *   - FusedChunkGLAFunction.forward: g is a natural-log decay (exp, not exp2).
+ * Packed variable-length sequences follow the page "fla/ops/ttt/fused_chunk.py"
+ * (fused_chunk_ttt_linear_fwd_kernel and fused_chunk_ttt_linear): sequence n
+ * owns tokens [cu[n], cu[n+1]) of a batch of one, the state restarts per
+ * sequence, and there is one initial / final state per sequence.
+ *
+ * Precision: q, k, v, g are read as float32 (bf16 inputs are handed over
+ * upcast, which is exact) and promoted to double, h0 is double; all arithmetic is double,
+ * exp is the C library's.  Build: gcc -O2 -fopenmp -shared -fPIC, no fast-math.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/*
+ * q, k, g : [T_total][H][K] float32, time-major (token, head, key)
+ * v       : [T_total][H][V] float32
+ * offsets : [N+1] int64 token offsets, offsets[0] = 0, non-decreasing
+ * h0      : [N][H][K][V] double or NULL (zero initial state); double so that a
+ *           final state can be fed back unrounded (fp32 h0 upcasts exactly)
+ * o       : [T_total][H][V] double, every token of every sequence is written
+ * ht      : [N][H][K][V] double or NULL
+ * nthreads: OpenMP threads to use (<= 0: library default)
+ * Returns 0, or -1 on invalid sizes / allocation failure (nothing written).
+ */
+int gla_oracle_fwd(int64_t N, const int64_t *offsets, int64_t H, int64_t K, int64_t V,
+                   const float *q, const float *k, const float *v, const float *g,
+                   const double *h0, double scale, double *o, double *ht, int nthreads)
+{
+    if (N < 0 || H <= 0 || K <= 0 || V <= 0 || !offsets || !o)
+        return -1;
+    for (int64_t n = 0; n < N; ++n)
+        if (offsets[n + 1] < offsets[n]) return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int failed = 0;
+    const int64_t jobs = N * H;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (int64_t job = 0; job < jobs; ++job) {
+        const int64_t n = job / H, h = job % H;
+        double *S = (double *)malloc(sizeof(double) * (size_t)(K * V));
+        double *acc = (double *)malloc(sizeof(double) * (size_t)V);
+        if (!S || !acc) { free(S); free(acc); failed |= 1; continue; }
+        if (h0) {
+            memcpy(S, h0 + (n * H + h) * K * V, sizeof(double) * (size_t)(K * V));
+        } else {
+            memset(S, 0, sizeof(double) * (size_t)(K * V));
+        }
+        for (int64_t t = offsets[n]; t < offsets[n + 1]; ++t) {
+            const float *qt = q + (t * H + h) * K;
+            const float *kt = k + (t * H + h) * K;
+            const float *gt = g + (t * H + h) * K;
+            const float *vt = v + (t * H + h) * V;
+            for (int64_t j = 0; j < V; ++j) acc[j] = 0.0;
+            for (int64_t i = 0; i < K; ++i) {
+                const double decay = exp((double)gt[i]);
+                const double ki = (double)kt[i];
+                const double qi = (double)qt[i];
+                double *row = S + i * V;
+                for (int64_t j = 0; j < V; ++j) {
+                    row[j] = decay * row[j] + ki * (double)vt[j];
+                    acc[j] += qi * row[j];
+                }
+            }
+            double *ot = o + (t * H + h) * V;
+            for (int64_t j = 0; j < V; ++j) ot[j] = scale * acc[j];
+        }
+        if (ht) memcpy(ht + (n * H + h) * K * V, S, sizeof(double) * (size_t)(K * V));
+        free(S);
+        free(acc);
+    }
+    return failed ? -1 : 0;
+}
+
+/* Threads an OpenMP parallel region of this library actually gets. */
+int gla_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

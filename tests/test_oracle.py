@@ -1,0 +1,284 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+The oracle (oracle/gla_oracle.c) is the token recurrence of gated linear
+attention.  Each test below checks it against something that is not the
+oracle itself:
+
+* hand-worked cases (tests/golden/hand_cases.json, exact rational values);
+* a brute-force O(T^2) decayed-attention formula written with a global
+  cumulative sum instead of a recurrence;
+* g == 0, where the method is plain causal linear attention, checked against
+  numpy matrix products;
+* the closed form of a single token;
+* exact identities of the recurrence: splitting a sequence and resuming from
+  the returned final state, packing sequences == running them one by one,
+  linearity in the scale, the strong-decay limit;
+* mutation checks: plausible mistakes (output read before the update, decay
+  applied after the add, exp2 instead of exp, transposed state, per-sequence
+  restart dropped, h0 dropped) written into a tiny pure-Python copy of the
+  recurrence are each caught by these pins.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import gla_inputs as gi
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    oracle.build(force=False)
+
+
+# ---------------------------------------------------------------- helpers
+def brute_force(q, k, v, g, h0=None, cu=None, scale=None):
+    """O(T^2) decayed attention with a global inclusive cumulative sum per sequence.
+
+    o_i = scale * sum_k q_ik * ( e^{Gam_ik} h0[k,:] + sum_{j<=i} e^{Gam_ik - Gam_jk} k_jk v_j )
+    ht  = e^{Gam_T} h0 + sum_j e^{Gam_T - Gam_j} k_j v_j^T
+    """
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    scale = K ** -0.5 if scale is None else scale
+    offs = list(cu) if cu is not None else [b * T for b in range(B + 1)]
+    qf = q.reshape(B * T, H, K).astype(np.float64)
+    kf = k.reshape(B * T, H, K).astype(np.float64)
+    vf = v.reshape(B * T, H, V).astype(np.float64)
+    gf = g.reshape(B * T, H, K).astype(np.float64)
+    o = np.zeros((B * T, H, V))
+    N = len(offs) - 1
+    ht = np.zeros((N, H, K, V))
+    for n in range(N):
+        a, b = offs[n], offs[n + 1]
+        for h in range(H):
+            init = np.zeros((K, V)) if h0 is None else h0[n, h].astype(np.float64)
+            if b == a:
+                ht[n, h] = init
+                continue
+            Q, Kk, Vv = qf[a:b, h], kf[a:b, h], vf[a:b, h]
+            gam = np.cumsum(gf[a:b, h], axis=0)                      # [L, K]
+            L = b - a
+            D = np.exp(gam[:, None, :] - gam[None, :, :])            # [i, j, K]
+            D = D * np.tril(np.ones((L, L)))[:, :, None]
+            A = np.einsum("ik,jk,ijk->ij", Q, Kk, D)
+            o[a:b, h] = scale * (A @ Vv + (Q * np.exp(gam)) @ init)
+            ht[n, h] = np.exp(gam[-1])[:, None] * init + (Kk * np.exp(gam[-1] - gam)).T @ Vv
+    return o.reshape(B, T, H, V), ht
+
+
+def rel_err(a, b):
+    den = max(np.max(np.abs(b)), 1e-300)
+    return float(np.max(np.abs(a - b)) / den)
+
+
+def small_inputs(seed, B=2, T=37, H=3, K=5, V=7, h0=True, lengths=None):
+    return gi.draw(seed, B, T, H, K, V, dtype="fp32", h0=h0, lengths=lengths, gate_scale=0.25)
+
+
+# ---------------------------------------------------------------- hand-worked values
+def _load_hand_cases():
+    with open(os.path.join(HERE, "golden", "hand_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _load_hand_cases(), ids=lambda c: c["name"])
+def test_hand_worked_cases(case):
+    arr = lambda key: np.array(case[key], dtype=np.float64)
+    g = np.log(arr("g_exp")).astype(np.float32)
+    h0 = None if case["h0"] is None else arr("h0")
+    cu = None if case["cu_seqlens"] is None else np.array(case["cu_seqlens"], dtype=np.int32)
+    o, ht = oracle.gla_reference(arr("q"), arr("k"), arr("v"), g, h0=h0, cu_seqlens=cu,
+                                 scale=case["scale"])
+    np.testing.assert_allclose(o, arr("o"), rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(ht, arr("ht"), rtol=1e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------- brute force
+@pytest.mark.parametrize("with_h0", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1, 1), (2, 37, 3, 5, 7), (1, 130, 2, 16, 8)])
+def test_matches_brute_force(shape, with_h0):
+    B, T, H, K, V = shape
+    d = small_inputs(11 + T, B, T, H, K, V, h0=with_h0)
+    o, ht = oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], h0=d["h0"])
+    ob, hb = brute_force(d["q"], d["k"], d["v"], d["g"], h0=d["h0"])
+    assert rel_err(o, ob) < 1e-12
+    assert rel_err(ht, hb) < 1e-12
+
+
+def test_matches_brute_force_packed_with_empty_sequence():
+    lengths = [5, 0, 1, 64, 65, 3]
+    d = small_inputs(7, H=2, K=6, V=4, h0=True, lengths=lengths)
+    o, ht = oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], h0=d["h0"], cu_seqlens=d["cu_seqlens"])
+    ob, hb = brute_force(d["q"], d["k"], d["v"], d["g"], h0=d["h0"], cu=d["cu_seqlens"])
+    assert rel_err(o, ob) < 1e-12
+    assert rel_err(ht, hb) < 1e-12
+    # the empty sequence hands its initial state straight back
+    np.testing.assert_array_equal(ht[1], d["h0"][1].astype(np.float64))
+
+
+# ---------------------------------------------------------------- g == 0: causal linear attention
+def test_zero_gate_is_causal_linear_attention():
+    B, T, H, K, V = 2, 50, 2, 8, 6
+    d = small_inputs(3, B, T, H, K, V, h0=True)
+    g = np.zeros_like(d["g"])
+    scale = 0.37
+    o, ht = oracle.gla_reference(d["q"], d["k"], d["v"], g, h0=d["h0"], scale=scale)
+    for b in range(B):
+        for h in range(H):
+            Q = d["q"][b, :, h].astype(np.float64)
+            Kk = d["k"][b, :, h].astype(np.float64)
+            Vv = d["v"][b, :, h].astype(np.float64)
+            H0 = d["h0"][b, h].astype(np.float64)
+            ref = scale * (np.tril(Q @ Kk.T) @ Vv + Q @ H0)
+            assert rel_err(o[b, :, h], ref) < 1e-12
+            assert rel_err(ht[b, h], H0 + Kk.T @ Vv) < 1e-12
+
+
+# ---------------------------------------------------------------- single token
+def test_single_token_closed_form():
+    d = small_inputs(5, 1, 1, 1, 4, 3, h0=True)
+    q, k, v, g = (d[x][0, 0, 0].astype(np.float64) for x in ("q", "k", "v", "g"))
+    H0 = d["h0"][0, 0].astype(np.float64)
+    o, ht = oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], h0=d["h0"], scale=0.5)
+    S = np.exp(g)[:, None] * H0 + np.outer(k, v)
+    np.testing.assert_allclose(ht[0, 0], S, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(o[0, 0, 0], 0.5 * q @ S, rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- identities
+@pytest.mark.parametrize("t1", [1, 63, 64, 65, 100])
+def test_split_sequence_resume(t1):
+    B, T, H, K, V = 2, 200, 2, 8, 12
+    d = small_inputs(21, B, T, H, K, V, h0=True)
+    o, ht = oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], h0=d["h0"])
+    part = lambda x, s: np.ascontiguousarray(x[:, s])
+    o1, h1 = oracle.gla_reference(*(part(d[x], slice(0, t1)) for x in "qkvg"), h0=d["h0"])
+    o2, h2 = oracle.gla_reference(*(part(d[x], slice(t1, T)) for x in "qkvg"), h0=h1)
+    assert rel_err(np.concatenate([o1, o2], axis=1), o) < 1e-12
+    assert rel_err(h2, ht) < 1e-12
+
+
+def test_packed_equals_separate_runs():
+    lengths = [3, 0, 70, 1, 128]
+    d = small_inputs(31, H=2, K=4, V=5, h0=True, lengths=lengths)
+    o, ht = oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], h0=d["h0"], cu_seqlens=d["cu_seqlens"])
+    cu = d["cu_seqlens"]
+    for n in range(len(lengths)):
+        sl = slice(cu[n], cu[n + 1])
+        on, hn = oracle.gla_reference(*(np.ascontiguousarray(d[x][:, sl]) for x in "qkvg"),
+                                      h0=d["h0"][n:n + 1])
+        np.testing.assert_array_equal(o[:, sl], on)
+        np.testing.assert_array_equal(ht[n], hn[0])
+
+
+def test_scale_is_linear_and_heads_permute():
+    d = small_inputs(41, 1, 33, 3, 4, 4, h0=True)
+    o1, _ = oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], h0=d["h0"], scale=0.25)
+    o2, _ = oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], h0=d["h0"], scale=0.75)
+    assert rel_err(o2, 3.0 * o1) < 1e-13
+    perm = [2, 0, 1]
+    op, hp = oracle.gla_reference(*(np.ascontiguousarray(d[x][:, :, perm]) for x in "qkvg"),
+                                  h0=np.ascontiguousarray(d["h0"][:, perm]), scale=0.25)
+    np.testing.assert_array_equal(op, o1[:, :, perm])
+
+
+def test_strong_decay_limit():
+    # With g = -50 every earlier token is forgotten (e^-50 ~ 2e-22).
+    d = small_inputs(51, 1, 20, 2, 6, 5, h0=True)
+    g = np.full_like(d["g"], -50.0)
+    o, ht = oracle.gla_reference(d["q"], d["k"], d["v"], g, h0=d["h0"], scale=1.0)
+    q, k, v = (d[x][0].astype(np.float64) for x in "qkv")
+    ref = np.einsum("thk,thk->th", q, k)[:, :, None] * v
+    np.testing.assert_allclose(o[0], ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ht[0], np.einsum("hk,hv->hkv", k[-1], v[-1]), rtol=1e-12, atol=1e-12)
+
+
+def test_no_final_state_and_threads_agree():
+    d = small_inputs(61, 2, 40, 3, 8, 8, h0=False)
+    o1, ht1 = oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], output_final_state=False, threads=1)
+    o4, _ = oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], threads=4)
+    assert ht1 is None
+    np.testing.assert_array_equal(o1, o4)
+
+
+def test_rejects_bad_offsets():
+    d = small_inputs(71, H=1, K=2, V=2, h0=False, lengths=[2, 3])
+    bad = np.array([0, 4, 3], dtype=np.int32)
+    with pytest.raises(ValueError):
+        oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], cu_seqlens=bad)
+
+
+# ---------------------------------------------------------------- the pins catch plausible mistakes
+def _mutant(q, k, v, g, h0, cu, scale, mutation):
+    """Tiny pure-Python copy of the recurrence with one planted mistake."""
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    offs = list(cu) if cu is not None else [b * T for b in range(B + 1)]
+    qf, kf, vf, gf = (x.reshape(B * T, H, -1).astype(np.float64) for x in (q, k, v, g))
+    o = np.zeros((B * T, H, V))
+    N = len(offs) - 1
+    ht = np.zeros((N, H, K, V))
+    for n in range(N):
+        for h in range(H):
+            if mutation == "no_restart" and n > 0:
+                S = ht[n - 1, h].copy()
+            elif h0 is None or mutation == "drop_h0":
+                S = np.zeros((K, V))
+            else:
+                S = h0[n, h].astype(np.float64)
+            for t in range(offs[n], offs[n + 1]):
+                dec = np.exp(gf[t, h]) if mutation != "exp2" else np.exp2(gf[t, h])
+                outer = np.outer(kf[t, h], vf[t, h])
+                if mutation == "read_before_update":
+                    o[t, h] = scale * qf[t, h] @ (dec[:, None] * S)
+                    S = dec[:, None] * S + outer
+                    continue
+                if mutation == "decay_after_add":
+                    S = dec[:, None] * (S + outer)
+                elif mutation == "decay_columns" and K == V:
+                    S = S * dec[None, :] + outer
+                else:
+                    S = dec[:, None] * S + outer
+                o[t, h] = scale * qf[t, h] @ S
+            ht[n, h] = S
+    return o.reshape(B, T, H, V), ht
+
+
+@pytest.mark.parametrize("mutation", ["none", "read_before_update", "decay_after_add", "exp2",
+                                      "decay_columns", "drop_h0", "no_restart"])
+def test_pins_catch_planted_mistakes(mutation):
+    lengths = [9, 4]
+    d = gi.draw(81, 1, 0, 2, 4, 4, dtype="fp32", h0=True, lengths=lengths, gate_scale=0.5)
+    args = (d["q"], d["k"], d["v"], d["g"], d["h0"], d["cu_seqlens"], 0.5)
+    om, hm = _mutant(*args, mutation)
+    ob, hb = brute_force(d["q"], d["k"], d["v"], d["g"], h0=d["h0"], cu=d["cu_seqlens"], scale=0.5)
+    caught = rel_err(om, ob) > 1e-6 or rel_err(hm, hb) > 1e-6
+    if mutation == "none":
+        assert not caught
+        # and the real oracle agrees with the unmutated copy
+        oo, ho = oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], h0=d["h0"],
+                                      cu_seqlens=d["cu_seqlens"], scale=0.5)
+        assert rel_err(oo, om) < 1e-12 and rel_err(ho, hm) < 1e-12
+    else:
+        assert caught, f"mutation {mutation} slipped through the brute-force pin"
+
+
+# ---------------------------------------------------------------- input recipe
+def test_input_generator_is_deterministic_and_rounded():
+    a = gi.draw(5, 1, 16, 2, 8, 8, dtype="bf16", h0=True)
+    b = gi.draw(5, 1, 16, 2, 8, 8, dtype="bf16", h0=True)
+    assert gi.array_digest(*a.values()) == gi.array_digest(*b.values())
+    # bf16 values have zero low mantissa bits
+    for x in ("q", "k", "v"):
+        assert np.all((a[x].view(np.uint32) & 0xFFFF) == 0)
+    assert np.all(a["g"] < 0) and a["g"].dtype == np.float32
+    w = gi.WORKLOADS["varlen"]
+    d = gi.make_inputs(w)
+    assert len(d["lengths"]) == 16 and all(256 <= x <= 4096 for x in d["lengths"])
+    assert d["cu_seqlens"][-1] == d["q"].shape[1]
