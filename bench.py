@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Benchmark: chunkwise gated linear attention forward on one MI355X.
+
+Default workload: B=8, H=16, T=2048, K=V=128, bf16 q/k/v, fp32 gates, chunk 64,
+final state stored (synthetic seeded inputs, recipe in gla_inputs.py).
+
+A step is one full forward (every kernel of the path) over the whole batch,
+with inputs resident in device memory.  W untimed warmup steps, then exactly K
+timed steps between two device synchronisations; one JSON line is printed.
+
+Also reported:
+  roofline      the dominant kernel's algorithmic bytes per launch divided by its
+                average launch time, measured with HIP events on the launch stream
+                inside the timed region, against the 8 TB/s HBM peak; `traffic`
+                is the HBM bytes per launch measured by rocprofv3 counters for the
+                current kernel source (null when no matching measurement exists).
+  cpu_baseline  the fp64 CPU oracle (test infrastructure) on the host cores, on the
+                whole workload, in tokens/s.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import gla_inputs as gi  # noqa: E402
+
+METRIC = "GLA chunked fwd tokens/s + TFLOP/s, fraction of MFMA/HBM roofline (1 GPU)"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+KERNEL_SRC = os.path.join(ROOT, "chunkwise_gated_linear_amd", "csrc", "gla_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic(w, n_tokens, n_seqs):
+    """Bytes (inputs read once + outputs written once) and flops of the method."""
+    e = 2 if w.dtype == "bf16" else 4
+    H, K, V = w.H, w.K, w.V
+    th = n_tokens * H
+    nbytes = th * (2 * K * e + V * e + 4 * K) + th * V * e + 4 * n_seqs * H * K * V * (int(w.h0) + int(w.ht))
+    flops = th * (4 * K * V + (64 + 1) * (K + V))
+    return nbytes, flops
+
+
+def describe(w, lengths):
+    if w.varlen:
+        return (f"varlen {w.n_seqs} seqs lengths U[{w.len_lo},{w.len_hi}] total {sum(lengths)}, "
+                f"H={w.H} K={w.K} V={w.V} {w.dtype}, chunk {w.chunk}")
+    return (f"B={w.B},H={w.H},T={w.T},K={w.K},V={w.V} {w.dtype} q/k/v, g fp32 logsigmoid(N(0,1))/16, "
+            f"chunk {w.chunk}, h0={'yes' if w.h0 else 'no'}, ht={'stored' if w.ht else 'no'}")
+
+
+def load_traffic(workload: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = t.get(workload)
+    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2048", choices=sorted(gi.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--segment-chunks", type=int, default=0)
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build is a single-GPU kernel library; run it with --gpus 1 "
+              "(multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunkwise_gated_linear_amd as gla
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    gla.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = gi.WORKLOADS[args.workload]
+    d = gi.make_inputs(w)
+    lengths = d.get("lengths")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(d[x]).to(tdt).to(dev) for x in ("q", "k", "v"))
+    g = torch.from_numpy(d["g"]).to(dev)
+    h0 = None if d["h0"] is None else torch.from_numpy(d["h0"]).to(dev)
+    cu = None if d["cu_seqlens"] is None else torch.from_numpy(d["cu_seqlens"]).to(dev)
+    n_tokens = int(q.shape[0] * q.shape[1])
+    n_seqs = w.n_seqs if w.varlen else w.B
+    call = gla.GlaCall(q, k, v, g, h0=h0, cu_seqlens=cu, output_final_state=w.ht,
+                       segment_chunks=args.segment_chunks)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    for _ in range(args.warmup):
+        call(sptr)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        call(sptr)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ev_ms = [a.elapsed_time(b) for a, b in ev]
+    launch_ms = float(np.mean(ev_ms))
+
+    nbytes, flops = algorithmic(w, n_tokens, n_seqs)
+    tokens_per_s = n_tokens / (ms_per_step * 1e-3)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    achieved_gbs = nbytes / (launch_ms * 1e-3) / 1e9
+    t_roof = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_MFMA_PEAK_TFLOPS * 1e12))
+    traffic = load_traffic(args.workload)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        threads = len(os.sched_getaffinity(0))
+        c0 = time.perf_counter()
+        oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], h0=d["h0"], cu_seqlens=d["cu_seqlens"],
+                             output_final_state=w.ht, threads=threads)
+        c1 = time.perf_counter()
+        cpu = {"value": n_tokens / (c1 - c0), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"the whole workload ({n_tokens} tokens x {w.H} heads), fp64 token recurrence, "
+                         f"one run, {c1 - c0:.2f} s"}
+
+    segmented = call.ws_bytes > 0
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": describe(w, lengths), "tokens": n_tokens, "heads": w.H,
+                   "segmented_state_scan": segmented},
+        "tflops_algorithmic": tflops,
+        "roofline_time_us": t_roof * 1e6,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gla_chunk_output" if not segmented else "gla_fwd (chunk_local + state_scan + chunk_output)",
+            "achieved": achieved_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": nbytes,
+            "launch_ms_avg": launch_ms,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+"""Chunkwise gated linear attention forward on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libgla.so`` (declared in
+``include/gla.h``).  It only marshals arguments: torch provides device memory
+and the current HIP stream, every step of the computation runs in the
+library's HIP kernels.  There is no fallback: if the library is missing,
+importing the binding still works but every call raises.
+
+    o, ht = gla_fwd(q, k, v, g, h0=None, cu_seqlens=None, scale=None,
+                    chunk=64, output_final_state=False)
+
+Shapes are time-major: q, k, g [B, T, H, K]; v [B, T, H, V]; h0, ht
+[N, H, K, V] float32; cu_seqlens int32 [N+1] for packed sequences (B == 1).
+Defaults follow page "fla/ops/gla/fused_chunk.py" (fused_chunk_gla: scale
+defaults to K^-0.5, the final state is returned only on request) and page
+"fla/ops/ttt/fused_chunk.py" (fused_chunk_ttt_linear: a given scale must be
+positive, packed inputs need a batch of one and one initial state per
+sequence).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = ["gla_fwd", "GlaCall", "workspace_bytes", "library_path", "load_library", "GlaError",
+           "STATUS", "Problem"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgla.so")
+_lib = None
+
+STATUS = {
+    0: "GLA_OK", 1: "GLA_ERR_NULL_ARG", 2: "GLA_ERR_BAD_SHAPE", 3: "GLA_ERR_BAD_DTYPE",
+    4: "GLA_ERR_BAD_SCALE", 5: "GLA_ERR_UNSUPPORTED", 6: "GLA_ERR_WORKSPACE", 7: "GLA_ERR_HIP",
+}
+GLA_F32, GLA_BF16 = 0, 1
+CHUNK = 64
+
+
+class GlaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("n_seqs", ctypes.c_int32), ("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("segment_chunks", ctypes.c_int32), ("packed", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libgla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it first (python -m "
+                           "chunkwise_gated_linear_amd.build or __graft_entry__.build())")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp = ctypes.c_void_p
+    lib.gla_fwd_workspace_bytes.argtypes = [ctypes.POINTER(Problem)]
+    lib.gla_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.gla_fwd.argtypes = [ctypes.POINTER(Problem), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                            ctypes.c_size_t, vp]
+    lib.gla_fwd.restype = ctypes.c_int
+    lib.gla_status_str.argtypes = [ctypes.c_int]
+    lib.gla_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _status_msg(lib, code: int) -> str:
+    return lib.gla_status_str(code).decode()
+
+
+def make_problem(B, T, H, K, V, dtype_code, n_seqs, chunk=CHUNK, scale=1.0,
+                 segment_chunks=0, packed=False) -> Problem:
+    return Problem(int(B), int(T), int(H), int(K), int(V), int(dtype_code), int(n_seqs),
+                   int(chunk), float(scale), int(segment_chunks), 1 if packed else 0)
+
+
+def workspace_bytes(problem: Problem) -> int:
+    lib = load_library()
+    n = lib.gla_fwd_workspace_bytes(ctypes.byref(problem))
+    if n == ctypes.c_size_t(-1).value:
+        raise GlaError(2, "invalid problem")
+    return int(n)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def gla_fwd(q, k, v, g, h0=None, cu_seqlens=None, scale: Optional[float] = None,
+            chunk: int = CHUNK, output_final_state: bool = False, segment_chunks: int = 0,
+            workspace=None, out=None) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
+    """Gated linear attention forward through libgla.so.
+
+    Returns (o, ht): o has v's shape and dtype; ht is [N, H, K, V] float32 when
+    ``output_final_state`` else None.  Inputs must be contiguous tensors on one
+    HIP device; the call is asynchronous on torch's current stream.
+    """
+    import torch
+
+    lib = load_library()
+    if q.dim() != 4 or k.shape != q.shape or g.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("expected q, k, g [B, T, H, K] and v [B, T, H, V]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share a dtype")
+    if q.dtype == torch.bfloat16:
+        code = GLA_BF16
+    elif q.dtype == torch.float32:
+        code = GLA_F32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if g.dtype != torch.float32:
+        raise ValueError("g must be float32")
+    tensors = [q, k, v, g] + [t for t in (h0, cu_seqlens, out) if t is not None]
+    dev = q.device
+    if dev.type != "cuda" or any(t.device != dev for t in tensors):
+        raise ValueError("all tensors must live on the same GPU")
+    if not all(t.is_contiguous() for t in tensors):
+        raise ValueError("all tensors must be contiguous")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError(f"packed sequences need a batch of one, got B={B}")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor of N+1 offsets")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if h0 is not None:
+        if h0.dtype != torch.float32 or tuple(h0.shape) != (N, H, K, V):
+            raise ValueError(f"initial state must be float32 [{N}, {H}, {K}, {V}], "
+                             f"got {tuple(h0.shape)} {h0.dtype}")
+    if scale is None:
+        scale = K ** -0.5
+    elif not (scale > 0):
+        raise ValueError("scale must be positive")
+    prob = make_problem(B, T, H, K, V, code, N, chunk, scale, segment_chunks, cu_seqlens is not None)
+    with torch.cuda.device(dev):
+        ws = lib.gla_fwd_workspace_bytes(ctypes.byref(prob))
+        if ws == ctypes.c_size_t(-1).value:
+            code_v = lib.gla_fwd(ctypes.byref(prob), None, None, None, None, None, None, None, None,
+                                 None, 0, None)
+            raise GlaError(code_v, _status_msg(lib, code_v))
+        o = out if out is not None else torch.empty_like(v)
+        if out is not None and (out.shape != v.shape or out.dtype != v.dtype):
+            raise ValueError("out must match v's shape and dtype")
+        ht = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+        if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
+            workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.gla_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0),
+                         _ptr(cu_seqlens), _ptr(o), _ptr(ht),
+                         _ptr(workspace) if ws > 0 else None,
+                         (workspace.numel() * workspace.element_size()) if ws > 0 else 0,
+                         stream)
+    if rc != 0:
+        raise GlaError(rc, _status_msg(lib, rc))
+    return o, ht
+
+
+class GlaCall:
+    """A prepared forward: validates once, allocates o, ht and the workspace once,
+    and then enqueues the same C ABI call on every ``__call__`` (for timing loops
+    and stream capture).  ``stream`` defaults to torch's current stream at call time."""
+
+    def __init__(self, q, k, v, g, h0=None, cu_seqlens=None, scale=None, chunk: int = CHUNK,
+                 output_final_state: bool = False, segment_chunks: int = 0):
+        import torch
+
+        self.lib = load_library()
+        # validation and allocation through the same path as gla_fwd
+        o, ht = gla_fwd(q, k, v, g, h0=h0, cu_seqlens=cu_seqlens, scale=scale, chunk=chunk,
+                        output_final_state=output_final_state, segment_chunks=segment_chunks)
+        B, T, H, K = q.shape
+        V = v.shape[-1]
+        N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+        code = GLA_BF16 if q.dtype == torch.bfloat16 else GLA_F32
+        self.problem = make_problem(B, T, H, K, V, code, N, chunk, K ** -0.5 if scale is None else scale,
+                                    segment_chunks, cu_seqlens is not None)
+        self.device = q.device
+        ws = workspace_bytes(self.problem)
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=self.device)
+        self.ws_bytes = ws
+        self.o, self.ht = o, ht
+        self._args = (q, k, v, g, h0, cu_seqlens)
+
+    def __call__(self, stream=None):
+        import torch
+        q, k, v, g, h0, cu = self._args
+        s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
+        rc = self.lib.gla_fwd(ctypes.byref(self.problem), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0),
+                              _ptr(cu), _ptr(self.o), _ptr(self.ht),
+                              self.workspace.data_ptr() if self.ws_bytes > 0 else None,
+                              self.ws_bytes, s)
+        if rc != 0:
+            raise GlaError(rc, _status_msg(self.lib, rc))
+        return self.o, self.ht

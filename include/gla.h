@@ -1,0 +1,112 @@
+/*
+ * gla.h - C ABI of the chunkwise gated linear attention forward for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed (page "fla/ops/gla/fused_chunk.py": fused_chunk_gla and
+ * FusedChunkGLAFunction.forward, with fused_chunk_gla_fwd_kernel for the
+ * carried state and fwd_inner_chunk for the in-chunk term): for every
+ * sequence n and head h a K x V fp32 state follows
+ *
+ *     S_t = diag(exp(g_t)) S_{t-1} + k_t v_t^T,     o_t = scale * q_t^T S_t,
+ *
+ * starting from S_0 = h0[n,h] (or 0) and ending at ht[n,h] = S_T.  It is
+ * evaluated chunk by chunk (chunk = 64 tokens): in-chunk inclusive cumulative
+ * log decay G, the causal (diagonal included) gated score term
+ * (q exp(G)) (k exp(-G))^T v, and the inter-chunk term q exp(G) S with S
+ * carried across chunks.  Packed variable-length batches follow page
+ * "fla/ops/ttt/fused_chunk.py" (fused_chunk_ttt_linear): cu_seqlens holds
+ * N+1 token offsets into a batch of one, the state restarts per sequence,
+ * one h0 / ht per sequence.
+ *
+ * Conventions (all entry points):
+ *  - Every pointer argument of gla_fwd is DEVICE memory owned by the caller;
+ *    the library never allocates, frees or synchronises.  Work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the default stream) and runs
+ *    asynchronously: results are valid once that stream has reached the call.
+ *  - Layout is time-major and contiguous: q, k, g are [B, T, H, K], v and o are
+ *    [B, T, H, V], h0 and ht are [N, H, K, V] (row-major, V fastest).
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error nothing is written and the status says why.  The contents of
+ *    cu_seqlens are a precondition (cu[0] = 0, non-decreasing, cu[N] = T) and
+ *    are not checked.  NaN / Inf inputs propagate; they are not checked.
+ *  - Reentrant; the only global state is a per-device cache of the compute
+ *    unit count.  Calls that share a workspace buffer must be ordered by the
+ *    caller (same stream, or synchronised).
+ */
+#ifndef GLA_H_
+#define GLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gla_status {
+    GLA_OK = 0,
+    GLA_ERR_NULL_ARG = 1,     /* a required pointer is NULL                      */
+    GLA_ERR_BAD_SHAPE = 2,    /* negative / inconsistent sizes, B != 1 with cu_seqlens */
+    GLA_ERR_BAD_DTYPE = 3,    /* dtype is not GLA_F32 or GLA_BF16                */
+    GLA_ERR_BAD_SCALE = 4,    /* scale is not finite and > 0                      */
+    GLA_ERR_UNSUPPORTED = 5,  /* K, V or chunk outside the built kernel shapes     */
+    GLA_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than gla_fwd_workspace_bytes */
+    GLA_ERR_HIP = 7           /* a HIP runtime call or kernel launch failed       */
+} gla_status;
+
+typedef enum gla_dtype {
+    GLA_F32 = 0,   /* q, k, v, o are float32                                    */
+    GLA_BF16 = 1   /* q, k, v, o are bfloat16; g, h0, ht are float32 either way */
+} gla_dtype;
+
+typedef struct gla_problem {
+    int32_t B;        /* batch; must be 1 for packed sequences                         */
+    int32_t T;        /* tokens per sequence, or total packed tokens with cu_seqlens  */
+    int32_t H;        /* heads                                                        */
+    int32_t K;        /* key width: 32, 64 or 128 (bf16); 16, 32, 64 or 128 (fp32)   */
+    int32_t V;        /* value width: a positive multiple of 64                       */
+    int32_t dtype;    /* gla_dtype of q, k, v and o                                   */
+    int32_t n_seqs;   /* N: equal to B without cu_seqlens, len(cu_seqlens)-1 with it  */
+    int32_t chunk;    /* chunk length in tokens; 64 is the supported value            */
+    float scale;      /* multiplies q; finite and > 0 (callers map "default" to K^-0.5) */
+    int32_t segment_chunks; /* 0: automatic.  Else chunks per state segment: a       */
+                      /* sequence longer than this is split into segments whose start */
+                      /* states are produced by a scan over segment summaries.        */
+    int32_t packed;   /* 1 when cu_seqlens will be passed (packed sequences), else 0  */
+} gla_problem;
+
+/*
+ * Workspace bytes gla_fwd needs for problem `p` on the current device (0 when
+ * no workspace is needed).  Returns (size_t)-1 when `p` is invalid.  The
+ * value depends on the device's compute-unit count when segment_chunks is 0.
+ */
+size_t gla_fwd_workspace_bytes(const gla_problem *p);
+
+/*
+ * Chunkwise gated linear attention forward.
+ *   q, k   : [B,T,H,K] dtype            g  : [B,T,H,K] float32, natural-log decay
+ *   v      : [B,T,H,V] dtype            h0 : [N,H,K,V] float32 or NULL (zero state)
+ *   cu_seqlens : [N+1] int32 token offsets or NULL (then N = B sequences of T tokens)
+ *   o      : [B,T,H,V] dtype, written for every token of every sequence
+ *   ht     : [N,H,K,V] float32 or NULL; when non-NULL it receives the state after
+ *            each sequence's last token (h0, or zeros, for an empty sequence)
+ *   workspace / workspace_bytes : device scratch of at least
+ *            gla_fwd_workspace_bytes(p) bytes (may be NULL when that is 0)
+ *   stream : hipStream_t to enqueue on
+ * Returns GLA_OK or an error code (see gla_status); on error nothing is written.
+ */
+gla_status gla_fwd(const gla_problem *p,
+                   const void *q, const void *k, const void *v, const float *g,
+                   const float *h0, const int32_t *cu_seqlens,
+                   void *o, float *ht,
+                   void *workspace, size_t workspace_bytes,
+                   void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *gla_status_str(gla_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H_ */

@@ -1,0 +1,146 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerance (stated for the method): max|err| <= 1e-4 * rms(o_oracle) for fp32
+inputs and <= 2e-2 * rms(o_oracle) for bf16 inputs; the same rule is applied
+to the final state with rms(ht_oracle).  A bf16 output also carries its own
+storage rounding (half a bf16 ulp per element), which by itself exceeds
+2e-2 * rms on some small inputs (e.g. the T=63 case below: 2.0145e-2), so every
+case is checked against tol * rms plus that half ulp, and the five full-size
+workloads are additionally checked against the rule as stated.
+"""
+import numpy as np
+import pytest
+
+import gla_inputs as gi
+from gpu_helpers import TOL, check_close, rounding_floor, run_gpu, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import chunkwise_gated_linear_amd as gla
+    gla.load_library()
+    import oracle
+    oracle.build(force=False)
+
+
+def _compare(d, dtype, tag, scale=None, segment_chunks=0, literal=False):
+    say(f"[case] {tag} dtype={dtype} seg={segment_chunks} shape={d['q'].shape} V={d['v'].shape[-1]}")
+    o, ht = run_gpu(d, dtype, scale=scale, segment_chunks=segment_chunks)
+    ro, rht = run_oracle(d, scale=scale)
+    floor = rounding_floor(ro) if dtype == "bf16" else 0.0
+    eo = check_close(f"{tag} o", o, ro, TOL[dtype], out_dtype=dtype, literal=literal)
+    eh = check_close(f"{tag} ht", ht, rht, TOL[dtype])
+    say(f"[ok]   {tag}: o max|err| {eo:.4e} rms (bf16 rounding of the exact o: {floor:.4e}), "
+        f"ht {eh:.3e} rms")
+    return o, ht
+
+
+# ------------------------------------------------------------------ the five workloads, full size
+@pytest.mark.parametrize("name", ["small", "c2048", "c4096", "varlen", "long"])
+def test_workload_full_size(name):
+    w = gi.WORKLOADS[name]
+    d = gi.make_inputs(w)
+    # on these workloads the stated rule holds without the rounding allowance
+    _compare(d, w.dtype, f"workload {name}", literal=True)
+
+
+# ------------------------------------------------------------------ ragged lengths, several tiles
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 127, 200])
+def test_ragged_lengths(dtype, T):
+    d = gi.draw(100 + T, 2, T, 3, 64, 64, dtype=dtype, h0=True)
+    _compare(d, dtype, f"ragged T={T}")
+
+
+@pytest.mark.parametrize("dtype,K,V", [("bf16", 32, 64), ("bf16", 64, 128), ("bf16", 128, 256),
+                                        ("bf16", 128, 64), ("fp32", 16, 64), ("fp32", 32, 128),
+                                        ("fp32", 128, 128)])
+def test_head_dims(dtype, K, V):
+    d = gi.draw(7 * K + V, 2, 300, 2, K, V, dtype=dtype, h0=True)
+    _compare(d, dtype, f"K={K} V={V}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("seg", [1, 2, 3, 5])
+def test_forced_segments(dtype, seg):
+    # long sequences cut into segments: summary kernel + state scan + output walk
+    d = gi.draw(300 + seg, 2, 700, 2, 64, 128, dtype=dtype, h0=(seg % 2 == 1))
+    _compare(d, dtype, f"segments of {seg} chunks", segment_chunks=seg)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("seg", [0, 1, 2])
+def test_packed_sequences(dtype, seg):
+    lengths = [0, 1, 64, 65, 130, 7, 256, 0, 191]
+    d = gi.draw(500 + seg, 1, 0, 3, 64, 64, dtype=dtype, h0=True, lengths=lengths)
+    o, ht = _compare(d, dtype, f"packed lengths={lengths}", segment_chunks=seg)
+    # empty sequences return their initial state unchanged
+    np.testing.assert_array_equal(ht[0], d["h0"][0].astype(np.float64))
+    np.testing.assert_array_equal(ht[7], d["h0"][7].astype(np.float64))
+
+
+def test_empty_sequence_batch_returns_h0():
+    d = gi.draw(601, 2, 0, 2, 64, 64, dtype="bf16", h0=True)
+    o, ht = run_gpu(d, "bf16")
+    assert o.shape == (2, 0, 2, 64)
+    np.testing.assert_array_equal(ht, d["h0"].astype(np.float64))
+
+
+def test_no_initial_state_and_explicit_scale():
+    d = gi.draw(602, 3, 150, 2, 128, 128, dtype="bf16", h0=False)
+    _compare(d, "bf16", "scale=0.3", scale=0.3)
+
+
+def test_split_sequence_resume_on_gpu():
+    import torch
+    import chunkwise_gated_linear_amd as gla
+    from gpu_helpers import to_device
+    d = gi.draw(603, 1, 1000, 4, 128, 128, dtype="bf16", h0=True)
+    t = to_device(d, "bf16")
+    o, ht = gla.gla_fwd(t["q"], t["k"], t["v"], t["g"], h0=t["h0"], output_final_state=True)
+    T1 = 333
+    sl = lambda x, a, b: x[:, a:b].contiguous()
+    o1, h1 = gla.gla_fwd(*(sl(t[x], 0, T1) for x in "qkvg"), h0=t["h0"], output_final_state=True)
+    o2, h2 = gla.gla_fwd(*(sl(t[x], T1, 1000) for x in "qkvg"), h0=h1, output_final_state=True)
+    torch.cuda.synchronize()
+    both = torch.cat([o1, o2], dim=1).float()
+    ref = o.float()
+    r = ref.pow(2).mean().sqrt().item()
+    assert (both - ref).abs().max().item() <= 2e-2 * r
+    assert (h2 - ht).abs().max().item() <= 1e-4 * ht.pow(2).mean().sqrt().item()
+
+
+def test_bitwise_deterministic():
+    import torch
+    import chunkwise_gated_linear_amd as gla
+    from gpu_helpers import to_device
+    d = gi.draw(604, 2, 777, 4, 128, 128, dtype="bf16", h0=True)
+    t = to_device(d, "bf16")
+    a = gla.gla_fwd(t["q"], t["k"], t["v"], t["g"], h0=t["h0"], output_final_state=True, segment_chunks=3)
+    b = gla.gla_fwd(t["q"], t["k"], t["v"], t["g"], h0=t["h0"], output_final_state=True, segment_chunks=3)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_invalid_arguments_raise():
+    import torch
+    import chunkwise_gated_linear_amd as gla
+    dev = torch.device("cuda:0")
+    q = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16, device=dev)
+    v = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16, device=dev)
+    g = torch.zeros(1, 8, 1, 64, dtype=torch.float32, device=dev)
+    with pytest.raises(ValueError):
+        gla.gla_fwd(q, q, v, g, scale=-1.0)
+    with pytest.raises(ValueError):
+        gla.gla_fwd(q, q.float(), v, g)
+    with pytest.raises(gla.GlaError):
+        gla.gla_fwd(q[..., :48].contiguous(), q[..., :48].contiguous(), v, g[..., :48].contiguous())
+    q2 = torch.zeros(2, 8, 1, 64, dtype=torch.bfloat16, device=dev)
+    cu = torch.tensor([0, 4, 8], dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError):
+        gla.gla_fwd(q2, q2, q2, g.expand(2, 8, 1, 64).contiguous(), cu_seqlens=cu)
