@@ -82,7 +82,9 @@ def main():
     ap.add_argument("--workload", default="c2048", choices=sorted(gi.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--segment-chunks", type=int, default=0)
-    ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of the forward, run a plain device copy of a known size "
+                         "(used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -99,6 +101,17 @@ def main():
     gla.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        nbytes = 512 << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written": nbytes,
+                          "launches": args.steps}), flush=True)
+        return
 
     w = gi.WORKLOADS[args.workload]
     d = gi.make_inputs(w)

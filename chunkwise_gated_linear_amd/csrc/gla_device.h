@@ -1,0 +1,142 @@
+// Device helpers shared by the walker kernels (gla_kernels.hip, gla_walk_bf16.hip).
+#pragma once
+
+#include "gla_internal.h"
+
+namespace gla {
+namespace dev {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int C = kChunk;
+constexpr int VT = kVTile;
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round two floats to bf16 (nearest-even) and pack them, x0 in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t h;
+  h[0] = (__bf16)x0;
+  h[1] = (__bf16)x1;
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// Split 4 floats into bf16 hi (nearest) and bf16 lo (nearest of the remainder).
+__device__ __forceinline__ void split4(const float x[4], u32x2_t &hi, u32x2_t &lo) {
+  hi[0] = pack_bf16(x[0], x[1]);
+  hi[1] = pack_bf16(x[2], x[3]);
+  lo[0] = pack_bf16(x[0] - bf_lo(hi[0]), x[1] - bf_hi(hi[0]));
+  lo[1] = pack_bf16(x[2] - bf_lo(hi[1]), x[3] - bf_hi(hi[1]));
+}
+
+__device__ __forceinline__ f32x4_t mfma_bf(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_ld(const char *base, int byte_off) {
+  return *reinterpret_cast<const T *>(base + byte_off);
+}
+template <typename T>
+__device__ __forceinline__ void lds_st(char *base, int byte_off, T v) {
+  *reinterpret_cast<T *>(base + byte_off) = v;
+}
+
+// Storage column of contraction index p along K (bf16 layout).  Within each
+// 32-block, p = 16h + 4G + r is stored at 8G + 4h + r so that the eight
+// elements lane group G feeds to one 16x16x32 MFMA are contiguous; the
+// element order matches the accumulator layout of the state (rows 4G + r of
+// k-tiles 2b and 2b+1), which is what lets the state registers act directly
+// as the B operand of qc S'.
+__device__ __forceinline__ int kperm_bf(int p) {
+  return (p & ~31) | (((p >> 2) & 3) << 3) | (((p >> 4) & 1) << 2) | (p & 3);
+}
+
+// ---------------------------------------------------------------- locate a segment
+struct SegInfo {
+  int n, s, nseg, first, bos, len;
+};
+
+__device__ __forceinline__ bool locate(const WalkParams &p, int seg, SegInfo &si) {
+  if (p.seg_base == nullptr) {
+    si.n = seg / p.P;
+    si.s = seg - si.n * p.P;
+    if (si.n >= p.N) return false;
+    si.nseg = p.P;
+    si.first = si.n * p.P;
+  } else {
+    const int total = p.seg_base[p.N];
+    if (seg >= total) return false;
+    int lo = 0, hi = p.N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.seg_base[mid] <= seg) lo = mid; else hi = mid - 1;
+    }
+    si.n = lo;
+    si.first = p.seg_base[lo];
+    si.nseg = p.seg_base[lo + 1] - si.first;
+    si.s = seg - si.first;
+  }
+  if (p.cu != nullptr) {
+    si.bos = p.cu[si.n];
+    si.len = p.cu[si.n + 1] - si.bos;
+  } else {
+    si.bos = si.n * p.T;
+    si.len = p.T;
+  }
+  // every lane of the workgroup holds the same values; say so, so that they
+  // live in scalar registers (buffer descriptors built from them must be uniform)
+  si.n = __builtin_amdgcn_readfirstlane(si.n);
+  si.s = __builtin_amdgcn_readfirstlane(si.s);
+  si.nseg = __builtin_amdgcn_readfirstlane(si.nseg);
+  si.first = __builtin_amdgcn_readfirstlane(si.first);
+  si.bos = __builtin_amdgcn_readfirstlane(si.bos);
+  si.len = __builtin_amdgcn_readfirstlane(si.len);
+  return true;
+}
+
+
+// ---------------------------------------------------------------- buffer access
+// Raw buffer descriptor over `bytes` bytes from `base` (word 3 as for the gfx9
+// family).  Loads past `bytes` return zero and stores past it are dropped,
+// which is how partial chunks are padded / clipped without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
+  n = __builtin_amdgcn_readfirstlane(n);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t au = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(au), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_ld128(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2_t buf_ld64(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_st128(__amdgpu_buffer_rsrc_t r, int off, u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off, 0, 0);
+}
+
+// LDS transposing read of four 16-bit elements (ds_read_b64_tr_b16).  Within
+// each group of 16 lanes, lane j receives component j%4 of the 8-byte words
+// addressed by lanes j/4, j/4+4, j/4+8 and j/4+12 of its group.
+__device__ __forceinline__ u32x2_t lds_tr16(const char *p) {
+  typedef short v4i16_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+  const lds_v4i16_t *lp = (const lds_v4i16_t *)(const __attribute__((address_space(3))) char *)p;
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_v4i16_t *>(lp)));
+}
+
+}  // namespace dev
+}  // namespace gla

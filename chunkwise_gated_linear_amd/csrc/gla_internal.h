@@ -32,6 +32,9 @@ struct WalkParams {
 // Launchers (return the hipGetLastError() of the launch).
 hipError_t launch_walk(bool local_mode, bool bf16, int K, const WalkParams &p, hipStream_t s);
 hipError_t launch_state_scan(const WalkParams &p, hipStream_t s);
+// bf16 walker for K in {64, 128} (gla_walk_bf16.hip)
+bool walk_bf16_supported(int K);
+hipError_t launch_walk_bf16(bool local_mode, int K, const WalkParams &p, hipStream_t s);
 hipError_t launch_segment_plan(const WalkParams &p, int32_t *seg_base, hipStream_t s);
 
 }  // namespace gla

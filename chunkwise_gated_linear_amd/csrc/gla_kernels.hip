@@ -37,102 +37,15 @@
 // slice; its lanes hold the K x 16 state block in MFMA accumulator layout
 // (lane l: column l%16, rows 16*kt + 4*(l/16) + r).
 #include "gla_internal.h"
+#include "gla_device.h"
 
+#include <cstdlib>
 #include <type_traits>
 
 namespace gla {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int C = kChunk;
-constexpr int VT = kVTile;
-
-// ---------------------------------------------------------------- helpers
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Round two floats to bf16 (nearest-even) and pack them, x0 in the low half.
-__device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  bf16x2_t h;
-  h[0] = (__bf16)x0;
-  h[1] = (__bf16)x1;
-  return __builtin_bit_cast(uint32_t, h);
-}
-
-// Split 4 floats into bf16 hi (nearest) and bf16 lo (nearest of the remainder).
-__device__ __forceinline__ void split4(const float x[4], u32x2_t &hi, u32x2_t &lo) {
-  hi[0] = pack_bf16(x[0], x[1]);
-  hi[1] = pack_bf16(x[2], x[3]);
-  lo[0] = pack_bf16(x[0] - bf_lo(hi[0]), x[1] - bf_hi(hi[0]));
-  lo[1] = pack_bf16(x[2] - bf_lo(hi[1]), x[3] - bf_hi(hi[1]));
-}
-
-__device__ __forceinline__ f32x4_t mfma_bf(u32x4_t a, u32x4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-template <typename T>
-__device__ __forceinline__ T lds_ld(const char *base, int byte_off) {
-  return *reinterpret_cast<const T *>(base + byte_off);
-}
-template <typename T>
-__device__ __forceinline__ void lds_st(char *base, int byte_off, T v) {
-  *reinterpret_cast<T *>(base + byte_off) = v;
-}
-
-// Storage column of contraction index p along K (bf16 layout).  Within each
-// 32-block, p = 16h + 4G + r is stored at 8G + 4h + r so that the eight
-// elements lane group G feeds to one 16x16x32 MFMA are contiguous; the
-// element order matches the accumulator layout of the state (rows 4G + r of
-// k-tiles 2b and 2b+1), which is what lets the state registers act directly
-// as the B operand of qc S'.
-__device__ __forceinline__ int kperm_bf(int p) {
-  return (p & ~31) | (((p >> 2) & 3) << 3) | (((p >> 4) & 1) << 2) | (p & 3);
-}
-
-// ---------------------------------------------------------------- locate a segment
-struct SegInfo {
-  int n, s, nseg, first, bos, len;
-};
-
-__device__ __forceinline__ bool locate(const WalkParams &p, int seg, SegInfo &si) {
-  if (p.seg_base == nullptr) {
-    si.n = seg / p.P;
-    si.s = seg - si.n * p.P;
-    if (si.n >= p.N) return false;
-    si.nseg = p.P;
-    si.first = si.n * p.P;
-  } else {
-    const int total = p.seg_base[p.N];
-    if (seg >= total) return false;
-    int lo = 0, hi = p.N - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.seg_base[mid] <= seg) lo = mid; else hi = mid - 1;
-    }
-    si.n = lo;
-    si.first = p.seg_base[lo];
-    si.nseg = p.seg_base[lo + 1] - si.first;
-    si.s = seg - si.first;
-  }
-  if (p.cu != nullptr) {
-    si.bos = p.cu[si.n];
-    si.len = p.cu[si.n + 1] - si.bos;
-  } else {
-    si.bos = si.n * p.T;
-    si.len = p.T;
-  }
-  return true;
-}
+using namespace dev;
 
 // ---------------------------------------------------------------- LDS plan
 template <bool BF, int KD, bool OUT>
@@ -704,9 +617,19 @@ hipError_t launch_walk_t(bool local_mode, const WalkParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// GLA_GENERAL_WALKER=1 routes bf16 through the general walker (for A/B comparisons).
+bool general_walker_forced() {
+  static const bool forced = [] {
+    const char *e = getenv("GLA_GENERAL_WALKER");
+    return e != nullptr && e[0] == '1';
+  }();
+  return forced;
+}
+
 }  // namespace
 
 hipError_t launch_walk(bool local_mode, bool bf16, int K, const WalkParams &p, hipStream_t s) {
+  if (bf16 && walk_bf16_supported(K) && !general_walker_forced()) return launch_walk_bf16(local_mode, K, p, s);
   if (bf16) {
     switch (K) {
       case 32: return launch_walk_t<true, 32>(local_mode, p, s);
