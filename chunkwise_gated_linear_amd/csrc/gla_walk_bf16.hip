@@ -9,19 +9,22 @@
 //   qc_i = scale q_i P_i / a,  kc_j = k_j R_j    (P, R: running products of exp(g))
 //   A = mask_{j<=i}(qc kc^T),  S' = diag(a) S,  o = A v + qc S',  S = S' + kc^T v
 //
-// Layout for gfx950:
-//  * The four waves tile the K x 64 state slice as 2 (key halves) x 2 (value
-//    halves of 32 columns); wave (kh, nh) keeps S[64kh + ..][32nh + ..] in MFMA
-//    accumulators.  Each wave forms a partial output over its key half; the
-//    two partials meet in LDS and are summed by the store pass.
-//  * qc and kc live in LDS once, token-major (key contiguous).  The key-major
-//    operand kc^T of S += kc^T v and the value operand v of A v and kc^T v are
-//    read with the LDS transpose read ds_read_b64_tr_b16, so no transposed copy
-//    is ever written.
-//  * Global traffic uses buffer descriptors per chunk: rows past the end of a
+// Layout for gfx950 (one workgroup of 8 waves per (segment, head, 64-column
+// slice of V), two waves per SIMD):
+//  * Waves 4-7 produce: they load the raw q, k, g, v of chunk c+2, form the
+//    gated and split operands of chunk c+1 in registers and write them to LDS
+//    when chunk c is done.  Their memory stalls and vector work run beside the
+//    matrix waves on the same SIMDs.
+//  * Waves 0-3 compute.  They tile the K x 64 state slice as 2 key halves x 2
+//    value halves (32 columns) and keep it in MFMA accumulators.  Each
+//    computes some of the ten lower 16x16 score tiles (shared through LDS),
+//    then a partial output over its key half (A v for one 32-token block of
+//    every row tile, qc S' over its key half) and its state update.  The two
+//    key-half partials meet in LDS and are summed by the store pass.
+//  * kc^T and v are read as MFMA operands with the LDS transpose read
+//    ds_read_b64_tr_b16, so no transposed copy is written.
+//  * Global traffic uses per-chunk buffer descriptors: rows past the end of a
 //    sequence read as zero and their output stores are dropped.
-//  * The next chunk's q, k, g, v are loaded into registers while the current
-//    chunk computes.
 #include "gla_device.h"
 #include "gla_internal.h"
 
@@ -32,39 +35,90 @@ namespace {
 
 using namespace dev;
 
+constexpr int kWsThreads = 512;  // 4 matrix waves + 4 producer waves
+
 template <int KD, bool OUT>
-struct LdsB {
-  static constexpr int NQ = KD / 4;                // prologue column quads
-  static constexpr int QPW = NQ / 4;               // column quads per wave
-  static constexpr int NG = 64 / QPW;              // prologue row groups
+struct LdsW {
+  static constexpr int NQ = KD / 4;                // producer column quads
+  static constexpr int QPW = NQ / 4;               // column quads per producer wave
+  static constexpr int NG = 64 / QPW;              // producer row groups
   static constexpr int QROW = 2 * KD + 16;         // qc / kc rows (bf16)
-  static constexpr int VROW = 2 * VT + 32;         // v rows (bf16): 4 rows x 32 B of one transpose read fall in distinct banks
+  static constexpr int VROW = 2 * VT + 32;         // v rows (bf16): the 4 rows x 32 B of one transpose read fall in distinct banks
+  static constexpr int AROW = 2 * C + 16;          // score rows (bf16)
   static constexpr int OROW = 4 * VT + 16;         // partial outputs (fp32)
   static constexpr int QPL = C * QROW;             // one plane of qc or kc
+  static constexpr int APL = C * AROW;
   static constexpr int OPL = C * OROW;
-  static constexpr int oQ = 0;                     // qc hi, lo            (OUT)
-  static constexpr int oK = oQ + (OUT ? 2 * QPL : 0);   // kc hi, lo
-  static constexpr int oV = oK + 2 * QPL;          // v [token][n]
-  static constexpr int oO = oV + C * VROW;         // partial o [kh][i][n] (OUT)
-  static constexpr int oDec = oO + (OUT ? 2 * OPL : 0); // a [K]
+  static constexpr int oQ = 0;                            // qc hi, lo              (OUT)
+  static constexpr int oK = oQ + (OUT ? 2 * QPL : 0);     // kc hi, lo
+  static constexpr int oV = oK + 2 * QPL;                 // v [token][n]
+  static constexpr int oA = oV + C * VROW;                // A hi, lo [i][j]        (OUT)
+  static constexpr int oO = oA + (OUT ? 2 * APL : 0);     // partial o [kh][i][n]   (OUT)
+  static constexpr int oDec = oO + (OUT ? 2 * OPL : 0);   // a [K]
   static constexpr int BYTES = oDec + 4 * KD;
 };
 
+// Score tiles (i-tile, j-tile) of the 64 x 64 lower triangle per matrix wave.
+template <int W> struct Tiles;
+template <> struct Tiles<0> { static constexpr int n = 3; static constexpr int it[3] = {0, 1, 1}, jt[3] = {0, 0, 1}; };
+template <> struct Tiles<1> { static constexpr int n = 3; static constexpr int it[3] = {2, 2, 2}, jt[3] = {0, 1, 2}; };
+template <> struct Tiles<2> { static constexpr int n = 2; static constexpr int it[2] = {3, 3}, jt[2] = {0, 1}; };
+template <> struct Tiles<3> { static constexpr int n = 2; static constexpr int it[2] = {3, 3}, jt[2] = {2, 3}; };
+
+// A^T tiles = kc qc^T for wave W's tiles, causal mask, split -> LDS A[i][j].
+template <int KD, int W>
+__device__ __forceinline__ void scores(char *smem, int l16, int lg) {
+  using L = LdsW<KD, true>;
+  using T = Tiles<W>;
+  f32x4_t acc[T::n];
+#pragma unroll
+  for (int t = 0; t < T::n; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int lq = l16 * L::QROW + 16 * lg;
+#pragma unroll
+  for (int kb = 0; kb < KD / 32; ++kb) {
+#pragma unroll
+    for (int t = 0; t < T::n; ++t) {
+      const int oa = lq + 16 * T::jt[t] * L::QROW + 64 * kb;
+      const int ob = lq + 16 * T::it[t] * L::QROW + 64 * kb;
+      const u32x4_t ah = lds_ld<u32x4_t>(smem + L::oK, oa);
+      const u32x4_t al = lds_ld<u32x4_t>(smem + L::oK + L::QPL, oa);
+      const u32x4_t bh = lds_ld<u32x4_t>(smem + L::oQ, ob);
+      const u32x4_t bl = lds_ld<u32x4_t>(smem + L::oQ + L::QPL, ob);
+      acc[t] = mfma_bf(al, bh, acc[t]);
+      acc[t] = mfma_bf(ah, bl, acc[t]);
+      acc[t] = mfma_bf(ah, bh, acc[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < T::n; ++t) {
+    // lane: i = 16 it + l16, j = 16 jt + 4 lg + r
+    const int i = 16 * T::it[t] + l16;
+    float av[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) av[r] = (16 * T::jt[t] + 4 * lg + r <= i) ? acc[t][r] : 0.f;
+    u32x2_t hi, lo;
+    split4(av, hi, lo);
+    const int off = i * L::AROW + (16 * T::jt[t] + 4 * lg) * 2;
+    lds_st<u32x2_t>(smem + L::oA, off, hi);
+    lds_st<u32x2_t>(smem + L::oA + L::APL, off, lo);
+  }
+}
+
 template <bool OUT, int KD>
 __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
-  using L = LdsB<KD, OUT>;
+  using L = LdsW<KD, OUT>;
   constexpr int QPW = L::QPW, NG = L::NG, RPG = C / NG;
-  constexpr int KH = KD / 2;        // state rows per wave
-  constexpr int NKT = KH / 16;      // 16-row k tiles per wave
-  constexpr int NKB = KH / 32;      // 32-wide k blocks per wave
+  constexpr int KH = KD / 2;        // state rows per matrix wave
+  constexpr int NKT = KH / 16;      // 16-row k tiles per matrix wave
+  constexpr int NKB = KH / 32;      // 32-wide k blocks per matrix wave
   static_assert(KD == 64 || KD == 128, "bf16 walker covers K = 64, 128");
-  static_assert(NG * QPW == 64 && RPG * NG == C, "prologue mapping");
+  static_assert(NG * QPW == 64 && RPG * NG == C, "producer mapping");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = wave >= 4;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int kh = wave >> 1, nh = wave & 1;
 
   // ---- (segment, head, value slice) of this workgroup; value slices of one
   // unit are 8 workgroup ids apart so they run on the same XCD and share L2.
@@ -84,10 +138,12 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   const int H = p.H, V = p.V;
   const int v0 = vt * VT;
   const int64_t rowK = (int64_t)H * KD, rowV = (int64_t)H * V;
+  const int seq_bos = si.bos, seq_len = si.len;
 
-  // ---- state block of this lane: S[KH kh + 16kt + 4lg + r][v0 + 32nh + 16nt + l16]
+  // ======================= matrix waves: state and lane bases
+  const int mw = wave & 3, kh = mw >> 1, nh = mw & 1;
   f32x4_t S[NKT][2];
-  {
+  if (!producer) {
     const float *src = nullptr;
     if (OUT) {
       if (si.s == 0) {
@@ -104,53 +160,74 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
         for (int r = 0; r < 4; ++r)
           S[kt][nt][r] = src ? src[(int64_t)(KH * kh + 16 * kt + 4 * lg + r) * V + v0 + 32 * nh + 16 * nt + l16] : 0.f;
   }
+  if (OUT) {  // score tiles above the diagonal are read as zeros and never written
+    for (int i = tid; i < 2 * L::APL / 16; i += kWsThreads)
+      lds_st<u32x4_t>(smem + L::oA, 16 * i, u32x4_t{0, 0, 0, 0});
+  }
+  const int base_q = l16 * L::QROW + 16 * lg;                                          // rows of qc
+  const int base_a = l16 * L::AROW + 16 * lg;                                          // rows of A
+  const int base_vt = (8 * lg + (l16 >> 2)) * L::VROW + (32 * nh + 4 * (l16 & 3)) * 2;  // v, transposed
+  const int base_kt = (8 * lg + (l16 >> 2)) * L::QROW + (KH * kh + 8 * (l16 & 3)) * 2;  // kc, transposed
+  const int base_o = 4 * lg * L::OROW + (32 * nh + l16) * 4 + kh * L::OPL;             // partial o
+  const int base_d = (KH * kh + 4 * lg) * 4;                                           // decay
 
-  // ---- prologue mapping: wave w gates key columns [32w, 32w+32) (K=128) of all 64
-  // rows; lane = rg * QPW + quad: rows rg*RPG .. +RPG-1, columns 4cq .. 4cq+3.
-  // The running products across row groups stay inside the wave (lane shuffles).
-  // v: row tid/4, 16 columns.
-  const int cq = wave * QPW + lane % QPW, rg = lane / QPW;
+  // ======================= producer waves: raw and gated registers
+  // producer thread pt: key columns 4cq..4cq+3 of rows rg*RPG..+RPG-1; v row pt/4, 16 columns
+  const int pt = tid - 4 * 64;
+  const int cq = (wave & 3) * QPW + lane % QPW, rg = lane / QPW;
   const int voff_g = (int)((rg * RPG * rowK + 4 * cq) * 4);
   const int voff_k = (int)((rg * RPG * rowK + 4 * cq) * 2);
-  const int vrow = tid >> 2, vcol = 16 * (tid & 3);
+  const int vrow = (pt & 255) >> 2, vcol = 16 * (pt & 3);
   const int voff_v = (int)((vrow * rowV + vcol) * 2);
   const int step_g = (int)(rowK * 4), step_k = (int)(rowK * 2);
   const int colq = kperm_bf(4 * cq) * 2;
-
-  // Software pipeline over chunks: while chunk c runs on the matrix cores, the
-  // gated operands of chunk c+1 are formed in registers and the raw inputs of
-  // chunk c+2 are loaded.  Loads past the sequence (or past the segment) read
-  // zeros, so the pipeline runs the same instruction stream every iteration.
-  u32x4_t rgG[RPG];                       // raw inputs of the chunk to gate next
+  u32x4_t rgG[RPG];
   u32x2_t rgQ[RPG], rgK[RPG];
   u32x4_t rgV[2];
-  u32x2_t gQh[RPG], gQl[RPG], gKh[RPG], gKl[RPG];   // gated operands of the chunk to compute next
+  u32x2_t gQh[RPG], gQl[RPG], gKh[RPG], gKl[RPG];
   u32x4_t gV[2];
   f32x4_t gDec = {1.f, 1.f, 1.f, 1.f};
-
+  float gPl[RPG][4], gRl[RPG][4], gSuf[4], gFq[4];
   float seg_decay[4] = {1.f, 1.f, 1.f, 1.f};
   const float scale = p.scale;
 
-  // gate: decays of the chunk and the gated, split q and k in registers.  It
-  // runs in stages so that its vector work can be spread between the matrix
-  // instructions of the previous chunk.
-  float gE[RPG][4], gPl[RPG][4], gRl[RPG][4], gSuf[4], gFq[4];
-  auto gate_a = [&]() {  // exp(g) and running products inside the row group
+  auto load_chunk = [&](int c) {
+    const int64_t t0 = (int64_t)seq_bos + (int64_t)c * C;
+    const int64_t valid = c < c_end ? min(C, seq_len - c * C) : 0;
+    const int64_t headK = (int64_t)h * KD, headV = (int64_t)h * V + v0;
+    const __amdgpu_buffer_rsrc_t rG = make_rsrc(p.g + t0 * rowK + headK, (valid * rowK - headK) * 4);
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc((const uint16_t *)p.k + t0 * rowK + headK, (valid * rowK - headK) * 2);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc((const uint16_t *)p.v + t0 * rowV + headV, (valid * rowV - headV) * 2);
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+      rgG[r] = buf_ld128(rG, voff_g + r * step_g);
+      rgK[r] = buf_ld64(rK, voff_k + r * step_k);
+    }
+    if (OUT) {
+      const __amdgpu_buffer_rsrc_t rQ = make_rsrc((const uint16_t *)p.q + t0 * rowK + headK, (valid * rowK - headK) * 2);
+#pragma unroll
+      for (int r = 0; r < RPG; ++r) rgQ[r] = buf_ld64(rQ, voff_k + r * step_k);
+    }
+    rgV[0] = buf_ld128(rV, voff_v);
+    rgV[1] = buf_ld128(rV, voff_v + 16);
+  };
+  // gate, stage 1: exp(g), running products inside the row group and across row
+  // groups (lane shuffles inside the wave), chunk decay and the q / k factors
+  auto gate_decays = [&]() {
+    float E[RPG][4];
 #pragma unroll
     for (int r = 0; r < RPG; ++r)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) gE[r][j] = __expf(__uint_as_float(rgG[r][j]));
+      for (int j = 0; j < 4; ++j) E[r][j] = __expf(__uint_as_float(rgG[r][j]));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      gPl[0][j] = gE[0][j];
+      gPl[0][j] = E[0][j];
 #pragma unroll
-      for (int r = 1; r < RPG; ++r) gPl[r][j] = gPl[r - 1][j] * gE[r][j];
+      for (int r = 1; r < RPG; ++r) gPl[r][j] = gPl[r - 1][j] * E[r][j];
       gRl[RPG - 1][j] = 1.f;
 #pragma unroll
-      for (int r = RPG - 2; r >= 0; --r) gRl[r][j] = gRl[r + 1][j] * gE[r + 1][j];
+      for (int r = RPG - 2; r >= 0; --r) gRl[r][j] = gRl[r + 1][j] * E[r + 1][j];
     }
-  };
-  auto gate_b = [&]() {  // products over row groups: inclusive scan across the lanes of a column quad
     float incl[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) incl[j] = gPl[RPG - 1][j];
@@ -170,7 +247,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       const float y = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src_pre, __float_as_int(incl[j])));
       const float pre = rg > 0 ? y : 1.f;
       const float tot = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src_tot, __float_as_int(incl[j])));
-      gSuf[j] = tot * __builtin_amdgcn_rcpf(incl[j]);
+      gSuf[j] = tot * __builtin_amdgcn_rcpf(incl[j]);   // product over the later row groups
       gFq[j] = OUT ? scale * pre * __builtin_amdgcn_rcpf(tot) : 0.f;
       gDec[j] = tot;
     }
@@ -179,9 +256,10 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       for (int j = 0; j < 4; ++j) seg_decay[j] *= gDec[j];
     }
   };
-  auto gate_rows = [&](int r0, int r1) {  // gated, split q and k of rows [r0, r1)
+  // gate, stage 2: gated and split q, k rows
+  auto gate_rows = [&]() {
 #pragma unroll
-    for (int r = r0; r < r1; ++r) {
+    for (int r = 0; r < RPG; ++r) {
       float kc[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -199,39 +277,9 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
         split4(qc, gQh[r], gQl[r]);
       }
     }
-  };
-  auto gate = [&]() {
-    gate_a();
-    gate_b();
-    gate_rows(0, RPG);
     gV[0] = rgV[0];
     gV[1] = rgV[1];
   };
-  // loads of one chunk in four parts (g first half, g second half, k and q, v)
-  auto load_part = [&](int c, int part) {
-    const int64_t t0 = (int64_t)si.bos + (int64_t)c * C;
-    const int64_t valid = c < c_end ? min(C, si.len - c * C) : 0;
-    const int64_t headK = (int64_t)h * KD, headV = (int64_t)h * V + v0;
-    if (part == 0 || part == 1) {
-      const __amdgpu_buffer_rsrc_t rG = make_rsrc(p.g + t0 * rowK + headK, (valid * rowK - headK) * 4);
-#pragma unroll
-      for (int r = part * RPG / 2; r < (part + 1) * RPG / 2; ++r) rgG[r] = buf_ld128(rG, voff_g + r * step_g);
-    } else if (part == 2) {
-      const __amdgpu_buffer_rsrc_t rK = make_rsrc((const uint16_t *)p.k + t0 * rowK + headK, (valid * rowK - headK) * 2);
-#pragma unroll
-      for (int r = 0; r < RPG; ++r) rgK[r] = buf_ld64(rK, voff_k + r * step_k);
-      if (OUT) {
-        const __amdgpu_buffer_rsrc_t rQ = make_rsrc((const uint16_t *)p.q + t0 * rowK + headK, (valid * rowK - headK) * 2);
-#pragma unroll
-        for (int r = 0; r < RPG; ++r) rgQ[r] = buf_ld64(rQ, voff_k + r * step_k);
-      }
-    } else {
-      const __amdgpu_buffer_rsrc_t rV = make_rsrc((const uint16_t *)p.v + t0 * rowV + headV, (valid * rowV - headV) * 2);
-      rgV[0] = buf_ld128(rV, voff_v);
-      rgV[1] = buf_ld128(rV, voff_v + 16);
-    }
-  };
-
   auto write_gated = [&]() {
 #pragma unroll
     for (int r = 0; r < RPG; ++r) {
@@ -248,240 +296,198 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
     if (rg == 0) lds_st<f32x4_t>(smem + L::oDec, 16 * cq, gDec);
   };
 
-  // lane bases of the matrix-phase LDS accesses
-  // The token (contraction) index of A v and kc^T v is taken in the order of
-  // the score accumulators: within a 32-token block jb, lane group lg holds
-  // tokens 32jb + 16h + 4lg + e (h = 0, 1; e = 0..3) -- so the score tiles
-  // feed A v straight from registers.  Transpose reads deliver that order.
-  const int base_q = l16 * L::QROW + 16 * lg;                                  // normal reads, rows of qc / kc
-  const int base_vt = (4 * lg + (l16 >> 2)) * L::VROW + (32 * nh + 4 * (l16 & 3)) * 2;   // transpose reads of v
-  const int base_kt = (4 * lg + (l16 >> 2)) * L::QROW + (KH * kh + 8 * (l16 & 3)) * 2;   // transpose reads of kc
-  const int base_o = 4 * lg * L::OROW + (32 * nh + l16) * 4 + kh * L::OPL;     // partial o writes
-  const int base_d = (KH * kh + 4 * lg) * 4;                                   // decay reads
-
-  // ---- pipeline fill
-  if (c_begin < c_end) {
-    for (int part = 0; part < 4; ++part) load_part(c_begin, part);
-    gate();
-    for (int part = 0; part < 4; ++part) load_part(c_begin + 1, part);
-  }
-
-  for (int c = c_begin; c < c_end; ++c) {
-    write_gated();
-    __syncthreads();  // chunk c operands visible
-
-    // ---- S' = diag(a) S
+  // Output pass after the third barrier of chunk c: all 512 threads sum the two
+  // key-half partials, round to bf16 and store 16 B each.
+  auto store_out = [&](int c) {
+    // ---- sum the two key-half partials, round to bf16, 16 B per thread
+    const int64_t t0 = (int64_t)seq_bos + (int64_t)c * C;
+    const int64_t valid = min(C, seq_len - c * C);
+    const int64_t headV = (int64_t)h * V + v0;
+    const __amdgpu_buffer_rsrc_t rO = make_rsrc((uint16_t *)p.o + t0 * rowV + headV, (valid * rowV - headV) * 2);
+    const int orow = tid >> 3, ocol = 8 * (tid & 7);
+    uint32_t w[4];
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      const f32x4_t a4 = lds_ld<f32x4_t>(smem + L::oDec, base_d + 64 * kt);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[kt][nt][r] *= a4[r];
+    for (int x = 0; x < 2; ++x) {
+      const f32x4_t a0 = lds_ld<f32x4_t>(smem + L::oO, orow * L::OROW + (ocol + 4 * x) * 4);
+      const f32x4_t a1 = lds_ld<f32x4_t>(smem + L::oO + L::OPL, orow * L::OROW + (ocol + 4 * x) * 4);
+      w[2 * x] = pack_bf16(a0[0] + a1[0], a0[1] + a1[1]);
+      w[2 * x + 1] = pack_bf16(a0[2] + a1[2], a0[3] + a1[3]);
     }
-    // ---- v fragments (B operand of A v and kc^T v)
-    u32x4_t vf[2][2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        const int off = base_vt + 32 * jb * L::VROW + 32 * nt;
-        const u32x2_t x0 = lds_tr16(smem + L::oV + off);
-        const u32x2_t x1 = lds_tr16(smem + L::oV + off + 16 * L::VROW);
-        vf[nt][jb] = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
-      }
+    buf_st128(rO, (int)((orow * rowV + ocol) * 2), u32x4_t{w[0], w[1], w[2], w[3]});
+  };
 
-    f32x4_t o[4][2];
-    if constexpr (OUT) {
-      // ---- this wave's key half: scores A_kh^T = kc qc^T (lower tiles) and o += qc S'
-      f32x4_t A[10];  // tile (it, jt), jt <= it, at index it*(it+1)/2 + jt
-#pragma unroll
-      for (int t = 0; t < 10; ++t) A[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) o[it][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int col = 64 * (NKB * kh + kb);
-        u32x4_t qh[4], ql[4], kh4[4], kl4[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int off = base_q + 16 * t * L::QROW + col;
-          qh[t] = lds_ld<u32x4_t>(smem + L::oQ, off);
-          ql[t] = lds_ld<u32x4_t>(smem + L::oQ + L::QPL, off);
-          kh4[t] = lds_ld<u32x4_t>(smem + L::oK, off);
-          kl4[t] = lds_ld<u32x4_t>(smem + L::oK + L::QPL, off);
-        }
-#pragma unroll
-        for (int it = 0; it < 4; ++it)
-#pragma unroll
-          for (int jt = 0; jt <= it; ++jt) {
-            f32x4_t &acc = A[it * (it + 1) / 2 + jt];
-            acc = mfma_bf(kl4[jt], qh[it], acc);
-            acc = mfma_bf(kh4[jt], ql[it], acc);
-            acc = mfma_bf(kh4[jt], qh[it], acc);
-          }
-        u32x4_t sh[2], sl[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const float s8[8] = {S[2 * kb][nt][0], S[2 * kb][nt][1], S[2 * kb][nt][2], S[2 * kb][nt][3],
-                               S[2 * kb + 1][nt][0], S[2 * kb + 1][nt][1], S[2 * kb + 1][nt][2], S[2 * kb + 1][nt][3]};
-          u32x2_t h0, l0, h1, l1;
-          split4(s8, h0, l0);
-          split4(s8 + 4, h1, l1);
-          sh[nt] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
-          sl[nt] = u32x4_t{l0[0], l0[1], l1[0], l1[1]};
-        }
-#pragma unroll
-        for (int it = 0; it < 4; ++it)
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            o[it][nt] = mfma_bf(ql[it], sh[nt], o[it][nt]);
-            o[it][nt] = mfma_bf(qh[it], sl[nt], o[it][nt]);
-            o[it][nt] = mfma_bf(qh[it], sh[nt], o[it][nt]);
-          }
-        // next chunk's gating, spread over the matrix work of this one
-        if (kb == 0) gate_a();
-        if (kb == NKB - 1) gate_b();
-        __builtin_amdgcn_sched_barrier(0);
-        if (kb == 0) {
-          load_part(c + 2, 0);
-          load_part(c + 2, 1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      // ---- o += A_kh v: causal mask, split, scores straight from the accumulators
-      // (lane: query i = 16it + l16, keys j = 16jt + 4lg + r)
-#pragma unroll
-      for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int jb = 0; jb <= it / 2; ++jb) {
-          float a8[8];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int jt = 2 * jb + hh;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              float x = 0.f;
-              if (jt < it) x = A[it * (it + 1) / 2 + jt][r];
-              else if (jt == it) x = (4 * lg + r <= l16) ? A[it * (it + 1) / 2 + jt][r] : 0.f;
-              a8[4 * hh + r] = x;
-            }
-          }
-          u32x2_t h0, l0, h1, l1;
-          split4(a8, h0, l0);
-          split4(a8 + 4, h1, l1);
-          const u32x4_t ah = {h0[0], h0[1], h1[0], h1[1]};
-          const u32x4_t al = {l0[0], l0[1], l1[0], l1[1]};
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            o[it][nt] = mfma_bf(al, vf[nt][jb], o[it][nt]);
-            o[it][nt] = mfma_bf(ah, vf[nt][jb], o[it][nt]);
-          }
-        }
-      gate_rows(0, RPG / 2);
-      __builtin_amdgcn_sched_barrier(0);
-    } else {
-      gate_a();
-      gate_b();
-      __builtin_amdgcn_sched_barrier(0);
-      load_part(c + 2, 0);
-      load_part(c + 2, 1);
-      __builtin_amdgcn_sched_barrier(0);
+  // Producer and matrix waves run separate loops (different register sets);
+  // both meet the same barriers per chunk: operands written | scores written
+  // (OUT) | chunk done.
+  if (producer) {
+    if (c_begin < c_end) {  // pipeline fill
+      load_chunk(c_begin);
+      gate_decays();
+      gate_rows();
+      load_chunk(c_begin + 1);
     }
-
-    // ---- S = S' + kc^T v   (kc^T rows via transpose reads of the token-major kc)
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        const int off = base_kt + 32 * jb * L::QROW + (32 * (kt >> 1) + 4 * (kt & 1)) * 2;
-        const u32x2_t h0 = lds_tr16(smem + L::oK + off);
-        const u32x2_t h1 = lds_tr16(smem + L::oK + off + 16 * L::QROW);
-        const u32x2_t g0 = lds_tr16(smem + L::oK + L::QPL + off);
-        const u32x2_t g1 = lds_tr16(smem + L::oK + L::QPL + off + 16 * L::QROW);
-        const u32x4_t ah = {h0[0], h0[1], h1[0], h1[1]};
-        const u32x4_t al = {g0[0], g0[1], g1[0], g1[1]};
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          S[kt][nt] = mfma_bf(al, vf[nt][jb], S[kt][nt]);
-          S[kt][nt] = mfma_bf(ah, vf[nt][jb], S[kt][nt]);
-        }
-      }
+    for (int c = c_begin; c < c_end; ++c) {
+      write_gated();
+      __syncthreads();  // operands of chunk c visible
+      gate_decays();    // chunk c+1
+      if constexpr (OUT) __syncthreads();  // scores visible
+      gate_rows();      // chunk c+1
+      load_chunk(c + 2);
+      __syncthreads();  // chunk c done
+      if constexpr (OUT) store_out(c);
     }
-    gate_rows(OUT ? RPG / 2 : 0, RPG);
-    gV[0] = rgV[0];
-    gV[1] = rgV[1];
-    __builtin_amdgcn_sched_barrier(0);
-    load_part(c + 2, 2);
-    load_part(c + 2, 3);
-    __builtin_amdgcn_sched_barrier(0);
-
-    if constexpr (OUT) {
-      // ---- partial o -> LDS [kh][i][n] (fp32)
+  } else {
+    for (int c = c_begin; c < c_end; ++c) {
+      __syncthreads();  // operands of chunk c visible
+      if constexpr (OUT) {
+        switch (mw) {
+          case 0: scores<KD, 0>(smem, l16, lg); break;
+          case 1: scores<KD, 1>(smem, l16, lg); break;
+          case 2: scores<KD, 2>(smem, l16, lg); break;
+          default: scores<KD, 3>(smem, l16, lg); break;
+        }
+        __syncthreads();  // scores visible
+      }
+      // ---- S' = diag(a) S
 #pragma unroll
-      for (int it = 0; it < 4; ++it)
+      for (int kt = 0; kt < NKT; ++kt) {
+        const f32x4_t a4 = lds_ld<f32x4_t>(smem + L::oDec, base_d + 64 * kt);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            lds_st<float>(smem + L::oO, base_o + (16 * it + r) * L::OROW + 64 * nt, o[it][nt][r]);
-    }
-    __syncthreads();  // partial outputs visible; every read of chunk c's operands is done
-
-    if constexpr (OUT) {
-      // ---- sum the two key-half partials, round to bf16, store 32 B per thread
-      const int64_t t0 = (int64_t)si.bos + (int64_t)c * C;
-      const int64_t valid = min(C, si.len - c * C);
-      const int64_t headV = (int64_t)h * V + v0;
-      const __amdgpu_buffer_rsrc_t rO = make_rsrc((uint16_t *)p.o + t0 * rowV + headV, (valid * rowV - headV) * 2);
-      const int orow = tid >> 2, ocol = 16 * (tid & 3);
-      uint32_t w[8];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const f32x4_t a0 = lds_ld<f32x4_t>(smem + L::oO, orow * L::OROW + (ocol + 4 * x) * 4);
-        const f32x4_t a1 = lds_ld<f32x4_t>(smem + L::oO + L::OPL, orow * L::OROW + (ocol + 4 * x) * 4);
-        w[2 * x] = pack_bf16(a0[0] + a1[0], a0[1] + a1[1]);
-        w[2 * x + 1] = pack_bf16(a0[2] + a1[2], a0[3] + a1[3]);
+          for (int r = 0; r < 4; ++r) S[kt][nt][r] *= a4[r];
       }
-      const int so = (int)((orow * rowV + ocol) * 2);
-      buf_st128(rO, so, u32x4_t{w[0], w[1], w[2], w[3]});
-      buf_st128(rO, so + 16, u32x4_t{w[4], w[5], w[6], w[7]});
+      // ---- v fragments: v[32jb + 8lg + e][32nh + 16nt + l16]
+      u32x4_t vf[2][2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          const int off = base_vt + 32 * jb * L::VROW + 32 * nt;
+          const u32x2_t x0 = lds_tr16(smem + L::oV + off);
+          const u32x2_t x1 = lds_tr16(smem + L::oV + off + 4 * L::VROW);
+          vf[nt][jb] = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
+        }
+      if constexpr (OUT) {
+        f32x4_t o[4][2];
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) o[it][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // ---- o += A v over token block jb = kh of every row tile (key half 0 takes
+        // tokens 0..31, key half 1 tokens 32..63; blocks above the diagonal are zero)
+        u32x4_t vs[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int off = base_vt + 32 * kh * L::VROW + 32 * nt;
+          const u32x2_t x0 = lds_tr16(smem + L::oV + off);
+          const u32x2_t x1 = lds_tr16(smem + L::oV + off + 4 * L::VROW);
+          vs[nt] = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int off = base_a + 16 * it * L::AROW + 64 * kh;
+          const u32x4_t ah = lds_ld<u32x4_t>(smem + L::oA, off);
+          const u32x4_t al = lds_ld<u32x4_t>(smem + L::oA + L::APL, off);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            o[it][nt] = mfma_bf(al, vs[nt], o[it][nt]);
+            o[it][nt] = mfma_bf(ah, vs[nt], o[it][nt]);
+          }
+        }
+        // ---- o += qc S' over this wave's key half (S' from the accumulators)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          u32x4_t sh[2], sl[2];
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const float s8[8] = {S[2 * kb][nt][0], S[2 * kb][nt][1], S[2 * kb][nt][2], S[2 * kb][nt][3],
+                                 S[2 * kb + 1][nt][0], S[2 * kb + 1][nt][1], S[2 * kb + 1][nt][2], S[2 * kb + 1][nt][3]};
+            u32x2_t h0, l0, h1, l1;
+            split4(s8, h0, l0);
+            split4(s8 + 4, h1, l1);
+            sh[nt] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
+            sl[nt] = u32x4_t{l0[0], l0[1], l1[0], l1[1]};
+          }
+#pragma unroll
+          for (int it = 0; it < 4; ++it) {
+            const int off = base_q + 16 * it * L::QROW + 64 * (NKB * kh + kb);
+            const u32x4_t qh = lds_ld<u32x4_t>(smem + L::oQ, off);
+            const u32x4_t ql = lds_ld<u32x4_t>(smem + L::oQ + L::QPL, off);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+              o[it][nt] = mfma_bf(ql, sh[nt], o[it][nt]);
+              o[it][nt] = mfma_bf(qh, sl[nt], o[it][nt]);
+              o[it][nt] = mfma_bf(qh, sh[nt], o[it][nt]);
+            }
+          }
+        }
+        // ---- partial o -> LDS [kh][i][n] (fp32)
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              lds_st<float>(smem + L::oO, base_o + (16 * it + r) * L::OROW + 64 * nt, o[it][nt][r]);
+      }
+      // ---- S = S' + kc^T v   (kc^T rows via transpose reads of the token-major kc)
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          const int off = base_kt + 32 * jb * L::QROW + (32 * (kt >> 1) + 4 * (kt & 1)) * 2;
+          const u32x2_t h0 = lds_tr16(smem + L::oK + off);
+          const u32x2_t h1 = lds_tr16(smem + L::oK + off + 4 * L::QROW);
+          const u32x2_t g0 = lds_tr16(smem + L::oK + L::QPL + off);
+          const u32x2_t g1 = lds_tr16(smem + L::oK + L::QPL + off + 4 * L::QROW);
+          const u32x4_t ah = {h0[0], h0[1], h1[0], h1[1]};
+          const u32x4_t al = {g0[0], g0[1], g1[0], g1[1]};
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            S[kt][nt] = mfma_bf(al, vf[nt][jb], S[kt][nt]);
+            S[kt][nt] = mfma_bf(ah, vf[nt][jb], S[kt][nt]);
+          }
+        }
+      }
+      __syncthreads();  // partial outputs visible; chunk c's operands are no longer read
+      if constexpr (OUT) store_out(c);
     }
   }
 
   // ================= results of the segment
-  float *dst = nullptr;
-  if (OUT) {
-    if (p.ht != nullptr && si.s == si.nseg - 1) dst = p.ht + ((int64_t)si.n * H + h) * KD * V;
-  } else {
+  if (!producer) {
+    float *dst = nullptr;
+    if (OUT) {
+      if (p.ht != nullptr && si.s == si.nseg - 1) dst = p.ht + ((int64_t)si.n * H + h) * KD * V;
+    } else {
+      dst = p.seg_state + ((int64_t)(si.first + si.s) * H + h) * KD * V;
+    }
+    if (dst) {
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            dst[(int64_t)(KH * kh + 16 * kt + 4 * lg + r) * V + v0 + 32 * nh + 16 * nt + l16] = S[kt][nt][r];
+    }
+  } else if (!OUT && vt == 0 && rg == 0) {
     const int slot = si.first + si.s;
-    dst = p.seg_state + ((int64_t)slot * H + h) * KD * V;
-    if (vt == 0 && rg == 0)
-      *reinterpret_cast<f32x4_t *>(p.seg_decay + ((int64_t)slot * H + h) * KD + 4 * cq) =
-          f32x4_t{seg_decay[0], seg_decay[1], seg_decay[2], seg_decay[3]};
-  }
-  if (dst) {
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          dst[(int64_t)(KH * kh + 16 * kt + 4 * lg + r) * V + v0 + 32 * nh + 16 * nt + l16] = S[kt][nt][r];
+    *reinterpret_cast<f32x4_t *>(p.seg_decay + ((int64_t)slot * H + h) * KD + 4 * cq) =
+        f32x4_t{seg_decay[0], seg_decay[1], seg_decay[2], seg_decay[3]};
   }
 }
 
 template <int KD>
-__global__ __launch_bounds__(kThreads, 1) void gla_chunk_output_bf16(WalkParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[LdsB<KD, true>::BYTES];
+__global__ __launch_bounds__(kWsThreads, 1) void gla_chunk_output_bf16(WalkParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[LdsW<KD, true>::BYTES];
   walk_bf16<true, KD>(p, smem);
 }
 
 template <int KD>
-__global__ __launch_bounds__(kThreads, 1) void gla_chunk_local_bf16(WalkParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[LdsB<KD, false>::BYTES];
+__global__ __launch_bounds__(kWsThreads, 1) void gla_chunk_local_bf16(WalkParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[LdsW<KD, false>::BYTES];
   walk_bf16<false, KD>(p, smem);
 }
 
@@ -491,9 +497,9 @@ hipError_t launch_t(bool local_mode, const WalkParams &p, hipStream_t s) {
   const int groups = (p.units + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * NV));
   if (local_mode)
-    hipLaunchKernelGGL(gla_chunk_local_bf16<KD>, grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(gla_chunk_local_bf16<KD>, grid, dim3(kWsThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(gla_chunk_output_bf16<KD>, grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(gla_chunk_output_bf16<KD>, grid, dim3(kWsThreads), 0, s, p);
   return hipGetLastError();
 }
 
