@@ -37,6 +37,15 @@ using namespace dev;
 
 constexpr int kWsThreads = 512;  // 4 matrix waves + 4 producer waves
 
+// Workgroup barrier that is also a hard scheduling boundary: the compiler may
+// otherwise move pure vector arithmetic (and lane shuffles) across s_barrier,
+// which shifts work from one pipeline phase into another.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int KD, bool OUT>
 struct LdsW {
   static constexpr int NQ = KD / 4;                // producer column quads
@@ -51,8 +60,9 @@ struct LdsW {
   static constexpr int OPL = C * OROW;
   static constexpr int oQ = 0;                            // qc hi, lo              (OUT)
   static constexpr int oK = oQ + (OUT ? 2 * QPL : 0);     // kc hi, lo
-  static constexpr int oV = oK + 2 * QPL;                 // v [token][n]
-  static constexpr int oA = oV + C * VROW;                // A hi, lo [i][j]        (OUT)
+  static constexpr int VPL = C * VROW;
+  static constexpr int oV = oK + 2 * QPL;                 // v [token][n], two chunks
+  static constexpr int oA = oV + 2 * VPL;                 // A hi, lo [i][j]        (OUT)
   static constexpr int oO = oA + (OUT ? 2 * APL : 0);     // partial o [kh][i][n]   (OUT)
   static constexpr int oDec = oO + (OUT ? 2 * OPL : 0);   // a [K]
   static constexpr int BYTES = oDec + 4 * KD;
@@ -185,31 +195,36 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   u32x2_t rgQ[RPG], rgK[RPG];
   u32x4_t rgV[2];
   u32x2_t gQh[RPG], gQl[RPG], gKh[RPG], gKl[RPG];
-  u32x4_t gV[2];
   f32x4_t gDec = {1.f, 1.f, 1.f, 1.f};
   float gPl[RPG][4], gRl[RPG][4], gSuf[4], gFq[4];
   float seg_decay[4] = {1.f, 1.f, 1.f, 1.f};
   const float scale = p.scale;
 
-  auto load_chunk = [&](int c) {
+  // Raw loads of chunk c (rows past the sequence end, and chunks past the
+  // segment, read as zero).
+  struct Rsrc { __amdgpu_buffer_rsrc_t g, q, k, v; };
+  auto rsrc = [&](int c) {
     const int64_t t0 = (int64_t)seq_bos + (int64_t)c * C;
     const int64_t valid = c < c_end ? min(C, seq_len - c * C) : 0;
     const int64_t headK = (int64_t)h * KD, headV = (int64_t)h * V + v0;
-    const __amdgpu_buffer_rsrc_t rG = make_rsrc(p.g + t0 * rowK + headK, (valid * rowK - headK) * 4);
-    const __amdgpu_buffer_rsrc_t rK = make_rsrc((const uint16_t *)p.k + t0 * rowK + headK, (valid * rowK - headK) * 2);
-    const __amdgpu_buffer_rsrc_t rV = make_rsrc((const uint16_t *)p.v + t0 * rowV + headV, (valid * rowV - headV) * 2);
+    Rsrc r;
+    r.g = make_rsrc(p.g + t0 * rowK + headK, (valid * rowK - headK) * 4);
+    r.q = make_rsrc((const uint16_t *)p.q + t0 * rowK + headK, OUT ? (valid * rowK - headK) * 2 : 0);
+    r.k = make_rsrc((const uint16_t *)p.k + t0 * rowK + headK, (valid * rowK - headK) * 2);
+    r.v = make_rsrc((const uint16_t *)p.v + t0 * rowV + headV, (valid * rowV - headV) * 2);
+    return r;
+  };
+  auto load_g = [&](const Rsrc &r) {
 #pragma unroll
-    for (int r = 0; r < RPG; ++r) {
-      rgG[r] = buf_ld128(rG, voff_g + r * step_g);
-      rgK[r] = buf_ld64(rK, voff_k + r * step_k);
-    }
-    if (OUT) {
-      const __amdgpu_buffer_rsrc_t rQ = make_rsrc((const uint16_t *)p.q + t0 * rowK + headK, (valid * rowK - headK) * 2);
-#pragma unroll
-      for (int r = 0; r < RPG; ++r) rgQ[r] = buf_ld64(rQ, voff_k + r * step_k);
-    }
-    rgV[0] = buf_ld128(rV, voff_v);
-    rgV[1] = buf_ld128(rV, voff_v + 16);
+    for (int i = 0; i < RPG; ++i) rgG[i] = buf_ld128(r.g, voff_g + i * step_g);
+  };
+  auto load_v = [&](const Rsrc &r) {
+    rgV[0] = buf_ld128(r.v, voff_v);
+    rgV[1] = buf_ld128(r.v, voff_v + 16);
+  };
+  auto load_qk_row = [&](const Rsrc &r, int i) {
+    rgK[i] = buf_ld64(r.k, voff_k + i * step_k);
+    if (OUT) rgQ[i] = buf_ld64(r.q, voff_k + i * step_k);
   };
   // gate, stage 1: exp(g), running products inside the row group and across row
   // groups (lane shuffles inside the wave), chunk decay and the q / k factors
@@ -256,29 +271,31 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       for (int j = 0; j < 4; ++j) seg_decay[j] *= gDec[j];
     }
   };
-  // gate, stage 2: gated and split q, k rows
-  auto gate_rows = [&]() {
+  // gate, stage 2: gated and split q, k of row i; the raw registers of the row are
+  // then free for the next load
+  auto gate_row = [&](int r) {
+    float kc[4];
 #pragma unroll
-    for (int r = 0; r < RPG; ++r) {
-      float kc[4];
+    for (int j = 0; j < 4; ++j) {
+      const float kk = (j & 1) ? bf_hi(rgK[r][j >> 1]) : bf_lo(rgK[r][j >> 1]);
+      kc[j] = kk * (gRl[r][j] * gSuf[j]);
+    }
+    split4(kc, gKh[r], gKl[r]);
+    if (OUT) {
+      float qc[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float kk = (j & 1) ? bf_hi(rgK[r][j >> 1]) : bf_lo(rgK[r][j >> 1]);
-        kc[j] = kk * (gRl[r][j] * gSuf[j]);
+        const float qq = (j & 1) ? bf_hi(rgQ[r][j >> 1]) : bf_lo(rgQ[r][j >> 1]);
+        qc[j] = qq * (gPl[r][j] * gFq[j]);
       }
-      split4(kc, gKh[r], gKl[r]);
-      if (OUT) {
-        float qc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float qq = (j & 1) ? bf_hi(rgQ[r][j >> 1]) : bf_lo(rgQ[r][j >> 1]);
-          qc[j] = qq * (gPl[r][j] * gFq[j]);
-        }
-        split4(qc, gQh[r], gQl[r]);
-      }
+      split4(qc, gQh[r], gQl[r]);
     }
-    gV[0] = rgV[0];
-    gV[1] = rgV[1];
+  };
+  // v goes to LDS straight from the load registers (two chunk buffers)
+  auto write_v = [&](int c) {
+    char *sv = smem + L::oV + (c & 1) * L::VPL;
+    lds_st<u32x4_t>(sv, vrow * L::VROW + vcol * 2, rgV[0]);
+    lds_st<u32x4_t>(sv, vrow * L::VROW + vcol * 2 + 16, rgV[1]);
   };
   auto write_gated = [&]() {
 #pragma unroll
@@ -291,54 +308,72 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
         lds_st<u32x2_t>(smem + L::oQ + L::QPL, off, gQl[r]);
       }
     }
-    lds_st<u32x4_t>(smem + L::oV, vrow * L::VROW + vcol * 2, gV[0]);
-    lds_st<u32x4_t>(smem + L::oV, vrow * L::VROW + vcol * 2 + 16, gV[1]);
     if (rg == 0) lds_st<f32x4_t>(smem + L::oDec, 16 * cq, gDec);
   };
 
-  // Output pass after the third barrier of chunk c: all 512 threads sum the two
-  // key-half partials, round to bf16 and store 16 B each.
+  // Output pass of the matrix waves after the third barrier of chunk c: sum the
+  // two key-half partials, round to bf16, two 16 B stores per thread.
   auto store_out = [&](int c) {
-    // ---- sum the two key-half partials, round to bf16, 16 B per thread
     const int64_t t0 = (int64_t)seq_bos + (int64_t)c * C;
     const int64_t valid = min(C, seq_len - c * C);
     const int64_t headV = (int64_t)h * V + v0;
     const __amdgpu_buffer_rsrc_t rO = make_rsrc((uint16_t *)p.o + t0 * rowV + headV, (valid * rowV - headV) * 2);
-    const int orow = tid >> 3, ocol = 8 * (tid & 7);
-    uint32_t w[4];
+    const int orow = tid >> 2, ocol = 16 * (tid & 3);
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const f32x4_t a0 = lds_ld<f32x4_t>(smem + L::oO, orow * L::OROW + (ocol + 4 * x) * 4);
-      const f32x4_t a1 = lds_ld<f32x4_t>(smem + L::oO + L::OPL, orow * L::OROW + (ocol + 4 * x) * 4);
-      w[2 * x] = pack_bf16(a0[0] + a1[0], a0[1] + a1[1]);
-      w[2 * x + 1] = pack_bf16(a0[2] + a1[2], a0[3] + a1[3]);
+    for (int y = 0; y < 2; ++y) {
+      uint32_t w[4];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int off = orow * L::OROW + (ocol + 8 * y + 4 * x) * 4;
+        const f32x4_t a0 = lds_ld<f32x4_t>(smem + L::oO, off);
+        const f32x4_t a1 = lds_ld<f32x4_t>(smem + L::oO + L::OPL, off);
+        w[2 * x] = pack_bf16(a0[0] + a1[0], a0[1] + a1[1]);
+        w[2 * x + 1] = pack_bf16(a0[2] + a1[2], a0[3] + a1[3]);
+      }
+      buf_st128(rO, (int)((orow * rowV + ocol + 8 * y) * 2), u32x4_t{w[0], w[1], w[2], w[3]});
     }
-    buf_st128(rO, (int)((orow * rowV + ocol) * 2), u32x4_t{w[0], w[1], w[2], w[3]});
   };
 
   // Producer and matrix waves run separate loops (different register sets);
   // both meet the same barriers per chunk: operands written | scores written
   // (OUT) | chunk done.
   if (producer) {
-    if (c_begin < c_end) {  // pipeline fill
-      load_chunk(c_begin);
+    if (c_begin < c_end) {  // pipeline fill: chunk c_begin gated, chunk c_begin+1 loading
+      const Rsrc r0 = rsrc(c_begin);
+      load_g(r0);
+      load_v(r0);
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) load_qk_row(r0, i);
       gate_decays();
-      gate_rows();
-      load_chunk(c_begin + 1);
+      write_v(c_begin);
+      const Rsrc r1 = rsrc(c_begin + 1);
+      load_g(r1);
+      load_v(r1);
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        gate_row(i);
+        load_qk_row(r1, i);
+      }
     }
     for (int c = c_begin; c < c_end; ++c) {
-      write_gated();
-      __syncthreads();  // operands of chunk c visible
+      write_gated();    // chunk c
+      phase_barrier();  // operands of chunk c visible
+      const Rsrc r2 = rsrc(c + 2);
       gate_decays();    // chunk c+1
-      if constexpr (OUT) __syncthreads();  // scores visible
-      gate_rows();      // chunk c+1
-      load_chunk(c + 2);
-      __syncthreads();  // chunk c done
-      if constexpr (OUT) store_out(c);
+      load_g(r2);
+      if constexpr (OUT) phase_barrier();  // scores visible
+      write_v(c + 1);
+      load_v(r2);
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        gate_row(i);    // chunk c+1
+        load_qk_row(r2, i);
+      }
+      phase_barrier();  // chunk c done
     }
   } else {
     for (int c = c_begin; c < c_end; ++c) {
-      __syncthreads();  // operands of chunk c visible
+      phase_barrier();  // operands of chunk c visible
       if constexpr (OUT) {
         switch (mw) {
           case 0: scores<KD, 0>(smem, l16, lg); break;
@@ -346,8 +381,9 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
           case 2: scores<KD, 2>(smem, l16, lg); break;
           default: scores<KD, 3>(smem, l16, lg); break;
         }
-        __syncthreads();  // scores visible
+        phase_barrier();  // scores visible
       }
+      const char *sv = smem + L::oV + (c & 1) * L::VPL;  // v of chunk c
       // ---- S' = diag(a) S
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
@@ -364,8 +400,8 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
           const int off = base_vt + 32 * jb * L::VROW + 32 * nt;
-          const u32x2_t x0 = lds_tr16(smem + L::oV + off);
-          const u32x2_t x1 = lds_tr16(smem + L::oV + off + 4 * L::VROW);
+          const u32x2_t x0 = lds_tr16(sv + off);
+          const u32x2_t x1 = lds_tr16(sv + off + 4 * L::VROW);
           vf[nt][jb] = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
         }
       if constexpr (OUT) {
@@ -380,8 +416,8 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           const int off = base_vt + 32 * kh * L::VROW + 32 * nt;
-          const u32x2_t x0 = lds_tr16(smem + L::oV + off);
-          const u32x2_t x1 = lds_tr16(smem + L::oV + off + 4 * L::VROW);
+          const u32x2_t x0 = lds_tr16(sv + off);
+          const u32x2_t x1 = lds_tr16(sv + off + 4 * L::VROW);
           vs[nt] = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
         }
 #pragma unroll
@@ -450,7 +486,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
           }
         }
       }
-      __syncthreads();  // partial outputs visible; chunk c's operands are no longer read
+      phase_barrier();  // partial outputs visible; chunk c's operands are no longer read
       if constexpr (OUT) store_out(c);
     }
   }
