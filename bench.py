@@ -5,8 +5,10 @@ Default workload: B=8, H=16, T=2048, K=V=128, bf16 q/k/v, fp32 gates, chunk 64,
 final state stored (synthetic seeded inputs, recipe in gla_inputs.py).
 
 A step is one full forward (every kernel of the path) over the whole batch,
-with inputs resident in device memory.  W untimed warmup steps, then exactly K
-timed steps between two device synchronisations; one JSON line is printed.
+with inputs resident in device memory.  Untimed steps for --settle-ms (the GPU
+clock ramps up over the first tens of milliseconds of load), W untimed warmup
+steps, then exactly K timed steps between two device synchronisations; one JSON
+line is printed.
 
 Also reported:
   roofline      the dominant kernel's algorithmic bytes per launch divided by its
@@ -28,20 +30,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-import numpy as np  # noqa: E402
 
 import gla_inputs as gi  # noqa: E402
 
 METRIC = "GLA chunked fwd tokens/s + TFLOP/s, fraction of MFMA/HBM roofline (1 GPU)"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
-KERNEL_SRC = os.path.join(ROOT, "chunkwise_gated_linear_amd", "csrc", "gla_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "chunkwise_gated_linear_amd", "csrc", f)
+               for f in ("gla_kernels.hip", "gla_walk_bf16.hip", "gla_device.h", "gla_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of every device source: counters measured on other kernel code are not reused."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def algorithmic(w, n_tokens, n_seqs):
@@ -77,8 +83,11 @@ def load_traffic(workload: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="before the W warmup steps, run untimed steps for this long so the GPU "
+                         "reaches its sustained clock (short runs otherwise measure the ramp)")
     ap.add_argument("--workload", default="c2048", choices=sorted(gi.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--segment-chunks", type=int, default=0)
@@ -128,23 +137,29 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
 
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            call(sptr)
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         call(sptr)
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # One event pair on the launch stream brackets the K back-to-back steps; the
+    # average launch duration is their span / K (per-step event records would
+    # add their own gaps between launches).
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
+    ev0.record(stream)
+    for _ in range(args.steps):
         call(sptr)
-        ev[i][1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    ev_ms = [a.elapsed_time(b) for a, b in ev]
-    launch_ms = float(np.mean(ev_ms))
+    launch_ms = ev0.elapsed_time(ev1) / args.steps
 
     nbytes, flops = algorithmic(w, n_tokens, n_seqs)
     tokens_per_s = n_tokens / (ms_per_step * 1e-3)

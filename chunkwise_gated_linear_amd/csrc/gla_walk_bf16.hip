@@ -51,10 +51,10 @@ struct LdsW {
   static constexpr int NQ = KD / 4;                // producer column quads
   static constexpr int QPW = NQ / 4;               // column quads per producer wave
   static constexpr int NG = 64 / QPW;              // producer row groups
-  static constexpr int QROW = 2 * KD + 16;         // qc / kc rows (bf16)
-  static constexpr int VROW = 2 * VT + 32;         // v rows (bf16): the 4 rows x 32 B of one transpose read fall in distinct banks
-  static constexpr int AROW = 2 * C + 16;          // score rows (bf16)
-  static constexpr int OROW = 4 * VT + 16;         // partial outputs (fp32)
+  static constexpr int QROW = 2 * KD;              // qc / kc rows (bf16, swizzled)
+  static constexpr int VROW = 2 * VT;              // v rows (bf16, swizzled)
+  static constexpr int AROW = 2 * C;               // score rows (bf16, swizzled)
+  static constexpr int OROW = 4 * VT + 16;         // partial outputs (fp32, padded)
   static constexpr int QPL = C * QROW;             // one plane of qc or kc
   static constexpr int APL = C * AROW;
   static constexpr int OPL = C * OROW;
@@ -66,6 +66,33 @@ struct LdsW {
   static constexpr int oO = oA + (OUT ? 2 * APL : 0);     // partial o [kh][i][n]   (OUT)
   static constexpr int oDec = oO + (OUT ? 2 * OPL : 0);   // a [K]
   static constexpr int BYTES = oDec + 4 * KD;
+
+  // Swizzled byte offsets.  On gfx950 an LDS access is served 32 lanes at a
+  // time (16 for writes) without bank conflicts when the lanes' addresses,
+  // counted in units of the access width, are distinct modulo 32 (16 for
+  // writes).  Rows are unpadded; a unit index inside the row is XORed with row
+  // bits so that every access pattern of the walker meets that rule, except
+  // the kc^T transpose reads and the score writes, which stay at the minimum of
+  // two passes their shapes allow:
+  //   qc / kc: 16 B chunk ^ sqk(row) -- row fragments (16 rows x 2 chunks),
+  //            transpose reads (8 rows x 4 pieces), producer writes (2 rows x 64 B)
+  //   v:       32 B pair ^ (b1 | b3 << 1) -- transpose reads, 128 B row writes
+  //   A:       16 B chunk ^ (b0 | b2 << 1 | b3 << 2) -- row fragments, 8 B writes
+  static __device__ __forceinline__ int sqk(int row) {
+    const int b1 = (row >> 1) & 1, b2 = (row >> 2) & 1, b3 = (row >> 3) & 1;
+    return KD == 128 ? (b2 << 1) | ((b1 ^ b3) << 2) | (b3 << 3) : (b2 << 1) | (b3 << 2);
+  }
+  static __device__ __forceinline__ int qk(int row, int byte) {
+    return row * QROW + (((byte >> 4) ^ sqk(row)) << 4) + (byte & 15);
+  }
+  static __device__ __forceinline__ int vo(int row, int byte) {
+    const int s = ((row >> 1) & 1) | (((row >> 3) & 1) << 1);
+    return row * VROW + (((byte >> 5) ^ s) << 5) + (byte & 31);
+  }
+  static __device__ __forceinline__ int ao(int row, int byte) {
+    const int s = (row & 1) | (((row >> 2) & 1) << 1) | (((row >> 3) & 1) << 2);
+    return row * AROW + (((byte >> 4) ^ s) << 4) + (byte & 15);
+  }
 };
 
 // Score tiles (i-tile, j-tile) of the 64 x 64 lower triangle per matrix wave.
@@ -76,20 +103,21 @@ template <> struct Tiles<2> { static constexpr int n = 2; static constexpr int i
 template <> struct Tiles<3> { static constexpr int n = 2; static constexpr int it[2] = {3, 3}, jt[2] = {2, 3}; };
 
 // A^T tiles = kc qc^T for wave W's tiles, causal mask, split -> LDS A[i][j].
+// rf[kb]: this lane's offset of row l16, k columns 32 kb + 8 lg .. + 7, in a
+// qc / kc plane (the swizzle depends on the row within a 16-row tile only).
 template <int KD, int W>
-__device__ __forceinline__ void scores(char *smem, int l16, int lg) {
+__device__ __forceinline__ void scores(char *smem, const int (&rf)[KD / 32], int l16, int lg) {
   using L = LdsW<KD, true>;
   using T = Tiles<W>;
   f32x4_t acc[T::n];
 #pragma unroll
   for (int t = 0; t < T::n; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int lq = l16 * L::QROW + 16 * lg;
 #pragma unroll
   for (int kb = 0; kb < KD / 32; ++kb) {
 #pragma unroll
     for (int t = 0; t < T::n; ++t) {
-      const int oa = lq + 16 * T::jt[t] * L::QROW + 64 * kb;
-      const int ob = lq + 16 * T::it[t] * L::QROW + 64 * kb;
+      const int oa = rf[kb] + 16 * T::jt[t] * L::QROW;
+      const int ob = rf[kb] + 16 * T::it[t] * L::QROW;
       const u32x4_t ah = lds_ld<u32x4_t>(smem + L::oK, oa);
       const u32x4_t al = lds_ld<u32x4_t>(smem + L::oK + L::QPL, oa);
       const u32x4_t bh = lds_ld<u32x4_t>(smem + L::oQ, ob);
@@ -108,7 +136,7 @@ __device__ __forceinline__ void scores(char *smem, int l16, int lg) {
     for (int r = 0; r < 4; ++r) av[r] = (16 * T::jt[t] + 4 * lg + r <= i) ? acc[t][r] : 0.f;
     u32x2_t hi, lo;
     split4(av, hi, lo);
-    const int off = i * L::AROW + (16 * T::jt[t] + 4 * lg) * 2;
+    const int off = L::ao(i, (16 * T::jt[t] + 4 * lg) * 2);
     lds_st<u32x2_t>(smem + L::oA, off, hi);
     lds_st<u32x2_t>(smem + L::oA + L::APL, off, lo);
   }
@@ -174,10 +202,23 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
     for (int i = tid; i < 2 * L::APL / 16; i += kWsThreads)
       lds_st<u32x4_t>(smem + L::oA, 16 * i, u32x4_t{0, 0, 0, 0});
   }
-  const int base_q = l16 * L::QROW + 16 * lg;                                          // rows of qc
-  const int base_a = l16 * L::AROW + 16 * lg;                                          // rows of A
-  const int base_vt = (8 * lg + (l16 >> 2)) * L::VROW + (32 * nh + 4 * (l16 & 3)) * 2;  // v, transposed
-  const int base_kt = (8 * lg + (l16 >> 2)) * L::QROW + (KH * kh + 8 * (l16 & 3)) * 2;  // kc, transposed
+  // Per-lane LDS offsets; the compile-time parts (row tiles, token blocks, the
+  // 8 B half of a chunk) are added at the access and do not change the swizzle.
+  int rf[KD / 32], rq[NKB];  // row fragments: all k blocks (scores), this wave's key half (qc S')
+#pragma unroll
+  for (int kb = 0; kb < KD / 32; ++kb) rf[kb] = L::qk(l16, 16 * (4 * kb + lg));
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) rq[kb] = L::qk(l16, 16 * (4 * (NKB * kh + kb) + lg));
+  const int base_a = L::ao(l16, 16 * (4 * kh + lg));  // A rows l16, tokens 32 kh + 8 lg ..
+  const int trow = 8 * lg + (l16 >> 2);               // token row of the transpose reads
+  int voff[2];                                        // v, transposed: columns 32 nh + 16 nt + 4 (l16 & 3)
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) voff[nt] = L::vo(trow, 64 * nh + 32 * nt + 8 * (l16 & 3));
+  int koff[NKT / 2][2];  // kc, transposed: key columns KH kh + 32 m + 8 (l16 & 3), token rows + 4 e
+#pragma unroll
+  for (int m = 0; m < NKT / 2; ++m)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) koff[m][e] = L::qk(trow + 4 * e, 2 * (KH * kh + 8 * (l16 & 3)) + 64 * m);
   const int base_o = 4 * lg * L::OROW + (32 * nh + l16) * 4 + kh * L::OPL;             // partial o
   const int base_d = (KH * kh + 4 * lg) * 4;                                           // decay
 
@@ -187,8 +228,10 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   const int cq = (wave & 3) * QPW + lane % QPW, rg = lane / QPW;
   const int voff_g = (int)((rg * RPG * rowK + 4 * cq) * 4);
   const int voff_k = (int)((rg * RPG * rowK + 4 * cq) * 2);
-  const int vrow = (pt & 255) >> 2, vcol = 16 * (pt & 3);
-  const int voff_v = (int)((vrow * rowV + vcol) * 2);
+  // v: 16 B chunk (pt & 7) of token rows pt / 8 and pt / 8 + 32 (8 lanes per 128 B row)
+  const int vrow = (pt & 255) >> 3, vch = pt & 7;
+  const int voff_v = (int)((vrow * rowV + 8 * vch) * 2);
+  const int vstep = (int)(32 * rowV * 2);
   const int step_g = (int)(rowK * 4), step_k = (int)(rowK * 2);
   const int colq = kperm_bf(4 * cq) * 2;
   u32x4_t rgG[RPG];
@@ -220,7 +263,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   };
   auto load_v = [&](const Rsrc &r) {
     rgV[0] = buf_ld128(r.v, voff_v);
-    rgV[1] = buf_ld128(r.v, voff_v + 16);
+    rgV[1] = buf_ld128(r.v, voff_v + vstep);
   };
   auto load_qk_row = [&](const Rsrc &r, int i) {
     rgK[i] = buf_ld64(r.k, voff_k + i * step_k);
@@ -294,21 +337,25 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   // v goes to LDS straight from the load registers (two chunk buffers)
   auto write_v = [&](int c) {
     char *sv = smem + L::oV + (c & 1) * L::VPL;
-    lds_st<u32x4_t>(sv, vrow * L::VROW + vcol * 2, rgV[0]);
-    lds_st<u32x4_t>(sv, vrow * L::VROW + vcol * 2 + 16, rgV[1]);
+    lds_st<u32x4_t>(sv, L::vo(vrow, 16 * vch), rgV[0]);
+    lds_st<u32x4_t>(sv, L::vo(vrow + 32, 16 * vch), rgV[1]);
   };
-  auto write_gated = [&]() {
+  auto write_k = [&]() {  // kc and the chunk decay
 #pragma unroll
     for (int r = 0; r < RPG; ++r) {
-      const int off = (rg * RPG + r) * L::QROW + colq;
+      const int off = L::qk(rg * RPG + r, colq);
       lds_st<u32x2_t>(smem + L::oK, off, gKh[r]);
       lds_st<u32x2_t>(smem + L::oK + L::QPL, off, gKl[r]);
-      if (OUT) {
-        lds_st<u32x2_t>(smem + L::oQ, off, gQh[r]);
-        lds_st<u32x2_t>(smem + L::oQ + L::QPL, off, gQl[r]);
-      }
     }
     if (rg == 0) lds_st<f32x4_t>(smem + L::oDec, 16 * cq, gDec);
+  };
+  auto write_q = [&]() {
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+      const int off = L::qk(rg * RPG + r, colq);
+      lds_st<u32x2_t>(smem + L::oQ, off, gQh[r]);
+      lds_st<u32x2_t>(smem + L::oQ + L::QPL, off, gQl[r]);
+    }
   };
 
   // Output pass of the matrix waves after the third barrier of chunk c: sum the
@@ -356,7 +403,8 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       }
     }
     for (int c = c_begin; c < c_end; ++c) {
-      write_gated();    // chunk c
+      write_k();        // chunk c
+      if constexpr (OUT) write_q();
       phase_barrier();  // operands of chunk c visible
       const Rsrc r2 = rsrc(c + 2);
       gate_decays();    // chunk c+1
@@ -376,10 +424,10 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       phase_barrier();  // operands of chunk c visible
       if constexpr (OUT) {
         switch (mw) {
-          case 0: scores<KD, 0>(smem, l16, lg); break;
-          case 1: scores<KD, 1>(smem, l16, lg); break;
-          case 2: scores<KD, 2>(smem, l16, lg); break;
-          default: scores<KD, 3>(smem, l16, lg); break;
+          case 0: scores<KD, 0>(smem, rf, l16, lg); break;
+          case 1: scores<KD, 1>(smem, rf, l16, lg); break;
+          case 2: scores<KD, 2>(smem, rf, l16, lg); break;
+          default: scores<KD, 3>(smem, rf, l16, lg); break;
         }
         phase_barrier();  // scores visible
       }
@@ -399,7 +447,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-          const int off = base_vt + 32 * jb * L::VROW + 32 * nt;
+          const int off = voff[nt] + 32 * jb * L::VROW;
           const u32x2_t x0 = lds_tr16(sv + off);
           const u32x2_t x1 = lds_tr16(sv + off + 4 * L::VROW);
           vf[nt][jb] = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
@@ -415,14 +463,14 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
         u32x4_t vs[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          const int off = base_vt + 32 * kh * L::VROW + 32 * nt;
+          const int off = voff[nt] + 32 * kh * L::VROW;
           const u32x2_t x0 = lds_tr16(sv + off);
           const u32x2_t x1 = lds_tr16(sv + off + 4 * L::VROW);
           vs[nt] = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
         }
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-          const int off = base_a + 16 * it * L::AROW + 64 * kh;
+          const int off = base_a + 16 * it * L::AROW;
           const u32x4_t ah = lds_ld<u32x4_t>(smem + L::oA, off);
           const u32x4_t al = lds_ld<u32x4_t>(smem + L::oA + L::APL, off);
 #pragma unroll
@@ -447,7 +495,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
           }
 #pragma unroll
           for (int it = 0; it < 4; ++it) {
-            const int off = base_q + 16 * it * L::QROW + 64 * (NKB * kh + kb);
+            const int off = rq[kb] + 16 * it * L::QROW;
             const u32x4_t qh = lds_ld<u32x4_t>(smem + L::oQ, off);
             const u32x4_t ql = lds_ld<u32x4_t>(smem + L::oQ + L::QPL, off);
 #pragma unroll
@@ -472,11 +520,12 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-          const int off = base_kt + 32 * jb * L::QROW + (32 * (kt >> 1) + 4 * (kt & 1)) * 2;
-          const u32x2_t h0 = lds_tr16(smem + L::oK + off);
-          const u32x2_t h1 = lds_tr16(smem + L::oK + off + 4 * L::QROW);
-          const u32x2_t g0 = lds_tr16(smem + L::oK + L::QPL + off);
-          const u32x2_t g1 = lds_tr16(smem + L::oK + L::QPL + off + 4 * L::QROW);
+          const int off0 = koff[kt >> 1][0] + 32 * jb * L::QROW + 8 * (kt & 1);
+          const int off1 = koff[kt >> 1][1] + 32 * jb * L::QROW + 8 * (kt & 1);
+          const u32x2_t h0 = lds_tr16(smem + L::oK + off0);
+          const u32x2_t h1 = lds_tr16(smem + L::oK + off1);
+          const u32x2_t g0 = lds_tr16(smem + L::oK + L::QPL + off0);
+          const u32x2_t g1 = lds_tr16(smem + L::oK + L::QPL + off1);
           const u32x4_t ah = {h0[0], h0[1], h1[0], h1[1]};
           const u32x4_t al = {g0[0], g0[1], g1[0], g1[1]};
 #pragma unroll
