@@ -80,6 +80,65 @@ def load_traffic(workload: str):
     return entry.get("bytes_per_launch")
 
 
+def _counter_per_dispatch(run_dir, counter, name_filter=None):
+    """Mean per-dispatch value of `counter` in a rocprofv3 --pmc CSV run directory,
+    for the kernel matching name_filter (default: the kernel with the largest value)."""
+    import csv
+    import glob
+    vals = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id", "")))
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    per_kernel = {}
+    for (name, _), v in vals.items():
+        per_kernel.setdefault(name, []).append(v)
+    if not per_kernel:
+        raise SystemExit(f"no {counter} rows under {run_dir}")
+    if name_filter is not None:
+        names = [n for n in per_kernel if name_filter in n]
+        if not names:
+            raise SystemExit(f"no kernel matching {name_filter!r} under {run_dir}")
+    else:
+        names = list(per_kernel)
+    means = {n: sum(per_kernel[n]) / len(per_kernel[n]) for n in names}
+    best = max(means, key=means.get)
+    return best, means[best]
+
+
+def record_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant kernel by what the
+    same counters read for a plain device copy of known size, and store the HBM bytes per
+    launch in profiles/traffic.json for the current device sources."""
+    copy_bytes = 512 << 20
+    _, cf = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE")
+    _, cw = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE")
+    f_factor, w_factor = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    kname, kf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", "gla_chunk_output")
+    _, kw = _counter_per_dispatch(write_dir, "WRITE_SIZE", "gla_chunk_output")
+    fetch_b, write_b = kf * 1024.0 * f_factor, kw * 1024.0 * w_factor
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    table[workload] = {
+        "kernel": kname.rsplit("(", 1)[0],
+        "bytes_per_launch": fetch_b + write_b,
+        "fetch_bytes": fetch_b, "write_bytes": write_b,
+        "fetch_kib_counter": kf, "write_kib_counter": kw,
+        "copy_fetch_factor": f_factor, "copy_write_factor": w_factor,
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(table[workload], indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,7 +153,13 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the forward, run a plain device copy of a known size "
                          "(used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="(no GPU) store HBM bytes per launch of --workload from rocprofv3 --pmc runs of "
+                         "FETCH_SIZE and WRITE_SIZE on this benchmark and on --copy-calibration")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build is a single-GPU kernel library; run it with --gpus 1 "
