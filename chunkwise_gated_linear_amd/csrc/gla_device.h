@@ -127,6 +127,9 @@ __device__ __forceinline__ u32x2_t buf_ld64(__amdgpu_buffer_rsrc_t r, int off) {
 __device__ __forceinline__ void buf_st128(__amdgpu_buffer_rsrc_t r, int off, u32x4_t v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off, 0, 0);
 }
+__device__ __forceinline__ void buf_st64(__amdgpu_buffer_rsrc_t r, int off, u32x2_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, off, 0, 0);
+}
 
 // LDS transposing read of four 16-bit elements (ds_read_b64_tr_b16).  Within
 // each group of 16 lanes, lane j receives component j%4 of the 8-byte words

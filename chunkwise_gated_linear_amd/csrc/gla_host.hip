@@ -62,6 +62,7 @@ struct Plan {
   int R;          // chunks per segment
   int P;          // segments per sequence (fixed length)
   int seg_slots;  // upper bound on segments over all sequences
+  int vtile;      // value columns per workgroup
   bool segmented; // some sequence may span several segments
   size_t ws_state, ws_decay, ws_base, ws_total;
 };
@@ -70,14 +71,31 @@ Plan make_plan(const gla_problem *p, bool varlen) {
   Plan pl{};
   pl.varlen = varlen;
   pl.N = varlen ? p->n_seqs : p->B;
-  const int H = p->H, NV = p->V / kVTile;
+  const int H = p->H;
+  // Value columns per workgroup.  The bf16 walker's 128-column workgroups form
+  // the gated operands of a head once for all 128 columns; they are used when
+  // they alone fill the device, or when sequences must be cut into segments
+  // anyway.  Otherwise 64-column workgroups double the parallelism without
+  // segmenting.  GLA_BF16_VTILE=64 / =128 fixes the choice (A/B runs).
+  int vtile = kVTile;
+  if (gla::bf16_walker_used(p->dtype == GLA_BF16, p->K) && p->V % 128 == 0) {
+    const long long rows = (long long)pl.N * H;
+    const char *env = getenv("GLA_BF16_VTILE");
+    if (env != nullptr && strcmp(env, "64") == 0) vtile = 64;
+    else if (env != nullptr && strcmp(env, "128") == 0) vtile = 128;
+    else if (varlen || rows * (p->V / 128) >= device_cu_count()) vtile = 128;
+    else vtile = rows * (p->V / 64) >= device_cu_count() ? 64 : 128;
+  }
+  pl.vtile = vtile;
+  const int NV = p->V / vtile;
   const long long chunks_total = ((long long)p->T + kChunk - 1) / kChunk;  // varlen: packed axis
   const long long chunks_seq = chunks_total;  // longest possible sequence
   int R = p->segment_chunks;
   if (R == 0) {
     // Enough (segment, head, value slice) workgroups to give every compute
-    // unit work; long sequences with few heads are cut into segments.
-    const long long target = 2LL * device_cu_count();
+    // unit work; long sequences with few heads are cut into segments.  A
+    // 128-column workgroup fills a compute unit on its own.
+    const long long target = (vtile == 128 ? 1LL : 2LL) * device_cu_count();
     const long long units_one = (long long)pl.N * H * NV;
     if (!varlen) {
       if (units_one >= device_cu_count() || chunks_seq <= 1) {
@@ -171,6 +189,7 @@ gla_status gla_fwd(const gla_problem *p, const void *q, const void *k, const voi
   w.R = pl.R;
   w.P = pl.P;
   w.units = (pl.segmented ? pl.seg_slots : (varlen ? N : N * pl.P)) * p->H;
+  w.vtile = pl.vtile;
   w.scale = p->scale;
   const bool bf = p->dtype == GLA_BF16;
 

@@ -26,15 +26,19 @@ struct WalkParams {
   int32_t R;                   // chunks per segment
   int32_t P;                   // segments per sequence when seg_base is null
   int32_t units;               // (segment, head) pairs covered by the grid
+  int32_t vtile;               // value columns per workgroup (64, or 128 for the bf16 walker)
   float scale;
 };
 
 // Launchers (return the hipGetLastError() of the launch).
 hipError_t launch_walk(bool local_mode, bool bf16, int K, const WalkParams &p, hipStream_t s);
 hipError_t launch_state_scan(const WalkParams &p, hipStream_t s);
-// bf16 walker for K in {64, 128} (gla_walk_bf16.hip)
+// bf16 walker for K in {64, 128} (gla_walk_bf16.hip), 64 or 128 value columns
+// per workgroup (WalkParams::vtile)
 bool walk_bf16_supported(int K);
 hipError_t launch_walk_bf16(bool local_mode, int K, const WalkParams &p, hipStream_t s);
+// whether launch_walk runs the bf16 walker for this dtype and K
+bool bf16_walker_used(bool bf16, int K);
 hipError_t launch_segment_plan(const WalkParams &p, int32_t *seg_base, hipStream_t s);
 
 }  // namespace gla

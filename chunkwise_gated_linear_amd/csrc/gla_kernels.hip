@@ -628,8 +628,10 @@ bool general_walker_forced() {
 
 }  // namespace
 
+bool bf16_walker_used(bool bf16, int K) { return bf16 && walk_bf16_supported(K) && !general_walker_forced(); }
+
 hipError_t launch_walk(bool local_mode, bool bf16, int K, const WalkParams &p, hipStream_t s) {
-  if (bf16 && walk_bf16_supported(K) && !general_walker_forced()) return launch_walk_bf16(local_mode, K, p, s);
+  if (bf16_walker_used(bf16, K)) return launch_walk_bf16(local_mode, K, p, s);
   if (bf16) {
     switch (K) {
       case 32: return launch_walk_t<true, 32>(local_mode, p, s);

@@ -46,25 +46,27 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int KD, bool OUT>
+template <int KD, bool OUT, int VW>
 struct LdsW {
   static constexpr int NQ = KD / 4;                // producer column quads
   static constexpr int QPW = NQ / 4;               // column quads per producer wave
   static constexpr int NG = 64 / QPW;              // producer row groups
   static constexpr int QROW = 2 * KD;              // qc / kc rows (bf16, swizzled)
-  static constexpr int VROW = 2 * VT;              // v rows (bf16, swizzled)
+  static constexpr int VROW = 2 * VW;              // v rows (bf16, swizzled)
   static constexpr int AROW = 2 * C;               // score rows (bf16, swizzled)
-  static constexpr int OROW = 4 * VT + 16;         // partial outputs (fp32, padded)
   static constexpr int QPL = C * QROW;             // one plane of qc or kc
   static constexpr int APL = C * AROW;
-  static constexpr int OPL = C * OROW;
   static constexpr int oQ = 0;                            // qc hi, lo              (OUT)
   static constexpr int oK = oQ + (OUT ? 2 * QPL : 0);     // kc hi, lo
   static constexpr int VPL = C * VROW;
   static constexpr int oV = oK + 2 * QPL;                 // v [token][n], two chunks
   static constexpr int oA = oV + 2 * VPL;                 // A hi, lo [i][j]        (OUT)
-  static constexpr int oO = oA + (OUT ? 2 * APL : 0);     // partial o [kh][i][n]   (OUT)
-  static constexpr int oDec = oO + (OUT ? 2 * OPL : 0);   // a [K]
+  // 64-column workgroups split the state rows in two key halves whose partial
+  // outputs meet in LDS; 128-column workgroups give each wave all K rows.
+  static constexpr int KS = VW == 64 ? 2 : 1;
+  static constexpr int PBYTES = KS == 2 ? 2 * 4 * 2 * 1024 : 0;  // o^T partial tiles [cw][it][nt], 16 B per lane
+  static constexpr int oP = oA + (OUT ? 2 * APL : 0);      // partial o^T exchanged between key halves (OUT)
+  static constexpr int oDec = oP + (OUT ? PBYTES : 0);     // a [K]
   static constexpr int BYTES = oDec + 4 * KD;
 
   // Swizzled byte offsets.  On gfx950 an LDS access is served 32 lanes at a
@@ -76,7 +78,8 @@ struct LdsW {
   // two passes their shapes allow:
   //   qc / kc: 16 B chunk ^ sqk(row) -- row fragments (16 rows x 2 chunks),
   //            transpose reads (8 rows x 4 pieces), producer writes (2 rows x 64 B)
-  //   v:       32 B pair ^ (b1 | b3 << 1) -- transpose reads, 128 B row writes
+  //   v:       32 B pair ^ (b1 | b3 << 1), 64 columns; ^ (b0 | b1 << 1 | b3 << 2),
+  //            128 columns -- transpose reads, whole-row writes
   //   A:       16 B chunk ^ (b0 | b2 << 1 | b3 << 2) -- row fragments, 8 B writes
   static __device__ __forceinline__ int sqk(int row) {
     const int b1 = (row >> 1) & 1, b2 = (row >> 2) & 1, b3 = (row >> 3) & 1;
@@ -86,7 +89,8 @@ struct LdsW {
     return row * QROW + (((byte >> 4) ^ sqk(row)) << 4) + (byte & 15);
   }
   static __device__ __forceinline__ int vo(int row, int byte) {
-    const int s = ((row >> 1) & 1) | (((row >> 3) & 1) << 1);
+    const int s = VW == 64 ? ((row >> 1) & 1) | (((row >> 3) & 1) << 1)
+                           : (row & 1) | (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2);
     return row * VROW + (((byte >> 5) ^ s) << 5) + (byte & 31);
   }
   static __device__ __forceinline__ int ao(int row, int byte) {
@@ -105,9 +109,9 @@ template <> struct Tiles<3> { static constexpr int n = 2; static constexpr int i
 // A^T tiles = kc qc^T for wave W's tiles, causal mask, split -> LDS A[i][j].
 // rf[kb]: this lane's offset of row l16, k columns 32 kb + 8 lg .. + 7, in a
 // qc / kc plane (the swizzle depends on the row within a 16-row tile only).
-template <int KD, int W>
+template <int KD, int VW, int W>
 __device__ __forceinline__ void scores(char *smem, const int (&rf)[KD / 32], int l16, int lg) {
-  using L = LdsW<KD, true>;
+  using L = LdsW<KD, true, VW>;
   using T = Tiles<W>;
   f32x4_t acc[T::n];
 #pragma unroll
@@ -142,11 +146,15 @@ __device__ __forceinline__ void scores(char *smem, const int (&rf)[KD / 32], int
   }
 }
 
-template <bool OUT, int KD>
+template <bool OUT, int KD, int VW>
 __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
-  using L = LdsW<KD, OUT>;
+  using L = LdsW<KD, OUT, VW>;
+  constexpr int KS = L::KS;         // key splits of the state over the 4 matrix waves
+  constexpr int CS = 4 / KS;        // column splits
+  constexpr int VQ = VW / CS;       // value columns per matrix wave (32)
+  constexpr int NT = VQ / 16;       // 16-column tiles per matrix wave
   constexpr int QPW = L::QPW, NG = L::NG, RPG = C / NG;
-  constexpr int KH = KD / 2;        // state rows per matrix wave
+  constexpr int KH = KD / KS;       // state rows per matrix wave
   constexpr int NKT = KH / 16;      // 16-row k tiles per matrix wave
   constexpr int NKB = KH / 32;      // 32-wide k blocks per matrix wave
   static_assert(KD == 64 || KD == 128, "bf16 walker covers K = 64, 128");
@@ -160,7 +168,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 
   // ---- (segment, head, value slice) of this workgroup; value slices of one
   // unit are 8 workgroup ids apart so they run on the same XCD and share L2.
-  const int NV = p.V / VT;
+  const int NV = p.V / VW;
   const int b = blockIdx.x;
   const int grp = b / (8 * NV), rem = b - grp * (8 * NV);
   const int vt = rem >> 3;
@@ -174,13 +182,16 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   const int c_begin = si.s * p.R;
   const int c_end = min(c_begin + p.R, nchunks);
   const int H = p.H, V = p.V;
-  const int v0 = vt * VT;
+  const int v0 = vt * VW;
   const int64_t rowK = (int64_t)H * KD, rowV = (int64_t)H * V;
   const int seq_bos = si.bos, seq_len = si.len;
 
   // ======================= matrix waves: state and lane bases
-  const int mw = wave & 3, kh = mw >> 1, nh = mw & 1;
-  f32x4_t S[NKT][2];
+  // matrix wave mw = CS kh + cw holds state rows KH kh .. + KH - 1, columns
+  // v0 + VQ cw .. + VQ - 1: S[kt][nt] lane rows KH kh + 16 kt + 4 lg + r,
+  // column VQ cw + 16 nt + l16
+  const int mw = wave & 3, kh = mw / CS, cw = mw % CS;
+  f32x4_t S[NKT][NT];
   if (!producer) {
     const float *src = nullptr;
     if (OUT) {
@@ -193,10 +204,10 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          S[kt][nt][r] = src ? src[(int64_t)(KH * kh + 16 * kt + 4 * lg + r) * V + v0 + 32 * nh + 16 * nt + l16] : 0.f;
+          S[kt][nt][r] = src ? src[(int64_t)(KH * kh + 16 * kt + 4 * lg + r) * V + v0 + VQ * cw + 16 * nt + l16] : 0.f;
   }
   if (OUT) {  // score tiles above the diagonal are read as zeros and never written
     for (int i = tid; i < 2 * L::APL / 16; i += kWsThreads)
@@ -204,23 +215,24 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   }
   // Per-lane LDS offsets; the compile-time parts (row tiles, token blocks, the
   // 8 B half of a chunk) are added at the access and do not change the swizzle.
-  int rf[KD / 32], rq[NKB];  // row fragments: all k blocks (scores), this wave's key half (qc S')
+  int rf[KD / 32], rq[NKB];  // row fragments: row l16, k columns 32 kb + 8 lg .. (all; this wave's keys)
 #pragma unroll
   for (int kb = 0; kb < KD / 32; ++kb) rf[kb] = L::qk(l16, 16 * (4 * kb + lg));
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) rq[kb] = L::qk(l16, 16 * (4 * (NKB * kh + kb) + lg));
-  const int base_a = L::ao(l16, 16 * (4 * kh + lg));  // A rows l16, tokens 32 kh + 8 lg ..
-  const int trow = 8 * lg + (l16 >> 2);               // token row of the transpose reads
-  int voff[2];                                        // v, transposed: columns 32 nh + 16 nt + 4 (l16 & 3)
+  int aoff[2];  // A row fragments: row l16, tokens 32 jb + 8 lg ..
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) voff[nt] = L::vo(trow, 64 * nh + 32 * nt + 8 * (l16 & 3));
-  int koff[NKT / 2][2];  // kc, transposed: key columns KH kh + 32 m + 8 (l16 & 3), token rows + 4 e
+  for (int jb = 0; jb < 2; ++jb) aoff[jb] = L::ao(l16, 16 * (4 * jb + lg));
+  const int trow = 8 * lg + (l16 >> 2);  // token row of the transpose reads
+  int voff[NT];                          // v, transposed: columns VQ cw + 16 nt + 4 (l16 & 3)
 #pragma unroll
-  for (int m = 0; m < NKT / 2; ++m)
+  for (int nt = 0; nt < NT; ++nt) voff[nt] = L::vo(trow, 2 * (VQ * cw + 16 * nt) + 8 * (l16 & 3));
+  int koff[NKB][2];  // kc, transposed: key columns KH kh + 32 m + 8 (l16 & 3), token rows + 4 e
+#pragma unroll
+  for (int m = 0; m < NKB; ++m)
 #pragma unroll
     for (int e = 0; e < 2; ++e) koff[m][e] = L::qk(trow + 4 * e, 2 * (KH * kh + 8 * (l16 & 3)) + 64 * m);
-  const int base_o = 4 * lg * L::OROW + (32 * nh + l16) * 4 + kh * L::OPL;             // partial o
-  const int base_d = (KH * kh + 4 * lg) * 4;                                           // decay
+  const int base_d = 4 * (KH * kh + 4 * lg);  // decay a of key rows KH kh + 16 kt + 4 lg ..
 
   // ======================= producer waves: raw and gated registers
   // producer thread pt: key columns 4cq..4cq+3 of rows rg*RPG..+RPG-1; v row pt/4, 16 columns
@@ -228,15 +240,16 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   const int cq = (wave & 3) * QPW + lane % QPW, rg = lane / QPW;
   const int voff_g = (int)((rg * RPG * rowK + 4 * cq) * 4);
   const int voff_k = (int)((rg * RPG * rowK + 4 * cq) * 2);
-  // v: 16 B chunk (pt & 7) of token rows pt / 8 and pt / 8 + 32 (8 lanes per 128 B row)
-  const int vrow = (pt & 255) >> 3, vch = pt & 7;
+  // v: 16 B chunk vch of token rows vrow + VRS j (VW / 8 lanes per row)
+  constexpr int VCH = VW / 8, VRS = 256 / VCH, NVL = C / VRS;
+  const int vrow = (pt & 255) / VCH, vch = pt % VCH;
   const int voff_v = (int)((vrow * rowV + 8 * vch) * 2);
-  const int vstep = (int)(32 * rowV * 2);
+  const int vstep = (int)(VRS * rowV * 2);
   const int step_g = (int)(rowK * 4), step_k = (int)(rowK * 2);
   const int colq = kperm_bf(4 * cq) * 2;
   u32x4_t rgG[RPG];
   u32x2_t rgQ[RPG], rgK[RPG];
-  u32x4_t rgV[2];
+  u32x4_t rgV[NVL];
   u32x2_t gQh[RPG], gQl[RPG], gKh[RPG], gKl[RPG];
   f32x4_t gDec = {1.f, 1.f, 1.f, 1.f};
   float gPl[RPG][4], gRl[RPG][4], gSuf[4], gFq[4];
@@ -262,8 +275,8 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
     for (int i = 0; i < RPG; ++i) rgG[i] = buf_ld128(r.g, voff_g + i * step_g);
   };
   auto load_v = [&](const Rsrc &r) {
-    rgV[0] = buf_ld128(r.v, voff_v);
-    rgV[1] = buf_ld128(r.v, voff_v + vstep);
+#pragma unroll
+    for (int j = 0; j < NVL; ++j) rgV[j] = buf_ld128(r.v, voff_v + j * vstep);
   };
   auto load_qk_row = [&](const Rsrc &r, int i) {
     rgK[i] = buf_ld64(r.k, voff_k + i * step_k);
@@ -337,8 +350,8 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   // v goes to LDS straight from the load registers (two chunk buffers)
   auto write_v = [&](int c) {
     char *sv = smem + L::oV + (c & 1) * L::VPL;
-    lds_st<u32x4_t>(sv, L::vo(vrow, 16 * vch), rgV[0]);
-    lds_st<u32x4_t>(sv, L::vo(vrow + 32, 16 * vch), rgV[1]);
+#pragma unroll
+    for (int j = 0; j < NVL; ++j) lds_st<u32x4_t>(sv, L::vo(vrow + VRS * j, 16 * vch), rgV[j]);
   };
   auto write_k = [&]() {  // kc and the chunk decay
 #pragma unroll
@@ -358,27 +371,18 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
     }
   };
 
-  // Output pass of the matrix waves after the third barrier of chunk c: sum the
-  // two key-half partials, round to bf16, two 16 B stores per thread.
-  auto store_out = [&](int c) {
+  // Output of chunk c from o^T tiles: lane = token 16 it + l16, columns VQ cw +
+  // 16 nt + 4 lg .. + 3, rounded to bf16 (8 B per lane and tile).
+  auto o_rsrc = [&](int c) {
     const int64_t t0 = (int64_t)seq_bos + (int64_t)c * C;
     const int64_t valid = min(C, seq_len - c * C);
     const int64_t headV = (int64_t)h * V + v0;
-    const __amdgpu_buffer_rsrc_t rO = make_rsrc((uint16_t *)p.o + t0 * rowV + headV, (valid * rowV - headV) * 2);
-    const int orow = tid >> 2, ocol = 16 * (tid & 3);
-#pragma unroll
-    for (int y = 0; y < 2; ++y) {
-      uint32_t w[4];
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int off = orow * L::OROW + (ocol + 8 * y + 4 * x) * 4;
-        const f32x4_t a0 = lds_ld<f32x4_t>(smem + L::oO, off);
-        const f32x4_t a1 = lds_ld<f32x4_t>(smem + L::oO + L::OPL, off);
-        w[2 * x] = pack_bf16(a0[0] + a1[0], a0[1] + a1[1]);
-        w[2 * x + 1] = pack_bf16(a0[2] + a1[2], a0[3] + a1[3]);
-      }
-      buf_st128(rO, (int)((orow * rowV + ocol + 8 * y) * 2), u32x4_t{w[0], w[1], w[2], w[3]});
-    }
+    return make_rsrc((uint16_t *)p.o + t0 * rowV + headV, (valid * rowV - headV) * 2);
+  };
+  auto store_tile = [&](const __amdgpu_buffer_rsrc_t &rO, int it, int nt, const f32x4_t &x) {
+    const int col = VQ * cw + 16 * nt + 4 * lg;
+    const u32x2_t w = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+    buf_st64(rO, (int)(((16 * it + l16) * rowV + col) * 2), w);
   };
 
   // Producer and matrix waves run separate loops (different register sets);
@@ -424,10 +428,10 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       phase_barrier();  // operands of chunk c visible
       if constexpr (OUT) {
         switch (mw) {
-          case 0: scores<KD, 0>(smem, rf, l16, lg); break;
-          case 1: scores<KD, 1>(smem, rf, l16, lg); break;
-          case 2: scores<KD, 2>(smem, rf, l16, lg); break;
-          default: scores<KD, 3>(smem, rf, l16, lg); break;
+          case 0: scores<KD, VW, 0>(smem, rf, l16, lg); break;
+          case 1: scores<KD, VW, 1>(smem, rf, l16, lg); break;
+          case 2: scores<KD, VW, 2>(smem, rf, l16, lg); break;
+          default: scores<KD, VW, 3>(smem, rf, l16, lg); break;
         }
         phase_barrier();  // scores visible
       }
@@ -437,14 +441,14 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       for (int kt = 0; kt < NKT; ++kt) {
         const f32x4_t a4 = lds_ld<f32x4_t>(smem + L::oDec, base_d + 64 * kt);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) S[kt][nt][r] *= a4[r];
       }
-      // ---- v fragments: v[32jb + 8lg + e][32nh + 16nt + l16]
-      u32x4_t vf[2][2];
+      // ---- v fragments: v[32 jb + 8 lg + e][VQ mw + 16 nt + l16]
+      u32x4_t vf[NT][2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
           const int off = voff[nt] + 32 * jb * L::VROW;
@@ -452,39 +456,37 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
           const u32x2_t x1 = lds_tr16(sv + off + 4 * L::VROW);
           vf[nt][jb] = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
         }
+      f32x4_t keep[4];
       if constexpr (OUT) {
-        f32x4_t o[4][2];
+        f32x4_t o[4][NT];  // o^T tiles: lane = token 16 it + l16, rows = columns 16 nt + 4 lg + r
 #pragma unroll
         for (int it = 0; it < 4; ++it)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) o[it][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        // ---- o += A v over token block jb = kh of every row tile (key half 0 takes
-        // tokens 0..31, key half 1 tokens 32..63; blocks above the diagonal are zero)
-        u32x4_t vs[2];
+          for (int nt = 0; nt < NT; ++nt) o[it][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // ---- o^T += v^T A^T over the 32-token blocks on or below the diagonal
+        // (with two key halves, half kh takes token block kh; kh is uniform)
+        auto av = [&](auto jbc) {
+          constexpr int jb = decltype(jbc)::value;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const int off = voff[nt] + 32 * kh * L::VROW;
-          const u32x2_t x0 = lds_tr16(sv + off);
-          const u32x2_t x1 = lds_tr16(sv + off + 4 * L::VROW);
-          vs[nt] = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
-        }
+          for (int it = 2 * jb; it < 4; ++it) {
+            const int off = aoff[jb] + 16 * it * L::AROW;
+            const u32x4_t ah = lds_ld<u32x4_t>(smem + L::oA, off);
+            const u32x4_t al = lds_ld<u32x4_t>(smem + L::oA + L::APL, off);
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int off = base_a + 16 * it * L::AROW;
-          const u32x4_t ah = lds_ld<u32x4_t>(smem + L::oA, off);
-          const u32x4_t al = lds_ld<u32x4_t>(smem + L::oA + L::APL, off);
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            o[it][nt] = mfma_bf(al, vs[nt], o[it][nt]);
-            o[it][nt] = mfma_bf(ah, vs[nt], o[it][nt]);
+            for (int nt = 0; nt < NT; ++nt) {
+              o[it][nt] = mfma_bf(vf[nt][jb], al, o[it][nt]);
+              o[it][nt] = mfma_bf(vf[nt][jb], ah, o[it][nt]);
+            }
           }
-        }
-        // ---- o += qc S' over this wave's key half (S' from the accumulators)
+        };
+        if (KS == 1 || kh == 0) av(std::integral_constant<int, 0>{});
+        if (KS == 1 || kh == 1) av(std::integral_constant<int, 1>{});
+        // ---- o^T += S'^T qc^T (S' from the accumulators, split hi + lo)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          u32x4_t sh[2], sl[2];
+          u32x4_t sh[NT], sl[NT];
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
+          for (int nt = 0; nt < NT; ++nt) {
             const float s8[8] = {S[2 * kb][nt][0], S[2 * kb][nt][1], S[2 * kb][nt][2], S[2 * kb][nt][3],
                                  S[2 * kb + 1][nt][0], S[2 * kb + 1][nt][1], S[2 * kb + 1][nt][2], S[2 * kb + 1][nt][3]};
             u32x2_t h0, l0, h1, l1;
@@ -499,21 +501,28 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
             const u32x4_t qh = lds_ld<u32x4_t>(smem + L::oQ, off);
             const u32x4_t ql = lds_ld<u32x4_t>(smem + L::oQ + L::QPL, off);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-              o[it][nt] = mfma_bf(ql, sh[nt], o[it][nt]);
-              o[it][nt] = mfma_bf(qh, sl[nt], o[it][nt]);
-              o[it][nt] = mfma_bf(qh, sh[nt], o[it][nt]);
+            for (int nt = 0; nt < NT; ++nt) {
+              o[it][nt] = mfma_bf(sh[nt], ql, o[it][nt]);
+              o[it][nt] = mfma_bf(sl[nt], qh, o[it][nt]);
+              o[it][nt] = mfma_bf(sh[nt], qh, o[it][nt]);
             }
           }
         }
-        // ---- partial o -> LDS [kh][i][n] (fp32)
+        if constexpr (KS == 1) {
+          const __amdgpu_buffer_rsrc_t rO = o_rsrc(c);
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
+          for (int it = 0; it < 4; ++it)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NT; ++nt) store_tile(rO, it, nt, o[it][nt]);
+        } else {
+          // keep tile nt = kh, send tile 1 - kh to the partner key half
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              lds_st<float>(smem + L::oO, base_o + (16 * it + r) * L::OROW + 64 * nt, o[it][nt][r]);
+          for (int it = 0; it < 4; ++it) {
+            keep[it] = kh ? o[it][1] : o[it][0];
+            const f32x4_t send = kh ? o[it][0] : o[it][1];
+            lds_st<f32x4_t>(smem + L::oP, ((cw * 4 + it) * 2 + (1 - kh)) * 1024 + 16 * lane, send);
+          }
+        }
       }
       // ---- S = S' + kc^T v   (kc^T rows via transpose reads of the token-major kc)
 #pragma unroll
@@ -529,14 +538,22 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
           const u32x4_t ah = {h0[0], h0[1], h1[0], h1[1]};
           const u32x4_t al = {g0[0], g0[1], g1[0], g1[1]};
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
+          for (int nt = 0; nt < NT; ++nt) {
             S[kt][nt] = mfma_bf(al, vf[nt][jb], S[kt][nt]);
             S[kt][nt] = mfma_bf(ah, vf[nt][jb], S[kt][nt]);
           }
         }
       }
-      phase_barrier();  // partial outputs visible; chunk c's operands are no longer read
-      if constexpr (OUT) store_out(c);
+      phase_barrier();  // chunk c's operands are no longer read; partial outputs visible
+      if constexpr (OUT && KS == 2) {
+        const __amdgpu_buffer_rsrc_t rO = o_rsrc(c);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const f32x4_t part = lds_ld<f32x4_t>(smem + L::oP, ((cw * 4 + it) * 2 + kh) * 1024 + 16 * lane);
+          store_tile(rO, it, kh, f32x4_t{keep[it][0] + part[0], keep[it][1] + part[1], keep[it][2] + part[2],
+                                         keep[it][3] + part[3]});
+        }
+      }
     }
   }
 
@@ -552,10 +569,10 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            dst[(int64_t)(KH * kh + 16 * kt + 4 * lg + r) * V + v0 + 32 * nh + 16 * nt + l16] = S[kt][nt][r];
+            dst[(int64_t)(KH * kh + 16 * kt + 4 * lg + r) * V + v0 + VQ * cw + 16 * nt + l16] = S[kt][nt][r];
     }
   } else if (!OUT && vt == 0 && rg == 0) {
     const int slot = si.first + si.s;
@@ -564,27 +581,27 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   }
 }
 
-template <int KD>
+template <int KD, int VW>
 __global__ __launch_bounds__(kWsThreads, 1) void gla_chunk_output_bf16(WalkParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[LdsW<KD, true>::BYTES];
-  walk_bf16<true, KD>(p, smem);
+  __shared__ __attribute__((aligned(16))) char smem[LdsW<KD, true, VW>::BYTES];
+  walk_bf16<true, KD, VW>(p, smem);
 }
 
-template <int KD>
+template <int KD, int VW>
 __global__ __launch_bounds__(kWsThreads, 1) void gla_chunk_local_bf16(WalkParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[LdsW<KD, false>::BYTES];
-  walk_bf16<false, KD>(p, smem);
+  __shared__ __attribute__((aligned(16))) char smem[LdsW<KD, false, VW>::BYTES];
+  walk_bf16<false, KD, VW>(p, smem);
 }
 
-template <int KD>
+template <int KD, int VW>
 hipError_t launch_t(bool local_mode, const WalkParams &p, hipStream_t s) {
-  const int NV = p.V / VT;
+  const int NV = p.V / VW;
   const int groups = (p.units + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * NV));
   if (local_mode)
-    hipLaunchKernelGGL(gla_chunk_local_bf16<KD>, grid, dim3(kWsThreads), 0, s, p);
+    hipLaunchKernelGGL((gla_chunk_local_bf16<KD, VW>), grid, dim3(kWsThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(gla_chunk_output_bf16<KD>, grid, dim3(kWsThreads), 0, s, p);
+    hipLaunchKernelGGL((gla_chunk_output_bf16<KD, VW>), grid, dim3(kWsThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -593,8 +610,10 @@ hipError_t launch_t(bool local_mode, const WalkParams &p, hipStream_t s) {
 bool walk_bf16_supported(int K) { return K == 64 || K == 128; }
 
 hipError_t launch_walk_bf16(bool local_mode, int K, const WalkParams &p, hipStream_t s) {
-  if (K == 128) return launch_t<128>(local_mode, p, s);
-  if (K == 64) return launch_t<64>(local_mode, p, s);
+  const int vw = p.vtile;
+  if ((vw != 64 && vw != 128) || p.V % vw != 0) return hipErrorInvalidValue;
+  if (K == 128) return vw == 128 ? launch_t<128, 128>(local_mode, p, s) : launch_t<128, 64>(local_mode, p, s);
+  if (K == 64) return vw == 128 ? launch_t<64, 128>(local_mode, p, s) : launch_t<64, 64>(local_mode, p, s);
   return hipErrorInvalidValue;
 }
 

@@ -73,6 +73,16 @@ def test_forced_segments(dtype, seg):
     _compare(d, dtype, f"segments of {seg} chunks", segment_chunks=seg)
 
 
+@pytest.mark.parametrize("vtile", ["64", "128"])
+@pytest.mark.parametrize("K,V,seg", [(128, 256, 0), (128, 128, 3), (64, 256, 0), (64, 128, 2)])
+def test_value_tile_widths(monkeypatch, vtile, K, V, seg):
+    # the bf16 walker runs 64- or 128-column workgroups; pin each width on the
+    # same inputs (ragged tail, initial state, with and without segments)
+    monkeypatch.setenv("GLA_BF16_VTILE", vtile)
+    d = gi.draw(800 + K + V + seg, 2, 333, 3, K, V, dtype="bf16", h0=True)
+    _compare(d, "bf16", f"vtile={vtile} K={K} V={V}", segment_chunks=seg)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("seg", [0, 1, 2])
 def test_packed_sequences(dtype, seg):
