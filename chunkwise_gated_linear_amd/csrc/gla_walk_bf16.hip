@@ -35,7 +35,6 @@ namespace {
 
 using namespace dev;
 
-constexpr int kWsThreads = 512;  // 4 matrix waves + 4 producer waves
 
 // Workgroup barrier that is also a hard scheduling boundary: the compiler may
 // otherwise move pure vector arithmetic (and lane shuffles) across s_barrier,
@@ -48,8 +47,12 @@ __device__ __forceinline__ void phase_barrier() {
 
 template <int KD, bool OUT, int VW>
 struct LdsW {
+  // 4 matrix waves and NPW producer waves, two waves per SIMD (eight producers,
+  // three waves per SIMD, leave the matrix waves too few registers)
+  static constexpr int NPW = 4;
+  static constexpr int THREADS = 64 * (4 + NPW);
   static constexpr int NQ = KD / 4;                // producer column quads
-  static constexpr int QPW = NQ / 4;               // column quads per producer wave
+  static constexpr int QPW = NQ / NPW;             // column quads per producer wave
   static constexpr int NG = 64 / QPW;              // producer row groups
   static constexpr int QROW = 2 * KD;              // qc / kc rows (bf16, swizzled)
   static constexpr int VROW = 2 * VW;              // v rows (bf16, swizzled)
@@ -210,7 +213,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
           S[kt][nt][r] = src ? src[(int64_t)(KH * kh + 16 * kt + 4 * lg + r) * V + v0 + VQ * cw + 16 * nt + l16] : 0.f;
   }
   if (OUT) {  // score tiles above the diagonal are read as zeros and never written
-    for (int i = tid; i < 2 * L::APL / 16; i += kWsThreads)
+    for (int i = tid; i < 2 * L::APL / 16; i += L::THREADS)
       lds_st<u32x4_t>(smem + L::oA, 16 * i, u32x4_t{0, 0, 0, 0});
   }
   // Per-lane LDS offsets; the compile-time parts (row tiles, token blocks, the
@@ -235,14 +238,14 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   const int base_d = 4 * (KH * kh + 4 * lg);  // decay a of key rows KH kh + 16 kt + 4 lg ..
 
   // ======================= producer waves: raw and gated registers
-  // producer thread pt: key columns 4cq..4cq+3 of rows rg*RPG..+RPG-1; v row pt/4, 16 columns
+  // producer thread pt: key columns 4cq..4cq+3 of rows rg*RPG..+RPG-1
   const int pt = tid - 4 * 64;
-  const int cq = (wave & 3) * QPW + lane % QPW, rg = lane / QPW;
+  const int cq = (wave - 4) * QPW + lane % QPW, rg = lane / QPW;
   const int voff_g = (int)((rg * RPG * rowK + 4 * cq) * 4);
   const int voff_k = (int)((rg * RPG * rowK + 4 * cq) * 2);
   // v: 16 B chunk vch of token rows vrow + VRS j (VW / 8 lanes per row)
-  constexpr int VCH = VW / 8, VRS = 256 / VCH, NVL = C / VRS;
-  const int vrow = (pt & 255) / VCH, vch = pt % VCH;
+  constexpr int VCH = VW / 8, VRS = 64 * L::NPW / VCH, NVL = C / VRS;
+  const int vrow = pt / VCH, vch = pt % VCH;
   const int voff_v = (int)((vrow * rowV + 8 * vch) * 2);
   const int vstep = (int)(VRS * rowV * 2);
   const int step_g = (int)(rowK * 4), step_k = (int)(rowK * 2);
@@ -582,13 +585,13 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 }
 
 template <int KD, int VW>
-__global__ __launch_bounds__(kWsThreads, 1) void gla_chunk_output_bf16(WalkParams p) {
+__global__ __launch_bounds__((LdsW<KD, true, VW>::THREADS), 1) void gla_chunk_output_bf16(WalkParams p) {
   __shared__ __attribute__((aligned(16))) char smem[LdsW<KD, true, VW>::BYTES];
   walk_bf16<true, KD, VW>(p, smem);
 }
 
 template <int KD, int VW>
-__global__ __launch_bounds__(kWsThreads, 1) void gla_chunk_local_bf16(WalkParams p) {
+__global__ __launch_bounds__((LdsW<KD, false, VW>::THREADS), 1) void gla_chunk_local_bf16(WalkParams p) {
   __shared__ __attribute__((aligned(16))) char smem[LdsW<KD, false, VW>::BYTES];
   walk_bf16<false, KD, VW>(p, smem);
 }
@@ -599,9 +602,9 @@ hipError_t launch_t(bool local_mode, const WalkParams &p, hipStream_t s) {
   const int groups = (p.units + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * NV));
   if (local_mode)
-    hipLaunchKernelGGL((gla_chunk_local_bf16<KD, VW>), grid, dim3(kWsThreads), 0, s, p);
+    hipLaunchKernelGGL((gla_chunk_local_bf16<KD, VW>), grid, dim3(LdsW<KD, false, VW>::THREADS), 0, s, p);
   else
-    hipLaunchKernelGGL((gla_chunk_output_bf16<KD, VW>), grid, dim3(kWsThreads), 0, s, p);
+    hipLaunchKernelGGL((gla_chunk_output_bf16<KD, VW>), grid, dim3(LdsW<KD, true, VW>::THREADS), 0, s, p);
   return hipGetLastError();
 }
 
