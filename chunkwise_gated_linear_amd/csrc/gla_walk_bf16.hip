@@ -59,8 +59,13 @@ struct LdsW {
   static constexpr int AROW = 2 * C;               // score rows (bf16, swizzled)
   static constexpr int QPL = C * QROW;             // one plane of qc or kc
   static constexpr int APL = C * AROW;
-  static constexpr int oQ = 0;                            // qc hi, lo              (OUT)
-  static constexpr int oK = oQ + (OUT ? 2 * QPL : 0);     // kc hi, lo
+  // qc hi, lo: two chunk buffers for 64-column workgroups (the producers write
+  // each row of chunk c+1 as soon as it is gated), one for 128 columns (there
+  // the second buffer's registers and LDS cost more than the earlier writes save)
+  static constexpr int NQB = VW == 64 ? 2 : 1;
+  static constexpr int oQ = 0;                                  // qc hi, lo per buffer (OUT)
+  static constexpr int oK = oQ + (OUT ? 2 * NQB * QPL : 0);     // kc hi, lo
+  static constexpr int qbuf(int c) { return oQ + (NQB == 2 ? (c & 1) : 0) * 2 * QPL; }
   static constexpr int VPL = C * VROW;
   static constexpr int oV = oK + 2 * QPL;                 // v [token][n], two chunks
   static constexpr int oA = oV + 2 * VPL;                 // A hi, lo [i][j]        (OUT)
@@ -111,9 +116,10 @@ template <> struct Tiles<3> { static constexpr int n = 2; static constexpr int i
 
 // A^T tiles = kc qc^T for wave W's tiles, causal mask, split -> LDS A[i][j].
 // rf[kb]: this lane's offset of row l16, k columns 32 kb + 8 lg .. + 7, in a
-// qc / kc plane (the swizzle depends on the row within a 16-row tile only).
+// qc / kc plane (the swizzle depends on the row within a 16-row tile only);
+// sq: the qc buffer of the chunk.
 template <int KD, int VW, int W>
-__device__ __forceinline__ void scores(char *smem, const int (&rf)[KD / 32], int l16, int lg) {
+__device__ __forceinline__ void scores(char *smem, const char *sq, const int (&rf)[KD / 32], int l16, int lg) {
   using L = LdsW<KD, true, VW>;
   using T = Tiles<W>;
   f32x4_t acc[T::n];
@@ -127,8 +133,8 @@ __device__ __forceinline__ void scores(char *smem, const int (&rf)[KD / 32], int
       const int ob = rf[kb] + 16 * T::it[t] * L::QROW;
       const u32x4_t ah = lds_ld<u32x4_t>(smem + L::oK, oa);
       const u32x4_t al = lds_ld<u32x4_t>(smem + L::oK + L::QPL, oa);
-      const u32x4_t bh = lds_ld<u32x4_t>(smem + L::oQ, ob);
-      const u32x4_t bl = lds_ld<u32x4_t>(smem + L::oQ + L::QPL, ob);
+      const u32x4_t bh = lds_ld<u32x4_t>(sq, ob);
+      const u32x4_t bl = lds_ld<u32x4_t>(sq + L::QPL, ob);
       acc[t] = mfma_bf(al, bh, acc[t]);
       acc[t] = mfma_bf(ah, bl, acc[t]);
       acc[t] = mfma_bf(ah, bh, acc[t]);
@@ -365,13 +371,11 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
     }
     if (rg == 0) lds_st<f32x4_t>(smem + L::oDec, 16 * cq, gDec);
   };
-  auto write_q = [&]() {
-#pragma unroll
-    for (int r = 0; r < RPG; ++r) {
-      const int off = L::qk(rg * RPG + r, colq);
-      lds_st<u32x2_t>(smem + L::oQ, off, gQh[r]);
-      lds_st<u32x2_t>(smem + L::oQ + L::QPL, off, gQl[r]);
-    }
+  auto write_q_row = [&](int c, int r) {
+    char *sq = smem + L::qbuf(c);
+    const int off = L::qk(rg * RPG + r, colq);
+    lds_st<u32x2_t>(sq, off, gQh[r]);
+    lds_st<u32x2_t>(sq + L::QPL, off, gQl[r]);
   };
 
   // Output of chunk c from o^T tiles: lane = token 16 it + l16, columns VQ cw +
@@ -406,12 +410,16 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 #pragma unroll
       for (int i = 0; i < RPG; ++i) {
         gate_row(i);
+        if constexpr (OUT && L::NQB == 2) write_q_row(c_begin, i);
         load_qk_row(r1, i);
       }
     }
     for (int c = c_begin; c < c_end; ++c) {
       write_k();        // chunk c
-      if constexpr (OUT) write_q();
+      if constexpr (OUT && L::NQB == 1) {
+#pragma unroll
+        for (int i = 0; i < RPG; ++i) write_q_row(c, i);
+      }
       phase_barrier();  // operands of chunk c visible
       const Rsrc r2 = rsrc(c + 2);
       gate_decays();    // chunk c+1
@@ -422,19 +430,21 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 #pragma unroll
       for (int i = 0; i < RPG; ++i) {
         gate_row(i);    // chunk c+1
+        if constexpr (OUT && L::NQB == 2) write_q_row(c + 1, i);
         load_qk_row(r2, i);
       }
       phase_barrier();  // chunk c done
     }
   } else {
     for (int c = c_begin; c < c_end; ++c) {
+      const char *sq = smem + L::qbuf(c);  // qc of chunk c
       phase_barrier();  // operands of chunk c visible
       if constexpr (OUT) {
         switch (mw) {
-          case 0: scores<KD, VW, 0>(smem, rf, l16, lg); break;
-          case 1: scores<KD, VW, 1>(smem, rf, l16, lg); break;
-          case 2: scores<KD, VW, 2>(smem, rf, l16, lg); break;
-          default: scores<KD, VW, 3>(smem, rf, l16, lg); break;
+          case 0: scores<KD, VW, 0>(smem, sq, rf, l16, lg); break;
+          case 1: scores<KD, VW, 1>(smem, sq, rf, l16, lg); break;
+          case 2: scores<KD, VW, 2>(smem, sq, rf, l16, lg); break;
+          default: scores<KD, VW, 3>(smem, sq, rf, l16, lg); break;
         }
         phase_barrier();  // scores visible
       }
@@ -501,8 +511,8 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 #pragma unroll
           for (int it = 0; it < 4; ++it) {
             const int off = rq[kb] + 16 * it * L::QROW;
-            const u32x4_t qh = lds_ld<u32x4_t>(smem + L::oQ, off);
-            const u32x4_t ql = lds_ld<u32x4_t>(smem + L::oQ + L::QPL, off);
+            const u32x4_t qh = lds_ld<u32x4_t>(sq, off);
+            const u32x4_t ql = lds_ld<u32x4_t>(sq + L::QPL, off);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
               o[it][nt] = mfma_bf(sh[nt], ql, o[it][nt]);
