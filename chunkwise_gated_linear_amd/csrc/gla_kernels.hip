@@ -111,8 +111,11 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
   if (!locate(p, seg, si)) return;
   if (!OUT && si.s >= si.nseg - 1) return;  // the last segment's summary is never used
   const int nchunks = (si.len + C - 1) / C;
-  const int c_begin = si.s * p.R;
-  const int c_end = min(c_begin + p.R, nchunks);
+  // the sequence's nseg = max(1, ceil(nchunks / R)) segments share its chunks
+  // evenly: ceil(nchunks / nseg) <= R each, none empty
+  const int seg_len = (nchunks + si.nseg - 1) / si.nseg;
+  const int c_begin = si.s * seg_len;
+  const int c_end = min(c_begin + seg_len, nchunks);
   const int v0 = vt * VT;
   const int H = p.H;
   const size_t rowK = (size_t)H * KD;  // element stride between tokens, q/k/g

@@ -188,8 +188,11 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   if (!locate(p, seg, si)) return;
   if (!OUT && si.s >= si.nseg - 1) return;
   const int nchunks = (si.len + C - 1) / C;
-  const int c_begin = si.s * p.R;
-  const int c_end = min(c_begin + p.R, nchunks);
+  // the sequence's nseg = max(1, ceil(nchunks / R)) segments share its chunks
+  // evenly: ceil(nchunks / nseg) <= R each, none empty
+  const int seg_len = (nchunks + si.nseg - 1) / si.nseg;
+  const int c_begin = si.s * seg_len;
+  const int c_end = min(c_begin + seg_len, nchunks);
   const int H = p.H, V = p.V;
   const int v0 = vt * VW;
   const int64_t rowK = (int64_t)H * KD, rowV = (int64_t)H * V;
