@@ -77,6 +77,7 @@ __device__ __forceinline__ bool locate(const WalkParams &p, int seg, SegInfo &si
   } else {
     const int total = p.seg_base[p.N];
     if (seg >= total) return false;
+    if (p.seg_order != nullptr) seg = p.seg_order[seg];  // longest segments are dispatched first
     int lo = 0, hi = p.N - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;

@@ -106,8 +106,13 @@ Plan make_plan(const gla_problem *p, bool varlen) {
         R = (int)((chunks_seq + P - 1) / P);
       }
     } else {
+      // packed: about 1.5 segment workgroups per compute unit balances the
+      // unequal segment lengths (dispatched longest first) against the extra
+      // summary work of cutting more sequences (measured optimum on the
+      // 16-sequence U[256, 4096] workload)
       const long long work = (chunks_total + pl.N) * H * NV;  // chunk-slices to spread
-      long long r = (work + target - 1) / target;
+      const long long tgt = vtile == 128 ? (3LL * device_cu_count()) / 2 : target;
+      long long r = (work + tgt - 1) / tgt;
       if (r < 4) r = 4;
       R = (int)r;
     }
@@ -129,7 +134,7 @@ Plan make_plan(const gla_problem *p, bool varlen) {
   if (pl.segmented) {
     pl.ws_state = (size_t)pl.seg_slots * H * p->K * p->V * sizeof(float);
     pl.ws_decay = (size_t)pl.seg_slots * H * p->K * sizeof(float);
-    pl.ws_base = varlen ? (size_t)(pl.N + 1) * sizeof(int32_t) : 0;
+    pl.ws_base = varlen ? (size_t)(pl.N + 1 + pl.seg_slots) * sizeof(int32_t) : 0;  // table + order
   }
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   pl.ws_total = up(pl.ws_state) + up(pl.ws_decay) + up(pl.ws_base);
@@ -185,6 +190,7 @@ gla_status gla_fwd(const gla_problem *p, const void *q, const void *k, const voi
                           ? reinterpret_cast<int32_t *>(ws + up(pl.ws_state) + up(pl.ws_decay))
                           : nullptr;
   w.seg_base = seg_base;
+  w.seg_order = seg_base ? seg_base + N + 1 : nullptr;
   w.T = p->T; w.H = p->H; w.K = p->K; w.V = p->V; w.N = N;
   w.R = pl.R;
   w.P = pl.P;
@@ -193,7 +199,7 @@ gla_status gla_fwd(const gla_problem *p, const void *q, const void *k, const voi
   w.scale = p->scale;
   const bool bf = p->dtype == GLA_BF16;
 
-  if (seg_base && gla::launch_segment_plan(w, seg_base, s) != hipSuccess) return GLA_ERR_HIP;
+  if (seg_base && gla::launch_segment_plan(w, seg_base, seg_base + N + 1, s) != hipSuccess) return GLA_ERR_HIP;
   if (pl.segmented) {
     if (gla::launch_walk(true, bf, p->K, w, s) != hipSuccess) return GLA_ERR_HIP;
     if (gla::launch_state_scan(w, s) != hipSuccess) return GLA_ERR_HIP;

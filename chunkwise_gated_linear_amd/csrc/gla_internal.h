@@ -22,6 +22,7 @@ struct WalkParams {
   float *seg_state;            // [seg_slots][H][K][V]: segment summaries, then start states
   float *seg_decay;            // [seg_slots][H][K]: product of the segment's decays
   const int32_t *seg_base;     // [N+1] first segment of each packed sequence, or null
+  const int32_t *seg_order;    // [segments] segment ids, longest first (packed), or null
   int32_t T, H, K, V, N;
   int32_t R;                   // chunks per segment
   int32_t P;                   // segments per sequence when seg_base is null
@@ -39,6 +40,6 @@ bool walk_bf16_supported(int K);
 hipError_t launch_walk_bf16(bool local_mode, int K, const WalkParams &p, hipStream_t s);
 // whether launch_walk runs the bf16 walker for this dtype and K
 bool bf16_walker_used(bool bf16, int K);
-hipError_t launch_segment_plan(const WalkParams &p, int32_t *seg_base, hipStream_t s);
+hipError_t launch_segment_plan(const WalkParams &p, int32_t *seg_base, int32_t *seg_order, hipStream_t s);
 
 }  // namespace gla

@@ -575,15 +575,24 @@ __global__ __launch_bounds__(256) void gla_state_scan(WalkParams p) {
 }
 
 // ---------------------------------------------------------------- varlen segment plan
-// seg_base[n] = sum over earlier sequences of max(1, ceil(ceil(len/64)/R)).
-__global__ __launch_bounds__(1024) void gla_segment_plan(const int32_t *cu, int N, int R, int32_t *seg_base) {
+// seg_base[n] = sum over earlier sequences of max(1, ceil(ceil(len/64)/R)), and
+// seg_order = the segment ids sorted by length (chunks), longest first, so that
+// workgroups of long segments are dispatched before short ones.  A counting sort
+// over min(length, kOrderBuckets - 1); the order inside a bucket is arbitrary
+// (segments are independent, so results do not depend on it).
+constexpr int kOrderBuckets = 1024;
+
+__global__ __launch_bounds__(1024) void gla_segment_plan(const int32_t *cu, int N, int R, int32_t *seg_base,
+                                                         int32_t *seg_order) {
   __shared__ int32_t part[1024];
   __shared__ int32_t carry;
+  __shared__ int32_t bucket[kOrderBuckets];
   const int tid = threadIdx.x;
   if (tid == 0) {
     carry = 0;
     seg_base[0] = 0;
   }
+  for (int i = tid; i < kOrderBuckets; i += 1024) bucket[i] = 0;
   __syncthreads();
   for (int base = 0; base < N; base += 1024) {
     const int n = base + tid;
@@ -592,6 +601,9 @@ __global__ __launch_bounds__(1024) void gla_segment_plan(const int32_t *cu, int 
       const int len = cu[n + 1] - cu[n];
       const int nc = (len + C - 1) / C;
       cnt = max(1, (nc + R - 1) / R);
+      // segment lengths of this sequence (the walkers cut it the same way)
+      const int sl = (nc + cnt - 1) / cnt;
+      for (int s = 0; s < cnt; ++s) atomicAdd(&bucket[min(max(0, min(sl, nc - s * sl)), kOrderBuckets - 1)], 1);
     }
     part[tid] = cnt;
     __syncthreads();
@@ -605,6 +617,27 @@ __global__ __launch_bounds__(1024) void gla_segment_plan(const int32_t *cu, int 
     __syncthreads();
     if (tid == 1023) carry += part[1023];
     __syncthreads();
+  }
+  // start of each length bucket in the order, longest first (one thread: 1024 adds)
+  if (tid == 0) {
+    int pos = 0;
+    for (int b = kOrderBuckets - 1; b >= 0; --b) {
+      const int c = bucket[b];
+      bucket[b] = pos;
+      pos += c;
+    }
+  }
+  __syncthreads();
+  for (int n = tid; n < N; n += 1024) {
+    const int len = cu[n + 1] - cu[n];
+    const int nc = (len + C - 1) / C;
+    const int cnt = max(1, (nc + R - 1) / R);
+    const int sl = (nc + cnt - 1) / cnt;
+    const int first = seg_base[n];  // written above by this or another thread of the block
+    for (int s = 0; s < cnt; ++s) {
+      const int slot = atomicAdd(&bucket[min(max(0, min(sl, nc - s * sl)), kOrderBuckets - 1)], 1);
+      seg_order[slot] = first + s;
+    }
   }
 }
 
@@ -659,8 +692,8 @@ hipError_t launch_state_scan(const WalkParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_segment_plan(const WalkParams &p, int32_t *seg_base, hipStream_t s) {
-  hipLaunchKernelGGL(gla_segment_plan, dim3(1), dim3(1024), 0, s, p.cu, p.N, p.R, seg_base);
+hipError_t launch_segment_plan(const WalkParams &p, int32_t *seg_base, int32_t *seg_order, hipStream_t s) {
+  hipLaunchKernelGGL(gla_segment_plan, dim3(1), dim3(1024), 0, s, p.cu, p.N, p.R, seg_base, seg_order);
   return hipGetLastError();
 }
 
