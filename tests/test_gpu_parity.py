@@ -94,6 +94,29 @@ def test_packed_sequences(dtype, seg):
     np.testing.assert_array_equal(ht[7], d["h0"][7].astype(np.float64))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_many_packed_sequences(dtype):
+    # more sequences than one pass of the segment-plan workgroup (1024), with a
+    # spread of lengths (empty to several segments) so the segment table, the
+    # longest-first order and the state scan all see multi-block inputs
+    rng = np.random.default_rng(900)
+    lengths = rng.integers(0, 140, size=1500).tolist()
+    lengths[7] = 1300   # one sequence much longer than the others
+    lengths[1200] = 900
+    d = gi.draw(901, 1, 0, 1, 64, 64, dtype=dtype, h0=True, lengths=lengths)
+    _compare(d, dtype, f"{len(lengths)} packed sequences", segment_chunks=3)
+
+
+@pytest.mark.parametrize("vtile", ["64", "128"])
+def test_uneven_packed_lengths(monkeypatch, vtile):
+    # a few long sequences among many short ones: several segments each, short
+    # ones in the tail of the longest-first dispatch
+    monkeypatch.setenv("GLA_BF16_VTILE", vtile)
+    lengths = [1800, 3, 64, 129, 0, 700, 1, 65, 2500, 17, 300, 63]
+    d = gi.draw(902, 1, 0, 2, 128, 128, dtype="bf16", h0=True, lengths=lengths)
+    _compare(d, "bf16", f"uneven packed lengths vtile={vtile}", segment_chunks=5)
+
+
 def test_empty_sequence_batch_returns_h0():
     d = gi.draw(601, 2, 0, 2, 64, 64, dtype="bf16", h0=True)
     o, ht = run_gpu(d, "bf16")
