@@ -238,13 +238,18 @@ def main():
         import oracle
         oracle.build(force=False)
         threads = len(os.sched_getaffinity(0))
-        c0 = time.perf_counter()
-        oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], h0=d["h0"], cu_seqlens=d["cu_seqlens"],
-                             output_final_state=w.ht, threads=threads)
+        # the whole workload, repeated until about 2 s of wall time (bounded at 20 runs)
+        runs, c0 = 0, time.perf_counter()
+        while True:
+            oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], h0=d["h0"], cu_seqlens=d["cu_seqlens"],
+                                 output_final_state=w.ht, threads=threads)
+            runs += 1
+            if time.perf_counter() - c0 >= 2.0 or runs >= 20:
+                break
         c1 = time.perf_counter()
-        cpu = {"value": n_tokens / (c1 - c0), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        cpu = {"value": runs * n_tokens / (c1 - c0), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"the whole workload ({n_tokens} tokens x {w.H} heads), fp64 token recurrence, "
-                         f"one run, {c1 - c0:.2f} s"}
+                         f"{runs} runs in {c1 - c0:.2f} s"}
 
     segmented = call.ws_bytes > 0
     line = {
