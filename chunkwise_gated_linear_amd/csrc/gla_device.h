@@ -128,6 +128,10 @@ __device__ __forceinline__ u32x2_t buf_ld64(__amdgpu_buffer_rsrc_t r, int off) {
 __device__ __forceinline__ void buf_st128(__amdgpu_buffer_rsrc_t r, int off, u32x4_t v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off, 0, 0);
 }
+// Nontemporal store (cache policy NT): for output written once and not read back.
+__device__ __forceinline__ void buf_st128_nt(__amdgpu_buffer_rsrc_t r, int off, u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off, 0, 2);
+}
 __device__ __forceinline__ void buf_st64(__amdgpu_buffer_rsrc_t r, int off, u32x2_t v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, off, 0, 0);
 }

@@ -74,8 +74,10 @@ struct LdsW {
   static constexpr int KS = VW == 64 ? 2 : 1;
   static constexpr int PBYTES = KS == 2 ? 2 * 4 * 2 * 1024 : 0;  // o^T partial tiles [cw][it][nt], 16 B per lane
   static constexpr int oP = oA + (OUT ? 2 * APL : 0);      // partial o^T exchanged between key halves (OUT)
-  static constexpr int oDec = oP + (OUT ? PBYTES : 0);     // a [K]
-  static constexpr int BYTES = oDec + 4 * KD;
+  static constexpr int oS = oP + (OUT ? PBYTES : 0);       // bf16 output tile [token][n], staged for row stores (OUT)
+  static constexpr int oDec = oS + (OUT ? VPL : 0);        // a [K]
+  static constexpr int oF = oDec + 4 * KD;                 // score-ready chunk index per matrix wave (OUT)
+  static constexpr int BYTES = oF + 16;
 
   // Swizzled byte offsets.  On gfx950 an LDS access is served 32 lanes at a
   // time (16 for writes) without bank conflicts when the lanes' addresses,
@@ -89,6 +91,7 @@ struct LdsW {
   //   v:       32 B pair ^ (b1 | b3 << 1), 64 columns; ^ (b0 | b1 << 1 | b3 << 2),
   //            128 columns -- transpose reads, whole-row writes
   //   A:       16 B chunk ^ (b0 | b2 << 1 | b3 << 2) -- row fragments, 8 B writes
+  //   output:  16 B chunk ^ (row & 7) -- whole-row reads; the 8 B tile writes take two passes
   static __device__ __forceinline__ int sqk(int row) {
     const int b1 = (row >> 1) & 1, b2 = (row >> 2) & 1, b3 = (row >> 3) & 1;
     return KD == 128 ? (b2 << 1) | ((b1 ^ b3) << 2) | (b3 << 3) : (b2 << 1) | (b3 << 2);
@@ -101,11 +104,32 @@ struct LdsW {
                            : (row & 1) | (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2);
     return row * VROW + (((byte >> 5) ^ s) << 5) + (byte & 31);
   }
+  static __device__ __forceinline__ int so(int row, int byte) {  // 16 B chunk ^ (row & 7)
+    return row * VROW + (((byte >> 4) ^ (row & 7)) << 4) + (byte & 15);
+  }
   static __device__ __forceinline__ int ao(int row, int byte) {
     const int s = (row & 1) | (((row >> 2) & 1) << 1) | (((row >> 3) & 1) << 2);
     return row * AROW + (((byte >> 4) ^ s) << 4) + (byte & 15);
   }
 };
+
+// The matrix waves share their score tiles among themselves only, so they meet
+// through per-wave chunk counters in LDS instead of a workgroup barrier (which
+// would also hold the producer waves): each wave publishes chunk c once its
+// tiles are written, then waits until all four have.  The wait is bounded so
+// that a wave always leaves it.
+__device__ __forceinline__ void scores_handoff(char *flags, int mw, int c) {
+  int *f = reinterpret_cast<int *>(flags);
+  __hip_atomic_store(f + mw, c, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);  // every lane: its own writes
+  for (int spin = 0; spin < (1 << 22); ++spin) {
+    const int m = min(min(__hip_atomic_load(f + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP),
+                          __hip_atomic_load(f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)),
+                      min(__hip_atomic_load(f + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP),
+                          __hip_atomic_load(f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)));
+    if (__builtin_amdgcn_readfirstlane(m) >= c) break;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
 // Score tiles (i-tile, j-tile) of the 64 x 64 lower triangle per matrix wave.
 template <int W> struct Tiles;
@@ -166,6 +190,9 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   constexpr int KH = KD / KS;       // state rows per matrix wave
   constexpr int NKT = KH / 16;      // 16-row k tiles per matrix wave
   constexpr int NKB = KH / 32;      // 32-wide k blocks per matrix wave
+  // 64-column output workgroups share score tiles through LDS counters (the
+  // producers skip that meeting); 128-column ones use a workgroup barrier
+  constexpr bool HANDOFF = OUT && VW == 64;
   static_assert(KD == 64 || KD == 128, "bf16 walker covers K = 64, 128");
   static_assert(NG * QPW == 64 && RPG * NG == C, "producer mapping");
 
@@ -224,6 +251,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   if (OUT) {  // score tiles above the diagonal are read as zeros and never written
     for (int i = tid; i < 2 * L::APL / 16; i += L::THREADS)
       lds_st<u32x4_t>(smem + L::oA, 16 * i, u32x4_t{0, 0, 0, 0});
+    if (tid < 4) lds_st<int>(smem + L::oF, 4 * tid, c_begin - 1);
   }
   // Per-lane LDS offsets; the compile-time parts (row tiles, token blocks, the
   // 8 B half of a chunk) are added at the access and do not change the swizzle.
@@ -265,6 +293,8 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   u32x2_t gQh[RPG], gQl[RPG], gKh[RPG], gKl[RPG];
   f32x4_t gDec = {1.f, 1.f, 1.f, 1.f};
   float gPl[RPG][4], gRl[RPG][4], gSuf[4], gFq[4];
+  float tQ[RPG][4], tK[RPG][4];  // q P, k R of a row (factors inside the row group)
+  float incl[4], shf[4];         // running products across row groups, shuffled values
   float seg_decay[4] = {1.f, 1.f, 1.f, 1.f};
   const float scale = p.scale;
 
@@ -294,9 +324,9 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
     rgK[i] = buf_ld64(r.k, voff_k + i * step_k);
     if (OUT) rgQ[i] = buf_ld64(r.q, voff_k + i * step_k);
   };
-  // gate, stage 1: exp(g), running products inside the row group and across row
-  // groups (lane shuffles inside the wave), chunk decay and the q / k factors
-  auto gate_decays = [&]() {
+  // gate, stage 1a: exp(g) and the running products inside the row group; the
+  // raw g registers are free afterwards
+  auto gate_local = [&]() {
     float E[RPG][4];
 #pragma unroll
     for (int r = 0; r < RPG; ++r)
@@ -310,19 +340,23 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       gRl[RPG - 1][j] = 1.f;
 #pragma unroll
       for (int r = RPG - 2; r >= 0; --r) gRl[r][j] = gRl[r + 1][j] * E[r + 1][j];
+      incl[j] = gPl[RPG - 1][j];
     }
-    float incl[4];
+  };
+  // gate, stage 1b: running products across row groups, an inclusive scan over
+  // the NG row groups with lane shuffles inside the wave (log2 NG rounds; each
+  // round's shuffles are issued, independent work runs, then they are used)
+  auto scan_issue = [&](int d) {
+    const int src = (lane - d * QPW) < 0 ? lane : lane - d * QPW;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) incl[j] = gPl[RPG - 1][j];
+    for (int j = 0; j < 4; ++j) shf[j] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(incl[j])));
+  };
+  auto scan_use = [&](int d) {
 #pragma unroll
-    for (int d = 1; d < NG; d *= 2) {
-      const int src = (lane - d * QPW) < 0 ? lane : lane - d * QPW;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float y = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(incl[j])));
-        incl[j] *= (rg >= d) ? y : 1.f;
-      }
-    }
+    for (int j = 0; j < 4; ++j) incl[j] *= (rg >= d) ? shf[j] : 1.f;
+  };
+  // gate, stage 1c: chunk decay and the q / k factors from the scan
+  auto gate_decays = [&]() {
     const int src_pre = rg > 0 ? lane - QPW : lane;
     const int src_tot = (NG - 1) * QPW + lane % QPW;
 #pragma unroll
@@ -339,23 +373,25 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       for (int j = 0; j < 4; ++j) seg_decay[j] *= gDec[j];
     }
   };
-  // gate, stage 2: gated and split q, k of row i; the raw registers of the row are
-  // then free for the next load
+  // gate, stage 2a: q, k of row r times their factors inside the row group (needs
+  // no scan); the raw registers of the row are then free for the next load
+  auto gate_part = [&](int r) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tK[r][j] = ((j & 1) ? bf_hi(rgK[r][j >> 1]) : bf_lo(rgK[r][j >> 1])) * gRl[r][j];
+      if (OUT) tQ[r][j] = ((j & 1) ? bf_hi(rgQ[r][j >> 1]) : bf_lo(rgQ[r][j >> 1])) * gPl[r][j];
+    }
+  };
+  // gate, stage 2b: gated and split q, k of row r
   auto gate_row = [&](int r) {
     float kc[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float kk = (j & 1) ? bf_hi(rgK[r][j >> 1]) : bf_lo(rgK[r][j >> 1]);
-      kc[j] = kk * (gRl[r][j] * gSuf[j]);
-    }
+    for (int j = 0; j < 4; ++j) kc[j] = tK[r][j] * gSuf[j];
     split4(kc, gKh[r], gKl[r]);
     if (OUT) {
       float qc[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float qq = (j & 1) ? bf_hi(rgQ[r][j >> 1]) : bf_lo(rgQ[r][j >> 1]);
-        qc[j] = qq * (gPl[r][j] * gFq[j]);
-      }
+      for (int j = 0; j < 4; ++j) qc[j] = tQ[r][j] * gFq[j];
       split4(qc, gQh[r], gQl[r]);
     }
   };
@@ -381,23 +417,36 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
     lds_st<u32x2_t>(sq + L::QPL, off, gQl[r]);
   };
 
-  // Output of chunk c from o^T tiles: lane = token 16 it + l16, columns VQ cw +
-  // 16 nt + 4 lg .. + 3, rounded to bf16 (8 B per lane and tile).
+  // Output of a chunk: the o^T tiles (lane = token 16 it + l16, columns VQ cw +
+  // 16 nt + 4 lg .. + 3) are rounded to bf16 and staged in LDS; after the next
+  // barrier each matrix wave stores 16 whole rows of the tile (VW / 8 lanes of
+  // 16 B per row), so every store fills complete cache lines.
   auto o_rsrc = [&](int c) {
     const int64_t t0 = (int64_t)seq_bos + (int64_t)c * C;
     const int64_t valid = min(C, seq_len - c * C);
     const int64_t headV = (int64_t)h * V + v0;
     return make_rsrc((uint16_t *)p.o + t0 * rowV + headV, (valid * rowV - headV) * 2);
   };
-  auto store_tile = [&](const __amdgpu_buffer_rsrc_t &rO, int it, int nt, const f32x4_t &x) {
+  auto stage_tile = [&](int it, int nt, const f32x4_t &x) {
     const int col = VQ * cw + 16 * nt + 4 * lg;
     const u32x2_t w = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
-    buf_st64(rO, (int)(((16 * it + l16) * rowV + col) * 2), w);
+    lds_st<u32x2_t>(smem + L::oS, L::so(16 * it + l16, 2 * col), w);
+  };
+  auto store_staged = [&](int cs) {
+    constexpr int LPR = VW / 8, RPI = 64 / LPR;  // lanes per row, rows per store
+    const __amdgpu_buffer_rsrc_t rO = o_rsrc(cs);
+#pragma unroll
+    for (int i = 0; i < 16 / RPI; ++i) {
+      const int row = 16 * mw + RPI * i + lane / LPR, ch = lane % LPR;
+      buf_st128_nt(rO, (int)((row * rowV + 8 * ch) * 2), lds_ld<u32x4_t>(smem + L::oS, L::so(row, 16 * ch)));
+    }
   };
 
   // Producer and matrix waves run separate loops (different register sets);
   // both meet the same barriers per chunk: operands written | scores written
-  // (OUT) | chunk done.
+  // (128-column output workgroups only) | chunk done.  64-column workgroups hand
+  // the score tiles between matrix waves through LDS counters instead, so the
+  // producers run on.
   if (producer) {
     if (c_begin < c_end) {  // pipeline fill: chunk c_begin gated, chunk c_begin+1 loading
       const Rsrc r0 = rsrc(c_begin);
@@ -405,6 +454,12 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       load_v(r0);
 #pragma unroll
       for (int i = 0; i < RPG; ++i) load_qk_row(r0, i);
+      gate_local();
+#pragma unroll
+      for (int d = 1; d < NG; d *= 2) {
+        scan_issue(d);
+        scan_use(d);
+      }
       gate_decays();
       write_v(c_begin);
       const Rsrc r1 = rsrc(c_begin + 1);
@@ -412,6 +467,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       load_v(r1);
 #pragma unroll
       for (int i = 0; i < RPG; ++i) {
+        gate_part(i);
         gate_row(i);
         if constexpr (OUT && L::NQB == 2) write_q_row(c_begin, i);
         load_qk_row(r1, i);
@@ -425,16 +481,60 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       }
       phase_barrier();  // operands of chunk c visible
       const Rsrc r2 = rsrc(c + 2);
-      gate_decays();    // chunk c+1
+      gate_local();     // chunk c+1
       load_g(r2);
-      if constexpr (OUT) phase_barrier();  // scores visible
-      write_v(c + 1);
-      load_v(r2);
+      if constexpr (OUT && !HANDOFF) {
+        // 128-column workgroups: the scan as one step, then the rows (the
+        // interleaved form below needs more registers than they have left)
+#pragma unroll
+        for (int d = 1; d < NG; d *= 2) {
+          scan_issue(d);
+          scan_use(d);
+        }
+        gate_decays();
+        phase_barrier();  // scores visible
+        write_v(c + 1);
+        load_v(r2);
+#pragma unroll
+        for (int i = 0; i < RPG; ++i) {
+          gate_part(i);
+          gate_row(i);    // chunk c+1
+          load_qk_row(r2, i);
+        }
+        phase_barrier();  // chunk c done
+        continue;
+      }
+      // the scan rounds wait on lane shuffles; the row products of the group,
+      // the next raw loads and the v copy fill those waits
+      constexpr int LOGNG = NG == 8 ? 3 : NG == 16 ? 4 : NG == 4 ? 2 : 5;
+      static_assert((1 << LOGNG) == NG, "row groups");
+#pragma unroll
+      for (int ri = 0; ri < LOGNG; ++ri) {
+        scan_issue(1 << ri);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ri == 0 || ri == 1) {
+#pragma unroll
+          for (int i = ri * RPG / 2; i < (ri + 1) * RPG / 2; ++i) {
+            gate_part(i);
+            load_qk_row(r2, i);
+          }
+        }
+        if (ri == 2) {
+          write_v(c + 1);
+          load_v(r2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        scan_use(1 << ri);
+      }
+      if constexpr (LOGNG < 3) {
+        write_v(c + 1);
+        load_v(r2);
+      }
+      gate_decays();
 #pragma unroll
       for (int i = 0; i < RPG; ++i) {
         gate_row(i);    // chunk c+1
         if constexpr (OUT && L::NQB == 2) write_q_row(c + 1, i);
-        load_qk_row(r2, i);
       }
       phase_barrier();  // chunk c done
     }
@@ -443,13 +543,15 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       const char *sq = smem + L::qbuf(c);  // qc of chunk c
       phase_barrier();  // operands of chunk c visible
       if constexpr (OUT) {
+        if (c > c_begin) store_staged(c - 1);
         switch (mw) {
           case 0: scores<KD, VW, 0>(smem, sq, rf, l16, lg); break;
           case 1: scores<KD, VW, 1>(smem, sq, rf, l16, lg); break;
           case 2: scores<KD, VW, 2>(smem, sq, rf, l16, lg); break;
           default: scores<KD, VW, 3>(smem, sq, rf, l16, lg); break;
         }
-        phase_barrier();  // scores visible
+        if constexpr (HANDOFF) scores_handoff(smem + L::oF, mw, c);
+        else phase_barrier();  // scores visible
       }
       const char *sv = smem + L::oV + (c & 1) * L::VPL;  // v of chunk c
       // ---- S' = diag(a) S
@@ -525,11 +627,12 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
           }
         }
         if constexpr (KS == 1) {
-          const __amdgpu_buffer_rsrc_t rO = o_rsrc(c);
+          // every wave has read the previous staged tile before it published its
+          // score tiles, so the staging area is free once the hand-off is done
 #pragma unroll
           for (int it = 0; it < 4; ++it)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) store_tile(rO, it, nt, o[it][nt]);
+            for (int nt = 0; nt < NT; ++nt) stage_tile(it, nt, o[it][nt]);
         } else {
           // keep tile nt = kh, send tile 1 - kh to the partner key half
 #pragma unroll
@@ -562,18 +665,21 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       }
       phase_barrier();  // chunk c's operands are no longer read; partial outputs visible
       if constexpr (OUT && KS == 2) {
-        const __amdgpu_buffer_rsrc_t rO = o_rsrc(c);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
           const f32x4_t part = lds_ld<f32x4_t>(smem + L::oP, ((cw * 4 + it) * 2 + kh) * 1024 + 16 * lane);
-          store_tile(rO, it, kh, f32x4_t{keep[it][0] + part[0], keep[it][1] + part[1], keep[it][2] + part[2],
-                                         keep[it][3] + part[3]});
+          stage_tile(it, kh, f32x4_t{keep[it][0] + part[0], keep[it][1] + part[1], keep[it][2] + part[2],
+                                     keep[it][3] + part[3]});
         }
       }
     }
   }
 
   // ================= results of the segment
+  if constexpr (OUT) {  // the last staged output tile
+    phase_barrier();
+    if (!producer && c_begin < c_end) store_staged(c_end - 1);
+  }
   if (!producer) {
     float *dst = nullptr;
     if (OUT) {
