@@ -120,7 +120,8 @@ struct LdsW {
 // that a wave always leaves it.
 __device__ __forceinline__ void scores_handoff(char *flags, int mw, int c) {
   int *f = reinterpret_cast<int *>(flags);
-  __hip_atomic_store(f + mw, c, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);  // every lane: its own writes
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __hip_atomic_store(f + mw, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   for (int spin = 0; spin < (1 << 22); ++spin) {
     const int m = min(min(__hip_atomic_load(f + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP),
                           __hip_atomic_load(f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)),
@@ -128,7 +129,7 @@ __device__ __forceinline__ void scores_handoff(char *flags, int mw, int c) {
                           __hip_atomic_load(f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)));
     if (__builtin_amdgcn_readfirstlane(m) >= c) break;
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Score tiles (i-tile, j-tile) of the 64 x 64 lower triangle per matrix wave.
