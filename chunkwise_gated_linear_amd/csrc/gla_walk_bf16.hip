@@ -120,6 +120,8 @@ struct LdsW {
 // that a wave always leaves it.
 __device__ __forceinline__ void scores_handoff(char *flags, int mw, int c) {
   int *f = reinterpret_cast<int *>(flags);
+  // release for LDS only: the wave's outstanding global loads and stores are not
+  // waited for
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __hip_atomic_store(f + mw, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   for (int spin = 0; spin < (1 << 22); ++spin) {
