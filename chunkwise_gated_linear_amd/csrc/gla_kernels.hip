@@ -618,14 +618,21 @@ __global__ __launch_bounds__(1024) void gla_segment_plan(const int32_t *cu, int 
     if (tid == 1023) carry += part[1023];
     __syncthreads();
   }
-  // start of each length bucket in the order, longest first (one thread: 1024 adds)
-  if (tid == 0) {
-    int pos = 0;
-    for (int b = kOrderBuckets - 1; b >= 0; --b) {
-      const int c = bucket[b];
-      bucket[b] = pos;
-      pos += c;
+  // start of each length bucket in the order, longest first: an exclusive scan
+  // over the buckets from the longest down, one bucket per thread
+  static_assert(kOrderBuckets == 1024, "one bucket per thread");
+  {
+    const int b = kOrderBuckets - 1 - tid;
+    const int cnt = bucket[b];
+    part[tid] = cnt;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+      const int add = tid >= d ? part[tid - d] : 0;
+      __syncthreads();
+      part[tid] += add;
+      __syncthreads();
     }
+    bucket[b] = part[tid] - cnt;
   }
   __syncthreads();
   for (int n = tid; n < N; n += 1024) {
