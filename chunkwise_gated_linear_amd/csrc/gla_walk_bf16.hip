@@ -679,27 +679,41 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   }
 
   // ================= results of the segment
+  // The final state (ht, or the segment summary) leaves through LDS as whole
+  // rows: after the last chunk nothing reads the operand area at offset 0, so
+  // the matrix waves write S there as [K][VW] fp32 (16 consecutive columns per
+  // 16 lanes: conflict-free), and after a barrier every wave stores rows of
+  // VW / 4 lanes x 16 B.
+  float *dst = nullptr;
+  if (OUT) {
+    if (p.ht != nullptr && si.s == si.nseg - 1) dst = p.ht + ((int64_t)si.n * H + h) * KD * V;
+  } else {
+    dst = p.seg_state + ((int64_t)(si.first + si.s) * H + h) * KD * V;
+  }
+  static_assert(KD * VW * 4 <= (OUT ? L::oS : L::oDec), "state staging must not overlap the output staging");
+  if (dst != nullptr && !producer) {
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          lds_st<float>(smem, 4 * ((KH * kh + 16 * kt + 4 * lg + r) * VW + VQ * cw + 16 * nt + l16), S[kt][nt][r]);
+  }
+  if (OUT || dst != nullptr) phase_barrier();  // staged output tile and state visible
   if constexpr (OUT) {  // the last staged output tile
-    phase_barrier();
     if (!producer && c_begin < c_end) store_staged(c_end - 1);
   }
-  if (!producer) {
-    float *dst = nullptr;
-    if (OUT) {
-      if (p.ht != nullptr && si.s == si.nseg - 1) dst = p.ht + ((int64_t)si.n * H + h) * KD * V;
-    } else {
-      dst = p.seg_state + ((int64_t)(si.first + si.s) * H + h) * KD * V;
+  if (dst != nullptr) {
+    constexpr int LPR = VW / 4, RPI = 64 / LPR;  // lanes per state row, rows per store
+    const int rr = lane / LPR, ch = lane % LPR;
+#pragma unroll
+    for (int i = wave; i < KD / RPI; i += L::THREADS / 64) {
+      const int row = RPI * i + rr;
+      *reinterpret_cast<f32x4_t *>(dst + (int64_t)row * V + v0 + 4 * ch) = lds_ld<f32x4_t>(smem, 16 * (row * LPR + ch));
     }
-    if (dst) {
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            dst[(int64_t)(KH * kh + 16 * kt + 4 * lg + r) * V + v0 + VQ * cw + 16 * nt + l16] = S[kt][nt][r];
-    }
-  } else if (!OUT && vt == 0 && rg == 0) {
+  }
+  if (producer && !OUT && vt == 0 && rg == 0) {
     const int slot = si.first + si.s;
     *reinterpret_cast<f32x4_t *>(p.seg_decay + ((int64_t)slot * H + h) * KD + 4 * cq) =
         f32x4_t{seg_decay[0], seg_decay[1], seg_decay[2], seg_decay[3]};
