@@ -116,20 +116,26 @@ struct LdsW {
 // The matrix waves share their score tiles among themselves only, so they meet
 // through per-wave chunk counters in LDS instead of a workgroup barrier (which
 // would also hold the producer waves): each wave publishes chunk c once its
-// tiles are written, then waits until all four have.  The wait is bounded so
-// that a wave always leaves it.
-__device__ __forceinline__ void scores_handoff(char *flags, int mw, int c) {
+// tiles are written, does the work that needs no other wave's tiles, then waits
+// until all four have published.  The wait is bounded so that a wave always
+// leaves it, and sleeps between polls so that it takes no issue slots or LDS
+// cycles from the producer wave on its SIMD.
+__device__ __forceinline__ void scores_publish(char *flags, int mw, int c) {
   int *f = reinterpret_cast<int *>(flags);
   // release for LDS only: the wave's outstanding global loads and stores are not
   // waited for
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __hip_atomic_store(f + mw, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void scores_wait(char *flags, int c) {
+  int *f = reinterpret_cast<int *>(flags);
   for (int spin = 0; spin < (1 << 22); ++spin) {
     const int m = min(min(__hip_atomic_load(f + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP),
                           __hip_atomic_load(f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)),
                       min(__hip_atomic_load(f + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP),
                           __hip_atomic_load(f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)));
     if (__builtin_amdgcn_readfirstlane(m) >= c) break;
+    __builtin_amdgcn_s_sleep(1);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
@@ -384,6 +390,16 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       tK[r][j] = ((j & 1) ? bf_hi(rgK[r][j >> 1]) : bf_lo(rgK[r][j >> 1])) * gRl[r][j];
       if (OUT) tQ[r][j] = ((j & 1) ? bf_hi(rgQ[r][j >> 1]) : bf_lo(rgQ[r][j >> 1])) * gPl[r][j];
     }
+    // The products must exist before the row's next raw load is issued: if the
+    // compiler defers them, the raw registers stay live, the next load goes to
+    // other registers, and the copy back at the end of the chunk loop waits for
+    // that load to arrive (a full memory latency on the path to the next chunk).
+    if constexpr (OUT) {
+      asm volatile("" ::"v"(tK[r][0]), "v"(tK[r][1]), "v"(tK[r][2]), "v"(tK[r][3]), "v"(tQ[r][0]), "v"(tQ[r][1]),
+                   "v"(tQ[r][2]), "v"(tQ[r][3]) : "memory");
+    } else {
+      asm volatile("" ::"v"(tK[r][0]), "v"(tK[r][1]), "v"(tK[r][2]), "v"(tK[r][3]) : "memory");
+    }
   };
   // gate, stage 2b: gated and split q, k of row r
   auto gate_row = [&](int r) {
@@ -553,7 +569,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
           case 2: scores<KD, VW, 2>(smem, sq, rf, l16, lg); break;
           default: scores<KD, VW, 3>(smem, sq, rf, l16, lg); break;
         }
-        if constexpr (HANDOFF) scores_handoff(smem + L::oF, mw, c);
+        if constexpr (HANDOFF) scores_publish(smem + L::oF, mw, c);
         else phase_barrier();  // scores visible
       }
       const char *sv = smem + L::oV + (c & 1) * L::VPL;  // v of chunk c
@@ -584,24 +600,6 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
         for (int it = 0; it < 4; ++it)
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) o[it][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        // ---- o^T += v^T A^T over the 32-token blocks on or below the diagonal
-        // (with two key halves, half kh takes token block kh; kh is uniform)
-        auto av = [&](auto jbc) {
-          constexpr int jb = decltype(jbc)::value;
-#pragma unroll
-          for (int it = 2 * jb; it < 4; ++it) {
-            const int off = aoff[jb] + 16 * it * L::AROW;
-            const u32x4_t ah = lds_ld<u32x4_t>(smem + L::oA, off);
-            const u32x4_t al = lds_ld<u32x4_t>(smem + L::oA + L::APL, off);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-              o[it][nt] = mfma_bf(vf[nt][jb], al, o[it][nt]);
-              o[it][nt] = mfma_bf(vf[nt][jb], ah, o[it][nt]);
-            }
-          }
-        };
-        if (KS == 1 || kh == 0) av(std::integral_constant<int, 0>{});
-        if (KS == 1 || kh == 1) av(std::integral_constant<int, 1>{});
         // ---- o^T += S'^T qc^T (S' from the accumulators, split hi + lo)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -629,6 +627,26 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
             }
           }
         }
+        // ---- o^T += v^T A^T over the 32-token blocks on or below the diagonal
+        // (with two key halves, half kh takes token block kh; kh is uniform)
+        auto av = [&](auto jbc) {
+          constexpr int jb = decltype(jbc)::value;
+#pragma unroll
+          for (int it = 2 * jb; it < 4; ++it) {
+            const int off = aoff[jb] + 16 * it * L::AROW;
+            const u32x4_t ah = lds_ld<u32x4_t>(smem + L::oA, off);
+            const u32x4_t al = lds_ld<u32x4_t>(smem + L::oA + L::APL, off);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              o[it][nt] = mfma_bf(vf[nt][jb], al, o[it][nt]);
+              o[it][nt] = mfma_bf(vf[nt][jb], ah, o[it][nt]);
+            }
+          }
+        };
+        // the other waves' score tiles are needed from here on
+        if constexpr (HANDOFF) scores_wait(smem + L::oF, c);
+        if (KS == 1 || kh == 0) av(std::integral_constant<int, 0>{});
+        if (KS == 1 || kh == 1) av(std::integral_constant<int, 1>{});
         if constexpr (KS == 1) {
           // every wave has read the previous staged tile before it published its
           // score tiles, so the staging area is free once the hand-off is done
