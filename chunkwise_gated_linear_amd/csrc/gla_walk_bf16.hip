@@ -63,11 +63,15 @@ struct LdsW {
   // each row of chunk c+1 as soon as it is gated), one for 128 columns (there
   // the second buffer's registers and LDS cost more than the earlier writes save)
   static constexpr int NQB = VW == 64 ? 2 : 1;
-  static constexpr int oQ = 0;                                  // qc hi, lo per buffer (OUT)
-  static constexpr int oK = oQ + (OUT ? 2 * NQB * QPL : 0);     // kc hi, lo
+  // kc comes first: the producers write it between two barriers, on the path
+  // from one chunk to the next, and below 64 KiB its LDS stores take immediate
+  // offsets (a store past that needs an address add into a temporary register,
+  // and the next store then waits until the previous one has read it)
+  static constexpr int oK = 0;                                  // kc hi, lo
+  static constexpr int oQ = oK + 2 * QPL;                       // qc hi, lo per buffer (OUT)
   static constexpr int qbuf(int c) { return oQ + (NQB == 2 ? (c & 1) : 0) * 2 * QPL; }
   static constexpr int VPL = C * VROW;
-  static constexpr int oV = oK + 2 * QPL;                 // v [token][n], two chunks
+  static constexpr int oV = oQ + (OUT ? 2 * NQB * QPL : 0);  // v [token][n], two chunks
   static constexpr int oA = oV + 2 * VPL;                 // A hi, lo [i][j]        (OUT)
   // 64-column workgroups split the state rows in two key halves whose partial
   // outputs meet in LDS; 128-column workgroups give each wave all K rows.
