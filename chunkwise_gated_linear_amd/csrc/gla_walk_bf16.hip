@@ -566,7 +566,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       const char *sq = smem + L::qbuf(c);  // qc of chunk c
       phase_barrier();  // operands of chunk c visible
       if constexpr (OUT) {
-        if (c > c_begin) store_staged(c - 1);
+        if (KS == 2 && c > c_begin) store_staged(c - 1);
         switch (mw) {
           case 0: scores<KD, VW, 0>(smem, sq, rf, l16, lg); break;
           case 1: scores<KD, VW, 1>(smem, sq, rf, l16, lg); break;
@@ -689,6 +689,9 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
         }
       }
       phase_barrier();  // chunk c's operands are no longer read; partial outputs visible
+      // 128-column workgroups staged this chunk's tile before the barrier: store
+      // it now, while the producers write the next chunk's operands
+      if constexpr (OUT && KS == 1) store_staged(c);
       if constexpr (OUT && KS == 2) {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -723,7 +726,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
           lds_st<float>(smem, 4 * ((KH * kh + 16 * kt + 4 * lg + r) * VW + VQ * cw + 16 * nt + l16), S[kt][nt][r]);
   }
   if (OUT || dst != nullptr) phase_barrier();  // staged output tile and state visible
-  if constexpr (OUT) {  // the last staged output tile
+  if constexpr (OUT && KS == 2) {  // the last staged output tile
     if (!producer && c_begin < c_end) store_staged(c_end - 1);
   }
   if (dst != nullptr) {
