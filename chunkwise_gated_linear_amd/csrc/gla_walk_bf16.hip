@@ -9,18 +9,21 @@
 //   qc_i = scale q_i P_i / a,  kc_j = k_j R_j    (P, R: running products of exp(g))
 //   A = mask_{j<=i}(qc kc^T),  S' = diag(a) S,  o = A v + qc S',  S = S' + kc^T v
 //
-// Layout for gfx950 (one workgroup of 8 waves per (segment, head, 64-column
-// slice of V), two waves per SIMD):
+// Layout for gfx950 (one workgroup of 8 waves per (segment, head, 64- or
+// 128-column slice of V), two waves per SIMD):
 //  * Waves 4-7 produce: they load the raw q, k, g, v of chunk c+2, form the
 //    gated and split operands of chunk c+1 in registers and write them to LDS
-//    when chunk c is done.  Their memory stalls and vector work run beside the
-//    matrix waves on the same SIMDs.
-//  * Waves 0-3 compute.  They tile the K x 64 state slice as 2 key halves x 2
-//    value halves (32 columns) and keep it in MFMA accumulators.  Each
+//    (qc row by row as it is gated, kc when chunk c is done).  Their memory
+//    stalls and vector work run beside the matrix waves on the same SIMDs.
+//  * Waves 0-3 compute.  With 64 columns they tile the K x 64 state slice as
+//    2 key halves x 2 value halves (32 columns); with 128 columns each holds
+//    all K rows of 32 columns; the state stays in MFMA accumulators.  Each
 //    computes some of the ten lower 16x16 score tiles (shared through LDS),
-//    then a partial output over its key half (A v for one 32-token block of
-//    every row tile, qc S' over its key half) and its state update.  The two
-//    key-half partials meet in LDS and are summed by the store pass.
+//    then its output tiles: qc S' first (it needs no other wave's tiles), then
+//    A v once every wave's tiles are there, then its state update.  With 64
+//    columns the two key-half partials meet in LDS and are summed after the
+//    chunk-done barrier; with 128 columns each wave stages whole tiles, which
+//    are stored right after that barrier.
 //  * kc^T and v are read as MFMA operands with the LDS transpose read
 //    ds_read_b64_tr_b16, so no transposed copy is written.
 //  * Global traffic uses per-chunk buffer descriptors: rows past the end of a
