@@ -27,12 +27,32 @@ __device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// x rounded to bf16 (nearest-even), as a float: the conversion writes the bf16
+// into the upper half of the word over a zero lower half, which is that float.
+// (Written out because the compiler otherwise forms it from the packed pair as
+// a second conversion plus a shift.)  The compiler does not insert wait states
+// before inline asm, so x must come from ordinary VALU arithmetic, never
+// straight from an MFMA result or a transcendental.
+__device__ __forceinline__ float bf16_round_valu(float x) {
+  float r;
+  asm("v_cvt_pk_bf16_f32 %0, 0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
 // Split 4 floats into bf16 hi (nearest) and bf16 lo (nearest of the remainder).
 __device__ __forceinline__ void split4(const float x[4], u32x2_t &hi, u32x2_t &lo) {
   hi[0] = pack_bf16(x[0], x[1]);
   hi[1] = pack_bf16(x[2], x[3]);
   lo[0] = pack_bf16(x[0] - bf_lo(hi[0]), x[1] - bf_hi(hi[0]));
   lo[1] = pack_bf16(x[2] - bf_lo(hi[1]), x[3] - bf_hi(hi[1]));
+}
+// The same split for x computed by ordinary VALU arithmetic (see
+// bf16_round_valu): one instruction fewer per pair.
+__device__ __forceinline__ void split4_valu(const float x[4], u32x2_t &hi, u32x2_t &lo) {
+  hi[0] = pack_bf16(x[0], x[1]);
+  hi[1] = pack_bf16(x[2], x[3]);
+  lo[0] = pack_bf16(x[0] - bf16_round_valu(x[0]), x[1] - bf_hi(hi[0]));
+  lo[1] = pack_bf16(x[2] - bf16_round_valu(x[2]), x[3] - bf_hi(hi[1]));
 }
 
 __device__ __forceinline__ f32x4_t mfma_bf(u32x4_t a, u32x4_t b, f32x4_t c) {

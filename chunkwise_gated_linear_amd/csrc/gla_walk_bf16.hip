@@ -413,12 +413,12 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
     float kc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) kc[j] = tK[r][j] * gSuf[j];
-    split4(kc, gKh[r], gKl[r]);
+    split4_valu(kc, gKh[r], gKl[r]);  // kc, qc: products of VALU multiplies
     if (OUT) {
       float qc[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) qc[j] = tQ[r][j] * gFq[j];
-      split4(qc, gQh[r], gQl[r]);
+      split4_valu(qc, gQh[r], gQl[r]);
     }
   };
   // v goes to LDS straight from the load registers (two chunk buffers)
