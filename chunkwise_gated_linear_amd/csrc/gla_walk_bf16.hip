@@ -616,8 +616,8 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
             const float s8[8] = {S[2 * kb][nt][0], S[2 * kb][nt][1], S[2 * kb][nt][2], S[2 * kb][nt][3],
                                  S[2 * kb + 1][nt][0], S[2 * kb + 1][nt][1], S[2 * kb + 1][nt][2], S[2 * kb + 1][nt][3]};
             u32x2_t h0, l0, h1, l1;
-            split4(s8, h0, l0);
-            split4(s8 + 4, h1, l1);
+            split4_valu(s8, h0, l0);  // S' = a S: products of VALU multiplies
+            split4_valu(s8 + 4, h1, l1);
             sh[nt] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
             sl[nt] = u32x4_t{l0[0], l0[1], l1[0], l1[1]};
           }
