@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import gla_inputs as gi
-from gpu_helpers import TOL, check_close, rounding_floor, run_gpu, run_oracle, say
+from gpu_helpers import TOL, check_close, rounding_floor, run_gpu, run_oracle, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -177,3 +177,36 @@ def test_invalid_arguments_raise():
     cu = torch.tensor([0, 4, 8], dtype=torch.int32, device=dev)
     with pytest.raises(ValueError):
         gla.gla_fwd(q2, q2, q2, g.expand(2, 8, 1, 64).contiguous(), cu_seqlens=cu)
+
+
+# ------------------------------------------------------------------ bounded waits never run out
+@pytest.mark.parametrize("name,segment_chunks,vtile", [("c2048", 0, ""), ("c2048", 8, "64"), ("c4096", 0, ""),
+                                                       ("varlen", 0, ""), ("long", 0, "")])
+def test_bounded_waits_are_never_exhausted(monkeypatch, name, segment_chunks, vtile):
+    """The walkers' counter waits between waves are bounded so that a wave always
+    leaves them; a wait that ran to its bound (tens of milliseconds of polling)
+    would still give correct-looking results if the data happened to be ready.
+    Every launch here takes about a millisecond or less, so each must finish in
+    well under one exhausted wait."""
+    import torch
+    import chunkwise_gated_linear_amd as gla
+    if vtile:
+        monkeypatch.setenv("GLA_BF16_VTILE", vtile)
+    w = gi.WORKLOADS[name]
+    d = gi.make_inputs(w)
+    t = to_device(d, w.dtype)
+    call = gla.GlaCall(t["q"], t["k"], t["v"], t["g"], h0=t["h0"], cu_seqlens=t["cu_seqlens"],
+                       output_final_state=w.ht, segment_chunks=segment_chunks)
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        call(stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        call(stream)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    say(f"[ok]   {name} seg={segment_chunks} vtile={vtile or 'auto'}: {ms:.3f} ms per launch")
+    assert ms < 20.0, f"{name}: {ms:.1f} ms per launch; a bounded wait probably ran out"
