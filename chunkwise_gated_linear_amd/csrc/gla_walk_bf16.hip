@@ -375,14 +375,24 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   auto gate_decays = [&]() {
     const int src_pre = rg > 0 ? lane - QPW : lane;
     const int src_tot = (NG - 1) * QPW + lane % QPW;
+    // all eight shuffles in flight at once, the reciprocals that need none of
+    // them computed meanwhile (one LDS round trip instead of one per key)
+    float y[4], tot[4], rin[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float y = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src_pre, __float_as_int(incl[j])));
-      const float pre = rg > 0 ? y : 1.f;
-      const float tot = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src_tot, __float_as_int(incl[j])));
-      gSuf[j] = tot * __builtin_amdgcn_rcpf(incl[j]);   // product over the later row groups
-      gFq[j] = OUT ? scale * pre * __builtin_amdgcn_rcpf(tot) : 0.f;
-      gDec[j] = tot;
+      y[j] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src_pre, __float_as_int(incl[j])));
+      tot[j] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src_tot, __float_as_int(incl[j])));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rin[j] = __builtin_amdgcn_rcpf(incl[j]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float pre = rg > 0 ? y[j] : 1.f;
+      gSuf[j] = tot[j] * rin[j];   // product over the later row groups
+      gFq[j] = OUT ? scale * pre * __builtin_amdgcn_rcpf(tot[j]) : 0.f;
+      gDec[j] = tot[j];
     }
     if (!OUT && rg == 0) {
 #pragma unroll
