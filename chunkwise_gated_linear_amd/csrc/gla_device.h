@@ -63,6 +63,13 @@ __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// An int the compiler cannot see through: keeps a per-lane base offset in a
+// register instead of letting it be folded with constants into each access.
+__device__ __forceinline__ int opaque_int(int x) {
+  asm("" : "+v"(x));
+  return x;
+}
+
 template <typename T>
 __device__ __forceinline__ T lds_ld(const char *base, int byte_off) {
   return *reinterpret_cast<const T *>(base + byte_off);

@@ -278,7 +278,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   for (int kb = 0; kb < NKB; ++kb) rq[kb] = L::qk(l16, 16 * (4 * (NKB * kh + kb) + lg));
   int aoff[2];  // A row fragments: row l16, tokens 32 jb + 8 lg ..
 #pragma unroll
-  for (int jb = 0; jb < 2; ++jb) aoff[jb] = L::ao(l16, 16 * (4 * jb + lg));
+  for (int jb = 0; jb < 2; ++jb) aoff[jb] = opaque_int(L::oA + L::ao(l16, 16 * (4 * jb + lg)));
   const int trow = 8 * lg + (l16 >> 2);  // token row of the transpose reads
   int voff[NT];                          // v, transposed: columns VQ cw + 16 nt + 4 (l16 & 3)
 #pragma unroll
@@ -288,7 +288,10 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   for (int m = 0; m < NKB; ++m)
 #pragma unroll
     for (int e = 0; e < 2; ++e) koff[m][e] = L::qk(trow + 4 * e, 2 * (KH * kh + 8 * (l16 & 3)) + 64 * m);
-  const int base_d = 4 * (KH * kh + 4 * lg);  // decay a of key rows KH kh + 16 kt + 4 lg ..
+  // LDS regions past 64 KiB are addressed from per-lane base registers so that
+  // the remaining offsets fit the 16-bit immediate of the LDS instructions
+  // (folded into one constant, every access would need an address add)
+  const int base_d = opaque_int(L::oDec + 4 * (KH * kh + 4 * lg));  // decay a of key rows KH kh + 16 kt + 4 lg ..
 
   // ======================= producer waves: raw and gated registers
   // producer thread pt: key columns 4cq..4cq+3 of rows rg*RPG..+RPG-1
@@ -593,7 +596,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       // ---- S' = diag(a) S
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
-        const f32x4_t a4 = lds_ld<f32x4_t>(smem + L::oDec, base_d + 64 * kt);
+        const f32x4_t a4 = lds_ld<f32x4_t>(smem, base_d + 64 * kt);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -651,8 +654,8 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 #pragma unroll
           for (int it = 2 * jb; it < 4; ++it) {
             const int off = aoff[jb] + 16 * it * L::AROW;
-            const u32x4_t ah = lds_ld<u32x4_t>(smem + L::oA, off);
-            const u32x4_t al = lds_ld<u32x4_t>(smem + L::oA + L::APL, off);
+            const u32x4_t ah = lds_ld<u32x4_t>(smem, off);
+            const u32x4_t al = lds_ld<u32x4_t>(smem + L::APL, off);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
               o[it][nt] = mfma_bf(vf[nt][jb], al, o[it][nt]);
