@@ -668,8 +668,9 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
         if (KS == 1 || kh == 0) av(std::integral_constant<int, 0>{});
         if (KS == 1 || kh == 1) av(std::integral_constant<int, 1>{});
         if constexpr (KS == 1) {
-          // every wave has read the previous staged tile before it published its
-          // score tiles, so the staging area is free once the hand-off is done
+          // the previous tile was stored right after the last chunk-done
+          // barrier; the operands and scores barriers lie between those reads
+          // and these writes
 #pragma unroll
           for (int it = 0; it < 4; ++it)
 #pragma unroll
