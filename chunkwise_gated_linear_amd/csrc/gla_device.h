@@ -39,8 +39,38 @@ __device__ __forceinline__ float bf16_round_valu(float x) {
   return r;
 }
 
+// x - (one bf16 half of the packed word w), from the word itself: a bf16 dot
+// product of w with (-1, 0) or (0, -1), accumulated onto x.  The product is
+// exact and so is the difference (the remainder of rounding x to bf16 is a
+// float), so this equals x - bf_lo(w) / x - bf_hi(w) in one instruction.
+// The pair (-1, 0) is the word 0x0000bf80, which the compiler encodes as the
+// inline constant -1.0; the hardware reads that operand as the float -1.0,
+// i.e. the word 0xbf800000 = (0, -1).  The word is therefore kept in a scalar
+// register the compiler cannot see into.
+__device__ __forceinline__ float minus_bf_lo(uint32_t w, float x) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  uint32_t m = 0x0000bf80u;
+  asm("" : "+s"(m));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, m), x, false);
+}
+__device__ __forceinline__ float minus_bf_hi(uint32_t w, float x) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, 0xbf800000u),
+                                         x, false);
+}
+
 // Split 4 floats into bf16 hi (nearest) and bf16 lo (nearest of the remainder).
+// The dot instruction accumulates into its destination, so this form suits
+// values that die at the split; a value that stays live (the carried state)
+// would first be copied, and split4_sub / split4_valu are used for it.
 __device__ __forceinline__ void split4(const float x[4], u32x2_t &hi, u32x2_t &lo) {
+  hi[0] = pack_bf16(x[0], x[1]);
+  hi[1] = pack_bf16(x[2], x[3]);
+  lo[0] = pack_bf16(minus_bf_lo(hi[0], x[0]), minus_bf_hi(hi[0], x[1]));
+  lo[1] = pack_bf16(minus_bf_lo(hi[1], x[2]), minus_bf_hi(hi[1], x[3]));
+}
+// The same split with the remainders formed by subtraction.
+__device__ __forceinline__ void split4_sub(const float x[4], u32x2_t &hi, u32x2_t &lo) {
   hi[0] = pack_bf16(x[0], x[1]);
   hi[1] = pack_bf16(x[2], x[3]);
   lo[0] = pack_bf16(x[0] - bf_lo(hi[0]), x[1] - bf_hi(hi[0]));

@@ -258,10 +258,10 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
       }
       if constexpr (BF) {
         const int off = row * L::QROW + kperm_bf(4 * cq) * 2;
-        split4(kc, kt_hi[r], kt_lo[r]);
+        split4_sub(kc, kt_hi[r], kt_lo[r]);
         if (OUT) {
           u32x2_t qh, ql;
-          split4(qc, qh, ql);
+          split4_sub(qc, qh, ql);
           lds_st<u32x2_t>(smem + L::oQ, off, qh);
           lds_st<u32x2_t>(smem + L::oQ + L::Q_PLANE, off, ql);
           lds_st<u32x2_t>(smem + L::oK, off, kt_hi[r]);
@@ -378,7 +378,7 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
         const int off = i * L::TROW + (16 * jt + 4 * lg) * ES;
         if constexpr (BF) {
           u32x2_t hi, lo;
-          split4(av, hi, lo);
+          split4_sub(av, hi, lo);
           lds_st<u32x2_t>(smem + L::oA, off, hi);
           lds_st<u32x2_t>(smem + L::oA + L::A_PLANE, off, lo);
         } else {
@@ -436,8 +436,8 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
           const float s8[8] = {S[2 * kb][0], S[2 * kb][1], S[2 * kb][2], S[2 * kb][3],
                                S[2 * kb + 1][0], S[2 * kb + 1][1], S[2 * kb + 1][2], S[2 * kb + 1][3]};
           u32x2_t h0, l0, h1, l1;
-          split4(s8, h0, l0);
-          split4(s8 + 4, h1, l1);
+          split4_sub(s8, h0, l0);  // the state stays live
+          split4_sub(s8 + 4, h1, l1);
           const u32x4_t sh = {h0[0], h0[1], h1[0], h1[1]};
           const u32x4_t sl = {l0[0], l0[1], l1[0], l1[1]};
 #pragma unroll

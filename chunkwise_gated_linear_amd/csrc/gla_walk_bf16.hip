@@ -147,6 +147,22 @@ __device__ __forceinline__ void scores_wait(char *flags, int c) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Split of values that are not used after it (gated q and k rows, score
+// tiles).  With 64 columns the producer waves set the pace and the form with
+// one dot instruction per remainder saves them VALU instructions; with 128
+// columns that form measured slower and the subtraction forms are kept there
+// (split4_valu for VALU products, split4_sub for MFMA results).
+template <int VW, bool VALU_FED>
+__device__ __forceinline__ void split4_dead(const float x[4], u32x2_t &hi, u32x2_t &lo) {
+  if constexpr (VW == 64) {
+    split4(x, hi, lo);
+  } else if constexpr (VALU_FED) {
+    split4_valu(x, hi, lo);
+  } else {
+    split4_sub(x, hi, lo);
+  }
+}
+
 // Score tiles (i-tile, j-tile) of the 64 x 64 lower triangle per matrix wave.
 template <int W> struct Tiles;
 template <> struct Tiles<0> { static constexpr int n = 3; static constexpr int it[3] = {0, 1, 1}, jt[3] = {0, 0, 1}; };
@@ -188,7 +204,7 @@ __device__ __forceinline__ void scores(char *smem, const char *sq, const int (&r
 #pragma unroll
     for (int r = 0; r < 4; ++r) av[r] = (16 * T::jt[t] + 4 * lg + r <= i) ? acc[t][r] : 0.f;
     u32x2_t hi, lo;
-    split4(av, hi, lo);
+    split4_dead<VW, false>(av, hi, lo);
     const int off = L::ao(i, (16 * T::jt[t] + 4 * lg) * 2);
     lds_st<u32x2_t>(smem + L::oA, off, hi);
     lds_st<u32x2_t>(smem + L::oA + L::APL, off, lo);
@@ -426,12 +442,12 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
     float kc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) kc[j] = tK[r][j] * gSuf[j];
-    split4_valu(kc, gKh[r], gKl[r]);  // kc, qc: products of VALU multiplies
+    split4_dead<VW, true>(kc, gKh[r], gKl[r]);  // kc, qc: products of VALU multiplies
     if (OUT) {
       float qc[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) qc[j] = tQ[r][j] * gFq[j];
-      split4_valu(qc, gQh[r], gQl[r]);
+      split4_dead<VW, true>(qc, gQh[r], gQl[r]);
     }
   };
   // v goes to LDS straight from the load registers (two chunk buffers)
@@ -629,7 +645,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
             const float s8[8] = {S[2 * kb][nt][0], S[2 * kb][nt][1], S[2 * kb][nt][2], S[2 * kb][nt][3],
                                  S[2 * kb + 1][nt][0], S[2 * kb + 1][nt][1], S[2 * kb + 1][nt][2], S[2 * kb + 1][nt][3]};
             u32x2_t h0, l0, h1, l1;
-            split4_valu(s8, h0, l0);  // S' = a S: products of VALU multiplies
+            split4_valu(s8, h0, l0);  // S' = a S: products of VALU multiplies; S stays live
             split4_valu(s8 + 4, h1, l1);
             sh[nt] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
             sl[nt] = u32x4_t{l0[0], l0[1], l1[0], l1[1]};

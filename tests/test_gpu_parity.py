@@ -124,6 +124,16 @@ def test_empty_sequence_batch_returns_h0():
     np.testing.assert_array_equal(ht, d["h0"].astype(np.float64))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_packed_batch_of_empty_sequences_returns_h0(dtype):
+    # packed input with no tokens at all: every sequence keeps its initial state
+    d = gi.draw(605, 1, 0, 2, 64, 64, dtype=dtype, h0=True, lengths=[0, 0, 0])
+    say(f"[case] packed, all sequences empty, dtype={dtype}")
+    o, ht = run_gpu(d, dtype)
+    assert o.shape == (1, 0, 2, 64)
+    np.testing.assert_array_equal(ht, d["h0"].astype(np.float64))
+
+
 def test_no_initial_state_and_explicit_scale():
     d = gi.draw(602, 3, 150, 2, 128, 128, dtype="bf16", h0=False)
     _compare(d, "bf16", "scale=0.3", scale=0.3)
