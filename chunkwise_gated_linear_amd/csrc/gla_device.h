@@ -76,8 +76,8 @@ __device__ __forceinline__ void split4_sub(const float x[4], u32x2_t &hi, u32x2_
   lo[0] = pack_bf16(x[0] - bf_lo(hi[0]), x[1] - bf_hi(hi[0]));
   lo[1] = pack_bf16(x[2] - bf_lo(hi[1]), x[3] - bf_hi(hi[1]));
 }
-// The same split for x computed by ordinary VALU arithmetic (see
-// bf16_round_valu): one instruction fewer per pair.
+// The subtraction split for x computed by ordinary VALU arithmetic (see
+// bf16_round_valu): one instruction fewer per pair than split4_sub.
 __device__ __forceinline__ void split4_valu(const float x[4], u32x2_t &hi, u32x2_t &lo) {
   hi[0] = pack_bf16(x[0], x[1]);
   hi[1] = pack_bf16(x[2], x[3]);
