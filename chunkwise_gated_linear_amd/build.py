@@ -13,15 +13,29 @@ SOURCES = ["gla_kernels.hip", "gla_walk_bf16.hip", "gla_host.hip"]
 ARCH = os.environ.get("GLA_OFFLOAD_ARCH", "gfx950")
 
 
-def hipcc_command(out: str) -> list:
-    return [
-        "hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+def _flags():
+    """hipcc flags of every compilation of the sources, in two parts (the
+    library build puts its own flags between them)."""
+    head = [f"--offload-arch={ARCH}", "-O3", "-std=c++17"]
+    tail = [
         # packed fp32 VALU forms are kept out of the generated code on purpose
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-        "-o", out,
-    ] + [os.path.join(CSRC, s) for s in SOURCES]
+    ]
+    return head, tail
+
+
+def hipcc_command(out: str) -> list:
+    head, tail = _flags()
+    return (["hipcc"] + head + ["-fPIC", "-shared"] + tail + ["-o", out]
+            + [os.path.join(CSRC, s) for s in SOURCES])
+
+
+def device_asm_command(source: str, out: str) -> list:
+    """The gfx950 assembly of one source file's device code, as the library builds it."""
+    head, tail = _flags()
+    return ["hipcc"] + head + tail + ["--cuda-device-only", "-S", "-o", out, os.path.join(CSRC, source)]
 
 
 def build(verbose: bool = False) -> str:
