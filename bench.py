@@ -41,6 +41,17 @@ KERNEL_SRCS = [os.path.join(ROOT, "chunkwise_gated_linear_amd", "csrc", f)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def kernel_source_hash() -> str:
     """Hash of every device source: counters measured on other kernel code are not reused."""
     h = hashlib.sha256()
@@ -149,6 +160,8 @@ def main():
                          "reaches its sustained clock (short runs otherwise measure the ramp)")
     ap.add_argument("--workload", default="c2048", choices=sorted(gi.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single", type=int, default=21,
+                    help="launches timed one by one after the timed steps, warm and with L2/MALL evicted")
     ap.add_argument("--segment-chunks", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the forward, run a plain device copy of a known size "
@@ -226,6 +239,45 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     launch_ms = ev0.elapsed_time(ev1) / args.steps
 
+    # After the timed steps (not part of `value`): single launches, each between
+    # its own event pair, back to back (warm) and after writing a 512 MiB buffer
+    # that evicts L2 and the MALL (cold); then the bandwidth of a plain 512 MiB
+    # device copy on this GPU, as a measured counterpart of the HBM peak.
+    def single_launches(n, evict=None):
+        ts = []
+        for _ in range(n):
+            if evict is not None:
+                evict.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call(sptr)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts.sort()
+        return ts[len(ts) // 2], ts[0]
+    launch_us = None
+    copy_gbs = None
+    if args.single > 0:
+        warm_med, warm_min = single_launches(args.single)
+        evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold_med, cold_min = single_launches(args.single, evict)
+        del evict
+        launch_us = {"warm_median": warm_med, "warm_min": warm_min, "cold_median": cold_med,
+                     "cold_min": cold_min, "launches": args.single}
+        src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbs = 2 * src.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        del src, dst
+
     nbytes, flops = algorithmic(w, n_tokens, n_seqs)
     tokens_per_s = n_tokens / (ms_per_step * 1e-3)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -249,7 +301,7 @@ def main():
         c1 = time.perf_counter()
         cpu = {"value": runs * n_tokens / (c1 - c0), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"the whole workload ({n_tokens} tokens x {w.H} heads), fp64 token recurrence, "
-                         f"{runs} runs in {c1 - c0:.2f} s"}
+                         f"{runs} runs in {c1 - c0:.2f} s on {cpu_model()}"}
 
     segmented = call.ws_bytes > 0
     line = {
@@ -279,7 +331,10 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": nbytes,
             "launch_ms_avg": launch_ms,
+            "measured_copy_GBs": copy_gbs,
+            "frac_of_measured_copy": None if copy_gbs is None else achieved_gbs / copy_gbs,
         },
+        "single_launch_us": launch_us,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
