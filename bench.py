@@ -240,14 +240,16 @@ def main():
     launch_ms = ev0.elapsed_time(ev1) / args.steps
 
     # After the timed steps (not part of `value`): single launches, each between
-    # its own event pair, back to back (warm) and after writing a 512 MiB buffer
-    # that evicts L2 and the MALL (cold); then the bandwidth of a plain 512 MiB
-    # device copy on this GPU, as a measured counterpart of the HBM peak.
-    def single_launches(n, evict=None):
+    # its own event pair: back to back (warm); cold, after writing one 512 MiB
+    # buffer and reading another, so that L2 and the MALL hold neither inputs nor
+    # dirty lines; and after the write alone, whose dirty lines are written back
+    # while the launch runs.  Then the bandwidth of a plain 512 MiB device copy
+    # on this GPU, as a measured counterpart of the HBM peak.
+    def single_launches(n, prep=None):
         ts = []
         for _ in range(n):
-            if evict is not None:
-                evict.fill_(1)
+            if prep is not None:
+                prep()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             call(sptr)
@@ -260,11 +262,13 @@ def main():
     copy_gbs = None
     if args.single > 0:
         warm_med, warm_min = single_launches(args.single)
-        evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        cold_med, cold_min = single_launches(args.single, evict)
-        del evict
+        wbuf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        rbuf = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        cold_med, cold_min = single_launches(args.single, lambda: (wbuf.fill_(1), rbuf.sum(dtype=torch.int64)))
+        dirty_med, _ = single_launches(args.single, lambda: wbuf.fill_(1))
+        del wbuf, rbuf
         launch_us = {"warm_median": warm_med, "warm_min": warm_min, "cold_median": cold_med,
-                     "cold_min": cold_min, "launches": args.single}
+                     "cold_min": cold_min, "after_write_median": dirty_med, "launches": args.single}
         src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
