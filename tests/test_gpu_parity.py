@@ -57,12 +57,30 @@ def test_ragged_lengths(dtype, T):
     _compare(d, dtype, f"ragged T={T}")
 
 
-@pytest.mark.parametrize("dtype,K,V", [("bf16", 32, 64), ("bf16", 64, 128), ("bf16", 128, 256),
+@pytest.mark.parametrize("dtype,K,V", [("bf16", 32, 64), ("bf16", 64, 64), ("bf16", 64, 128), ("bf16", 128, 256),
                                         ("bf16", 128, 64), ("fp32", 16, 64), ("fp32", 32, 128),
-                                        ("fp32", 128, 128)])
+                                        ("fp32", 64, 256), ("fp32", 128, 128)])
 def test_head_dims(dtype, K, V):
     d = gi.draw(7 * K + V, 2, 300, 2, K, V, dtype=dtype, h0=True)
     _compare(d, dtype, f"K={K} V={V}")
+
+
+@pytest.mark.parametrize("dtype,vtile", [("bf16", "64"), ("bf16", "128"), ("fp32", "")])
+@pytest.mark.parametrize("seg,packed", [(0, False), (3, False), (0, True), (2, True)])
+def test_without_final_state(monkeypatch, dtype, vtile, seg, packed):
+    # o alone (ht not requested): the walkers skip the state store, segment
+    # summaries are still formed when the sequence is cut
+    if vtile:
+        monkeypatch.setenv("GLA_BF16_VTILE", vtile)
+    lengths = [300, 1, 0, 129, 64] if packed else None
+    d = gi.draw(700 + seg + (50 if packed else 0), 1 if packed else 2, 0 if packed else 400, 2, 128, 128,
+                dtype=dtype, h0=True, lengths=lengths)
+    say(f"[case] no ht, dtype={dtype} vtile={vtile or 'auto'} seg={seg} packed={packed}")
+    o, ht = run_gpu(d, dtype, output_final_state=False, segment_chunks=seg)
+    assert ht is None
+    ro, _ = run_oracle(d)
+    eo = check_close("o without ht", o, ro, TOL[dtype], out_dtype=dtype)
+    say(f"[ok]   no ht: o max|err| {eo:.4e} rms")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
