@@ -84,6 +84,23 @@ def test_without_final_state(monkeypatch, dtype, vtile, seg, packed):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("gate", ["zero", "strong", "mixed"])
+def test_gate_extremes(dtype, gate):
+    # g = 0 is plain causal linear attention; g = -1 per step puts a chunk's
+    # summed log decay at -64, where the in-chunk factors exp(G_i - G_last) and
+    # exp(G_last - G_j) reach e^64 and e^-64 (the kernels require |sum| < ~80
+    # per chunk); "mixed" gives half the keys each
+    d = gi.draw(640, 2, 200, 2, 128, 128, dtype=dtype, h0=True)
+    g = np.zeros_like(d["g"])
+    if gate == "strong":
+        g[:] = -1.0
+    elif gate == "mixed":
+        g[..., ::2] = -1.0
+    d["g"] = g
+    _compare(d, dtype, f"gate {gate}", segment_chunks=2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("seg", [1, 2, 3, 5])
 def test_forced_segments(dtype, seg):
     # long sequences cut into segments: summary kernel + state scan + output walk
