@@ -1,23 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark: chunkwise gated linear attention forward on one MI355X.
 
-Default workload: B=8, H=16, T=2048, K=V=128, bf16 q/k/v, fp32 gates, chunk 64,
-final state stored (synthetic seeded inputs, recipe in gla_inputs.py).
+Default workload ("long"): B=1, H=32, T=65536, K=V=128, bf16 q/k/v, fp32 gates
+logsigmoid(N(0,1))/16, chunk 64, final state stored -- the largest of the five
+measured configurations (synthetic seeded inputs, recipe in gla_inputs.py).
+``--workload`` selects another one (small, c2048, c4096, varlen).
 
-A step is one full forward (every kernel of the path) over the whole batch,
-with inputs resident in device memory.  Untimed steps for --settle-ms (the GPU
-clock ramps up over the first tens of milliseconds of load), W untimed warmup
-steps, then exactly K timed steps between two device synchronisations; one JSON
-line is printed.
+A step is one full forward (every kernel of the path: segment plan, segment
+summaries, state scan, output walk, as the library schedules them) over the
+whole batch, with inputs resident in device memory.  Untimed steps for
+--settle-ms (the GPU clock ramps up over the first tens of milliseconds of
+load), W untimed warmup steps, then exactly K timed steps between two device
+synchronisations; one JSON line is printed.
 
 Also reported:
-  roofline      the dominant kernel's algorithmic bytes per launch divided by its
-                average launch time, measured with HIP events on the launch stream
-                inside the timed region, against the 8 TB/s HBM peak; `traffic`
-                is the HBM bytes per launch measured by rocprofv3 counters for the
-                current kernel source (null when no matching measurement exists).
-  cpu_baseline  the fp64 CPU oracle (test infrastructure) on the host cores, on the
-                whole workload, in tokens/s.
+  roofline      algorithmic bytes (and flops) of one forward divided by its
+                average duration, measured with HIP events on the launch stream
+                over the timed region, against the 8 TB/s HBM peak or the dense
+                MFMA peak, whichever bound gives the longer ideal time; `traffic`
+                is the HBM bytes one forward moves (FETCH_SIZE + WRITE_SIZE of all
+                its kernels, from rocprofv3 counter runs of the current device
+                sources), null when no matching measurement exists.
+  cpu_baseline  the fp64 CPU oracle (test infrastructure) on the host cores, on a
+                bounded sample of the same workload (whole sequences of the first
+                heads), in tokens/s of the full workload's head count.
 """
 import argparse
 import hashlib
@@ -35,10 +41,12 @@ import gla_inputs as gi  # noqa: E402
 
 METRIC = "GLA chunked fwd tokens/s + TFLOP/s, fraction of MFMA/HBM roofline (1 GPU)"
 HBM_PEAK_GBS = 8000.0
-BF16_MFMA_PEAK_TFLOPS = 2500.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
 KERNEL_SRCS = [os.path.join(ROOT, "chunkwise_gated_linear_amd", "csrc", f)
-               for f in ("gla_kernels.hip", "gla_walk_bf16.hip", "gla_device.h", "gla_internal.h")]
+               for f in ("gla_kernels.hip", "gla_walk_bf16.hip", "gla_device.h", "gla_internal.h",
+                         "gla_host.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CALIB_BYTES = 512 << 20
 
 
 def cpu_model() -> str:
@@ -53,7 +61,7 @@ def cpu_model() -> str:
 
 
 def kernel_source_hash() -> str:
-    """Hash of every device source: counters measured on other kernel code are not reused."""
+    """Hash of every device and launch source: counters measured on other code are not reused."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
         with open(path, "rb") as f:
@@ -62,12 +70,15 @@ def kernel_source_hash() -> str:
 
 
 def algorithmic(w, n_tokens, n_seqs):
-    """Bytes (inputs read once + outputs written once) and flops of the method."""
+    """Bytes (inputs read once + outputs written once) and flops of the method.
+
+    Flops per token-head: 4KV (the state contribution k^T v and the read q S)
+    plus (C+1)(K+V) (the causal halves of the in-chunk scores and of A v)."""
     e = 2 if w.dtype == "bf16" else 4
     H, K, V = w.H, w.K, w.V
     th = n_tokens * H
     nbytes = th * (2 * K * e + V * e + 4 * K) + th * V * e + 4 * n_seqs * H * K * V * (int(w.h0) + int(w.ht))
-    flops = th * (4 * K * V + (64 + 1) * (K + V))
+    flops = th * (4 * K * V + (w.chunk + 1) * (K + V))
     return nbytes, flops
 
 
@@ -91,9 +102,9 @@ def load_traffic(workload: str):
     return entry.get("bytes_per_launch")
 
 
-def _counter_per_dispatch(run_dir, counter, name_filter=None):
-    """Mean per-dispatch value of `counter` in a rocprofv3 --pmc CSV run directory,
-    for the kernel matching name_filter (default: the kernel with the largest value)."""
+def _counter_means(run_dir, counter):
+    """Mean per-dispatch value of `counter` per kernel name in a rocprofv3 --pmc CSV
+    run directory (values of one dispatch are summed over the counter's instances)."""
     import csv
     import glob
     vals = {}
@@ -109,39 +120,47 @@ def _counter_per_dispatch(run_dir, counter, name_filter=None):
         per_kernel.setdefault(name, []).append(v)
     if not per_kernel:
         raise SystemExit(f"no {counter} rows under {run_dir}")
-    if name_filter is not None:
-        names = [n for n in per_kernel if name_filter in n]
-        if not names:
-            raise SystemExit(f"no kernel matching {name_filter!r} under {run_dir}")
-    else:
-        names = list(per_kernel)
-    means = {n: sum(per_kernel[n]) / len(per_kernel[n]) for n in names}
-    best = max(means, key=means.get)
-    return best, means[best]
+    return {n: sum(v) / len(v) for n, v in per_kernel.items()}
 
 
-def record_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
-    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant kernel by what the
-    same counters read for a plain device copy of known size, and store the HBM bytes per
-    launch in profiles/traffic.json for the current device sources."""
-    copy_bytes = 512 << 20
-    _, cf = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE")
-    _, cw = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE")
-    f_factor, w_factor = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
-    kname, kf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", "gla_chunk_output")
-    _, kw = _counter_per_dispatch(write_dir, "WRITE_SIZE", "gla_chunk_output")
-    fetch_b, write_b = kf * 1024.0 * f_factor, kw * 1024.0 * w_factor
+def _largest(means):
+    name = max(means, key=means.get)
+    return name, means[name]
+
+
+def record_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, read_fetch_dir=None):
+    """HBM bytes of one forward: FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of every kernel
+    of the library, each scaled by what the same counter reads for a plain device copy of
+    known size, summed over the kernels one forward launches.  Stored in
+    profiles/traffic.json under the workload name and the hash of the current sources."""
+    _, cf = _largest(_counter_means(copy_fetch_dir, "FETCH_SIZE"))
+    _, cw = _largest(_counter_means(copy_write_dir, "WRITE_SIZE"))
+    f_factor, w_factor = CALIB_BYTES / (cf * 1024.0), CALIB_BYTES / (cw * 1024.0)
+    read_factor = None
+    if read_fetch_dir:
+        _, rf = _largest(_counter_means(read_fetch_dir, "FETCH_SIZE"))
+        read_factor = CALIB_BYTES / (rf * 1024.0)
+    fetch = {n: v for n, v in _counter_means(fetch_dir, "FETCH_SIZE").items() if "gla" in n}
+    write = {n: v for n, v in _counter_means(write_dir, "WRITE_SIZE").items() if "gla" in n}
+    kernels = {}
+    for n in sorted(set(fetch) | set(write)):
+        short = n.rsplit("(", 1)[0]
+        kernels[short] = {"fetch_kib_counter": fetch.get(n, 0.0), "write_kib_counter": write.get(n, 0.0),
+                          "fetch_bytes": fetch.get(n, 0.0) * 1024.0 * f_factor,
+                          "write_bytes": write.get(n, 0.0) * 1024.0 * w_factor}
+    total_f = sum(k["fetch_bytes"] for k in kernels.values())
+    total_w = sum(k["write_bytes"] for k in kernels.values())
     try:
         with open(TRAFFIC_FILE) as f:
             table = json.load(f)
     except (OSError, ValueError):
         table = {}
     table[workload] = {
-        "kernel": kname.rsplit("(", 1)[0],
-        "bytes_per_launch": fetch_b + write_b,
-        "fetch_bytes": fetch_b, "write_bytes": write_b,
-        "fetch_kib_counter": kf, "write_kib_counter": kw,
+        "bytes_per_launch": total_f + total_w,
+        "fetch_bytes": total_f, "write_bytes": total_w,
+        "kernels": kernels,
         "copy_fetch_factor": f_factor, "copy_write_factor": w_factor,
+        "read_only_fetch_factor": read_factor,
         "kernel_source_sha256_16": kernel_source_hash(),
     }
     with open(TRAFFIC_FILE, "w") as f:
@@ -150,33 +169,77 @@ def record_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_di
     print(json.dumps(table[workload], indent=1))
 
 
+def cpu_baseline(d, w, n_tokens, target_s=10.0):
+    """The fp64 oracle on whole sequences of the first heads, grown until about
+    target_s seconds of wall time; reported as tokens/s of the full head count."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    threads = len(os.sched_getaffinity(0))
+    H = w.H
+
+    def run(nh, reps=1):
+        sl = lambda a: np.ascontiguousarray(a[:, :, :nh])
+        h0 = None if d["h0"] is None else np.ascontiguousarray(d["h0"][:, :nh])
+        args = (sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.gla_reference(*args, h0=h0, cu_seqlens=d["cu_seqlens"], output_final_state=w.ht,
+                                 threads=threads)
+        return (time.perf_counter() - t0) / reps
+
+    # the oracle runs one (sequence, head) per thread: start with enough heads to
+    # occupy every core, double until about target_s / 2, then repeat the run
+    # until about target_s of wall time in total
+    n_seqs = w.n_seqs if w.varlen else w.B
+    nh = min(H, max(1, -(-threads // n_seqs)))
+    dt = run(nh)
+    while dt < target_s / 2 and nh < H:
+        nh = min(H, 2 * nh)
+        dt = run(nh)
+    reps = 1
+    while dt * reps < 0.8 * target_s:
+        reps = max(2 * reps, int(target_s / max(dt, 1e-5)))
+        dt = run(nh, reps)
+    used = min(threads, n_seqs * nh)
+    return {"value": n_tokens * (nh / H) / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{nh} of {H} heads, all {n_tokens} tokens ({n_seqs} sequences), fp64 token "
+                      f"recurrence, {dt * reps:.2f} s for {reps} run(s) on {cpu_model()}; tokens/s "
+                      f"scaled to {H} heads"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="before the W warmup steps, run untimed steps for this long so the GPU "
                          "reaches its sustained clock (short runs otherwise measure the ramp)")
-    ap.add_argument("--workload", default="c2048", choices=sorted(gi.WORKLOADS))
+    ap.add_argument("--workload", default="long", choices=sorted(gi.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--single", type=int, default=21,
+    ap.add_argument("--single", type=int, default=11,
                     help="launches timed one by one after the timed steps, warm and with L2/MALL evicted")
     ap.add_argument("--segment-chunks", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="instead of the forward, run a plain device copy of a known size "
+                    help="instead of the forward, run a plain 512 MiB device copy "
                          "(used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
-    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                    help="(no GPU) store HBM bytes per launch of --workload from rocprofv3 --pmc runs of "
-                         "FETCH_SIZE and WRITE_SIZE on this benchmark and on --copy-calibration")
+    ap.add_argument("--read-calibration", action="store_true",
+                    help="instead of the forward, read a 512 MiB buffer once per step (a sum), "
+                         "to check the FETCH_SIZE scale on a read-only kernel")
+    ap.add_argument("--record-traffic", nargs="+", metavar="DIR",
+                    help="(no GPU) FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR [READ_FETCH_DIR]: "
+                         "store the HBM bytes per forward of --workload from rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.record_traffic:
+        if len(args.record_traffic) not in (4, 5):
+            ap.error("--record-traffic takes 4 or 5 directories")
         record_traffic(args.workload, *args.record_traffic)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build is a single-GPU kernel library; run it with --gpus 1 "
-              "(multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        print("bench.py: this library runs on one GPU; run it with --gpus 1 (how the path would "
+              "shard over several GPUs is described in DESIGN.md, not built)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -189,20 +252,25 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    if args.copy_calibration:
-        nbytes = 512 << 20
-        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    if args.copy_calibration or args.read_calibration:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(args.steps):
-            dst.copy_(src)
+            if args.copy_calibration:
+                dst.copy_(src)
+            else:
+                src.sum()
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written": nbytes,
+        print(json.dumps({"calibration": "copy" if args.copy_calibration else "read",
+                          "bytes_read": CALIB_BYTES,
+                          "bytes_written": CALIB_BYTES if args.copy_calibration else 0,
                           "launches": args.steps}), flush=True)
         return
 
     w = gi.WORKLOADS[args.workload]
     d = gi.make_inputs(w)
     lengths = d.get("lengths")
+    digest = gi.array_digest(d["q"], d["k"], d["v"], d["g"], d["h0"], d["cu_seqlens"])
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     q, k, v = (torch.from_numpy(d[x]).to(tdt).to(dev) for x in ("q", "k", "v"))
     g = torch.from_numpy(d["g"]).to(dev)
@@ -217,7 +285,7 @@ def main():
 
     t_settle = time.perf_counter()
     while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
-        for _ in range(10):
+        for _ in range(4):
             call(sptr)
         torch.cuda.synchronize()
     for _ in range(args.warmup):
@@ -225,7 +293,7 @@ def main():
     torch.cuda.synchronize()
 
     # One event pair on the launch stream brackets the K back-to-back steps; the
-    # average launch duration is their span / K (per-step event records would
+    # average forward duration is their span / K (per-step event records would
     # add their own gaps between launches).
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -239,12 +307,11 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     launch_ms = ev0.elapsed_time(ev1) / args.steps
 
-    # After the timed steps (not part of `value`): single launches, each between
+    # After the timed steps (not part of `value`): single forwards, each between
     # its own event pair: back to back (warm); cold, after writing one 512 MiB
     # buffer and reading another, so that L2 and the MALL hold neither inputs nor
-    # dirty lines; and after the write alone, whose dirty lines are written back
-    # while the launch runs.  Then the bandwidth of a plain 512 MiB device copy
-    # on this GPU, as a measured counterpart of the HBM peak.
+    # dirty lines.  Then the bandwidth of a plain 512 MiB device copy on this GPU,
+    # as a measured counterpart of the HBM peak.
     def single_launches(n, prep=None):
         ts = []
         for _ in range(n):
@@ -265,10 +332,9 @@ def main():
         wbuf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         rbuf = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
         cold_med, cold_min = single_launches(args.single, lambda: (wbuf.fill_(1), rbuf.sum(dtype=torch.int64)))
-        dirty_med, _ = single_launches(args.single, lambda: wbuf.fill_(1))
         del wbuf, rbuf
         launch_us = {"warm_median": warm_med, "warm_min": warm_min, "cold_median": cold_med,
-                     "cold_min": cold_min, "after_write_median": dirty_med, "launches": args.single}
+                     "cold_min": cold_min, "launches": args.single}
         src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -285,29 +351,20 @@ def main():
     nbytes, flops = algorithmic(w, n_tokens, n_seqs)
     tokens_per_s = n_tokens / (ms_per_step * 1e-3)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
-    achieved_gbs = nbytes / (launch_ms * 1e-3) / 1e9
-    t_roof = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_MFMA_PEAK_TFLOPS * 1e12))
+    mfma_peak = MFMA_PEAK_TFLOPS[w.dtype]
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (mfma_peak * 1e12)
     traffic = load_traffic(args.workload)
+    if t_hbm >= t_mfma:
+        bound, achieved, peak, unit = "hbm", nbytes / (launch_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", flops / (launch_ms * 1e-3) / 1e12, mfma_peak, "TFLOP/s"
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        oracle.build(force=False)
-        threads = len(os.sched_getaffinity(0))
-        # the whole workload, repeated until about 10 s of wall time (bounded at 100 runs)
-        runs, c0 = 0, time.perf_counter()
-        while True:
-            oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], h0=d["h0"], cu_seqlens=d["cu_seqlens"],
-                                 output_final_state=w.ht, threads=threads)
-            runs += 1
-            if time.perf_counter() - c0 >= 10.0 or runs >= 100:
-                break
-        c1 = time.perf_counter()
-        cpu = {"value": runs * n_tokens / (c1 - c0), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": f"the whole workload ({n_tokens} tokens x {w.H} heads), fp64 token recurrence, "
-                         f"{runs} runs in {c1 - c0:.2f} s on {cpu_model()}"}
+        cpu = cpu_baseline(d, w, n_tokens)
 
-    segmented = call.ws_bytes > 0
+    ws_bytes = call.ws_bytes
     line = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -321,22 +378,22 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": describe(w, lengths), "tokens": n_tokens, "heads": w.H,
-                   "segmented_state_scan": segmented},
+        "config": {"workload": describe(w, lengths), "name": w.name, "tokens": n_tokens, "heads": w.H,
+                   "seed": w.seed, "inputs_digest": digest, "workspace_bytes": ws_bytes},
         "tflops_algorithmic": tflops,
-        "roofline_time_us": t_roof * 1e6,
+        "roofline_time_us": max(t_hbm, t_mfma) * 1e6,
         "roofline": {
-            "bound": "hbm",
-            "kernel": "gla_chunk_output" if not segmented else "gla_fwd (chunk_local + state_scan + chunk_output)",
-            "achieved": achieved_gbs,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved_gbs / HBM_PEAK_GBS,
+            "bound": bound,
+            "kernel": "gla_fwd (every kernel of one forward)",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": unit,
+            "frac": achieved / peak,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": nbytes,
+            "algorithmic_flops_per_launch": flops,
             "launch_ms_avg": launch_ms,
             "measured_copy_GBs": copy_gbs,
-            "frac_of_measured_copy": None if copy_gbs is None else achieved_gbs / copy_gbs,
         },
         "single_launch_us": launch_us,
         "cpu_baseline": cpu,

@@ -9,6 +9,8 @@ importing the binding still works but every call raises.
     o, ht = gla_fwd(q, k, v, g, h0=None, cu_seqlens=None, scale=None,
                     chunk=64, output_final_state=False)
 
+K and V are multiples of 16 in [16, 256].
+
 Shapes are time-major: q, k, g [B, T, H, K]; v [B, T, H, V]; h0, ht
 [N, H, K, V] float32; cu_seqlens int32 [N+1] for packed sequences (B == 1).
 Defaults follow page "fla/ops/gla/fused_chunk.py" (fused_chunk_gla: scale
@@ -24,7 +26,7 @@ import os
 from typing import Optional, Tuple
 
 __all__ = ["gla_fwd", "GlaCall", "workspace_bytes", "library_path", "load_library", "GlaError",
-           "STATUS", "Problem"]
+           "STATUS", "Problem", "STATUS_WAIT_EXHAUSTED", "read_status"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgla.so")
@@ -36,6 +38,7 @@ STATUS = {
 }
 GLA_F32, GLA_BF16 = 0, 1
 CHUNK = 64
+STATUS_WAIT_EXHAUSTED = 1  # bit of the workspace status word: a bounded wait between waves ran out
 
 
 class GlaError(RuntimeError):
@@ -48,7 +51,8 @@ class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("n_seqs", ctypes.c_int32), ("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("segment_chunks", ctypes.c_int32), ("packed", ctypes.c_int32)]
+                ("segment_chunks", ctypes.c_int32), ("packed", ctypes.c_int32),
+                ("value_tile", ctypes.c_int32), ("wait_limit", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -81,9 +85,10 @@ def _status_msg(lib, code: int) -> str:
 
 
 def make_problem(B, T, H, K, V, dtype_code, n_seqs, chunk=CHUNK, scale=1.0,
-                 segment_chunks=0, packed=False) -> Problem:
+                 segment_chunks=0, packed=False, value_tile=0, wait_limit=0) -> Problem:
     return Problem(int(B), int(T), int(H), int(K), int(V), int(dtype_code), int(n_seqs),
-                   int(chunk), float(scale), int(segment_chunks), 1 if packed else 0)
+                   int(chunk), float(scale), int(segment_chunks), 1 if packed else 0,
+                   int(value_tile), int(wait_limit))
 
 
 def workspace_bytes(problem: Problem) -> int:
@@ -98,14 +103,29 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _new_workspace(nbytes: int, dev):
+    """Workspace of nbytes; zeroed, so that its status word starts clear."""
+    import torch
+    return torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+
+
+def read_status(workspace) -> int:
+    """The sticky status word (first 4 bytes) of a workspace; synchronises with the device."""
+    import torch
+    return int(workspace[:4].cpu().view(torch.int32).item()) & 0xFFFFFFFF
+
+
 def gla_fwd(q, k, v, g, h0=None, cu_seqlens=None, scale: Optional[float] = None,
             chunk: int = CHUNK, output_final_state: bool = False, segment_chunks: int = 0,
-            workspace=None, out=None) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
+            workspace=None, out=None, value_tile: int = 0,
+            wait_limit: int = 0) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
     """Gated linear attention forward through libgla.so.
 
     Returns (o, ht): o has v's shape and dtype; ht is [N, H, K, V] float32 when
     ``output_final_state`` else None.  Inputs must be contiguous tensors on one
-    HIP device; the call is asynchronous on torch's current stream.
+    HIP device; the call is asynchronous on torch's current stream.  A given
+    ``workspace`` (uint8, zeroed before its first use) is used when it is large
+    enough; its status word can then be read with ``read_status``.
     """
     import torch
 
@@ -146,7 +166,8 @@ def gla_fwd(q, k, v, g, h0=None, cu_seqlens=None, scale: Optional[float] = None,
         scale = K ** -0.5
     elif not (scale > 0):
         raise ValueError("scale must be positive")
-    prob = make_problem(B, T, H, K, V, code, N, chunk, scale, segment_chunks, cu_seqlens is not None)
+    prob = make_problem(B, T, H, K, V, code, N, chunk, scale, segment_chunks, cu_seqlens is not None,
+                        value_tile, wait_limit)
     with torch.cuda.device(dev):
         ws = lib.gla_fwd_workspace_bytes(ctypes.byref(prob))
         if ws == ctypes.c_size_t(-1).value:
@@ -157,14 +178,12 @@ def gla_fwd(q, k, v, g, h0=None, cu_seqlens=None, scale: Optional[float] = None,
         if out is not None and (out.shape != v.shape or out.dtype != v.dtype):
             raise ValueError("out must match v's shape and dtype")
         ht = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if output_final_state else None
-        if ws > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws):
-            workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        if workspace is None or workspace.numel() * workspace.element_size() < ws:
+            workspace = _new_workspace(ws, dev)
         stream = torch.cuda.current_stream(dev).cuda_stream
         rc = lib.gla_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0),
-                         _ptr(cu_seqlens), _ptr(o), _ptr(ht),
-                         _ptr(workspace) if ws > 0 else None,
-                         (workspace.numel() * workspace.element_size()) if ws > 0 else 0,
-                         stream)
+                         _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), stream)
     if rc != 0:
         raise GlaError(rc, _status_msg(lib, rc))
     return o, ht
@@ -176,23 +195,25 @@ class GlaCall:
     and stream capture).  ``stream`` defaults to torch's current stream at call time."""
 
     def __init__(self, q, k, v, g, h0=None, cu_seqlens=None, scale=None, chunk: int = CHUNK,
-                 output_final_state: bool = False, segment_chunks: int = 0):
+                 output_final_state: bool = False, segment_chunks: int = 0, value_tile: int = 0,
+                 wait_limit: int = 0):
         import torch
 
         self.lib = load_library()
-        # validation and allocation through the same path as gla_fwd
-        o, ht = gla_fwd(q, k, v, g, h0=h0, cu_seqlens=cu_seqlens, scale=scale, chunk=chunk,
-                        output_final_state=output_final_state, segment_chunks=segment_chunks)
         B, T, H, K = q.shape
         V = v.shape[-1]
         N = B if cu_seqlens is None else cu_seqlens.numel() - 1
         code = GLA_BF16 if q.dtype == torch.bfloat16 else GLA_F32
         self.problem = make_problem(B, T, H, K, V, code, N, chunk, K ** -0.5 if scale is None else scale,
-                                    segment_chunks, cu_seqlens is not None)
+                                    segment_chunks, cu_seqlens is not None, value_tile, wait_limit)
         self.device = q.device
         ws = workspace_bytes(self.problem)
-        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=self.device)
+        self.workspace = _new_workspace(ws, self.device)
         self.ws_bytes = ws
+        # validation and allocation of o and ht through the same path as gla_fwd
+        o, ht = gla_fwd(q, k, v, g, h0=h0, cu_seqlens=cu_seqlens, scale=scale, chunk=chunk,
+                        output_final_state=output_final_state, segment_chunks=segment_chunks,
+                        workspace=self.workspace, value_tile=value_tile, wait_limit=wait_limit)
         self.o, self.ht = o, ht
         self._args = (q, k, v, g, h0, cu_seqlens)
 
@@ -201,9 +222,12 @@ class GlaCall:
         q, k, v, g, h0, cu = self._args
         s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
         rc = self.lib.gla_fwd(ctypes.byref(self.problem), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0),
-                              _ptr(cu), _ptr(self.o), _ptr(self.ht),
-                              self.workspace.data_ptr() if self.ws_bytes > 0 else None,
+                              _ptr(cu), _ptr(self.o), _ptr(self.ht), self.workspace.data_ptr(),
                               self.ws_bytes, s)
         if rc != 0:
             raise GlaError(rc, _status_msg(self.lib, rc))
         return self.o, self.ht
+
+    def status(self) -> int:
+        """Sticky status word of this call's workspace (GLA_STATUS_* bits); synchronises."""
+        return read_status(self.workspace)

@@ -120,8 +120,19 @@ __device__ __forceinline__ int kperm_bf(int p) {
 }
 
 // ---------------------------------------------------------------- locate a segment
+// Token range of packed sequence n, clamped to [0, T]: offsets that break the
+// documented precondition (non-decreasing, cu[N] = T) give wrong outputs but
+// never an access outside the caller's buffers.
+__device__ __forceinline__ void seq_extent(const int32_t *cu, int n, int T, int &bos, int &len) {
+  const int a = min(max(cu[n], 0), T);
+  const int b = min(max(cu[n + 1], a), T);
+  bos = a;
+  len = b - a;
+}
+
 struct SegInfo {
-  int n, s, nseg, first, bos, len;
+  int n, s, nseg, first, len;
+  int64_t bos;  // first token of the sequence on the flattened [B*T] token axis
 };
 
 __device__ __forceinline__ bool locate(const WalkParams &p, int seg, SegInfo &si) {
@@ -132,7 +143,7 @@ __device__ __forceinline__ bool locate(const WalkParams &p, int seg, SegInfo &si
     si.nseg = p.P;
     si.first = si.n * p.P;
   } else {
-    const int total = p.seg_base[p.N];
+    const int total = p.seg_base[p.N];  // <= seg_slots (the segment plan caps it)
     if (seg >= total) return false;
     if (p.seg_order != nullptr) seg = p.seg_order[seg];  // longest segments are dispatched first
     int lo = 0, hi = p.N - 1;
@@ -144,12 +155,15 @@ __device__ __forceinline__ bool locate(const WalkParams &p, int seg, SegInfo &si
     si.first = p.seg_base[lo];
     si.nseg = p.seg_base[lo + 1] - si.first;
     si.s = seg - si.first;
+    if (si.s < 0 || si.s >= si.nseg) return false;
   }
   if (p.cu != nullptr) {
-    si.bos = p.cu[si.n];
-    si.len = p.cu[si.n + 1] - si.bos;
+    int bos, len;
+    seq_extent(p.cu, si.n, p.T, bos, len);
+    si.bos = bos;
+    si.len = len;
   } else {
-    si.bos = si.n * p.T;
+    si.bos = (int64_t)si.n * p.T;
     si.len = p.T;
   }
   // every lane of the workgroup holds the same values; say so, so that they
@@ -158,8 +172,10 @@ __device__ __forceinline__ bool locate(const WalkParams &p, int seg, SegInfo &si
   si.s = __builtin_amdgcn_readfirstlane(si.s);
   si.nseg = __builtin_amdgcn_readfirstlane(si.nseg);
   si.first = __builtin_amdgcn_readfirstlane(si.first);
-  si.bos = __builtin_amdgcn_readfirstlane(si.bos);
   si.len = __builtin_amdgcn_readfirstlane(si.len);
+  const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)si.bos);
+  const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)si.bos >> 32));
+  si.bos = (int64_t)(((uint64_t)bhi << 32) | blo);
   return true;
 }
 

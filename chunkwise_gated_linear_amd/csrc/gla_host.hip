@@ -1,13 +1,15 @@
 // Host side of the C ABI declared in include/gla.h: validation, workspace
-// sizing, the choice of state segments and the launch sequence.
+// sizing, the choice of state segments and key blocks, and the launch sequence.
 //
 // Launch sequence on the caller's stream (page "fla/ops/gla/fused_chunk.py",
 // FusedChunkGLAFunction.forward, re-planned for one MI355X):
 //   [packed input, several segments possible]  gla_segment_plan
-//   [some sequence spans several segments]    gla_chunk_local -> gla_state_scan
-//   always                                    gla_chunk_output
+//   per key block (one, or two when K > 128):
+//     [some sequence spans several segments]   gla_chunk_local -> gla_state_scan
+//     always                                   gla_chunk_output
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -20,6 +22,8 @@ namespace {
 
 using gla::kChunk;
 using gla::kVTile;
+
+constexpr size_t kHeaderBytes = 256;  // status word + padding at the start of the workspace
 
 int device_cu_count() {
   static std::mutex mu;
@@ -35,9 +39,29 @@ int device_cu_count() {
   return cus;
 }
 
-bool k_supported(int dtype, int K) {
-  if (dtype == GLA_BF16) return K == 32 || K == 64 || K == 128;
-  return K == 16 || K == 32 || K == 64 || K == 128;
+// Keys of each launch: K itself up to 128, else two blocks (each a multiple of
+// 16, at most 128).
+int key_blocks(int K, int kb[2]) {
+  if (K <= gla::kMaxKeyBlock) {
+    kb[0] = K;
+    kb[1] = 0;
+    return 1;
+  }
+  kb[0] = ((K / 2 + 15) / 16) * 16;
+  kb[1] = K - kb[0];
+  return 2;
+}
+
+// The fast bf16 walker handles a problem whose keys fit one block.
+bool uses_bf16_walker(const gla_problem *p) { return p->dtype == GLA_BF16 && p->K <= gla::kMaxKeyBlock; }
+
+// Padded key width of the instantiation that runs a key block of kb keys.
+int kernel_key_width(bool bf16_walker, bool bf16, int kb) {
+  if (bf16_walker) return kb <= 64 ? 64 : 128;
+  const int lo = bf16 ? 32 : 16;  // keys per contraction step of the general walker
+  for (int w = lo; w <= 128; w *= 2)
+    if (kb <= w) return w;
+  return 128;
 }
 
 gla_status validate(const gla_problem *p) {
@@ -46,16 +70,20 @@ gla_status validate(const gla_problem *p) {
   if (p->dtype != GLA_F32 && p->dtype != GLA_BF16) return GLA_ERR_BAD_DTYPE;
   if (!(std::isfinite(p->scale) && p->scale > 0.f)) return GLA_ERR_BAD_SCALE;
   if (p->chunk != kChunk) return GLA_ERR_UNSUPPORTED;
-  if (!k_supported(p->dtype, p->K) || p->V % kVTile != 0) return GLA_ERR_UNSUPPORTED;
-  if (p->segment_chunks < 0 || (p->packed != 0 && p->packed != 1)) return GLA_ERR_BAD_SHAPE;
+  if (p->K % 16 != 0 || p->K > 256 || p->V % 16 != 0 || p->V > 256) return GLA_ERR_UNSUPPORTED;
+  if (p->value_tile != 0 && p->value_tile != 64 && p->value_tile != 128) return GLA_ERR_UNSUPPORTED;
+  if (p->segment_chunks < 0 || (p->packed != 0 && p->packed != 1) || p->wait_limit < -1) return GLA_ERR_BAD_SHAPE;
   if (p->packed ? p->B != 1 : p->n_seqs != p->B) return GLA_ERR_BAD_SHAPE;
-  // element counts must stay addressable
-  const double elems = (double)p->B * p->T * p->H * (p->K > p->V ? p->K : p->V);
-  if (elems > 9.0e15) return GLA_ERR_BAD_SHAPE;
+  // token-head rows and state elements must stay addressable with 64-bit
+  // offsets; one chunk's byte range of any tensor (64 token rows of H heads)
+  // must stay below 2^30, where the kernels put lanes with nothing to load
+  const double rows = (double)p->B * p->T * p->H;
+  if (rows * (p->K > p->V ? p->K : p->V) > 4.0e15) return GLA_ERR_BAD_SHAPE;
+  if ((long long)p->H * (p->K > p->V ? p->K : p->V) > (1LL << 22)) return GLA_ERR_BAD_SHAPE;
   return GLA_OK;
 }
 
-// How the sequence axis is cut into state segments.
+// How the sequence axis is cut into state segments, and the workspace layout.
 struct Plan {
   bool varlen;
   int N;          // sequences
@@ -63,34 +91,41 @@ struct Plan {
   int P;          // segments per sequence (fixed length)
   int seg_slots;  // upper bound on segments over all sequences
   int vtile;      // value columns per workgroup
+  int NV;         // value slices per (segment, head)
+  int nkb;        // key blocks
+  int kb[2];      // keys per block
   bool segmented; // some sequence may span several segments
-  size_t ws_state, ws_decay, ws_base, ws_total;
+  long long units;
+  size_t ws_state, ws_decay, ws_base, ws_opart, ws_total;
+  bool ok;        // index spaces fit the kernels' 32-bit grids
 };
 
 Plan make_plan(const gla_problem *p, bool varlen) {
   Plan pl{};
   pl.varlen = varlen;
   pl.N = varlen ? p->n_seqs : p->B;
+  pl.nkb = key_blocks(p->K, pl.kb);
   const int H = p->H;
+  const bool fast = uses_bf16_walker(p);
   // Value columns per workgroup.  The bf16 walker's 128-column workgroups form
   // the gated operands of a head once for all 128 columns; they are used when
   // they alone fill the device, or when sequences must be cut into segments
   // anyway.  Otherwise 64-column workgroups double the parallelism without
-  // segmenting.  GLA_BF16_VTILE=64 / =128 fixes the choice (A/B runs).
+  // segmenting.  value_tile fixes the choice.
   int vtile = kVTile;
-  if (gla::bf16_walker_used(p->dtype == GLA_BF16, p->K) && p->V % 128 == 0) {
+  if (fast) {
     const long long rows = (long long)pl.N * H;
-    const char *env = getenv("GLA_BF16_VTILE");
-    if (env != nullptr && strcmp(env, "64") == 0) vtile = 64;
-    else if (env != nullptr && strcmp(env, "128") == 0) vtile = 128;
+    if (p->value_tile != 0) vtile = p->value_tile;
+    else if (p->V % 128 != 0) vtile = 64;
     else if (varlen || rows * (p->V / 128) >= device_cu_count()) vtile = 128;
     else vtile = rows * (p->V / 64) >= device_cu_count() ? 64 : 128;
   }
   pl.vtile = vtile;
-  const int NV = p->V / vtile;
+  pl.NV = (p->V + vtile - 1) / vtile;
+  const int NV = pl.NV;
   const long long chunks_total = ((long long)p->T + kChunk - 1) / kChunk;  // varlen: packed axis
   const long long chunks_seq = chunks_total;  // longest possible sequence
-  int R = p->segment_chunks;
+  long long R = p->segment_chunks;
   if (R == 0) {
     // Enough (segment, head, value slice) workgroups to give every compute
     // unit work; long sequences with few heads are cut into segments.  A
@@ -99,11 +134,11 @@ Plan make_plan(const gla_problem *p, bool varlen) {
     const long long units_one = (long long)pl.N * H * NV;
     if (!varlen) {
       if (units_one >= device_cu_count() || chunks_seq <= 1) {
-        R = (int)(chunks_seq > 0 ? chunks_seq : 1);
+        R = chunks_seq > 0 ? chunks_seq : 1;
       } else {
         long long P = (target + units_one - 1) / units_one;
         if (P > chunks_seq) P = chunks_seq;
-        R = (int)((chunks_seq + P - 1) / P);
+        R = (chunks_seq + P - 1) / P;
       }
     } else {
       // packed: about 1.5 segment workgroups per compute unit balances the
@@ -114,30 +149,39 @@ Plan make_plan(const gla_problem *p, bool varlen) {
       const long long tgt = vtile == 128 ? (3LL * device_cu_count()) / 2 : target;
       long long r = (work + tgt - 1) / tgt;
       if (r < 4) r = 4;
-      R = (int)r;
+      R = r;
     }
     if (R < 1) R = 1;
   }
-  pl.R = R;
+  if (R > INT_MAX) R = INT_MAX;
+  pl.R = (int)R;
+  long long slots;
   if (!varlen) {
     const long long P = chunks_seq <= 0 ? 1 : (chunks_seq + R - 1) / R;
-    pl.P = (int)P;
-    pl.seg_slots = pl.N * pl.P;
-    pl.segmented = pl.P > 1;
+    pl.P = P > INT_MAX ? INT_MAX : (int)P;
+    slots = (long long)pl.N * P;
+    pl.segmented = P > 1;
   } else {
     pl.P = 1;
     // every sequence has max(1, ceil(nc/R)) segments; nc <= len/64 + 1
-    const long long bound = pl.N + (chunks_total + pl.N + R - 1) / R;
-    pl.seg_slots = (int)bound;
+    slots = pl.N + (chunks_total + pl.N + R - 1) / R;
     pl.segmented = chunks_total > R;  // a sequence needs more than one segment only if it has > R chunks
   }
+  pl.seg_slots = slots > INT_MAX ? INT_MAX : (int)slots;
+  pl.units = (pl.segmented ? slots : (long long)pl.N * (varlen ? 1 : pl.P)) * H;
+  // grids: walker blocks = ceil(units / 8) * 8 * NV; scan blocks = N * H * ceil(K V / 1024)
+  const long long walk_blocks = (pl.units + 7) / 8 * 8 * NV;
+  const long long kmax = pl.kb[0] > pl.kb[1] ? pl.kb[0] : pl.kb[1];
+  const long long scan_blocks = (long long)pl.N * H * ((kmax * p->V / 4 + 255) / 256);
+  pl.ok = slots <= INT_MAX && pl.units <= INT_MAX && walk_blocks <= INT_MAX && scan_blocks <= INT_MAX;
   if (pl.segmented) {
-    pl.ws_state = (size_t)pl.seg_slots * H * p->K * p->V * sizeof(float);
-    pl.ws_decay = (size_t)pl.seg_slots * H * p->K * sizeof(float);
-    pl.ws_base = varlen ? (size_t)(pl.N + 1 + pl.seg_slots) * sizeof(int32_t) : 0;  // table + order
+    pl.ws_state = (size_t)slots * H * kmax * p->V * sizeof(float);
+    pl.ws_decay = (size_t)slots * H * kmax * sizeof(float);
+    pl.ws_base = varlen ? (size_t)(pl.N + 1 + slots) * sizeof(int32_t) : 0;  // table + order
   }
+  if (pl.nkb == 2) pl.ws_opart = (size_t)p->B * p->T * H * p->V * sizeof(float);
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  pl.ws_total = up(pl.ws_state) + up(pl.ws_decay) + up(pl.ws_base);
+  pl.ws_total = kHeaderBytes + up(pl.ws_state) + up(pl.ws_decay) + up(pl.ws_base) + up(pl.ws_opart);
   return pl;
 }
 
@@ -152,7 +196,7 @@ const char *gla_status_str(gla_status s) {
     case GLA_ERR_BAD_SHAPE: return "invalid or inconsistent sizes";
     case GLA_ERR_BAD_DTYPE: return "dtype must be GLA_F32 or GLA_BF16";
     case GLA_ERR_BAD_SCALE: return "scale must be finite and > 0";
-    case GLA_ERR_UNSUPPORTED: return "unsupported K, V or chunk for the built kernels";
+    case GLA_ERR_UNSUPPORTED: return "unsupported K, V, chunk or value tile";
     case GLA_ERR_WORKSPACE: return "workspace missing or too small";
     case GLA_ERR_HIP: return "HIP runtime or launch failure";
   }
@@ -161,7 +205,9 @@ const char *gla_status_str(gla_status s) {
 
 size_t gla_fwd_workspace_bytes(const gla_problem *p) {
   if (validate(p) != GLA_OK) return (size_t)-1;
-  return make_plan(p, p->packed == 1).ws_total;
+  const Plan pl = make_plan(p, p->packed == 1);
+  if (!pl.ok) return (size_t)-1;
+  return pl.ws_total;
 }
 
 gla_status gla_fwd(const gla_problem *p, const void *q, const void *k, const void *v, const float *g,
@@ -174,37 +220,58 @@ gla_status gla_fwd(const gla_problem *p, const void *q, const void *k, const voi
   const bool empty_tokens = (long long)p->B * p->T == 0;
   if (!empty_tokens && (!q || !k || !v || !g || !o)) return GLA_ERR_NULL_ARG;
   const int N = varlen ? p->n_seqs : p->B;
-  if (N == 0) return GLA_OK;  // nothing to compute and no state to return
   const Plan pl = make_plan(p, varlen);
-  if (pl.ws_total > 0 && (workspace == nullptr || workspace_bytes < pl.ws_total)) return GLA_ERR_WORKSPACE;
+  if (!pl.ok) return GLA_ERR_BAD_SHAPE;
+  if (workspace == nullptr || workspace_bytes < pl.ws_total) return GLA_ERR_WORKSPACE;
+  if (N == 0) return GLA_OK;  // nothing to compute and no state to return
   if (empty_tokens && ht == nullptr) return GLA_OK;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  gla::WalkParams w{};
-  w.q = q; w.k = k; w.v = v; w.g = g; w.h0 = h0; w.cu = cu_seqlens; w.o = o; w.ht = ht;
+  const bool fast = uses_bf16_walker(p);
+  const bool bf = p->dtype == GLA_BF16;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   char *ws = reinterpret_cast<char *>(workspace);
-  w.seg_state = pl.segmented ? reinterpret_cast<float *>(ws) : nullptr;
-  w.seg_decay = pl.segmented ? reinterpret_cast<float *>(ws + up(pl.ws_state)) : nullptr;
-  int32_t *seg_base = (pl.segmented && varlen)
-                          ? reinterpret_cast<int32_t *>(ws + up(pl.ws_state) + up(pl.ws_decay))
-                          : nullptr;
+  gla::WalkParams w{};
+  w.q = q; w.k = k; w.v = v; w.g = g; w.h0 = h0; w.cu = cu_seqlens; w.o = o; w.ht = ht;
+  w.status = reinterpret_cast<uint32_t *>(ws);
+  char *cur = ws + kHeaderBytes;
+  w.seg_state = pl.segmented ? reinterpret_cast<float *>(cur) : nullptr;
+  cur += up(pl.ws_state);
+  w.seg_decay = pl.segmented ? reinterpret_cast<float *>(cur) : nullptr;
+  cur += up(pl.ws_decay);
+  int32_t *seg_base = (pl.segmented && varlen) ? reinterpret_cast<int32_t *>(cur) : nullptr;
+  cur += up(pl.ws_base);
+  float *o_part = pl.nkb == 2 ? reinterpret_cast<float *>(cur) : nullptr;
   w.seg_base = seg_base;
   w.seg_order = seg_base ? seg_base + N + 1 : nullptr;
-  w.T = p->T; w.H = p->H; w.K = p->K; w.V = p->V; w.N = N;
+  w.T = p->T; w.H = p->H; w.V = p->V; w.N = N;
+  w.Kmem = p->K;
   w.R = pl.R;
   w.P = pl.P;
-  w.units = (pl.segmented ? pl.seg_slots : (varlen ? N : N * pl.P)) * p->H;
+  w.units = (int)pl.units;
+  w.seg_slots = pl.seg_slots;
   w.vtile = pl.vtile;
+  w.wait_polls = p->wait_limit == 0 ? gla::kDefaultWaitPolls : (p->wait_limit < 0 ? 0 : p->wait_limit);
   w.scale = p->scale;
-  const bool bf = p->dtype == GLA_BF16;
 
   if (seg_base && gla::launch_segment_plan(w, seg_base, seg_base + N + 1, s) != hipSuccess) return GLA_ERR_HIP;
-  if (pl.segmented) {
-    if (gla::launch_walk(true, bf, p->K, w, s) != hipSuccess) return GLA_ERR_HIP;
-    if (gla::launch_state_scan(w, s) != hipSuccess) return GLA_ERR_HIP;
+  int koff = 0;
+  for (int b = 0; b < pl.nkb; ++b) {
+    w.K = pl.kb[b];
+    w.koff = koff;
+    w.o_part = (pl.nkb == 2 && b == 0) ? o_part : nullptr;
+    w.o_add = (pl.nkb == 2 && b == 1) ? o_part : nullptr;
+    const int kd = kernel_key_width(fast, bf, w.K);
+    auto walk = [&](bool local_mode) {
+      return fast ? gla::launch_walk_bf16(local_mode, kd, w, s) : gla::launch_walk_general(local_mode, bf, kd, w, s);
+    };
+    if (pl.segmented) {
+      if (walk(true) != hipSuccess) return GLA_ERR_HIP;
+      if (gla::launch_state_scan(w, s) != hipSuccess) return GLA_ERR_HIP;
+    }
+    if (walk(false) != hipSuccess) return GLA_ERR_HIP;
+    koff += w.K;
   }
-  if (gla::launch_walk(false, bf, p->K, w, s) != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
 }
 

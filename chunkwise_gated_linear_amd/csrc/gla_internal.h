@@ -1,5 +1,5 @@
 // Internal interface between the host library (gla_host.hip) and the device
-// kernels (gla_kernels.hip).  Not part of the public C ABI.
+// kernels (gla_kernels.hip, gla_walk_bf16.hip).  Not part of the public C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -8,38 +8,53 @@
 namespace gla {
 
 constexpr int kChunk = 64;     // tokens per chunk
-constexpr int kVTile = 64;     // value columns handled by one workgroup
-constexpr int kThreads = 256;  // threads per walker workgroup (4 waves of 64)
+constexpr int kVTile = 64;     // value columns handled by one general-walker workgroup
+constexpr int kThreads = 256;  // threads per general-walker workgroup (4 waves of 64)
+constexpr int kMaxKeyBlock = 128;  // keys one launch handles; wider K is cut into key blocks
+constexpr int kDefaultWaitPolls = 1 << 22;
 
 // Everything a launch needs; passed by value as the kernel argument.
+//
+// Key blocks: one launch covers keys [koff, koff + K) of the Kmem keys per head
+// in q, k, g, h0 and ht.  Every key row of the state evolves on its own, so the
+// output is the sum of the key blocks' outputs: with two blocks the first writes
+// its fp32 partial output to o_part, the second adds o_add (= that partial)
+// before rounding and storing o.
 struct WalkParams {
-  const void *q, *k, *v;       // [B,T,H,K] / [B,T,H,V], dtype per instantiation
-  const float *g;              // [B,T,H,K]
-  const float *h0;             // [N,H,K,V] or null
+  const void *q, *k, *v;       // [B,T,H,Kmem] / [B,T,H,V], dtype per instantiation
+  const float *g;              // [B,T,H,Kmem]
+  const float *h0;             // [N,H,Kmem,V] or null
   const int32_t *cu;           // [N+1] or null
   void *o;                     // [B,T,H,V]
-  float *ht;                   // [N,H,K,V] or null
+  float *ht;                   // [N,H,Kmem,V] or null
   float *seg_state;            // [seg_slots][H][K][V]: segment summaries, then start states
   float *seg_decay;            // [seg_slots][H][K]: product of the segment's decays
   const int32_t *seg_base;     // [N+1] first segment of each packed sequence, or null
-  const int32_t *seg_order;    // [segments] segment ids, longest first (packed), or null
-  int32_t T, H, K, V, N;
+  const int32_t *seg_order;    // [seg_slots] segment ids, longest first (packed), or null
+  uint32_t *status;            // sticky status word (GLA_STATUS_* bits)
+  float *o_part;               // [B,T,H,V] fp32: write the partial output here instead of o, or null
+  const float *o_add;          // [B,T,H,V] fp32: partial output of the other key block, or null
+  int32_t T, H, K, V, N;       // K: keys of this launch's block
+  int32_t Kmem;                // keys per head in memory (row stride of q, k, g, h0, ht)
+  int32_t koff;                // first key of this launch's block
   int32_t R;                   // chunks per segment
   int32_t P;                   // segments per sequence when seg_base is null
   int32_t units;               // (segment, head) pairs covered by the grid
+  int32_t seg_slots;           // segment slots the workspace holds
   int32_t vtile;               // value columns per workgroup (64, or 128 for the bf16 walker)
+  int32_t wait_polls;          // bound on each wait between waves (0: none, report at once)
   float scale;
 };
 
 // Launchers (return the hipGetLastError() of the launch).
-hipError_t launch_walk(bool local_mode, bool bf16, int K, const WalkParams &p, hipStream_t s);
+// The general walker (gla_kernels.hip): fp32 any key block, bf16 key blocks of a
+// split K; kd is the padded key width of the instantiation (16, 32, 64, 128).
+hipError_t launch_walk_general(bool local_mode, bool bf16, int kd, const WalkParams &p, hipStream_t s);
 hipError_t launch_state_scan(const WalkParams &p, hipStream_t s);
-// bf16 walker for K in {64, 128} (gla_walk_bf16.hip), 64 or 128 value columns
-// per workgroup (WalkParams::vtile)
-bool walk_bf16_supported(int K);
-hipError_t launch_walk_bf16(bool local_mode, int K, const WalkParams &p, hipStream_t s);
-// whether launch_walk runs the bf16 walker for this dtype and K
-bool bf16_walker_used(bool bf16, int K);
 hipError_t launch_segment_plan(const WalkParams &p, int32_t *seg_base, int32_t *seg_order, hipStream_t s);
+// bf16 walker (gla_walk_bf16.hip): key widths kd in {64, 128} (a narrower key
+// block is padded with zero keys), 64 or 128 value columns per workgroup
+// (WalkParams::vtile), any V (columns past V are masked)
+hipError_t launch_walk_bf16(bool local_mode, int kd, const WalkParams &p, hipStream_t s);
 
 }  // namespace gla

@@ -34,8 +34,14 @@
 //
 // Workgroup: 256 threads = 4 waves; one workgroup owns one (segment, head,
 // 64-column slice of V).  Wave w owns value columns [16w, 16w+16) of the
-// slice; its lanes hold the K x 16 state block in MFMA accumulator layout
+// slice; its lanes hold the KD x 16 state block in MFMA accumulator layout
 // (lane l: column l%16, rows 16*kt + 4*(l/16) + r).
+//
+// Shapes: a launch covers one key block of K <= KD keys (the instantiation's
+// width KD; keys K..KD-1 are zero padding: g = 0, q = k = 0, so they add
+// nothing and decay by exp(0) = 1) and value columns v0.. of each slice below V
+// (columns past V read as zero and are never stored).  With two key blocks the
+// first writes its fp32 partial output to o_part and the second adds it.
 #include "gla_internal.h"
 #include "gla_device.h"
 
@@ -100,7 +106,7 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
 
   // ---- which (segment, head, value slice) this workgroup owns; the value
   // slices of one unit sit 8 workgroup ids apart so they land on one XCD.
-  const int NV = p.V / VT;
+  const int NV = (p.V + VT - 1) / VT;
   const int b = blockIdx.x;
   const int grp = b / (8 * NV), rem = b - grp * (8 * NV);
   const int vt = rem >> 3;
@@ -118,26 +124,32 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
   const int c_end = min(c_begin + seg_len, nchunks);
   const int v0 = vt * VT;
   const int H = p.H;
-  const size_t rowK = (size_t)H * KD;  // element stride between tokens, q/k/g
-  const size_t rowV = (size_t)H * p.V; // element stride between tokens, v/o
+  const int nkeys = p.K;                // real keys of this block (<= KD)
+  const size_t rowK = (size_t)H * p.Kmem;  // element stride between tokens, q/k/g
+  const size_t rowV = (size_t)H * p.V;     // element stride between tokens, v/o
+  const size_t headK = (size_t)h * p.Kmem + p.koff;  // first key of the block in a token row
 
   // ---- state block of this lane: S[16kt + 4lg + r][v0 + 16wave + l16]
   f32x4_t S[NKT];
   const int scol = v0 + 16 * wave + l16;
+  const bool col_ok = scol < p.V;
   {
+    // h0 rows are [Kmem] wide (this block's rows start at koff), start states [K]
     const float *src = nullptr;
     if (OUT) {
       if (si.s == 0) {
-        if (p.h0) src = p.h0 + ((size_t)si.n * H + h) * KD * p.V;
+        if (p.h0) src = p.h0 + (((size_t)si.n * H + h) * p.Kmem + p.koff) * p.V;
       } else {
-        src = p.seg_state + ((size_t)(si.first + si.s - 1) * H + h) * KD * p.V;
+        src = p.seg_state + ((size_t)(si.first + si.s - 1) * H + h) * nkeys * p.V;
       }
     }
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        S[kt][r] = src ? src[(size_t)(16 * kt + 4 * lg + r) * p.V + scol] : 0.f;
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * kt + 4 * lg + r;
+        S[kt][r] = (src && col_ok && row < nkeys) ? src[(size_t)row * p.V + scol] : 0.f;
+      }
   }
 
   // zero the score block once: tiles above the diagonal are read by the
@@ -156,14 +168,16 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
   f32x4_t rg_g[RPG];
   QReg rg_q[RPG], rg_k[RPG], rg_v[4];
 
+  const bool key_ok = 4 * cq < nkeys;        // this thread's key quad is a real key
+  const bool vcol_ok = v0 + 4 * vq < p.V;  // this thread's v column quad exists
   auto load_chunk = [&](int c) {
-    const int t0 = si.bos + c * C;
+    const size_t t0 = (size_t)si.bos + (size_t)c * C;
     const int valid = min(C, si.len - c * C);
 #pragma unroll
     for (int r = 0; r < RPG; ++r) {
       const int row = rg * RPG + r;
-      const bool ok = row < valid;
-      const size_t off = ((size_t)(t0 + row)) * rowK + (size_t)h * KD + 4 * cq;
+      const bool ok = row < valid && key_ok;
+      const size_t off = (t0 + row) * rowK + headK + 4 * cq;
       rg_g[r] = ok ? *reinterpret_cast<const f32x4_t *>(p.g + off) : f32x4_t{0, 0, 0, 0};
       if constexpr (BF) {
         rg_k[r] = ok ? *reinterpret_cast<const u32x2_t *>((const uint16_t *)p.k + off) : u32x2_t{0, 0};
@@ -176,8 +190,8 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * vg + r;
-      const bool ok = row < valid;
-      const size_t off = ((size_t)(t0 + row)) * rowV + (size_t)h * p.V + v0 + 4 * vq;
+      const bool ok = row < valid && vcol_ok;
+      const size_t off = (t0 + row) * rowV + (size_t)h * p.V + v0 + 4 * vq;
       if constexpr (BF)
         rg_v[r] = ok ? *reinterpret_cast<const u32x2_t *>((const uint16_t *)p.v + off) : u32x2_t{0, 0};
       else
@@ -458,6 +472,23 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
           }
         }
       }
+      // ---- key blocks: add the other block's fp32 partial output, or write this
+      // block's partial instead of o (rows 16it + 4lg + r, column scol)
+      if (p.o_add != nullptr || p.o_part != nullptr) {
+        const int valid = min(C, si.len - c * C);
+        const size_t t0 = (size_t)si.bos + (size_t)c * C;
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 16 * it + 4 * lg + r;
+            if (row < valid && col_ok) {
+              const size_t idx = (t0 + row) * rowV + (size_t)h * p.V + scol;
+              if (p.o_add != nullptr) o[it][r] += p.o_add[idx];
+              else p.o_part[idx] = o[it][r];
+            }
+          }
+      }
       // ---- stage o (rows 16it + 4lg + r, column 16wave + l16) for coalesced stores
 #pragma unroll
       for (int it = 0; it < 4; ++it)
@@ -491,14 +522,15 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
     }
     __syncthreads();
 
-    if constexpr (OUT) {
-      // ---- coalesced output stores: 16-byte pieces of the staged tile
+    if (OUT && p.o_part == nullptr) {
+      // ---- coalesced output stores: 16-byte pieces of the staged tile (a piece
+      // holds 16 / ES columns, all below V or all past it)
       const int valid = min(C, si.len - c * C);
       const size_t t0 = (size_t)si.bos + (size_t)c * C;
       constexpr int PIECES_PER_ROW = VT * ES / 16;
       for (int pc = tid; pc < C * PIECES_PER_ROW; pc += kThreads) {
         const int row = pc / PIECES_PER_ROW, piece = pc - row * PIECES_PER_ROW;
-        if (row < valid) {
+        if (row < valid && v0 + piece * (16 / ES) < p.V) {
           const u32x4_t val = lds_ld<u32x4_t>(smem + L::oO, row * L::OROW + piece * 16);
           char *dst = reinterpret_cast<char *>(p.o) +
                       (((t0 + row) * rowV + (size_t)h * p.V + v0) * ES) + piece * 16;
@@ -509,25 +541,25 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
   }
 
   // ================= results of the segment
+  // (rows of padded keys and columns past V are not stored)
+  float *dst = nullptr;
   if constexpr (OUT) {
-    if (p.ht != nullptr && si.s == si.nseg - 1) {
-      float *dst = p.ht + ((size_t)si.n * H + h) * KD * p.V;
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(size_t)(16 * kt + 4 * lg + r) * p.V + scol] = S[kt][r];
-    }
+    if (p.ht != nullptr && si.s == si.nseg - 1) dst = p.ht + (((size_t)si.n * H + h) * p.Kmem + p.koff) * p.V;
   } else {
-    const int slot = si.first + si.s;
-    float *dst = p.seg_state + ((size_t)slot * H + h) * KD * p.V;
+    dst = p.seg_state + ((size_t)(si.first + si.s) * H + h) * nkeys * p.V;
+  }
+  if (dst != nullptr && col_ok) {
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(size_t)(16 * kt + 4 * lg + r) * p.V + scol] = S[kt][r];
-    if (vt == 0 && rg == 0) {
-      *reinterpret_cast<f32x4_t *>(p.seg_decay + ((size_t)slot * H + h) * KD + 4 * cq) =
-          f32x4_t{seg_decay[0], seg_decay[1], seg_decay[2], seg_decay[3]};
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * kt + 4 * lg + r;
+        if (row < nkeys) dst[(size_t)row * p.V + scol] = S[kt][r];
+      }
+  }
+  if (!OUT && vt == 0 && rg == 0 && key_ok) {
+    *reinterpret_cast<f32x4_t *>(p.seg_decay + ((size_t)(si.first + si.s) * H + h) * nkeys + 4 * cq) =
+        f32x4_t{seg_decay[0], seg_decay[1], seg_decay[2], seg_decay[3]};
   }
 }
 
@@ -544,14 +576,18 @@ __global__ __launch_bounds__(kThreads, 1) void gla_chunk_output(WalkParams p) {
 }
 
 // ---------------------------------------------------------------- state scan
-// One thread per 4 consecutive state elements of one (sequence, head):
-// start(0) = h0 or 0, start(s+1) = diag(decay_s) start(s) + summary_s; the
-// start state of segment s+1 overwrites the summary slot of segment s.
-__global__ __launch_bounds__(256) void gla_state_scan(WalkParams p) {
-  const int n = blockIdx.z, h = blockIdx.y;
-  const int e4 = blockIdx.x * 256 + threadIdx.x;
-  const int KV4 = p.K * p.V / 4;
-  if (e4 >= KV4) return;
+// One thread per 4 consecutive state elements of one (sequence, head) of the
+// key block: start(0) = h0 or 0, start(s+1) = diag(decay_s) start(s) +
+// summary_s; the start state of segment s+1 overwrites the summary slot of
+// segment s.  A 1-D grid: block b covers (sequence, head) b / per_state, and
+// 1024 elements of its K x V state.
+__global__ __launch_bounds__(256) void gla_state_scan(WalkParams p, int per_state) {
+  const long long pair = blockIdx.x / per_state;
+  const int eb = (int)(blockIdx.x - pair * per_state);
+  const int n = (int)(pair / p.H), h = (int)(pair - (long long)n * p.H);
+  const int e4 = eb * 256 + threadIdx.x;
+  const int KV4 = p.K * p.V / 4;  // V is a multiple of 16: a quad never crosses a row
+  if (n >= p.N || e4 >= KV4) return;
   int first, nseg;
   if (p.seg_base == nullptr) {
     first = n * p.P;
@@ -561,9 +597,10 @@ __global__ __launch_bounds__(256) void gla_state_scan(WalkParams p) {
     nseg = p.seg_base[n + 1] - first;
   }
   if (nseg <= 1) return;
-  const int krow = (4 * e4) / p.V;
+  const int krow = (4 * e4) / p.V, col = 4 * e4 - krow * p.V;
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-  if (p.h0) s = reinterpret_cast<const f32x4_t *>(p.h0 + ((size_t)n * p.H + h) * p.K * p.V)[e4];
+  if (p.h0)
+    s = *reinterpret_cast<const f32x4_t *>(p.h0 + (((size_t)n * p.H + h) * p.Kmem + p.koff + krow) * p.V + col);
   for (int j = 0; j + 1 < nseg; ++j) {
     const size_t slot = (size_t)(first + j) * p.H + h;
     const float a = p.seg_decay[slot * p.K + krow];
@@ -575,15 +612,23 @@ __global__ __launch_bounds__(256) void gla_state_scan(WalkParams p) {
 }
 
 // ---------------------------------------------------------------- varlen segment plan
-// seg_base[n] = sum over earlier sequences of max(1, ceil(ceil(len/64)/R)), and
-// seg_order = the segment ids sorted by length (chunks), longest first, so that
-// workgroups of long segments are dispatched before short ones.  A counting sort
-// over min(length, kOrderBuckets - 1); the order inside a bucket is arbitrary
-// (segments are independent, so results do not depend on it).
+// seg_base[n] = sum over earlier sequences of max(1, ceil(ceil(len/64)/R)),
+// capped at seg_slots, and seg_order = the segment ids sorted by length
+// (chunks), longest first, so that workgroups of long segments are dispatched
+// before short ones.  A counting sort over min(length, kOrderBuckets - 1); the
+// order inside a bucket is arbitrary (segments are independent, so results do
+// not depend on it).  Offsets are clamped to [0, T] (seq_extent), so offsets
+// that break the documented precondition change outputs but never the bounds
+// of any access; the cap keeps every segment id below seg_slots.
 constexpr int kOrderBuckets = 1024;
 
-__global__ __launch_bounds__(1024) void gla_segment_plan(const int32_t *cu, int N, int R, int32_t *seg_base,
-                                                         int32_t *seg_order) {
+__device__ __forceinline__ int seg_count(int len, int R) {
+  const int nc = (len + C - 1) / C;
+  return max(1, (nc + R - 1) / R);
+}
+
+__global__ __launch_bounds__(1024) void gla_segment_plan(const int32_t *cu, int N, int T, int R, int seg_slots,
+                                                         int32_t *seg_base, int32_t *seg_order) {
   __shared__ int32_t part[1024];
   __shared__ int32_t carry;
   __shared__ int32_t bucket[kOrderBuckets];
@@ -594,16 +639,14 @@ __global__ __launch_bounds__(1024) void gla_segment_plan(const int32_t *cu, int 
   }
   for (int i = tid; i < kOrderBuckets; i += 1024) bucket[i] = 0;
   __syncthreads();
+  // segment table (inclusive block scans of the per-sequence counts)
   for (int base = 0; base < N; base += 1024) {
     const int n = base + tid;
     int cnt = 0;
     if (n < N) {
-      const int len = cu[n + 1] - cu[n];
-      const int nc = (len + C - 1) / C;
-      cnt = max(1, (nc + R - 1) / R);
-      // segment lengths of this sequence (the walkers cut it the same way)
-      const int sl = (nc + cnt - 1) / cnt;
-      for (int s = 0; s < cnt; ++s) atomicAdd(&bucket[min(max(0, min(sl, nc - s * sl)), kOrderBuckets - 1)], 1);
+      int bos, len;
+      seq_extent(cu, n, T, bos, len);
+      cnt = seg_count(len, R);
     }
     part[tid] = cnt;
     __syncthreads();
@@ -613,11 +656,22 @@ __global__ __launch_bounds__(1024) void gla_segment_plan(const int32_t *cu, int 
       part[tid] += add;
       __syncthreads();
     }
-    if (n < N) seg_base[n + 1] = carry + part[tid];
+    if (n < N) seg_base[n + 1] = (int32_t)min((long long)carry + part[tid], (long long)seg_slots);
     __syncthreads();
-    if (tid == 1023) carry += part[1023];
+    if (tid == 1023) carry = (int32_t)min((long long)carry + part[1023], (long long)seg_slots);
     __syncthreads();
   }
+  // lengths of the segments each sequence actually gets (the walkers cut it the same way)
+  for (int n = tid; n < N; n += 1024) {
+    int bos, len;
+    seq_extent(cu, n, T, bos, len);
+    const int nc = (len + C - 1) / C;
+    const int cnt = seg_base[n + 1] - seg_base[n];  // written above by this or another thread
+    if (cnt <= 0) continue;
+    const int sl = (nc + cnt - 1) / cnt;
+    for (int s = 0; s < cnt; ++s) atomicAdd(&bucket[min(max(0, min(sl, nc - s * sl)), kOrderBuckets - 1)], 1);
+  }
+  __syncthreads();
   // start of each length bucket in the order, longest first: an exclusive scan
   // over the buckets from the longest down, one bucket per thread
   static_assert(kOrderBuckets == 1024, "one bucket per thread");
@@ -636,21 +690,23 @@ __global__ __launch_bounds__(1024) void gla_segment_plan(const int32_t *cu, int 
   }
   __syncthreads();
   for (int n = tid; n < N; n += 1024) {
-    const int len = cu[n + 1] - cu[n];
+    int bos, len;
+    seq_extent(cu, n, T, bos, len);
     const int nc = (len + C - 1) / C;
-    const int cnt = max(1, (nc + R - 1) / R);
+    const int first = seg_base[n];
+    const int cnt = seg_base[n + 1] - first;
+    if (cnt <= 0) continue;
     const int sl = (nc + cnt - 1) / cnt;
-    const int first = seg_base[n];  // written above by this or another thread of the block
     for (int s = 0; s < cnt; ++s) {
       const int slot = atomicAdd(&bucket[min(max(0, min(sl, nc - s * sl)), kOrderBuckets - 1)], 1);
-      seg_order[slot] = first + s;
+      seg_order[slot] = first + s;  // slot < seg_base[N] <= seg_slots
     }
   }
 }
 
 template <bool BF, int KD>
 hipError_t launch_walk_t(bool local_mode, const WalkParams &p, hipStream_t s) {
-  const int NV = p.V / VT;
+  const int NV = (p.V + VT - 1) / VT;
   const int groups = (p.units + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * NV));
   if (local_mode)
@@ -660,29 +716,18 @@ hipError_t launch_walk_t(bool local_mode, const WalkParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// GLA_GENERAL_WALKER=1 routes bf16 through the general walker (for A/B comparisons).
-bool general_walker_forced() {
-  static const bool forced = [] {
-    const char *e = getenv("GLA_GENERAL_WALKER");
-    return e != nullptr && e[0] == '1';
-  }();
-  return forced;
-}
-
 }  // namespace
 
-bool bf16_walker_used(bool bf16, int K) { return bf16 && walk_bf16_supported(K) && !general_walker_forced(); }
-
-hipError_t launch_walk(bool local_mode, bool bf16, int K, const WalkParams &p, hipStream_t s) {
-  if (bf16_walker_used(bf16, K)) return launch_walk_bf16(local_mode, K, p, s);
+hipError_t launch_walk_general(bool local_mode, bool bf16, int kd, const WalkParams &p, hipStream_t s) {
+  if (p.K > kd || p.vtile != VT) return hipErrorInvalidValue;
   if (bf16) {
-    switch (K) {
+    switch (kd) {
       case 32: return launch_walk_t<true, 32>(local_mode, p, s);
       case 64: return launch_walk_t<true, 64>(local_mode, p, s);
       case 128: return launch_walk_t<true, 128>(local_mode, p, s);
     }
   } else {
-    switch (K) {
+    switch (kd) {
       case 16: return launch_walk_t<false, 16>(local_mode, p, s);
       case 32: return launch_walk_t<false, 32>(local_mode, p, s);
       case 64: return launch_walk_t<false, 64>(local_mode, p, s);
@@ -694,13 +739,16 @@ hipError_t launch_walk(bool local_mode, bool bf16, int K, const WalkParams &p, h
 
 hipError_t launch_state_scan(const WalkParams &p, hipStream_t s) {
   const int KV4 = p.K * p.V / 4;
-  const dim3 grid((unsigned)((KV4 + 255) / 256), (unsigned)p.H, (unsigned)p.N);
-  hipLaunchKernelGGL(gla_state_scan, grid, dim3(256), 0, s, p);
+  const int per_state = (KV4 + 255) / 256;
+  const long long blocks = (long long)p.N * p.H * per_state;
+  if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gla_state_scan, dim3((unsigned)blocks), dim3(256), 0, s, p, per_state);
   return hipGetLastError();
 }
 
 hipError_t launch_segment_plan(const WalkParams &p, int32_t *seg_base, int32_t *seg_order, hipStream_t s) {
-  hipLaunchKernelGGL(gla_segment_plan, dim3(1), dim3(1024), 0, s, p.cu, p.N, p.R, seg_base, seg_order);
+  hipLaunchKernelGGL(gla_segment_plan, dim3(1), dim3(1024), 0, s, p.cu, p.N, p.T, p.R, p.seg_slots, seg_base,
+                     seg_order);
   return hipGetLastError();
 }
 

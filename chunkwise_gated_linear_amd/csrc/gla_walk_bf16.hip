@@ -28,6 +28,7 @@
 //    ds_read_b64_tr_b16, so no transposed copy is written.
 //  * Global traffic uses per-chunk buffer descriptors: rows past the end of a
 //    sequence read as zero and their output stores are dropped.
+#include "gla.h"
 #include "gla_device.h"
 #include "gla_internal.h"
 
@@ -134,17 +135,30 @@ __device__ __forceinline__ void scores_publish(char *flags, int mw, int c) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __hip_atomic_store(f + mw, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void scores_wait(char *flags, int c) {
+// Returns false when the bound ran out before every wave had published chunk c
+// (the wave then goes on with whatever the score tiles hold; the caller reports it).
+__device__ __forceinline__ bool scores_wait(char *flags, int c, int polls) {
   int *f = reinterpret_cast<int *>(flags);
-  for (int spin = 0; spin < (1 << 22); ++spin) {
+  bool ready = false;
+  for (int spin = 0; spin < polls; ++spin) {
     const int m = min(min(__hip_atomic_load(f + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP),
                           __hip_atomic_load(f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)),
                       min(__hip_atomic_load(f + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP),
                           __hip_atomic_load(f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)));
-    if (__builtin_amdgcn_readfirstlane(m) >= c) break;
+    if (__builtin_amdgcn_readfirstlane(m) >= c) {
+      ready = true;
+      break;
+    }
     __builtin_amdgcn_s_sleep(1);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  return ready;
+}
+
+// Sets bits in the caller-visible status word (a vector-memory atomic OR from
+// one lane; the word is only ever OR-ed, never cleared, by the kernels).
+__device__ __forceinline__ void report_status(uint32_t *status, uint32_t bits, int lane) {
+  if (lane == 0) __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Split of values that are not used after it (gated q and k rows, score
@@ -225,7 +239,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   // 64-column output workgroups share score tiles through LDS counters (the
   // producers skip that meeting); 128-column ones use a workgroup barrier
   constexpr bool HANDOFF = OUT && VW == 64;
-  static_assert(KD == 64 || KD == 128, "bf16 walker covers K = 64, 128");
+  static_assert(KD == 64 || KD == 128, "bf16 walker covers key widths 64, 128");
   static_assert(NG * QPW == 64 && RPG * NG == C, "producer mapping");
 
   const int tid = threadIdx.x;
@@ -236,7 +250,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 
   // ---- (segment, head, value slice) of this workgroup; value slices of one
   // unit are 8 workgroup ids apart so they run on the same XCD and share L2.
-  const int NV = p.V / VW;
+  const int NV = (p.V + VW - 1) / VW;
   const int b = blockIdx.x;
   const int grp = b / (8 * NV), rem = b - grp * (8 * NV);
   const int vt = rem >> 3;
@@ -254,8 +268,14 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   const int c_end = min(c_begin + seg_len, nchunks);
   const int H = p.H, V = p.V;
   const int v0 = vt * VW;
-  const int64_t rowK = (int64_t)H * KD, rowV = (int64_t)H * V;
-  const int seq_bos = si.bos, seq_len = si.len;
+  const int nkeys = p.K;  // real keys (<= KD); keys nkeys..KD-1 are zero padding
+  const int64_t rowK = (int64_t)H * p.Kmem, rowV = (int64_t)H * V;
+  const int64_t seq_bos = si.bos;
+  const int seq_len = si.len;
+  // Lanes whose key quad or value chunk lies past the real keys / columns use
+  // this offset: past every buffer range (the host keeps a chunk's range below
+  // 2^30 bytes), so their loads read zero and their stores are dropped.
+  constexpr int kOff = 1 << 30;
 
   // ======================= matrix waves: state and lane bases
   // matrix wave mw = CS kh + cw holds state rows KH kh .. + KH - 1, columns
@@ -264,12 +284,13 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   const int mw = wave & 3, kh = mw / CS, cw = mw % CS;
   f32x4_t S[NKT][NT];
   if (!producer) {
+    // h0 rows are [Kmem] wide (this block's rows start at koff), start states [nkeys]
     const float *src = nullptr;
     if (OUT) {
       if (si.s == 0) {
-        if (p.h0) src = p.h0 + ((int64_t)si.n * H + h) * KD * V;
+        if (p.h0) src = p.h0 + (((int64_t)si.n * H + h) * p.Kmem + p.koff) * V;
       } else {
-        src = p.seg_state + ((int64_t)(si.first + si.s - 1) * H + h) * KD * V;
+        src = p.seg_state + ((int64_t)(si.first + si.s - 1) * H + h) * nkeys * V;
       }
     }
 #pragma unroll
@@ -277,8 +298,10 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          S[kt][nt][r] = src ? src[(int64_t)(KH * kh + 16 * kt + 4 * lg + r) * V + v0 + VQ * cw + 16 * nt + l16] : 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int row = KH * kh + 16 * kt + 4 * lg + r, col = v0 + VQ * cw + 16 * nt + l16;
+          S[kt][nt][r] = (src && row < nkeys && col < V) ? src[(int64_t)row * V + col] : 0.f;
+        }
   }
   if (OUT) {  // score tiles above the diagonal are read as zeros and never written
     for (int i = tid; i < 2 * L::APL / 16; i += L::THREADS)
@@ -313,12 +336,13 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   // producer thread pt: key columns 4cq..4cq+3 of rows rg*RPG..+RPG-1
   const int pt = tid - 4 * 64;
   const int cq = (wave - 4) * QPW + lane % QPW, rg = lane / QPW;
-  const int voff_g = (int)((rg * RPG * rowK + 4 * cq) * 4);
-  const int voff_k = (int)((rg * RPG * rowK + 4 * cq) * 2);
+  const bool key_ok = 4 * cq < nkeys;
+  const int voff_g = key_ok ? (int)((rg * RPG * rowK + 4 * cq) * 4) : kOff;
+  const int voff_k = key_ok ? (int)((rg * RPG * rowK + 4 * cq) * 2) : kOff;
   // v: 16 B chunk vch of token rows vrow + VRS j (VW / 8 lanes per row)
   constexpr int VCH = VW / 8, VRS = 64 * L::NPW / VCH, NVL = C / VRS;
   const int vrow = pt / VCH, vch = pt % VCH;
-  const int voff_v = (int)((vrow * rowV + 8 * vch) * 2);
+  const int voff_v = v0 + 8 * vch < V ? (int)((vrow * rowV + 8 * vch) * 2) : kOff;
   const int vstep = (int)(VRS * rowV * 2);
   const int step_g = (int)(rowK * 4), step_k = (int)(rowK * 2);
   const int colq = kperm_bf(4 * cq) * 2;
@@ -339,7 +363,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   auto rsrc = [&](int c) {
     const int64_t t0 = (int64_t)seq_bos + (int64_t)c * C;
     const int64_t valid = c < c_end ? min(C, seq_len - c * C) : 0;
-    const int64_t headK = (int64_t)h * KD, headV = (int64_t)h * V + v0;
+    const int64_t headK = (int64_t)h * p.Kmem + p.koff, headV = (int64_t)h * V + v0;
     Rsrc r;
     r.g = make_rsrc(p.g + t0 * rowK + headK, (valid * rowK - headK) * 4);
     r.q = make_rsrc((const uint16_t *)p.q + t0 * rowK + headK, OUT ? (valid * rowK - headK) * 2 : 0);
@@ -493,7 +517,8 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 #pragma unroll
     for (int i = 0; i < 16 / RPI; ++i) {
       const int row = 16 * mw + RPI * i + lane / LPR, ch = lane % LPR;
-      buf_st128_nt(rO, (int)((row * rowV + 8 * ch) * 2), lds_ld<u32x4_t>(smem + L::oS, L::so(row, 16 * ch)));
+      const int off = v0 + 8 * ch < V ? (int)((row * rowV + 8 * ch) * 2) : kOff;
+      buf_st128_nt(rO, off, lds_ld<u32x4_t>(smem + L::oS, L::so(row, 16 * ch)));
     }
   };
 
@@ -680,7 +705,9 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
           }
         };
         // the other waves' score tiles are needed from here on
-        if constexpr (HANDOFF) scores_wait(smem + L::oF, c);
+        if constexpr (HANDOFF) {
+          if (!scores_wait(smem + L::oF, c, p.wait_polls)) report_status(p.status, GLA_STATUS_WAIT_EXHAUSTED, lane);
+        }
         if (KS == 1 || kh == 0) av(std::integral_constant<int, 0>{});
         if (KS == 1 || kh == 1) av(std::integral_constant<int, 1>{});
         if constexpr (KS == 1) {
@@ -744,9 +771,9 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   // VW / 4 lanes x 16 B.
   float *dst = nullptr;
   if (OUT) {
-    if (p.ht != nullptr && si.s == si.nseg - 1) dst = p.ht + ((int64_t)si.n * H + h) * KD * V;
+    if (p.ht != nullptr && si.s == si.nseg - 1) dst = p.ht + (((int64_t)si.n * H + h) * p.Kmem + p.koff) * V;
   } else {
-    dst = p.seg_state + ((int64_t)(si.first + si.s) * H + h) * KD * V;
+    dst = p.seg_state + ((int64_t)(si.first + si.s) * H + h) * nkeys * V;
   }
   static_assert(KD * VW * 4 <= (OUT ? L::oS : L::oDec), "state staging must not overlap the output staging");
   if (dst != nullptr && !producer) {
@@ -768,12 +795,13 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 #pragma unroll
     for (int i = wave; i < KD / RPI; i += L::THREADS / 64) {
       const int row = RPI * i + rr;
-      *reinterpret_cast<f32x4_t *>(dst + (int64_t)row * V + v0 + 4 * ch) = lds_ld<f32x4_t>(smem, 16 * (row * LPR + ch));
+      if (row < nkeys && v0 + 4 * ch < V)  // padded key rows and columns past V are not stored
+        *reinterpret_cast<f32x4_t *>(dst + (int64_t)row * V + v0 + 4 * ch) = lds_ld<f32x4_t>(smem, 16 * (row * LPR + ch));
     }
   }
-  if (producer && !OUT && vt == 0 && rg == 0) {
+  if (producer && !OUT && vt == 0 && rg == 0 && key_ok) {
     const int slot = si.first + si.s;
-    *reinterpret_cast<f32x4_t *>(p.seg_decay + ((int64_t)slot * H + h) * KD + 4 * cq) =
+    *reinterpret_cast<f32x4_t *>(p.seg_decay + ((int64_t)slot * H + h) * nkeys + 4 * cq) =
         f32x4_t{seg_decay[0], seg_decay[1], seg_decay[2], seg_decay[3]};
   }
 }
@@ -792,7 +820,7 @@ __global__ __launch_bounds__((LdsW<KD, false, VW>::THREADS), 1) void gla_chunk_l
 
 template <int KD, int VW>
 hipError_t launch_t(bool local_mode, const WalkParams &p, hipStream_t s) {
-  const int NV = p.V / VW;
+  const int NV = (p.V + VW - 1) / VW;
   const int groups = (p.units + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * NV));
   if (local_mode)
@@ -804,13 +832,11 @@ hipError_t launch_t(bool local_mode, const WalkParams &p, hipStream_t s) {
 
 }  // namespace
 
-bool walk_bf16_supported(int K) { return K == 64 || K == 128; }
-
-hipError_t launch_walk_bf16(bool local_mode, int K, const WalkParams &p, hipStream_t s) {
+hipError_t launch_walk_bf16(bool local_mode, int kd, const WalkParams &p, hipStream_t s) {
   const int vw = p.vtile;
-  if ((vw != 64 && vw != 128) || p.V % vw != 0) return hipErrorInvalidValue;
-  if (K == 128) return vw == 128 ? launch_t<128, 128>(local_mode, p, s) : launch_t<128, 64>(local_mode, p, s);
-  if (K == 64) return vw == 128 ? launch_t<64, 128>(local_mode, p, s) : launch_t<64, 64>(local_mode, p, s);
+  if ((vw != 64 && vw != 128) || p.K > kd || p.K % 16 != 0 || p.V % 16 != 0) return hipErrorInvalidValue;
+  if (kd == 128) return vw == 128 ? launch_t<128, 128>(local_mode, p, s) : launch_t<128, 64>(local_mode, p, s);
+  if (kd == 64) return vw == 128 ? launch_t<64, 128>(local_mode, p, s) : launch_t<64, 64>(local_mode, p, s);
   return hipErrorInvalidValue;
 }
 

@@ -25,10 +25,17 @@
  *    asynchronously: results are valid once that stream has reached the call.
  *  - Layout is time-major and contiguous: q, k, g are [B, T, H, K], v and o are
  *    [B, T, H, V], h0 and ht are [N, H, K, V] (row-major, V fastest).
- *  - Arguments are validated on the host before anything is enqueued; on any
- *    error nothing is written and the status says why.  The contents of
- *    cu_seqlens are a precondition (cu[0] = 0, non-decreasing, cu[N] = T) and
- *    are not checked.  NaN / Inf inputs propagate; they are not checked.
+ *  - Shapes: K and V are multiples of 16 in [16, 256]; any T >= 0, B >= 0,
+ *    H >= 1.  Arguments are validated on the host before anything is
+ *    enqueued; on any error nothing is written and the status says why.
+ *  - cu_seqlens contents are a precondition (cu[0] = 0, non-decreasing,
+ *    cu[N] = T) and are not checked.  Offsets that break it give undefined
+ *    output values but no access outside the caller's buffers: the kernels
+ *    clamp every sequence to [0, T) and never index past the workspace.
+ *  - NaN / Inf inputs propagate; they are not checked.  Finite gates are
+ *    supported while the summed log decay of one key over one 64-token chunk
+ *    stays above -80 (the in-chunk factors exp(G_i - G_last) are formed in
+ *    fp32); below that the outputs of that chunk are undefined.
  *  - Reentrant; the only global state is a per-device cache of the compute
  *    unit count.  Calls that share a workspace buffer must be ordered by the
  *    caller (same stream, or synchronised).
@@ -46,10 +53,11 @@ extern "C" {
 typedef enum gla_status {
     GLA_OK = 0,
     GLA_ERR_NULL_ARG = 1,     /* a required pointer is NULL                      */
-    GLA_ERR_BAD_SHAPE = 2,    /* negative / inconsistent sizes, B != 1 with cu_seqlens */
+    GLA_ERR_BAD_SHAPE = 2,    /* negative / inconsistent sizes, B != 1 with cu_seqlens,
+                                 or sizes whose index space exceeds the kernels' 32-bit grids */
     GLA_ERR_BAD_DTYPE = 3,    /* dtype is not GLA_F32 or GLA_BF16                */
     GLA_ERR_BAD_SCALE = 4,    /* scale is not finite and > 0                      */
-    GLA_ERR_UNSUPPORTED = 5,  /* K, V or chunk outside the built kernel shapes     */
+    GLA_ERR_UNSUPPORTED = 5,  /* K, V, chunk or value_tile outside the supported set */
     GLA_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than gla_fwd_workspace_bytes */
     GLA_ERR_HIP = 7           /* a HIP runtime call or kernel launch failed       */
 } gla_status;
@@ -59,12 +67,15 @@ typedef enum gla_dtype {
     GLA_BF16 = 1   /* q, k, v, o are bfloat16; g, h0, ht are float32 either way */
 } gla_dtype;
 
+/* Bits of the status word (see gla_fwd's workspace). */
+#define GLA_STATUS_WAIT_EXHAUSTED 1u  /* a bounded wait between waves ran out: o may be wrong */
+
 typedef struct gla_problem {
     int32_t B;        /* batch; must be 1 for packed sequences                         */
     int32_t T;        /* tokens per sequence, or total packed tokens with cu_seqlens  */
     int32_t H;        /* heads                                                        */
-    int32_t K;        /* key width: 32, 64 or 128 (bf16); 16, 32, 64 or 128 (fp32)   */
-    int32_t V;        /* value width: a positive multiple of 64                       */
+    int32_t K;        /* key width: a multiple of 16 in [16, 256]                      */
+    int32_t V;        /* value width: a multiple of 16 in [16, 256]                    */
     int32_t dtype;    /* gla_dtype of q, k, v and o                                   */
     int32_t n_seqs;   /* N: equal to B without cu_seqlens, len(cu_seqlens)-1 with it  */
     int32_t chunk;    /* chunk length in tokens; 64 is the supported value            */
@@ -73,12 +84,17 @@ typedef struct gla_problem {
                       /* sequence longer than this is split into segments whose start */
                       /* states are produced by a scan over segment summaries.        */
     int32_t packed;   /* 1 when cu_seqlens will be passed (packed sequences), else 0  */
+    int32_t value_tile; /* 0: automatic.  Else value columns per workgroup, 64 or 128 */
+                      /* (bf16 with K <= 128 only; a tuning choice, results agree)    */
+    int32_t wait_limit; /* 0: default bound on each wait between waves (2^22 polls);  */
+                      /* > 0: that many polls; -1: no polls, every such wait reports */
+                      /* GLA_STATUS_WAIT_EXHAUSTED at once (a test hook)               */
 } gla_problem;
 
 /*
- * Workspace bytes gla_fwd needs for problem `p` on the current device (0 when
- * no workspace is needed).  Returns (size_t)-1 when `p` is invalid.  The
- * value depends on the device's compute-unit count when segment_chunks is 0.
+ * Workspace bytes gla_fwd needs for problem `p` on the current device; at
+ * least 256.  Returns (size_t)-1 when `p` is invalid.  The value depends on
+ * the device's compute-unit count when segment_chunks is 0.
  */
 size_t gla_fwd_workspace_bytes(const gla_problem *p);
 
@@ -91,7 +107,12 @@ size_t gla_fwd_workspace_bytes(const gla_problem *p);
  *   ht     : [N,H,K,V] float32 or NULL; when non-NULL it receives the state after
  *            each sequence's last token (h0, or zeros, for an empty sequence)
  *   workspace / workspace_bytes : device scratch of at least
- *            gla_fwd_workspace_bytes(p) bytes (may be NULL when that is 0)
+ *            gla_fwd_workspace_bytes(p) bytes.  Its first 4 bytes are a sticky
+ *            status word (uint32, GLA_STATUS_* bits): the kernels only ever set
+ *            bits in it and the library never clears it, so the caller zeroes
+ *            it once (for example when allocating the workspace) and reads it
+ *            after the stream has reached the call.  The rest is scratch that
+ *            each call overwrites.
  *   stream : hipStream_t to enqueue on
  * Returns GLA_OK or an error code (see gla_status); on error nothing is written.
  */

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def prob(**kw):
     base = dict(B=2, T=100, H=3, K=64, V=128, dtype=gla.GLA_BF16, n_seqs=2, chunk=64, scale=0.125,
-                segment_chunks=1, packed=0)
+                segment_chunks=1, packed=0, value_tile=0, wait_limit=0)
     base.update(kw)
     return gla.Problem(**base)
 
@@ -53,7 +53,7 @@ def prob(**kw):
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
 
 
-def call(lib, p, q=FAKE, k=FAKE, v=FAKE, g=FAKE, cu=None, o=FAKE, ws=None, ws_bytes=0):
+def call(lib, p, q=FAKE, k=FAKE, v=FAKE, g=FAKE, cu=None, o=FAKE, ws=FAKE, ws_bytes=1 << 40):
     return lib.gla_fwd(ctypes.byref(p) if p is not None else None, q, k, v, g, None, cu, o, None,
                        ws, ws_bytes, None)
 
@@ -65,15 +65,20 @@ def call(lib, p, q=FAKE, k=FAKE, v=FAKE, g=FAKE, cu=None, o=FAKE, ws=None, ws_by
     (dict(scale=math.nan), BAD_SCALE),
     (dict(scale=math.inf), BAD_SCALE),
     (dict(chunk=32), UNSUPPORTED),
-    (dict(K=48), UNSUPPORTED),
-    (dict(K=256), UNSUPPORTED),
-    (dict(K=16), UNSUPPORTED),          # bf16 needs K in {32, 64, 128}
-    (dict(V=96), UNSUPPORTED),
+    (dict(K=8), UNSUPPORTED),           # K and V: multiples of 16 in [16, 256]
+    (dict(K=24), UNSUPPORTED),
+    (dict(K=272), UNSUPPORTED),
+    (dict(V=8), UNSUPPORTED),
+    (dict(V=40), UNSUPPORTED),
+    (dict(V=272), UNSUPPORTED),
+    (dict(value_tile=32), UNSUPPORTED),
     (dict(T=-1), BAD_SHAPE),
     (dict(H=0), BAD_SHAPE),
+    (dict(H=20000, K=256), BAD_SHAPE),  # one chunk of one tensor would span 2^30 bytes or more
     (dict(n_seqs=3), BAD_SHAPE),        # without packing N must equal B
     (dict(packed=1), BAD_SHAPE),        # packing needs B == 1
     (dict(segment_chunks=-2), BAD_SHAPE),
+    (dict(wait_limit=-2), BAD_SHAPE),
 ])
 def test_invalid_problems_are_rejected(lib, kw, code):
     p = prob(**kw)
@@ -81,37 +86,50 @@ def test_invalid_problems_are_rejected(lib, kw, code):
     assert lib.gla_fwd_workspace_bytes(ctypes.byref(p)) == ctypes.c_size_t(-1).value
 
 
-def test_fp32_accepts_k16(lib):
-    p = prob(dtype=gla.GLA_F32, K=16)
+@pytest.mark.parametrize("dtype", [gla.GLA_BF16, gla.GLA_F32])
+@pytest.mark.parametrize("K", [16, 48, 64, 96, 128, 144, 256])
+@pytest.mark.parametrize("V", [16, 96, 128, 256])
+def test_every_multiple_of_16_up_to_256_is_accepted(lib, dtype, K, V):
+    p = prob(dtype=dtype, K=K, V=V)
     assert lib.gla_fwd_workspace_bytes(ctypes.byref(p)) != ctypes.c_size_t(-1).value
 
 
-def test_null_arguments(lib):
-    assert call(lib, None) == NULL_ARG
-    assert call(lib, prob(), q=None) == NULL_ARG
-    assert call(lib, prob(), o=None) == NULL_ARG
-    # packed problem without offsets, offsets without a packed problem
-    assert call(lib, prob(B=1, n_seqs=4, packed=1), cu=None) == NULL_ARG
-    assert call(lib, prob(), cu=FAKE) == NULL_ARG
+def up(x):
+    return (x + 255) // 256 * 256
+
+
+WS_HEADER = 256  # status word + padding at the start of every workspace
 
 
 def test_workspace_size_and_check(lib):
     # B=2, T=1000 -> 16 chunks per sequence; 2 chunks per segment -> 8 segments each
     p = prob(T=1000, K=64, V=128, H=3, segment_chunks=2)
-    up = lambda x: (x + 255) // 256 * 256
     slots = 2 * 8
-    expect = up(slots * 3 * 64 * 128 * 4) + up(slots * 3 * 64 * 4)
+    expect = WS_HEADER + up(slots * 3 * 64 * 128 * 4) + up(slots * 3 * 64 * 4)
     assert lib.gla_fwd_workspace_bytes(ctypes.byref(p)) == expect
     assert call(lib, p, ws=None, ws_bytes=0) == WORKSPACE
     assert call(lib, p, ws=FAKE, ws_bytes=expect - 1) == WORKSPACE
-    # one segment per sequence needs no workspace
+    # one segment per sequence: the status header only
     p1 = prob(T=1000, segment_chunks=16)
-    assert lib.gla_fwd_workspace_bytes(ctypes.byref(p1)) == 0
-    # packed: slots bounded by N + ceil((ceil(T/64) + N) / R), plus N+1 offsets
+    assert lib.gla_fwd_workspace_bytes(ctypes.byref(p1)) == WS_HEADER
+    assert call(lib, p1, ws=None, ws_bytes=0) == WORKSPACE
+    # packed: slots bounded by N + ceil((ceil(T/64) + N) / R), plus N+1 offsets and the order
     pv = prob(B=1, T=1000, n_seqs=5, packed=1, segment_chunks=3)
     slots_v = 5 + -(-(16 + 5) // 3)
-    expect_v = up(slots_v * 3 * 64 * 128 * 4) + up(slots_v * 3 * 64 * 4) + up(6 * 4)
+    expect_v = WS_HEADER + up(slots_v * 3 * 64 * 128 * 4) + up(slots_v * 3 * 64 * 4) + up((6 + slots_v) * 4)
     assert lib.gla_fwd_workspace_bytes(ctypes.byref(pv)) == expect_v
+
+
+def test_workspace_of_split_keys(lib):
+    # K > 128 runs as two key blocks (here 80 + 64); the first block's fp32
+    # partial output [B, T, H, V] lives in the workspace, segment summaries are
+    # sized for the wider block
+    p = prob(T=1000, K=144, V=96, H=3, segment_chunks=16)
+    assert lib.gla_fwd_workspace_bytes(ctypes.byref(p)) == WS_HEADER + up(2 * 1000 * 3 * 96 * 4)
+    p2 = prob(T=1000, K=144, V=96, H=3, segment_chunks=2)
+    slots = 2 * 8
+    assert lib.gla_fwd_workspace_bytes(ctypes.byref(p2)) == (WS_HEADER + up(slots * 3 * 80 * 96 * 4)
+                                                            + up(slots * 3 * 80 * 4) + up(2 * 1000 * 3 * 96 * 4))
 
 
 def test_status_strings(lib):
