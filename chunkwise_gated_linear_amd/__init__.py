@@ -25,7 +25,7 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
-__all__ = ["gla_fwd", "GlaCall", "workspace_bytes", "library_path", "load_library", "GlaError",
+__all__ = ["gla_fwd", "gla_fwd_noalloc", "GlaCall", "workspace_bytes", "library_path", "load_library", "GlaError",
            "STATUS", "Problem", "STATUS_WAIT_EXHAUSTED", "read_status"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +74,8 @@ def load_library():
     lib.gla_fwd.argtypes = [ctypes.POINTER(Problem), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                             ctypes.c_size_t, vp]
     lib.gla_fwd.restype = ctypes.c_int
+    lib.gla_fwd_noalloc.argtypes = [ctypes.POINTER(Problem), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gla_fwd_noalloc.restype = ctypes.c_int
     lib.gla_status_str.argtypes = [ctypes.c_int]
     lib.gla_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -130,6 +132,66 @@ def gla_fwd(q, k, v, g, h0=None, cu_seqlens=None, scale: Optional[float] = None,
     import torch
 
     lib = load_library()
+    prob, N, dev = _problem_for(q, k, v, g, h0, cu_seqlens, out, scale, chunk, segment_chunks,
+                                value_tile, wait_limit)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    with torch.cuda.device(dev):
+        ws = lib.gla_fwd_workspace_bytes(ctypes.byref(prob))
+        if ws == ctypes.c_size_t(-1).value:
+            code_v = lib.gla_fwd(ctypes.byref(prob), None, None, None, None, None, None, None, None,
+                                 None, 0, None)
+            raise GlaError(code_v, _status_msg(lib, code_v))
+        o = out if out is not None else torch.empty_like(v)
+        if out is not None and (out.shape != v.shape or out.dtype != v.dtype):
+            raise ValueError("out must match v's shape and dtype")
+        ht = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+        if workspace is None or workspace.numel() * workspace.element_size() < ws:
+            workspace = _new_workspace(ws, dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.gla_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0),
+                         _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), stream)
+    if rc != 0:
+        raise GlaError(rc, _status_msg(lib, rc))
+    return o, ht
+
+
+def gla_fwd_noalloc(q, k, v, g, o, h0=None, cu_seqlens=None, ht=None, scale: Optional[float] = None,
+                    status=None, chunk: int = CHUNK, segment_chunks: int = 0, value_tile: int = 0) -> None:
+    """The forward through the library's no-allocation entry point (gla_fwd_noalloc).
+
+    The caller provides o (v's shape and dtype) and, when wanted, ht ([N, H, K, V]
+    float32) and a device int32 status word (zeroed; receives GLA_STATUS_* bits).
+    Nothing is allocated on the device; problems whose workspace would exceed the
+    library's 64 MiB scratch raise GlaError(GLA_ERR_WORKSPACE).  Asynchronous on
+    torch's current stream.
+    """
+    import torch
+
+    lib = load_library()
+    prob, N, dev = _problem_for(q, k, v, g, h0, cu_seqlens, o, scale, chunk, segment_chunks, value_tile, 0)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if o.shape != v.shape or o.dtype != v.dtype:
+        raise ValueError("o must match v's shape and dtype")
+    if ht is not None and (tuple(ht.shape) != (N, H, K, V) or ht.dtype != torch.float32 or ht.device != dev
+                           or not ht.is_contiguous()):
+        raise ValueError(f"ht must be a contiguous float32 [{N}, {H}, {K}, {V}] tensor on {dev}")
+    if status is not None and (status.dtype != torch.int32 or status.numel() < 1 or status.device != dev):
+        raise ValueError("status must be an int32 device tensor")
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.gla_fwd_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0),
+                                 _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(status), stream)
+    if rc != 0:
+        raise GlaError(rc, _status_msg(lib, rc))
+
+
+def _problem_for(q, k, v, g, h0, cu_seqlens, out, scale, chunk, segment_chunks, value_tile, wait_limit):
+    """Checks the tensors of a call and builds its gla_problem (page defaults for scale)."""
+    import torch
+
     if q.dim() != 4 or k.shape != q.shape or g.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("expected q, k, g [B, T, H, K] and v [B, T, H, V]")
     if not (q.dtype == k.dtype == v.dtype):
@@ -168,25 +230,7 @@ def gla_fwd(q, k, v, g, h0=None, cu_seqlens=None, scale: Optional[float] = None,
         raise ValueError("scale must be positive")
     prob = make_problem(B, T, H, K, V, code, N, chunk, scale, segment_chunks, cu_seqlens is not None,
                         value_tile, wait_limit)
-    with torch.cuda.device(dev):
-        ws = lib.gla_fwd_workspace_bytes(ctypes.byref(prob))
-        if ws == ctypes.c_size_t(-1).value:
-            code_v = lib.gla_fwd(ctypes.byref(prob), None, None, None, None, None, None, None, None,
-                                 None, 0, None)
-            raise GlaError(code_v, _status_msg(lib, code_v))
-        o = out if out is not None else torch.empty_like(v)
-        if out is not None and (out.shape != v.shape or out.dtype != v.dtype):
-            raise ValueError("out must match v's shape and dtype")
-        ht = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if output_final_state else None
-        if workspace is None or workspace.numel() * workspace.element_size() < ws:
-            workspace = _new_workspace(ws, dev)
-        stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = lib.gla_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0),
-                         _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(workspace),
-                         workspace.numel() * workspace.element_size(), stream)
-    if rc != 0:
-        raise GlaError(rc, _status_msg(lib, rc))
-    return o, ht
+    return prob, N, dev
 
 
 class GlaCall:

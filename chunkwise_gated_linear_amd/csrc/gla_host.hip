@@ -185,55 +185,21 @@ Plan make_plan(const gla_problem *p, bool varlen) {
   return pl;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char *gla_status_str(gla_status s) {
-  switch (s) {
-    case GLA_OK: return "ok";
-    case GLA_ERR_NULL_ARG: return "a required pointer is NULL";
-    case GLA_ERR_BAD_SHAPE: return "invalid or inconsistent sizes";
-    case GLA_ERR_BAD_DTYPE: return "dtype must be GLA_F32 or GLA_BF16";
-    case GLA_ERR_BAD_SCALE: return "scale must be finite and > 0";
-    case GLA_ERR_UNSUPPORTED: return "unsupported K, V, chunk or value tile";
-    case GLA_ERR_WORKSPACE: return "workspace missing or too small";
-    case GLA_ERR_HIP: return "HIP runtime or launch failure";
-  }
-  return "unknown status";
-}
-
-size_t gla_fwd_workspace_bytes(const gla_problem *p) {
-  if (validate(p) != GLA_OK) return (size_t)-1;
-  const Plan pl = make_plan(p, p->packed == 1);
-  if (!pl.ok) return (size_t)-1;
-  return pl.ws_total;
-}
-
-gla_status gla_fwd(const gla_problem *p, const void *q, const void *k, const void *v, const float *g,
-                   const float *h0, const int32_t *cu_seqlens, void *o, float *ht, void *workspace,
-                   size_t workspace_bytes, void *stream) {
-  gla_status st = validate(p);
-  if (st != GLA_OK) return st;
+// The launch sequence shared by the entry points: `workspace` holds at least
+// plan.ws_total bytes, `status` is the word the kernels report into.
+gla_status run_forward(const gla_problem *p, const Plan &pl, const void *q, const void *k, const void *v,
+                       const float *g, const float *h0, const int32_t *cu_seqlens, void *o, float *ht,
+                       char *ws, uint32_t *status, hipStream_t s) {
   const bool varlen = p->packed == 1;
-  if (varlen != (cu_seqlens != nullptr)) return GLA_ERR_NULL_ARG;
-  const bool empty_tokens = (long long)p->B * p->T == 0;
-  if (!empty_tokens && (!q || !k || !v || !g || !o)) return GLA_ERR_NULL_ARG;
   const int N = varlen ? p->n_seqs : p->B;
-  const Plan pl = make_plan(p, varlen);
-  if (!pl.ok) return GLA_ERR_BAD_SHAPE;
-  if (workspace == nullptr || workspace_bytes < pl.ws_total) return GLA_ERR_WORKSPACE;
   if (N == 0) return GLA_OK;  // nothing to compute and no state to return
-  if (empty_tokens && ht == nullptr) return GLA_OK;
-
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((long long)p->B * p->T == 0 && ht == nullptr) return GLA_OK;
   const bool fast = uses_bf16_walker(p);
   const bool bf = p->dtype == GLA_BF16;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  char *ws = reinterpret_cast<char *>(workspace);
   gla::WalkParams w{};
   w.q = q; w.k = k; w.v = v; w.g = g; w.h0 = h0; w.cu = cu_seqlens; w.o = o; w.ht = ht;
-  w.status = reinterpret_cast<uint32_t *>(ws);
+  w.status = status;
   char *cur = ws + kHeaderBytes;
   w.seg_state = pl.segmented ? reinterpret_cast<float *>(cur) : nullptr;
   cur += up(pl.ws_state);
@@ -273,6 +239,93 @@ gla_status gla_fwd(const gla_problem *p, const void *q, const void *k, const voi
     koff += w.K;
   }
   return GLA_OK;
+}
+
+// Host-side checks of a call (same for both entry points).
+gla_status check_call(const gla_problem *p, const void *q, const void *k, const void *v, const float *g,
+                      const void *o, const int32_t *cu_seqlens, Plan &pl) {
+  gla_status st = validate(p);
+  if (st != GLA_OK) return st;
+  const bool varlen = p->packed == 1;
+  if (varlen != (cu_seqlens != nullptr)) return GLA_ERR_NULL_ARG;
+  const bool empty_tokens = (long long)p->B * p->T == 0;
+  if (!empty_tokens && (!q || !k || !v || !g || !o)) return GLA_ERR_NULL_ARG;
+  pl = make_plan(p, varlen);
+  if (!pl.ok) return GLA_ERR_BAD_SHAPE;
+  return GLA_OK;
+}
+
+// Scratch of gla_fwd_noalloc: one array per device, resident until the process
+// ends.  Host code never uses the array's name as an address (on the host it
+// is a stand-in, not device memory): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+char *scratch_for_current_device() {
+  static std::mutex mu;
+  static char *addr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    addr[dev] = reinterpret_cast<char *>(ptr);
+  }
+  return addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gla_status_str(gla_status s) {
+  switch (s) {
+    case GLA_OK: return "ok";
+    case GLA_ERR_NULL_ARG: return "a required pointer is NULL";
+    case GLA_ERR_BAD_SHAPE: return "invalid or inconsistent sizes";
+    case GLA_ERR_BAD_DTYPE: return "dtype must be GLA_F32 or GLA_BF16";
+    case GLA_ERR_BAD_SCALE: return "scale must be finite and > 0";
+    case GLA_ERR_UNSUPPORTED: return "unsupported K, V, chunk or value tile";
+    case GLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case GLA_ERR_HIP: return "HIP runtime or launch failure";
+  }
+  return "unknown status";
+}
+
+size_t gla_fwd_workspace_bytes(const gla_problem *p) {
+  if (validate(p) != GLA_OK) return (size_t)-1;
+  const Plan pl = make_plan(p, p->packed == 1);
+  if (!pl.ok) return (size_t)-1;
+  return pl.ws_total;
+}
+
+gla_status gla_fwd(const gla_problem *p, const void *q, const void *k, const void *v, const float *g,
+                   const float *h0, const int32_t *cu_seqlens, void *o, float *ht, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+  Plan pl;
+  const gla_status st = check_call(p, q, k, v, g, o, cu_seqlens, pl);
+  if (st != GLA_OK) return st;
+  if (workspace == nullptr || workspace_bytes < pl.ws_total) return GLA_ERR_WORKSPACE;
+  char *ws = reinterpret_cast<char *>(workspace);
+  return run_forward(p, pl, q, k, v, g, h0, cu_seqlens, o, ht, ws, reinterpret_cast<uint32_t *>(ws),
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+gla_status gla_fwd_noalloc(const gla_problem *p, const void *q, const void *k, const void *v, const float *g,
+                           const float *h0, const int32_t *cu_seqlens, void *o, float *ht, uint32_t *status,
+                           void *stream) {
+  Plan pl;
+  const gla_status st = check_call(p, q, k, v, g, o, cu_seqlens, pl);
+  if (st != GLA_OK) return st;
+  if (pl.ws_total > kScratchBytes) return GLA_ERR_WORKSPACE;
+  char *ws = scratch_for_current_device();
+  if (ws == nullptr) return GLA_ERR_HIP;
+  // without a caller word, reports go to the scratch header, which nobody reads
+  return run_forward(p, pl, q, k, v, g, h0, cu_seqlens, o, ht, ws,
+                     status != nullptr ? status : reinterpret_cast<uint32_t *>(ws),
+                     reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

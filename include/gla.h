@@ -123,6 +123,28 @@ gla_status gla_fwd(const gla_problem *p,
                    void *workspace, size_t workspace_bytes,
                    void *stream);
 
+/*
+ * The same forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * instead of a caller workspace it uses a scratch array of 64 MiB that the
+ * library holds on each device it runs on until the process ends, and it
+ * calls no allocating routine.  Problems whose gla_fwd_workspace_bytes exceed
+ * 64 MiB are rejected with GLA_ERR_WORKSPACE (the scratch holds the segment
+ * summaries of long sequences and, for K > 128, the fp32 partial output
+ * B*T*H*V*4 bytes).  Arguments and outputs are as for gla_fwd.
+ *   status : a caller-owned device uint32 that receives the GLA_STATUS_* bits
+ *            (OR-ed, never cleared: zero it first), or NULL to discard them.
+ * Every call on one device shares that device's scratch: calls that overlap
+ * in time on one device (different streams without ordering between them)
+ * race and give undefined results; calls ordered on one stream are safe.
+ * Returns GLA_OK or an error code; on error nothing is written.
+ */
+gla_status gla_fwd_noalloc(const gla_problem *p,
+                           const void *q, const void *k, const void *v, const float *g,
+                           const float *h0, const int32_t *cu_seqlens,
+                           void *o, float *ht, uint32_t *status,
+                           void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *gla_status_str(gla_status s);
 

@@ -31,7 +31,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["gla_fwd", "gla_fwd_workspace_bytes", "gla_status_str"]
+    assert declared_functions() == ["gla_fwd", "gla_fwd_noalloc", "gla_fwd_workspace_bytes", "gla_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -56,6 +56,11 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails val
 def call(lib, p, q=FAKE, k=FAKE, v=FAKE, g=FAKE, cu=None, o=FAKE, ws=FAKE, ws_bytes=1 << 40):
     return lib.gla_fwd(ctypes.byref(p) if p is not None else None, q, k, v, g, None, cu, o, None,
                        ws, ws_bytes, None)
+
+
+def call_noalloc(lib, p, q=FAKE, k=FAKE, v=FAKE, g=FAKE, cu=None, o=FAKE):
+    return lib.gla_fwd_noalloc(ctypes.byref(p) if p is not None else None, q, k, v, g, None, cu, o, None,
+                               None, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -83,6 +88,7 @@ def call(lib, p, q=FAKE, k=FAKE, v=FAKE, g=FAKE, cu=None, o=FAKE, ws=FAKE, ws_by
 def test_invalid_problems_are_rejected(lib, kw, code):
     p = prob(**kw)
     assert call(lib, p) == code
+    assert call_noalloc(lib, p) == code
     assert lib.gla_fwd_workspace_bytes(ctypes.byref(p)) == ctypes.c_size_t(-1).value
 
 
@@ -130,6 +136,17 @@ def test_workspace_of_split_keys(lib):
     slots = 2 * 8
     assert lib.gla_fwd_workspace_bytes(ctypes.byref(p2)) == (WS_HEADER + up(slots * 3 * 80 * 96 * 4)
                                                             + up(slots * 3 * 80 * 4) + up(2 * 1000 * 3 * 96 * 4))
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    # the no-allocation entry point holds 64 MiB of device scratch; a larger
+    # workspace (here the fp32 partial output of split keys, 328 MB) is refused
+    # on the host before anything touches the device
+    big = prob(B=1, T=40000, H=8, K=256, V=256, n_seqs=1, segment_chunks=0)
+    assert lib.gla_fwd_workspace_bytes(ctypes.byref(big)) > (64 << 20)
+    assert call_noalloc(lib, big) == WORKSPACE
+    assert call_noalloc(lib, None) == NULL_ARG
+    assert call_noalloc(lib, prob(), q=None) == NULL_ARG
 
 
 def test_status_strings(lib):
