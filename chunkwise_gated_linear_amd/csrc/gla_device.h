@@ -209,6 +209,114 @@ __device__ __forceinline__ void buf_st64(__amdgpu_buffer_rsrc_t r, int off, u32x
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, off, 0, 0);
 }
 
+// ---------------------------------------------------------------- exact segment re-evaluation
+// Four consecutive elements (bf16 or fp32 storage) as floats.
+template <bool BF>
+__device__ __forceinline__ f32x4_t load4(const void *base, int64_t idx) {
+  if constexpr (BF) {
+    const u32x2_t w = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(base) + idx);
+    return f32x4_t{bf_lo(w[0]), bf_hi(w[0]), bf_lo(w[1]), bf_hi(w[1])};
+  } else {
+    return *reinterpret_cast<const f32x4_t *>(reinterpret_cast<const float *>(base) + idx);
+  }
+}
+template <bool BF>
+__device__ __forceinline__ float load1(const void *base, int64_t idx) {
+  if constexpr (BF) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(base)[idx] << 16);
+  else return reinterpret_cast<const float *>(base)[idx];
+}
+
+// Token-by-token re-evaluation of one (segment, head, value slice): the
+// recurrence itself, S = diag(exp(g_t)) S + k_t v_t^T and o_t = scale q_t^T S.
+// The walkers run it after their chunk loop for a segment in which some key
+// decayed by more than kMinChunkDecay over one chunk, beyond the fp32 range of
+// the factorised in-chunk form.
+//   OUT:  from the segment's start state (h0, or the start state the scan left
+//         in seg_state), rewrites o (or the key block's partial) for every token
+//         of the segment.
+//   !OUT: from a zero state, forms the segment summary, and writes the per-key
+//         product of decays (value slice 0).
+// With `stage` (the caller's [KD][VW] fp32 staging area) the final state is
+// written there, for the caller to store as ht or as the summary.
+// Wave w < VW / 16 takes columns v0 + 16 w + lane % 16; the four lane groups
+// lane / 16 hold contiguous quarters of the KD keys and are summed by shuffles.
+template <int KD, bool BF, bool OUT>
+__device__ void exact_segment(const WalkParams &p, const SegInfo &si, int h, int v0, int VW, int c_begin,
+                              int c_end, int wave, int vt, float *stage) {
+  if (wave >= VW / 16) return;
+  constexpr int KQ = KD / 4;  // keys per lane group
+  const int lane = threadIdx.x & 63, l16 = lane & 15, kg = lane >> 4;
+  const int col = v0 + 16 * wave + l16;
+  const bool col_ok = col < p.V;
+  const int nkeys = p.K;
+  const int64_t rowK = (int64_t)p.H * p.Kmem, rowV = (int64_t)p.H * p.V;
+  const int64_t headK = (int64_t)h * p.Kmem + p.koff, headV = (int64_t)h * p.V + col;
+  const float *src = nullptr;
+  if (OUT) {
+    if (si.s == 0) {
+      if (p.h0) src = p.h0 + (((int64_t)si.n * p.H + h) * p.Kmem + p.koff) * p.V;
+    } else {
+      src = p.seg_state + ((int64_t)(si.first + si.s - 1) * p.H + h) * nkeys * p.V;
+    }
+  }
+  float st[KQ], dec[KQ];
+#pragma unroll
+  for (int j = 0; j < KQ; ++j) {
+    const int key = kg * KQ + j;
+    st[j] = (src != nullptr && col_ok && key < nkeys) ? src[(int64_t)key * p.V + col] : 0.f;
+    dec[j] = 1.f;
+  }
+  const int t_end = min(c_end * C, si.len);
+  for (int t = c_begin * C; t < t_end; ++t) {
+    const int64_t tok = si.bos + t;
+    const float vv = col_ok ? load1<BF>(p.v, tok * rowV + headV) : 0.f;
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < KQ; j += 4) {
+      const int key = kg * KQ + j;  // a quad of keys is all real or all padding
+      if (key < nkeys) {
+        const int64_t kidx = tok * rowK + headK + key;
+        const f32x4_t g4 = *reinterpret_cast<const f32x4_t *>(p.g + kidx);
+        const f32x4_t k4 = load4<BF>(p.k, kidx);
+        f32x4_t q4 = {0.f, 0.f, 0.f, 0.f};
+        if (OUT) q4 = load4<BF>(p.q, kidx);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __expf(g4[r]);
+          st[j + r] = e * st[j + r] + k4[r] * vv;
+          if (OUT) part += q4[r] * st[j + r];
+          else dec[j + r] *= e;
+        }
+      }
+    }
+    if constexpr (OUT) {
+      part += __shfl_xor(part, 16);  // sum over the four key quarters
+      part += __shfl_xor(part, 32);
+      if (kg == 0 && col_ok) {
+        float ov = p.scale * part;
+        const int64_t oidx = tok * rowV + headV;
+        if (p.o_part != nullptr) {
+          p.o_part[oidx] = ov;
+        } else {
+          if (p.o_add != nullptr) ov += p.o_add[oidx];
+          if constexpr (BF) reinterpret_cast<__bf16 *>(p.o)[oidx] = (__bf16)ov;
+          else reinterpret_cast<float *>(p.o)[oidx] = ov;
+        }
+      }
+    }
+  }
+  if (!OUT && vt == 0 && wave == 0 && l16 == 0) {
+    float *dd = p.seg_decay + ((int64_t)(si.first + si.s) * p.H + h) * nkeys;
+#pragma unroll
+    for (int j = 0; j < KQ; ++j)
+      if (kg * KQ + j < nkeys) dd[kg * KQ + j] = dec[j];
+  }
+  if (stage != nullptr) {
+#pragma unroll
+    for (int j = 0; j < KQ; ++j) stage[(kg * KQ + j) * VW + 16 * wave + l16] = st[j];
+  }
+}
+
 // LDS transposing read of four 16-bit elements (ds_read_b64_tr_b16).  Within
 // each group of 16 lanes, lane j receives component j%4 of the 8-byte words
 // addressed by lanes j/4, j/4+4, j/4+8 and j/4+12 of its group.

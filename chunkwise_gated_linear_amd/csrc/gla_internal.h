@@ -12,6 +12,11 @@ constexpr int kVTile = 64;     // value columns handled by one general-walker wo
 constexpr int kThreads = 256;  // threads per general-walker workgroup (4 waves of 64)
 constexpr int kMaxKeyBlock = 128;  // keys one launch handles; wider K is cut into key blocks
 constexpr int kDefaultWaitPolls = 1 << 22;
+// Smallest decay of one key over one chunk (exp of its summed log decay) that
+// the factorised in-chunk form holds in fp32: its factors reach 1 / decay.
+// Chunks below it are evaluated token by token (e^-80).
+constexpr float kMinChunkDecay = 1.80485139e-35f;
+constexpr float kMinChunkLogDecay = -80.f;  // the same bound on the summed log decay
 
 // Everything a launch needs; passed by value as the kernel argument.
 //

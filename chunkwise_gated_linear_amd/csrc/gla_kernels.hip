@@ -75,7 +75,8 @@ struct Lds {
   static constexpr int oO = oA + (OUT ? NS * A_PLANE : 0);        // o   [C][VT]  (OUT)
   static constexpr int oDec = oO + (OUT ? C * OROW : 0);          // a   [K] fp32
   static constexpr int oTot = oDec + KD * 4;                     // group products [NG][K]
-  static constexpr int BYTES = oTot + NG * KD * 4;
+  static constexpr int oBad = oTot + NG * KD * 4;                 // a chunk needs the exact path (OUT)
+  static constexpr int BYTES = oBad + 16;
 };
 
 // P1 tiles (i-tile, j-tile) per wave: the 10 lower-triangular 16x16 tiles of the 64x64 score block.
@@ -200,7 +201,9 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
   };
 
   float seg_decay[4] = {1.f, 1.f, 1.f, 1.f};  // product of chunk decays (summary mode)
+  bool seg_bad = false;  // some key of a chunk decayed by more than kMinChunkDecay (OUT)
   const float scale = p.scale;
+  if (OUT && tid == 0) lds_st<int>(smem + L::oBad, 0, 0);
 
   if (c_begin < c_end) load_chunk(c_begin);
 
@@ -241,6 +244,9 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
     for (int j = 0; j < 4; ++j) {
       dec[j] = pre[j] * Pl[RPG - 1][j] * suf[j];   // a = product over the whole chunk
       fq[j] = OUT ? scale * pre[j] / dec[j] : 0.f;
+      // beyond this decay scale q exp(G - G_last) overflows: the segment's
+      // outputs are then re-evaluated token by token
+      if (OUT) seg_bad = seg_bad || dec[j] < kMinChunkDecay;
     }
     if (rg == 0) {
       lds_st<f32x4_t>(smem + L::oDec, 16 * cq, f32x4_t{dec[0], dec[1], dec[2], dec[3]});
@@ -541,6 +547,12 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
   }
 
   // ================= results of the segment
+  if constexpr (OUT) {
+    if (seg_bad) lds_st<int>(smem + L::oBad, 0, 1);
+    __syncthreads();  // also orders the chunk loop's output stores before a rewrite
+    if (__builtin_amdgcn_readfirstlane(lds_ld<int>(smem + L::oBad, 0)) != 0)
+      exact_segment<KD, BF, true>(p, si, h, v0, VT, c_begin, c_end, wave, vt, nullptr);
+  }
   // (rows of padded keys and columns past V are not stored)
   float *dst = nullptr;
   if constexpr (OUT) {

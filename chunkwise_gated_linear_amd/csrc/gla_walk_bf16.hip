@@ -85,7 +85,8 @@ struct LdsW {
   static constexpr int oS = oP + (OUT ? PBYTES : 0);       // bf16 output tile [token][n], staged for row stores (OUT)
   static constexpr int oDec = oS + (OUT ? VPL : 0);        // a [K]
   static constexpr int oF = oDec + 4 * KD;                 // score-ready chunk index per matrix wave (OUT)
-  static constexpr int BYTES = oF + 16;
+  static constexpr int oBad = oF + 16;                     // a chunk of the segment needs the exact path (OUT)
+  static constexpr int BYTES = oBad + 16;
 
   // Swizzled byte offsets.  On gfx950 an LDS access is served 32 lanes at a
   // time (16 for writes) without bank conflicts when the lanes' addresses,
@@ -303,6 +304,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
           S[kt][nt][r] = (src && row < nkeys && col < V) ? src[(int64_t)row * V + col] : 0.f;
         }
   }
+  if (tid == 0) lds_st<int>(smem + L::oBad, 0, 0);
   if (OUT) {  // score tiles above the diagonal are read as zeros and never written
     for (int i = tid; i < 2 * L::APL / 16; i += L::THREADS)
       lds_st<u32x4_t>(smem + L::oA, 16 * i, u32x4_t{0, 0, 0, 0});
@@ -355,6 +357,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   float tQ[RPG][4], tK[RPG][4];  // q P, k R of a row (factors inside the row group)
   float incl[4], shf[4];         // running products across row groups, shuffled values
   float seg_decay[4] = {1.f, 1.f, 1.f, 1.f};
+  bool seg_bad = false;          // some key of a chunk decayed by more than kMinChunkDecay
   const float scale = p.scale;
 
   // Raw loads of chunk c (rows past the sequence end, and chunks past the
@@ -414,7 +417,10 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) incl[j] *= (rg >= d) ? shf[j] : 1.f;
   };
-  // gate, stage 1c: chunk decay and the q / k factors from the scan
+  // gate, stage 1c: chunk decay and the q / k factors from the scan.  A chunk in
+  // which some key decays by more than kMinChunkDecay makes these factors
+  // overflow (and the quotient tot / incl can be 0 / 0); write_k flags it and the
+  // whole segment is then evaluated again token by token.
   auto gate_decays = [&]() {
     const int src_pre = rg > 0 ? lane - QPW : lane;
     const int src_tot = (NG - 1) * QPW + lane % QPW;
@@ -488,6 +494,10 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
       lds_st<u32x2_t>(smem + L::oK + L::QPL, off, gKl[r]);
     }
     if (rg == 0) lds_st<f32x4_t>(smem + L::oDec, 16 * cq, gDec);
+    // the flag of the segment (wave-uniform, a scalar register)
+    const bool low = gDec[0] < kMinChunkDecay || gDec[1] < kMinChunkDecay || gDec[2] < kMinChunkDecay ||
+                     gDec[3] < kMinChunkDecay;
+    if (__ballot(low) != 0ull) seg_bad = true;
   };
   auto write_q_row = [&](int c, int r) {
     char *sq = smem + L::qbuf(c);
@@ -785,9 +795,20 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
         for (int r = 0; r < 4; ++r)
           lds_st<float>(smem, 4 * ((KH * kh + 16 * kt + 4 * lg + r) * VW + VQ * cw + 16 * nt + l16), S[kt][nt][r]);
   }
+  if (producer && seg_bad && lane == 0) lds_st<int>(smem + L::oBad, 0, 1);
   if (OUT || dst != nullptr) phase_barrier();  // staged output tile and state visible
+  const bool exact = __builtin_amdgcn_readfirstlane(lds_ld<int>(smem + L::oBad, 0)) != 0;
   if constexpr (OUT && KS == 2) {  // the last staged output tile
     if (!producer && c_begin < c_end) store_staged(c_end - 1);
+  }
+  if (exact) {
+    // the chunk form's products overflowed in some chunk of this segment (its
+    // outputs, state and summary may hold inf or NaN): every result of the
+    // segment is formed again from the token recurrence, after every store of
+    // the chunk loop; its final state replaces S in the staging area
+    __syncthreads();
+    exact_segment<KD, true, OUT>(p, si, h, v0, VW, c_begin, c_end, wave, vt, reinterpret_cast<float *>(smem));
+    __syncthreads();
   }
   if (dst != nullptr) {
     constexpr int LPR = VW / 4, RPI = 64 / LPR;  // lanes per state row, rows per store
@@ -799,7 +820,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
         *reinterpret_cast<f32x4_t *>(dst + (int64_t)row * V + v0 + 4 * ch) = lds_ld<f32x4_t>(smem, 16 * (row * LPR + ch));
     }
   }
-  if (producer && !OUT && vt == 0 && rg == 0 && key_ok) {
+  if (producer && !OUT && !exact && vt == 0 && rg == 0 && key_ok) {
     const int slot = si.first + si.s;
     *reinterpret_cast<f32x4_t *>(p.seg_decay + ((int64_t)slot * H + h) * nkeys + 4 * cq) =
         f32x4_t{seg_decay[0], seg_decay[1], seg_decay[2], seg_decay[3]};

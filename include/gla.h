@@ -32,10 +32,13 @@
  *    cu[N] = T) and are not checked.  Offsets that break it give undefined
  *    output values but no access outside the caller's buffers: the kernels
  *    clamp every sequence to [0, T) and never index past the workspace.
- *  - NaN / Inf inputs propagate; they are not checked.  Finite gates are
- *    supported while the summed log decay of one key over one 64-token chunk
- *    stays above -80 (the in-chunk factors exp(G_i - G_last) are formed in
- *    fp32); below that the outputs of that chunk are undefined.
+ *  - NaN / Inf inputs propagate; they are not checked.  g is a log decay
+ *    (g <= 0, as logsigmoid gates are); any such finite gate is exact.  The
+ *    chunk form's in-chunk factors exp(G_i - G_last) leave the fp32 range once
+ *    a key decays by more than e^-80 within one 64-token chunk; a segment with
+ *    such a chunk is evaluated again token by token by the same kernels (same
+ *    results, slower).  Positive g makes the state grow and is only as exact as
+ *    the fp32 range of the state allows.
  *  - Reentrant; the only global state is a per-device cache of the compute
  *    unit count.  Calls that share a workspace buffer must be ordered by the
  *    caller (same stream, or synchronised).

@@ -120,6 +120,38 @@ def test_gate_extremes(dtype, gate):
     _compare(d, dtype, f"gate {gate}", segment_chunks=2)
 
 
+# Gates whose summed log decay over one 64-token chunk goes below -80 on some
+# key: beyond the fp32 range of the factorised in-chunk form, such segments are
+# re-evaluated token by token.  g = -2 per step gives -128 per chunk, -6 gives
+# -384 (exp(-6) per step), -40 makes every step forget the state almost
+# entirely, -1.3 stays in range for most chunks (-83 per chunk); "one" puts a
+# single strong chunk among ordinary ones, "keys" only some keys.
+@pytest.mark.parametrize("dtype,vtile", [("bf16", 64), ("bf16", 128), ("fp32", 0)])
+@pytest.mark.parametrize("gate", ["m2", "m6", "m40", "m1.3", "one", "keys"])
+@pytest.mark.parametrize("seg", [0, 2, 6])  # 6: one segment per sequence
+def test_gates_beyond_the_chunk_range(dtype, vtile, gate, seg):
+    d = gi.draw(660 + seg, 2, 333, 2, 128, 128, dtype=dtype, h0=True)
+    g = d["g"].copy()
+    if gate.startswith("m"):
+        g[:] = -float(gate[1:])
+    elif gate == "one":
+        g[:, 130:190] = -3.0  # chunk 2 (tokens 128..191) mostly
+    else:
+        g[..., 5:40] = -2.5
+    d["g"] = g.astype(np.float32)
+    _compare(d, dtype, f"gate {gate}", segment_chunks=seg, value_tile=vtile)
+
+
+@pytest.mark.parametrize("dtype,K,V", [("bf16", 48, 80), ("bf16", 256, 64), ("fp32", 160, 48)])
+def test_strong_gates_packed_and_split_keys(dtype, K, V):
+    lengths = [200, 0, 65, 131]
+    d = gi.draw(670 + K, 1, 0, 2, K, V, dtype=dtype, h0=True, lengths=lengths)
+    g = d["g"].copy()
+    g[:, 60:140] = -2.0
+    d["g"] = g
+    _compare(d, dtype, f"strong gates packed K={K} V={V}", segment_chunks=1)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("seg", [1, 2, 3, 5])
 def test_forced_segments(dtype, seg):
