@@ -99,15 +99,18 @@ def array_digest(*arrays: np.ndarray) -> str:
 
 
 def draw(seed: int, B: int, T: int, H: int, K: int, V: int, dtype: str = "bf16",
-         h0: bool = False, lengths: Optional[list] = None, gate_scale: float = 1.0 / 16.0):
+         h0: bool = False, lengths: Optional[list] = None, gate_scale: float = 1.0 / 16.0,
+         HV: Optional[int] = None, gate: str = "key"):
     """Draw one input set from ``numpy.random.default_rng(seed)``.
 
     Returns a dict of float32 numpy arrays (q, k, v already rounded to bf16 when
-    ``dtype == "bf16"``): q, k, g [B, T, H, K]; v [B, T, H, V]; h0 [N, H, K, V] or None;
-    cu_seqlens int32 [N+1] or None.  With ``lengths`` the input is packed
-    (B = 1, T = sum(lengths)).
+    ``dtype == "bf16"``): q, k [B, T, H, K]; v [B, T, HV, V]; g [B, T, HV, K]
+    (``gate == "key"``) or [B, T, HV] (``gate == "head"``); h0 [N, HV, K, V] or
+    None; cu_seqlens int32 [N+1] or None.  HV defaults to H.  With ``lengths``
+    the input is packed (B = 1, T = sum(lengths)).
     """
-    return _draw_from(np.random.default_rng(seed), B, T, H, K, V, dtype, h0, lengths, gate_scale)
+    return _draw_from(np.random.default_rng(seed), B, T, H, K, V, dtype, h0, lengths, gate_scale,
+                      HV, gate)
 
 
 def make_inputs(w: Workload):
@@ -115,13 +118,16 @@ def make_inputs(w: Workload):
     if w.varlen:
         rng = np.random.default_rng(w.seed)
         lengths = rng.integers(w.len_lo, w.len_hi, size=w.n_seqs, endpoint=True).tolist()
-        d = _draw_from(rng, 1, 0, w.H, w.K, w.V, w.dtype, w.h0, lengths, 1.0 / 16.0)
+        d = _draw_from(rng, 1, 0, w.H, w.K, w.V, w.dtype, w.h0, lengths, 1.0 / 16.0, None, "key")
         d["lengths"] = lengths
         return d
     return draw(w.seed, w.B, w.T, w.H, w.K, w.V, w.dtype, w.h0)
 
 
-def _draw_from(rng, B, T, H, K, V, dtype, h0, lengths, gate_scale):
+def _draw_from(rng, B, T, H, K, V, dtype, h0, lengths, gate_scale, HV=None, gate="key"):
+    HV = H if HV is None else HV
+    if HV % H != 0 or gate not in ("key", "head"):
+        raise ValueError("HV must be a multiple of H; gate is 'key' or 'head'")
     cu = None
     if lengths is not None:
         lengths = [int(x) for x in lengths]
@@ -131,13 +137,13 @@ def _draw_from(rng, B, T, H, K, V, dtype, h0, lengths, gate_scale):
     N = len(lengths) if lengths is not None else B
     q = rng.standard_normal((B, T, H, K), dtype=np.float32)
     k = rng.standard_normal((B, T, H, K), dtype=np.float32)
-    v = rng.standard_normal((B, T, H, V), dtype=np.float32)
-    z = rng.standard_normal((B, T, H, K), dtype=np.float32)
+    v = rng.standard_normal((B, T, HV, V), dtype=np.float32)
+    z = rng.standard_normal((B, T, HV, K) if gate == "key" else (B, T, HV), dtype=np.float32)
     g = (logsigmoid_f32(z) * np.float32(gate_scale)).astype(np.float32)
     del z
     h = None
     if h0:
-        h = (np.float32(0.1) * rng.standard_normal((N, H, K, V), dtype=np.float32)).astype(np.float32)
+        h = (np.float32(0.1) * rng.standard_normal((N, HV, K, V), dtype=np.float32)).astype(np.float32)
     if dtype == "bf16":
         q, k, v = to_bf16_f32(q), to_bf16_f32(k), to_bf16_f32(v)
     elif dtype != "fp32":

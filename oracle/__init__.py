@@ -46,6 +46,9 @@ def _load():
         lib.gla_oracle_fwd.argtypes = [i64, p, i64, i64, i64, p, p, p, p, p,
                                        ctypes.c_double, p, p, ctypes.c_int]
         lib.gla_oracle_fwd.restype = ctypes.c_int
+        lib.gla_oracle_fwd_heads.argtypes = [i64, p, i64, i64, i64, i64, ctypes.c_int, p, p, p, p, p,
+                                             ctypes.c_double, p, p, ctypes.c_int]
+        lib.gla_oracle_fwd_heads.restype = ctypes.c_int
         lib.gla_oracle_max_threads.argtypes = []
         lib.gla_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -66,16 +69,21 @@ def gla_reference(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray,
                   threads: int = 0) -> Tuple[np.ndarray, Optional[np.ndarray]]:
     """Token-by-token fp64 recurrence.
 
-    q, k, g: [B, T, H, K]; v: [B, T, H, V] (any float dtype; converted to float32,
-    which is exact for bf16 and fp32 data).  h0: [N, H, K, V] or None.
+    q, k: [B, T, H, K]; v: [B, T, HV, V] with HV a multiple of H (value head hv
+    reads key head hv // (HV // H)); g: [B, T, HV, K] (a decay per key) or
+    [B, T, HV] (one decay per value head and token).  Any float dtype; converted
+    to float32, which is exact for bf16 and fp32 data.  h0: [N, HV, K, V] or None.
     cu_seqlens: [N+1] offsets into the packed token axis (requires B == 1) or None.
     scale: None means K ** -0.5.
-    Returns o [B, T, H, V] float64 and ht [N, H, K, V] float64 (or None).
+    Returns o [B, T, HV, V] float64 and ht [N, HV, K, V] float64 (or None).
     """
     B, T, H, K = q.shape
-    V = v.shape[-1]
-    if k.shape != (B, T, H, K) or g.shape != (B, T, H, K) or v.shape != (B, T, H, V):
+    HV, V = v.shape[2], v.shape[3]
+    per_head = g.ndim == 3
+    if k.shape != (B, T, H, K) or v.shape[:2] != (B, T) or HV % H != 0:
         raise ValueError("shape mismatch")
+    if g.shape != ((B, T, HV) if per_head else (B, T, HV, K)):
+        raise ValueError("g must be [B, T, HV, K] or [B, T, HV]")
     if scale is None:
         scale = K ** -0.5
     if cu_seqlens is not None:
@@ -91,14 +99,14 @@ def gla_reference(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray,
     qf, kf, vf, gf = f32(q), f32(k), f32(v), f32(g)
     hf = None
     if h0 is not None:
-        if h0.shape != (N, H, K, V):
-            raise ValueError(f"h0 must be [{N}, {H}, {K}, {V}]")
+        if h0.shape != (N, HV, K, V):
+            raise ValueError(f"h0 must be [{N}, {HV}, {K}, {V}]")
         hf = np.ascontiguousarray(h0, dtype=np.float64)
-    o = np.zeros((B, T, H, V), dtype=np.float64)
-    ht = np.zeros((N, H, K, V), dtype=np.float64) if output_final_state else None
-    rc = _load().gla_oracle_fwd(N, _ptr(offsets), H, K, V, _ptr(qf), _ptr(kf), _ptr(vf),
-                                _ptr(gf), _ptr(hf), float(scale), _ptr(o), _ptr(ht),
-                                int(threads))
+    o = np.zeros((B, T, HV, V), dtype=np.float64)
+    ht = np.zeros((N, HV, K, V), dtype=np.float64) if output_final_state else None
+    rc = _load().gla_oracle_fwd_heads(N, _ptr(offsets), H, HV, K, V, 1 if per_head else 0,
+                                      _ptr(qf), _ptr(kf), _ptr(vf), _ptr(gf), _ptr(hf), float(scale),
+                                      _ptr(o), _ptr(ht), int(threads))
     if rc != 0:
         raise RuntimeError("oracle failed")
     return o, ht

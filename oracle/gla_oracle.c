@@ -44,21 +44,29 @@
 #endif
 
 /*
- * q, k, g : [T_total][H][K] float32, time-major (token, head, key)
- * v       : [T_total][H][V] float32
+ * Head and gate variants (page "fla/ops/gated_delta_rule/backends/triton_ascend/wy_fast.py",
+ * recompute_w_u_fwd_kernel_npu and its wrapper): keys and queries have H heads,
+ * values, gates and states have HV heads (HV a multiple of H), and value head hv
+ * reads key / query head hv / (HV / H).  The gate is either one log decay per
+ * key (g [T][HV][K]) or one per value head and token (g [T][HV], the same decay
+ * for every key of the state).
+ *
+ * q, k    : [T_total][H][K] float32, time-major (token, head, key)
+ * v       : [T_total][HV][V] float32
+ * g       : [T_total][HV][K] float32 (gate_per_head = 0) or [T_total][HV] (= 1)
  * offsets : [N+1] int64 token offsets, offsets[0] = 0, non-decreasing
- * h0      : [N][H][K][V] double or NULL (zero initial state); double so that a
+ * h0      : [N][HV][K][V] double or NULL (zero initial state); double so that a
  *           final state can be fed back unrounded (fp32 h0 upcasts exactly)
- * o       : [T_total][H][V] double, every token of every sequence is written
- * ht      : [N][H][K][V] double or NULL
+ * o       : [T_total][HV][V] double, every token of every sequence is written
+ * ht      : [N][HV][K][V] double or NULL
  * nthreads: OpenMP threads to use (<= 0: library default)
  * Returns 0, or -1 on invalid sizes / allocation failure (nothing written).
  */
-int gla_oracle_fwd(int64_t N, const int64_t *offsets, int64_t H, int64_t K, int64_t V,
-                   const float *q, const float *k, const float *v, const float *g,
-                   const double *h0, double scale, double *o, double *ht, int nthreads)
+int gla_oracle_fwd_heads(int64_t N, const int64_t *offsets, int64_t H, int64_t HV, int64_t K, int64_t V,
+                         int gate_per_head, const float *q, const float *k, const float *v, const float *g,
+                         const double *h0, double scale, double *o, double *ht, int nthreads)
 {
-    if (N < 0 || H <= 0 || K <= 0 || V <= 0 || !offsets || !o)
+    if (N < 0 || H <= 0 || HV <= 0 || HV % H != 0 || K <= 0 || V <= 0 || !offsets || !o)
         return -1;
     for (int64_t n = 0; n < N; ++n)
         if (offsets[n + 1] < offsets[n]) return -1;
@@ -67,27 +75,28 @@ int gla_oracle_fwd(int64_t N, const int64_t *offsets, int64_t H, int64_t K, int6
 #else
     (void)nthreads;
 #endif
+    const int64_t group = HV / H;
     int failed = 0;
-    const int64_t jobs = N * H;
+    const int64_t jobs = N * HV;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
     for (int64_t job = 0; job < jobs; ++job) {
-        const int64_t n = job / H, h = job % H;
+        const int64_t n = job / HV, hv = job % HV, hk = hv / group;
         double *S = (double *)malloc(sizeof(double) * (size_t)(K * V));
         double *acc = (double *)malloc(sizeof(double) * (size_t)V);
         if (!S || !acc) { free(S); free(acc); failed |= 1; continue; }
         if (h0) {
-            memcpy(S, h0 + (n * H + h) * K * V, sizeof(double) * (size_t)(K * V));
+            memcpy(S, h0 + (n * HV + hv) * K * V, sizeof(double) * (size_t)(K * V));
         } else {
             memset(S, 0, sizeof(double) * (size_t)(K * V));
         }
         for (int64_t t = offsets[n]; t < offsets[n + 1]; ++t) {
-            const float *qt = q + (t * H + h) * K;
-            const float *kt = k + (t * H + h) * K;
-            const float *gt = g + (t * H + h) * K;
-            const float *vt = v + (t * H + h) * V;
+            const float *qt = q + (t * H + hk) * K;
+            const float *kt = k + (t * H + hk) * K;
+            const float *vt = v + (t * HV + hv) * V;
             for (int64_t j = 0; j < V; ++j) acc[j] = 0.0;
             for (int64_t i = 0; i < K; ++i) {
-                const double decay = exp((double)gt[i]);
+                const float gi = gate_per_head ? g[t * HV + hv] : g[(t * HV + hv) * K + i];
+                const double decay = exp((double)gi);
                 const double ki = (double)kt[i];
                 const double qi = (double)qt[i];
                 double *row = S + i * V;
@@ -96,14 +105,22 @@ int gla_oracle_fwd(int64_t N, const int64_t *offsets, int64_t H, int64_t K, int6
                     acc[j] += qi * row[j];
                 }
             }
-            double *ot = o + (t * H + h) * V;
+            double *ot = o + (t * HV + hv) * V;
             for (int64_t j = 0; j < V; ++j) ot[j] = scale * acc[j];
         }
-        if (ht) memcpy(ht + (n * H + h) * K * V, S, sizeof(double) * (size_t)(K * V));
+        if (ht) memcpy(ht + (n * HV + hv) * K * V, S, sizeof(double) * (size_t)(K * V));
         free(S);
         free(acc);
     }
     return failed ? -1 : 0;
+}
+
+/* The method with one value head per key head and a decay per key (HV = H). */
+int gla_oracle_fwd(int64_t N, const int64_t *offsets, int64_t H, int64_t K, int64_t V,
+                   const float *q, const float *k, const float *v, const float *g,
+                   const double *h0, double scale, double *o, double *ht, int nthreads)
+{
+    return gla_oracle_fwd_heads(N, offsets, H, H, K, V, 0, q, k, v, g, h0, scale, o, ht, nthreads);
 }
 
 /* Threads an OpenMP parallel region of this library actually gets. */

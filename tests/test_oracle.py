@@ -122,6 +122,88 @@ def test_matches_brute_force_packed_with_empty_sequence():
     np.testing.assert_array_equal(ht[1], d["h0"][1].astype(np.float64))
 
 
+# ---------------------------------------------------------------- head and gate variants
+def brute_force_heads(q, k, v, g, h0=None, cu=None, scale=None):
+    """The O(T^2) closed form for value heads HV = group * H (value head hv reads
+    key head hv // group) and a gate per key [.., HV, K] or per head [.., HV]:
+    o_i = scale sum_k q_ik (e^{Gam_ik} h0[k,:] + sum_{j<=i} e^{Gam_ik - Gam_jk} k_jk v_j)
+    with Gam the global inclusive cumulative sum of the gate (broadcast over keys
+    when it is per head)."""
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    grp = HV // H
+    scale = K ** -0.5 if scale is None else scale
+    offs = list(cu) if cu is not None else [b * T for b in range(B + 1)]
+    qf = q.reshape(B * T, H, K).astype(np.float64)
+    kf = k.reshape(B * T, H, K).astype(np.float64)
+    vf = v.reshape(B * T, HV, V).astype(np.float64)
+    gf = g.reshape(B * T, HV, -1).astype(np.float64) * np.ones((1, 1, K))
+    o = np.zeros((B * T, HV, V))
+    N = len(offs) - 1
+    ht = np.zeros((N, HV, K, V))
+    for n in range(N):
+        a, b = offs[n], offs[n + 1]
+        for hv in range(HV):
+            hk = hv // grp
+            init = np.zeros((K, V)) if h0 is None else h0[n, hv].astype(np.float64)
+            if b == a:
+                ht[n, hv] = init
+                continue
+            Q, Kk, Vv = qf[a:b, hk], kf[a:b, hk], vf[a:b, hv]
+            gam = np.cumsum(gf[a:b, hv], axis=0)
+            L = b - a
+            D = np.exp(gam[:, None, :] - gam[None, :, :]) * np.tril(np.ones((L, L)))[:, :, None]
+            A = np.einsum("ik,jk,ijk->ij", Q, Kk, D)
+            o[a:b, hv] = scale * (A @ Vv + (Q * np.exp(gam)) @ init)
+            ht[n, hv] = np.exp(gam[-1])[:, None] * init + (Kk * np.exp(gam[-1] - gam)).T @ Vv
+    return o.reshape(B, T, HV, V), ht
+
+
+@pytest.mark.parametrize("H,HV,gate", [(2, 2, "head"), (2, 4, "key"), (2, 6, "head"), (1, 3, "key"),
+                                       (3, 3, "key")])
+@pytest.mark.parametrize("packed", [False, True])
+def test_head_variants_match_brute_force(H, HV, gate, packed):
+    lengths = [7, 0, 40, 1] if packed else None
+    d = gi.draw(90 + HV, 1 if packed else 2, 0 if packed else 33, H, 5, 6, dtype="fp32", h0=True,
+                lengths=lengths, gate_scale=0.3, HV=HV, gate=gate)
+    o, ht = oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], h0=d["h0"], cu_seqlens=d["cu_seqlens"])
+    ob, hb = brute_force_heads(d["q"], d["k"], d["v"], d["g"], h0=d["h0"], cu=d["cu_seqlens"])
+    assert o.shape == (d["q"].shape[0], d["q"].shape[1], HV, 6) and ht.shape[1] == HV
+    assert rel_err(o, ob) < 1e-12
+    assert rel_err(ht, hb) < 1e-12
+
+
+def test_head_gate_is_a_key_gate_broadcast_over_keys():
+    d = gi.draw(95, 2, 30, 2, 4, 3, dtype="fp32", h0=True, gate_scale=0.4, HV=4, gate="head")
+    o1, h1 = oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], h0=d["h0"])
+    gk = np.repeat(d["g"][..., None], 4, axis=-1)
+    o2, h2 = oracle.gla_reference(d["q"], d["k"], d["v"], gk, h0=d["h0"])
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(h1, h2)
+
+
+def test_grouped_value_heads_equal_repeated_key_heads():
+    # value heads 2m and 2m+1 read key head m: the same as giving every value
+    # head its own copy of the key head
+    d = gi.draw(96, 2, 25, 2, 4, 3, dtype="fp32", h0=True, gate_scale=0.4, HV=4, gate="key")
+    o1, h1 = oracle.gla_reference(d["q"], d["k"], d["v"], d["g"], h0=d["h0"])
+    rep = lambda x: np.repeat(x, 2, axis=2)
+    o2, h2 = oracle.gla_reference(rep(d["q"]), rep(d["k"]), d["v"], d["g"], h0=d["h0"])
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(h1, h2)
+
+
+def test_head_pin_catches_a_wrong_head_mapping():
+    # hv % H instead of hv // (HV / H) reads the wrong key head: the closed form
+    # with that mapping must disagree with the oracle
+    d = gi.draw(97, 1, 20, 2, 4, 3, dtype="fp32", h0=False, gate_scale=0.4, HV=4, gate="key")
+    o, _ = oracle.gla_reference(d["q"], d["k"], d["v"], d["g"])
+    perm = [hv % 2 for hv in range(4)]
+    ob, _ = brute_force_heads(d["q"][:, :, perm].reshape(1, 20, 4, 4), d["k"][:, :, perm].reshape(1, 20, 4, 4),
+                              d["v"], d["g"])
+    assert rel_err(o, ob) > 1e-3
+
+
 # ---------------------------------------------------------------- g == 0: causal linear attention
 def test_zero_gate_is_causal_linear_attention():
     B, T, H, K, V = 2, 50, 2, 8, 6
