@@ -11,8 +11,11 @@ importing the binding still works but every call raises.
 
 K and V are multiples of 16 in [16, 256].
 
-Shapes are time-major: q, k, g [B, T, H, K]; v [B, T, H, V]; h0, ht
-[N, H, K, V] float32; cu_seqlens int32 [N+1] for packed sequences (B == 1).
+Shapes are time-major: q, k [B, T, H, K]; v [B, T, HV, V]; g [B, T, HV, K]
+(a decay per key) or [B, T, HV] (one per value head); h0, ht [N, HV, K, V]
+float32; cu_seqlens int32 [N+1] for packed sequences (B == 1).  HV = H is the
+plain method; HV a multiple of H groups value heads on key heads (value head
+hv reads key head hv // (HV // H)).
 Defaults follow page "fla/ops/gla/fused_chunk.py" (fused_chunk_gla: scale
 defaults to K^-0.5, the final state is returned only on request) and page
 "fla/ops/ttt/fused_chunk.py" (fused_chunk_ttt_linear: a given scale must be
@@ -37,6 +40,7 @@ STATUS = {
     4: "GLA_ERR_BAD_SCALE", 5: "GLA_ERR_UNSUPPORTED", 6: "GLA_ERR_WORKSPACE", 7: "GLA_ERR_HIP",
 }
 GLA_F32, GLA_BF16 = 0, 1
+GATE_PER_KEY, GATE_PER_HEAD = 0, 1
 CHUNK = 64
 STATUS_WAIT_EXHAUSTED = 1  # bit of the workspace status word: a bounded wait between waves ran out
 
@@ -52,7 +56,8 @@ class Problem(ctypes.Structure):
                 ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("n_seqs", ctypes.c_int32), ("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("segment_chunks", ctypes.c_int32), ("packed", ctypes.c_int32),
-                ("value_tile", ctypes.c_int32), ("wait_limit", ctypes.c_int32)]
+                ("value_tile", ctypes.c_int32), ("wait_limit", ctypes.c_int32),
+                ("HV", ctypes.c_int32), ("gate", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -87,10 +92,11 @@ def _status_msg(lib, code: int) -> str:
 
 
 def make_problem(B, T, H, K, V, dtype_code, n_seqs, chunk=CHUNK, scale=1.0,
-                 segment_chunks=0, packed=False, value_tile=0, wait_limit=0) -> Problem:
+                 segment_chunks=0, packed=False, value_tile=0, wait_limit=0, HV=0,
+                 gate=GATE_PER_KEY) -> Problem:
     return Problem(int(B), int(T), int(H), int(K), int(V), int(dtype_code), int(n_seqs),
                    int(chunk), float(scale), int(segment_chunks), 1 if packed else 0,
-                   int(value_tile), int(wait_limit))
+                   int(value_tile), int(wait_limit), int(HV), int(gate))
 
 
 def workspace_bytes(problem: Problem) -> int:
@@ -135,7 +141,7 @@ def gla_fwd(q, k, v, g, h0=None, cu_seqlens=None, scale: Optional[float] = None,
     prob, N, dev = _problem_for(q, k, v, g, h0, cu_seqlens, out, scale, chunk, segment_chunks,
                                 value_tile, wait_limit)
     B, T, H, K = q.shape
-    V = v.shape[-1]
+    HV, V = v.shape[2], v.shape[3]
     with torch.cuda.device(dev):
         ws = lib.gla_fwd_workspace_bytes(ctypes.byref(prob))
         if ws == ctypes.c_size_t(-1).value:
@@ -145,7 +151,7 @@ def gla_fwd(q, k, v, g, h0=None, cu_seqlens=None, scale: Optional[float] = None,
         o = out if out is not None else torch.empty_like(v)
         if out is not None and (out.shape != v.shape or out.dtype != v.dtype):
             raise ValueError("out must match v's shape and dtype")
-        ht = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+        ht = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev) if output_final_state else None
         if workspace is None or workspace.numel() * workspace.element_size() < ws:
             workspace = _new_workspace(ws, dev)
         stream = torch.cuda.current_stream(dev).cuda_stream
@@ -172,12 +178,12 @@ def gla_fwd_noalloc(q, k, v, g, o, h0=None, cu_seqlens=None, ht=None, scale: Opt
     lib = load_library()
     prob, N, dev = _problem_for(q, k, v, g, h0, cu_seqlens, o, scale, chunk, segment_chunks, value_tile, 0)
     B, T, H, K = q.shape
-    V = v.shape[-1]
+    HV, V = v.shape[2], v.shape[3]
     if o.shape != v.shape or o.dtype != v.dtype:
         raise ValueError("o must match v's shape and dtype")
-    if ht is not None and (tuple(ht.shape) != (N, H, K, V) or ht.dtype != torch.float32 or ht.device != dev
+    if ht is not None and (tuple(ht.shape) != (N, HV, K, V) or ht.dtype != torch.float32 or ht.device != dev
                            or not ht.is_contiguous()):
-        raise ValueError(f"ht must be a contiguous float32 [{N}, {H}, {K}, {V}] tensor on {dev}")
+        raise ValueError(f"ht must be a contiguous float32 [{N}, {HV}, {K}, {V}] tensor on {dev}")
     if status is not None and (status.dtype != torch.int32 or status.numel() < 1 or status.device != dev):
         raise ValueError("status must be an int32 device tensor")
     with torch.cuda.device(dev):
@@ -192,8 +198,17 @@ def _problem_for(q, k, v, g, h0, cu_seqlens, out, scale, chunk, segment_chunks, 
     """Checks the tensors of a call and builds its gla_problem (page defaults for scale)."""
     import torch
 
-    if q.dim() != 4 or k.shape != q.shape or g.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
-        raise ValueError("expected q, k, g [B, T, H, K] and v [B, T, H, V]")
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("expected q, k [B, T, H, K] and v [B, T, HV, V]")
+    HV = v.shape[2]
+    if HV % q.shape[2] != 0:
+        raise ValueError(f"value heads ({HV}) must be a multiple of key heads ({q.shape[2]})")
+    if g.shape == (*v.shape[:3], q.shape[3]):
+        gate = GATE_PER_KEY
+    elif g.shape == v.shape[:3]:
+        gate = GATE_PER_HEAD
+    else:
+        raise ValueError("g must be [B, T, HV, K] (a decay per key) or [B, T, HV] (one per value head)")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k and v must share a dtype")
     if q.dtype == torch.bfloat16:
@@ -221,15 +236,15 @@ def _problem_for(q, k, v, g, h0, cu_seqlens, out, scale, chunk, segment_chunks, 
     else:
         N = B
     if h0 is not None:
-        if h0.dtype != torch.float32 or tuple(h0.shape) != (N, H, K, V):
-            raise ValueError(f"initial state must be float32 [{N}, {H}, {K}, {V}], "
+        if h0.dtype != torch.float32 or tuple(h0.shape) != (N, HV, K, V):
+            raise ValueError(f"initial state must be float32 [{N}, {HV}, {K}, {V}], "
                              f"got {tuple(h0.shape)} {h0.dtype}")
     if scale is None:
         scale = K ** -0.5
     elif not (scale > 0):
         raise ValueError("scale must be positive")
     prob = make_problem(B, T, H, K, V, code, N, chunk, scale, segment_chunks, cu_seqlens is not None,
-                        value_tile, wait_limit)
+                        value_tile, wait_limit, HV, gate)
     return prob, N, dev
 
 
@@ -244,13 +259,8 @@ class GlaCall:
         import torch
 
         self.lib = load_library()
-        B, T, H, K = q.shape
-        V = v.shape[-1]
-        N = B if cu_seqlens is None else cu_seqlens.numel() - 1
-        code = GLA_BF16 if q.dtype == torch.bfloat16 else GLA_F32
-        self.problem = make_problem(B, T, H, K, V, code, N, chunk, K ** -0.5 if scale is None else scale,
-                                    segment_chunks, cu_seqlens is not None, value_tile, wait_limit)
-        self.device = q.device
+        self.problem, N, self.device = _problem_for(q, k, v, g, h0, cu_seqlens, None, scale, chunk,
+                                                    segment_chunks, value_tile, wait_limit)
         ws = workspace_bytes(self.problem)
         self.workspace = _new_workspace(ws, self.device)
         self.ws_bytes = ws

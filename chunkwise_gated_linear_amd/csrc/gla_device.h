@@ -249,14 +249,17 @@ __device__ void exact_segment(const WalkParams &p, const SegInfo &si, int h, int
   const int col = v0 + 16 * wave + l16;
   const bool col_ok = col < p.V;
   const int nkeys = p.K;
-  const int64_t rowK = (int64_t)p.H * p.Kmem, rowV = (int64_t)p.H * p.V;
-  const int64_t headK = (int64_t)h * p.Kmem + p.koff, headV = (int64_t)h * p.V + col;
+  // h is the value head; q, k are read from key head h / G
+  const int64_t rowK = (int64_t)p.H * p.Kmem, rowV = (int64_t)p.HV * p.V;
+  const int64_t headK = (int64_t)(h / p.G) * p.Kmem + p.koff, headV = (int64_t)h * p.V + col;
+  const int64_t rowG = p.gate_head ? (int64_t)p.HV : (int64_t)p.HV * p.Kmem;
+  const int64_t headG = p.gate_head ? (int64_t)h : (int64_t)h * p.Kmem + p.koff;
   const float *src = nullptr;
   if (OUT) {
     if (si.s == 0) {
-      if (p.h0) src = p.h0 + (((int64_t)si.n * p.H + h) * p.Kmem + p.koff) * p.V;
+      if (p.h0) src = p.h0 + (((int64_t)si.n * p.HV + h) * p.Kmem + p.koff) * p.V;
     } else {
-      src = p.seg_state + ((int64_t)(si.first + si.s - 1) * p.H + h) * nkeys * p.V;
+      src = p.seg_state + ((int64_t)(si.first + si.s - 1) * p.HV + h) * nkeys * p.V;
     }
   }
   float st[KQ], dec[KQ];
@@ -276,7 +279,13 @@ __device__ void exact_segment(const WalkParams &p, const SegInfo &si, int h, int
       const int key = kg * KQ + j;  // a quad of keys is all real or all padding
       if (key < nkeys) {
         const int64_t kidx = tok * rowK + headK + key;
-        const f32x4_t g4 = *reinterpret_cast<const f32x4_t *>(p.g + kidx);
+        f32x4_t g4;
+        if (p.gate_head) {
+          const float x = p.g[tok * rowG + headG];
+          g4 = f32x4_t{x, x, x, x};
+        } else {
+          g4 = *reinterpret_cast<const f32x4_t *>(p.g + tok * rowG + headG + key);
+        }
         const f32x4_t k4 = load4<BF>(p.k, kidx);
         f32x4_t q4 = {0.f, 0.f, 0.f, 0.f};
         if (OUT) q4 = load4<BF>(p.q, kidx);
@@ -306,7 +315,7 @@ __device__ void exact_segment(const WalkParams &p, const SegInfo &si, int h, int
     }
   }
   if (!OUT && vt == 0 && wave == 0 && l16 == 0) {
-    float *dd = p.seg_decay + ((int64_t)(si.first + si.s) * p.H + h) * nkeys;
+    float *dd = p.seg_decay + ((int64_t)(si.first + si.s) * p.HV + h) * nkeys;
 #pragma unroll
     for (int j = 0; j < KQ; ++j)
       if (kg * KQ + j < nkeys) dd[kg * KQ + j] = dec[j];

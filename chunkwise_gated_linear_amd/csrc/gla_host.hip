@@ -74,12 +74,15 @@ gla_status validate(const gla_problem *p) {
   if (p->value_tile != 0 && p->value_tile != 64 && p->value_tile != 128) return GLA_ERR_UNSUPPORTED;
   if (p->segment_chunks < 0 || (p->packed != 0 && p->packed != 1) || p->wait_limit < -1) return GLA_ERR_BAD_SHAPE;
   if (p->packed ? p->B != 1 : p->n_seqs != p->B) return GLA_ERR_BAD_SHAPE;
+  if (p->HV < 0 || (p->HV != 0 && p->HV % p->H != 0)) return GLA_ERR_BAD_SHAPE;
+  if (p->gate != GLA_GATE_PER_KEY && p->gate != GLA_GATE_PER_HEAD) return GLA_ERR_UNSUPPORTED;
   // token-head rows and state elements must stay addressable with 64-bit
   // offsets; one chunk's byte range of any tensor (64 token rows of H heads)
   // must stay below 2^30, where the kernels put lanes with nothing to load
-  const double rows = (double)p->B * p->T * p->H;
+  const long long HV = p->HV == 0 ? p->H : p->HV;
+  const double rows = (double)p->B * p->T * HV;
   if (rows * (p->K > p->V ? p->K : p->V) > 4.0e15) return GLA_ERR_BAD_SHAPE;
-  if ((long long)p->H * (p->K > p->V ? p->K : p->V) > (1LL << 22)) return GLA_ERR_BAD_SHAPE;
+  if (HV * (p->K > p->V ? p->K : p->V) > (1LL << 22)) return GLA_ERR_BAD_SHAPE;
   return GLA_OK;
 }
 
@@ -105,7 +108,7 @@ Plan make_plan(const gla_problem *p, bool varlen) {
   pl.varlen = varlen;
   pl.N = varlen ? p->n_seqs : p->B;
   pl.nkb = key_blocks(p->K, pl.kb);
-  const int H = p->H;
+  const int H = p->HV == 0 ? p->H : p->HV;  // value heads: walkers, states and outputs count these
   const bool fast = uses_bf16_walker(p);
   // Value columns per workgroup.  The bf16 walker's 128-column workgroups form
   // the gated operands of a head once for all 128 columns; they are used when
@@ -211,6 +214,9 @@ gla_status run_forward(const gla_problem *p, const Plan &pl, const void *q, cons
   w.seg_base = seg_base;
   w.seg_order = seg_base ? seg_base + N + 1 : nullptr;
   w.T = p->T; w.H = p->H; w.V = p->V; w.N = N;
+  w.HV = p->HV == 0 ? p->H : p->HV;
+  w.G = w.HV / p->H;
+  w.gate_head = p->gate == GLA_GATE_PER_HEAD ? 1 : 0;
   w.Kmem = p->K;
   w.R = pl.R;
   w.P = pl.P;

@@ -25,26 +25,32 @@ constexpr float kMinChunkLogDecay = -80.f;  // the same bound on the summed log 
 // output is the sum of the key blocks' outputs: with two blocks the first writes
 // its fp32 partial output to o_part, the second adds o_add (= that partial)
 // before rounding and storing o.
+//
+// Heads: q and k have H key heads; v, g, o, h0, ht and every state have HV value
+// heads (HV = G H), and value head hv reads key head hv / G.  Walkers, segments
+// and units count value heads.
 struct WalkParams {
-  const void *q, *k, *v;       // [B,T,H,Kmem] / [B,T,H,V], dtype per instantiation
-  const float *g;              // [B,T,H,Kmem]
-  const float *h0;             // [N,H,Kmem,V] or null
+  const void *q, *k, *v;       // [B,T,H,Kmem] / [B,T,HV,V], dtype per instantiation
+  const float *g;              // [B,T,HV,Kmem] (a decay per key) or [B,T,HV] (gate_head)
+  const float *h0;             // [N,HV,Kmem,V] or null
   const int32_t *cu;           // [N+1] or null
-  void *o;                     // [B,T,H,V]
-  float *ht;                   // [N,H,Kmem,V] or null
-  float *seg_state;            // [seg_slots][H][K][V]: segment summaries, then start states
-  float *seg_decay;            // [seg_slots][H][K]: product of the segment's decays
+  void *o;                     // [B,T,HV,V]
+  float *ht;                   // [N,HV,Kmem,V] or null
+  float *seg_state;            // [seg_slots][HV][K][V]: segment summaries, then start states
+  float *seg_decay;            // [seg_slots][HV][K]: product of the segment's decays
   const int32_t *seg_base;     // [N+1] first segment of each packed sequence, or null
   const int32_t *seg_order;    // [seg_slots] segment ids, longest first (packed), or null
   uint32_t *status;            // sticky status word (GLA_STATUS_* bits)
-  float *o_part;               // [B,T,H,V] fp32: write the partial output here instead of o, or null
-  const float *o_add;          // [B,T,H,V] fp32: partial output of the other key block, or null
-  int32_t T, H, K, V, N;       // K: keys of this launch's block
+  float *o_part;               // [B,T,HV,V] fp32: write the partial output here instead of o, or null
+  const float *o_add;          // [B,T,HV,V] fp32: partial output of the other key block, or null
+  int32_t T, H, K, V, N;       // H: key heads; K: keys of this launch's block
+  int32_t HV, G;               // value heads, value heads per key head
+  int32_t gate_head;           // 1: one decay per value head and token, g [B,T,HV]
   int32_t Kmem;                // keys per head in memory (row stride of q, k, g, h0, ht)
   int32_t koff;                // first key of this launch's block
   int32_t R;                   // chunks per segment
   int32_t P;                   // segments per sequence when seg_base is null
-  int32_t units;               // (segment, head) pairs covered by the grid
+  int32_t units;               // (segment, value head) pairs covered by the grid
   int32_t seg_slots;           // segment slots the workspace holds
   int32_t vtile;               // value columns per workgroup (64, or 128 for the bf16 walker)
   int32_t wait_polls;          // bound on each wait between waves (0: none, report at once)

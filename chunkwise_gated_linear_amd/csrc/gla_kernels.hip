@@ -89,7 +89,8 @@ __constant__ const int8_t kP1[4][3][2] = {
 
 // ---------------------------------------------------------------- the chunk walker
 // OUT = false: gla_chunk_local (segment summary).  OUT = true: gla_chunk_output.
-template <bool OUT, bool BF, int KD>
+// GH: one decay per value head and token (g [B,T,HV]) instead of one per key.
+template <bool OUT, bool BF, int KD, bool GH>
 __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
   using L = Lds<BF, KD, OUT>;
   constexpr int ES = L::ES;
@@ -113,7 +114,7 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
   const int vt = rem >> 3;
   const int unit = grp * 8 + (rem & 7);
   if (unit >= p.units) return;
-  const int seg = unit / p.H, h = unit - seg * p.H;
+  const int seg = unit / p.HV, h = unit - seg * p.HV;  // h: value head
   SegInfo si;
   if (!locate(p, seg, si)) return;
   if (!OUT && si.s >= si.nseg - 1) return;  // the last segment's summary is never used
@@ -124,11 +125,14 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
   const int c_begin = si.s * seg_len;
   const int c_end = min(c_begin + seg_len, nchunks);
   const int v0 = vt * VT;
-  const int H = p.H;
+  const int H = p.HV;                   // value heads: v, o, g, states
   const int nkeys = p.K;                // real keys of this block (<= KD)
-  const size_t rowK = (size_t)H * p.Kmem;  // element stride between tokens, q/k/g
-  const size_t rowV = (size_t)H * p.V;     // element stride between tokens, v/o
-  const size_t headK = (size_t)h * p.Kmem + p.koff;  // first key of the block in a token row
+  const size_t rowK = (size_t)p.H * p.Kmem;  // element stride between tokens, q/k
+  const size_t rowV = (size_t)H * p.V;       // element stride between tokens, v/o
+  const size_t headK = (size_t)(h / p.G) * p.Kmem + p.koff;  // first key of the block, key head of h
+  // g: a decay per key [.., HV, Kmem] or one per value head [.., HV]
+  const size_t rowG = GH ? (size_t)H : (size_t)H * p.Kmem;
+  const size_t headG = GH ? (size_t)h : (size_t)h * p.Kmem + p.koff;
 
   // ---- state block of this lane: S[16kt + 4lg + r][v0 + 16wave + l16]
   f32x4_t S[NKT];
@@ -179,7 +183,12 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
       const int row = rg * RPG + r;
       const bool ok = row < valid && key_ok;
       const size_t off = (t0 + row) * rowK + headK + 4 * cq;
-      rg_g[r] = ok ? *reinterpret_cast<const f32x4_t *>(p.g + off) : f32x4_t{0, 0, 0, 0};
+      if constexpr (GH) {  // one decay for every key of the row
+        const float x = ok ? p.g[(t0 + row) * rowG + headG] : 0.f;
+        rg_g[r] = f32x4_t{x, x, x, x};
+      } else {
+        rg_g[r] = ok ? *reinterpret_cast<const f32x4_t *>(p.g + (t0 + row) * rowG + headG + 4 * cq) : f32x4_t{0, 0, 0, 0};
+      }
       if constexpr (BF) {
         rg_k[r] = ok ? *reinterpret_cast<const u32x2_t *>((const uint16_t *)p.k + off) : u32x2_t{0, 0};
         if (OUT) rg_q[r] = ok ? *reinterpret_cast<const u32x2_t *>((const uint16_t *)p.q + off) : u32x2_t{0, 0};
@@ -575,16 +584,16 @@ __device__ __forceinline__ void walk(const WalkParams &p, char *smem) {
   }
 }
 
-template <bool BF, int KD>
+template <bool BF, int KD, bool GH>
 __global__ __launch_bounds__(kThreads, 1) void gla_chunk_local(WalkParams p) {
   __shared__ __attribute__((aligned(16))) char smem[Lds<BF, KD, false>::BYTES];
-  walk<false, BF, KD>(p, smem);
+  walk<false, BF, KD, GH>(p, smem);
 }
 
-template <bool BF, int KD>
+template <bool BF, int KD, bool GH>
 __global__ __launch_bounds__(kThreads, 1) void gla_chunk_output(WalkParams p) {
   __shared__ __attribute__((aligned(16))) char smem[Lds<BF, KD, true>::BYTES];
-  walk<true, BF, KD>(p, smem);
+  walk<true, BF, KD, GH>(p, smem);
 }
 
 // ---------------------------------------------------------------- state scan
@@ -596,7 +605,7 @@ __global__ __launch_bounds__(kThreads, 1) void gla_chunk_output(WalkParams p) {
 __global__ __launch_bounds__(256) void gla_state_scan(WalkParams p, int per_state) {
   const long long pair = blockIdx.x / per_state;
   const int eb = (int)(blockIdx.x - pair * per_state);
-  const int n = (int)(pair / p.H), h = (int)(pair - (long long)n * p.H);
+  const int n = (int)(pair / p.HV), h = (int)(pair - (long long)n * p.HV);
   const int e4 = eb * 256 + threadIdx.x;
   const int KV4 = p.K * p.V / 4;  // V is a multiple of 16: a quad never crosses a row
   if (n >= p.N || e4 >= KV4) return;
@@ -612,9 +621,9 @@ __global__ __launch_bounds__(256) void gla_state_scan(WalkParams p, int per_stat
   const int krow = (4 * e4) / p.V, col = 4 * e4 - krow * p.V;
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
   if (p.h0)
-    s = *reinterpret_cast<const f32x4_t *>(p.h0 + (((size_t)n * p.H + h) * p.Kmem + p.koff + krow) * p.V + col);
+    s = *reinterpret_cast<const f32x4_t *>(p.h0 + (((size_t)n * p.HV + h) * p.Kmem + p.koff + krow) * p.V + col);
   for (int j = 0; j + 1 < nseg; ++j) {
-    const size_t slot = (size_t)(first + j) * p.H + h;
+    const size_t slot = (size_t)(first + j) * p.HV + h;
     const float a = p.seg_decay[slot * p.K + krow];
     f32x4_t *cell = reinterpret_cast<f32x4_t *>(p.seg_state + slot * p.K * p.V) + e4;
     const f32x4_t u = *cell;
@@ -716,16 +725,21 @@ __global__ __launch_bounds__(1024) void gla_segment_plan(const int32_t *cu, int 
   }
 }
 
-template <bool BF, int KD>
-hipError_t launch_walk_t(bool local_mode, const WalkParams &p, hipStream_t s) {
+template <bool BF, int KD, bool GH>
+hipError_t launch_walk_g(bool local_mode, const WalkParams &p, hipStream_t s) {
   const int NV = (p.V + VT - 1) / VT;
   const int groups = (p.units + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * NV));
   if (local_mode)
-    hipLaunchKernelGGL((gla_chunk_local<BF, KD>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gla_chunk_local<BF, KD, GH>), grid, dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((gla_chunk_output<BF, KD>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gla_chunk_output<BF, KD, GH>), grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
+}
+
+template <bool BF, int KD>
+hipError_t launch_walk_t(bool local_mode, const WalkParams &p, hipStream_t s) {
+  return p.gate_head ? launch_walk_g<BF, KD, true>(local_mode, p, s) : launch_walk_g<BF, KD, false>(local_mode, p, s);
 }
 
 }  // namespace
@@ -752,7 +766,7 @@ hipError_t launch_walk_general(bool local_mode, bool bf16, int kd, const WalkPar
 hipError_t launch_state_scan(const WalkParams &p, hipStream_t s) {
   const int KV4 = p.K * p.V / 4;
   const int per_state = (KV4 + 255) / 256;
-  const long long blocks = (long long)p.N * p.H * per_state;
+  const long long blocks = (long long)p.N * p.HV * per_state;
   if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gla_state_scan, dim3((unsigned)blocks), dim3(256), 0, s, p, per_state);
   return hipGetLastError();

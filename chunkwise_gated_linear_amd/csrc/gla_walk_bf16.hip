@@ -226,7 +226,9 @@ __device__ __forceinline__ void scores(char *smem, const char *sq, const int (&r
   }
 }
 
-template <bool OUT, int KD, int VW>
+// GH: the gate is one decay per value head and token (g [B,T,HV]) instead of one
+// per key; a compile-time choice, so that the per-key walker's code is untouched.
+template <bool OUT, int KD, int VW, bool GH>
 __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   using L = LdsW<KD, OUT, VW>;
   constexpr int KS = L::KS;         // key splits of the state over the 4 matrix waves
@@ -257,7 +259,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   const int vt = rem >> 3;
   const int unit = grp * 8 + (rem & 7);
   if (unit >= p.units) return;
-  const int seg = unit / p.H, h = unit - seg * p.H;
+  const int seg = unit / p.HV, h = unit - seg * p.HV;  // h: value head
   SegInfo si;
   if (!locate(p, seg, si)) return;
   if (!OUT && si.s >= si.nseg - 1) return;
@@ -267,10 +269,13 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   const int seg_len = (nchunks + si.nseg - 1) / si.nseg;
   const int c_begin = si.s * seg_len;
   const int c_end = min(c_begin + seg_len, nchunks);
-  const int H = p.H, V = p.V;
+  const int H = p.HV, V = p.V;  // value heads: v, o, g, states
   const int v0 = vt * VW;
   const int nkeys = p.K;  // real keys (<= KD); keys nkeys..KD-1 are zero padding
-  const int64_t rowK = (int64_t)H * p.Kmem, rowV = (int64_t)H * V;
+  // q, k come from key head h / G (rows of H key heads); g has a decay per key
+  // (rows of HV x Kmem) or one per value head (rows of HV)
+  const int64_t rowK = (int64_t)p.H * p.Kmem, rowV = (int64_t)H * V;
+  const int64_t rowG = GH ? (int64_t)H : (int64_t)H * p.Kmem;
   const int64_t seq_bos = si.bos;
   const int seq_len = si.len;
   // Lanes whose key quad or value chunk lies past the real keys / columns use
@@ -339,14 +344,15 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   const int pt = tid - 4 * 64;
   const int cq = (wave - 4) * QPW + lane % QPW, rg = lane / QPW;
   const bool key_ok = 4 * cq < nkeys;
-  const int voff_g = key_ok ? (int)((rg * RPG * rowK + 4 * cq) * 4) : kOff;
+  // a per-head gate is read once per row and used for every key
+  const int voff_g = GH ? (int)(rg * RPG * rowG * 4) : key_ok ? (int)((rg * RPG * rowG + 4 * cq) * 4) : kOff;
   const int voff_k = key_ok ? (int)((rg * RPG * rowK + 4 * cq) * 2) : kOff;
   // v: 16 B chunk vch of token rows vrow + VRS j (VW / 8 lanes per row)
   constexpr int VCH = VW / 8, VRS = 64 * L::NPW / VCH, NVL = C / VRS;
   const int vrow = pt / VCH, vch = pt % VCH;
   const int voff_v = v0 + 8 * vch < V ? (int)((vrow * rowV + 8 * vch) * 2) : kOff;
   const int vstep = (int)(VRS * rowV * 2);
-  const int step_g = (int)(rowK * 4), step_k = (int)(rowK * 2);
+  const int step_g = (int)(rowG * 4), step_k = (int)(rowK * 2);
   const int colq = kperm_bf(4 * cq) * 2;
   u32x4_t rgG[RPG];
   u32x2_t rgQ[RPG], rgK[RPG];
@@ -366,17 +372,26 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   auto rsrc = [&](int c) {
     const int64_t t0 = (int64_t)seq_bos + (int64_t)c * C;
     const int64_t valid = c < c_end ? min(C, seq_len - c * C) : 0;
-    const int64_t headK = (int64_t)h * p.Kmem + p.koff, headV = (int64_t)h * V + v0;
+    const int64_t headK = (int64_t)(h / p.G) * p.Kmem + p.koff, headV = (int64_t)h * V + v0;
+    const int64_t headG = GH ? (int64_t)h : (int64_t)h * p.Kmem + p.koff;
     Rsrc r;
-    r.g = make_rsrc(p.g + t0 * rowK + headK, (valid * rowK - headK) * 4);
+    r.g = make_rsrc(p.g + t0 * rowG + headG, (valid * rowG - headG) * 4);
     r.q = make_rsrc((const uint16_t *)p.q + t0 * rowK + headK, OUT ? (valid * rowK - headK) * 2 : 0);
     r.k = make_rsrc((const uint16_t *)p.k + t0 * rowK + headK, (valid * rowK - headK) * 2);
     r.v = make_rsrc((const uint16_t *)p.v + t0 * rowV + headV, (valid * rowV - headV) * 2);
     return r;
   };
   auto load_g = [&](const Rsrc &r) {
+    if constexpr (GH) {
 #pragma unroll
-    for (int i = 0; i < RPG; ++i) rgG[i] = buf_ld128(r.g, voff_g + i * step_g);
+      for (int i = 0; i < RPG; ++i) {
+        const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(r.g, voff_g + i * step_g, 0, 0);
+        rgG[i] = u32x4_t{x, x, x, x};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) rgG[i] = buf_ld128(r.g, voff_g + i * step_g);
+    }
   };
   auto load_v = [&](const Rsrc &r) {
 #pragma unroll
@@ -827,28 +842,33 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   }
 }
 
-template <int KD, int VW>
+template <int KD, int VW, bool GH>
 __global__ __launch_bounds__((LdsW<KD, true, VW>::THREADS), 1) void gla_chunk_output_bf16(WalkParams p) {
   __shared__ __attribute__((aligned(16))) char smem[LdsW<KD, true, VW>::BYTES];
-  walk_bf16<true, KD, VW>(p, smem);
+  walk_bf16<true, KD, VW, GH>(p, smem);
 }
 
-template <int KD, int VW>
+template <int KD, int VW, bool GH>
 __global__ __launch_bounds__((LdsW<KD, false, VW>::THREADS), 1) void gla_chunk_local_bf16(WalkParams p) {
   __shared__ __attribute__((aligned(16))) char smem[LdsW<KD, false, VW>::BYTES];
-  walk_bf16<false, KD, VW>(p, smem);
+  walk_bf16<false, KD, VW, GH>(p, smem);
 }
 
-template <int KD, int VW>
-hipError_t launch_t(bool local_mode, const WalkParams &p, hipStream_t s) {
+template <int KD, int VW, bool GH>
+hipError_t launch_g(bool local_mode, const WalkParams &p, hipStream_t s) {
   const int NV = (p.V + VW - 1) / VW;
   const int groups = (p.units + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * NV));
   if (local_mode)
-    hipLaunchKernelGGL((gla_chunk_local_bf16<KD, VW>), grid, dim3(LdsW<KD, false, VW>::THREADS), 0, s, p);
+    hipLaunchKernelGGL((gla_chunk_local_bf16<KD, VW, GH>), grid, dim3(LdsW<KD, false, VW>::THREADS), 0, s, p);
   else
-    hipLaunchKernelGGL((gla_chunk_output_bf16<KD, VW>), grid, dim3(LdsW<KD, true, VW>::THREADS), 0, s, p);
+    hipLaunchKernelGGL((gla_chunk_output_bf16<KD, VW, GH>), grid, dim3(LdsW<KD, true, VW>::THREADS), 0, s, p);
   return hipGetLastError();
+}
+
+template <int KD, int VW>
+hipError_t launch_t(bool local_mode, const WalkParams &p, hipStream_t s) {
+  return p.gate_head ? launch_g<KD, VW, true>(local_mode, p, s) : launch_g<KD, VW, false>(local_mode, p, s);
 }
 
 }  // namespace

@@ -23,8 +23,13 @@
  *    the library never allocates, frees or synchronises.  Work is enqueued on
  *    `stream` (a hipStream_t; NULL = the default stream) and runs
  *    asynchronously: results are valid once that stream has reached the call.
- *  - Layout is time-major and contiguous: q, k, g are [B, T, H, K], v and o are
- *    [B, T, H, V], h0 and ht are [N, H, K, V] (row-major, V fastest).
+ *  - Layout is time-major and contiguous: q, k are [B, T, H, K], v and o are
+ *    [B, T, HV, V], g is [B, T, HV, K] (a decay per key) or [B, T, HV] (one
+ *    per value head and token), h0 and ht are [N, HV, K, V] (row-major, V
+ *    fastest).  HV = H is the plain method; with HV a multiple of H, value head
+ *    hv reads key head hv / (HV / H) (the head layout of page
+ *    "fla/ops/gated_delta_rule/backends/triton_ascend/wy_fast.py",
+ *    recompute_w_u_fwd_kernel_npu), and each value head has its own state.
  *  - Shapes: K and V are multiples of 16 in [16, 256]; any T >= 0, B >= 0,
  *    H >= 1.  Arguments are validated on the host before anything is
  *    enqueued; on any error nothing is written and the status says why.
@@ -70,13 +75,18 @@ typedef enum gla_dtype {
     GLA_BF16 = 1   /* q, k, v, o are bfloat16; g, h0, ht are float32 either way */
 } gla_dtype;
 
+typedef enum gla_gate {
+    GLA_GATE_PER_KEY = 0,   /* g [B, T, HV, K]: a log decay per key of the state */
+    GLA_GATE_PER_HEAD = 1   /* g [B, T, HV]: one log decay per value head and token */
+} gla_gate;
+
 /* Bits of the status word (see gla_fwd's workspace). */
 #define GLA_STATUS_WAIT_EXHAUSTED 1u  /* a bounded wait between waves ran out: o may be wrong */
 
 typedef struct gla_problem {
     int32_t B;        /* batch; must be 1 for packed sequences                         */
     int32_t T;        /* tokens per sequence, or total packed tokens with cu_seqlens  */
-    int32_t H;        /* heads                                                        */
+    int32_t H;        /* key heads (q, k)                                             */
     int32_t K;        /* key width: a multiple of 16 in [16, 256]                      */
     int32_t V;        /* value width: a multiple of 16 in [16, 256]                    */
     int32_t dtype;    /* gla_dtype of q, k, v and o                                   */
@@ -92,6 +102,8 @@ typedef struct gla_problem {
     int32_t wait_limit; /* 0: default bound on each wait between waves (2^22 polls);  */
                       /* > 0: that many polls; -1: no polls, every such wait reports */
                       /* GLA_STATUS_WAIT_EXHAUSTED at once (a test hook)               */
+    int32_t HV;       /* value heads (v, g, o, h0, ht): 0 means H; else a multiple of H */
+    int32_t gate;     /* gla_gate: layout of g                                        */
 } gla_problem;
 
 /*
@@ -103,11 +115,11 @@ size_t gla_fwd_workspace_bytes(const gla_problem *p);
 
 /*
  * Chunkwise gated linear attention forward.
- *   q, k   : [B,T,H,K] dtype            g  : [B,T,H,K] float32, natural-log decay
- *   v      : [B,T,H,V] dtype            h0 : [N,H,K,V] float32 or NULL (zero state)
+ *   q, k   : [B,T,H,K] dtype            g  : [B,T,HV,K] or [B,T,HV] float32, natural-log decay
+ *   v      : [B,T,HV,V] dtype           h0 : [N,HV,K,V] float32 or NULL (zero state)
  *   cu_seqlens : [N+1] int32 token offsets or NULL (then N = B sequences of T tokens)
- *   o      : [B,T,H,V] dtype, written for every token of every sequence
- *   ht     : [N,H,K,V] float32 or NULL; when non-NULL it receives the state after
+ *   o      : [B,T,HV,V] dtype, written for every token of every sequence
+ *   ht     : [N,HV,K,V] float32 or NULL; when non-NULL it receives the state after
  *            each sequence's last token (h0, or zeros, for an empty sequence)
  *   workspace / workspace_bytes : device scratch of at least
  *            gla_fwd_workspace_bytes(p) bytes.  Its first 4 bytes are a sticky

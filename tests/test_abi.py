@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def prob(**kw):
     base = dict(B=2, T=100, H=3, K=64, V=128, dtype=gla.GLA_BF16, n_seqs=2, chunk=64, scale=0.125,
-                segment_chunks=1, packed=0, value_tile=0, wait_limit=0)
+                segment_chunks=1, packed=0, value_tile=0, wait_limit=0, HV=0, gate=0)
     base.update(kw)
     return gla.Problem(**base)
 
@@ -84,6 +84,9 @@ def call_noalloc(lib, p, q=FAKE, k=FAKE, v=FAKE, g=FAKE, cu=None, o=FAKE):
     (dict(packed=1), BAD_SHAPE),        # packing needs B == 1
     (dict(segment_chunks=-2), BAD_SHAPE),
     (dict(wait_limit=-2), BAD_SHAPE),
+    (dict(HV=4), BAD_SHAPE),            # value heads must be a multiple of the key heads
+    (dict(HV=-3), BAD_SHAPE),
+    (dict(gate=2), UNSUPPORTED),
 ])
 def test_invalid_problems_are_rejected(lib, kw, code):
     p = prob(**kw)
@@ -147,6 +150,14 @@ def test_noalloc_rejects_problems_beyond_its_scratch(lib):
     assert call_noalloc(lib, big) == WORKSPACE
     assert call_noalloc(lib, None) == NULL_ARG
     assert call_noalloc(lib, prob(), q=None) == NULL_ARG
+
+
+def test_value_heads_size_the_workspace(lib):
+    # states and segment summaries exist per value head
+    p = prob(T=1000, K=64, V=128, H=3, HV=6, segment_chunks=2, gate=1)
+    slots = 2 * 8
+    assert lib.gla_fwd_workspace_bytes(ctypes.byref(p)) == (WS_HEADER + up(slots * 6 * 64 * 128 * 4)
+                                                           + up(slots * 6 * 64 * 4))
 
 
 def test_status_strings(lib):

@@ -152,6 +152,28 @@ def test_strong_gates_packed_and_split_keys(dtype, K, V):
     _compare(d, dtype, f"strong gates packed K={K} V={V}", segment_chunks=1)
 
 
+# value heads grouped on key heads (HV = G H: value head hv reads key head
+# hv // G) and a gate per value head and token instead of per key
+@pytest.mark.parametrize("dtype,K,V,vtile", [("bf16", 128, 128, 128), ("bf16", 128, 128, 64), ("bf16", 64, 96, 0),
+                                             ("fp32", 64, 64, 0), ("bf16", 192, 64, 0)])
+@pytest.mark.parametrize("H,HV,gate", [(2, 2, "head"), (1, 4, "key"), (2, 6, "head"), (2, 4, "key")])
+@pytest.mark.parametrize("seg", [0, 3])
+def test_head_and_gate_variants(dtype, K, V, vtile, H, HV, gate, seg):
+    d = gi.draw(1300 + HV + K + seg, 2, 200, H, K, V, dtype=dtype, h0=True, HV=HV, gate=gate)
+    _compare(d, dtype, f"H={H} HV={HV} gate={gate} K={K} V={V}", segment_chunks=seg, value_tile=vtile)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_head_variants_packed_and_strong(dtype):
+    # packed sequences with a per-head gate strong enough for the token-by-token path
+    lengths = [150, 0, 64, 97]
+    d = gi.draw(1310, 1, 0, 2, 128, 64, dtype=dtype, h0=True, lengths=lengths, HV=4, gate="head")
+    g = d["g"].copy()
+    g[:, 40:120, 1] = -3.0
+    d["g"] = g
+    _compare(d, dtype, "packed H=2 HV=4 per-head gate", segment_chunks=1)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("seg", [1, 2, 3, 5])
 def test_forced_segments(dtype, seg):
