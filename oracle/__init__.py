@@ -49,6 +49,9 @@ def _load():
         lib.gla_oracle_fwd_heads.argtypes = [i64, p, i64, i64, i64, i64, ctypes.c_int, p, p, p, p, p,
                                              ctypes.c_double, p, p, ctypes.c_int]
         lib.gla_oracle_fwd_heads.restype = ctypes.c_int
+        lib.gla_oracle_bwd.argtypes = [i64, p, i64, i64, i64, p, p, p, p, p, ctypes.c_double, p, p,
+                                       p, p, p, p, p, ctypes.c_int]
+        lib.gla_oracle_bwd.restype = ctypes.c_int
         lib.gla_oracle_max_threads.argtypes = []
         lib.gla_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -110,3 +113,45 @@ def gla_reference(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray,
     if rc != 0:
         raise RuntimeError("oracle failed")
     return o, ht
+
+
+def gla_reference_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, do: np.ndarray,
+                      h0: Optional[np.ndarray] = None, dht: Optional[np.ndarray] = None,
+                      cu_seqlens: Optional[np.ndarray] = None, scale: Optional[float] = None,
+                      threads: int = 0):
+    """Gradients of L = sum(do * o) + sum(dht * ht) by the reverse token recurrence (fp64).
+
+    q, k, g: [B, T, H, K]; v, do: [B, T, H, V]; h0, dht: [N, H, K, V] or None.
+    Returns dq, dk, dg [B, T, H, K], dv [B, T, H, V] and dh0 [N, H, K, V], float64.
+    Memory is T * K * V doubles per (sequence, head) job: for test sizes.
+    """
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, V) or do.shape != v.shape:
+        raise ValueError("shape mismatch")
+    if scale is None:
+        scale = K ** -0.5
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("packed sequences need a batch of one")
+        offsets = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+        if offsets[0] != 0 or offsets[-1] != T or np.any(np.diff(offsets) < 0):
+            raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+    else:
+        offsets = np.arange(B + 1, dtype=np.int64) * T
+    N = len(offsets) - 1
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    f64 = lambda a: None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+    for a in (h0, dht):
+        if a is not None and a.shape != (N, H, K, V):
+            raise ValueError(f"h0 and dht must be [{N}, {H}, {K}, {V}]")
+    dq = np.zeros((B, T, H, K)); dk = np.zeros((B, T, H, K)); dg = np.zeros((B, T, H, K))
+    dv = np.zeros((B, T, H, V)); dh0 = np.zeros((N, H, K, V))
+    qf, kf, vf, gf, dof = f32(q), f32(k), f32(v), f32(g), f32(do)
+    h0d, dhtd = f64(h0), f64(dht)
+    rc = _load().gla_oracle_bwd(N, _ptr(offsets), H, K, V, _ptr(qf), _ptr(kf), _ptr(vf), _ptr(gf),
+                                _ptr(h0d), float(scale), _ptr(dof), _ptr(dhtd), _ptr(dq), _ptr(dk),
+                                _ptr(dv), _ptr(dg), _ptr(dh0), int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle failed")
+    return dq, dk, dv, dg, dh0

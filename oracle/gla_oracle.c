@@ -123,6 +123,104 @@ int gla_oracle_fwd(int64_t N, const int64_t *offsets, int64_t H, int64_t K, int6
     return gla_oracle_fwd_heads(N, offsets, H, H, K, V, 0, q, k, v, g, h0, scale, o, ht, nthreads);
 }
 
+/*
+ * Backward of the recurrence (the gradients that page "fla/ops/gla/fused_chunk.py"
+ * computes in FusedChunkGLAFunction.backward, fused_chunk_gla_bwd_kernel,
+ * bwd_inner_chunk and bwd_decay_global_cumsum, here by the chain rule of the
+ * token recurrence itself), for one value head per key head and a decay per key.
+ * With L = sum_t do_t . o_t + <dht, S_T>, and U_t = dL/dS_t (all later uses):
+ *
+ *     U_T = dht + scale q_T do_T^T,   U_t = diag(exp(g_{t+1})) U_{t+1} + scale q_t do_t^T
+ *     dq_t = scale S_t do_t           dk_t = U_t v_t           dv_t = U_t^T k_t
+ *     dg_t = exp(g_t) * rowsum(U_t (.) S_{t-1})               dh0 = diag(exp(g_1)) U_1
+ *
+ * (S_{t-1} of the first token is h0.)  The page's backward takes no dht and
+ * returns no dh0; here dht may be given (NULL: zero) and dh0 is returned when
+ * asked for.  Every S_t of a (sequence, head) is kept, so memory is
+ * T * K * V doubles per job (test sizes only).
+ *
+ * Arguments as gla_oracle_fwd plus: do_ [T][H][V], dht [N][H][K][V] double or NULL;
+ * outputs dq, dk [T][H][K], dv [T][H][V], dg [T][H][K], dh0 [N][H][K][V] or NULL,
+ * all double.
+ */
+int gla_oracle_bwd(int64_t N, const int64_t *offsets, int64_t H, int64_t K, int64_t V,
+                   const float *q, const float *k, const float *v, const float *g,
+                   const double *h0, double scale, const float *do_, const double *dht,
+                   double *dq, double *dk, double *dv, double *dg, double *dh0, int nthreads)
+{
+    if (N < 0 || H <= 0 || K <= 0 || V <= 0 || !offsets || !dq || !dk || !dv || !dg)
+        return -1;
+    for (int64_t n = 0; n < N; ++n)
+        if (offsets[n + 1] < offsets[n]) return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int failed = 0;
+    const int64_t jobs = N * H;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (int64_t job = 0; job < jobs; ++job) {
+        const int64_t n = job / H, h = job % H;
+        const int64_t t0 = offsets[n], L = offsets[n + 1] - offsets[n];
+        const int64_t KV = K * V;
+        /* states S_{-1} (h0) .. S_{L-1}, one K x V block each */
+        double *S = (double *)malloc(sizeof(double) * (size_t)((L + 1) * KV));
+        double *U = (double *)malloc(sizeof(double) * (size_t)KV);
+        if (!S || !U) { free(S); free(U); failed |= 1; continue; }
+        if (h0) memcpy(S, h0 + (n * H + h) * KV, sizeof(double) * (size_t)KV);
+        else memset(S, 0, sizeof(double) * (size_t)KV);
+        for (int64_t t = 0; t < L; ++t) {
+            const float *kt = k + ((t0 + t) * H + h) * K;
+            const float *gt = g + ((t0 + t) * H + h) * K;
+            const float *vt = v + ((t0 + t) * H + h) * V;
+            const double *prev = S + t * KV;
+            double *cur = S + (t + 1) * KV;
+            for (int64_t i = 0; i < K; ++i) {
+                const double decay = exp((double)gt[i]);
+                for (int64_t j = 0; j < V; ++j)
+                    cur[i * V + j] = decay * prev[i * V + j] + (double)kt[i] * (double)vt[j];
+            }
+        }
+        /* reverse sweep: U holds dL/dS_t once the term of o_t is added */
+        if (dht) memcpy(U, dht + (n * H + h) * KV, sizeof(double) * (size_t)KV);
+        else memset(U, 0, sizeof(double) * (size_t)KV);
+        for (int64_t t = L - 1; t >= 0; --t) {
+            const int64_t row = (t0 + t) * H + h;
+            const float *qt = q + row * K, *kt = k + row * K, *gt = g + row * K;
+            const float *vt = v + row * V, *dot = do_ + row * V;
+            const double *St = S + (t + 1) * KV, *Sp = S + t * KV;
+            for (int64_t i = 0; i < K; ++i)
+                for (int64_t j = 0; j < V; ++j) U[i * V + j] += scale * (double)qt[i] * (double)dot[j];
+            for (int64_t i = 0; i < K; ++i) {
+                double aq = 0.0, ak = 0.0, ag = 0.0;
+                for (int64_t j = 0; j < V; ++j) {
+                    aq += St[i * V + j] * (double)dot[j];
+                    ak += U[i * V + j] * (double)vt[j];
+                    ag += U[i * V + j] * Sp[i * V + j];
+                }
+                dq[row * K + i] = scale * aq;
+                dk[row * K + i] = ak;
+                dg[row * K + i] = exp((double)gt[i]) * ag;
+            }
+            for (int64_t j = 0; j < V; ++j) {
+                double a = 0.0;
+                for (int64_t i = 0; i < K; ++i) a += U[i * V + j] * (double)kt[i];
+                dv[row * V + j] = a;
+            }
+            /* dL/dS_{t-1} from S_t = diag(exp(g_t)) S_{t-1} + ... */
+            for (int64_t i = 0; i < K; ++i) {
+                const double decay = exp((double)gt[i]);
+                for (int64_t j = 0; j < V; ++j) U[i * V + j] *= decay;
+            }
+        }
+        if (dh0) memcpy(dh0 + (n * H + h) * KV, U, sizeof(double) * (size_t)KV);
+        free(S);
+        free(U);
+    }
+    return failed ? -1 : 0;
+}
+
 /* Threads an OpenMP parallel region of this library actually gets. */
 int gla_oracle_max_threads(void)
 {
