@@ -8,8 +8,10 @@ importing the binding still works but every call raises.
 
     o, ht = gla_fwd(q, k, v, g, h0=None, cu_seqlens=None, scale=None,
                     chunk=64, output_final_state=False)
+    dq, dk, dv, dg, dh0 = gla_bwd(q, k, v, g, do, h0=None, dht=None,
+                                  cu_seqlens=None, scale=None)
 
-K and V are multiples of 16 in [16, 256].
+K and V are multiples of 16 in [16, 256] (the backward: up to 128).
 
 Shapes are time-major: q, k [B, T, H, K]; v [B, T, HV, V]; g [B, T, HV, K]
 (a decay per key) or [B, T, HV] (one per value head); h0, ht [N, HV, K, V]
@@ -28,7 +30,7 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
-__all__ = ["gla_fwd", "gla_fwd_noalloc", "GlaCall", "workspace_bytes", "library_path", "load_library", "GlaError",
+__all__ = ["gla_fwd", "gla_bwd", "gla_fwd_noalloc", "bwd_workspace_bytes", "GlaCall", "workspace_bytes", "library_path", "load_library", "GlaError",
            "STATUS", "Problem", "STATUS_WAIT_EXHAUSTED", "read_status"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +83,10 @@ def load_library():
     lib.gla_fwd.restype = ctypes.c_int
     lib.gla_fwd_noalloc.argtypes = [ctypes.POINTER(Problem), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gla_fwd_noalloc.restype = ctypes.c_int
+    lib.gla_bwd_workspace_bytes.argtypes = [ctypes.POINTER(Problem)]
+    lib.gla_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.gla_bwd.argtypes = [ctypes.POINTER(Problem)] + [vp] * 14 + [ctypes.c_size_t, vp]
+    lib.gla_bwd.restype = ctypes.c_int
     lib.gla_status_str.argtypes = [ctypes.c_int]
     lib.gla_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -104,6 +110,14 @@ def workspace_bytes(problem: Problem) -> int:
     n = lib.gla_fwd_workspace_bytes(ctypes.byref(problem))
     if n == ctypes.c_size_t(-1).value:
         raise GlaError(2, "invalid problem")
+    return int(n)
+
+
+def bwd_workspace_bytes(problem: Problem) -> int:
+    lib = load_library()
+    n = lib.gla_bwd_workspace_bytes(ctypes.byref(problem))
+    if n == ctypes.c_size_t(-1).value:
+        raise GlaError(5, "invalid problem for the backward")
     return int(n)
 
 
@@ -192,6 +206,50 @@ def gla_fwd_noalloc(q, k, v, g, o, h0=None, cu_seqlens=None, ht=None, scale: Opt
                                  _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(status), stream)
     if rc != 0:
         raise GlaError(rc, _status_msg(lib, rc))
+
+
+def gla_bwd(q, k, v, g, do, h0=None, dht=None, cu_seqlens=None, scale: Optional[float] = None,
+            chunk: int = CHUNK, need_dh0: Optional[bool] = None, workspace=None):
+    """Gradients of the forward through libgla.so's gla_bwd.
+
+    ``do`` is the gradient of o (v's shape and dtype), ``dht`` that of the final
+    state ([N, HV, K, V] float32) or None.  Returns (dq, dk, dv, dg, dh0): dq, dk
+    like q, dv like v, dg like g (float32), dh0 [N, HV, K, V] float32 when
+    ``need_dh0`` (default: h0 was given) else None.  Asynchronous on torch's
+    current stream; a given ``workspace`` (uint8, zeroed before its first use) is
+    used when large enough.
+    """
+    import torch
+
+    lib = load_library()
+    prob, N, dev = _problem_for(q, k, v, g, h0, cu_seqlens, None, scale, chunk, 0, 0, 0)
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    if do.shape != v.shape or do.dtype != v.dtype or do.device != dev or not do.is_contiguous():
+        raise ValueError("do must be a contiguous tensor of v's shape and dtype on v's device")
+    if dht is not None and (tuple(dht.shape) != (N, HV, K, V) or dht.dtype != torch.float32
+                            or dht.device != dev or not dht.is_contiguous()):
+        raise ValueError(f"dht must be a contiguous float32 [{N}, {HV}, {K}, {V}] tensor on {dev}")
+    if need_dh0 is None:
+        need_dh0 = h0 is not None
+    with torch.cuda.device(dev):
+        ws = lib.gla_bwd_workspace_bytes(ctypes.byref(prob))
+        if ws == ctypes.c_size_t(-1).value:
+            rc = lib.gla_bwd(ctypes.byref(prob), *([None] * 14), 0, None)
+            raise GlaError(rc, _status_msg(lib, rc))
+        dq, dk = torch.empty_like(q), torch.empty_like(k)
+        dv = torch.empty_like(v)
+        dg = torch.empty_like(g)
+        dh0 = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev) if need_dh0 else None
+        if workspace is None or workspace.numel() * workspace.element_size() < ws:
+            workspace = _new_workspace(ws, dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.gla_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0), _ptr(cu_seqlens),
+                         _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dh0),
+                         _ptr(workspace), workspace.numel() * workspace.element_size(), stream)
+    if rc != 0:
+        raise GlaError(rc, _status_msg(lib, rc))
+    return dq, dk, dv, dg, dh0
 
 
 def _problem_for(q, k, v, g, h0, cu_seqlens, out, scale, chunk, segment_chunks, value_tile, wait_limit):

@@ -7,6 +7,15 @@
 //   per key block (one, or two when K > 128):
 //     [some sequence spans several segments]   gla_chunk_local -> gla_state_scan
 //     always                                   gla_chunk_output
+//
+// Backward (page "fla/ops/gla/fused_chunk.py", FusedChunkGLAFunction.backward):
+//   [packed input]                       gla_segment_plan (one chunk per segment)
+//   [some sequence has 2+ chunks]        gla_chunk_local -> gla_state_scan: the state
+//                                        after every chunk
+//   [tokens]                             gla_bwd_dlocal: chunk summaries of the state gradient
+//   [tokens, or dh0 wanted]              gla_bwd_dscan: E_c per chunk, dh0
+//   [tokens]                             gla_bwd_chunk, gla_bwd_chunk_exact
+//                                        (+ gla_bwd_group_sum with HV > H)
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -247,6 +256,113 @@ gla_status run_forward(const gla_problem *p, const Plan &pl, const void *q, cons
   return GLA_OK;
 }
 
+// Backward: the forward plan with one chunk per segment (so that the forward
+// kernels leave the state after every chunk), followed by the backward's own
+// tables.  K and V of at most 128.
+struct BwdPlan {
+  Plan fwd;
+  size_t off_base, off_dstate, off_ddecay, off_flags, off_dq_part, off_dk_part, total;
+  bool ok;
+};
+
+BwdPlan make_bwd_plan(const gla_problem *p, bool varlen) {
+  BwdPlan b{};
+  gla_problem p1 = *p;
+  p1.segment_chunks = 1;
+  b.fwd = make_plan(&p1, varlen);
+  const Plan &pl = b.fwd;
+  const long long HV = p->HV == 0 ? p->H : p->HV;
+  const long long G = HV / p->H;
+  const long long slots = pl.seg_slots;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t cur = kHeaderBytes + up(pl.ws_state) + up(pl.ws_decay);
+  b.off_base = cur;
+  cur += up(varlen ? (size_t)(pl.N + 1 + slots) * sizeof(int32_t) : 0);
+  b.off_dstate = cur;
+  cur += up((size_t)slots * HV * p->K * p->V * sizeof(float));
+  b.off_ddecay = cur;
+  cur += up((size_t)slots * HV * p->K * sizeof(float));
+  b.off_flags = cur;
+  cur += up((size_t)slots * HV * sizeof(int32_t));
+  const size_t part = G > 1 ? up((size_t)p->B * p->T * HV * p->K * sizeof(float)) : 0;
+  b.off_dq_part = cur;
+  cur += part;
+  b.off_dk_part = cur;
+  cur += part;
+  b.total = cur;
+  const long long scan_blocks = (long long)pl.N * HV * ((p->K * p->V / 4 + 255) / 256);
+  const long long rows_quads = (long long)p->B * p->T * p->H * (p->K / 4);
+  b.ok = pl.ok && slots * HV <= INT_MAX && scan_blocks <= INT_MAX && (rows_quads + 255) / 256 <= INT_MAX;
+  return b;
+}
+
+gla_status validate_bwd(const gla_problem *p) {
+  const gla_status st = validate(p);
+  if (st != GLA_OK) return st;
+  if (p->K > gla::kMaxKeyBlock || p->V > 128) return GLA_ERR_UNSUPPORTED;
+  return GLA_OK;
+}
+
+gla_status run_backward(const gla_problem *p, const BwdPlan &bpl, const void *q, const void *k, const void *v,
+                        const float *g, const float *h0, const int32_t *cu_seqlens, const void *dout,
+                        const float *dht, void *dq, void *dk, void *dv, float *dg, float *dh0, char *ws,
+                        uint32_t *status, hipStream_t s) {
+  const bool varlen = p->packed == 1;
+  const int N = varlen ? p->n_seqs : p->B;
+  if (N == 0) return GLA_OK;
+  const bool tokens = (long long)p->B * p->T > 0;
+  if (!tokens && dh0 == nullptr) return GLA_OK;
+  const Plan &pl = bpl.fwd;
+  const bool fast = uses_bf16_walker(p);
+  const bool bf = p->dtype == GLA_BF16;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  gla::WalkParams w{};
+  w.q = q; w.k = k; w.v = v; w.g = g; w.h0 = h0; w.cu = cu_seqlens;
+  w.status = status;
+  w.seg_state = pl.segmented ? reinterpret_cast<float *>(ws + kHeaderBytes) : nullptr;
+  w.seg_decay = pl.segmented ? reinterpret_cast<float *>(ws + kHeaderBytes + up(pl.ws_state)) : nullptr;
+  int32_t *seg_base = varlen ? reinterpret_cast<int32_t *>(ws + bpl.off_base) : nullptr;
+  w.seg_base = seg_base;
+  w.seg_order = seg_base ? seg_base + N + 1 : nullptr;
+  w.T = p->T; w.H = p->H; w.K = p->K; w.V = p->V; w.N = N;
+  w.HV = p->HV == 0 ? p->H : p->HV;
+  w.G = w.HV / p->H;
+  w.gate_head = p->gate == GLA_GATE_PER_HEAD ? 1 : 0;
+  w.Kmem = p->K;
+  w.koff = 0;
+  w.R = pl.R;
+  w.P = pl.P;
+  w.units = (int)pl.units;
+  w.seg_slots = pl.seg_slots;
+  w.vtile = pl.vtile;
+  w.wait_polls = p->wait_limit == 0 ? gla::kDefaultWaitPolls : (p->wait_limit < 0 ? 0 : p->wait_limit);
+  w.scale = p->scale;
+
+  if (seg_base && gla::launch_segment_plan(w, seg_base, seg_base + N + 1, s) != hipSuccess) return GLA_ERR_HIP;
+  if (tokens && pl.segmented) {
+    const int kd = kernel_key_width(fast, bf, w.K);
+    const hipError_t e = fast ? gla::launch_walk_bf16(true, kd, w, s) : gla::launch_walk_general(true, bf, kd, w, s);
+    if (e != hipSuccess || gla::launch_state_scan(w, s) != hipSuccess) return GLA_ERR_HIP;
+  }
+  gla::BwdParams b{};
+  b.w = w;
+  b.w.seg_order = nullptr;
+  b.dout = dout; b.dht = dht;
+  b.dq = dq; b.dk = dk; b.dv = dv; b.dg = dg; b.dh0 = dh0;
+  b.fstate = w.seg_state;
+  b.dstate = reinterpret_cast<float *>(ws + bpl.off_dstate);
+  b.ddecay = reinterpret_cast<float *>(ws + bpl.off_ddecay);
+  b.flags = reinterpret_cast<int32_t *>(ws + bpl.off_flags);
+  if (w.G > 1) {
+    b.dq_part = reinterpret_cast<float *>(ws + bpl.off_dq_part);
+    b.dk_part = reinterpret_cast<float *>(ws + bpl.off_dk_part);
+  }
+  if (tokens && gla::launch_bwd_dlocal(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
+  if (gla::launch_bwd_dscan(b, s) != hipSuccess) return GLA_ERR_HIP;
+  if (tokens && gla::launch_bwd_chunk(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
 // Host-side checks of a call (same for both entry points).
 gla_status check_call(const gla_problem *p, const void *q, const void *k, const void *v, const float *g,
                       const void *o, const int32_t *cu_seqlens, Plan &pl) {
@@ -293,7 +409,7 @@ const char *gla_status_str(gla_status s) {
     case GLA_ERR_BAD_SHAPE: return "invalid or inconsistent sizes";
     case GLA_ERR_BAD_DTYPE: return "dtype must be GLA_F32 or GLA_BF16";
     case GLA_ERR_BAD_SCALE: return "scale must be finite and > 0";
-    case GLA_ERR_UNSUPPORTED: return "unsupported K, V, chunk or value tile";
+    case GLA_ERR_UNSUPPORTED: return "unsupported K, V, chunk or value tile (backward: K, V <= 128)";
     case GLA_ERR_WORKSPACE: return "workspace missing or too small";
     case GLA_ERR_HIP: return "HIP runtime or launch failure";
   }
@@ -317,6 +433,31 @@ gla_status gla_fwd(const gla_problem *p, const void *q, const void *k, const voi
   char *ws = reinterpret_cast<char *>(workspace);
   return run_forward(p, pl, q, k, v, g, h0, cu_seqlens, o, ht, ws, reinterpret_cast<uint32_t *>(ws),
                      reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t gla_bwd_workspace_bytes(const gla_problem *p) {
+  if (validate_bwd(p) != GLA_OK) return (size_t)-1;
+  const BwdPlan b = make_bwd_plan(p, p->packed == 1);
+  if (!b.ok) return (size_t)-1;
+  return b.total;
+}
+
+gla_status gla_bwd(const gla_problem *p, const void *q, const void *k, const void *v, const float *g,
+                   const float *h0, const int32_t *cu_seqlens, const void *dout, const float *dht, void *dq,
+                   void *dk, void *dv, float *dg, float *dh0, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+  const gla_status st = validate_bwd(p);
+  if (st != GLA_OK) return st;
+  const bool varlen = p->packed == 1;
+  if (varlen != (cu_seqlens != nullptr)) return GLA_ERR_NULL_ARG;
+  const bool empty_tokens = (long long)p->B * p->T == 0;
+  if (!empty_tokens && (!q || !k || !v || !g || !dout || !dq || !dk || !dv || !dg)) return GLA_ERR_NULL_ARG;
+  const BwdPlan b = make_bwd_plan(p, varlen);
+  if (!b.ok) return GLA_ERR_BAD_SHAPE;
+  if (workspace == nullptr || workspace_bytes < b.total) return GLA_ERR_WORKSPACE;
+  char *ws = reinterpret_cast<char *>(workspace);
+  return run_backward(p, b, q, k, v, g, h0, cu_seqlens, dout, dht, dq, dk, dv, dg, dh0, ws,
+                      reinterpret_cast<uint32_t *>(ws), reinterpret_cast<hipStream_t>(stream));
 }
 
 gla_status gla_fwd_noalloc(const gla_problem *p, const void *q, const void *k, const void *v, const float *g,

@@ -160,6 +160,51 @@ gla_status gla_fwd_noalloc(const gla_problem *p,
                            void *o, float *ht, uint32_t *status,
                            void *stream);
 
+/*
+ * Workspace bytes gla_bwd needs for problem `p` on the current device; at
+ * least 256.  Returns (size_t)-1 when `p` is invalid for the backward.
+ */
+size_t gla_bwd_workspace_bytes(const gla_problem *p);
+
+/*
+ * Backward of the forward above (page "fla/ops/gla/fused_chunk.py":
+ * FusedChunkGLAFunction.backward with fused_chunk_gla_bwd_kernel and
+ * bwd_inner_chunk): for the loss L with dL/do = do_ and dL/dht = dht it returns
+ * the gradients of q, k, v, g and h0.  With U_t = dL/dS_t of each sequence and
+ * value head:
+ *     dq_t = scale S_t do_t,  dk_t = U_t v_t,  dv_t = U_t^T k_t,
+ *     dg_t = sum over tokens s >= t of (q_s * dq_s - k_s * dk_s)  +  rowsum(dht * ht)
+ *     dh0  = dL/dS_0
+ * (elementwise products; dq and dk of a key head sum over its value heads; a
+ * per-head gate's gradient sums over keys).  Forward states are recomputed;
+ * nothing from a forward call is needed.
+ *   q, k, v, g, h0, cu_seqlens : as for gla_fwd (h0 NULL = zero state)
+ *   do_    : [B,T,HV,V] dtype, gradient of o
+ *   dht    : [N,HV,K,V] float32 gradient of ht, or NULL (zero)
+ *   dq, dk : [B,T,H,K] dtype      dv : [B,T,HV,V] dtype
+ *   dg     : [B,T,HV,K] float32 (per-key gate) or [B,T,HV] (per-head gate)
+ *   dh0    : [N,HV,K,V] float32 or NULL (not computed)
+ *   workspace / workspace_bytes : device scratch of at least
+ *            gla_bwd_workspace_bytes(p) bytes, first 4 bytes a sticky status
+ *            word as for gla_fwd.  It holds the state after every chunk and the
+ *            state gradient reaching every chunk: 2 * chunks * HV * K * V * 4
+ *            bytes and more.
+ * Supported: K and V multiples of 16 up to 128 (else GLA_ERR_UNSUPPORTED),
+ * both dtypes, both gate layouts, HV a multiple of H, packed sequences.  Every
+ * output row of a token is written; rows of other tokens are untouched.
+ * Gates are exact as in the forward: a chunk in which some key decays by more
+ * than e^-80 is evaluated token by token.  Returns GLA_OK or an error code; on
+ * error nothing is written.  Pointers are device memory owned by the caller,
+ * 16-byte aligned; work is asynchronous on `stream`.
+ */
+gla_status gla_bwd(const gla_problem *p,
+                   const void *q, const void *k, const void *v, const float *g,
+                   const float *h0, const int32_t *cu_seqlens,
+                   const void *do_, const float *dht,
+                   void *dq, void *dk, void *dv, float *dg, float *dh0,
+                   void *workspace, size_t workspace_bytes,
+                   void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *gla_status_str(gla_status s);
 

@@ -121,10 +121,43 @@ def gla_reference_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray
                       threads: int = 0):
     """Gradients of L = sum(do * o) + sum(dht * ht) by the reverse token recurrence (fp64).
 
-    q, k, g: [B, T, H, K]; v, do: [B, T, H, V]; h0, dht: [N, H, K, V] or None.
-    Returns dq, dk, dg [B, T, H, K], dv [B, T, H, V] and dh0 [N, H, K, V], float64.
-    Memory is T * K * V doubles per (sequence, head) job: for test sizes.
+    q, k: [B, T, H, K]; v, do: [B, T, HV, V]; g: [B, T, HV, K] (a decay per key)
+    or [B, T, HV] (one per value head); h0, dht: [N, HV, K, V] or None.
+    Returns dq, dk [B, T, H, K], dv [B, T, HV, V], dg (g's shape), dh0 [N, HV, K, V],
+    float64.
+
+    Value-head groups and per-head gates reduce exactly to the plain method
+    (page "fla/ops/gated_delta_rule/backends/triton_ascend/wy_fast.py" maps value
+    head hv to key head hv // (HV // H)): value head hv is an independent plain
+    head whose q, k are key head hv // G's, and a per-head gate is the same
+    decay on every key.  So the plain backward runs on q, k repeated per value
+    head and the gate broadcast over keys, and the chain rule sums back: dq, dk
+    of a key head over its G value heads, a per-head dg over keys.
     """
+    B, T, H, K = q.shape
+    HV = v.shape[2]
+    if HV % H != 0 or v.shape[:2] != (B, T):
+        raise ValueError("v must be [B, T, HV, V] with HV a multiple of H")
+    per_head = g.shape == (B, T, HV)
+    if not per_head and g.shape != (B, T, HV, K):
+        raise ValueError("g must be [B, T, HV, K] or [B, T, HV]")
+    if HV != H or per_head:
+        G = HV // H
+        qe = np.repeat(np.asarray(q), G, axis=2)
+        ke = np.repeat(np.asarray(k), G, axis=2)
+        ge = np.broadcast_to(np.asarray(g)[..., None], (B, T, HV, K)) if per_head else np.asarray(g)
+        dq, dk, dv, dg, dh0 = _reference_bwd_plain(qe, ke, v, ge, do, h0, dht, cu_seqlens, scale, threads)
+        dq = dq.reshape(B, T, H, G, K).sum(axis=3)
+        dk = dk.reshape(B, T, H, G, K).sum(axis=3)
+        if per_head:
+            dg = dg.sum(axis=3)
+        return dq, dk, dv, dg, dh0
+    return _reference_bwd_plain(q, k, v, g, do, h0, dht, cu_seqlens, scale, threads)
+
+
+def _reference_bwd_plain(q, k, v, g, do, h0, dht, cu_seqlens, scale, threads):
+    """The plain method (HV = H, a decay per key) through gla_oracle_bwd.
+    Memory is T * K * V doubles per (sequence, head) job: for test sizes."""
     B, T, H, K = q.shape
     V = v.shape[-1]
     if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, V) or do.shape != v.shape:

@@ -31,7 +31,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["gla_fwd", "gla_fwd_noalloc", "gla_fwd_workspace_bytes", "gla_status_str"]
+    assert declared_functions() == ["gla_bwd", "gla_bwd_workspace_bytes", "gla_fwd", "gla_fwd_noalloc",
+                                    "gla_fwd_workspace_bytes", "gla_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -174,3 +175,63 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 4, 1, 64)
     with pytest.raises(ValueError):
         gla.gla_fwd(x, x, x, x)
+
+
+# ---------------------------------------------------------------- backward entry point
+
+def call_bwd(lib, p, ws=FAKE, ws_bytes=1 << 40, cu=None, dq=FAKE, do=FAKE):
+    return lib.gla_bwd(ctypes.byref(p) if p is not None else None, FAKE, FAKE, FAKE, FAKE, None, cu,
+                       do, None, dq, FAKE, FAKE, FAKE, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), BAD_DTYPE),
+    (dict(scale=0.0), BAD_SCALE),
+    (dict(chunk=32), UNSUPPORTED),
+    (dict(K=24), UNSUPPORTED),
+    (dict(K=144), UNSUPPORTED),         # the backward takes K, V up to 128
+    (dict(V=144), UNSUPPORTED),
+    (dict(K=256, V=256), UNSUPPORTED),
+    (dict(n_seqs=3), BAD_SHAPE),
+    (dict(HV=4), BAD_SHAPE),
+    (dict(gate=2), UNSUPPORTED),
+])
+def test_backward_rejects_invalid_problems(lib, kw, code):
+    p = prob(**kw)
+    assert call_bwd(lib, p) == code
+    assert lib.gla_bwd_workspace_bytes(ctypes.byref(p)) == ctypes.c_size_t(-1).value
+
+
+def test_backward_null_arguments(lib):
+    assert call_bwd(lib, None) == NULL_ARG
+    assert call_bwd(lib, prob(), dq=None) == NULL_ARG
+    assert call_bwd(lib, prob(), do=None) == NULL_ARG
+    assert call_bwd(lib, prob(B=1, n_seqs=1, packed=1)) == NULL_ARG   # packed without cu_seqlens
+
+
+@pytest.mark.parametrize("dtype", [gla.GLA_BF16, gla.GLA_F32])
+@pytest.mark.parametrize("K", [16, 48, 64, 128])
+@pytest.mark.parametrize("V", [16, 96, 128])
+def test_backward_accepts_widths_up_to_128(lib, dtype, K, V):
+    p = prob(dtype=dtype, K=K, V=V)
+    assert lib.gla_bwd_workspace_bytes(ctypes.byref(p)) != ctypes.c_size_t(-1).value
+
+
+def test_backward_workspace_size_and_check(lib):
+    # B=2, T=1000: 16 chunks per sequence, one chunk per slot; the forward
+    # states after every chunk, the state gradients and chunk decays, the flags
+    B, T, H, K, V = 2, 1000, 3, 64, 128
+    p = prob(B=B, T=T, H=H, K=K, V=V)
+    slots = 2 * 16
+    states = up(slots * H * K * V * 4)
+    decays = up(slots * H * K * 4)
+    expect = WS_HEADER + states + decays + states + decays + up(slots * H * 4)
+    assert lib.gla_bwd_workspace_bytes(ctypes.byref(p)) == expect
+    assert call_bwd(lib, p, ws=None, ws_bytes=0) == WORKSPACE
+    assert call_bwd(lib, p, ws_bytes=expect - 1) == WORKSPACE
+    # value-head groups add the fp32 shares of dq and dk per value head
+    pg = prob(B=B, T=T, H=H, K=K, V=V, HV=6)
+    states6, decays6 = up(slots * 6 * K * V * 4), up(slots * 6 * K * 4)
+    expect_g = (WS_HEADER + states6 + decays6 + states6 + decays6 + up(slots * 6 * 4)
+                + 2 * up(B * T * 6 * K * 4))
+    assert lib.gla_bwd_workspace_bytes(ctypes.byref(pg)) == expect_g

@@ -1,0 +1,202 @@
+"""GPU parity of the backward (gla_bwd through the C ABI) with the fp64 oracle.
+
+Every output (dq, dk, dv, dg, dh0) is compared element by element with
+oracle.gla_reference_bwd on the same seeded inputs.  Rules, per output:
+max|err| <= tol * rms(ref), tol = 1e-4 for fp32 inputs and 2e-2 for bf16
+inputs (the forward's rule), plus half a bf16 ulp per element for outputs
+stored in bf16.  dg and dh0 are fp32 for either input dtype and are formed from
+fp32 products of exact inputs, so they are held to 1e-4 as the final state is.
+"""
+import numpy as np
+import pytest
+
+import gla_inputs as gi
+import oracle
+from gpu_helpers import TOL, TOL_HT, check_close, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import chunkwise_gated_linear_amd as gla
+    gla.load_library()
+    oracle.build(force=False)
+
+
+def grads_in(d, dtype, seed):
+    """do (v's shape, rounded like v) and dht (fp32) for input set d."""
+    rng = np.random.default_rng(seed)
+    do = rng.standard_normal(d["v"].shape).astype(np.float32)
+    if dtype == "bf16":
+        do = gi.to_bf16_f32(do)
+    N = len(d["cu_seqlens"]) - 1 if d["cu_seqlens"] is not None else d["q"].shape[0]
+    HV, K, V = d["v"].shape[2], d["q"].shape[3], d["v"].shape[3]
+    dht = rng.standard_normal((N, HV, K, V)).astype(np.float32)
+    return do, dht
+
+
+def run_bwd_gpu(d, do, dht, dtype, scale=None, need_dh0=True):
+    import torch
+    import chunkwise_gated_linear_amd as gla
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(d[n]).to(tdt).to(dev).contiguous() for n in ("q", "k", "v")}
+    g = torch.from_numpy(d["g"]).to(dev).contiguous()
+    h0 = None if d["h0"] is None else torch.from_numpy(d["h0"]).to(dev).contiguous()
+    cu = None if d["cu_seqlens"] is None else torch.from_numpy(d["cu_seqlens"]).to(dev)
+    tdo = torch.from_numpy(do).to(tdt).to(dev).contiguous()
+    tdht = None if dht is None else torch.from_numpy(dht).to(dev).contiguous()
+    ws = torch.zeros(1, dtype=torch.uint8, device=dev)
+    dq, dk, dv, dg, dh0 = gla.gla_bwd(t["q"], t["k"], t["v"], g, tdo, h0=h0, dht=tdht, cu_seqlens=cu,
+                                      scale=scale, need_dh0=need_dh0)
+    torch.cuda.synchronize()
+    f = lambda x: None if x is None else x.float().cpu().numpy().astype(np.float64)
+    return f(dq), f(dk), f(dv), f(dg), f(dh0)
+
+
+def check_bwd(d, dtype, seed, scale=None, use_dht=True, need_dh0=True, label=""):
+    do, dht = grads_in(d, dtype, seed)
+    if not use_dht:
+        dht = None
+    say(f"bwd {label}: q{tuple(d['q'].shape)} v{tuple(d['v'].shape)} g{tuple(d['g'].shape)} {dtype} "
+        f"h0={d['h0'] is not None} dht={dht is not None} packed={d['cu_seqlens'] is not None}")
+    got = run_bwd_gpu(d, do, dht, dtype, scale=scale, need_dh0=need_dh0)
+    ref = oracle.gla_reference_bwd(d["q"], d["k"], d["v"], d["g"], do, h0=d["h0"], dht=dht,
+                                   cu_seqlens=d["cu_seqlens"], scale=scale)
+    tol = TOL[dtype]
+    errs = {}
+    for name, a, b in zip(("dq", "dk", "dv", "dg", "dh0"), got, ref):
+        if name == "dh0" and not need_dh0:
+            assert a is None
+            continue
+        if name in ("dg", "dh0"):
+            errs[name] = check_close(name, a, b, TOL_HT)
+        else:
+            errs[name] = check_close(name, a, b, tol, out_dtype=dtype)
+    say("   max|err|/rms: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    return errs
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("B,T,H,K,V", [
+    (2, 200, 2, 64, 64),
+    (1, 256, 2, 128, 128),
+    (2, 130, 3, 128, 64),
+    (1, 150, 2, 64, 128),
+])
+def test_shapes(dtype, B, T, H, K, V):
+    d = gi.draw(100 + T + K, B, T, H, K, V, dtype=dtype, h0=True)
+    check_bwd(d, dtype, seed=7, label="shapes")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("K,V", [(16, 16), (48, 96), (16, 128), (112, 32)])
+def test_narrow_and_odd_widths(dtype, K, V):
+    d = gi.draw(200 + K + V, 2, 100, 2, K, V, dtype=dtype, h0=True)
+    check_bwd(d, dtype, seed=8, label="widths")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 127, 129])
+def test_ragged_lengths(dtype, T):
+    d = gi.draw(300 + T, 2, T, 2, 64, 64, dtype=dtype, h0=True)
+    check_bwd(d, dtype, seed=9, label=f"T={T}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_packed(dtype):
+    d = gi.draw(401, 1, 0, 2, 64, 128, dtype=dtype, h0=True, lengths=[0, 1, 64, 65, 200, 3, 128])
+    check_bwd(d, dtype, seed=10, label="packed")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("h0,use_dht,need_dh0", [(False, True, True), (True, False, True), (False, False, False),
+                                                 (True, True, False)])
+def test_optional_states(dtype, h0, use_dht, need_dh0):
+    d = gi.draw(500, 2, 150, 2, 64, 64, dtype=dtype, h0=h0)
+    check_bwd(d, dtype, seed=11, use_dht=use_dht, need_dh0=need_dh0, label="optional")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("HV,gate", [(2, "key"), (1, "head"), (3, "head")])
+def test_head_and_gate_variants(dtype, HV, gate):
+    H = 2
+    d = gi.draw(600 + HV, 2, 140, H, 64, 64, dtype=dtype, h0=True, HV=H * HV, gate=gate)
+    check_bwd(d, dtype, seed=12, label=f"HV={H * HV} gate={gate}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_head_variants_packed(dtype):
+    d = gi.draw(650, 1, 0, 2, 64, 128, dtype=dtype, h0=True, lengths=[70, 0, 190, 5], HV=4, gate="head")
+    check_bwd(d, dtype, seed=13, label="packed heads")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("gate_scale", [4.0, 40.0])
+def test_strong_gates(dtype, gate_scale):
+    # logsigmoid(N(0,1)) * gate_scale: with 4, some chunks decay by more than
+    # e^-80 over 64 tokens on some key; with 40 nearly every chunk does.  Those
+    # chunks take the token-by-token kernel; the results must not change.
+    d = gi.draw(700, 2, 200, 2, 64, 64, dtype=dtype, h0=True, gate_scale=gate_scale)
+    check_bwd(d, dtype, seed=14, label=f"gate x{gate_scale}")
+
+
+def test_strong_gates_packed_heads():
+    d = gi.draw(710, 1, 0, 2, 64, 64, dtype="bf16", h0=True, lengths=[100, 64, 7], gate_scale=8.0, HV=4)
+    check_bwd(d, "bf16", seed=15, label="strong packed heads")
+
+
+def test_scale():
+    d = gi.draw(800, 1, 100, 2, 64, 64, dtype="fp32", h0=True)
+    check_bwd(d, "fp32", seed=16, scale=0.37, label="scale")
+
+
+def test_zero_gate_is_linear_attention():
+    # g == 0: dq = scale (tril(dO V^T) K + dO h0^T), etc.; also the GPU result
+    d = gi.draw(810, 1, 130, 1, 64, 64, dtype="fp32", h0=True)
+    d["g"] = np.zeros_like(d["g"])
+    check_bwd(d, "fp32", seed=17, label="g=0")
+
+
+def test_deterministic():
+    d = gi.draw(900, 2, 300, 2, 128, 128, dtype="bf16", h0=True)
+    do, dht = grads_in(d, "bf16", 18)
+    a = run_bwd_gpu(d, do, dht, "bf16")
+    b = run_bwd_gpu(d, do, dht, "bf16")
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def head_slice(d, heads):
+    """The same inputs restricted to some heads (heads are independent)."""
+    out = dict(d)
+    for n in ("q", "k", "v", "g"):
+        out[n] = np.ascontiguousarray(d[n][:, :, heads])
+    if d["h0"] is not None:
+        out["h0"] = np.ascontiguousarray(d["h0"][:, heads])
+    return out
+
+
+@pytest.mark.parametrize("name", ["c2048", "varlen"])
+def test_workload_sampled_heads(name):
+    """A full-size workload on the GPU; the oracle on two of its heads."""
+    w = gi.WORKLOADS[name]
+    d = gi.make_inputs(w)
+    do, dht = grads_in(d, w.dtype, 19)
+    say(f"bwd workload {name}: {w.describe() if hasattr(w, 'describe') else name}")
+    got = run_bwd_gpu(d, do, dht, w.dtype)
+    heads = [0, w.H - 1]
+    ds = head_slice(d, heads)
+    ref = oracle.gla_reference_bwd(ds["q"], ds["k"], ds["v"], ds["g"], np.ascontiguousarray(do[:, :, heads]),
+                                   h0=ds["h0"], dht=np.ascontiguousarray(dht[:, heads]),
+                                   cu_seqlens=d["cu_seqlens"])
+    errs = {}
+    for name_, a, b in zip(("dq", "dk", "dv", "dg", "dh0"), got, ref):
+        a = a[:, heads] if name_ == "dh0" else a[:, :, heads]
+        tol = TOL_HT if name_ in ("dg", "dh0") else TOL[w.dtype]
+        errs[name_] = check_close(name_, a, b, tol, out_dtype="fp32" if name_ in ("dg", "dh0") else w.dtype)
+    say("   max|err|/rms: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))

@@ -9,14 +9,16 @@ reverse.  It is checked against things that are not itself:
 * g == 0, where the method is causal linear attention and every gradient is a
   plain product of matrices;
 * planted mistakes (a dropped dht, a missing exp(g) factor in dg, dq taken
-  from the state before the update) each fail the finite-difference pin.
+  from the state before the update) each fail the finite-difference pin;
+* value-head groups and a per-head gate: central differences of the head-variant
+  closed form (brute_force_heads), for every input element.
 """
 import numpy as np
 import pytest
 
 import gla_inputs as gi
 import oracle
-from test_oracle import brute_force
+from test_oracle import brute_force, brute_force_heads
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -118,3 +120,35 @@ def test_finite_differences_catch_planted_mistakes(mistake):
         got, name = np.roll(dq, 1, axis=1), "q"
     fd = finite_difference(d["q"], d["k"], d["v"], d["g"], d["h0"], do, dht, None, scale)
     assert not close(got, fd[name]), f"planted mistake {mistake} slipped through"
+
+
+@pytest.mark.parametrize("gate", ["key", "head"])
+@pytest.mark.parametrize("HV", [1, 3])
+def test_head_variants_match_finite_differences(gate, HV):
+    B, T, H, K, V = 2, 6, 1, 3, 2
+    d = gi.draw(61 + HV, B, T, H, K, V, dtype="fp32", h0=True, HV=HV, gate=gate, gate_scale=0.5)
+    rng = np.random.default_rng(62)
+    do = rng.standard_normal(d["v"].shape)
+    dht = rng.standard_normal(d["h0"].shape)
+    scale = 0.8
+    got = oracle.gla_reference_bwd(d["q"], d["k"], d["v"], d["g"], do, h0=d["h0"], dht=dht, scale=scale)
+
+    def lossf(q, k, v, g, h0):
+        o, ht = brute_force_heads(q, k, v, g, h0=h0, scale=scale)
+        return float(np.sum(do * o) + np.sum(dht * ht))
+
+    args = {n: d[n].astype(np.float64) for n in ("q", "k", "v", "g", "h0")}
+    eps = 1e-5
+    for name, g_got in zip(("q", "k", "v", "g", "h0"), got):
+        x = args[name]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            lp = lossf(**args)
+            x[idx] = old - eps
+            lm = lossf(**args)
+            x[idx] = old
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert g_got.shape == fd.shape, name
+        assert close(g_got, fd), f"d{name} disagrees with finite differences (gate {gate}, HV {HV})"
