@@ -242,7 +242,9 @@ def gla_bwd(q, k, v, g, do, h0=None, dht=None, cu_seqlens=None, scale: Optional[
         dg = torch.empty_like(g)
         dh0 = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev) if need_dh0 else None
         if workspace is None or workspace.numel() * workspace.element_size() < ws:
-            workspace = _new_workspace(ws, dev)
+            # every byte past the status header is written before it is read
+            workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+            workspace[:256].zero_()
         stream = torch.cuda.current_stream(dev).cuda_stream
         rc = lib.gla_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0), _ptr(cu_seqlens),
                          _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dh0),

@@ -28,16 +28,18 @@
 //         rowsum(E_c . S_{c+1}) = a . rowsum(E_c . S_c) + sum_j k_j . e^{G_last - G_j} . (E_c v_j)
 //   E_{c-1} = scale (q e^G)^T do + diag(a) E_c,   E_last = dht,   dh0 = E_{-1}
 //
-// Kernels (launched by the host in this order, after the forward kernels have
-// produced the state after every chunk):
-//   gla_bwd_dlocal      per (chunk, value head): scale (q e^G)^T do and a
-//   gla_bwd_dscan       per state element, chunks in reverse: E_c in place, dh0
+// Kernels (launched by the host in this order):
+//   gla_bwd_local       per (chunk, value head): the chunk's summaries
+//                       sum_j k_j e^{G_last - G_j} v_j^T and scale (q e^G)^T do, and a
+//   gla_bwd_scan        per state element: S_c forward, E_c in reverse, dh0
 //   gla_bwd_chunk       per (chunk, value head): dq, dk, dv, dg on fp32 MFMA
 //   gla_bwd_chunk_exact per (chunk, value head) whose decay leaves the fp32 range
 //                       of the factors e^-G (some key below e^-80 within the
 //                       chunk): the same gradients token by token
 //   gla_bwd_group_sum   with several value heads per key head: dq, dk summed
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "gla_device.h"
 
@@ -110,25 +112,23 @@ __device__ __forceinline__ bool chunk_at(const WalkParams &p, int slot, ChunkAt 
   return true;
 }
 
-// Inclusive cumsum of the chunk's log decays for value head hv.  Thread t owns
-// key t % KD and rows [part * RP, part * RP + RP), part = t / KD, and returns
-// G at those rows in G[]; rows past L and keys past K count as zero decay.
-// Part totals go through tot[256]; the function ends with a barrier after
-// which tot may be reused.  Every kernel that decides whether a chunk fits the
-// factorised form calls this same function, so they decide alike.
-template <int KD, bool GH>
-__device__ __forceinline__ void chunk_cumsum(const WalkParams &p, int64_t row0, int L, int hv,
-                                             float (&G)[64 * KD / 256], float *tot) {
-  constexpr int PARTS = 256 / KD, RP = 64 / PARTS;
+// In-place inclusive cumsum down the 64 rows of a chunk's log decays in LDS:
+// buf holds the gate rows as [64][KD] fp32 (swizzled; rows past the chunk and
+// keys past K zero), or with a per-head gate one value per row in buf[0..63];
+// afterwards buf[swz<KD>(row, key)] = G for every row and key (keys past K
+// get 0).  Thread t of NT sums key t % KD over rows [part RP, part RP + RP),
+// part = t / KD; part totals go through tot[NT].  Starts after a barrier that
+// made buf visible and ends with one.
+template <int KD, bool GH, int NT>
+__device__ __forceinline__ void gate_cumsum_lds(int K, float *buf, float *tot) {
+  constexpr int PARTS = NT / KD, RP = 64 / PARTS;
   const int kk = threadIdx.x % KD, part = threadIdx.x / KD;
+  float G[RP];
   float x = 0.f;
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
     const int i = part * RP + r;
-    float gi = 0.f;
-    if (i < L && kk < p.K)
-      gi = GH ? p.g[(row0 + i) * p.HV + hv] : p.g[((row0 + i) * p.HV + hv) * p.K + kk];
-    x += gi;
+    x += (kk < K) ? (GH ? buf[i] : buf[swz<KD>(i, kk)]) : 0.f;
     G[r] = x;
   }
   tot[threadIdx.x] = x;
@@ -136,90 +136,226 @@ __device__ __forceinline__ void chunk_cumsum(const WalkParams &p, int64_t row0, 
   float off = 0.f;
   for (int q = 0; q < part; ++q) off += tot[q * KD + kk];
 #pragma unroll
-  for (int r = 0; r < RP; ++r) G[r] += off;
+  for (int r = 0; r < RP; ++r) buf[swz<KD>(part * RP + r, kk)] = G[r] + off;
   __syncthreads();
 }
 
-// ---------------------------------------------------------------- gla_bwd_dlocal
-// Chunk summary of the state gradient: dstate[slot][hv] = scale (q e^G)^T do
-// (K x V) and ddecay[slot][hv] = e^{G_last} (K).  One workgroup per
-// (chunk slot, value head); fp32 MFMA over the chunk's 64 tokens.
-template <bool BF, int KD, int VD, bool GH>
-__global__ __launch_bounds__(256, 1) void gla_bwd_dlocal(BwdParams bp) {
-  const WalkParams &p = bp.w;
-  constexpr int PARTS = 256 / KD, RP = 64 / PARTS;
-  constexpr int NKB = KD / 64, NVB = VD / 16;
-  __shared__ __attribute__((aligned(16))) float sQ[64 * KD];
-  __shared__ __attribute__((aligned(16))) float sO[64 * VD];
-  __shared__ float tot[256];
-  const int hv = (int)(blockIdx.x % (unsigned)p.HV);
-  const int slot = (int)(blockIdx.x / (unsigned)p.HV);
-  ChunkAt ca;
-  if (!chunk_at(p, slot, ca)) return;
-  const int h = hv / p.G;
-  float G[RP];
-  chunk_cumsum<KD, GH>(p, ca.row0, ca.L, hv, G, tot);
-  const int kk = threadIdx.x % KD, part = threadIdx.x / KD;
-#pragma unroll
-  for (int r = 0; r < RP; ++r) {
-    const int i = part * RP + r;
-    const float qv = (i < ca.L && kk < p.K) ? ld_el<BF>(p.q, (ca.row0 + i) * p.H * p.K + h * p.K + kk) : 0.f;
-    sQ[swz<KD>(i, kk)] = qv * __expf(G[r]);
-  }
-  if (part == PARTS - 1 && kk < p.K) bp.ddecay[((int64_t)slot * p.HV + hv) * p.K + kk] = __expf(G[RP - 1]);
-  for (int e = threadIdx.x; e < 64 * VD / 4; e += 256) {
-    const int i = e / (VD / 4), c4 = (e % (VD / 4)) * 4;
-    f32x4_t x = zero4();
-    if (i < ca.L && c4 < p.V) x = ld_el4<BF>(bp.dout, ((ca.row0 + i) * p.HV + hv) * p.V + c4);
-    lds4_st<VD>(sO, i, c4, x);
-  }
-  __syncthreads();
+// Raw row quads as loaded: bf16 quads stay packed (two words) until staged.
+template <bool BF> struct RawQuad;
+template <> struct RawQuad<true> { typedef u32x2_t type; };
+template <> struct RawQuad<false> { typedef f32x4_t type; };
+template <bool BF>
+__device__ __forceinline__ typename RawQuad<BF>::type ld_raw4(const void *base, int64_t i) {
+  if constexpr (BF) return *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(base) + i);
+  else return *reinterpret_cast<const f32x4_t *>(reinterpret_cast<const float *>(base) + i);
+}
+template <bool BF>
+__device__ __forceinline__ f32x4_t unpack4(typename RawQuad<BF>::type w) {
+  if constexpr (BF) return f32x4_t{bf_lo(w[0]), bf_hi(w[0]), bf_lo(w[1]), bf_hi(w[1])};
+  else return w;
+}
 
+// Gate rows of a chunk (value head hv) into registers: quad t of thread
+// threadIdx.x + NT t; with a per-head gate, row threadIdx.x in gh.
+template <int KD, bool GH, int NT>
+struct GateRows {
+  static constexpr int TG = 64 * KD / 4 / NT;
+  f32x4_t g[GH ? 1 : TG];
+  float gh;
+};
+template <int KD, bool GH, int NT>
+__device__ __forceinline__ void gate_load(const WalkParams &p, const ChunkAt &ca, int hv, GateRows<KD, GH, NT> &gr) {
+  if constexpr (GH) {
+    gr.gh = threadIdx.x < ca.L ? p.g[(ca.row0 + threadIdx.x) * p.HV + hv] : 0.f;
+  } else {
+#pragma unroll
+    for (int t = 0; t < GateRows<KD, GH, NT>::TG; ++t) {
+      const int e = threadIdx.x + NT * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
+      gr.g[t] = zero4();
+      if (i < ca.L && c4 < p.K) gr.g[t] = *reinterpret_cast<const f32x4_t *>(p.g + ((ca.row0 + i) * p.HV + hv) * p.K + c4);
+    }
+  }
+}
+template <int KD, bool GH, int NT>
+__device__ __forceinline__ void gate_stage(const GateRows<KD, GH, NT> &gr, float *buf) {
+  if constexpr (GH) {
+    if (threadIdx.x < 64) buf[threadIdx.x] = gr.gh;
+  } else {
+#pragma unroll
+    for (int t = 0; t < GateRows<KD, GH, NT>::TG; ++t) {
+      const int e = threadIdx.x + NT * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
+      lds4_st<KD>(buf, i, c4, gr.g[t]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- gla_bwd_local
+// Chunk summaries of the state and of its gradient, on fp32 MFMA over the
+// chunk's 64 tokens.  Task t < 2 slots HV: the first half forms, for chunk
+// slot t / HV and value head t % HV,
+//   fstate[slot][hv] = sum_j (k_j e^{G_last - G_j}) v_j^T      (K x V)
+//   ddecay[slot][hv] = e^{G_last}                               (K)
+// and the second half
+//   dstate[slot][hv] = scale sum_i (q_i e^{G_i}) do_i^T        (K x V).
+// Every factor is a decay (at most 1), so any gate is exact here.
+// Persistent workgroups (two per compute unit) walk the tasks with a stride
+// of the grid; the rows of a workgroup's next task are loaded into registers
+// while it forms and stores the current one.
+template <bool BF, int KD, int VD, bool GH>
+struct LocalRows {
+  static constexpr int TK = 64 * KD / 4 / 256, TV = 64 * VD / 4 / 256;  // row quads per thread
+  typename RawQuad<BF>::type x[TK], y[TV];
+  GateRows<KD, GH, 256> gate;
+};
+
+template <bool BF, int KD, int VD, bool GH>
+__device__ __forceinline__ bool local_task(const BwdParams &bp, long long task, ChunkAt &ca, int &hv, bool &grad) {
+  const WalkParams &p = bp.w;
+  const long long half = (long long)p.seg_slots * p.HV;
+  grad = task >= half;
+  const long long blk = grad ? task - half : task;
+  hv = (int)(blk % p.HV);
+  return chunk_at(p, (int)(blk / p.HV), ca);
+}
+
+template <bool BF, int KD, int VD, bool GH>
+__device__ __forceinline__ void local_load(const BwdParams &bp, const ChunkAt &ca, int hv, bool grad,
+                                           LocalRows<BF, KD, VD, GH> &rw) {
+  using R = LocalRows<BF, KD, VD, GH>;
+  const WalkParams &p = bp.w;
+  const int h = hv / p.G;
+  const void *xs = grad ? p.q : p.k;      // key-side rows
+  const void *ys = grad ? bp.dout : p.v;  // value-side rows
+#pragma unroll
+  for (int t = 0; t < R::TK; ++t) {
+    const int e = threadIdx.x + 256 * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
+    rw.x[t] = {};
+    if (i < ca.L && c4 < p.K) rw.x[t] = ld_raw4<BF>(xs, (ca.row0 + i) * p.H * p.K + h * p.K + c4);
+  }
+  gate_load<KD, GH, 256>(p, ca, hv, rw.gate);
+#pragma unroll
+  for (int t = 0; t < R::TV; ++t) {
+    const int e = threadIdx.x + 256 * t, i = e / (VD / 4), c4 = (e % (VD / 4)) * 4;
+    rw.y[t] = {};
+    if (i < ca.L && c4 < p.V) rw.y[t] = ld_raw4<BF>(ys, ((ca.row0 + i) * p.HV + hv) * p.V + c4);
+  }
+}
+
+template <bool BF, int KD, int VD, bool GH>
+__global__ __launch_bounds__(256, 2) void gla_bwd_local(BwdParams bp) {
+  const WalkParams &p = bp.w;
+  using R = LocalRows<BF, KD, VD, GH>;
+  constexpr int NKB = KD / 64, NVB = VD / 16;
+  __shared__ __attribute__((aligned(16))) float sA[64 * KD];  // G, then k e^{G_last - G} or scale q e^G
+  __shared__ __attribute__((aligned(16))) float sB[64 * VD];  // v or do
+  __shared__ float tot[256];
+  const long long ntask = 2LL * p.seg_slots * p.HV;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
-  f32x4_t acc[NKB][NVB];
+
+  R rw;
+  long long task = blockIdx.x;
+  ChunkAt ca;
+  int hv = 0;
+  bool grad = false;
+  // first task with a chunk (slots past a sequence's chunks have none)
+  bool have = false;
+  for (; task < ntask; task += gridDim.x)
+    if ((have = local_task<BF, KD, VD, GH>(bp, task, ca, hv, grad))) break;
+  if (have) local_load<BF, KD, VD, GH>(bp, ca, hv, grad, rw);
+  while (have) {
+    const int chv = hv;
+    const bool cgrad = grad;
+    const int slot = (int)((cgrad ? task - ntask / 2 : task) / p.HV);
+    // gate rows -> LDS, cumsum down each key column (G in sA)
+    gate_stage<KD, GH, 256>(rw.gate, sA);
+    __syncthreads();
+    gate_cumsum_lds<KD, GH, 256>(p.K, sA, tot);
+    f32x4_t xg[R::TK];
 #pragma unroll
-  for (int a = 0; a < NKB; ++a)
+    for (int t = 0; t < R::TK; ++t) {
+      const int e = threadIdx.x + 256 * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
+      const f32x4_t G4 = lds4<KD>(sA, i, c4), Gl4 = lds4<KD>(sA, 63, c4);
+      f32x4_t xt = unpack4<BF>(rw.x[t]);
 #pragma unroll
-    for (int b = 0; b < NVB; ++b) acc[a][b] = zero4();
+      for (int r = 0; r < 4; ++r) xt[r] *= cgrad ? p.scale * __expf(G4[r]) : __expf(Gl4[r] - G4[r]);
+      xg[t] = xt;
+      if (!cgrad && i == 63 && c4 < p.K) {
 #pragma unroll
-  for (int ib = 0; ib < 4; ++ib) {
-    float qa[NKB][4], ob[NVB][4];
+        for (int r = 0; r < 4; ++r) bp.ddecay[((int64_t)slot * p.HV + chv) * p.K + c4 + r] = __expf(Gl4[r]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < R::TV; ++t) {
+      const int e = threadIdx.x + 256 * t, i = e / (VD / 4), c4 = (e % (VD / 4)) * 4;
+      lds4_st<VD>(sB, i, c4, unpack4<BF>(rw.y[t]));
+    }
+    __syncthreads();  // G read by every thread
+#pragma unroll
+    for (int t = 0; t < R::TK; ++t) {
+      const int e = threadIdx.x + 256 * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
+      lds4_st<KD>(sA, i, c4, xg[t]);
+    }
+    __syncthreads();
+    // the next task's rows travel while this one's products are formed
+    have = false;
+    for (task += gridDim.x; task < ntask; task += gridDim.x)
+      if ((have = local_task<BF, KD, VD, GH>(bp, task, ca, hv, grad))) break;
+    if (have) local_load<BF, KD, VD, GH>(bp, ca, hv, grad, rw);
+
+    // transposed product (rows v, columns k): each lane then holds 4
+    // consecutive values of one state row and stores them as one float4
+    f32x4_t acc[NKB][NVB];
 #pragma unroll
     for (int a = 0; a < NKB; ++a)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) qa[a][r] = sQ[swz<KD>(ib * 16 + 4 * lg + r, (wave * NKB + a) * 16 + l16)];
+      for (int b = 0; b < NVB; ++b) acc[a][b] = zero4();
+#pragma unroll 1
+    for (int ib = 0; ib < 4; ++ib) {  // not unrolled: keeps the operand registers of one row block
+      float xa[NKB][4], yb[NVB][4];
 #pragma unroll
-    for (int b = 0; b < NVB; ++b)
+      for (int a = 0; a < NKB; ++a)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ob[b][r] = sO[swz<VD>(ib * 16 + 4 * lg + r, b * 16 + l16)];
-#pragma unroll
-    for (int a = 0; a < NKB; ++a)
+        for (int r = 0; r < 4; ++r) xa[a][r] = sA[swz<KD>(ib * 16 + 4 * lg + r, (wave * NKB + a) * 16 + l16)];
 #pragma unroll
       for (int b = 0; b < NVB; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[a][b] = mfma_f32(qa[a][r], ob[b][r], acc[a][b]);
-  }
-  float *dst = bp.dstate + ((int64_t)slot * p.HV + hv) * p.K * p.V;
+        for (int r = 0; r < 4; ++r) yb[b][r] = sB[swz<VD>(ib * 16 + 4 * lg + r, b * 16 + l16)];
 #pragma unroll
-  for (int a = 0; a < NKB; ++a)
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int b = 0; b < NVB; ++b)
+        for (int a = 0; a < NKB; ++a)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int krow = (wave * NKB + a) * 16 + 4 * lg + r, col = b * 16 + l16;
-        if (krow < p.K && col < p.V) dst[(int64_t)krow * p.V + col] = p.scale * acc[a][b][r];
+          for (int b = 0; b < NVB; ++b) acc[a][b] = mfma_f32(yb[b][r], xa[a][r], acc[a][b]);
+    }
+    float *dst = (cgrad ? bp.dstate : bp.fstate) + ((int64_t)slot * p.HV + chv) * p.K * p.V;
+#pragma unroll
+    for (int a = 0; a < NKB; ++a)
+#pragma unroll
+      for (int b = 0; b < NVB; ++b) {
+        const int krow = (wave * NKB + a) * 16 + l16, col = b * 16 + 4 * lg;
+        if (krow < p.K && col < p.V) *reinterpret_cast<f32x4_t *>(dst + (int64_t)krow * p.V + col) = acc[a][b];
       }
+    __syncthreads();  // LDS is refilled for the next task
+  }
 }
 
-// ---------------------------------------------------------------- gla_bwd_dscan
-// Reverse walk of the state gradient over each sequence's chunks, per float4
-// of the K x V state: the carry starts at dht (or 0); chunk c's slot receives
-// the carry E_c, then carry = summary_c + a_c . carry.  The final carry is
-// dh0.  Loads of a batch of chunks are issued before its serial updates.
-__global__ __launch_bounds__(256) void gla_bwd_dscan(BwdParams bp, int per_state) {
+// ---------------------------------------------------------------- gla_bwd_scan
+// Both walks over each sequence's chunks, per float4 of the K x V state:
+//   forward: carry = h0 (or 0); slot c receives the carry S_c (the state
+//            before chunk c), then carry = a_c . carry + summary_c
+//   reverse: carry = dht (or 0); slot c receives the carry E_c (the gradient
+//            reaching the state after chunk c), then carry = dsummary_c + a_c . carry;
+//            the final carry is dh0.
+// The first half of the grid runs the forward walks, the second half the
+// reverse ones.  Loads of a batch of chunks are issued before its serial updates.
+__global__ __launch_bounds__(256) void gla_bwd_scan(BwdParams bp, int per_state) {
   const WalkParams &p = bp.w;
-  const long long pair = blockIdx.x / per_state;
-  const int eb = (int)(blockIdx.x - pair * per_state);
+  const long long pairs = (long long)p.N * p.HV;
+  long long blk = blockIdx.x;
+  const bool reverse = blk >= pairs * per_state;  // the second half of the grid walks the gradient
+  if (reverse) blk -= pairs * per_state;
+  const long long pair = blk / per_state;
+  const int eb = (int)(blk - pair * per_state);
   const int n = (int)(pair / p.HV), hv = (int)(pair - (long long)n * p.HV);
   const int e4 = eb * 256 + threadIdx.x;
   const int KV4 = p.K * p.V / 4;
@@ -237,31 +373,52 @@ __global__ __launch_bounds__(256) void gla_bwd_dscan(BwdParams bp, int per_state
   }
   const int nc = min((len + kChunk - 1) / kChunk, nseg);
   const int krow = (4 * e4) / p.V, col = 4 * e4 - krow * p.V;
-  f32x4_t e = zero4();
-  if (bp.dht) e = *reinterpret_cast<const f32x4_t *>(bp.dht + (((int64_t)n * p.HV + hv) * p.K + krow) * p.V + col);
-  constexpr int BATCH = 8;
+  const int64_t sidx = (((int64_t)n * p.HV + hv) * p.K + krow) * p.V + col;
+  constexpr int BATCH = 16;
+  auto cell = [&](float *base, int c) {
+    return reinterpret_cast<f32x4_t *>(base + ((int64_t)(first + c) * p.HV + hv) * p.K * p.V) + e4;
+  };
+  auto decay = [&](int c) { return bp.ddecay[((int64_t)(first + c) * p.HV + hv) * p.K + krow]; };
+  if (!reverse) {
+    f32x4_t s = p.h0 ? *reinterpret_cast<const f32x4_t *>(p.h0 + sidx) : zero4();
+    for (int c0 = 0; c0 < nc; c0 += BATCH) {
+      const int nb = min(BATCH, nc - c0);
+      f32x4_t d[BATCH];
+      float a[BATCH];
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b)
+        if (b < nb) {
+          d[b] = *cell(bp.fstate, c0 + b);
+          a[b] = decay(c0 + b);
+        }
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b)
+        if (b < nb) {
+          *cell(bp.fstate, c0 + b) = s;
+          s = a[b] * s + d[b];
+        }
+    }
+    return;
+  }
+  f32x4_t e = bp.dht ? *reinterpret_cast<const f32x4_t *>(bp.dht + sidx) : zero4();
   for (int c1 = nc; c1 > 0; c1 -= BATCH) {
     const int nb = min(BATCH, c1);
     f32x4_t d[BATCH];
     float a[BATCH];
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
+    for (int b = 0; b < BATCH; ++b)
       if (b < nb) {
-        const int64_t slot = (int64_t)(first + c1 - 1 - b) * p.HV + hv;
-        d[b] = reinterpret_cast<const f32x4_t *>(bp.dstate + slot * p.K * p.V)[e4];
-        a[b] = bp.ddecay[slot * p.K + krow];
+        d[b] = *cell(bp.dstate, c1 - 1 - b);
+        a[b] = decay(c1 - 1 - b);
       }
-    }
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
+    for (int b = 0; b < BATCH; ++b)
       if (b < nb) {
-        const int64_t slot = (int64_t)(first + c1 - 1 - b) * p.HV + hv;
-        reinterpret_cast<f32x4_t *>(bp.dstate + slot * p.K * p.V)[e4] = e;
+        *cell(bp.dstate, c1 - 1 - b) = e;
         e = d[b] + a[b] * e;
       }
-    }
   }
-  if (bp.dh0) *reinterpret_cast<f32x4_t *>(bp.dh0 + (((int64_t)n * p.HV + hv) * p.K + krow) * p.V + col) = e;
+  if (bp.dh0) *reinterpret_cast<f32x4_t *>(bp.dh0 + sidx) = e;
 }
 
 // ---------------------------------------------------------------- dq / dk stores
@@ -284,316 +441,358 @@ __device__ __forceinline__ void store_dqk(const BwdParams &bp, int64_t row, int 
 
 // ---------------------------------------------------------------- gla_bwd_chunk
 // The gradients of one chunk of one value head on fp32 MFMA
-// (v_mfma_f32_16x16x4f32).  4 waves; wave w owns key blocks [w NKB, w NKB +
-// NKB) and value blocks [w NVB, w NVB + NVB) of 16; score tiles are shared
-// through LDS.  A chunk with a key whose decay over the chunk is below e^-80
-// sets its flag and leaves its outputs to gla_bwd_chunk_exact.
+// (v_mfma_f32_16x16x4f32).  NW waves (8 for 128 keys: two per SIMD, so that
+// one wave's products run while the other waits for state tiles); wave w owns
+// key block w of 16 keys in every key-space product and the dg cumsum down its
+// columns.  Value blocks of 16 are dealt to waves; with fewer value blocks
+// than waves, a wave takes half of the row blocks of one value block.  Score
+// tiles are shared through LDS.  One workgroup per (chunk slot, value head);
+// its row loads are issued together, before the gate cumsum.  A chunk with a
+// key whose decay over the chunk is below e^-80 sets its flag and leaves its
+// outputs to gla_bwd_chunk_exact.
+template <int KD>
+constexpr int chunk_waves() { return KD == 128 ? 8 : 4; }
+
 template <bool BF, int KD, int VD, bool GH>
-__global__ __launch_bounds__(256, 1) void gla_bwd_chunk(BwdParams bp) {
+struct ChunkRows {
+  static constexpr int NT = 64 * chunk_waves<KD>();
+  static constexpr int TK = 64 * KD / 4 / NT, TV = 64 * VD / 4 / NT;  // row quads per thread
+  typename RawQuad<BF>::type q[TK], k[TK], v[TV], o[TV];
+  GateRows<KD, GH, NT> gate;
+};
+
+__device__ __forceinline__ bool chunk_task(const WalkParams &p, long long task, ChunkAt &ca, int &hv, int &slot) {
+  hv = (int)(task % p.HV);
+  slot = (int)(task / p.HV);
+  return chunk_at(p, slot, ca);
+}
+
+template <bool BF, int KD, int VD, bool GH>
+__device__ __forceinline__ void chunk_load(const BwdParams &bp, const ChunkAt &ca, int hv, ChunkRows<BF, KD, VD, GH> &rw) {
+  using R = ChunkRows<BF, KD, VD, GH>;
   const WalkParams &p = bp.w;
+  const int h = hv / p.G;
+#pragma unroll
+  for (int t = 0; t < R::TK; ++t) {
+    const int e = threadIdx.x + R::NT * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
+    rw.q[t] = rw.k[t] = {};
+    if (i < ca.L && c4 < p.K) {
+      const int64_t off = (ca.row0 + i) * p.H * p.K + h * p.K + c4;
+      rw.q[t] = ld_raw4<BF>(p.q, off);
+      rw.k[t] = ld_raw4<BF>(p.k, off);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < R::TV; ++t) {
+    const int e = threadIdx.x + R::NT * t, i = e / (VD / 4), c4 = (e % (VD / 4)) * 4;
+    rw.v[t] = rw.o[t] = {};
+    if (i < ca.L && c4 < p.V) {
+      const int64_t off = ((ca.row0 + i) * p.HV + hv) * p.V + c4;
+      rw.o[t] = ld_raw4<BF>(bp.dout, off);
+      rw.v[t] = ld_raw4<BF>(p.v, off);
+    }
+  }
+  gate_load<KD, GH, R::NT>(p, ca, hv, rw.gate);
+}
+
+template <bool BF, int KD, int VD, bool GH>
+__global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdParams bp) {
+  const WalkParams &p = bp.w;
+  using R = ChunkRows<BF, KD, VD, GH>;
+  constexpr int NW = chunk_waves<KD>(), NT = 64 * NW;
   constexpr int WV = KD > VD ? KD : VD;
-  constexpr int PARTS = 256 / KD, RP = 64 / PARTS;
-  constexpr int NKB = KD / 64, NVB = VD / 64;
+  constexpr int NVBLK = VD / 16;                      // value blocks
+  constexpr int JSPLIT = NW > NVBLK ? NW / NVBLK : 1; // waves sharing one value block
+  constexpr int NVB = NVBLK >= NW ? NVBLK / NW : 1;   // value blocks per wave
+  constexpr int NJB = 4 / JSPLIT;                     // row blocks per wave in value space
+  constexpr int NTILE = (10 + NW - 1) / NW;           // score tiles per wave (at most)
+  static_assert(KD / 16 == NW, "one key block per wave");
   __shared__ __attribute__((aligned(16))) float sQ[64 * KD];  // q e^G
   __shared__ __attribute__((aligned(16))) float sK[64 * KD];  // k e^-G
   __shared__ __attribute__((aligned(16))) float sO[64 * VD];  // do
-  __shared__ __attribute__((aligned(16))) float sV[64 * WV];  // v, then G as [64][KD]
+  __shared__ __attribute__((aligned(16))) float sV[64 * WV];  // G, then v
   __shared__ __attribute__((aligned(16))) float sX[64 * 64];  // A, then dA'
   __shared__ __attribute__((aligned(16))) float sEl[KD];      // e^{G_last}
   __shared__ float sGl[KD];                                   // G_last
-  __shared__ float tot[256];
+  __shared__ float tot[NT];
   __shared__ float sRow[64];                                  // per-row dg sums (per-head gate)
 
-  const int hv = (int)(blockIdx.x % (unsigned)p.HV);
-  const int slot = (int)(blockIdx.x / (unsigned)p.HV);
-  ChunkAt ca;
-  if (!chunk_at(p, slot, ca)) return;
-  const int h = hv / p.G;
-  const int L = ca.L;
-  const int64_t row0 = ca.row0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
-  const int kk = threadIdx.x % KD, part = threadIdx.x / KD;
-  bool low;
+  const int kb = wave * 16;                                        // this wave's key block
+  const int vb0 = (JSPLIT > 1 ? wave % NVBLK : wave * NVB) * 16;   // first value column of its blocks
+  const int jb0 = JSPLIT > 1 ? (wave / NVBLK) * NJB : 0;           // first row block (value space)
+  ChunkAt ca;
+  int hv = 0, slot = 0;
+  if (!chunk_task(p, blockIdx.x, ca, hv, slot)) return;
+  R rw;
+  chunk_load<BF, KD, VD, GH>(bp, ca, hv, rw);
   {
-    float G[RP];
-    chunk_cumsum<KD, GH>(p, row0, L, hv, G, tot);
-    low = part == PARTS - 1 && kk < p.K && !(G[RP - 1] >= kMinChunkLogDecay);
-#pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      const int i = part * RP + r;
-      const bool in = i < L && kk < p.K;
-      const int64_t off = (row0 + i) * p.H * p.K + h * p.K + kk;
-      const float qv = in ? ld_el<BF>(p.q, off) : 0.f;
-      const float kv = in ? ld_el<BF>(p.k, off) : 0.f;
-      sQ[swz<KD>(i, kk)] = qv * __expf(G[r]);
-      sK[swz<KD>(i, kk)] = kv * __expf(-G[r]);
-    }
-    if (part == PARTS - 1) {
-      sGl[kk] = G[RP - 1];
-      sEl[kk] = __expf(G[RP - 1]);
-    }
-  }
-  for (int e = threadIdx.x; e < 64 * VD / 4; e += 256) {
-    const int i = e / (VD / 4), c4 = (e % (VD / 4)) * 4;
-    f32x4_t xo = zero4(), xv = zero4();
-    if (i < L && c4 < p.V) {
-      const int64_t off = ((row0 + i) * p.HV + hv) * p.V + c4;
-      xo = ld_el4<BF>(bp.dout, off);
-      xv = ld_el4<BF>(p.v, off);
-    }
-    lds4_st<VD>(sO, i, c4, xo);
-    lds4_st<VD>(sV, i, c4, xv);
-  }
-  if (GH && threadIdx.x < 64) sRow[threadIdx.x] = 0.f;
-  const bool exact = __syncthreads_or(low);
-  if (threadIdx.x == 0) bp.flags[(int64_t)slot * p.HV + hv] = exact ? 1 : 0;
-  if (exact) return;
-
-  // ---- scores: A -> sX, dA' kept in registers until A has been used
-  f32x4_t dAr[3];
-#pragma unroll
-  for (int t = 0; t < 3; ++t) {
-    const int idx = wave + 4 * t;
-    dAr[t] = zero4();
-    if (idx >= 10) continue;
-    int ib, jb;
-    tri_tile(idx, ib, jb);
-    f32x4_t a = zero4(), d = zero4();
-#pragma unroll 4
-    for (int k0 = 0; k0 < KD; k0 += 16) {
-      const f32x4_t q4 = lds4<KD>(sQ, ib * 16 + l16, k0 + 4 * lg);
-      const f32x4_t k4 = lds4<KD>(sK, jb * 16 + l16, k0 + 4 * lg);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) a = mfma_f32(q4[r], k4[r], a);
-    }
-#pragma unroll 4
-    for (int v0 = 0; v0 < VD; v0 += 16) {
-      const f32x4_t o4 = lds4<VD>(sO, ib * 16 + l16, v0 + 4 * lg);
-      const f32x4_t w4 = lds4<VD>(sV, jb * 16 + l16, v0 + 4 * lg);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) d = mfma_f32(o4[r], w4[r], d);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool keep = ib > jb || l16 <= 4 * lg + r;  // column j <= row i
-      sX[swz<64>(ib * 16 + 4 * lg + r, jb * 16 + l16)] = keep ? p.scale * a[r] : 0.f;
-      dAr[t][r] = keep ? p.scale * d[r] : 0.f;
-    }
-  }
-  __syncthreads();
-
-  // ---- dv = A^T do (this wave's value blocks, all row blocks)
-  f32x4_t dv[NVB][4];
-#pragma unroll
-  for (int b = 0; b < NVB; ++b)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dv[b][j] = zero4();
-#pragma unroll
-  for (int ib = 0; ib < 4; ++ib) {
-    float ov[NVB][4];
-#pragma unroll
-    for (int b = 0; b < NVB; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ov[b][r] = sO[swz<VD>(ib * 16 + 4 * lg + r, (wave * NVB + b) * 16 + l16)];
-#pragma unroll
-    for (int jb = 0; jb <= ib; ++jb) {
-      float av[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) av[r] = sX[swz<64>(ib * 16 + 4 * lg + r, jb * 16 + l16)];
-#pragma unroll
-      for (int b = 0; b < NVB; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dv[b][jb] = mfma_f32(av[r], ov[b][r], dv[b][jb]);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < 3; ++t) {
-    const int idx = wave + 4 * t;
-    if (idx >= 10) continue;
-    int ib, jb;
-    tri_tile(idx, ib, jb);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sX[swz<64>(ib * 16 + 4 * lg + r, jb * 16 + l16)] = dAr[t][r];
-  }
-
-  // ---- inter-chunk terms: dq = do S_c^T, dkI = v E_c^T, rs = rowsum(S_c . E_c)
-  const float *Sc = nullptr;
-  if (ca.c > 0) Sc = bp.fstate + ((int64_t)(ca.si.first + ca.c - 1) * p.HV + hv) * p.K * p.V;
-  else if (p.h0) Sc = p.h0 + ((int64_t)ca.si.n * p.HV + hv) * p.K * p.V;
-  const float *Ec = bp.dstate + ((int64_t)(ca.si.first + ca.c) * p.HV + hv) * p.K * p.V;
-  f32x4_t dq[NKB][4], dkI[NKB][4];
-  float rs[NKB];
-#pragma unroll
-  for (int a = 0; a < NKB; ++a) {
-    rs[a] = 0.f;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) dq[a][b] = dkI[a][b] = zero4();
-  }
-#pragma unroll 2
-  for (int v0 = 0; v0 < VD; v0 += 16) {
-    f32x4_t s4[NKB], e4[NKB];
-#pragma unroll
-    for (int a = 0; a < NKB; ++a) {
-      const int krow = (wave * NKB + a) * 16 + l16, col = v0 + 4 * lg;
-      const bool in = krow < p.K && col < p.V;
-      const int64_t off = (int64_t)krow * p.V + col;
-      s4[a] = (in && Sc) ? *reinterpret_cast<const f32x4_t *>(Sc + off) : zero4();
-      e4[a] = in ? *reinterpret_cast<const f32x4_t *>(Ec + off) : zero4();
-      rs[a] += s4[a][0] * e4[a][0] + s4[a][1] * e4[a][1] + s4[a][2] * e4[a][2] + s4[a][3] * e4[a][3];
-    }
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
-      const f32x4_t o4 = lds4<VD>(sO, ib * 16 + l16, v0 + 4 * lg);
-      const f32x4_t w4 = lds4<VD>(sV, ib * 16 + l16, v0 + 4 * lg);
-#pragma unroll
-      for (int a = 0; a < NKB; ++a)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          dq[a][ib] = mfma_f32(o4[r], s4[a][r], dq[a][ib]);
-          dkI[a][ib] = mfma_f32(w4[r], e4[a][r], dkI[a][ib]);
-        }
-    }
-  }
-  __syncthreads();  // v consumed, dA' visible
-  {
-    float G[RP];  // the same cumsum again (cheaper than holding it in registers)
-    chunk_cumsum<KD, GH>(p, row0, L, hv, G, tot);
-#pragma unroll
-    for (int r = 0; r < RP; ++r) sV[swz<KD>(part * RP + r, kk)] = G[r];
-  }
-  __syncthreads();
-  const float *sG = sV;
-
-  // ---- dv += (k e^{G_last - G}) E_c, store dv
-#pragma unroll 2
-  for (int k0 = 0; k0 < KD; k0 += 16) {
-    const f32x4_t el4 = *reinterpret_cast<const f32x4_t *>(sEl + k0 + 4 * lg);
-    float ev[NVB][4];
-#pragma unroll
-    for (int b = 0; b < NVB; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int krow = k0 + 4 * lg + r, col = (wave * NVB + b) * 16 + l16;
-        ev[b][r] = (krow < p.K && col < p.V) ? Ec[(int64_t)krow * p.V + col] : 0.f;
-      }
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      const f32x4_t k4 = lds4<KD>(sK, jb * 16 + l16, k0 + 4 * lg) * el4;
-#pragma unroll
-      for (int b = 0; b < NVB; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dv[b][jb] = mfma_f32(k4[r], ev[b][r], dv[b][jb]);
-    }
-  }
-#pragma unroll
-  for (int b = 0; b < NVB; ++b)
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = jb * 16 + 4 * lg + r, col = (wave * NVB + b) * 16 + l16;
-        if (j < L && col < p.V) st_el<BF>(bp.dv, ((row0 + j) * p.HV + hv) * p.V + col, dv[b][jb][r]);
-      }
-
-  // ---- dq = scale (do S_c^T) + dA' (k e^-G)
-#pragma unroll
-  for (int a = 0; a < NKB; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) dq[a][b] *= p.scale;
-#pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-    float kv[NKB][4];
-#pragma unroll
-    for (int a = 0; a < NKB; ++a)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) kv[a][r] = sK[swz<KD>(jb * 16 + 4 * lg + r, (wave * NKB + a) * 16 + l16)];
-#pragma unroll
-    for (int ib = jb; ib < 4; ++ib) {
-      const f32x4_t a4 = lds4<64>(sX, ib * 16 + l16, jb * 16 + 4 * lg);
-#pragma unroll
-      for (int a = 0; a < NKB; ++a)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dq[a][ib] = mfma_f32(a4[r], kv[a][r], dq[a][ib]);
-    }
-  }
-  // ---- dkA = dA'^T (q e^G)
-  f32x4_t dkA[NKB][4];
-#pragma unroll
-  for (int a = 0; a < NKB; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) dkA[a][b] = zero4();
-#pragma unroll
-  for (int ib = 0; ib < 4; ++ib) {
-    float qv[NKB][4];
-#pragma unroll
-    for (int a = 0; a < NKB; ++a)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) qv[a][r] = sQ[swz<KD>(ib * 16 + 4 * lg + r, (wave * NKB + a) * 16 + l16)];
-#pragma unroll
-    for (int jb = 0; jb <= ib; ++jb) {
-      float av[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) av[r] = sX[swz<64>(ib * 16 + 4 * lg + r, jb * 16 + l16)];
-#pragma unroll
-      for (int a = 0; a < NKB; ++a)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dkA[a][jb] = mfma_f32(av[r], qv[a][r], dkA[a][jb]);
-    }
-  }
-
-  // ---- gradients in key space, and dg by a reverse cumsum down each key column
-#pragma unroll
-  for (int a = 0; a < NKB; ++a) {
-    const int k = (wave * NKB + a) * 16 + l16;
-    const float gl = sGl[k], el = sEl[k];
-    float t[4][4];
-    float colk = 0.f;
+    const int chv = hv, cslot = slot;
+    const int L = ca.L;
+    const int64_t row0 = ca.row0;
+    const int cfirst = ca.si.first, cc = ca.c;
+    // G -> sV; q e^G, k e^-G -> sQ, sK; this lane's G values; the chunk's decay per key
+    gate_stage<KD, GH, NT>(rw.gate, sV);
+    __syncthreads();
+    gate_cumsum_lds<KD, GH, NT>(p.K, sV, tot);
+    float Gr[4][4];  // G at rows b*16 + 4 lg + r of key kb + l16 (the epilogue's elements)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
+      for (int r = 0; r < 4; ++r) Gr[b][r] = sV[swz<KD>(b * 16 + 4 * lg + r, kb + l16)];
+    bool low = false;
+#pragma unroll
+    for (int t = 0; t < R::TK; ++t) {
+      const int e = threadIdx.x + NT * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
+      const f32x4_t G4 = lds4<KD>(sV, i, c4);
+      f32x4_t xq = unpack4<BF>(rw.q[t]), xk = unpack4<BF>(rw.k[t]);
+#pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = b * 16 + 4 * lg + r;
-        const float Gv = sG[swz<KD>(i, k)], qg = sQ[swz<KD>(i, k)], kg = sK[swz<KD>(i, k)];
-        const float kdkI = kg * el * dkI[a][b][r];
-        const float dqv = __expf(Gv) * dq[a][b][r];
-        const float dkv = __expf(-Gv) * dkA[a][b][r] + __expf(gl - Gv) * dkI[a][b][r];
-        if (i < L && k < p.K) store_dqk<BF>(bp, row0 + i, hv, k, dqv, dkv);
-        t[b][r] = qg * dq[a][b][r] - (kg * dkA[a][b][r] + kdkI);
-        colk += kdkI;
+        xq[r] *= __expf(G4[r]);
+        xk[r] *= __expf(-G4[r]);
       }
-    float rsa = rs[a];
-    rsa += __shfl_xor(rsa, 16);
-    rsa += __shfl_xor(rsa, 32);
-    colk += __shfl_xor(colk, 16);
-    colk += __shfl_xor(colk, 32);
-    float carry = el * rsa + colk;  // dg of the first token after the chunk
+      lds4_st<KD>(sQ, i, c4, xq);
+      lds4_st<KD>(sK, i, c4, xk);
+      if (i == 63) {
 #pragma unroll
-    for (int b = 3; b >= 0; --b) {
-      const float sb = t[b][0] + t[b][1] + t[b][2] + t[b][3];
-      float after = 0.f, total = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float sq = __shfl(sb, q * 16 + l16);
-        total += sq;
-        if (q > lg) after += sq;
-      }
-      float run = carry + after;
-#pragma unroll
-      for (int r = 3; r >= 0; --r) {
-        run += t[b][r];
-        const int i = b * 16 + 4 * lg + r;
-        if (i < L && k < p.K) {
-          if (GH) atomicAdd(&sRow[i], run);
-          else bp.dg[((row0 + i) * p.HV + hv) * p.K + k] = run;
+        for (int r = 0; r < 4; ++r) {
+          sGl[c4 + r] = G4[r];
+          sEl[c4 + r] = __expf(G4[r]);
+          if (c4 + r < p.K && !(G4[r] >= kMinChunkLogDecay)) low = true;
         }
       }
-      carry += total;
     }
-  }
-  if (GH) {
+    if (GH && threadIdx.x < 64) sRow[threadIdx.x] = 0.f;
+    const bool exact = __syncthreads_or(low);  // also: every thread is done reading G from sV
+    if (threadIdx.x == 0) bp.flags[(int64_t)cslot * p.HV + chv] = exact ? 1 : 0;
+    if (exact) return;
+#pragma unroll
+    for (int t = 0; t < R::TV; ++t) {
+      const int e = threadIdx.x + NT * t, i = e / (VD / 4), c4 = (e % (VD / 4)) * 4;
+      lds4_st<VD>(sO, i, c4, unpack4<BF>(rw.o[t]));
+      lds4_st<VD>(sV, i, c4, unpack4<BF>(rw.v[t]));
+    }
     __syncthreads();
-    if (threadIdx.x < L) bp.dg[(row0 + threadIdx.x) * p.HV + hv] = sRow[threadIdx.x];
+
+    // ---- scores: A -> sX, dA' kept in registers until A has been used
+    f32x4_t dAr[NTILE];
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      const int idx = wave + NW * t;
+      dAr[t] = zero4();
+      if (idx >= 10) continue;
+      int ib, jb;
+      tri_tile(idx, ib, jb);
+      f32x4_t a = zero4(), d = zero4();
+#pragma unroll 4
+      for (int k0 = 0; k0 < KD; k0 += 16) {
+        const f32x4_t q4 = lds4<KD>(sQ, ib * 16 + l16, k0 + 4 * lg);
+        const f32x4_t k4 = lds4<KD>(sK, jb * 16 + l16, k0 + 4 * lg);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a = mfma_f32(q4[r], k4[r], a);
+      }
+#pragma unroll 4
+      for (int v0 = 0; v0 < VD; v0 += 16) {
+        const f32x4_t o4 = lds4<VD>(sO, ib * 16 + l16, v0 + 4 * lg);
+        const f32x4_t w4 = lds4<VD>(sV, jb * 16 + l16, v0 + 4 * lg);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d = mfma_f32(o4[r], w4[r], d);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool keep = ib > jb || l16 <= 4 * lg + r;  // column j <= row i
+        sX[swz<64>(ib * 16 + 4 * lg + r, jb * 16 + l16)] = keep ? p.scale * a[r] : 0.f;
+        dAr[t][r] = keep ? p.scale * d[r] : 0.f;
+      }
+    }
+    __syncthreads();
+
+    // ---- dv = A^T do (this wave's value blocks and row blocks)
+    f32x4_t dv[NVB][NJB];
+#pragma unroll
+    for (int b = 0; b < NVB; ++b)
+#pragma unroll
+      for (int j = 0; j < NJB; ++j) dv[b][j] = zero4();
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      if (ib < jb0) continue;
+      float ov[NVB][4];
+#pragma unroll
+      for (int b = 0; b < NVB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ov[b][r] = sO[swz<VD>(ib * 16 + 4 * lg + r, vb0 + b * 16 + l16)];
+#pragma unroll
+      for (int j = 0; j < NJB; ++j) {
+        const int jb = jb0 + j;
+        if (jb > ib) continue;
+        float av[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) av[r] = sX[swz<64>(ib * 16 + 4 * lg + r, jb * 16 + l16)];
+#pragma unroll
+        for (int b = 0; b < NVB; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dv[b][j] = mfma_f32(av[r], ov[b][r], dv[b][j]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      const int idx = wave + NW * t;
+      if (idx >= 10) continue;
+      int ib, jb;
+      tri_tile(idx, ib, jb);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sX[swz<64>(ib * 16 + 4 * lg + r, jb * 16 + l16)] = dAr[t][r];
+    }
+
+    // ---- inter-chunk terms: dq = do S_c^T, dkI = v E_c^T, rs = rowsum(S_c . E_c)
+    const float *Sc = bp.fstate + ((int64_t)(cfirst + cc) * p.HV + chv) * p.K * p.V;
+    const float *Ec = bp.dstate + ((int64_t)(cfirst + cc) * p.HV + chv) * p.K * p.V;
+    f32x4_t dq[4], dkI[4];
+    float rs = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) dq[b] = dkI[b] = zero4();
+    {
+      const int krow = kb + l16;
+#pragma unroll 4
+      for (int v0 = 0; v0 < VD; v0 += 16) {
+        const int col = v0 + 4 * lg;
+        const bool in = krow < p.K && col < p.V;
+        const int64_t off = (int64_t)krow * p.V + col;
+        const f32x4_t s4 = in ? *reinterpret_cast<const f32x4_t *>(Sc + off) : zero4();
+        const f32x4_t e4 = in ? *reinterpret_cast<const f32x4_t *>(Ec + off) : zero4();
+        rs += s4[0] * e4[0] + s4[1] * e4[1] + s4[2] * e4[2] + s4[3] * e4[3];
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) {
+          const f32x4_t o4 = lds4<VD>(sO, ib * 16 + l16, v0 + 4 * lg);
+          const f32x4_t w4 = lds4<VD>(sV, ib * 16 + l16, v0 + 4 * lg);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            dq[ib] = mfma_f32(o4[r], s4[r], dq[ib]);
+            dkI[ib] = mfma_f32(w4[r], e4[r], dkI[ib]);
+          }
+        }
+      }
+    }
+    __syncthreads();  // dA' visible
+
+    // ---- dv += (k e^{G_last - G}) E_c, store dv
+#pragma unroll 2
+    for (int k0 = 0; k0 < KD; k0 += 16) {
+      const f32x4_t el4 = *reinterpret_cast<const f32x4_t *>(sEl + k0 + 4 * lg);
+      float ev[NVB][4];
+#pragma unroll
+      for (int b = 0; b < NVB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int krow = k0 + 4 * lg + r, col = vb0 + b * 16 + l16;
+          ev[b][r] = (krow < p.K && col < p.V) ? Ec[(int64_t)krow * p.V + col] : 0.f;
+        }
+#pragma unroll
+      for (int j = 0; j < NJB; ++j) {
+        const f32x4_t k4 = lds4<KD>(sK, (jb0 + j) * 16 + l16, k0 + 4 * lg) * el4;
+#pragma unroll
+        for (int b = 0; b < NVB; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dv[b][j] = mfma_f32(k4[r], ev[b][r], dv[b][j]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NVB; ++b)
+#pragma unroll
+      for (int j = 0; j < NJB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = (jb0 + j) * 16 + 4 * lg + r, col = vb0 + b * 16 + l16;
+          if (row < L && col < p.V) st_el<BF>(bp.dv, ((row0 + row) * p.HV + chv) * p.V + col, dv[b][j][r]);
+        }
+
+    // ---- dq = scale (do S_c^T) + dA' (k e^-G)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) dq[b] *= p.scale;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      float kv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) kv[r] = sK[swz<KD>(jb * 16 + 4 * lg + r, kb + l16)];
+#pragma unroll
+      for (int ib = jb; ib < 4; ++ib) {
+        const f32x4_t a4 = lds4<64>(sX, ib * 16 + l16, jb * 16 + 4 * lg);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dq[ib] = mfma_f32(a4[r], kv[r], dq[ib]);
+      }
+    }
+    // ---- dkA = dA'^T (q e^G)
+    f32x4_t dkA[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) dkA[b] = zero4();
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      float qv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qv[r] = sQ[swz<KD>(ib * 16 + 4 * lg + r, kb + l16)];
+#pragma unroll
+      for (int jb = 0; jb <= ib; ++jb) {
+        float av[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) av[r] = sX[swz<64>(ib * 16 + 4 * lg + r, jb * 16 + l16)];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dkA[jb] = mfma_f32(av[r], qv[r], dkA[jb]);
+      }
+    }
+
+    // ---- gradients in key space, and dg by a reverse cumsum down each key column
+    {
+      const int k = kb + l16;
+      const float gl = sGl[k], el = sEl[k];
+      float t[4][4];
+      float colk = 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = b * 16 + 4 * lg + r;
+          const float Gv = Gr[b][r], qg = sQ[swz<KD>(i, k)], kg = sK[swz<KD>(i, k)];
+          const float kdkI = kg * el * dkI[b][r];
+          const float dqv = __expf(Gv) * dq[b][r];
+          const float dkv = __expf(-Gv) * dkA[b][r] + __expf(gl - Gv) * dkI[b][r];
+          if (i < L && k < p.K) store_dqk<BF>(bp, row0 + i, chv, k, dqv, dkv);
+          t[b][r] = qg * dq[b][r] - (kg * dkA[b][r] + kdkI);
+          colk += kdkI;
+        }
+      float rsa = rs;
+      rsa += __shfl_xor(rsa, 16);
+      rsa += __shfl_xor(rsa, 32);
+      colk += __shfl_xor(colk, 16);
+      colk += __shfl_xor(colk, 32);
+      float carry = el * rsa + colk;  // dg of the first token after the chunk
+#pragma unroll
+      for (int b = 3; b >= 0; --b) {
+        const float sb = t[b][0] + t[b][1] + t[b][2] + t[b][3];
+        float after = 0.f, total = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float sq = __shfl(sb, q * 16 + l16);
+          total += sq;
+          if (q > lg) after += sq;
+        }
+        float run = carry + after;
+#pragma unroll
+        for (int r = 3; r >= 0; --r) {
+          run += t[b][r];
+          const int i = b * 16 + 4 * lg + r;
+          if (i < L && k < p.K) {
+            if (GH) atomicAdd(&sRow[i], run);
+            else bp.dg[((row0 + i) * p.HV + chv) * p.K + k] = run;
+          }
+        }
+        carry += total;
+      }
+    }
+    if (GH) {
+      __syncthreads();
+      if (threadIdx.x < L) bp.dg[(row0 + threadIdx.x) * p.HV + chv] = sRow[threadIdx.x];
+    }
   }
 }
 
@@ -650,9 +849,7 @@ __global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
   if (GH && threadIdx.x < 64) sRow[threadIdx.x] = 0.f;
   __syncthreads();
 
-  const float *Sc = nullptr;
-  if (ca.c > 0) Sc = bp.fstate + ((int64_t)(ca.si.first + ca.c - 1) * p.HV + hv) * p.K * p.V;
-  else if (p.h0) Sc = p.h0 + ((int64_t)ca.si.n * p.HV + hv) * p.K * p.V;
+  const float *Sc = bp.fstate + ((int64_t)(ca.si.first + ca.c) * p.HV + hv) * p.K * p.V;
   const float *Ec = bp.dstate + ((int64_t)(ca.si.first + ca.c) * p.HV + hv) * p.K * p.V;
   auto dout = [&](int i, int j) -> float {  // do at token i, column col0 + j
     const int col = col0 + j;
@@ -667,7 +864,7 @@ __global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     const int col = col0 + j;
-    S[j] = (Sc && kin && col < p.V) ? Sc[(int64_t)key * p.V + col] : 0.f;
+    S[j] = (kin && col < p.V) ? Sc[(int64_t)key * p.V + col] : 0.f;
   }
   // forward over the chunk: dq
   for (int i = 0; i < L; ++i) {
@@ -711,7 +908,7 @@ __global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
       w *= sA[j * KD + key];
     }
     float dots = 0.f;
-    if (Sc && kin) {
+    if (kin) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
         if (col0 + c < p.V) dots += U[c] * Sc[(int64_t)key * p.V + col0 + c];
@@ -778,8 +975,10 @@ template <bool BF, int KD, int VD, bool GH>
 hipError_t launch_bwd_t(int which, const BwdParams &bp, long long blocks, hipStream_t s) {
   const dim3 grid((unsigned)blocks), block(256);
   switch (which) {
-    case 0: hipLaunchKernelGGL((gla_bwd_dlocal<BF, KD, VD, GH>), grid, block, 0, s, bp); break;
-    case 1: hipLaunchKernelGGL((gla_bwd_chunk<BF, KD, VD, GH>), grid, block, 0, s, bp); break;
+    case 0: hipLaunchKernelGGL((gla_bwd_local<BF, KD, VD, GH>), grid, block, 0, s, bp); break;
+    case 1:
+      hipLaunchKernelGGL((gla_bwd_chunk<BF, KD, VD, GH>), grid, dim3(64 * chunk_waves<KD>()), 0, s, bp);
+      break;
     default: hipLaunchKernelGGL((gla_bwd_chunk_exact<BF, KD, VD, GH>), grid, block, 0, s, bp); break;
   }
   return hipGetLastError();
@@ -795,7 +994,8 @@ hipError_t launch_bwd_kv(int which, const BwdParams &bp, long long blocks, hipSt
 
 // Per-chunk kernels: one workgroup per (chunk slot, value head).
 hipError_t launch_bwd_kernel(int which, bool bf16, const BwdParams &bp, hipStream_t s) {
-  const long long blocks = (long long)bp.w.seg_slots * bp.w.HV;
+  long long blocks = (long long)bp.w.seg_slots * bp.w.HV;
+  if (which == 0) blocks = std::min<long long>(bp.persistent_blocks, 2 * blocks);  // two per compute unit
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL || bp.w.K > 128 || bp.w.V > 128) return hipErrorInvalidValue;
   const bool gh = bp.w.gate_head != 0;
@@ -805,7 +1005,7 @@ hipError_t launch_bwd_kernel(int which, bool bf16, const BwdParams &bp, hipStrea
 
 }  // namespace
 
-hipError_t launch_bwd_dlocal(bool bf16, const BwdParams &bp, hipStream_t s) { return launch_bwd_kernel(0, bf16, bp, s); }
+hipError_t launch_bwd_local(bool bf16, const BwdParams &bp, hipStream_t s) { return launch_bwd_kernel(0, bf16, bp, s); }
 
 hipError_t launch_bwd_chunk(bool bf16, const BwdParams &bp, hipStream_t s) {
   hipError_t e = launch_bwd_kernel(1, bf16, bp, s);
@@ -822,13 +1022,13 @@ hipError_t launch_bwd_chunk(bool bf16, const BwdParams &bp, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dscan(const BwdParams &bp, hipStream_t s) {
+hipError_t launch_bwd_scan(const BwdParams &bp, hipStream_t s) {
   const int KV4 = bp.w.K * bp.w.V / 4;
   const int per_state = (KV4 + 255) / 256;
-  const long long blocks = (long long)bp.w.N * bp.w.HV * per_state;
+  const long long blocks = 2LL * bp.w.N * bp.w.HV * per_state;  // forward walks, then reverse walks
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gla_bwd_dscan, dim3((unsigned)blocks), dim3(256), 0, s, bp, per_state);
+  hipLaunchKernelGGL(gla_bwd_scan, dim3((unsigned)blocks), dim3(256), 0, s, bp, per_state);
   return hipGetLastError();
 }
 

@@ -10,10 +10,9 @@
 //
 // Backward (page "fla/ops/gla/fused_chunk.py", FusedChunkGLAFunction.backward):
 //   [packed input]                       gla_segment_plan (one chunk per segment)
-//   [some sequence has 2+ chunks]        gla_chunk_local -> gla_state_scan: the state
-//                                        after every chunk
-//   [tokens]                             gla_bwd_dlocal: chunk summaries of the state gradient
-//   [tokens, or dh0 wanted]              gla_bwd_dscan: E_c per chunk, dh0
+//   [tokens]                             gla_bwd_local: chunk summaries of the state
+//                                        and of its gradient
+//   [tokens, or dh0 wanted]              gla_bwd_scan: S_c and E_c per chunk, dh0
 //   [tokens]                             gla_bwd_chunk, gla_bwd_chunk_exact
 //                                        (+ gla_bwd_group_sum with HV > H)
 #include <hip/hip_runtime.h>
@@ -256,12 +255,11 @@ gla_status run_forward(const gla_problem *p, const Plan &pl, const void *q, cons
   return GLA_OK;
 }
 
-// Backward: the forward plan with one chunk per segment (so that the forward
-// kernels leave the state after every chunk), followed by the backward's own
-// tables.  K and V of at most 128.
+// Backward: one chunk per slot (the forward's segment numbering with R = 1),
+// and the backward's tables.  K and V of at most 128.
 struct BwdPlan {
-  Plan fwd;
-  size_t off_base, off_dstate, off_ddecay, off_flags, off_dq_part, off_dk_part, total;
+  Plan fwd;  // slot numbering only (R = 1)
+  size_t off_base, off_fstate, off_dstate, off_ddecay, off_flags, off_dq_part, off_dk_part, total;
   bool ok;
 };
 
@@ -275,9 +273,11 @@ BwdPlan make_bwd_plan(const gla_problem *p, bool varlen) {
   const long long G = HV / p->H;
   const long long slots = pl.seg_slots;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  size_t cur = kHeaderBytes + up(pl.ws_state) + up(pl.ws_decay);
+  size_t cur = kHeaderBytes;
   b.off_base = cur;
   cur += up(varlen ? (size_t)(pl.N + 1 + slots) * sizeof(int32_t) : 0);
+  b.off_fstate = cur;
+  cur += up((size_t)slots * HV * p->K * p->V * sizeof(float));
   b.off_dstate = cur;
   cur += up((size_t)slots * HV * p->K * p->V * sizeof(float));
   b.off_ddecay = cur;
@@ -290,9 +290,9 @@ BwdPlan make_bwd_plan(const gla_problem *p, bool varlen) {
   b.off_dk_part = cur;
   cur += part;
   b.total = cur;
-  const long long scan_blocks = (long long)pl.N * HV * ((p->K * p->V / 4 + 255) / 256);
+  const long long scan_blocks = 2LL * pl.N * HV * ((p->K * p->V / 4 + 255) / 256);
   const long long rows_quads = (long long)p->B * p->T * p->H * (p->K / 4);
-  b.ok = pl.ok && slots * HV <= INT_MAX && scan_blocks <= INT_MAX && (rows_quads + 255) / 256 <= INT_MAX;
+  b.ok = pl.ok && 2 * slots * HV <= INT_MAX && scan_blocks <= INT_MAX && (rows_quads + 255) / 256 <= INT_MAX;
   return b;
 }
 
@@ -313,43 +313,28 @@ gla_status run_backward(const gla_problem *p, const BwdPlan &bpl, const void *q,
   const bool tokens = (long long)p->B * p->T > 0;
   if (!tokens && dh0 == nullptr) return GLA_OK;
   const Plan &pl = bpl.fwd;
-  const bool fast = uses_bf16_walker(p);
   const bool bf = p->dtype == GLA_BF16;
-  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   gla::WalkParams w{};
   w.q = q; w.k = k; w.v = v; w.g = g; w.h0 = h0; w.cu = cu_seqlens;
   w.status = status;
-  w.seg_state = pl.segmented ? reinterpret_cast<float *>(ws + kHeaderBytes) : nullptr;
-  w.seg_decay = pl.segmented ? reinterpret_cast<float *>(ws + kHeaderBytes + up(pl.ws_state)) : nullptr;
   int32_t *seg_base = varlen ? reinterpret_cast<int32_t *>(ws + bpl.off_base) : nullptr;
   w.seg_base = seg_base;
-  w.seg_order = seg_base ? seg_base + N + 1 : nullptr;
   w.T = p->T; w.H = p->H; w.K = p->K; w.V = p->V; w.N = N;
   w.HV = p->HV == 0 ? p->H : p->HV;
   w.G = w.HV / p->H;
   w.gate_head = p->gate == GLA_GATE_PER_HEAD ? 1 : 0;
   w.Kmem = p->K;
-  w.koff = 0;
   w.R = pl.R;
   w.P = pl.P;
-  w.units = (int)pl.units;
   w.seg_slots = pl.seg_slots;
-  w.vtile = pl.vtile;
-  w.wait_polls = p->wait_limit == 0 ? gla::kDefaultWaitPolls : (p->wait_limit < 0 ? 0 : p->wait_limit);
   w.scale = p->scale;
-
   if (seg_base && gla::launch_segment_plan(w, seg_base, seg_base + N + 1, s) != hipSuccess) return GLA_ERR_HIP;
-  if (tokens && pl.segmented) {
-    const int kd = kernel_key_width(fast, bf, w.K);
-    const hipError_t e = fast ? gla::launch_walk_bf16(true, kd, w, s) : gla::launch_walk_general(true, bf, kd, w, s);
-    if (e != hipSuccess || gla::launch_state_scan(w, s) != hipSuccess) return GLA_ERR_HIP;
-  }
   gla::BwdParams b{};
-  b.w = w;
-  b.w.seg_order = nullptr;
+  b.w = w;  // seg_order stays null: the backward's kernels take slots in plain order
+  b.persistent_blocks = 2 * device_cu_count();
   b.dout = dout; b.dht = dht;
   b.dq = dq; b.dk = dk; b.dv = dv; b.dg = dg; b.dh0 = dh0;
-  b.fstate = w.seg_state;
+  b.fstate = reinterpret_cast<float *>(ws + bpl.off_fstate);
   b.dstate = reinterpret_cast<float *>(ws + bpl.off_dstate);
   b.ddecay = reinterpret_cast<float *>(ws + bpl.off_ddecay);
   b.flags = reinterpret_cast<int32_t *>(ws + bpl.off_flags);
@@ -357,8 +342,8 @@ gla_status run_backward(const gla_problem *p, const BwdPlan &bpl, const void *q,
     b.dq_part = reinterpret_cast<float *>(ws + bpl.off_dq_part);
     b.dk_part = reinterpret_cast<float *>(ws + bpl.off_dk_part);
   }
-  if (tokens && gla::launch_bwd_dlocal(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
-  if (gla::launch_bwd_dscan(b, s) != hipSuccess) return GLA_ERR_HIP;
+  if (tokens && gla::launch_bwd_local(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
+  if (gla::launch_bwd_scan(b, s) != hipSuccess) return GLA_ERR_HIP;
   if (tokens && gla::launch_bwd_chunk(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
 }

@@ -70,8 +70,8 @@ hipError_t launch_walk_bf16(bool local_mode, int kd, const WalkParams &p, hipStr
 
 // Backward (gla_bwd.hip).  The state tables hold one chunk per slot: chunk c
 // of sequence n is slot first(n) + c, with first(n) = n P (fixed length) or
-// seg_base[n] (packed), exactly as the forward kernels number segments of one
-// chunk.  K and V are at most 128 (one key block).
+// seg_base[n] (packed), as the forward kernels number segments of one chunk
+// (gla_segment_plan with R = 1 fills seg_base).  K and V are at most 128.
 struct BwdParams {
   WalkParams w;          // problem sizes, q, k, v, g, h0, cu, seg_base (seg_order null), scale
   const void *dout;      // [B,T,HV,V] dtype: gradient of o
@@ -80,14 +80,15 @@ struct BwdParams {
   void *dv;              // [B,T,HV,V] dtype
   float *dg;             // [B,T,HV,K], or [B,T,HV] with a per-head gate
   float *dh0;            // [N,HV,K,V] or null
-  const float *fstate;   // [slots][HV][K][V]: slot first + c holds the state after chunk c (c < chunks - 1)
+  float *fstate;         // [slots][HV][K][V]: chunk summaries of the state, then S_c (state before chunk c)
   float *dstate;         // [slots][HV][K][V]: chunk summaries of the state gradient, then E_c
   float *ddecay;         // [slots][HV][K]: e^{G_last} of each chunk
   int32_t *flags;        // [slots][HV]: 1 when the chunk is left to the token-by-token kernel
   float *dq_part, *dk_part;  // [B,T,HV,K] fp32 shares of dq, dk per value head (G > 1), else null
+  int32_t persistent_blocks; // workgroups of the persistent kernels (a few per compute unit)
 };
-hipError_t launch_bwd_dlocal(bool bf16, const BwdParams &bp, hipStream_t s);
-hipError_t launch_bwd_dscan(const BwdParams &bp, hipStream_t s);
+hipError_t launch_bwd_local(bool bf16, const BwdParams &bp, hipStream_t s);
+hipError_t launch_bwd_scan(const BwdParams &bp, hipStream_t s);
 // the fast chunk kernel, the token-by-token kernel for flagged chunks, and
 // (G > 1) the sum of dq, dk over each key head's value heads
 hipError_t launch_bwd_chunk(bool bf16, const BwdParams &bp, hipStream_t s);

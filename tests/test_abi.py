@@ -218,20 +218,25 @@ def test_backward_accepts_widths_up_to_128(lib, dtype, K, V):
 
 
 def test_backward_workspace_size_and_check(lib):
-    # B=2, T=1000: 16 chunks per sequence, one chunk per slot; the forward
-    # states after every chunk, the state gradients and chunk decays, the flags
+    # B=2, T=1000: 16 chunks per sequence, one chunk per slot; the state and
+    # the state gradient of every chunk, the chunk decays, the flags
     B, T, H, K, V = 2, 1000, 3, 64, 128
     p = prob(B=B, T=T, H=H, K=K, V=V)
     slots = 2 * 16
     states = up(slots * H * K * V * 4)
     decays = up(slots * H * K * 4)
-    expect = WS_HEADER + states + decays + states + decays + up(slots * H * 4)
+    expect = WS_HEADER + states + states + decays + up(slots * H * 4)
     assert lib.gla_bwd_workspace_bytes(ctypes.byref(p)) == expect
     assert call_bwd(lib, p, ws=None, ws_bytes=0) == WORKSPACE
     assert call_bwd(lib, p, ws_bytes=expect - 1) == WORKSPACE
     # value-head groups add the fp32 shares of dq and dk per value head
     pg = prob(B=B, T=T, H=H, K=K, V=V, HV=6)
     states6, decays6 = up(slots * 6 * K * V * 4), up(slots * 6 * K * 4)
-    expect_g = (WS_HEADER + states6 + decays6 + states6 + decays6 + up(slots * 6 * 4)
-                + 2 * up(B * T * 6 * K * 4))
+    expect_g = WS_HEADER + 2 * states6 + decays6 + up(slots * 6 * 4) + 2 * up(B * T * 6 * K * 4)
     assert lib.gla_bwd_workspace_bytes(ctypes.byref(pg)) == expect_g
+    # packed: the slot table (N + 1 offsets and the order) comes first
+    pv = prob(B=1, T=1000, n_seqs=5, packed=1, H=H, K=K, V=V)
+    slots_v = 5 + 16 + 5
+    sv, dv_ = up(slots_v * H * K * V * 4), up(slots_v * H * K * 4)
+    assert lib.gla_bwd_workspace_bytes(ctypes.byref(pv)) == (WS_HEADER + up((6 + slots_v) * 4) + 2 * sv + dv_
+                                                             + up(slots_v * H * 4))
