@@ -6,6 +6,11 @@ logsigmoid(N(0,1))/16, chunk 64, final state stored -- the largest of the five
 measured configurations (synthetic seeded inputs, recipe in gla_inputs.py).
 ``--workload`` selects another one (small, c2048, c4096, varlen).
 
+``--pass bwd`` measures the backward instead (gla_bwd: dq, dk, dv, dg and, with
+an initial state, dh0, for seeded gradients do of o and dht of ht), with the
+same line format, the backward's own algorithmic bytes and flops, and the fp64
+backward oracle as the CPU baseline.
+
 A step is one full forward (every kernel of the path: segment plan, segment
 summaries, state scan, output walk, as the library schedules them) over the
 whole batch, with inputs resident in device memory.  Untimed steps for
@@ -40,11 +45,12 @@ if ROOT not in sys.path:
 import gla_inputs as gi  # noqa: E402
 
 METRIC = "GLA chunked fwd tokens/s + TFLOP/s, fraction of MFMA/HBM roofline (1 GPU)"
+METRIC_BWD = "GLA chunked bwd tokens/s + TFLOP/s, fraction of MFMA/HBM roofline (1 GPU)"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
 KERNEL_SRCS = [os.path.join(ROOT, "chunkwise_gated_linear_amd", "csrc", f)
-               for f in ("gla_kernels.hip", "gla_walk_bf16.hip", "gla_device.h", "gla_internal.h",
-                         "gla_host.hip")]
+               for f in ("gla_kernels.hip", "gla_walk_bf16.hip", "gla_bwd.hip", "gla_device.h",
+                         "gla_internal.h", "gla_host.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CALIB_BYTES = 512 << 20
 
@@ -82,6 +88,24 @@ def algorithmic(w, n_tokens, n_seqs):
     return nbytes, flops
 
 
+def algorithmic_bwd(w, n_tokens, n_seqs):
+    """Bytes (q, k, v, g, do, h0, dht read once; dq, dk, dv, dg, dh0 written once)
+    and flops of the backward.
+
+    Flops per token-head: 10KV (the two chunk summaries k~^T v and (q e^G)^T do,
+    do S^T, v E^T and k~ E) plus (C+1)(3K+2V) (the causal halves of the in-chunk
+    scores A and dA', of A^T do, dA' k and dA'^T q)."""
+    e = 2 if w.dtype == "bf16" else 4
+    H, K, V = w.H, w.K, w.V
+    th = n_tokens * H
+    state = 4 * n_seqs * H * K * V
+    nbytes = (th * (2 * K * e + 2 * V * e + 4 * K)           # q, k, v, do, g
+              + th * (2 * K * e + V * e + 4 * K)             # dq, dk, dv, dg
+              + state * (2 * int(w.h0) + int(w.ht)))         # h0 and dh0, dht
+    flops = th * (10 * K * V + (w.chunk + 1) * (3 * K + 2 * V))
+    return nbytes, flops
+
+
 def describe(w, lengths):
     if w.varlen:
         return (f"varlen {w.n_seqs} seqs lengths U[{w.len_lo},{w.len_hi}] total {sum(lengths)}, "
@@ -91,6 +115,7 @@ def describe(w, lengths):
 
 
 def load_traffic(workload: str):
+    """HBM bytes per launch recorded for `workload` (forward) or "bwd:<workload>"."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -208,6 +233,50 @@ def cpu_baseline(d, w, n_tokens, target_s=10.0):
                       f"scaled to {H} heads"}
 
 
+def cpu_baseline_bwd(d, w, n_tokens, do, dht, target_s=10.0, max_seq_tokens=4096):
+    """The fp64 backward oracle on whole sequences (at most max_seq_tokens of
+    each: the oracle keeps every state of a sequence) of the first heads, grown
+    until about target_s seconds; reported as tokens/s of the full head count."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    threads = len(os.sched_getaffinity(0))
+    H = w.H
+    cu = d["cu_seqlens"]
+    T = d["q"].shape[1]
+    tcut = T if cu is not None else min(T, max_seq_tokens)
+    if cu is not None and int(np.max(np.diff(cu))) > max_seq_tokens:
+        raise ValueError("backward CPU baseline: packed sequences longer than the sample bound")
+
+    def run(nh, reps=1):
+        sl = lambda a: np.ascontiguousarray(a[:, :tcut, :nh])
+        h0 = None if d["h0"] is None else np.ascontiguousarray(d["h0"][:, :nh])
+        dh = None if dht is None else np.ascontiguousarray(dht[:, :nh])
+        args = (sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]), sl(do))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.gla_reference_bwd(*args, h0=h0, dht=dh, cu_seqlens=cu, threads=threads)
+        return (time.perf_counter() - t0) / reps
+
+    n_seqs = w.n_seqs if w.varlen else w.B
+    nh = min(H, max(1, -(-threads // n_seqs)))
+    dt = run(nh)
+    while dt < target_s / 2 and nh < H:
+        nh = min(H, 2 * nh)
+        dt = run(nh)
+    reps = 1
+    while dt * reps < 0.8 * target_s:
+        reps = max(2 * reps, int(target_s / max(dt, 1e-5)))
+        dt = run(nh, reps)
+    used = min(threads, n_seqs * nh)
+    sample_tokens = n_tokens if cu is not None else n_seqs * tcut
+    return {"value": sample_tokens * (nh / H) / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{nh} of {H} heads, {sample_tokens} tokens ({n_seqs} sequences"
+                      f"{'' if tcut == T else f', first {tcut} tokens of each'}), fp64 reverse token "
+                      f"recurrence, {dt * reps:.2f} s for {reps} run(s) on {cpu_model()}; tokens/s "
+                      f"scaled to {H} heads"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,7 +285,10 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="before the W warmup steps, run untimed steps for this long so the GPU "
                          "reaches its sustained clock (short runs otherwise measure the ramp)")
-    ap.add_argument("--workload", default="long", choices=sorted(gi.WORKLOADS))
+    ap.add_argument("--workload", default=None, choices=sorted(gi.WORKLOADS),
+                    help="default: long for the forward, c2048 for the backward")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
+                    help="fwd (default): the forward; bwd: the backward (gla_bwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--single", type=int, default=11,
                     help="launches timed one by one after the timed steps, warm and with L2/MALL evicted")
@@ -231,10 +303,13 @@ def main():
                     help="(no GPU) FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR [READ_FETCH_DIR]: "
                          "store the HBM bytes per forward of --workload from rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.workload is None:
+        args.workload = "long" if args.which == "fwd" else "c2048"
+    traffic_key = args.workload if args.which == "fwd" else "bwd:" + args.workload
     if args.record_traffic:
         if len(args.record_traffic) not in (4, 5):
             ap.error("--record-traffic takes 4 or 5 directories")
-        record_traffic(args.workload, *args.record_traffic)
+        record_traffic(traffic_key, *args.record_traffic)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -278,8 +353,22 @@ def main():
     cu = None if d["cu_seqlens"] is None else torch.from_numpy(d["cu_seqlens"]).to(dev)
     n_tokens = int(q.shape[0] * q.shape[1])
     n_seqs = w.n_seqs if w.varlen else w.B
-    call = gla.GlaCall(q, k, v, g, h0=h0, cu_seqlens=cu, output_final_state=w.ht,
-                       segment_chunks=args.segment_chunks)
+    do = dht = None
+    if args.which == "fwd":
+        call = gla.GlaCall(q, k, v, g, h0=h0, cu_seqlens=cu, output_final_state=w.ht,
+                           segment_chunks=args.segment_chunks)
+    else:
+        # seeded gradients of the outputs: do like v (rounded to its dtype), dht
+        # for a stored final state
+        import numpy as np
+        rng = np.random.default_rng(w.seed + 1)
+        do = rng.standard_normal(d["v"].shape).astype(np.float32)
+        dht = (rng.standard_normal(d["h0"].shape if d["h0"] is not None else (n_seqs, w.H, w.K, w.V))
+               .astype(np.float32) if w.ht else None)
+        tdo = torch.from_numpy(do).to(tdt).to(dev)
+        do = tdo.float().cpu().numpy()
+        tdht = None if dht is None else torch.from_numpy(dht).to(dev)
+        call = gla.GlaBwdCall(q, k, v, g, tdo, h0=h0, dht=tdht, cu_seqlens=cu)
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
 
@@ -348,13 +437,13 @@ def main():
         copy_gbs = 2 * src.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
         del src, dst
 
-    nbytes, flops = algorithmic(w, n_tokens, n_seqs)
+    nbytes, flops = (algorithmic if args.which == "fwd" else algorithmic_bwd)(w, n_tokens, n_seqs)
     tokens_per_s = n_tokens / (ms_per_step * 1e-3)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     mfma_peak = MFMA_PEAK_TFLOPS[w.dtype]
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = flops / (mfma_peak * 1e12)
-    traffic = load_traffic(args.workload)
+    traffic = load_traffic(traffic_key)
     if t_hbm >= t_mfma:
         bound, achieved, peak, unit = "hbm", nbytes / (launch_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
     else:
@@ -362,11 +451,12 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(d, w, n_tokens)
+        cpu = (cpu_baseline(d, w, n_tokens) if args.which == "fwd"
+               else cpu_baseline_bwd(d, w, n_tokens, do, dht))
 
     ws_bytes = call.ws_bytes
     line = {
-        "metric": METRIC,
+        "metric": METRIC if args.which == "fwd" else METRIC_BWD,
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -384,7 +474,8 @@ def main():
         "roofline_time_us": max(t_hbm, t_mfma) * 1e6,
         "roofline": {
             "bound": bound,
-            "kernel": "gla_fwd (every kernel of one forward)",
+            "kernel": ("gla_fwd (every kernel of one forward)" if args.which == "fwd"
+                       else "gla_bwd (every kernel of one backward)"),
             "achieved": achieved,
             "peak": peak,
             "unit": unit,

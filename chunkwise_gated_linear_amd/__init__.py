@@ -30,7 +30,7 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
-__all__ = ["gla_fwd", "gla_bwd", "gla_fwd_noalloc", "bwd_workspace_bytes", "GlaCall", "workspace_bytes", "library_path", "load_library", "GlaError",
+__all__ = ["gla_fwd", "gla_bwd", "gla_fwd_noalloc", "bwd_workspace_bytes", "GlaCall", "GlaBwdCall", "workspace_bytes", "library_path", "load_library", "GlaError",
            "STATUS", "Problem", "STATUS_WAIT_EXHAUSTED", "read_status"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -341,6 +341,41 @@ class GlaCall:
         if rc != 0:
             raise GlaError(rc, _status_msg(self.lib, rc))
         return self.o, self.ht
+
+    def status(self) -> int:
+        """Sticky status word of this call's workspace (GLA_STATUS_* bits); synchronises."""
+        return read_status(self.workspace)
+
+
+class GlaBwdCall:
+    """A prepared backward: validates once, allocates dq, dk, dv, dg, dh0 and the
+    workspace once, then enqueues the same gla_bwd call on every ``__call__``."""
+
+    def __init__(self, q, k, v, g, do, h0=None, dht=None, cu_seqlens=None, scale=None, chunk: int = CHUNK,
+                 need_dh0: Optional[bool] = None):
+        import torch
+
+        self.lib = load_library()
+        self.problem, N, self.device = _problem_for(q, k, v, g, h0, cu_seqlens, None, scale, chunk, 0, 0, 0)
+        self.ws_bytes = bwd_workspace_bytes(self.problem)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.workspace[:256].zero_()
+        dq, dk, dv, dg, dh0 = gla_bwd(q, k, v, g, do, h0=h0, dht=dht, cu_seqlens=cu_seqlens, scale=scale,
+                                      chunk=chunk, need_dh0=need_dh0, workspace=self.workspace)
+        self.out = (dq, dk, dv, dg, dh0)
+        self._args = (q, k, v, g, h0, cu_seqlens, do, dht)
+
+    def __call__(self, stream=None):
+        import torch
+        q, k, v, g, h0, cu, do, dht = self._args
+        dq, dk, dv, dg, dh0 = self.out
+        s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
+        rc = self.lib.gla_bwd(ctypes.byref(self.problem), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0), _ptr(cu),
+                              _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dh0),
+                              self.workspace.data_ptr(), self.ws_bytes, s)
+        if rc != 0:
+            raise GlaError(rc, _status_msg(self.lib, rc))
+        return self.out
 
     def status(self) -> int:
         """Sticky status word of this call's workspace (GLA_STATUS_* bits); synchronises."""
