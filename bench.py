@@ -48,9 +48,14 @@ METRIC = "GLA chunked fwd tokens/s + TFLOP/s, fraction of MFMA/HBM roofline (1 G
 METRIC_BWD = "GLA chunked bwd tokens/s + TFLOP/s, fraction of MFMA/HBM roofline (1 GPU)"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
-KERNEL_SRCS = [os.path.join(ROOT, "chunkwise_gated_linear_amd", "csrc", f)
-               for f in ("gla_kernels.hip", "gla_walk_bf16.hip", "gla_bwd.hip", "gla_device.h",
-                         "gla_internal.h", "gla_host.hip")]
+_CSRC = os.path.join(ROOT, "chunkwise_gated_linear_amd", "csrc")
+# the sources each pass's kernels and launches are built from
+KERNEL_SRCS = {
+    "fwd": [os.path.join(_CSRC, f) for f in ("gla_kernels.hip", "gla_walk_bf16.hip", "gla_device.h",
+                                            "gla_internal.h", "gla_host.hip")],
+    "bwd": [os.path.join(_CSRC, f) for f in ("gla_bwd.hip", "gla_kernels.hip", "gla_device.h",
+                                            "gla_internal.h", "gla_host.hip")],
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CALIB_BYTES = 512 << 20
 
@@ -66,10 +71,10 @@ def cpu_model() -> str:
     return "unknown CPU"
 
 
-def kernel_source_hash() -> str:
-    """Hash of every device and launch source: counters measured on other code are not reused."""
+def kernel_source_hash(which: str = "fwd") -> str:
+    """Hash of the device and launch sources of one pass: counters measured on other code are not reused."""
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
+    for path in KERNEL_SRCS[which]:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -122,7 +127,8 @@ def load_traffic(workload: str):
     except (OSError, ValueError):
         return None
     entry = t.get(workload)
-    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
+    which = "bwd" if workload.startswith("bwd:") else "fwd"
+    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash(which):
         return None
     return entry.get("bytes_per_launch")
 
@@ -186,7 +192,7 @@ def record_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_di
         "kernels": kernels,
         "copy_fetch_factor": f_factor, "copy_write_factor": w_factor,
         "read_only_fetch_factor": read_factor,
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_source_sha256_16": kernel_source_hash("bwd" if workload.startswith("bwd:") else "fwd"),
     }
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(table, f, indent=1, sort_keys=True)
