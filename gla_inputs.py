@@ -27,7 +27,7 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "draw", "logsigmoid_f32",
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "draw", "draw_wy", "logsigmoid_f32",
            "to_bf16_f32", "array_digest"]
 
 
@@ -149,3 +149,51 @@ def _draw_from(rng, B, T, H, K, V, dtype, h0, lengths, gate_scale, HV=None, gate
     elif dtype != "fp32":
         raise ValueError(f"unknown dtype {dtype}")
     return {"q": q, "k": k, "v": v, "g": g, "h0": h, "cu_seqlens": cu}
+
+
+def draw_wy(seed: int, B: int, T: int, H: int, K: int, V: int, dtype: str = "bf16",
+            HV: Optional[int] = None, lengths: Optional[list] = None, use_g: bool = True,
+            dense_A: bool = False, chunk: int = 64):
+    """Inputs of the WY-representation forward, from ``numpy.random.default_rng(seed)``.
+
+    Draw order: [lengths given], k, v, beta, A, [g].  k [B,T,H,K] and v
+    [B,T,HV,V] ~ N(0,1); beta [B,T,HV] = sigmoid(N(0,1)); A [B,T,HV,chunk]: for
+    each token, the row of its chunk's matrix, unit diagonal and N(0,1)/8 below
+    it, zero above (a unit lower-triangular matrix, the shape of a WY inverse);
+    with ``dense_A`` every entry of the row is N(0,1)/8 (columns past a partial
+    chunk's rows included).  g [B,T,HV] = 4 logsigmoid(N(0,1)) (a log gate in
+    (-inf, 0)).  k, v and A are rounded to bf16 for bf16; beta and g are float32.
+    Returns k, v, beta, A, g (or None), cu_seqlens (or None).
+    """
+    rng = np.random.default_rng(seed)
+    HV = H if HV is None else HV
+    if HV % H != 0:
+        raise ValueError("HV must be a multiple of H")
+    cu = None
+    if lengths is not None:
+        lengths = [int(x) for x in lengths]
+        cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(lengths)
+        B, T = 1, int(cu[-1])
+    k = rng.standard_normal((B, T, H, K), dtype=np.float32)
+    v = rng.standard_normal((B, T, HV, V), dtype=np.float32)
+    zb = rng.standard_normal((B, T, HV), dtype=np.float32)
+    beta = (1.0 / (1.0 + np.exp(-zb))).astype(np.float32)
+    A = (rng.standard_normal((B, T, HV, chunk), dtype=np.float32) / np.float32(8.0)).astype(np.float32)
+    if not dense_A:
+        # position of each token inside its chunk (chunks restart per sequence)
+        offs = cu if cu is not None else np.arange(B + 1, dtype=np.int64) * T
+        pos = np.zeros(B * T, dtype=np.int64)
+        for n in range(len(offs) - 1):
+            pos[offs[n]:offs[n + 1]] = np.arange(offs[n + 1] - offs[n]) % chunk
+        col = np.arange(chunk)[None, :]
+        pos = pos.reshape(B, T)[:, :, None, None]
+        A = np.where(col[None, None] < pos, A, np.where(col[None, None] == pos, np.float32(1.0),
+                                                         np.float32(0.0))).astype(np.float32)
+    g = (np.float32(4.0) * logsigmoid_f32(rng.standard_normal((B, T, HV), dtype=np.float32))).astype(
+        np.float32) if use_g else None
+    if dtype == "bf16":
+        k, v, A = to_bf16_f32(k), to_bf16_f32(v), to_bf16_f32(A)
+    elif dtype != "fp32":
+        raise ValueError(f"unknown dtype {dtype}")
+    return {"k": k, "v": v, "beta": beta, "A": A, "g": g, "cu_seqlens": cu}

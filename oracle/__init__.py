@@ -18,6 +18,8 @@ from typing import Optional, Tuple
 
 import numpy as np
 
+from .wy import wy_reference  # noqa: E402,F401  (WY-representation forward, numpy fp64)
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gla_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libgla_oracle.so")
