@@ -6,6 +6,11 @@ logsigmoid(N(0,1))/16, chunk 64, final state stored -- the largest of the five
 measured configurations (synthetic seeded inputs, recipe in gla_inputs.py).
 ``--workload`` selects another one (small, c2048, c4096, varlen).
 
+``--pass wy`` measures the WY-representation forward of the gated delta rule
+(gla_wy_fwd: w = A (beta 2^g k), u = A (beta v) per chunk) on inputs of the
+workload's shape (k, v, A bf16 or fp32, beta and g fp32, seed 1006), with the
+numpy fp64 oracle as the CPU baseline.
+
 ``--pass bwd`` measures the backward instead (gla_bwd: dq, dk, dv, dg and, with
 an initial state, dh0, for seeded gradients do of o and dht of ht), with the
 same line format, the backward's own algorithmic bytes and flops, and the fp64
@@ -46,6 +51,8 @@ import gla_inputs as gi  # noqa: E402
 
 METRIC = "GLA chunked fwd tokens/s + TFLOP/s, fraction of MFMA/HBM roofline (1 GPU)"
 METRIC_BWD = "GLA chunked bwd tokens/s + TFLOP/s, fraction of MFMA/HBM roofline (1 GPU)"
+METRIC_WY = "WY forward (gated delta rule) tokens/s + TFLOP/s, fraction of MFMA/HBM roofline (1 GPU)"
+WY_SEED = 1006
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
 _CSRC = os.path.join(ROOT, "chunkwise_gated_linear_amd", "csrc")
@@ -55,6 +62,8 @@ KERNEL_SRCS = {
                                             "gla_internal.h", "gla_host.hip")],
     "bwd": [os.path.join(_CSRC, f) for f in ("gla_bwd.hip", "gla_kernels.hip", "gla_device.h",
                                             "gla_internal.h", "gla_host.hip")],
+    "wy": [os.path.join(_CSRC, f) for f in ("gla_wy.hip", "gla_kernels.hip", "gla_device.h",
+                                           "gla_internal.h", "gla_host.hip")],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CALIB_BYTES = 512 << 20
@@ -111,6 +120,46 @@ def algorithmic_bwd(w, n_tokens, n_seqs):
     return nbytes, flops
 
 
+def algorithmic_wy(w, n_tokens, n_seqs):
+    """Bytes (k, v, beta, A, g read once; w, u written once) and flops (the full
+    64-wide rows of A times the K + V scaled columns) of the WY forward."""
+    e = 2 if w.dtype == "bf16" else 4
+    th = n_tokens * w.H
+    nbytes = th * (w.K * e + w.V * e + 4 + 64 * e + 4) + th * (w.K + w.V) * e
+    flops = th * 2 * 64 * (w.K + w.V)
+    return nbytes, flops
+
+
+def cpu_baseline_wy(d, w, n_tokens, target_s=10.0):
+    """The numpy fp64 WY oracle on the first heads, grown until about target_s
+    seconds; reported as tokens/s of the full head count."""
+    import numpy as np
+    import oracle
+    H = w.H
+
+    def run(nh, reps=1):
+        sl = lambda a: None if a is None else np.ascontiguousarray(a[:, :, :nh])
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.wy_reference(sl(d["k"]), sl(d["v"]), sl(d["beta"]), sl(d["A"]), sl(d["g"]),
+                                cu_seqlens=d["cu_seqlens"])
+        return (time.perf_counter() - t0) / reps
+
+    nh = 1
+    dt = run(nh)
+    while dt < target_s / 2 and nh < H:
+        nh = min(H, 2 * nh)
+        dt = run(nh)
+    reps = 1
+    while dt * reps < 0.8 * target_s:
+        reps = max(2 * reps, int(target_s / max(dt, 1e-5)))
+        dt = run(nh, reps)
+    return {"value": n_tokens * (nh / H) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nh} of {H} heads, all {n_tokens} tokens, fp64 numpy matrix product per chunk "
+                      f"(one thread), {dt * reps:.2f} s for {reps} run(s) on {cpu_model()}; tokens/s "
+                      f"scaled to {H} heads"}
+
+
 def describe(w, lengths):
     if w.varlen:
         return (f"varlen {w.n_seqs} seqs lengths U[{w.len_lo},{w.len_hi}] total {sum(lengths)}, "
@@ -127,7 +176,7 @@ def load_traffic(workload: str):
     except (OSError, ValueError):
         return None
     entry = t.get(workload)
-    which = "bwd" if workload.startswith("bwd:") else "fwd"
+    which = workload.split(":")[0] if ":" in workload else "fwd"
     if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash(which):
         return None
     return entry.get("bytes_per_launch")
@@ -192,7 +241,7 @@ def record_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_di
         "kernels": kernels,
         "copy_fetch_factor": f_factor, "copy_write_factor": w_factor,
         "read_only_fetch_factor": read_factor,
-        "kernel_source_sha256_16": kernel_source_hash("bwd" if workload.startswith("bwd:") else "fwd"),
+        "kernel_source_sha256_16": kernel_source_hash(workload.split(":")[0] if ":" in workload else "fwd"),
     }
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(table, f, indent=1, sort_keys=True)
@@ -283,6 +332,67 @@ def cpu_baseline_bwd(d, w, n_tokens, do, dht, target_s=10.0, max_seq_tokens=4096
                       f"scaled to {H} heads"}
 
 
+def run_wy_bench(args, w, d):
+    """Timed steps of gla_wy_fwd on inputs d of workload w's shape; prints the JSON line."""
+    import torch
+    import chunkwise_gated_linear_amd as gla
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    k, v, A = (torch.from_numpy(d[x]).to(tdt).to(dev) for x in ("k", "v", "A"))
+    beta = torch.from_numpy(d["beta"]).to(dev)
+    g = torch.from_numpy(d["g"]).to(dev)
+    call = gla.WyCall(k, v, beta, A, g=g)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(4):
+            call(sptr)
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        call(sptr)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        call(sptr)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    launch_ms = ev0.elapsed_time(ev1) / args.steps
+    n_tokens = w.B * w.T
+    nbytes, flops = algorithmic_wy(w, n_tokens, w.B)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    mfma_peak = MFMA_PEAK_TFLOPS[w.dtype]
+    t_mfma = flops / (mfma_peak * 1e12)
+    if t_hbm >= t_mfma:
+        bound, achieved, peak, unit = "hbm", nbytes / (launch_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", flops / (launch_ms * 1e-3) / 1e12, mfma_peak, "TFLOP/s"
+    cpu = None if args.no_cpu_baseline else cpu_baseline_wy(d, w, n_tokens)
+    line = {
+        "metric": METRIC_WY, "value": n_tokens / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"WY forward, B={w.B},H={w.H},T={w.T},K={w.K},V={w.V} {w.dtype} k/v/A, "
+                               f"beta, g fp32, chunk 64", "name": "wy:" + w.name, "tokens": n_tokens,
+                   "heads": w.H, "seed": WY_SEED,
+                   "inputs_digest": gi.array_digest(d["k"], d["v"], d["beta"], d["A"], d["g"]),
+                   "workspace_bytes": call.ws_bytes},
+        "tflops_algorithmic": flops / (ms_per_step * 1e-3) / 1e12,
+        "roofline_time_us": max(t_hbm, t_mfma) * 1e6,
+        "roofline": {"bound": bound, "kernel": "gla_wy_fwd_kernel", "achieved": achieved, "peak": peak,
+                     "unit": unit, "frac": achieved / peak, "traffic": load_traffic("wy:" + w.name),
+                     "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
+                     "launch_ms_avg": launch_ms, "measured_copy_GBs": None},
+        "single_launch_us": None,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,8 +403,9 @@ def main():
                          "reaches its sustained clock (short runs otherwise measure the ramp)")
     ap.add_argument("--workload", default=None, choices=sorted(gi.WORKLOADS),
                     help="default: long for the forward, c2048 for the backward")
-    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
-                    help="fwd (default): the forward; bwd: the backward (gla_bwd)")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "wy"],
+                    help="fwd (default): the forward; bwd: the backward (gla_bwd); wy: the WY-representation "
+                         "forward of the gated delta rule (gla_wy_fwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--single", type=int, default=11,
                     help="launches timed one by one after the timed steps, warm and with L2/MALL evicted")
@@ -311,7 +422,7 @@ def main():
     args = ap.parse_args()
     if args.workload is None:
         args.workload = "long" if args.which == "fwd" else "c2048"
-    traffic_key = args.workload if args.which == "fwd" else "bwd:" + args.workload
+    traffic_key = args.workload if args.which == "fwd" else args.which + ":" + args.workload
     if args.record_traffic:
         if len(args.record_traffic) not in (4, 5):
             ap.error("--record-traffic takes 4 or 5 directories")
@@ -349,6 +460,12 @@ def main():
         return
 
     w = gi.WORKLOADS[args.workload]
+    if args.which == "wy":
+        if w.varlen:
+            ap.error("--pass wy takes a fixed-length workload")
+        d = gi.draw_wy(WY_SEED, w.B, w.T, w.H, w.K, w.V, dtype=w.dtype)
+        run_wy_bench(args, w, d)
+        return
     d = gi.make_inputs(w)
     lengths = d.get("lengths")
     digest = gi.array_digest(d["q"], d["k"], d["v"], d["g"], d["h0"], d["cu_seqlens"])

@@ -30,7 +30,8 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
-__all__ = ["gla_fwd", "gla_bwd", "gla_fwd_noalloc", "bwd_workspace_bytes", "GlaCall", "GlaBwdCall", "workspace_bytes", "library_path", "load_library", "GlaError",
+__all__ = ["gla_fwd", "gla_bwd", "gla_fwd_noalloc", "wy_fwd", "bwd_workspace_bytes", "GlaCall", "GlaBwdCall",
+           "WyProblem", "WyCall", "workspace_bytes", "library_path", "load_library", "GlaError",
            "STATUS", "Problem", "STATUS_WAIT_EXHAUSTED", "read_status"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +63,12 @@ class Problem(ctypes.Structure):
                 ("HV", ctypes.c_int32), ("gate", ctypes.c_int32)]
 
 
+class WyProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("HV", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("n_seqs", ctypes.c_int32), ("chunk", ctypes.c_int32), ("packed", ctypes.c_int32)]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -87,6 +94,10 @@ def load_library():
     lib.gla_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.gla_bwd.argtypes = [ctypes.POINTER(Problem)] + [vp] * 14 + [ctypes.c_size_t, vp]
     lib.gla_bwd.restype = ctypes.c_int
+    lib.gla_wy_fwd_workspace_bytes.argtypes = [ctypes.POINTER(WyProblem)]
+    lib.gla_wy_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.gla_wy_fwd.argtypes = [ctypes.POINTER(WyProblem)] + [vp] * 9 + [ctypes.c_size_t, vp]
+    lib.gla_wy_fwd.restype = ctypes.c_int
     lib.gla_status_str.argtypes = [ctypes.c_int]
     lib.gla_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -380,3 +391,97 @@ class GlaBwdCall:
     def status(self) -> int:
         """Sticky status word of this call's workspace (GLA_STATUS_* bits); synchronises."""
         return read_status(self.workspace)
+
+
+def _wy_problem(k, v, beta, A, g, cu_seqlens):
+    """Checks the tensors of a WY call and builds its gla_wy_problem."""
+    import torch
+
+    if k.dim() != 4 or v.dim() != 4 or v.shape[:2] != k.shape[:2] or v.shape[2] % k.shape[2] != 0:
+        raise ValueError("expected k [B, T, H, K] and v [B, T, HV, V] with HV a multiple of H")
+    B, T, H, K = k.shape
+    HV, V = v.shape[2], v.shape[3]
+    if tuple(A.shape) != (B, T, HV, CHUNK) or tuple(beta.shape) != (B, T, HV):
+        raise ValueError(f"A must be [{B}, {T}, {HV}, {CHUNK}] and beta [{B}, {T}, {HV}]")
+    if g is not None and tuple(g.shape) != (B, T, HV):
+        raise ValueError(f"g must be [{B}, {T}, {HV}]")
+    if not (k.dtype == v.dtype == A.dtype) or k.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("k, v and A must share a dtype, bfloat16 or float32")
+    if beta.dtype != torch.float32 or (g is not None and g.dtype != torch.float32):
+        raise ValueError("beta and g must be float32")
+    tensors = [k, v, beta, A] + [t for t in (g, cu_seqlens) if t is not None]
+    dev = k.device
+    if dev.type != "cuda" or any(t.device != dev for t in tensors) or not all(t.is_contiguous() for t in tensors):
+        raise ValueError("all tensors must be contiguous and on the same GPU")
+    if cu_seqlens is not None:
+        if B != 1 or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise ValueError("packed sequences need B == 1 and int32 cu_seqlens")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    prob = WyProblem(B, T, H, HV, K, V, GLA_BF16 if k.dtype == torch.bfloat16 else GLA_F32, N, CHUNK,
+                     1 if cu_seqlens is not None else 0)
+    return prob, dev
+
+
+class WyCall:
+    """A prepared WY forward: validates once, allocates w, u and the workspace
+    once, then enqueues the same gla_wy_fwd call on every ``__call__``."""
+
+    def __init__(self, k, v, beta, A, g=None, cu_seqlens=None):
+        import torch
+
+        self.lib = load_library()
+        self.problem, self.device = _wy_problem(k, v, beta, A, g, cu_seqlens)
+        n = self.lib.gla_wy_fwd_workspace_bytes(ctypes.byref(self.problem))
+        if n == ctypes.c_size_t(-1).value:
+            raise GlaError(2, "invalid problem")
+        self.ws_bytes = int(n)
+        self.workspace = _new_workspace(self.ws_bytes, self.device)
+        B, T, H, K = k.shape
+        self.w = torch.empty((B, T, v.shape[2], K), dtype=k.dtype, device=self.device)
+        self.u = torch.empty_like(v)
+        self._args = (k, v, beta, A, g, cu_seqlens)
+        self()
+
+    def __call__(self, stream=None):
+        import torch
+        k, v, beta, A, g, cu = self._args
+        s = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
+        rc = self.lib.gla_wy_fwd(ctypes.byref(self.problem), _ptr(k), _ptr(v), _ptr(beta), _ptr(A), _ptr(g),
+                                 _ptr(cu), _ptr(self.w), _ptr(self.u), self.workspace.data_ptr(), self.ws_bytes, s)
+        if rc != 0:
+            raise GlaError(rc, _status_msg(self.lib, rc))
+        return self.w, self.u
+
+
+def wy_fwd(k, v, beta, A, g=None, cu_seqlens=None, workspace=None):
+    """WY-representation forward of the gated delta rule through libgla.so's gla_wy_fwd.
+
+    k [B, T, H, K], v [B, T, HV, V], A [B, T, HV, 64] in one dtype (bf16 or
+    fp32); beta [B, T, HV] and g [B, T, HV] (base-2 log gate, optional) float32;
+    cu_seqlens int32 [N+1] for packed sequences.  Returns (w [B, T, HV, K],
+    u [B, T, HV, V]) in the input dtype.  Asynchronous on torch's current stream.
+    """
+    import torch
+
+    lib = load_library()
+    prob, dev = _wy_problem(k, v, beta, A, g, cu_seqlens)
+    B, T, H, K = k.shape
+    HV = v.shape[2]
+    with torch.cuda.device(dev):
+        ws = lib.gla_wy_fwd_workspace_bytes(ctypes.byref(prob))
+        if ws == ctypes.c_size_t(-1).value:
+            rc = lib.gla_wy_fwd(ctypes.byref(prob), *([None] * 9), 0, None)
+            raise GlaError(rc, _status_msg(lib, rc))
+        w = torch.empty((B, T, HV, K), dtype=k.dtype, device=dev)
+        u = torch.empty_like(v)
+        if workspace is None or workspace.numel() * workspace.element_size() < ws:
+            workspace = _new_workspace(ws, dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.gla_wy_fwd(ctypes.byref(prob), _ptr(k), _ptr(v), _ptr(beta), _ptr(A), _ptr(g),
+                            _ptr(cu_seqlens), _ptr(w), _ptr(u), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), stream)
+    if rc != 0:
+        raise GlaError(rc, _status_msg(lib, rc))
+    return w, u

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgla.so")
-SOURCES = ["gla_kernels.hip", "gla_walk_bf16.hip", "gla_bwd.hip", "gla_host.hip"]
+SOURCES = ["gla_kernels.hip", "gla_walk_bf16.hip", "gla_bwd.hip", "gla_wy.hip", "gla_host.hip"]
 ARCH = os.environ.get("GLA_OFFLOAD_ARCH", "gfx950")
 
 

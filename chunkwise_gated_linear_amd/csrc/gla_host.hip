@@ -348,6 +348,39 @@ gla_status run_backward(const gla_problem *p, const BwdPlan &bpl, const void *q,
   return GLA_OK;
 }
 
+// WY-representation forward: one chunk per slot, the slot table of packed
+// inputs in the workspace after the status header.
+struct WyPlan {
+  Plan fwd;  // slot numbering (R = 1)
+  size_t total;
+  bool ok;
+};
+
+gla_problem wy_as_problem(const gla_wy_problem *p) {
+  gla_problem q{};
+  q.B = p->B; q.T = p->T; q.H = p->H; q.K = p->K; q.V = p->V; q.dtype = p->dtype;
+  q.n_seqs = p->n_seqs; q.chunk = p->chunk; q.scale = 1.f; q.segment_chunks = 1; q.packed = p->packed;
+  q.HV = p->HV;
+  return q;
+}
+
+gla_status validate_wy(const gla_wy_problem *p) {
+  if (!p) return GLA_ERR_NULL_ARG;
+  const gla_problem q = wy_as_problem(p);
+  return validate(&q);
+}
+
+WyPlan make_wy_plan(const gla_wy_problem *p) {
+  WyPlan w{};
+  const gla_problem q = wy_as_problem(p);
+  w.fwd = make_plan(&q, p->packed == 1);
+  const long long HV = p->HV == 0 ? p->H : p->HV;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  w.total = kHeaderBytes + up(p->packed == 1 ? (size_t)(w.fwd.N + 1 + w.fwd.seg_slots) * sizeof(int32_t) : 0);
+  w.ok = w.fwd.ok && (long long)w.fwd.seg_slots * HV <= INT_MAX;
+  return w;
+}
+
 // Host-side checks of a call (same for both entry points).
 gla_status check_call(const gla_problem *p, const void *q, const void *k, const void *v, const float *g,
                       const void *o, const int32_t *cu_seqlens, Plan &pl) {
@@ -443,6 +476,46 @@ gla_status gla_bwd(const gla_problem *p, const void *q, const void *k, const voi
   char *ws = reinterpret_cast<char *>(workspace);
   return run_backward(p, b, q, k, v, g, h0, cu_seqlens, dout, dht, dq, dk, dv, dg, dh0, ws,
                       reinterpret_cast<uint32_t *>(ws), reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t gla_wy_fwd_workspace_bytes(const gla_wy_problem *p) {
+  if (validate_wy(p) != GLA_OK) return (size_t)-1;
+  const WyPlan w = make_wy_plan(p);
+  return w.ok ? w.total : (size_t)-1;
+}
+
+gla_status gla_wy_fwd(const gla_wy_problem *p, const void *k, const void *v, const float *beta, const void *A,
+                      const float *g, const int32_t *cu_seqlens, void *w, void *u, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  const gla_status st = validate_wy(p);
+  if (st != GLA_OK) return st;
+  const bool varlen = p->packed == 1;
+  if (varlen != (cu_seqlens != nullptr)) return GLA_ERR_NULL_ARG;
+  if ((long long)p->B * p->T > 0 && (!k || !v || !beta || !A || !w || !u)) return GLA_ERR_NULL_ARG;
+  const WyPlan pl = make_wy_plan(p);
+  if (!pl.ok) return GLA_ERR_BAD_SHAPE;
+  if (workspace == nullptr || workspace_bytes < pl.total) return GLA_ERR_WORKSPACE;
+  const int N = varlen ? p->n_seqs : p->B;
+  if (N == 0 || (long long)p->B * p->T == 0) return GLA_OK;
+  char *ws = reinterpret_cast<char *>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  gla::WyParams wp{};
+  gla::WalkParams &wk = wp.w;
+  wk.k = k; wk.v = v; wk.cu = cu_seqlens;
+  wk.status = reinterpret_cast<uint32_t *>(ws);
+  int32_t *seg_base = varlen ? reinterpret_cast<int32_t *>(ws + kHeaderBytes) : nullptr;
+  wk.seg_base = seg_base;
+  wk.T = p->T; wk.H = p->H; wk.K = p->K; wk.V = p->V; wk.N = N;
+  wk.HV = p->HV == 0 ? p->H : p->HV;
+  wk.G = wk.HV / p->H;
+  wk.Kmem = p->K;
+  wk.R = pl.fwd.R;
+  wk.P = pl.fwd.P;
+  wk.seg_slots = pl.fwd.seg_slots;
+  wp.beta = beta; wp.A = A; wp.g = g; wp.wout = w; wp.u = u;
+  if (seg_base && gla::launch_segment_plan(wk, seg_base, seg_base + N + 1, s) != hipSuccess) return GLA_ERR_HIP;
+  if (gla::launch_wy_fwd(p->dtype == GLA_BF16, wp, s) != hipSuccess) return GLA_ERR_HIP;
+  return GLA_OK;
 }
 
 gla_status gla_fwd_noalloc(const gla_problem *p, const void *q, const void *k, const void *v, const float *g,

@@ -1,5 +1,6 @@
 // Internal interface between the host library (gla_host.hip) and the device
-// kernels (gla_kernels.hip, gla_walk_bf16.hip).  Not part of the public C ABI.
+// kernels (gla_kernels.hip, gla_walk_bf16.hip, gla_bwd.hip, gla_wy.hip).  Not
+// part of the public C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -92,5 +93,16 @@ hipError_t launch_bwd_scan(const BwdParams &bp, hipStream_t s);
 // the fast chunk kernel, the token-by-token kernel for flagged chunks, and
 // (G > 1) the sum of dq, dk over each key head's value heads
 hipError_t launch_bwd_chunk(bool bf16, const BwdParams &bp, hipStream_t s);
+
+// WY-representation forward (gla_wy.hip): one chunk per slot as in the backward.
+struct WyParams {
+  WalkParams w;        // sizes (T, H, HV, G, K, V, N, P, seg_slots), k = w.k, v = w.v, cu, seg_base
+  const float *beta;   // [B,T,HV]
+  const void *A;       // [B,T,HV,64] dtype: each token's row of its chunk matrix
+  const float *g;      // [B,T,HV] base-2 log gate, or null
+  void *wout;          // [B,T,HV,K] dtype
+  void *u;             // [B,T,HV,V] dtype
+};
+hipError_t launch_wy_fwd(bool bf16, const WyParams &wp, hipStream_t s);
 
 }  // namespace gla

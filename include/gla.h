@@ -205,6 +205,50 @@ gla_status gla_bwd(const gla_problem *p,
                    void *workspace, size_t workspace_bytes,
                    void *stream);
 
+/*
+ * WY-representation forward of the gated delta rule, on the same chunk and
+ * packed-sequence skeleton (page "fla/ops/gated_delta_rule/backends/
+ * triton_ascend/wy_fast.py": recompute_w_u_fwd_kernel_npu and its wrapper
+ * recompute_w_u_fwd_npu).  For every chunk of 64 tokens of a sequence
+ * (restarting per packed sequence) and value head hv, with A_c the chunk's
+ * 64 x 64 matrix:
+ *     u = A_c (beta . v),    w = A_c (beta . 2^g . k)       (rows: the chunk's tokens)
+ * k of key head hv / (HV / H); the factor 2^g (the page applies exp2 to g)
+ * only when g is given.  A's columns past a partial chunk's tokens meet zero
+ * rows and add nothing.
+ */
+typedef struct gla_wy_problem {
+    int32_t B;        /* batch; 1 for packed sequences                        */
+    int32_t T;        /* tokens per sequence, or total packed tokens          */
+    int32_t H;        /* key heads (k)                                        */
+    int32_t HV;       /* value heads (v, beta, A, g, w, u); a multiple of H; 0 means H */
+    int32_t K;        /* key width, a multiple of 16 in [16, 256]             */
+    int32_t V;        /* value width, a multiple of 16 in [16, 256]           */
+    int32_t dtype;    /* gla_dtype of k, v, A, w and u; beta and g are float32 */
+    int32_t n_seqs;   /* N: B without cu_seqlens, len(cu_seqlens)-1 with it   */
+    int32_t chunk;    /* 64, the width of A's rows                           */
+    int32_t packed;   /* 1 when cu_seqlens will be passed                     */
+} gla_wy_problem;
+
+/* Workspace bytes gla_wy_fwd needs (at least 256), or (size_t)-1 when invalid. */
+size_t gla_wy_fwd_workspace_bytes(const gla_wy_problem *p);
+
+/*
+ *   k    : [B,T,H,K] dtype             v : [B,T,HV,V] dtype
+ *   beta : [B,T,HV] float32            A : [B,T,HV,64] dtype, each token's row of its chunk matrix
+ *   g    : [B,T,HV] float32 base-2 log gate, or NULL (no gate factor)
+ *   cu_seqlens : [N+1] int32 or NULL
+ *   w    : [B,T,HV,K] dtype            u : [B,T,HV,V] dtype (every token's row written)
+ *   workspace / workspace_bytes : device scratch, first 4 bytes a status word as for gla_fwd
+ * All pointers are device memory owned by the caller (16-byte aligned); work
+ * is asynchronous on `stream`.  Returns GLA_OK or an error code; on error
+ * nothing is written.
+ */
+gla_status gla_wy_fwd(const gla_wy_problem *p,
+                      const void *k, const void *v, const float *beta, const void *A, const float *g,
+                      const int32_t *cu_seqlens, void *w, void *u,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *gla_status_str(gla_status s);
 

@@ -32,7 +32,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["gla_bwd", "gla_bwd_workspace_bytes", "gla_fwd", "gla_fwd_noalloc",
-                                    "gla_fwd_workspace_bytes", "gla_status_str"]
+                                    "gla_fwd_workspace_bytes", "gla_status_str", "gla_wy_fwd",
+                                    "gla_wy_fwd_workspace_bytes"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -240,3 +241,43 @@ def test_backward_workspace_size_and_check(lib):
     sv, dv_ = up(slots_v * H * K * V * 4), up(slots_v * H * K * 4)
     assert lib.gla_bwd_workspace_bytes(ctypes.byref(pv)) == (WS_HEADER + up((6 + slots_v) * 4) + 2 * sv + dv_
                                                              + up(slots_v * H * 4))
+
+
+# ---------------------------------------------------------------- WY-representation forward
+
+def wy_prob(**kw):
+    base = dict(B=2, T=100, H=2, HV=4, K=64, V=128, dtype=gla.GLA_BF16, n_seqs=2, chunk=64, packed=0)
+    base.update(kw)
+    return gla.WyProblem(**base)
+
+
+def call_wy(lib, p, ws=FAKE, ws_bytes=1 << 40, cu=None, k=FAKE):
+    return lib.gla_wy_fwd(ctypes.byref(p) if p is not None else None, k, FAKE, FAKE, FAKE, None, cu,
+                          FAKE, FAKE, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), BAD_DTYPE),
+    (dict(chunk=32), UNSUPPORTED),
+    (dict(K=24), UNSUPPORTED),
+    (dict(V=272), UNSUPPORTED),
+    (dict(HV=3), BAD_SHAPE),
+    (dict(n_seqs=3), BAD_SHAPE),
+    (dict(packed=1), BAD_SHAPE),
+    (dict(T=-1), BAD_SHAPE),
+])
+def test_wy_rejects_invalid_problems(lib, kw, code):
+    p = wy_prob(**kw)
+    assert call_wy(lib, p) == code
+    assert lib.gla_wy_fwd_workspace_bytes(ctypes.byref(p)) == ctypes.c_size_t(-1).value
+
+
+def test_wy_null_arguments_and_workspace(lib):
+    assert call_wy(lib, None) == NULL_ARG
+    assert call_wy(lib, wy_prob(), k=None) == NULL_ARG
+    assert call_wy(lib, wy_prob(B=1, n_seqs=1, packed=1)) == NULL_ARG  # packed without cu_seqlens
+    assert lib.gla_wy_fwd_workspace_bytes(ctypes.byref(wy_prob())) == WS_HEADER
+    pv = wy_prob(B=1, T=1000, n_seqs=5, packed=1)
+    slots = 5 + 16 + 5
+    assert lib.gla_wy_fwd_workspace_bytes(ctypes.byref(pv)) == WS_HEADER + up((6 + slots) * 4)
+    assert call_wy(lib, wy_prob(), ws=None, ws_bytes=0) == WORKSPACE
