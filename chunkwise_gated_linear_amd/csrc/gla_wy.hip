@@ -15,10 +15,11 @@
 // gla_wy_fwd: one workgroup of 4 waves per (chunk slot, value head), slots
 // numbered as the segments of one chunk of the forward (gla_segment_plan with
 // R = 1 for packed inputs).  A and one 64-column block of the scaled operand
-// are staged in LDS (32 KB), so several workgroups share a compute unit and
-// hide each other's loads.  Products on v_mfma_f32_16x16x4f32, taken
-// transposed (rows: operand columns, columns: tokens) so that each lane holds
-// four consecutive output columns of one token and stores them at once.
+// are staged in LDS, so several workgroups share a compute unit and hide each
+// other's loads.  Products are taken transposed (rows: operand columns,
+// columns: tokens) so that each lane holds four consecutive output columns of
+// one token and stores them at once: v_mfma_f32_16x16x4f32 for fp32 inputs,
+// v_mfma_f32_16x16x32_bf16 with a hi/lo split of the scaled operand for bf16.
 #include <hip/hip_runtime.h>
 
 #include "gla_device.h"
@@ -141,13 +142,128 @@ __global__ __launch_bounds__(256) void gla_wy_fwd_kernel(WyParams wp) {
   }
 }
 
+// bf16 inputs: v_mfma_f32_16x16x32_bf16.  A is exact in bf16 and is the
+// product's right operand as stored; the scaled rows beta v and beta 2^g k
+// are fp32 products, split into bf16 hi + lo (hi = the nearest bf16, lo = the
+// nearest bf16 of the remainder) so that hi*A + lo*A carries them to fp32
+// accuracy.  Both planes are staged transposed, X^T[c][j], so that a lane
+// reads its 8 consecutive tokens j with one 16-byte load.  bf16 tiles of
+// [64][64] use 16-byte groups XOR-swizzled by 2 ((row >> 2) & 3): the 16-byte
+// reads of 16 consecutive rows then fall on distinct banks for each 32 lanes.
+__device__ __forceinline__ int bswz(int row, int col) {
+  return row * 64 + ((((col >> 3) ^ (2 * ((row >> 2) & 3)))) << 3) + (col & 7);
+}
+
+__global__ __launch_bounds__(256) void gla_wy_fwd_kernel_bf16(WyParams wp) {
+  const WalkParams &p = wp.w;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[64 * 64];   // A[i][j], bf16
+  __shared__ __attribute__((aligned(16))) uint16_t sXh[64 * 64];  // X^T[c][j], hi
+  __shared__ __attribute__((aligned(16))) uint16_t sXl[64 * 64];  // X^T[c][j], lo
+  __shared__ float sS[2][64];                                     // beta_j, beta_j 2^{g_j}
+
+  const int hv = (int)(blockIdx.x % (unsigned)p.HV);
+  const int slot = (int)(blockIdx.x / (unsigned)p.HV);
+  SegInfo si;
+  if (!locate(p, slot, si)) return;
+  const int nch = (si.len + kChunk - 1) / kChunk;
+  if (si.s >= nch) return;
+  const int L = min(kChunk, si.len - kChunk * si.s);
+  const int64_t row0 = si.bos + (int64_t)kChunk * si.s;
+  const int h = hv / p.G;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
+
+  // A rows as stored (2 groups of 8 per thread) and the row scales
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int e = threadIdx.x + 256 * t, i = e >> 3, c8 = (e & 7) * 8;
+    u32x4_t x = {0u, 0u, 0u, 0u};
+    if (i < L)
+      x = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint16_t *>(wp.A) +
+                                            ((row0 + i) * p.HV + hv) * kChunk + c8);
+    *reinterpret_cast<u32x4_t *>(sA + bswz(i, c8)) = x;
+  }
+  if (threadIdx.x < 64) {
+    const int j = threadIdx.x;
+    const float b = j < L ? wp.beta[(row0 + j) * p.HV + hv] : 0.f;
+    sS[0][j] = b;
+    sS[1][j] = (wp.g != nullptr && j < L) ? b * exp2f(wp.g[(row0 + j) * p.HV + hv]) : b;
+  }
+
+  // blocks of 64 output columns: u's first (from v), then w's (from k); the
+  // rows of block b + 1 are loaded while block b is formed and stored
+  const int nbu = (p.V + 63) / 64, nb = nbu + (p.K + 63) / 64;
+  auto block = [&](int b, int &which, int &c0, int &W) {
+    which = b < nbu ? 0 : 1;
+    c0 = (b < nbu ? b : b - nbu) * 64;
+    W = which == 0 ? p.V : p.K;
+  };
+  auto load_rows = [&](int b, u32x2_t (&xr)[4]) {
+    int which, c0, W;
+    block(b, which, c0, W);
+    const void *src = which == 0 ? p.v : p.k;
+    const int64_t srow = which == 0 ? (int64_t)p.HV * p.V : (int64_t)p.H * p.K;  // source row stride
+    const int64_t soff = which == 0 ? (int64_t)hv * p.V : (int64_t)h * p.K;      // source head offset
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int e = threadIdx.x + 256 * t, j = e >> 4, c4 = (e & 15) * 4;
+      xr[t] = u32x2_t{0u, 0u};
+      if (j < L && c0 + c4 < W)
+        xr[t] = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(src) +
+                                                  (row0 + j) * srow + soff + c0 + c4);
+    }
+  };
+  u32x2_t xr[4];
+  load_rows(0, xr);
+  for (int b = 0; b < nb; ++b) {
+    int which, c0, W;
+    block(b, which, c0, W);
+    __syncthreads();  // sS / sA ready (first block); sX free (later blocks)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int e = threadIdx.x + 256 * t, j = e >> 4, c4 = (e & 15) * 4;
+      const float sc = sS[which][j];
+      const float x[4] = {bf_lo(xr[t][0]) * sc, bf_hi(xr[t][0]) * sc, bf_lo(xr[t][1]) * sc,
+                          bf_hi(xr[t][1]) * sc};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const __bf16 hi = (__bf16)x[r];
+        const __bf16 lo = (__bf16)(x[r] - (float)hi);
+        sXh[bswz(c4 + r, j)] = __builtin_bit_cast(uint16_t, hi);
+        sXl[bswz(c4 + r, j)] = __builtin_bit_cast(uint16_t, lo);
+      }
+    }
+    if (b + 1 < nb) load_rows(b + 1, xr);
+    __syncthreads();
+    // D[c][i] = sum_j X[j][c] A[i][j]: wave w takes columns c0 + 16 w .. + 15, all 64 tokens
+    f32x4_t acc[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int j0 = 0; j0 < 64; j0 += 32) {
+      const u32x4_t xh = *reinterpret_cast<const u32x4_t *>(sXh + bswz(wave * 16 + l16, j0 + 8 * lg));
+      const u32x4_t xl = *reinterpret_cast<const u32x4_t *>(sXl + bswz(wave * 16 + l16, j0 + 8 * lg));
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        const u32x4_t a8 = *reinterpret_cast<const u32x4_t *>(sA + bswz(ib * 16 + l16, j0 + 8 * lg));
+        acc[ib] = mfma_bf(xl, a8, acc[ib]);
+        acc[ib] = mfma_bf(xh, a8, acc[ib]);
+      }
+    }
+    void *dst = which == 0 ? wp.u : wp.wout;
+    const int col = c0 + wave * 16 + 4 * lg;
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      const int i = ib * 16 + l16;
+      if (i < L && col < W) st4<true>(dst, ((row0 + i) * p.HV + hv) * W + col, acc[ib]);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_wy_fwd(bool bf16, const WyParams &wp, hipStream_t s) {
   const long long blocks = (long long)wp.w.seg_slots * wp.w.HV;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (bf16) hipLaunchKernelGGL(gla_wy_fwd_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, wp);
+  if (bf16) hipLaunchKernelGGL(gla_wy_fwd_kernel_bf16, dim3((unsigned)blocks), dim3(256), 0, s, wp);
   else hipLaunchKernelGGL(gla_wy_fwd_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, wp);
   return hipGetLastError();
 }
