@@ -421,6 +421,24 @@ __global__ __launch_bounds__(256) void gla_bwd_scan(BwdParams bp, int per_state)
   if (bp.dh0) *reinterpret_cast<f32x4_t *>(bp.dh0 + sidx) = e;
 }
 
+// Eight floats as three bf16 terms (8 lanes each, packed pairs): hi = the
+// nearest bf16, mid = the nearest bf16 of x - hi, lo = the nearest bf16 of
+// x - hi - mid.  Each remainder is exact in fp32, and hi + mid + lo equals x
+// to fp32 precision.
+__device__ __forceinline__ void split8_3(const float (&x)[8], u32x4_t &hi, u32x4_t &mid, u32x4_t &lo) {
+  float r1[8], r2[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    hi[q] = pack_bf16(x[2 * q], x[2 * q + 1]);
+    r1[2 * q] = x[2 * q] - bf_lo(hi[q]);
+    r1[2 * q + 1] = x[2 * q + 1] - bf_hi(hi[q]);
+    mid[q] = pack_bf16(r1[2 * q], r1[2 * q + 1]);
+    r2[2 * q] = r1[2 * q] - bf_lo(mid[q]);
+    r2[2 * q + 1] = r1[2 * q + 1] - bf_hi(mid[q]);
+    lo[q] = pack_bf16(r2[2 * q], r2[2 * q + 1]);
+  }
+}
+
 // ---------------------------------------------------------------- dq / dk stores
 // dq and dk belong to key heads.  With one value head per key head they are
 // stored in the input dtype; with G > 1 each value head stores its fp32 share
@@ -652,7 +670,53 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
     float rs = 0.f;
 #pragma unroll
     for (int b = 0; b < 4; ++b) dq[b] = dkI[b] = zero4();
-    {
+    if constexpr (BF) {
+      // bf16 inputs: do and v are exact in bf16; S and E are split into three
+      // bf16 terms (hi, the rounded remainder, the rounded remainder of that;
+      // every remainder is exact in fp32), so do S^T = sum of three products
+      // keeps fp32 accuracy, on v_mfma_f32_16x16x32_bf16 (each lane: 8
+      // consecutive values).  Two terms carried 16 bits, which the reverse
+      // cumsum of dg amplified past its fp32 bound under strong gates.
+      const int krow = kb + l16;
+#pragma unroll 2
+      for (int v0 = 0; v0 < VD; v0 += 32) {
+        const int col = v0 + 8 * lg;
+        const bool in = krow < p.K && col < p.V;  // V is a multiple of 16: col < V covers col + 7
+        const int64_t off = (int64_t)krow * p.V + col;
+        float sv[8], ev[8];
+        {
+          const f32x4_t s0 = in ? *reinterpret_cast<const f32x4_t *>(Sc + off) : zero4();
+          const f32x4_t s1 = in ? *reinterpret_cast<const f32x4_t *>(Sc + off + 4) : zero4();
+          const f32x4_t e0 = in ? *reinterpret_cast<const f32x4_t *>(Ec + off) : zero4();
+          const f32x4_t e1 = in ? *reinterpret_cast<const f32x4_t *>(Ec + off + 4) : zero4();
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sv[r] = s0[r]; sv[4 + r] = s1[r];
+            ev[r] = e0[r]; ev[4 + r] = e1[r];
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) rs += sv[r] * ev[r];
+        u32x4_t sh, sm, sl, eh, em, el;
+        split8_3(sv, sh, sm, sl);
+        split8_3(ev, eh, em, el);
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) {
+          const f32x4_t o0 = lds4<VD>(sO, ib * 16 + l16, col), o1 = lds4<VD>(sO, ib * 16 + l16, col + 4);
+          const f32x4_t w0 = lds4<VD>(sV, ib * 16 + l16, col), w1 = lds4<VD>(sV, ib * 16 + l16, col + 4);
+          const u32x4_t o8 = {pack_bf16(o0[0], o0[1]), pack_bf16(o0[2], o0[3]), pack_bf16(o1[0], o1[1]),
+                              pack_bf16(o1[2], o1[3])};
+          const u32x4_t w8 = {pack_bf16(w0[0], w0[1]), pack_bf16(w0[2], w0[3]), pack_bf16(w1[0], w1[1]),
+                              pack_bf16(w1[2], w1[3])};
+          dq[ib] = mfma_bf(o8, sl, dq[ib]);
+          dq[ib] = mfma_bf(o8, sm, dq[ib]);
+          dq[ib] = mfma_bf(o8, sh, dq[ib]);
+          dkI[ib] = mfma_bf(w8, el, dkI[ib]);
+          dkI[ib] = mfma_bf(w8, em, dkI[ib]);
+          dkI[ib] = mfma_bf(w8, eh, dkI[ib]);
+        }
+      }
+    } else {
       const int krow = kb + l16;
 #pragma unroll 4
       for (int v0 = 0; v0 < VD; v0 += 16) {
