@@ -410,6 +410,8 @@ def main():
     ap.add_argument("--single", type=int, default=11,
                     help="launches timed one by one after the timed steps, warm and with L2/MALL evicted")
     ap.add_argument("--segment-chunks", type=int, default=0)
+    ap.add_argument("--schedule", type=int, default=0, choices=[0, 1, 2],
+                    help="segmented sequences: 0 automatic, 1 three passes, 2 one pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the forward, run a plain 512 MiB device copy "
                          "(used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -479,7 +481,7 @@ def main():
     do = dht = None
     if args.which == "fwd":
         call = gla.GlaCall(q, k, v, g, h0=h0, cu_seqlens=cu, output_final_state=w.ht,
-                           segment_chunks=args.segment_chunks)
+                           segment_chunks=args.segment_chunks, schedule=args.schedule)
     else:
         # seeded gradients of the outputs: do like v (rounded to its dtype), dht
         # for a stored final state

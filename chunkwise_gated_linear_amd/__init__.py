@@ -60,7 +60,7 @@ class Problem(ctypes.Structure):
                 ("n_seqs", ctypes.c_int32), ("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("segment_chunks", ctypes.c_int32), ("packed", ctypes.c_int32),
                 ("value_tile", ctypes.c_int32), ("wait_limit", ctypes.c_int32),
-                ("HV", ctypes.c_int32), ("gate", ctypes.c_int32)]
+                ("HV", ctypes.c_int32), ("gate", ctypes.c_int32), ("schedule", ctypes.c_int32)]
 
 
 class WyProblem(ctypes.Structure):
@@ -110,10 +110,10 @@ def _status_msg(lib, code: int) -> str:
 
 def make_problem(B, T, H, K, V, dtype_code, n_seqs, chunk=CHUNK, scale=1.0,
                  segment_chunks=0, packed=False, value_tile=0, wait_limit=0, HV=0,
-                 gate=GATE_PER_KEY) -> Problem:
+                 gate=GATE_PER_KEY, schedule=0) -> Problem:
     return Problem(int(B), int(T), int(H), int(K), int(V), int(dtype_code), int(n_seqs),
                    int(chunk), float(scale), int(segment_chunks), 1 if packed else 0,
-                   int(value_tile), int(wait_limit), int(HV), int(gate))
+                   int(value_tile), int(wait_limit), int(HV), int(gate), int(schedule))
 
 
 def workspace_bytes(problem: Problem) -> int:
@@ -151,7 +151,7 @@ def read_status(workspace) -> int:
 def gla_fwd(q, k, v, g, h0=None, cu_seqlens=None, scale: Optional[float] = None,
             chunk: int = CHUNK, output_final_state: bool = False, segment_chunks: int = 0,
             workspace=None, out=None, value_tile: int = 0,
-            wait_limit: int = 0) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
+            wait_limit: int = 0, schedule: int = 0) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
     """Gated linear attention forward through libgla.so.
 
     Returns (o, ht): o has v's shape and dtype; ht is [N, H, K, V] float32 when
@@ -164,7 +164,7 @@ def gla_fwd(q, k, v, g, h0=None, cu_seqlens=None, scale: Optional[float] = None,
 
     lib = load_library()
     prob, N, dev = _problem_for(q, k, v, g, h0, cu_seqlens, out, scale, chunk, segment_chunks,
-                                value_tile, wait_limit)
+                                value_tile, wait_limit, schedule)
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
     with torch.cuda.device(dev):
@@ -189,7 +189,8 @@ def gla_fwd(q, k, v, g, h0=None, cu_seqlens=None, scale: Optional[float] = None,
 
 
 def gla_fwd_noalloc(q, k, v, g, o, h0=None, cu_seqlens=None, ht=None, scale: Optional[float] = None,
-                    status=None, chunk: int = CHUNK, segment_chunks: int = 0, value_tile: int = 0) -> None:
+                    status=None, chunk: int = CHUNK, segment_chunks: int = 0, value_tile: int = 0,
+                    schedule: int = 0) -> None:
     """The forward through the library's no-allocation entry point (gla_fwd_noalloc).
 
     The caller provides o (v's shape and dtype) and, when wanted, ht ([N, H, K, V]
@@ -201,7 +202,8 @@ def gla_fwd_noalloc(q, k, v, g, o, h0=None, cu_seqlens=None, ht=None, scale: Opt
     import torch
 
     lib = load_library()
-    prob, N, dev = _problem_for(q, k, v, g, h0, cu_seqlens, o, scale, chunk, segment_chunks, value_tile, 0)
+    prob, N, dev = _problem_for(q, k, v, g, h0, cu_seqlens, o, scale, chunk, segment_chunks, value_tile, 0,
+                                schedule)
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
     if o.shape != v.shape or o.dtype != v.dtype:
@@ -265,7 +267,8 @@ def gla_bwd(q, k, v, g, do, h0=None, dht=None, cu_seqlens=None, scale: Optional[
     return dq, dk, dv, dg, dh0
 
 
-def _problem_for(q, k, v, g, h0, cu_seqlens, out, scale, chunk, segment_chunks, value_tile, wait_limit):
+def _problem_for(q, k, v, g, h0, cu_seqlens, out, scale, chunk, segment_chunks, value_tile, wait_limit,
+                 schedule=0):
     """Checks the tensors of a call and builds its gla_problem (page defaults for scale)."""
     import torch
 
@@ -315,7 +318,7 @@ def _problem_for(q, k, v, g, h0, cu_seqlens, out, scale, chunk, segment_chunks, 
     elif not (scale > 0):
         raise ValueError("scale must be positive")
     prob = make_problem(B, T, H, K, V, code, N, chunk, scale, segment_chunks, cu_seqlens is not None,
-                        value_tile, wait_limit, HV, gate)
+                        value_tile, wait_limit, HV, gate, schedule)
     return prob, N, dev
 
 
@@ -326,19 +329,20 @@ class GlaCall:
 
     def __init__(self, q, k, v, g, h0=None, cu_seqlens=None, scale=None, chunk: int = CHUNK,
                  output_final_state: bool = False, segment_chunks: int = 0, value_tile: int = 0,
-                 wait_limit: int = 0):
+                 wait_limit: int = 0, schedule: int = 0):
         import torch
 
         self.lib = load_library()
         self.problem, N, self.device = _problem_for(q, k, v, g, h0, cu_seqlens, None, scale, chunk,
-                                                    segment_chunks, value_tile, wait_limit)
+                                                    segment_chunks, value_tile, wait_limit, schedule)
         ws = workspace_bytes(self.problem)
         self.workspace = _new_workspace(ws, self.device)
         self.ws_bytes = ws
         # validation and allocation of o and ht through the same path as gla_fwd
         o, ht = gla_fwd(q, k, v, g, h0=h0, cu_seqlens=cu_seqlens, scale=scale, chunk=chunk,
                         output_final_state=output_final_state, segment_chunks=segment_chunks,
-                        workspace=self.workspace, value_tile=value_tile, wait_limit=wait_limit)
+                        workspace=self.workspace, value_tile=value_tile, wait_limit=wait_limit,
+                        schedule=schedule)
         self.o, self.ht = o, ht
         self._args = (q, k, v, g, h0, cu_seqlens)
 

@@ -84,6 +84,7 @@ gla_status validate(const gla_problem *p) {
   if (p->packed ? p->B != 1 : p->n_seqs != p->B) return GLA_ERR_BAD_SHAPE;
   if (p->HV < 0 || (p->HV != 0 && p->HV % p->H != 0)) return GLA_ERR_BAD_SHAPE;
   if (p->gate != GLA_GATE_PER_KEY && p->gate != GLA_GATE_PER_HEAD) return GLA_ERR_UNSUPPORTED;
+  if (p->schedule < 0 || p->schedule > 2) return GLA_ERR_UNSUPPORTED;
   // token-head rows and state elements must stay addressable with 64-bit
   // offsets; one chunk's byte range of any tensor (64 token rows of H heads)
   // must stay below 2^30, where the kernels put lanes with nothing to load
@@ -106,8 +107,9 @@ struct Plan {
   int nkb;        // key blocks
   int kb[2];      // keys per block
   bool segmented; // some sequence may span several segments
+  bool fused;     // segments chained in one pass (gla_chunk_fused_bf16)
   long long units;
-  size_t ws_state, ws_decay, ws_base, ws_opart, ws_total;
+  size_t ws_state, ws_decay, ws_base, ws_opart, ws_link, ws_total;
   bool ok;        // index spaces fit the kernels' 32-bit grids
 };
 
@@ -133,6 +135,11 @@ Plan make_plan(const gla_problem *p, bool varlen) {
   }
   pl.vtile = vtile;
   pl.NV = (p->V + vtile - 1) / vtile;
+  // one pass with chained segments (the bf16 walker with one key block) unless
+  // three passes are asked for: it skips the scan launch, and with packed
+  // sequences its longer segments do better than the three passes' shorter
+  // ones (U[256, 4096] x 16 sequences: 233 against 276 us at best)
+  const bool single = fast && p->schedule != 1;
   const int NV = pl.NV;
   const long long chunks_total = ((long long)p->T + kChunk - 1) / kChunk;  // varlen: packed axis
   const long long chunks_seq = chunks_total;  // longest possible sequence
@@ -157,7 +164,11 @@ Plan make_plan(const gla_problem *p, bool varlen) {
       // summary work of cutting more sequences (measured optimum on the
       // 16-sequence U[256, 4096] workload)
       const long long work = (chunks_total + pl.N) * H * NV;  // chunk-slices to spread
-      const long long tgt = vtile == 128 ? (3LL * device_cu_count()) / 2 : target;
+      // one pass: about 3 workgroups per 4 compute units (fewer, longer
+      // segments: each costs a walk start-up and a link in the chain; measured
+      // optimum on the same workload, 48-chunk segments)
+      const long long tgt = single ? (3LL * device_cu_count()) / 4
+                                   : vtile == 128 ? (3LL * device_cu_count()) / 2 : target;
       long long r = (work + tgt - 1) / tgt;
       if (r < 4) r = 4;
       R = r;
@@ -191,8 +202,10 @@ Plan make_plan(const gla_problem *p, bool varlen) {
     pl.ws_base = varlen ? (size_t)(pl.N + 1 + slots) * sizeof(int32_t) : 0;  // table + order
   }
   if (pl.nkb == 2) pl.ws_opart = (size_t)p->B * p->T * H * p->V * sizeof(float);
+  pl.fused = pl.segmented && fast && single;
+  if (pl.fused) pl.ws_link = (size_t)(1 + slots * H * NV) * sizeof(int32_t);  // counter + one flag per item
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  pl.ws_total = kHeaderBytes + up(pl.ws_state) + up(pl.ws_decay) + up(pl.ws_base) + up(pl.ws_opart);
+  pl.ws_total = kHeaderBytes + up(pl.ws_state) + up(pl.ws_decay) + up(pl.ws_base) + up(pl.ws_opart) + up(pl.ws_link);
   return pl;
 }
 
@@ -219,6 +232,8 @@ gla_status run_forward(const gla_problem *p, const Plan &pl, const void *q, cons
   int32_t *seg_base = (pl.segmented && varlen) ? reinterpret_cast<int32_t *>(cur) : nullptr;
   cur += up(pl.ws_base);
   float *o_part = pl.nkb == 2 ? reinterpret_cast<float *>(cur) : nullptr;
+  cur += up(pl.ws_opart);
+  w.link = pl.fused ? reinterpret_cast<int32_t *>(cur) : nullptr;
   w.seg_base = seg_base;
   w.seg_order = seg_base ? seg_base + N + 1 : nullptr;
   w.T = p->T; w.H = p->H; w.V = p->V; w.N = N;
@@ -235,6 +250,13 @@ gla_status run_forward(const gla_problem *p, const Plan &pl, const void *q, cons
   w.scale = p->scale;
 
   if (seg_base && gla::launch_segment_plan(w, seg_base, seg_base + N + 1, s) != hipSuccess) return GLA_ERR_HIP;
+  if (pl.fused) {  // one key block (the bf16 walker)
+    w.K = pl.kb[0];
+    w.koff = 0;
+    if (gla::launch_clear(w.link, (long long)(pl.ws_link / sizeof(int32_t)), s) != hipSuccess) return GLA_ERR_HIP;
+    if (gla::launch_fused_bf16(kernel_key_width(true, bf, w.K), w, s) != hipSuccess) return GLA_ERR_HIP;
+    return GLA_OK;
+  }
   int koff = 0;
   for (int b = 0; b < pl.nkb; ++b) {
     w.K = pl.kb[b];

@@ -42,6 +42,7 @@ struct WalkParams {
   const int32_t *seg_base;     // [N+1] first segment of each packed sequence, or null
   const int32_t *seg_order;    // [seg_slots] segment ids, longest first (packed), or null
   uint32_t *status;            // sticky status word (GLA_STATUS_* bits)
+  int32_t *link;               // single pass: [0] item counter, then one flag per (slot, HV, value slice); zeroed before the launch
   float *o_part;               // [B,T,HV,V] fp32: write the partial output here instead of o, or null
   const float *o_add;          // [B,T,HV,V] fp32: partial output of the other key block, or null
   int32_t T, H, K, V, N;       // H: key heads; K: keys of this launch's block
@@ -68,6 +69,11 @@ hipError_t launch_segment_plan(const WalkParams &p, int32_t *seg_base, int32_t *
 // block is padded with zero keys), 64 or 128 value columns per workgroup
 // (WalkParams::vtile), any V (columns past V are masked)
 hipError_t launch_walk_bf16(bool local_mode, int kd, const WalkParams &p, hipStream_t s);
+// The single pass (summary, scan and outputs in one launch) of the bf16 walker;
+// needs seg_state, seg_decay and a zeroed link table.
+hipError_t launch_fused_bf16(int kd, const WalkParams &p, hipStream_t s);
+// Zeroes n 32-bit words (a kernel, not a memset node, so callers may capture it).
+hipError_t launch_clear(int32_t *words, long long n, hipStream_t s);
 
 // Backward (gla_bwd.hip).  The state tables hold one chunk per slot: chunk c
 // of sequence n is slot first(n) + c, with first(n) = n P (fixed length) or

@@ -725,6 +725,10 @@ __global__ __launch_bounds__(1024) void gla_segment_plan(const int32_t *cu, int 
   }
 }
 
+__global__ __launch_bounds__(256) void gla_clear_words(int32_t *words, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) words[i] = 0;
+}
+
 template <bool BF, int KD, bool GH>
 hipError_t launch_walk_g(bool local_mode, const WalkParams &p, hipStream_t s) {
   const int NV = (p.V + VT - 1) / VT;
@@ -769,6 +773,13 @@ hipError_t launch_state_scan(const WalkParams &p, hipStream_t s) {
   const long long blocks = (long long)p.N * p.HV * per_state;
   if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gla_state_scan, dim3((unsigned)blocks), dim3(256), 0, s, p, per_state);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear(int32_t *words, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const long long blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(gla_clear_words, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, s, words, n);
   return hipGetLastError();
 }
 

@@ -228,8 +228,14 @@ __device__ __forceinline__ void scores(char *smem, const char *sq, const int (&r
 
 // GH: the gate is one decay per value head and token (g [B,T,HV]) instead of one
 // per key; a compile-time choice, so that the per-key walker's code is untouched.
-template <bool OUT, int KD, int VW, bool GH>
-__device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
+// b: the workgroup's index in the (segment, head, value slice) order.
+// FUSED: one of the two walks of the single pass.  Its summary walk keeps the
+// summary in LDS as [K][VW] fp32 at offset 0 instead of storing it to
+// seg_state, and every value slice writes the segment's decay product (the
+// same values).
+template <bool OUT, int KD, int VW, bool GH, bool FUSED = false>
+__device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem, int b) {
+  constexpr bool KEEP = FUSED && !OUT;
   using L = LdsW<KD, OUT, VW>;
   constexpr int KS = L::KS;         // key splits of the state over the 4 matrix waves
   constexpr int CS = 4 / KS;        // column splits
@@ -254,7 +260,6 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
   // ---- (segment, head, value slice) of this workgroup; value slices of one
   // unit are 8 workgroup ids apart so they run on the same XCD and share L2.
   const int NV = (p.V + VW - 1) / VW;
-  const int b = blockIdx.x;
   const int grp = b / (8 * NV), rem = b - grp * (8 * NV);
   const int vt = rem >> 3;
   const int unit = grp * 8 + (rem & 7);
@@ -822,10 +827,11 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
     // segment is formed again from the token recurrence, after every store of
     // the chunk loop; its final state replaces S in the staging area
     __syncthreads();
-    exact_segment<KD, true, OUT>(p, si, h, v0, VW, c_begin, c_end, wave, vt, reinterpret_cast<float *>(smem));
+    exact_segment<KD, true, OUT>(p, si, h, v0, VW, c_begin, c_end, wave, KEEP ? 0 : vt,
+                                 reinterpret_cast<float *>(smem));
     __syncthreads();
   }
-  if (dst != nullptr) {
+  if (dst != nullptr && !KEEP) {
     constexpr int LPR = VW / 4, RPI = 64 / LPR;  // lanes per state row, rows per store
     const int rr = lane / LPR, ch = lane % LPR;
 #pragma unroll
@@ -835,7 +841,7 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
         *reinterpret_cast<f32x4_t *>(dst + (int64_t)row * V + v0 + 4 * ch) = lds_ld<f32x4_t>(smem, 16 * (row * LPR + ch));
     }
   }
-  if (producer && !OUT && !exact && vt == 0 && rg == 0 && key_ok) {
+  if (producer && !OUT && !exact && (KEEP || vt == 0) && rg == 0 && key_ok) {
     const int slot = si.first + si.s;
     *reinterpret_cast<f32x4_t *>(p.seg_decay + ((int64_t)slot * H + h) * nkeys + 4 * cq) =
         f32x4_t{seg_decay[0], seg_decay[1], seg_decay[2], seg_decay[3]};
@@ -845,21 +851,143 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem) {
 template <int KD, int VW, bool GH>
 __global__ __launch_bounds__((LdsW<KD, true, VW>::THREADS), 1) void gla_chunk_output_bf16(WalkParams p) {
   __shared__ __attribute__((aligned(16))) char smem[LdsW<KD, true, VW>::BYTES];
-  walk_bf16<true, KD, VW, GH>(p, smem);
+  walk_bf16<true, KD, VW, GH>(p, smem, blockIdx.x);
 }
 
 template <int KD, int VW, bool GH>
 __global__ __launch_bounds__((LdsW<KD, false, VW>::THREADS), 1) void gla_chunk_local_bf16(WalkParams p) {
   __shared__ __attribute__((aligned(16))) char smem[LdsW<KD, false, VW>::BYTES];
-  walk_bf16<false, KD, VW, GH>(p, smem);
+  walk_bf16<false, KD, VW, GH>(p, smem, blockIdx.x);
+}
+
+// ---------------------------------------------------------------- single pass
+// Summary, scan and outputs in one launch.  Segment s of a sequence publishes
+// its end state P_s = diag(a_s) P_{s-1} + Sigma_s (P_{-1} = h0 or 0; a_s and
+// Sigma_s: the decay product and the summary of its own chunks) in seg_state
+// slot s, and then walks its chunks from P_{s-1} (page "fla/ops/gla/
+// fused_chunk.py", fused_chunk_gla_fwd_kernel, carries the same state through
+// one serial loop; here the loop is cut into segments joined by that
+// recurrence, in the order a decoupled look-back scan uses).
+//
+// Workgroups take (segment, head, value slice) items from a counter in the
+// order of the segment numbering, in which segment s - 1 of a sequence comes
+// before segment s.  A workgroup therefore only ever waits for an item that a
+// running workgroup has already taken, so the chain always moves.  All waves
+// store their rows of P_s; once every store has completed, one wave makes them
+// visible to the device (agent-scope release) and sets the item's flag.  In
+// the successor one wave polls the flag and acquires while a barrier holds the
+// others.  The wait is bounded (WalkParams::wait_polls, with sleeps):
+// when the bound runs out, the status word reports it and the results of the
+// sequence may be wrong, but the kernel ends.  The walk over the segment's
+// chunks follows right after its summary, so its k, v, g are read again from
+// the caches instead of HBM.
+template <int KD, int VW>
+__device__ __forceinline__ void link_segment(const WalkParams &p, const char *smem, int b) {
+  constexpr int NW = LdsW<KD, true, VW>::THREADS / 64;
+  constexpr int LPR = VW / 4, RPI = 64 / LPR;  // lanes per state row, rows per pass
+  constexpr int ITER = (KD / RPI + NW - 1) / NW;  // passes per wave
+  const int NV = (p.V + VW - 1) / VW;
+  const int grp = b / (8 * NV), rem = b - grp * (8 * NV);
+  const int vt = rem >> 3;
+  const int unit = grp * 8 + (rem & 7);
+  if (unit >= p.units) return;
+  const int seg = unit / p.HV, h = unit - seg * p.HV;
+  SegInfo si;
+  if (!locate(p, seg, si) || si.nseg <= 1) return;  // uniform over the workgroup
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = p.HV, V = p.V, nkeys = p.K, v0 = vt * VW;
+  int32_t *flags = p.link + 1;
+  const int64_t slot = (int64_t)si.first + si.s;
+  if (si.s > 0) {
+    // one wave waits and acquires (its cache invalidation covers the
+    // workgroup's later loads); the barrier holds the others until then
+    if (wave == 0) {
+      const int32_t *f = flags + ((slot - 1) * H + h) * NV + vt;
+      int ready = 0;
+      if (lane == 0) {
+        for (int spin = 0; spin < p.wait_polls; ++spin) {
+          if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+            ready = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      if (__builtin_amdgcn_readfirstlane(ready) == 0) report_status(p.status, GLA_STATUS_WAIT_EXHAUSTED, lane);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+  }
+  if (si.s >= si.nseg - 1) return;  // the last segment's end state is the walk's ht
+  const float *prev = nullptr;
+  if (si.s > 0) prev = p.seg_state + ((slot - 1) * H + h) * nkeys * V;
+  else if (p.h0) prev = p.h0 + (((int64_t)si.n * H + h) * p.Kmem + p.koff) * V;
+  float *dst = p.seg_state + (slot * H + h) * nkeys * V;
+  const float *dec = p.seg_decay + (slot * H + h) * nkeys;
+  const int rr = lane / LPR, ch = lane % LPR;
+  const int col = v0 + 4 * ch;
+  // every load of the wave is issued before any store (the stores could alias
+  // the loads as far as the compiler knows, which would serialise them)
+  f32x4_t x[ITER];
+  float a[ITER];
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int row = RPI * (wave + NW * it) + rr;
+    const bool ok = row < nkeys && col < V;
+    x[it] = (ok && prev) ? *reinterpret_cast<const f32x4_t *>(prev + (int64_t)row * V + col)
+                         : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    a[it] = ok ? dec[row] : 0.f;
+  }
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int row = RPI * (wave + NW * it) + rr;
+    if (row < nkeys && col < V) {
+      const f32x4_t sum = lds_ld<f32x4_t>(smem, 16 * (row * LPR + ch));
+      *reinterpret_cast<f32x4_t *>(dst + (int64_t)row * V + col) =
+          f32x4_t{a[it] * x[it][0] + sum[0], a[it] * x[it][1] + sum[1], a[it] * x[it][2] + sum[2],
+                  a[it] * x[it][3] + sum[3]};
+    }
+  }
+  // every wave's stores have completed before the barrier; one wave then
+  // writes the caches back (agent-scope release) and sets the flag
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (wave == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (lane == 0) __hip_atomic_store(flags + (slot * H + h) * NV + vt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <int KD, int VW, bool GH>
-hipError_t launch_g(bool local_mode, const WalkParams &p, hipStream_t s) {
+__global__ __launch_bounds__((LdsW<KD, true, VW>::THREADS), 1) void gla_chunk_fused_bf16(WalkParams p) {
+  static_assert(LdsW<KD, true, VW>::THREADS == LdsW<KD, false, VW>::THREADS, "one block shape for both walks");
+  static_assert(LdsW<KD, false, VW>::BYTES <= LdsW<KD, true, VW>::BYTES, "the output walk's LDS holds both");
+  // the item index passes through a word of the flag area, which the walks
+  // only write after this read (a separate __shared__ variable would move the
+  // walks' LDS offsets off their folded constants)
+  __shared__ __attribute__((aligned(16))) char smem[LdsW<KD, true, VW>::BYTES];
+  constexpr int kItem = LdsW<KD, true, VW>::oBad + 8;
+  if (threadIdx.x == 0)
+    lds_st<int>(smem, kItem, __hip_atomic_fetch_add(p.link, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  __syncthreads();
+  const int b = __builtin_amdgcn_readfirstlane(lds_ld<int>(smem, kItem));  // uniform: the walks' indices stay scalar
+  __syncthreads();
+  walk_bf16<false, KD, VW, GH, true>(p, smem, b);
+  __syncthreads();
+  link_segment<KD, VW>(p, smem, b);
+  __syncthreads();
+  walk_bf16<true, KD, VW, GH, true>(p, smem, b);
+}
+
+template <int KD, int VW, bool GH>
+hipError_t launch_g(int mode, const WalkParams &p, hipStream_t s) {
   const int NV = (p.V + VW - 1) / VW;
   const int groups = (p.units + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * NV));
-  if (local_mode)
+  if (mode == 2)
+    hipLaunchKernelGGL((gla_chunk_fused_bf16<KD, VW, GH>), grid, dim3(LdsW<KD, true, VW>::THREADS), 0, s, p);
+  else if (mode == 1)
     hipLaunchKernelGGL((gla_chunk_local_bf16<KD, VW, GH>), grid, dim3(LdsW<KD, false, VW>::THREADS), 0, s, p);
   else
     hipLaunchKernelGGL((gla_chunk_output_bf16<KD, VW, GH>), grid, dim3(LdsW<KD, true, VW>::THREADS), 0, s, p);
@@ -867,18 +995,27 @@ hipError_t launch_g(bool local_mode, const WalkParams &p, hipStream_t s) {
 }
 
 template <int KD, int VW>
-hipError_t launch_t(bool local_mode, const WalkParams &p, hipStream_t s) {
-  return p.gate_head ? launch_g<KD, VW, true>(local_mode, p, s) : launch_g<KD, VW, false>(local_mode, p, s);
+hipError_t launch_t(int mode, const WalkParams &p, hipStream_t s) {
+  return p.gate_head ? launch_g<KD, VW, true>(mode, p, s) : launch_g<KD, VW, false>(mode, p, s);
+}
+
+hipError_t launch_mode(int mode, int kd, const WalkParams &p, hipStream_t s) {
+  const int vw = p.vtile;
+  if ((vw != 64 && vw != 128) || p.K > kd || p.K % 16 != 0 || p.V % 16 != 0) return hipErrorInvalidValue;
+  if (kd == 128) return vw == 128 ? launch_t<128, 128>(mode, p, s) : launch_t<128, 64>(mode, p, s);
+  if (kd == 64) return vw == 128 ? launch_t<64, 128>(mode, p, s) : launch_t<64, 64>(mode, p, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_walk_bf16(bool local_mode, int kd, const WalkParams &p, hipStream_t s) {
-  const int vw = p.vtile;
-  if ((vw != 64 && vw != 128) || p.K > kd || p.K % 16 != 0 || p.V % 16 != 0) return hipErrorInvalidValue;
-  if (kd == 128) return vw == 128 ? launch_t<128, 128>(local_mode, p, s) : launch_t<128, 64>(local_mode, p, s);
-  if (kd == 64) return vw == 128 ? launch_t<64, 128>(local_mode, p, s) : launch_t<64, 64>(local_mode, p, s);
-  return hipErrorInvalidValue;
+  return launch_mode(local_mode ? 1 : 0, kd, p, s);
+}
+
+hipError_t launch_fused_bf16(int kd, const WalkParams &p, hipStream_t s) {
+  if (p.link == nullptr || p.seg_state == nullptr || p.seg_decay == nullptr) return hipErrorInvalidValue;
+  return launch_mode(2, kd, p, s);
 }
 
 }  // namespace gla

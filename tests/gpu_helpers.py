@@ -31,14 +31,14 @@ def to_device(d, dtype):
     return out
 
 
-def run_gpu(d, dtype, scale=None, output_final_state=True, segment_chunks=0, value_tile=0):
+def run_gpu(d, dtype, scale=None, output_final_state=True, segment_chunks=0, value_tile=0, schedule=0):
     """One forward through the C ABI; asserts that the workspace status word stayed clear."""
     import torch
     import chunkwise_gated_linear_amd as gla
     t = to_device(d, dtype)
     call = gla.GlaCall(t["q"], t["k"], t["v"], t["g"], h0=t["h0"], cu_seqlens=t["cu_seqlens"],
                        scale=scale, output_final_state=output_final_state,
-                       segment_chunks=segment_chunks, value_tile=value_tile)
+                       segment_chunks=segment_chunks, value_tile=value_tile, schedule=schedule)
     o, ht = call.o, call.ht
     torch.cuda.synchronize()
     assert call.status() == 0, f"status word {call.status():#x} after the call"

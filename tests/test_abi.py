@@ -89,6 +89,8 @@ def call_noalloc(lib, p, q=FAKE, k=FAKE, v=FAKE, g=FAKE, cu=None, o=FAKE):
     (dict(HV=4), BAD_SHAPE),            # value heads must be a multiple of the key heads
     (dict(HV=-3), BAD_SHAPE),
     (dict(gate=2), UNSUPPORTED),
+    (dict(schedule=3), UNSUPPORTED),
+    (dict(schedule=-1), UNSUPPORTED),
 ])
 def test_invalid_problems_are_rejected(lib, kw, code):
     p = prob(**kw)
@@ -113,13 +115,24 @@ WS_HEADER = 256  # status word + padding at the start of every workspace
 
 
 def test_workspace_size_and_check(lib):
-    # B=2, T=1000 -> 16 chunks per sequence; 2 chunks per segment -> 8 segments each
-    p = prob(T=1000, K=64, V=128, H=3, segment_chunks=2)
+    # B=2, T=1000 -> 16 chunks per sequence; 2 chunks per segment -> 8 segments each.
+    # Three passes: segment states and decay products
+    p = prob(T=1000, K=64, V=128, H=3, segment_chunks=2, schedule=1)
     slots = 2 * 8
     expect = WS_HEADER + up(slots * 3 * 64 * 128 * 4) + up(slots * 3 * 64 * 4)
     assert lib.gla_fwd_workspace_bytes(ctypes.byref(p)) == expect
+    # one pass (the automatic schedule of the bf16 walker): also an item counter
+    # and one flag per (segment, head, value slice)
+    link = up((1 + slots * 3) * 4)
+    for sched in (0, 2):
+        p1 = prob(T=1000, K=64, V=128, H=3, segment_chunks=2, schedule=sched)
+        assert lib.gla_fwd_workspace_bytes(ctypes.byref(p1)) == expect + link
+    # fp32 runs three passes whatever the schedule
+    p2 = prob(T=1000, K=64, V=128, H=3, segment_chunks=2, schedule=2, dtype=gla.GLA_F32)
+    assert lib.gla_fwd_workspace_bytes(ctypes.byref(p2)) == expect
     assert call(lib, p, ws=None, ws_bytes=0) == WORKSPACE
     assert call(lib, p, ws=FAKE, ws_bytes=expect - 1) == WORKSPACE
+    assert call(lib, p1, ws=FAKE, ws_bytes=expect + link - 1) == WORKSPACE
     # one segment per sequence: the status header only
     p1 = prob(T=1000, segment_chunks=16)
     assert lib.gla_fwd_workspace_bytes(ctypes.byref(p1)) == WS_HEADER
@@ -128,6 +141,8 @@ def test_workspace_size_and_check(lib):
     pv = prob(B=1, T=1000, n_seqs=5, packed=1, segment_chunks=3)
     slots_v = 5 + -(-(16 + 5) // 3)
     expect_v = WS_HEADER + up(slots_v * 3 * 64 * 128 * 4) + up(slots_v * 3 * 64 * 4) + up((6 + slots_v) * 4)
+    assert lib.gla_fwd_workspace_bytes(ctypes.byref(pv)) == expect_v + up((1 + slots_v * 3) * 4)
+    pv.schedule = 1
     assert lib.gla_fwd_workspace_bytes(ctypes.byref(pv)) == expect_v
 
 
@@ -159,7 +174,7 @@ def test_value_heads_size_the_workspace(lib):
     p = prob(T=1000, K=64, V=128, H=3, HV=6, segment_chunks=2, gate=1)
     slots = 2 * 8
     assert lib.gla_fwd_workspace_bytes(ctypes.byref(p)) == (WS_HEADER + up(slots * 6 * 64 * 128 * 4)
-                                                           + up(slots * 6 * 64 * 4))
+                                                           + up(slots * 6 * 64 * 4) + up((1 + slots * 6) * 4))
 
 
 def test_status_strings(lib):
@@ -196,6 +211,8 @@ def call_bwd(lib, p, ws=FAKE, ws_bytes=1 << 40, cu=None, dq=FAKE, do=FAKE):
     (dict(n_seqs=3), BAD_SHAPE),
     (dict(HV=4), BAD_SHAPE),
     (dict(gate=2), UNSUPPORTED),
+    (dict(schedule=3), UNSUPPORTED),
+    (dict(schedule=-1), UNSUPPORTED),
 ])
 def test_backward_rejects_invalid_problems(lib, kw, code):
     p = prob(**kw)
