@@ -138,7 +138,7 @@ Plan make_plan(const gla_problem *p, bool varlen) {
   // one pass with chained segments (the bf16 walker with one key block) unless
   // three passes are asked for: it skips the scan launch, and with packed
   // sequences its longer segments do better than the three passes' shorter
-  // ones (U[256, 4096] x 16 sequences: 233 against 276 us at best)
+  // ones (16 sequences of U[256, 4096] tokens: 221 against 276 us at best)
   const bool single = fast && p->schedule != 1;
   const int NV = pl.NV;
   const long long chunks_total = ((long long)p->T + kChunk - 1) / kChunk;  // varlen: packed axis
@@ -164,10 +164,11 @@ Plan make_plan(const gla_problem *p, bool varlen) {
       // summary work of cutting more sequences (measured optimum on the
       // 16-sequence U[256, 4096] workload)
       const long long work = (chunks_total + pl.N) * H * NV;  // chunk-slices to spread
-      // one pass: about 3 workgroups per 4 compute units (fewer, longer
-      // segments: each costs a walk start-up and a link in the chain; measured
-      // optimum on the same workload, 48-chunk segments)
-      const long long tgt = single ? (3LL * device_cu_count()) / 4
+      // one pass: about 2 workgroups per 3 compute units (fewer, longer
+      // segments: each costs a walk start-up and a link in the chain; on the
+      // same workload 48- to 52-chunk segments measured best, 221 us, against
+      // 236 us at 42 to 47 and 258 us unsegmented)
+      const long long tgt = single ? (2LL * device_cu_count()) / 3
                                    : vtile == 128 ? (3LL * device_cu_count()) / 2 : target;
       long long r = (work + tgt - 1) / tgt;
       if (r < 4) r = 4;
