@@ -16,9 +16,10 @@ an initial state, dh0, for seeded gradients do of o and dht of ht), with the
 same line format, the backward's own algorithmic bytes and flops, and the fp64
 backward oracle as the CPU baseline.
 
-A step is one full forward (every kernel of the path: segment plan, segment
-summaries, state scan, output walk, as the library schedules them) over the
-whole batch, with inputs resident in device memory.  Untimed steps for
+A step is one full forward (every kernel of the path as the library schedules
+it: for segmented sequences the segment plan or a table clear and the single
+pass, or with --schedule 1 segment summaries, state scan and output walk) over
+the whole batch, with inputs resident in device memory.  Untimed steps for
 --settle-ms (the GPU clock ramps up over the first tens of milliseconds of
 load), W untimed warmup steps, then exactly K timed steps between two device
 synchronisations; one JSON line is printed.

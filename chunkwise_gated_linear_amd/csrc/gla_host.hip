@@ -135,11 +135,14 @@ Plan make_plan(const gla_problem *p, bool varlen) {
   }
   pl.vtile = vtile;
   pl.NV = (p->V + vtile - 1) / vtile;
-  // one pass with chained segments (the bf16 walker with one key block) unless
-  // three passes are asked for: it skips the scan launch, and with packed
-  // sequences its longer segments do better than the three passes' shorter
-  // ones (16 sequences of U[256, 4096] tokens: 221 against 276 us at best)
-  const bool single = fast && p->schedule != 1;
+  // one pass with chained segments (the bf16 walker with one key block): on
+  // request, and by default for packed sequences, where its longer segments do
+  // better than the three passes' shorter ones (16 sequences of U[256, 4096]
+  // tokens: 224 against 250 us).  Fixed-length sequences default to three
+  // passes: with one segment per compute unit every segment runs at once, and
+  // the single pass's chain of start states costs what the scan launch saves
+  // (B=1, H=32, T=65536: 998 against 987 us).
+  const bool single = fast && (p->schedule == 2 || (p->schedule == 0 && varlen));
   const int NV = pl.NV;
   const long long chunks_total = ((long long)p->T + kChunk - 1) / kChunk;  // varlen: packed axis
   const long long chunks_seq = chunks_total;  // longest possible sequence
@@ -204,7 +207,10 @@ Plan make_plan(const gla_problem *p, bool varlen) {
   }
   if (pl.nkb == 2) pl.ws_opart = (size_t)p->B * p->T * H * p->V * sizeof(float);
   pl.fused = pl.segmented && fast && single;
-  if (pl.fused) pl.ws_link = (size_t)(1 + slots * H * NV) * sizeof(int32_t);  // counter + one flag per item
+  if (pl.fused) {
+    pl.ws_link = (size_t)(1 + slots * H * NV) * sizeof(int32_t);  // counter + one flag per item
+    pl.ok = pl.ok && 1 + slots * H * NV <= INT_MAX;
+  }
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   pl.ws_total = kHeaderBytes + up(pl.ws_state) + up(pl.ws_decay) + up(pl.ws_base) + up(pl.ws_opart) + up(pl.ws_link);
   return pl;
@@ -250,11 +256,15 @@ gla_status run_forward(const gla_problem *p, const Plan &pl, const void *q, cons
   w.wait_polls = p->wait_limit == 0 ? gla::kDefaultWaitPolls : (p->wait_limit < 0 ? 0 : p->wait_limit);
   w.scale = p->scale;
 
-  if (seg_base && gla::launch_segment_plan(w, seg_base, seg_base + N + 1, s) != hipSuccess) return GLA_ERR_HIP;
+  const long long nlink = (long long)(pl.ws_link / sizeof(int32_t));
+  // packed sequences: the segment plan also zeroes the single pass's link table
+  if (seg_base && gla::launch_segment_plan(w, seg_base, seg_base + N + 1, s, pl.fused ? w.link : nullptr,
+                                           pl.fused ? (int)nlink : 0) != hipSuccess)
+    return GLA_ERR_HIP;
   if (pl.fused) {  // one key block (the bf16 walker)
     w.K = pl.kb[0];
     w.koff = 0;
-    if (gla::launch_clear(w.link, (long long)(pl.ws_link / sizeof(int32_t)), s) != hipSuccess) return GLA_ERR_HIP;
+    if (!seg_base && gla::launch_clear(w.link, nlink, s) != hipSuccess) return GLA_ERR_HIP;
     if (gla::launch_fused_bf16(kernel_key_width(true, bf, w.K), w, s) != hipSuccess) return GLA_ERR_HIP;
     return GLA_OK;
   }

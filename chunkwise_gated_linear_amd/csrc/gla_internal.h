@@ -64,7 +64,10 @@ struct WalkParams {
 // split K; kd is the padded key width of the instantiation (16, 32, 64, 128).
 hipError_t launch_walk_general(bool local_mode, bool bf16, int kd, const WalkParams &p, hipStream_t s);
 hipError_t launch_state_scan(const WalkParams &p, hipStream_t s);
-hipError_t launch_segment_plan(const WalkParams &p, int32_t *seg_base, int32_t *seg_order, hipStream_t s);
+// The segment table of packed sequences; it also zeroes `nclear` words at
+// `clear` (the single pass's link table), or none.
+hipError_t launch_segment_plan(const WalkParams &p, int32_t *seg_base, int32_t *seg_order, hipStream_t s,
+                               int32_t *clear = nullptr, int nclear = 0);
 // bf16 walker (gla_walk_bf16.hip): key widths kd in {64, 128} (a narrower key
 // block is padded with zero keys), 64 or 128 value columns per workgroup
 // (WalkParams::vtile), any V (columns past V are masked)

@@ -649,11 +649,13 @@ __device__ __forceinline__ int seg_count(int len, int R) {
 }
 
 __global__ __launch_bounds__(1024) void gla_segment_plan(const int32_t *cu, int N, int T, int R, int seg_slots,
-                                                         int32_t *seg_base, int32_t *seg_order) {
+                                                         int32_t *seg_base, int32_t *seg_order, int32_t *clear,
+                                                         int nclear) {
   __shared__ int32_t part[1024];
   __shared__ int32_t carry;
   __shared__ int32_t bucket[kOrderBuckets];
   const int tid = threadIdx.x;
+  for (int i = tid; i < nclear; i += 1024) clear[i] = 0;  // the single pass's link table
   if (tid == 0) {
     carry = 0;
     seg_base[0] = 0;
@@ -783,9 +785,10 @@ hipError_t launch_clear(int32_t *words, long long n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_segment_plan(const WalkParams &p, int32_t *seg_base, int32_t *seg_order, hipStream_t s) {
+hipError_t launch_segment_plan(const WalkParams &p, int32_t *seg_base, int32_t *seg_order, hipStream_t s,
+                               int32_t *clear, int nclear) {
   hipLaunchKernelGGL(gla_segment_plan, dim3(1), dim3(1024), 0, s, p.cu, p.N, p.T, p.R, p.seg_slots, seg_base,
-                     seg_order);
+                     seg_order, clear, nclear);
   return hipGetLastError();
 }
 

@@ -104,10 +104,11 @@ typedef struct gla_problem {
                       /* GLA_STATUS_WAIT_EXHAUSTED at once (a test hook)               */
     int32_t HV;       /* value heads (v, g, o, h0, ht): 0 means H; else a multiple of H */
     int32_t gate;     /* gla_gate: layout of g                                        */
-    int32_t schedule; /* segmented sequences: 0 automatic; 1 three passes (summaries, */
-                      /* a scan of them, outputs); 2 one pass, segments chained by    */
-                      /* their end states (bf16 with K <= 128, else three passes).    */
-                      /* A tuning choice: results agree to rounding.                  */
+    int32_t schedule; /* segmented sequences: 0 automatic (one pass for packed bf16  */
+                      /* sequences, else three); 1 three passes (summaries, a scan of */
+                      /* them, outputs); 2 one pass, segments chained by their end    */
+                      /* states (bf16 with K <= 128, else three passes).  A tuning    */
+                      /* choice: results agree to rounding.                           */
 } gla_problem;
 
 /*

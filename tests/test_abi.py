@@ -121,12 +121,13 @@ def test_workspace_size_and_check(lib):
     slots = 2 * 8
     expect = WS_HEADER + up(slots * 3 * 64 * 128 * 4) + up(slots * 3 * 64 * 4)
     assert lib.gla_fwd_workspace_bytes(ctypes.byref(p)) == expect
-    # one pass (the automatic schedule of the bf16 walker): also an item counter
-    # and one flag per (segment, head, value slice)
+    # fixed-length sequences default to three passes
+    p0 = prob(T=1000, K=64, V=128, H=3, segment_chunks=2, schedule=0)
+    assert lib.gla_fwd_workspace_bytes(ctypes.byref(p0)) == expect
+    # one pass: also an item counter and one flag per (segment, head, value slice)
     link = up((1 + slots * 3) * 4)
-    for sched in (0, 2):
-        p1 = prob(T=1000, K=64, V=128, H=3, segment_chunks=2, schedule=sched)
-        assert lib.gla_fwd_workspace_bytes(ctypes.byref(p1)) == expect + link
+    p1 = prob(T=1000, K=64, V=128, H=3, segment_chunks=2, schedule=2)
+    assert lib.gla_fwd_workspace_bytes(ctypes.byref(p1)) == expect + link
     # fp32 runs three passes whatever the schedule
     p2 = prob(T=1000, K=64, V=128, H=3, segment_chunks=2, schedule=2, dtype=gla.GLA_F32)
     assert lib.gla_fwd_workspace_bytes(ctypes.byref(p2)) == expect
@@ -173,6 +174,9 @@ def test_value_heads_size_the_workspace(lib):
     # states and segment summaries exist per value head
     p = prob(T=1000, K=64, V=128, H=3, HV=6, segment_chunks=2, gate=1)
     slots = 2 * 8
+    assert lib.gla_fwd_workspace_bytes(ctypes.byref(p)) == (WS_HEADER + up(slots * 6 * 64 * 128 * 4)
+                                                           + up(slots * 6 * 64 * 4))
+    p.schedule = 2
     assert lib.gla_fwd_workspace_bytes(ctypes.byref(p)) == (WS_HEADER + up(slots * 6 * 64 * 128 * 4)
                                                            + up(slots * 6 * 64 * 4) + up((1 + slots * 6) * 4))
 
