@@ -189,9 +189,32 @@ __device__ __forceinline__ void gate_stage(const GateRows<KD, GH, NT> &gr, float
   }
 }
 
+// Eight floats as three bf16 terms (8 lanes each, packed pairs): hi = the
+// nearest bf16, mid = the nearest bf16 of x - hi, lo = the nearest bf16 of
+// x - hi - mid.  Each remainder is exact in fp32, and hi + mid + lo equals x
+// to fp32 precision.
+__device__ __forceinline__ void split8_3(const float (&x)[8], u32x4_t &hi, u32x4_t &mid, u32x4_t &lo) {
+  float r1[8], r2[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    hi[q] = pack_bf16(x[2 * q], x[2 * q + 1]);
+    r1[2 * q] = x[2 * q] - bf_lo(hi[q]);
+    r1[2 * q + 1] = x[2 * q + 1] - bf_hi(hi[q]);
+    mid[q] = pack_bf16(r1[2 * q], r1[2 * q + 1]);
+    r2[2 * q] = r1[2 * q] - bf_lo(mid[q]);
+    r2[2 * q + 1] = r1[2 * q + 1] - bf_hi(mid[q]);
+    lo[q] = pack_bf16(r2[2 * q], r2[2 * q + 1]);
+  }
+}
+
+// Eight floats that are bf16 values, packed (exact).
+__device__ __forceinline__ u32x4_t pack8(const float (&x)[8]) {
+  return u32x4_t{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
+}
+
 // ---------------------------------------------------------------- gla_bwd_local
-// Chunk summaries of the state and of its gradient, on fp32 MFMA over the
-// chunk's 64 tokens.  Task t < 2 slots HV: the first half forms, for chunk
+// Chunk summaries of the state and of its gradient over the chunk's 64
+// tokens (bf16 MFMA on split operands for bf16 inputs, fp32 MFMA for fp32).  Task t < 2 slots HV: the first half forms, for chunk
 // slot t / HV and value head t % HV,
 //   fstate[slot][hv] = sum_j (k_j e^{G_last - G_j}) v_j^T      (K x V)
 //   ddecay[slot][hv] = e^{G_last}                               (K)
@@ -309,23 +332,60 @@ __global__ __launch_bounds__(256, 2) void gla_bwd_local(BwdParams bp) {
     for (int a = 0; a < NKB; ++a)
 #pragma unroll
       for (int b = 0; b < NVB; ++b) acc[a][b] = zero4();
+    if constexpr (BF) {
+      // bf16 inputs: the value-side rows (v or do) are exact in bf16, the gated
+      // key-side rows are split into three bf16 terms (fp32 accuracy); 32
+      // tokens per v_mfma_f32_16x16x32_bf16, each lane 8 consecutive tokens of
+      // one column
+      // lane indices through an opaque copy: the compiler would otherwise hoist
+      // every swizzled LDS address out of the task loop and keep them live
+      // beside the next task's rows
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int m16 = ln & 15, mg = ln >> 4;
 #pragma unroll 1
-    for (int ib = 0; ib < 4; ++ib) {  // not unrolled: keeps the operand registers of one row block
-      float xa[NKB][4], yb[NVB][4];
+      for (int tb = 0; tb < 2; ++tb) {
+        u32x4_t xh[NKB], xm[NKB], xl[NKB];
 #pragma unroll
-      for (int a = 0; a < NKB; ++a)
+        for (int a = 0; a < NKB; ++a) {
+          float x8[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) xa[a][r] = sA[swz<KD>(ib * 16 + 4 * lg + r, (wave * NKB + a) * 16 + l16)];
+          for (int e = 0; e < 8; ++e) x8[e] = sA[swz<KD>(tb * 32 + 8 * mg + e, (wave * NKB + a) * 16 + m16)];
+          split8_3(x8, xh[a], xm[a], xl[a]);
+        }
 #pragma unroll
-      for (int b = 0; b < NVB; ++b)
+        for (int b = 0; b < NVB; ++b) {
+          float y8[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) yb[b][r] = sB[swz<VD>(ib * 16 + 4 * lg + r, b * 16 + l16)];
+          for (int e = 0; e < 8; ++e) y8[e] = sB[swz<VD>(tb * 32 + 8 * mg + e, b * 16 + m16)];
+          const u32x4_t yv = pack8(y8);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+          for (int a = 0; a < NKB; ++a) {
+            acc[a][b] = mfma_bf(yv, xl[a], acc[a][b]);
+            acc[a][b] = mfma_bf(yv, xm[a], acc[a][b]);
+            acc[a][b] = mfma_bf(yv, xh[a], acc[a][b]);
+          }
+        }
+      }
+    } else {
+#pragma unroll 1
+      for (int ib = 0; ib < 4; ++ib) {  // not unrolled: keeps the operand registers of one row block
+        float xa[NKB][4], yb[NVB][4];
 #pragma unroll
         for (int a = 0; a < NKB; ++a)
 #pragma unroll
-          for (int b = 0; b < NVB; ++b) acc[a][b] = mfma_f32(yb[b][r], xa[a][r], acc[a][b]);
+          for (int r = 0; r < 4; ++r) xa[a][r] = sA[swz<KD>(ib * 16 + 4 * lg + r, (wave * NKB + a) * 16 + l16)];
+#pragma unroll
+        for (int b = 0; b < NVB; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) yb[b][r] = sB[swz<VD>(ib * 16 + 4 * lg + r, b * 16 + l16)];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int a = 0; a < NKB; ++a)
+#pragma unroll
+            for (int b = 0; b < NVB; ++b) acc[a][b] = mfma_f32(yb[b][r], xa[a][r], acc[a][b]);
+      }
     }
     float *dst = (cgrad ? bp.dstate : bp.fstate) + ((int64_t)slot * p.HV + chv) * p.K * p.V;
 #pragma unroll
@@ -419,24 +479,6 @@ __global__ __launch_bounds__(256) void gla_bwd_scan(BwdParams bp, int per_state)
       }
   }
   if (bp.dh0) *reinterpret_cast<f32x4_t *>(bp.dh0 + sidx) = e;
-}
-
-// Eight floats as three bf16 terms (8 lanes each, packed pairs): hi = the
-// nearest bf16, mid = the nearest bf16 of x - hi, lo = the nearest bf16 of
-// x - hi - mid.  Each remainder is exact in fp32, and hi + mid + lo equals x
-// to fp32 precision.
-__device__ __forceinline__ void split8_3(const float (&x)[8], u32x4_t &hi, u32x4_t &mid, u32x4_t &lo) {
-  float r1[8], r2[8];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    hi[q] = pack_bf16(x[2 * q], x[2 * q + 1]);
-    r1[2 * q] = x[2 * q] - bf_lo(hi[q]);
-    r1[2 * q + 1] = x[2 * q + 1] - bf_hi(hi[q]);
-    mid[q] = pack_bf16(r1[2 * q], r1[2 * q + 1]);
-    r2[2 * q] = r1[2 * q] - bf_lo(mid[q]);
-    r2[2 * q + 1] = r1[2 * q + 1] - bf_hi(mid[q]);
-    lo[q] = pack_bf16(r2[2 * q], r2[2 * q + 1]);
-  }
 }
 
 // ---------------------------------------------------------------- dq / dk stores
