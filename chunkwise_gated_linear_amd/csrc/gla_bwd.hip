@@ -207,6 +207,27 @@ __device__ __forceinline__ void split8_3(const float (&x)[8], u32x4_t &hi, u32x4
   }
 }
 
+// Eight floats as two bf16 terms: hi = the nearest bf16, lo = the nearest bf16
+// of the exact remainder x - hi (about 16 significant bits together).
+__device__ __forceinline__ void split8_2(const float (&x)[8], u32x4_t &hi, u32x4_t &lo) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    hi[q] = pack_bf16(x[2 * q], x[2 * q + 1]);
+    lo[q] = pack_bf16(x[2 * q] - bf_lo(hi[q]), x[2 * q + 1] - bf_hi(hi[q]));
+  }
+}
+
+// Eight consecutive floats of an LDS row (two swizzled quads).
+template <int W>
+__device__ __forceinline__ void lds8(const float *buf, int row, int col, float (&x)[8]) {
+  const f32x4_t a = lds4<W>(buf, row, col), b = lds4<W>(buf, row, col + 4);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    x[r] = a[r];
+    x[4 + r] = b[r];
+  }
+}
+
 // Eight floats that are bf16 values, packed (exact).
 __device__ __forceinline__ u32x4_t pack8(const float (&x)[8]) {
   return u32x4_t{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
@@ -644,19 +665,44 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
       int ib, jb;
       tri_tile(idx, ib, jb);
       f32x4_t a = zero4(), d = zero4();
+      if constexpr (BF) {
+        // A feeds dv only (held to the bf16 rule): q e^G and k e^-G split into
+        // bf16 hi + lo, three products.  do and v are exact in bf16: dA' is
+        // one product per 32 columns.
+#pragma unroll 2
+        for (int k0 = 0; k0 < KD; k0 += 32) {
+          float q8[8], k8[8];
+          lds8<KD>(sQ, ib * 16 + l16, k0 + 8 * lg, q8);
+          lds8<KD>(sK, jb * 16 + l16, k0 + 8 * lg, k8);
+          u32x4_t qh, ql, kh, kl;
+          split8_2(q8, qh, ql);
+          split8_2(k8, kh, kl);
+          a = mfma_bf(qh, kl, a);
+          a = mfma_bf(ql, kh, a);
+          a = mfma_bf(qh, kh, a);
+        }
+#pragma unroll 2
+        for (int v0 = 0; v0 < VD; v0 += 32) {
+          float o8[8], w8[8];
+          lds8<VD>(sO, ib * 16 + l16, v0 + 8 * lg, o8);
+          lds8<VD>(sV, jb * 16 + l16, v0 + 8 * lg, w8);
+          d = mfma_bf(pack8(o8), pack8(w8), d);
+        }
+      } else {
 #pragma unroll 4
-      for (int k0 = 0; k0 < KD; k0 += 16) {
-        const f32x4_t q4 = lds4<KD>(sQ, ib * 16 + l16, k0 + 4 * lg);
-        const f32x4_t k4 = lds4<KD>(sK, jb * 16 + l16, k0 + 4 * lg);
+        for (int k0 = 0; k0 < KD; k0 += 16) {
+          const f32x4_t q4 = lds4<KD>(sQ, ib * 16 + l16, k0 + 4 * lg);
+          const f32x4_t k4 = lds4<KD>(sK, jb * 16 + l16, k0 + 4 * lg);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) a = mfma_f32(q4[r], k4[r], a);
-      }
+          for (int r = 0; r < 4; ++r) a = mfma_f32(q4[r], k4[r], a);
+        }
 #pragma unroll 4
-      for (int v0 = 0; v0 < VD; v0 += 16) {
-        const f32x4_t o4 = lds4<VD>(sO, ib * 16 + l16, v0 + 4 * lg);
-        const f32x4_t w4 = lds4<VD>(sV, jb * 16 + l16, v0 + 4 * lg);
+        for (int v0 = 0; v0 < VD; v0 += 16) {
+          const f32x4_t o4 = lds4<VD>(sO, ib * 16 + l16, v0 + 4 * lg);
+          const f32x4_t w4 = lds4<VD>(sV, jb * 16 + l16, v0 + 4 * lg);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) d = mfma_f32(o4[r], w4[r], d);
+          for (int r = 0; r < 4; ++r) d = mfma_f32(o4[r], w4[r], d);
+        }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -783,24 +829,63 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
     __syncthreads();  // dA' visible
 
     // ---- dv += (k e^{G_last - G}) E_c, store dv
-#pragma unroll 2
-    for (int k0 = 0; k0 < KD; k0 += 16) {
-      const f32x4_t el4 = *reinterpret_cast<const f32x4_t *>(sEl + k0 + 4 * lg);
-      float ev[NVB][4];
+    if constexpr (BF) {
+      // both operands computed: bf16 hi + lo each, three products (dv is held
+      // to the bf16 rule)
+#pragma unroll 1
+      for (int k0 = 0; k0 < KD; k0 += 32) {
+        u32x4_t eh[NVB], elo[NVB];
 #pragma unroll
-      for (int b = 0; b < NVB; ++b)
+        for (int b = 0; b < NVB; ++b) {
+          float e8[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int krow = k0 + 4 * lg + r, col = vb0 + b * 16 + l16;
-          ev[b][r] = (krow < p.K && col < p.V) ? Ec[(int64_t)krow * p.V + col] : 0.f;
+          for (int e = 0; e < 8; ++e) {
+            const int krow = k0 + 8 * lg + e, col = vb0 + b * 16 + l16;
+            e8[e] = (krow < p.K && col < p.V) ? Ec[(int64_t)krow * p.V + col] : 0.f;
+          }
+          split8_2(e8, eh[b], elo[b]);
         }
+        const f32x4_t el0 = *reinterpret_cast<const f32x4_t *>(sEl + k0 + 8 * lg);
+        const f32x4_t el1 = *reinterpret_cast<const f32x4_t *>(sEl + k0 + 8 * lg + 4);
 #pragma unroll
-      for (int j = 0; j < NJB; ++j) {
-        const f32x4_t k4 = lds4<KD>(sK, (jb0 + j) * 16 + l16, k0 + 4 * lg) * el4;
+        for (int j = 0; j < NJB; ++j) {
+          float k8[8];
+          lds8<KD>(sK, (jb0 + j) * 16 + l16, k0 + 8 * lg, k8);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            k8[r] *= el0[r];
+            k8[4 + r] *= el1[r];
+          }
+          u32x4_t kh, kl;
+          split8_2(k8, kh, kl);
+#pragma unroll
+          for (int b = 0; b < NVB; ++b) {
+            dv[b][j] = mfma_bf(kh, elo[b], dv[b][j]);
+            dv[b][j] = mfma_bf(kl, eh[b], dv[b][j]);
+            dv[b][j] = mfma_bf(kh, eh[b], dv[b][j]);
+          }
+        }
+      }
+    } else {
+#pragma unroll 2
+      for (int k0 = 0; k0 < KD; k0 += 16) {
+        const f32x4_t el4 = *reinterpret_cast<const f32x4_t *>(sEl + k0 + 4 * lg);
+        float ev[NVB][4];
 #pragma unroll
         for (int b = 0; b < NVB; ++b)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) dv[b][j] = mfma_f32(k4[r], ev[b][r], dv[b][j]);
+          for (int r = 0; r < 4; ++r) {
+            const int krow = k0 + 4 * lg + r, col = vb0 + b * 16 + l16;
+            ev[b][r] = (krow < p.K && col < p.V) ? Ec[(int64_t)krow * p.V + col] : 0.f;
+          }
+#pragma unroll
+        for (int j = 0; j < NJB; ++j) {
+          const f32x4_t k4 = lds4<KD>(sK, (jb0 + j) * 16 + l16, k0 + 4 * lg) * el4;
+#pragma unroll
+          for (int b = 0; b < NVB; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dv[b][j] = mfma_f32(k4[r], ev[b][r], dv[b][j]);
+        }
       }
     }
 #pragma unroll
