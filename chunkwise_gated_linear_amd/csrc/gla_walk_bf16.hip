@@ -228,6 +228,29 @@ __device__ __forceinline__ void scores(char *smem, const char *sq, const int (&r
 
 // GH: the gate is one decay per value head and token (g [B,T,HV]) instead of one
 // per key; a compile-time choice, so that the per-key walker's code is untouched.
+// Device-coherent accesses for data that one workgroup publishes to another
+// within a launch: agent-scope atomic loads and stores, which no compute unit
+// or die keeps a private cached copy of (plain accesses would rely on cache
+// write-back and invalidation reaching every line of the other die's L2).
+__device__ __forceinline__ float ld_agent(const float *p) {
+  return __uint_as_float(
+      __hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ f32x4_t ld_agent4(const float *p) {
+  const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x4_t{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)), __uint_as_float((uint32_t)b),
+                 __uint_as_float((uint32_t)(b >> 32))};
+}
+__device__ __forceinline__ void st_agent4(float *p, const f32x4_t &v) {
+  uint64_t *q = reinterpret_cast<uint64_t *>(p);
+  const uint64_t a = (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32);
+  const uint64_t b = (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32);
+  __hip_atomic_store(q, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // b: the workgroup's index in the (segment, head, value slice) order.
 // FUSED: one of the two walks of the single pass.  Its summary walk keeps the
 // summary in LDS as [K][VW] fp32 at offset 0 instead of storing it to
@@ -311,7 +334,11 @@ __device__ __forceinline__ void walk_bf16(const WalkParams &p, char *smem, int b
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = KH * kh + 16 * kt + 4 * lg + r, col = v0 + VQ * cw + 16 * nt + l16;
-          S[kt][nt][r] = (src && row < nkeys && col < V) ? src[(int64_t)row * V + col] : 0.f;
+          const bool in = src && row < nkeys && col < V;
+          // a start state published by another workgroup of the same launch
+          // (the single pass) is read device-coherently
+          if (FUSED && si.s > 0) S[kt][nt][r] = in ? ld_agent(src + (int64_t)row * V + col) : 0.f;
+          else S[kt][nt][r] = in ? src[(int64_t)row * V + col] : 0.f;
         }
   }
   if (tid == 0) lds_st<int>(smem + L::oBad, 0, 0);
@@ -873,10 +900,11 @@ __global__ __launch_bounds__((LdsW<KD, false, VW>::THREADS), 1) void gla_chunk_l
 // order of the segment numbering, in which segment s - 1 of a sequence comes
 // before segment s.  A workgroup therefore only ever waits for an item that a
 // running workgroup has already taken, so the chain always moves.  All waves
-// store their rows of P_s; once every store has completed, one wave makes them
-// visible to the device (agent-scope release) and sets the item's flag.  In
-// the successor one wave polls the flag and acquires while a barrier holds the
-// others.  The wait is bounded (WalkParams::wait_polls, with sleeps):
+// store their rows of P_s with device-coherent (agent-scope atomic) stores;
+// once every store has completed, one wave releases at agent scope and sets
+// the item's flag.  In the successor one wave polls the flag and acquires
+// while a barrier holds the others, and P_{s-1} is read with device-coherent
+// loads (by the link and by the walk's start-state load).  The wait is bounded (WalkParams::wait_polls, with sleeps):
 // when the bound runs out, the status word reports it and the results of the
 // sequence may be wrong, but the kernel ends.  The walk over the segment's
 // chunks follows right after its summary, so its k, v, g are read again from
@@ -935,7 +963,10 @@ __device__ __forceinline__ void link_segment(const WalkParams &p, const char *sm
   for (int it = 0; it < ITER; ++it) {
     const int row = RPI * (wave + NW * it) + rr;
     const bool ok = row < nkeys && col < V;
-    x[it] = (ok && prev) ? *reinterpret_cast<const f32x4_t *>(prev + (int64_t)row * V + col)
+    // the predecessor's state comes from another workgroup (device-coherent
+    // loads); h0 is an input
+    x[it] = (ok && prev) ? (si.s > 0 ? ld_agent4(prev + (int64_t)row * V + col)
+                                     : *reinterpret_cast<const f32x4_t *>(prev + (int64_t)row * V + col))
                          : f32x4_t{0.f, 0.f, 0.f, 0.f};
     a[it] = ok ? dec[row] : 0.f;
   }
@@ -944,9 +975,9 @@ __device__ __forceinline__ void link_segment(const WalkParams &p, const char *sm
     const int row = RPI * (wave + NW * it) + rr;
     if (row < nkeys && col < V) {
       const f32x4_t sum = lds_ld<f32x4_t>(smem, 16 * (row * LPR + ch));
-      *reinterpret_cast<f32x4_t *>(dst + (int64_t)row * V + col) =
-          f32x4_t{a[it] * x[it][0] + sum[0], a[it] * x[it][1] + sum[1], a[it] * x[it][2] + sum[2],
-                  a[it] * x[it][3] + sum[3]};
+      st_agent4(dst + (int64_t)row * V + col,
+                f32x4_t{a[it] * x[it][0] + sum[0], a[it] * x[it][1] + sum[1], a[it] * x[it][2] + sum[2],
+                        a[it] * x[it][3] + sum[3]});
     }
   }
   // every wave's stores have completed before the barrier; one wave then
