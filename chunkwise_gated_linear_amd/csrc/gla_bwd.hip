@@ -32,7 +32,8 @@
 //   gla_bwd_local       per (chunk, value head): the chunk's summaries
 //                       sum_j k_j e^{G_last - G_j} v_j^T and scale (q e^G)^T do, and a
 //   gla_bwd_scan        per state element: S_c forward, E_c in reverse, dh0
-//   gla_bwd_chunk       per (chunk, value head): dq, dk, dv, dg on fp32 MFMA
+//   gla_bwd_chunk       per (chunk, value head): dq, dk, dv, dg (bf16 MFMA on split
+//                       operands for the bf16 products named below, fp32 MFMA otherwise)
 //   gla_bwd_chunk_exact per (chunk, value head) whose decay leaves the fp32 range
 //                       of the factors e^-G (some key below e^-80 within the
 //                       chunk): the same gradients token by token
@@ -235,8 +236,9 @@ __device__ __forceinline__ u32x4_t pack8(const float (&x)[8]) {
 
 // ---------------------------------------------------------------- gla_bwd_local
 // Chunk summaries of the state and of its gradient over the chunk's 64
-// tokens (bf16 MFMA on split operands for bf16 inputs, fp32 MFMA for fp32).  Task t < 2 slots HV: the first half forms, for chunk
-// slot t / HV and value head t % HV,
+// tokens (bf16 MFMA on split operands for bf16 inputs, fp32 MFMA for fp32).
+// Task t < 2 slots HV: the first half forms, for chunk slot t / HV and value
+// head t % HV,
 //   fstate[slot][hv] = sum_j (k_j e^{G_last - G_j}) v_j^T      (K x V)
 //   ddecay[slot][hv] = e^{G_last}                               (K)
 // and the second half
@@ -521,8 +523,11 @@ __device__ __forceinline__ void store_dqk(const BwdParams &bp, int64_t row, int 
 }
 
 // ---------------------------------------------------------------- gla_bwd_chunk
-// The gradients of one chunk of one value head on fp32 MFMA
-// (v_mfma_f32_16x16x4f32).  NW waves (8 for 128 keys: two per SIMD, so that
+// The gradients of one chunk of one value head.  For bf16 inputs the score
+// tiles, the inter-chunk products and (k e^{G_last - G}) E_c run on
+// v_mfma_f32_16x16x32_bf16 with split operands; A^T do, dA' (k e^-G) and
+// dA'^T (q e^G), and every product of fp32 inputs, on v_mfma_f32_16x16x4f32.
+// NW waves (8 for 128 keys: two per SIMD, so that
 // one wave's products run while the other waits for state tiles); wave w owns
 // key block w of 16 keys in every key-space product and the dg cumsum down its
 // columns.  Value blocks of 16 are dealt to waves; with fewer value blocks
