@@ -412,7 +412,8 @@ def main():
                     help="launches timed one by one after the timed steps, warm and with L2/MALL evicted")
     ap.add_argument("--segment-chunks", type=int, default=0)
     ap.add_argument("--schedule", type=int, default=0, choices=[0, 1, 2],
-                    help="segmented sequences: 0 automatic, 1 three passes, 2 one pass")
+                    help="segmented sequences: 0 automatic, 1 three passes, 2 one pass; with --pass bwd: "
+                         "0 automatic, 1 a separate scan launch, 2 the scan chained into the summary kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the forward, run a plain 512 MiB device copy "
                          "(used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -426,6 +427,10 @@ def main():
     if args.workload is None:
         args.workload = "long" if args.which == "fwd" else "c2048"
     traffic_key = args.workload if args.which == "fwd" else args.which + ":" + args.workload
+    if args.schedule != 0 or args.segment_chunks != 0:
+        # counters are recorded for the library's own choices; another
+        # schedule runs other kernels and has its own entry (or none)
+        traffic_key += f"@schedule={args.schedule},segment_chunks={args.segment_chunks}"
     if args.record_traffic:
         if len(args.record_traffic) not in (4, 5):
             ap.error("--record-traffic takes 4 or 5 directories")
@@ -494,7 +499,7 @@ def main():
         tdo = torch.from_numpy(do).to(tdt).to(dev)
         do = tdo.float().cpu().numpy()
         tdht = None if dht is None else torch.from_numpy(dht).to(dev)
-        call = gla.GlaBwdCall(q, k, v, g, tdo, h0=h0, dht=tdht, cu_seqlens=cu)
+        call = gla.GlaBwdCall(q, k, v, g, tdo, h0=h0, dht=tdht, cu_seqlens=cu, schedule=args.schedule)
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
 
@@ -562,6 +567,12 @@ def main():
         torch.cuda.synchronize()
         copy_gbs = 2 * src.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
         del src, dst
+
+    # the workspace's sticky status word: a bounded wait that ran out in any
+    # step means that step's results may be wrong, and the line is not printed
+    st = call.status()
+    if st != 0:
+        sys.exit(f"bench.py: status word {st:#x} after the timed steps (a bounded wait between waves ran out)")
 
     nbytes, flops = (algorithmic if args.which == "fwd" else algorithmic_bwd)(w, n_tokens, n_seqs)
     tokens_per_s = n_tokens / (ms_per_step * 1e-3)

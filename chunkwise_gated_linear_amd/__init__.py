@@ -222,7 +222,8 @@ def gla_fwd_noalloc(q, k, v, g, o, h0=None, cu_seqlens=None, ht=None, scale: Opt
 
 
 def gla_bwd(q, k, v, g, do, h0=None, dht=None, cu_seqlens=None, scale: Optional[float] = None,
-            chunk: int = CHUNK, need_dh0: Optional[bool] = None, workspace=None):
+            chunk: int = CHUNK, need_dh0: Optional[bool] = None, workspace=None, schedule: int = 0,
+            wait_limit: int = 0):
     """Gradients of the forward through libgla.so's gla_bwd.
 
     ``do`` is the gradient of o (v's shape and dtype), ``dht`` that of the final
@@ -230,12 +231,14 @@ def gla_bwd(q, k, v, g, do, h0=None, dht=None, cu_seqlens=None, scale: Optional[
     like q, dv like v, dg like g (float32), dh0 [N, HV, K, V] float32 when
     ``need_dh0`` (default: h0 was given) else None.  Asynchronous on torch's
     current stream; a given ``workspace`` (uint8, zeroed before its first use) is
-    used when large enough.
+    used when large enough.  ``schedule``: 0 automatic, 1 a separate scan
+    launch, 2 the scan chained into the summary kernel (fixed-length
+    sequences); ``wait_limit`` bounds the chained scan's waits as for gla_fwd.
     """
     import torch
 
     lib = load_library()
-    prob, N, dev = _problem_for(q, k, v, g, h0, cu_seqlens, None, scale, chunk, 0, 0, 0)
+    prob, N, dev = _problem_for(q, k, v, g, h0, cu_seqlens, None, scale, chunk, 0, 0, wait_limit, schedule)
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
     if do.shape != v.shape or do.dtype != v.dtype or do.device != dev or not do.is_contiguous():
@@ -367,16 +370,18 @@ class GlaBwdCall:
     workspace once, then enqueues the same gla_bwd call on every ``__call__``."""
 
     def __init__(self, q, k, v, g, do, h0=None, dht=None, cu_seqlens=None, scale=None, chunk: int = CHUNK,
-                 need_dh0: Optional[bool] = None):
+                 need_dh0: Optional[bool] = None, schedule: int = 0):
         import torch
 
         self.lib = load_library()
-        self.problem, N, self.device = _problem_for(q, k, v, g, h0, cu_seqlens, None, scale, chunk, 0, 0, 0)
+        self.problem, N, self.device = _problem_for(q, k, v, g, h0, cu_seqlens, None, scale, chunk, 0, 0, 0,
+                                                    schedule)
         self.ws_bytes = bwd_workspace_bytes(self.problem)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         self.workspace[:256].zero_()
         dq, dk, dv, dg, dh0 = gla_bwd(q, k, v, g, do, h0=h0, dht=dht, cu_seqlens=cu_seqlens, scale=scale,
-                                      chunk=chunk, need_dh0=need_dh0, workspace=self.workspace)
+                                      chunk=chunk, need_dh0=need_dh0, workspace=self.workspace,
+                                      schedule=schedule)
         self.out = (dq, dk, dv, dg, dh0)
         self._args = (q, k, v, g, h0, cu_seqlens, do, dht)
 

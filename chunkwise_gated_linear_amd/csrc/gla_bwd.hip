@@ -30,7 +30,9 @@
 //
 // Kernels (launched by the host in this order):
 //   gla_bwd_local       per (chunk, value head): the chunk's summaries
-//                       sum_j k_j e^{G_last - G_j} v_j^T and scale (q e^G)^T do, and a
+//                       sum_j k_j e^{G_last - G_j} v_j^T and scale (q e^G)^T do, and a;
+//                       for fixed-length sequences it can also chain them into
+//                       S_c, E_c and dh0 itself (then gla_bwd_scan is not launched)
 //   gla_bwd_scan        per state element: S_c forward, E_c in reverse, dh0
 //   gla_bwd_chunk       per (chunk, value head): dq, dk, dv, dg (bf16 MFMA on split
 //                       operands for the bf16 products named below, fp32 MFMA otherwise)
@@ -42,6 +44,7 @@
 
 #include <algorithm>
 
+#include "gla.h"
 #include "gla_device.h"
 
 namespace gla {
@@ -237,16 +240,39 @@ __device__ __forceinline__ u32x4_t pack8(const float (&x)[8]) {
 // ---------------------------------------------------------------- gla_bwd_local
 // Chunk summaries of the state and of its gradient over the chunk's 64
 // tokens (bf16 MFMA on split operands for bf16 inputs, fp32 MFMA for fp32).
-// Task t < 2 slots HV: the first half forms, for chunk slot t / HV and value
-// head t % HV,
-//   fstate[slot][hv] = sum_j (k_j e^{G_last - G_j}) v_j^T      (K x V)
-//   ddecay[slot][hv] = e^{G_last}                               (K)
-// and the second half
-//   dstate[slot][hv] = scale sum_i (q_i e^{G_i}) do_i^T        (K x V).
+// For chunk c of a sequence and value head hv:
+//   Sigma_c = sum_j (k_j e^{G_last - G_j}) v_j^T      (K x V), the state's
+//   D_c     = scale sum_i (q_i e^{G_i}) do_i^T       (K x V), the gradient's
+//   a_c     = e^{G_last}                             (K)
 // Every factor is a decay (at most 1), so any gate is exact here.
-// Persistent workgroups (two per compute unit) walk the tasks with a stride
-// of the grid; the rows of a workgroup's next task are loaded into registers
-// while it forms and stores the current one.
+//
+// Two schedules.  Without bp.chain, task t < 2 slots HV forms Sigma (first
+// half) or D (second half) of slot t / HV and head t % HV, stores it in
+// fstate / dstate (and a_c in ddecay), and gla_bwd_scan then walks the
+// tables.  With bp.chain (fixed-length sequences) the walks run inside this
+// kernel: every (sequence, value head) has a state chain over chunks
+// 0, 1, .., P-1 and a gradient chain over P-1, .., 0, and each task applies
+// one step of the scan's recurrences to the state its predecessor published:
+//   state:    slot c holds S_c;  S_{c+1} = a_c S_c + Sigma_c goes to slot c + 1
+//   gradient: slot c holds E_c;  E_{c-1} = D_c + a_c E_c goes to slot c - 1,
+//             after chunk 0 to dh0
+// (S_0 = h0 and E_{P-1} = dht, or zero).  Tasks are taken from a counter in
+// step order (step s: chunk s of every state chain, chunk P-1-s of every
+// gradient chain), so a task's predecessor always has a lower number and has
+// been taken by a running workgroup: the chains always move.  A published
+// state is written and read only with device-scope stores and loads (those
+// of relaxed agent-scope atomics: no compute unit or die serves them from a
+// private copy); every wave waits for its stores to complete before a
+// barrier, after which one lane sets the flag, and the successor loads the
+// state only after it has seen the flag (polled within the bound
+// wait_polls).  No cache-wide write-back or invalidation is needed for that,
+// and none is made: with one link per chunk (every few microseconds on each
+// die) they cost more than the scan launch this schedule saves.  The state
+// summary of the last chunk and, without dh0, the gradient summary of chunk
+// 0 feed nothing and are not formed.
+//
+// Persistent workgroups (two per compute unit); the rows of a workgroup's
+// next task are loaded into registers while it forms the current one.
 template <bool BF, int KD, int VD, bool GH>
 struct LocalRows {
   static constexpr int TK = 64 * KD / 4 / 256, TV = 64 * VD / 4 / 256;  // row quads per thread
@@ -254,36 +280,173 @@ struct LocalRows {
   GateRows<KD, GH, 256> gate;
 };
 
-template <bool BF, int KD, int VD, bool GH>
-__device__ __forceinline__ bool local_task(const BwdParams &bp, long long task, ChunkAt &ca, int &hv, bool &grad) {
+// A task: chunk ca of value head hv, the state summary (grad false) or the
+// gradient summary (grad true); work: the summary is formed.
+struct LocalTask {
+  ChunkAt ca;
+  int hv, slot;
+  bool grad, work;
+};
+
+// Task t of the three-launch schedule.
+__device__ __forceinline__ bool local_task(const BwdParams &bp, long long t, LocalTask &lt) {
   const WalkParams &p = bp.w;
   const long long half = (long long)p.seg_slots * p.HV;
-  grad = task >= half;
-  const long long blk = grad ? task - half : task;
-  hv = (int)(blk % p.HV);
-  return chunk_at(p, (int)(blk / p.HV), ca);
+  lt.grad = t >= half;
+  const long long blk = lt.grad ? t - half : t;
+  lt.hv = (int)(blk % p.HV);
+  lt.slot = (int)(blk / p.HV);
+  lt.work = true;
+  return chunk_at(p, lt.slot, lt.ca);
+}
+
+// Task t of the chained schedule (fixed-length sequences, P chunks each).
+__device__ __forceinline__ bool chained_task(const BwdParams &bp, long long t, LocalTask &lt) {
+  const WalkParams &p = bp.w;
+  const long long pairs = (long long)p.N * p.HV;
+  const long long step = t / (2 * pairs);
+  long long rem = t - step * 2 * pairs;
+  lt.grad = rem >= pairs;
+  if (lt.grad) rem -= pairs;
+  const int n = (int)(rem / p.HV);
+  lt.hv = (int)(rem - (long long)n * p.HV);
+  const int c = lt.grad ? p.P - 1 - (int)step : (int)step;
+  lt.slot = n * p.P + c;
+  lt.work = lt.grad ? (c > 0 || bp.dh0 != nullptr) : c < p.P - 1;
+  return chunk_at(p, lt.slot, lt.ca);
 }
 
 template <bool BF, int KD, int VD, bool GH>
-__device__ __forceinline__ void local_load(const BwdParams &bp, const ChunkAt &ca, int hv, bool grad,
-                                           LocalRows<BF, KD, VD, GH> &rw) {
+__device__ __forceinline__ void local_load(const BwdParams &bp, const LocalTask &lt, LocalRows<BF, KD, VD, GH> &rw) {
   using R = LocalRows<BF, KD, VD, GH>;
   const WalkParams &p = bp.w;
-  const int h = hv / p.G;
-  const void *xs = grad ? p.q : p.k;      // key-side rows
-  const void *ys = grad ? bp.dout : p.v;  // value-side rows
+  const ChunkAt &ca = lt.ca;
+  const int h = lt.hv / p.G;
+  const void *xs = lt.grad ? p.q : p.k;      // key-side rows
+  const void *ys = lt.grad ? bp.dout : p.v;  // value-side rows
 #pragma unroll
   for (int t = 0; t < R::TK; ++t) {
     const int e = threadIdx.x + 256 * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
     rw.x[t] = {};
     if (i < ca.L && c4 < p.K) rw.x[t] = ld_raw4<BF>(xs, (ca.row0 + i) * p.H * p.K + h * p.K + c4);
   }
-  gate_load<KD, GH, 256>(p, ca, hv, rw.gate);
+  gate_load<KD, GH, 256>(p, ca, lt.hv, rw.gate);
 #pragma unroll
   for (int t = 0; t < R::TV; ++t) {
     const int e = threadIdx.x + 256 * t, i = e / (VD / 4), c4 = (e % (VD / 4)) * 4;
     rw.y[t] = {};
-    if (i < ca.L && c4 < p.V) rw.y[t] = ld_raw4<BF>(ys, ((ca.row0 + i) * p.HV + hv) * p.V + c4);
+    if (i < ca.L && c4 < p.V) rw.y[t] = ld_raw4<BF>(ys, ((ca.row0 + i) * p.HV + lt.hv) * p.V + c4);
+  }
+}
+
+// One step of a chain (chained schedule) for task lt, whose summary is in acc
+// (in the MFMA layout: row (wave NKB + a) 16 + lane % 16, columns
+// b 16 + 4 (lane / 16) + [0, 4)) and whose decays a_c are in dec[K].  The
+// chain's first chunk takes its state from h0 / dht (or zero) and also stores
+// it in its own slot for the chunk kernel.  Every access goes through a buffer
+// descriptor over one K x V state: rows past K and columns past V (whole
+// 16-row and 16-column blocks, K and V being multiples of 16) get an offset
+// past its end, so that their loads return zero and their stores are dropped
+// without a branch, and the loads of the step all travel at once.
+template <int KD, int VD>
+__device__ __forceinline__ void chain_step(const BwdParams &bp, const LocalTask &lt,
+                                           const f32x4_t (&acc)[KD / 64][VD / 16], const float *dec) {
+  constexpr int NKB = KD / 64, NVB = VD / 16;
+  constexpr int kOutside = 0x40000000;  // a byte offset past any state
+  const WalkParams &p = bp.w;
+  const int c = lt.ca.c, n = lt.ca.si.n;
+  const bool first = lt.grad ? c == p.P - 1 : c == 0;
+  const bool publish = lt.grad ? c > 0 : c < p.P - 1;
+  if (!first && !lt.work) return;  // a summary nobody needs, and a slot its predecessor filled
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the lane through an opaque copy: the offsets below would otherwise be
+  // hoisted out of the task loop and held in registers across the products
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int64_t KV = (int64_t)p.K * p.V;
+  float *tab = lt.grad ? bp.dstate : bp.fstate;
+  int32_t *flags = bp.chain + 1 + (lt.grad ? (int64_t)p.seg_slots * p.HV : 0);
+  const float *bound = lt.grad ? bp.dht : p.h0;
+  if (bound != nullptr) bound += ((int64_t)n * p.HV + lt.hv) * KV;
+  const int next = lt.grad ? lt.slot - 1 : lt.slot + 1;
+  float *out = nullptr;
+  if (publish) out = tab + ((int64_t)next * p.HV + lt.hv) * KV;
+  else if (lt.work) out = bp.dh0 + ((int64_t)n * p.HV + lt.hv) * KV;  // gradient chunk 0 with dh0
+  const __amdgpu_buffer_rsrc_t rHere = make_rsrc(tab + ((int64_t)lt.slot * p.HV + lt.hv) * KV, KV * 4);
+  int off[NKB][NVB];
+#pragma unroll
+  for (int a = 0; a < NKB; ++a)
+#pragma unroll
+    for (int b = 0; b < NVB; ++b) {
+      const int rb = wave * NKB + a;  // 16-row block
+      const bool in = rb * 16 < p.K && b * 16 < p.V;
+      off[a][b] = in ? ((rb * 16 + l16) * p.V + b * 16 + 4 * lg) * 4 : kOutside;
+    }
+  if (!first) {
+    // one wave waits; the barrier holds the others until then, and the state
+    // is loaded after it
+    if (wave == 0) {
+      const int32_t *f = flags + (int64_t)lt.slot * p.HV + lt.hv;
+      int ready = 0;
+      if (lane == 0) {
+        for (int spin = 0; spin < p.wait_polls; ++spin) {
+          if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+            ready = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      if (__builtin_amdgcn_readfirstlane(ready) == 0) report_status(p.status, GLA_STATUS_WAIT_EXHAUSTED, lane);
+    }
+    __syncthreads();
+  }
+  f32x4_t x[NKB][NVB];
+  if (!first) {
+#pragma unroll
+    for (int a = 0; a < NKB; ++a)
+#pragma unroll
+      for (int b = 0; b < NVB; ++b) x[a][b] = buf_ldf4<kDeviceScope>(rHere, off[a][b]);
+  } else if (bound != nullptr) {
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(bound, KV * 4);
+#pragma unroll
+    for (int a = 0; a < NKB; ++a)
+#pragma unroll
+      for (int b = 0; b < NVB; ++b) x[a][b] = buf_ldf4<0>(rB, off[a][b]);
+  } else {
+#pragma unroll
+    for (int a = 0; a < NKB; ++a)
+#pragma unroll
+      for (int b = 0; b < NVB; ++b) x[a][b] = zero4();
+  }
+  if (first) {
+#pragma unroll
+    for (int a = 0; a < NKB; ++a)
+#pragma unroll
+      for (int b = 0; b < NVB; ++b) buf_stf4<0>(rHere, off[a][b], x[a][b]);
+  }
+  if (out == nullptr) return;
+  const __amdgpu_buffer_rsrc_t rOut = make_rsrc(out, KV * 4);
+  float ak[NKB];
+#pragma unroll
+  for (int a = 0; a < NKB; ++a) ak[a] = dec[(wave * NKB + a) * 16 + l16];  // rows past K: stores dropped
+  if (publish) {
+#pragma unroll
+    for (int a = 0; a < NKB; ++a)
+#pragma unroll
+      for (int b = 0; b < NVB; ++b) buf_stf4<kDeviceScope>(rOut, off[a][b], ak[a] * x[a][b] + acc[a][b]);
+    // every wave's stores have completed (at device scope) before the barrier;
+    // then one lane sets the flag
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_store(flags + (int64_t)next * p.HV + lt.hv, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+#pragma unroll
+    for (int a = 0; a < NKB; ++a)
+#pragma unroll
+      for (int b = 0; b < NVB; ++b) buf_stf4<0>(rOut, off[a][b], ak[a] * x[a][b] + acc[a][b]);
   }
 }
 
@@ -295,58 +458,78 @@ __global__ __launch_bounds__(256, 2) void gla_bwd_local(BwdParams bp) {
   __shared__ __attribute__((aligned(16))) float sA[64 * KD];  // G, then k e^{G_last - G} or scale q e^G
   __shared__ __attribute__((aligned(16))) float sB[64 * VD];  // v or do
   __shared__ float tot[256];
+  __shared__ float sdec[KD];  // a_c per key
+  __shared__ int sclaim;      // chained schedule: the task number taken from the counter
+  const bool chained = bp.chain != nullptr;
   const long long ntask = 2LL * p.seg_slots * p.HV;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
 
+  // the next task: from the counter (chained; sclaim was written before a
+  // barrier), else the next one with a chunk on the grid stride
+  long long task = (long long)blockIdx.x - gridDim.x;
+  auto advance = [&](LocalTask &lt) -> bool {
+    if (chained) {
+      const long long t = __builtin_amdgcn_readfirstlane(sclaim);
+      return t < ntask && chained_task(bp, t, lt);
+    }
+    for (task += gridDim.x; task < ntask; task += gridDim.x)
+      if (local_task(bp, task, lt)) return true;
+    return false;
+  };
+  auto claim = [&]() {
+    if (chained && threadIdx.x == 0)
+      sclaim = __hip_atomic_fetch_add(bp.chain, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
   R rw;
-  long long task = blockIdx.x;
-  ChunkAt ca;
-  int hv = 0;
-  bool grad = false;
-  // first task with a chunk (slots past a sequence's chunks have none)
-  bool have = false;
-  for (; task < ntask; task += gridDim.x)
-    if ((have = local_task<BF, KD, VD, GH>(bp, task, ca, hv, grad))) break;
-  if (have) local_load<BF, KD, VD, GH>(bp, ca, hv, grad, rw);
+  LocalTask nxt;
+  claim();
+  __syncthreads();
+  bool have = advance(nxt);
+  __syncthreads();  // sclaim is read before the loop's first claim overwrites it
+  if (have && nxt.work) local_load<BF, KD, VD, GH>(bp, nxt, rw);
   while (have) {
-    const int chv = hv;
-    const bool cgrad = grad;
-    const int slot = (int)((cgrad ? task - ntask / 2 : task) / p.HV);
-    // gate rows -> LDS, cumsum down each key column (G in sA)
-    gate_stage<KD, GH, 256>(rw.gate, sA);
-    __syncthreads();
-    gate_cumsum_lds<KD, GH, 256>(p.K, sA, tot);
-    f32x4_t xg[R::TK];
+    const LocalTask cur = nxt;
+    claim();
+    if (cur.work) {
+      // gate rows -> LDS, cumsum down each key column (G in sA)
+      gate_stage<KD, GH, 256>(rw.gate, sA);
+      __syncthreads();
+      gate_cumsum_lds<KD, GH, 256>(p.K, sA, tot);
+      f32x4_t xg[R::TK];
 #pragma unroll
-    for (int t = 0; t < R::TK; ++t) {
-      const int e = threadIdx.x + 256 * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
-      const f32x4_t G4 = lds4<KD>(sA, i, c4), Gl4 = lds4<KD>(sA, 63, c4);
-      f32x4_t xt = unpack4<BF>(rw.x[t]);
+      for (int t = 0; t < R::TK; ++t) {
+        const int e = threadIdx.x + 256 * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
+        const f32x4_t G4 = lds4<KD>(sA, i, c4), Gl4 = lds4<KD>(sA, 63, c4);
+        f32x4_t xt = unpack4<BF>(rw.x[t]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) xt[r] *= cgrad ? p.scale * __expf(G4[r]) : __expf(Gl4[r] - G4[r]);
-      xg[t] = xt;
-      if (!cgrad && i == 63 && c4 < p.K) {
+        for (int r = 0; r < 4; ++r) xt[r] *= cur.grad ? p.scale * __expf(G4[r]) : __expf(Gl4[r] - G4[r]);
+        xg[t] = xt;
+        if (i == 63 && c4 < p.K) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bp.ddecay[((int64_t)slot * p.HV + chv) * p.K + c4 + r] = __expf(Gl4[r]);
+          for (int r = 0; r < 4; ++r) {
+            const float a = __expf(Gl4[r]);
+            sdec[c4 + r] = a;
+            if (!chained && !cur.grad) bp.ddecay[((int64_t)cur.slot * p.HV + cur.hv) * p.K + c4 + r] = a;
+          }
+        }
       }
-    }
 #pragma unroll
-    for (int t = 0; t < R::TV; ++t) {
-      const int e = threadIdx.x + 256 * t, i = e / (VD / 4), c4 = (e % (VD / 4)) * 4;
-      lds4_st<VD>(sB, i, c4, unpack4<BF>(rw.y[t]));
-    }
-    __syncthreads();  // G read by every thread
+      for (int t = 0; t < R::TV; ++t) {
+        const int e = threadIdx.x + 256 * t, i = e / (VD / 4), c4 = (e % (VD / 4)) * 4;
+        lds4_st<VD>(sB, i, c4, unpack4<BF>(rw.y[t]));
+      }
+      __syncthreads();  // G read by every thread
 #pragma unroll
-    for (int t = 0; t < R::TK; ++t) {
-      const int e = threadIdx.x + 256 * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
-      lds4_st<KD>(sA, i, c4, xg[t]);
+      for (int t = 0; t < R::TK; ++t) {
+        const int e = threadIdx.x + 256 * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
+        lds4_st<KD>(sA, i, c4, xg[t]);
+      }
     }
     __syncthreads();
     // the next task's rows travel while this one's products are formed
-    have = false;
-    for (task += gridDim.x; task < ntask; task += gridDim.x)
-      if ((have = local_task<BF, KD, VD, GH>(bp, task, ca, hv, grad))) break;
-    if (have) local_load<BF, KD, VD, GH>(bp, ca, hv, grad, rw);
+    have = advance(nxt);
+    if (have && nxt.work) local_load<BF, KD, VD, GH>(bp, nxt, rw);
 
     // transposed product (rows v, columns k): each lane then holds 4
     // consecutive values of one state row and stores them as one float4
@@ -355,7 +538,8 @@ __global__ __launch_bounds__(256, 2) void gla_bwd_local(BwdParams bp) {
     for (int a = 0; a < NKB; ++a)
 #pragma unroll
       for (int b = 0; b < NVB; ++b) acc[a][b] = zero4();
-    if constexpr (BF) {
+    if (!cur.work) {
+    } else if constexpr (BF) {
       // bf16 inputs: the value-side rows (v or do) are exact in bf16, the gated
       // key-side rows are split into three bf16 terms (fp32 accuracy); 32
       // tokens per v_mfma_f32_16x16x32_bf16, each lane 8 consecutive tokens of
@@ -410,14 +594,18 @@ __global__ __launch_bounds__(256, 2) void gla_bwd_local(BwdParams bp) {
             for (int b = 0; b < NVB; ++b) acc[a][b] = mfma_f32(yb[b][r], xa[a][r], acc[a][b]);
       }
     }
-    float *dst = (cgrad ? bp.dstate : bp.fstate) + ((int64_t)slot * p.HV + chv) * p.K * p.V;
+    if (chained) {
+      chain_step<KD, VD>(bp, cur, acc, sdec);
+    } else {
+      float *dst = (cur.grad ? bp.dstate : bp.fstate) + ((int64_t)cur.slot * p.HV + cur.hv) * p.K * p.V;
 #pragma unroll
-    for (int a = 0; a < NKB; ++a)
+      for (int a = 0; a < NKB; ++a)
 #pragma unroll
-      for (int b = 0; b < NVB; ++b) {
-        const int krow = (wave * NKB + a) * 16 + l16, col = b * 16 + 4 * lg;
-        if (krow < p.K && col < p.V) *reinterpret_cast<f32x4_t *>(dst + (int64_t)krow * p.V + col) = acc[a][b];
-      }
+        for (int b = 0; b < NVB; ++b) {
+          const int krow = (wave * NKB + a) * 16 + l16, col = b * 16 + 4 * lg;
+          if (krow < p.K && col < p.V) *reinterpret_cast<f32x4_t *>(dst + (int64_t)krow * p.V + col) = acc[a][b];
+        }
+    }
     __syncthreads();  // LDS is refilled for the next task
   }
 }
@@ -601,7 +789,7 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
   __shared__ __attribute__((aligned(16))) float sEl[KD];      // e^{G_last}
   __shared__ float sGl[KD];                                   // G_last
   __shared__ float tot[NT];
-  __shared__ float sRow[64];                                  // per-row dg sums (per-head gate)
+  __shared__ float sRow[NW * 64];  // per-head gate: dg of each row summed over each wave's keys
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
   const int kb = wave * 16;                                        // this wave's key block
@@ -648,7 +836,6 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
         }
       }
     }
-    if (GH && threadIdx.x < 64) sRow[threadIdx.x] = 0.f;
     const bool exact = __syncthreads_or(low);  // also: every thread is done reading G from sV
     if (threadIdx.x == 0) bp.flags[(int64_t)cslot * p.HV + chv] = exact ? 1 : 0;
     if (exact) return;
@@ -962,6 +1149,7 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
       colk += __shfl_xor(colk, 16);
       colk += __shfl_xor(colk, 32);
       float carry = el * rsa + colk;  // dg of the first token after the chunk
+      float runv[4][4];                // per-head gate: this key's share of each row's dg
 #pragma unroll
       for (int b = 3; b >= 0; --b) {
         const float sb = t[b][0] + t[b][1] + t[b][2] + t[b][3];
@@ -977,17 +1165,35 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
         for (int r = 3; r >= 0; --r) {
           run += t[b][r];
           const int i = b * 16 + 4 * lg + r;
-          if (i < L && k < p.K) {
-            if (GH) atomicAdd(&sRow[i], run);
-            else bp.dg[((row0 + i) * p.HV + chv) * p.K + k] = run;
-          }
+          if constexpr (GH) runv[b][r] = k < p.K ? run : 0.f;
+          else if (i < L && k < p.K) bp.dg[((row0 + i) * p.HV + chv) * p.K + k] = run;
         }
         carry += total;
+      }
+      if constexpr (GH) {
+        // sums over the wave's 16 keys, then over the waves, in a fixed order
+        // (the same dg on every run)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x = runv[b][r];
+            x += __shfl_xor(x, 1);
+            x += __shfl_xor(x, 2);
+            x += __shfl_xor(x, 4);
+            x += __shfl_xor(x, 8);
+            if (l16 == 0) sRow[wave * 64 + b * 16 + 4 * lg + r] = x;
+          }
       }
     }
     if (GH) {
       __syncthreads();
-      if (threadIdx.x < L) bp.dg[(row0 + threadIdx.x) * p.HV + chv] = sRow[threadIdx.x];
+      if (threadIdx.x < L) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sum += sRow[w * 64 + threadIdx.x];
+        bp.dg[(row0 + threadIdx.x) * p.HV + chv] = sum;
+      }
     }
   }
 }
@@ -1015,7 +1221,8 @@ __global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
   __shared__ float sA[64 * KD];    // e^{g} per token and key
   __shared__ float sDq[64 * KD];   // dq
   __shared__ float sRed[4 * VD];   // per-wave partial dv of one token
-  __shared__ float sRow[64];
+  __shared__ float sRow[64];       // per-head gate: dg of each token
+  __shared__ float sKeyDg[KD];     // per-head gate: each key's share of one token's dg
 
   const int hv = (int)(blockIdx.x % (unsigned)p.HV);
   const int slot = (int)(blockIdx.x / (unsigned)p.HV);
@@ -1125,10 +1332,17 @@ __global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
       const int64_t row = row0 + i;
       const float dgi = a * acc;
       store_dqk<BF>(bp, row, hv, key, sDq[i * KD + key], dkp);
-      if (GH) atomicAdd(&sRow[i], dgi);
-      else bp.dg[(row * p.HV + hv) * p.K + key] = dgi;
+      if (!GH) bp.dg[(row * p.HV + hv) * p.K + key] = dgi;
     }
+    if (GH && cp == 0) sKeyDg[key] = kin ? a * acc : 0.f;
     __syncthreads();
+    if (GH && wave == 0) {
+      // the sum over keys in a fixed order (the same dg on every run)
+      float x = sKeyDg[lane] + (KD > 64 ? sKeyDg[lane + 64] : 0.f);
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+      if (lane == 0) sRow[i] = x;
+    }
     for (int col = threadIdx.x; col < p.V; col += 256) {
       const float sv = sRed[col] + sRed[VD + col] + sRed[2 * VD + col] + sRed[3 * VD + col];
       st_el<BF>(bp.dv, ((row0 + i) * p.HV + hv) * p.V + col, sv);

@@ -1,4 +1,4 @@
-// Device helpers shared by the walker kernels (gla_kernels.hip, gla_walk_bf16.hip).
+// Device helpers shared by the kernels (gla_kernels.hip, gla_walk_bf16.hip, gla_bwd.hip, gla_wy.hip).
 #pragma once
 
 #include "gla_internal.h"
@@ -205,6 +205,19 @@ __device__ __forceinline__ void buf_st128(__amdgpu_buffer_rsrc_t r, int off, u32
 __device__ __forceinline__ void buf_st128_nt(__amdgpu_buffer_rsrc_t r, int off, u32x4_t v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off, 0, 2);
 }
+// fp32 quads with cache policy AUX: 0 plain; 16 (sc1) device scope, the form
+// a relaxed agent-scope atomic load or store takes on this GPU (no compute
+// unit or die serves it from a private copy)
+template <int AUX>
+__device__ __forceinline__ f32x4_t buf_ldf4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ void buf_stf4(__amdgpu_buffer_rsrc_t r, int off, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v),
+                                         r, off, 0, AUX);
+}
+constexpr int kDeviceScope = 16;
 __device__ __forceinline__ void buf_st64(__amdgpu_buffer_rsrc_t r, int off, u32x2_t v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, off, 0, 0);
 }
@@ -334,6 +347,36 @@ __device__ __forceinline__ u32x2_t lds_tr16(const char *p) {
   typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
   const lds_v4i16_t *lp = (const lds_v4i16_t *)(const __attribute__((address_space(3))) char *)p;
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_v4i16_t *>(lp)));
+}
+
+// ---------------------------------------------------------------- coherence
+// Sets bits in the caller-visible status word (a vector-memory atomic OR from
+// one lane; the word is only ever OR-ed, never cleared, by the kernels).
+__device__ __forceinline__ void report_status(uint32_t *status, uint32_t bits, int lane) {
+  if (lane == 0) __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Device-coherent accesses for data that one workgroup publishes to another
+// within a launch: agent-scope atomic loads and stores, which no compute unit
+// or die keeps a private cached copy of (plain accesses would rely on cache
+// write-back and invalidation reaching every line of the other die's L2).
+__device__ __forceinline__ float ld_agent(const float *p) {
+  return __uint_as_float(
+      __hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ f32x4_t ld_agent4(const float *p) {
+  const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x4_t{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)), __uint_as_float((uint32_t)b),
+                 __uint_as_float((uint32_t)(b >> 32))};
+}
+__device__ __forceinline__ void st_agent4(float *p, const f32x4_t &v) {
+  uint64_t *q = reinterpret_cast<uint64_t *>(p);
+  const uint64_t a = (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32);
+  const uint64_t b = (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32);
+  __hip_atomic_store(q, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace dev

@@ -93,6 +93,9 @@ struct BwdParams {
   float *fstate;         // [slots][HV][K][V]: chunk summaries of the state, then S_c (state before chunk c)
   float *dstate;         // [slots][HV][K][V]: chunk summaries of the state gradient, then E_c
   float *ddecay;         // [slots][HV][K]: e^{G_last} of each chunk
+  int32_t *chain;        // fixed-length sequences, or null: gla_bwd_local also walks the chains of S_c and
+                         // E_c ([0] task counter, then flags [2][slots][HV]; zeroed before the launch) and
+                         // gla_bwd_scan is not launched
   int32_t *flags;        // [slots][HV]: 1 when the chunk is left to the token-by-token kernel
   float *dq_part, *dk_part;  // [B,T,HV,K] fp32 shares of dq, dk per value head (G > 1), else null
   int32_t persistent_blocks; // workgroups of the persistent kernels (a few per compute unit)

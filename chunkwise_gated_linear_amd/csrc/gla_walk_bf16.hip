@@ -156,12 +156,6 @@ __device__ __forceinline__ bool scores_wait(char *flags, int c, int polls) {
   return ready;
 }
 
-// Sets bits in the caller-visible status word (a vector-memory atomic OR from
-// one lane; the word is only ever OR-ed, never cleared, by the kernels).
-__device__ __forceinline__ void report_status(uint32_t *status, uint32_t bits, int lane) {
-  if (lane == 0) __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Split of values that are not used after it (gated q and k rows, score
 // tiles).  With 64 columns the producer waves set the pace and the form with
 // one dot instruction per remainder saves them VALU instructions; with 128
@@ -228,29 +222,6 @@ __device__ __forceinline__ void scores(char *smem, const char *sq, const int (&r
 
 // GH: the gate is one decay per value head and token (g [B,T,HV]) instead of one
 // per key; a compile-time choice, so that the per-key walker's code is untouched.
-// Device-coherent accesses for data that one workgroup publishes to another
-// within a launch: agent-scope atomic loads and stores, which no compute unit
-// or die keeps a private cached copy of (plain accesses would rely on cache
-// write-back and invalidation reaching every line of the other die's L2).
-__device__ __forceinline__ float ld_agent(const float *p) {
-  return __uint_as_float(
-      __hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ f32x4_t ld_agent4(const float *p) {
-  const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
-  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return f32x4_t{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)), __uint_as_float((uint32_t)b),
-                 __uint_as_float((uint32_t)(b >> 32))};
-}
-__device__ __forceinline__ void st_agent4(float *p, const f32x4_t &v) {
-  uint64_t *q = reinterpret_cast<uint64_t *>(p);
-  const uint64_t a = (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32);
-  const uint64_t b = (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32);
-  __hip_atomic_store(q, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // b: the workgroup's index in the (segment, head, value slice) order.
 // FUSED: one of the two walks of the single pass.  Its summary walk keeps the
 // summary in LDS as [K][VW] fp32 at offset 0 instead of storing it to

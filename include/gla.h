@@ -81,7 +81,7 @@ typedef enum gla_gate {
 } gla_gate;
 
 /* Bits of the status word (see gla_fwd's workspace). */
-#define GLA_STATUS_WAIT_EXHAUSTED 1u  /* a bounded wait between waves ran out: o may be wrong */
+#define GLA_STATUS_WAIT_EXHAUSTED 1u  /* a bounded wait between waves ran out: the outputs may be wrong */
 
 typedef struct gla_problem {
     int32_t B;        /* batch; must be 1 for packed sequences                         */
@@ -108,7 +108,10 @@ typedef struct gla_problem {
                       /* sequences, else three); 1 three passes (summaries, a scan of */
                       /* them, outputs); 2 one pass, segments chained by their end    */
                       /* states (bf16 with K <= 128, else three passes).  A tuning    */
-                      /* choice: results agree to rounding.                           */
+                      /* choice: results agree to rounding.  gla_bwd: 0 automatic;    */
+                      /* 1 a separate scan over the chunk summaries; 2 the scan       */
+                      /* chained into the summary kernel (fixed-length sequences;     */
+                      /* packed ones always take 1).  Results are the same.           */
 } gla_problem;
 
 /*
@@ -191,9 +194,10 @@ size_t gla_bwd_workspace_bytes(const gla_problem *p);
  *   dh0    : [N,HV,K,V] float32 or NULL (not computed)
  *   workspace / workspace_bytes : device scratch of at least
  *            gla_bwd_workspace_bytes(p) bytes, first 4 bytes a sticky status
- *            word as for gla_fwd.  It holds the state after every chunk and the
- *            state gradient reaching every chunk: 2 * chunks * HV * K * V * 4
- *            bytes and more.
+ *            word as for gla_fwd (GLA_STATUS_WAIT_EXHAUSTED when a wait of the
+ *            chained scan, see schedule, ran out).  It holds the state before
+ *            every chunk and the state gradient reaching every chunk:
+ *            2 * chunks * HV * K * V * 4 bytes and more.
  * Supported: K and V multiples of 16 up to 128 (else GLA_ERR_UNSUPPORTED),
  * both dtypes, both gate layouts, HV a multiple of H, packed sequences.  Every
  * output row of a token is written; rows of other tokens are untouched.

@@ -39,7 +39,7 @@ def grads_in(d, dtype, seed):
     return do, dht
 
 
-def run_bwd_gpu(d, do, dht, dtype, scale=None, need_dh0=True):
+def run_bwd_gpu(d, do, dht, dtype, scale=None, need_dh0=True, schedule=0, wait_limit=0, status=None):
     import torch
     import chunkwise_gated_linear_amd as gla
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -50,21 +50,29 @@ def run_bwd_gpu(d, do, dht, dtype, scale=None, need_dh0=True):
     cu = None if d["cu_seqlens"] is None else torch.from_numpy(d["cu_seqlens"]).to(dev)
     tdo = torch.from_numpy(do).to(tdt).to(dev).contiguous()
     tdht = None if dht is None else torch.from_numpy(dht).to(dev).contiguous()
-    ws = torch.zeros(1, dtype=torch.uint8, device=dev)
+    ws = None
+    if status is not None:  # a zeroed workspace whose status word is returned in status[0]
+        prob, _, _ = gla._problem_for(t["q"], t["k"], t["v"], g, h0, cu, None, scale, 64, 0, 0, wait_limit,
+                                      schedule)
+        ws = torch.zeros(gla.bwd_workspace_bytes(prob), dtype=torch.uint8, device=dev)
     dq, dk, dv, dg, dh0 = gla.gla_bwd(t["q"], t["k"], t["v"], g, tdo, h0=h0, dht=tdht, cu_seqlens=cu,
-                                      scale=scale, need_dh0=need_dh0)
+                                      scale=scale, need_dh0=need_dh0, workspace=ws, schedule=schedule,
+                                      wait_limit=wait_limit)
     torch.cuda.synchronize()
+    if status is not None:
+        status.append(gla.read_status(ws))
     f = lambda x: None if x is None else x.float().cpu().numpy().astype(np.float64)
     return f(dq), f(dk), f(dv), f(dg), f(dh0)
 
 
-def check_bwd(d, dtype, seed, scale=None, use_dht=True, need_dh0=True, label=""):
+def check_bwd(d, dtype, seed, scale=None, use_dht=True, need_dh0=True, label="", schedule=0):
     do, dht = grads_in(d, dtype, seed)
     if not use_dht:
         dht = None
     say(f"bwd {label}: q{tuple(d['q'].shape)} v{tuple(d['v'].shape)} g{tuple(d['g'].shape)} {dtype} "
-        f"h0={d['h0'] is not None} dht={dht is not None} packed={d['cu_seqlens'] is not None}")
-    got = run_bwd_gpu(d, do, dht, dtype, scale=scale, need_dh0=need_dh0)
+        f"h0={d['h0'] is not None} dht={dht is not None} packed={d['cu_seqlens'] is not None} "
+        f"schedule={schedule}")
+    got = run_bwd_gpu(d, do, dht, dtype, scale=scale, need_dh0=need_dh0, schedule=schedule)
     ref = oracle.gla_reference_bwd(d["q"], d["k"], d["v"], d["g"], do, h0=d["h0"], dht=dht,
                                    cu_seqlens=d["cu_seqlens"], scale=scale)
     tol = TOL[dtype]
@@ -81,6 +89,12 @@ def check_bwd(d, dtype, seed, scale=None, use_dht=True, need_dh0=True, label="")
     return errs
 
 
+# schedule 1: summaries, a separate scan launch, chunk kernel; 2: the scan
+# chained into the summary kernel (fixed-length sequences)
+SCHEDULES = [1, 2]
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("B,T,H,K,V", [
     (2, 200, 2, 64, 64),
@@ -88,9 +102,9 @@ def check_bwd(d, dtype, seed, scale=None, use_dht=True, need_dh0=True, label="")
     (2, 130, 3, 128, 64),
     (1, 150, 2, 64, 128),
 ])
-def test_shapes(dtype, B, T, H, K, V):
+def test_shapes(dtype, B, T, H, K, V, schedule):
     d = gi.draw(100 + T + K, B, T, H, K, V, dtype=dtype, h0=True)
-    check_bwd(d, dtype, seed=7, label="shapes")
+    check_bwd(d, dtype, seed=7, label="shapes", schedule=schedule)
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
@@ -100,11 +114,12 @@ def test_narrow_and_odd_widths(dtype, K, V):
     check_bwd(d, dtype, seed=8, label="widths")
 
 
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 127, 129])
-def test_ragged_lengths(dtype, T):
+def test_ragged_lengths(dtype, T, schedule):
     d = gi.draw(300 + T, 2, T, 2, 64, 64, dtype=dtype, h0=True)
-    check_bwd(d, dtype, seed=9, label=f"T={T}")
+    check_bwd(d, dtype, seed=9, label=f"T={T}", schedule=schedule)
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
@@ -113,20 +128,22 @@ def test_packed(dtype):
     check_bwd(d, dtype, seed=10, label="packed")
 
 
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("h0,use_dht,need_dh0", [(False, True, True), (True, False, True), (False, False, False),
                                                  (True, True, False)])
-def test_optional_states(dtype, h0, use_dht, need_dh0):
+def test_optional_states(dtype, h0, use_dht, need_dh0, schedule):
     d = gi.draw(500, 2, 150, 2, 64, 64, dtype=dtype, h0=h0)
-    check_bwd(d, dtype, seed=11, use_dht=use_dht, need_dh0=need_dh0, label="optional")
+    check_bwd(d, dtype, seed=11, use_dht=use_dht, need_dh0=need_dh0, label="optional", schedule=schedule)
 
 
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("HV,gate", [(2, "key"), (1, "head"), (3, "head")])
-def test_head_and_gate_variants(dtype, HV, gate):
+def test_head_and_gate_variants(dtype, HV, gate, schedule):
     H = 2
     d = gi.draw(600 + HV, 2, 140, H, 64, 64, dtype=dtype, h0=True, HV=H * HV, gate=gate)
-    check_bwd(d, dtype, seed=12, label=f"HV={H * HV} gate={gate}")
+    check_bwd(d, dtype, seed=12, label=f"HV={H * HV} gate={gate}", schedule=schedule)
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
@@ -135,14 +152,15 @@ def test_head_variants_packed(dtype):
     check_bwd(d, dtype, seed=13, label="packed heads")
 
 
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("gate_scale", [4.0, 40.0])
-def test_strong_gates(dtype, gate_scale):
+def test_strong_gates(dtype, gate_scale, schedule):
     # logsigmoid(N(0,1)) * gate_scale: with 4, some chunks decay by more than
     # e^-80 over 64 tokens on some key; with 40 nearly every chunk does.  Those
     # chunks take the token-by-token kernel; the results must not change.
     d = gi.draw(700, 2, 200, 2, 64, 64, dtype=dtype, h0=True, gate_scale=gate_scale)
-    check_bwd(d, dtype, seed=14, label=f"gate x{gate_scale}")
+    check_bwd(d, dtype, seed=14, label=f"gate x{gate_scale}", schedule=schedule)
 
 
 def test_strong_gates_packed_heads():
@@ -162,13 +180,17 @@ def test_zero_gate_is_linear_attention():
     check_bwd(d, "fp32", seed=17, label="g=0")
 
 
-def test_deterministic():
-    d = gi.draw(900, 2, 300, 2, 128, 128, dtype="bf16", h0=True)
+@pytest.mark.parametrize("gate,strong", [("key", False), ("head", False), ("head", True)])
+def test_deterministic(gate, strong):
+    # every sum has a fixed order, the per-head gate's sums over keys included
+    # (strong gates: in the token-by-token kernel)
+    d = gi.draw(900, 2, 300, 2, 128, 128, dtype="bf16", h0=True, gate=gate, gate_scale=40.0 if strong else 1.0 / 16.0)
     do, dht = grads_in(d, "bf16", 18)
+    say(f"bwd determinism: B=2 T=300 H=2 K=V=128 bf16 gate={gate} strong={strong}")
     a = run_bwd_gpu(d, do, dht, "bf16")
     b = run_bwd_gpu(d, do, dht, "bf16")
-    for x, y in zip(a, b):
-        assert np.array_equal(x, y)
+    for name, x, y in zip(("dq", "dk", "dv", "dg", "dh0"), a, b):
+        assert np.array_equal(x, y), name
 
 
 def head_slice(d, heads):
@@ -200,3 +222,64 @@ def test_workload_sampled_heads(name):
         tol = TOL_HT if name_ in ("dg", "dh0") else TOL[w.dtype]
         errs[name_] = check_close(name_, a, b, tol, out_dtype="fp32" if name_ in ("dg", "dh0") else w.dtype)
     say("   max|err|/rms: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+@pytest.mark.parametrize("dtype,gate", [("bf16", "key"), ("fp32", "key"), ("bf16", "head")])
+def test_chained_scan_matches_separate_scan(dtype, gate):
+    """The chained scan applies the separate scan's recurrences in the same
+    order and precision to the same summaries: every output agrees bit for bit.
+    Many chains of many chunks (B=4, H=16, T=1000: 64 chains of 16 chunks per
+    direction) cross workgroups on different dies; the oracle checks two heads."""
+    d = gi.draw(920, 4, 1000, 16, 128, 128, dtype=dtype, h0=True, gate=gate)
+    do, dht = grads_in(d, dtype, 21)
+    say(f"bwd chained vs separate scan: B=4 T=1000 H=16 K=V=128 {dtype} gate={gate}")
+    a = run_bwd_gpu(d, do, dht, dtype, schedule=1)
+    b = run_bwd_gpu(d, do, dht, dtype, schedule=2)
+    for name, x, y in zip(("dq", "dk", "dv", "dg", "dh0"), a, b):
+        assert np.array_equal(x, y), f"{name}: max|diff| {np.max(np.abs(x - y)):.3e}"
+    heads = [3, 14]
+    ds = head_slice(d, heads)
+    ref = oracle.gla_reference_bwd(ds["q"], ds["k"], ds["v"], ds["g"], np.ascontiguousarray(do[:, :, heads]),
+                                   h0=ds["h0"], dht=np.ascontiguousarray(dht[:, heads]))
+    for name, x, r in zip(("dq", "dk", "dv", "dg", "dh0"), b, ref):
+        x = x[:, heads] if name == "dh0" else x[:, :, heads]
+        check_close(name, x, r, TOL_HT if name in ("dg", "dh0") else TOL[dtype],
+                    out_dtype="fp32" if name in ("dg", "dh0") else dtype)
+
+
+def test_chained_scan_repeated_calls():
+    """Back-to-back chained backward calls on one workspace: each call clears
+    the chains' flags before its summary kernel, so no call sees another's."""
+    import torch
+    import chunkwise_gated_linear_amd as gla
+    d = gi.draw(930, 8, 300, 8, 64, 64, dtype="bf16", h0=True)
+    do, dht = grads_in(d, "bf16", 22)
+    ref = run_bwd_gpu(d, do, dht, "bf16", schedule=1)
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(d[n]).to(torch.bfloat16).to(dev) for n in ("q", "k", "v")}
+    g, h0 = torch.from_numpy(d["g"]).to(dev), torch.from_numpy(d["h0"]).to(dev)
+    tdo, tdht = torch.from_numpy(do).to(torch.bfloat16).to(dev), torch.from_numpy(dht).to(dev)
+    prob, _, _ = gla._problem_for(t["q"], t["k"], t["v"], g, h0, None, None, None, 64, 0, 0, 0, 2)
+    ws = torch.zeros(gla.bwd_workspace_bytes(prob), dtype=torch.uint8, device=dev)
+    say("bwd chained: 5 calls on one workspace, B=8 T=300 H=8 K=V=64 bf16")
+    outs = [gla.gla_bwd(t["q"], t["k"], t["v"], g, tdo, h0=h0, dht=tdht, workspace=ws, schedule=2)
+            for _ in range(5)]
+    torch.cuda.synchronize()
+    assert gla.read_status(ws) == 0
+    for out in outs:
+        for name, x, y in zip(("dq", "dk", "dv", "dg", "dh0"), out, ref):
+            assert np.array_equal(x.float().cpu().numpy().astype(np.float64), y), name
+
+
+def test_chained_scan_wait_bound_reports():
+    """wait_limit = -1 turns every wait of the chained scan into an immediate
+    report: the kernels still end, and the status word says the results are
+    not to be trusted.  The separate scan has no waits and reports nothing."""
+    d = gi.draw(940, 2, 300, 2, 64, 64, dtype="bf16", h0=True)
+    do, dht = grads_in(d, "bf16", 23)
+    say("bwd chained with wait_limit=-1 (status report), B=2 T=300 H=2 K=V=64 bf16")
+    st = []
+    run_bwd_gpu(d, do, dht, "bf16", schedule=2, wait_limit=-1, status=st)
+    run_bwd_gpu(d, do, dht, "bf16", schedule=1, wait_limit=-1, status=st)
+    assert st[0] & 1 == 1
+    assert st[1] == 0
