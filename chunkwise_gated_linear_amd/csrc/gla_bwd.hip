@@ -90,6 +90,17 @@ __device__ __forceinline__ void st_el(void *base, int64_t i, float x) {
   if constexpr (BF) reinterpret_cast<__bf16 *>(base)[i] = (__bf16)x;
   else reinterpret_cast<float *>(base)[i] = x;
 }
+// One element through a buffer descriptor (byte offset; past the range:
+// dropped / zero), as bf16 (rounded to nearest even) or fp32.
+template <bool BF>
+__device__ __forceinline__ void bst_el(__amdgpu_buffer_rsrc_t r, int off, float x) {
+  if constexpr (BF) __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)x), r, off, 0, 0);
+  else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+}
+__device__ __forceinline__ float bld_f32(__amdgpu_buffer_rsrc_t r, int off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+constexpr int kOutsideRange = 0x40000000;  // a byte offset past any descriptor's range
 
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 
@@ -149,14 +160,32 @@ template <bool BF> struct RawQuad;
 template <> struct RawQuad<true> { typedef u32x2_t type; };
 template <> struct RawQuad<false> { typedef f32x4_t type; };
 template <bool BF>
-__device__ __forceinline__ typename RawQuad<BF>::type ld_raw4(const void *base, int64_t i) {
-  if constexpr (BF) return *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(base) + i);
-  else return *reinterpret_cast<const f32x4_t *>(reinterpret_cast<const float *>(base) + i);
-}
-template <bool BF>
 __device__ __forceinline__ f32x4_t unpack4(typename RawQuad<BF>::type w) {
   if constexpr (BF) return f32x4_t{bf_lo(w[0]), bf_hi(w[0]), bf_lo(w[1]), bf_hi(w[1])};
   else return w;
+}
+
+// A chunk's token rows of one head in a [.., T, heads, width] tensor, through
+// a buffer descriptor from its first row: rows `stride` elements apart, rows
+// past the chunk's L tokens outside the range (they read zero), 32-bit
+// offsets.
+struct ChunkRowsRsrc {
+  __amdgpu_buffer_rsrc_t r;
+  int stride, width;
+};
+template <bool BF>
+__device__ __forceinline__ ChunkRowsRsrc chunk_rows(const void *base, int64_t first, int stride, int width, int L) {
+  constexpr int ES = BF ? 2 : 4;
+  return {make_rsrc(static_cast<const char *>(base) + first * ES, ((int64_t)(L - 1) * stride + width) * ES), stride,
+          width};
+}
+// Quad c4 of row i (c4 a multiple of 4; quads past the width read zero).
+template <bool BF>
+__device__ __forceinline__ typename RawQuad<BF>::type ld_row4(const ChunkRowsRsrc &rr, int i, int c4) {
+  constexpr int ES = BF ? 2 : 4;
+  const int off = c4 < rr.width ? (i * rr.stride + c4) * ES : kOutsideRange;
+  if constexpr (BF) return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rr.r, off, 0, 0));
+  else return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rr.r, off, 0, 0));
 }
 
 // Gate rows of a chunk (value head hv) into registers: quad t of thread
@@ -172,11 +201,11 @@ __device__ __forceinline__ void gate_load(const WalkParams &p, const ChunkAt &ca
   if constexpr (GH) {
     gr.gh = threadIdx.x < ca.L ? p.g[(ca.row0 + threadIdx.x) * p.HV + hv] : 0.f;
   } else {
+    const ChunkRowsRsrc rg = chunk_rows<false>(p.g, (ca.row0 * p.HV + hv) * p.K, p.HV * p.K, p.K, ca.L);
 #pragma unroll
     for (int t = 0; t < GateRows<KD, GH, NT>::TG; ++t) {
       const int e = threadIdx.x + NT * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
-      gr.g[t] = zero4();
-      if (i < ca.L && c4 < p.K) gr.g[t] = *reinterpret_cast<const f32x4_t *>(p.g + ((ca.row0 + i) * p.HV + hv) * p.K + c4);
+      gr.g[t] = ld_row4<false>(rg, i, c4);
     }
   }
 }
@@ -322,20 +351,18 @@ __device__ __forceinline__ void local_load(const BwdParams &bp, const LocalTask 
   const WalkParams &p = bp.w;
   const ChunkAt &ca = lt.ca;
   const int h = lt.hv / p.G;
-  const void *xs = lt.grad ? p.q : p.k;      // key-side rows
-  const void *ys = lt.grad ? bp.dout : p.v;  // value-side rows
+  const ChunkRowsRsrc rx = chunk_rows<BF>(lt.grad ? p.q : p.k, (ca.row0 * p.H + h) * p.K, p.H * p.K, p.K, ca.L);
+  const ChunkRowsRsrc ry = chunk_rows<BF>(lt.grad ? bp.dout : p.v, (ca.row0 * p.HV + lt.hv) * p.V, p.HV * p.V, p.V, ca.L);
 #pragma unroll
   for (int t = 0; t < R::TK; ++t) {
     const int e = threadIdx.x + 256 * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
-    rw.x[t] = {};
-    if (i < ca.L && c4 < p.K) rw.x[t] = ld_raw4<BF>(xs, (ca.row0 + i) * p.H * p.K + h * p.K + c4);
+    rw.x[t] = ld_row4<BF>(rx, i, c4);  // key-side rows: k, or q for the gradient
   }
   gate_load<KD, GH, 256>(p, ca, lt.hv, rw.gate);
 #pragma unroll
   for (int t = 0; t < R::TV; ++t) {
     const int e = threadIdx.x + 256 * t, i = e / (VD / 4), c4 = (e % (VD / 4)) * 4;
-    rw.y[t] = {};
-    if (i < ca.L && c4 < p.V) rw.y[t] = ld_raw4<BF>(ys, ((ca.row0 + i) * p.HV + lt.hv) * p.V + c4);
+    rw.y[t] = ld_row4<BF>(ry, i, c4);  // value-side rows: v, or do
   }
 }
 
@@ -746,25 +773,22 @@ __device__ __forceinline__ void chunk_load(const BwdParams &bp, const ChunkAt &c
   using R = ChunkRows<BF, KD, VD, GH>;
   const WalkParams &p = bp.w;
   const int h = hv / p.G;
+  const int64_t fk = (ca.row0 * p.H + h) * p.K, fv = (ca.row0 * p.HV + hv) * p.V;
+  const ChunkRowsRsrc rq = chunk_rows<BF>(p.q, fk, p.H * p.K, p.K, ca.L);
+  const ChunkRowsRsrc rk = chunk_rows<BF>(p.k, fk, p.H * p.K, p.K, ca.L);
+  const ChunkRowsRsrc ro = chunk_rows<BF>(bp.dout, fv, p.HV * p.V, p.V, ca.L);
+  const ChunkRowsRsrc rv = chunk_rows<BF>(p.v, fv, p.HV * p.V, p.V, ca.L);
 #pragma unroll
   for (int t = 0; t < R::TK; ++t) {
     const int e = threadIdx.x + R::NT * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
-    rw.q[t] = rw.k[t] = {};
-    if (i < ca.L && c4 < p.K) {
-      const int64_t off = (ca.row0 + i) * p.H * p.K + h * p.K + c4;
-      rw.q[t] = ld_raw4<BF>(p.q, off);
-      rw.k[t] = ld_raw4<BF>(p.k, off);
-    }
+    rw.q[t] = ld_row4<BF>(rq, i, c4);
+    rw.k[t] = ld_row4<BF>(rk, i, c4);
   }
 #pragma unroll
   for (int t = 0; t < R::TV; ++t) {
     const int e = threadIdx.x + R::NT * t, i = e / (VD / 4), c4 = (e % (VD / 4)) * 4;
-    rw.v[t] = rw.o[t] = {};
-    if (i < ca.L && c4 < p.V) {
-      const int64_t off = ((ca.row0 + i) * p.HV + hv) * p.V + c4;
-      rw.o[t] = ld_raw4<BF>(bp.dout, off);
-      rw.v[t] = ld_raw4<BF>(p.v, off);
-    }
+    rw.o[t] = ld_row4<BF>(ro, i, c4);
+    rw.v[t] = ld_row4<BF>(rv, i, c4);
   }
   gate_load<KD, GH, R::NT>(p, ca, hv, rw.gate);
 }
@@ -791,7 +815,8 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
   __shared__ float tot[NT];
   __shared__ float sRow[NW * 64];  // per-head gate: dg of each row summed over each wave's keys
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
   const int kb = wave * 16;                                        // this wave's key block
   const int vb0 = (JSPLIT > 1 ? wave % NVBLK : wave * NVB) * 16;   // first value column of its blocks
   const int jb0 = JSPLIT > 1 ? (wave / NVBLK) * NJB : 0;           // first row block (value space)
@@ -805,6 +830,24 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
     const int L = ca.L;
     const int64_t row0 = ca.row0;
     const int cfirst = ca.si.first, cc = ca.c;
+    // The outputs leave through buffer descriptors over this chunk's token
+    // rows: rows past its last token lie outside the range, so their stores
+    // are dropped without a branch, and the offsets are 32-bit.  (K and V are
+    // multiples of 16, so a key or value block is wholly inside or outside.)
+    // dq, dk: [B,T,H,K] in the input dtype with one value head per key head
+    // (then H = HV), else this value head's fp32 share [B,T,HV,K].
+    constexpr int ES = BF ? 2 : 4;
+    const bool part = p.G > 1;
+    const int ESQ = part ? 4 : ES;
+    const int strideV = p.HV * p.V, strideK = p.HV * p.K;  // elements between token rows
+    const __amdgpu_buffer_rsrc_t rDv =
+        make_rsrc(static_cast<char *>(bp.dv) + (row0 * p.HV + chv) * p.V * ES, ((int64_t)(L - 1) * strideV + p.V) * ES);
+    const int64_t qk0 = (row0 * p.HV + chv) * p.K, qkBytes = ((int64_t)(L - 1) * strideK + p.K) * ESQ;
+    const __amdgpu_buffer_rsrc_t rDq =
+        make_rsrc(part ? static_cast<char *>(static_cast<void *>(bp.dq_part)) + qk0 * 4 : static_cast<char *>(bp.dq) + qk0 * ES, qkBytes);
+    const __amdgpu_buffer_rsrc_t rDk =
+        make_rsrc(part ? static_cast<char *>(static_cast<void *>(bp.dk_part)) + qk0 * 4 : static_cast<char *>(bp.dk) + qk0 * ES, qkBytes);
+    const __amdgpu_buffer_rsrc_t rDg = make_rsrc(GH ? bp.dg : bp.dg + qk0, GH ? 0 : ((int64_t)(L - 1) * strideK + p.K) * 4);
     // G -> sV; q e^G, k e^-G -> sQ, sK; this lane's G values; the chunk's decay per key
     gate_stage<KD, GH, NT>(rw.gate, sV);
     __syncthreads();
@@ -946,6 +989,7 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
     // ---- inter-chunk terms: dq = do S_c^T, dkI = v E_c^T, rs = rowsum(S_c . E_c)
     const float *Sc = bp.fstate + ((int64_t)(cfirst + cc) * p.HV + chv) * p.K * p.V;
     const float *Ec = bp.dstate + ((int64_t)(cfirst + cc) * p.HV + chv) * p.K * p.V;
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(Sc, (int64_t)p.K * p.V * 4), rE = make_rsrc(Ec, (int64_t)p.K * p.V * 4);
     f32x4_t dq[4], dkI[4];
     float rs = 0.f;
 #pragma unroll
@@ -962,13 +1006,11 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
       for (int v0 = 0; v0 < VD; v0 += 32) {
         const int col = v0 + 8 * lg;
         const bool in = krow < p.K && col < p.V;  // V is a multiple of 16: col < V covers col + 7
-        const int64_t off = (int64_t)krow * p.V + col;
+        const int off = in ? (krow * p.V + col) * 4 : kOutsideRange;
         float sv[8], ev[8];
         {
-          const f32x4_t s0 = in ? *reinterpret_cast<const f32x4_t *>(Sc + off) : zero4();
-          const f32x4_t s1 = in ? *reinterpret_cast<const f32x4_t *>(Sc + off + 4) : zero4();
-          const f32x4_t e0 = in ? *reinterpret_cast<const f32x4_t *>(Ec + off) : zero4();
-          const f32x4_t e1 = in ? *reinterpret_cast<const f32x4_t *>(Ec + off + 4) : zero4();
+          const f32x4_t s0 = buf_ldf4<0>(rS, off), s1 = buf_ldf4<0>(rS, off + 16);
+          const f32x4_t e0 = buf_ldf4<0>(rE, off), e1 = buf_ldf4<0>(rE, off + 16);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             sv[r] = s0[r]; sv[4 + r] = s1[r];
@@ -1002,9 +1044,8 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
       for (int v0 = 0; v0 < VD; v0 += 16) {
         const int col = v0 + 4 * lg;
         const bool in = krow < p.K && col < p.V;
-        const int64_t off = (int64_t)krow * p.V + col;
-        const f32x4_t s4 = in ? *reinterpret_cast<const f32x4_t *>(Sc + off) : zero4();
-        const f32x4_t e4 = in ? *reinterpret_cast<const f32x4_t *>(Ec + off) : zero4();
+        const int off = in ? (krow * p.V + col) * 4 : kOutsideRange;
+        const f32x4_t s4 = buf_ldf4<0>(rS, off), e4 = buf_ldf4<0>(rE, off);
         rs += s4[0] * e4[0] + s4[1] * e4[1] + s4[2] * e4[2] + s4[3] * e4[3];
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {
@@ -1029,12 +1070,12 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
         u32x4_t eh[NVB], elo[NVB];
 #pragma unroll
         for (int b = 0; b < NVB; ++b) {
+          // keys past K lie past the state's range; a value block past V is
+          // sent outside it
+          const int cb = vb0 + b * 16 < p.V ? ((k0 + 8 * lg) * p.V + vb0 + b * 16 + l16) * 4 : kOutsideRange;
           float e8[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int krow = k0 + 8 * lg + e, col = vb0 + b * 16 + l16;
-            e8[e] = (krow < p.K && col < p.V) ? Ec[(int64_t)krow * p.V + col] : 0.f;
-          }
+          for (int e = 0; e < 8; ++e) e8[e] = bld_f32(rE, cb + e * p.V * 4);
           split8_2(e8, eh[b], elo[b]);
         }
         const f32x4_t el0 = *reinterpret_cast<const f32x4_t *>(sEl + k0 + 8 * lg);
@@ -1064,12 +1105,11 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
         const f32x4_t el4 = *reinterpret_cast<const f32x4_t *>(sEl + k0 + 4 * lg);
         float ev[NVB][4];
 #pragma unroll
-        for (int b = 0; b < NVB; ++b)
+        for (int b = 0; b < NVB; ++b) {
+          const int cb = vb0 + b * 16 < p.V ? ((k0 + 4 * lg) * p.V + vb0 + b * 16 + l16) * 4 : kOutsideRange;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int krow = k0 + 4 * lg + r, col = vb0 + b * 16 + l16;
-            ev[b][r] = (krow < p.K && col < p.V) ? Ec[(int64_t)krow * p.V + col] : 0.f;
-          }
+          for (int r = 0; r < 4; ++r) ev[b][r] = bld_f32(rE, cb + r * p.V * 4);
+        }
 #pragma unroll
         for (int j = 0; j < NJB; ++j) {
           const f32x4_t k4 = lds4<KD>(sK, (jb0 + j) * 16 + l16, k0 + 4 * lg) * el4;
@@ -1081,14 +1121,16 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
       }
     }
 #pragma unroll
-    for (int b = 0; b < NVB; ++b)
+    for (int b = 0; b < NVB; ++b) {
+      if (vb0 + b * 16 >= p.V) continue;  // uniform over the wave
 #pragma unroll
       for (int j = 0; j < NJB; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = (jb0 + j) * 16 + 4 * lg + r, col = vb0 + b * 16 + l16;
-          if (row < L && col < p.V) st_el<BF>(bp.dv, ((row0 + row) * p.HV + chv) * p.V + col, dv[b][j][r]);
+          bst_el<BF>(rDv, (row * strideV + col) * ES, dv[b][j][r]);
         }
+    }
 
     // ---- dq = scale (do S_c^T) + dA' (k e^-G)
 #pragma unroll
@@ -1139,7 +1181,16 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
           const float kdkI = kg * el * dkI[b][r];
           const float dqv = __expf(Gv) * dq[b][r];
           const float dkv = __expf(-Gv) * dkA[b][r] + __expf(gl - Gv) * dkI[b][r];
-          if (i < L && k < p.K) store_dqk<BF>(bp, row0 + i, chv, k, dqv, dkv);
+          if (kb < p.K) {  // uniform over the wave; rows past the chunk fall outside the range
+            const int off = i * strideK + k;
+            if (part) {
+              bst_el<false>(rDq, off * 4, dqv);
+              bst_el<false>(rDk, off * 4, dkv);
+            } else {
+              bst_el<BF>(rDq, off * ES, dqv);
+              bst_el<BF>(rDk, off * ES, dkv);
+            }
+          }
           t[b][r] = qg * dq[b][r] - (kg * dkA[b][r] + kdkI);
           colk += kdkI;
         }
@@ -1166,7 +1217,7 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
           run += t[b][r];
           const int i = b * 16 + 4 * lg + r;
           if constexpr (GH) runv[b][r] = k < p.K ? run : 0.f;
-          else if (i < L && k < p.K) bp.dg[((row0 + i) * p.HV + chv) * p.K + k] = run;
+          else if (kb < p.K) bst_el<false>(rDg, (i * strideK + k) * 4, run);
         }
         carry += total;
       }

@@ -325,7 +325,11 @@ BwdPlan make_bwd_plan(const gla_problem *p, bool varlen) {
   b.total = cur;
   const long long scan_blocks = 2LL * pl.N * HV * ((p->K * p->V / 4 + 255) / 256);
   const long long rows_quads = (long long)p->B * p->T * p->H * (p->K / 4);
-  b.ok = pl.ok && 2 * slots * HV <= INT_MAX && scan_blocks <= INT_MAX && (rows_quads + 255) / 256 <= INT_MAX;
+  // the chunk kernel addresses a chunk's 64 token rows of an output with
+  // 32-bit byte offsets
+  const long long row_bytes = 64LL * HV * (p->K > p->V ? p->K : p->V) * 4;
+  b.ok = pl.ok && 2 * slots * HV <= INT_MAX && scan_blocks <= INT_MAX && (rows_quads + 255) / 256 <= INT_MAX &&
+         row_bytes <= INT_MAX;
   return b;
 }
 
