@@ -289,9 +289,9 @@ __device__ __forceinline__ u32x4_t pack8(const float (&x)[8]) {
 // step order (step s: chunk s of every state chain, chunk P-1-s of every
 // gradient chain), so a task's predecessor always has a lower number and has
 // been taken by a running workgroup: the chains always move.  A published
-// state is written and read only with device-scope stores and loads (those
-// of relaxed agent-scope atomics: no compute unit or die serves them from a
-// private copy); every wave waits for its stores to complete before a
+// state is written and read only with device-scope stores and loads (the sc1
+// cache policy that relaxed agent-scope atomics use: no compute unit or die
+// serves them from a private copy); every wave waits for its stores to complete before a
 // barrier, after which one lane sets the flag, and the successor loads the
 // state only after it has seen the flag (polled within the bound
 // wait_polls).  No cache-wide write-back or invalidation is needed for that,
