@@ -352,7 +352,8 @@ __device__ __forceinline__ void local_load(const BwdParams &bp, const LocalTask 
   const ChunkAt &ca = lt.ca;
   const int h = lt.hv / p.G;
   const ChunkRowsRsrc rx = chunk_rows<BF>(lt.grad ? p.q : p.k, (ca.row0 * p.H + h) * p.K, p.H * p.K, p.K, ca.L);
-  const ChunkRowsRsrc ry = chunk_rows<BF>(lt.grad ? bp.dout : p.v, (ca.row0 * p.HV + lt.hv) * p.V, p.HV * p.V, p.V, ca.L);
+  const ChunkRowsRsrc ry =
+      chunk_rows<BF>(lt.grad ? bp.dout : p.v, (ca.row0 * p.HV + lt.hv) * bp.Vmem, p.HV * bp.Vmem, p.V, ca.L);
 #pragma unroll
   for (int t = 0; t < R::TK; ++t) {
     const int e = threadIdx.x + 256 * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
@@ -394,6 +395,8 @@ __device__ __forceinline__ void chain_step(const BwdParams &bp, const LocalTask 
   const int64_t KV = (int64_t)p.K * p.V;
   float *tab = lt.grad ? bp.dstate : bp.fstate;
   int32_t *flags = bp.chain + 1 + (lt.grad ? (int64_t)p.seg_slots * p.HV : 0);
+  // h0, dht, dh0 and the state slots are all [K][V] here (the chained
+  // schedule runs with one value slice, Vmem = V)
   const float *bound = lt.grad ? bp.dht : p.h0;
   if (bound != nullptr) bound += ((int64_t)n * p.HV + lt.hv) * KV;
   const int next = lt.grad ? lt.slot - 1 : lt.slot + 1;
@@ -671,7 +674,7 @@ __global__ __launch_bounds__(256) void gla_bwd_scan(BwdParams bp, int per_state)
   }
   const int nc = min((len + kChunk - 1) / kChunk, nseg);
   const int krow = (4 * e4) / p.V, col = 4 * e4 - krow * p.V;
-  const int64_t sidx = (((int64_t)n * p.HV + hv) * p.K + krow) * p.V + col;
+  const int64_t sidx = (((int64_t)n * p.HV + hv) * p.K + krow) * bp.Vmem + col;  // h0, dht, dh0 element
   constexpr int BATCH = 16;
   auto cell = [&](float *base, int c) {
     return reinterpret_cast<f32x4_t *>(base + ((int64_t)(first + c) * p.HV + hv) * p.K * p.V) + e4;
@@ -720,13 +723,14 @@ __global__ __launch_bounds__(256) void gla_bwd_scan(BwdParams bp, int per_state)
 }
 
 // ---------------------------------------------------------------- dq / dk stores
-// dq and dk belong to key heads.  With one value head per key head they are
-// stored in the input dtype; with G > 1 each value head stores its fp32 share
-// to dq_part / dk_part [B,T,HV,K] and gla_bwd_group_sum adds the G shares.
+// dq and dk belong to key heads.  With one value head per key head and one
+// value slice they are stored in the input dtype; otherwise each value head
+// (and slice) stores its fp32 share to dq_part / dk_part [B,T,HV,K] and
+// gla_bwd_group_sum adds the shares.
 template <bool BF>
 __device__ __forceinline__ void store_dqk(const BwdParams &bp, int64_t row, int hv, int k, float dqv, float dkv) {
   const WalkParams &p = bp.w;
-  if (p.G == 1) {
+  if (bp.dq_part == nullptr) {
     const int64_t off = (row * p.H + hv) * p.K + k;
     st_el<BF>(bp.dq, off, dqv);
     st_el<BF>(bp.dk, off, dkv);
@@ -773,11 +777,11 @@ __device__ __forceinline__ void chunk_load(const BwdParams &bp, const ChunkAt &c
   using R = ChunkRows<BF, KD, VD, GH>;
   const WalkParams &p = bp.w;
   const int h = hv / p.G;
-  const int64_t fk = (ca.row0 * p.H + h) * p.K, fv = (ca.row0 * p.HV + hv) * p.V;
+  const int64_t fk = (ca.row0 * p.H + h) * p.K, fv = (ca.row0 * p.HV + hv) * bp.Vmem;
   const ChunkRowsRsrc rq = chunk_rows<BF>(p.q, fk, p.H * p.K, p.K, ca.L);
   const ChunkRowsRsrc rk = chunk_rows<BF>(p.k, fk, p.H * p.K, p.K, ca.L);
-  const ChunkRowsRsrc ro = chunk_rows<BF>(bp.dout, fv, p.HV * p.V, p.V, ca.L);
-  const ChunkRowsRsrc rv = chunk_rows<BF>(p.v, fv, p.HV * p.V, p.V, ca.L);
+  const ChunkRowsRsrc ro = chunk_rows<BF>(bp.dout, fv, p.HV * bp.Vmem, p.V, ca.L);
+  const ChunkRowsRsrc rv = chunk_rows<BF>(p.v, fv, p.HV * bp.Vmem, p.V, ca.L);
 #pragma unroll
   for (int t = 0; t < R::TK; ++t) {
     const int e = threadIdx.x + R::NT * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
@@ -835,13 +839,14 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
     // are dropped without a branch, and the offsets are 32-bit.  (K and V are
     // multiples of 16, so a key or value block is wholly inside or outside.)
     // dq, dk: [B,T,H,K] in the input dtype with one value head per key head
-    // (then H = HV), else this value head's fp32 share [B,T,HV,K].
+    // (then H = HV) and one value slice, else this value head's and slice's
+    // fp32 share [B,T,HV,K].  dv: [B,T,HV,Vmem], this launch's columns.
     constexpr int ES = BF ? 2 : 4;
-    const bool part = p.G > 1;
+    const bool part = bp.dq_part != nullptr;
     const int ESQ = part ? 4 : ES;
-    const int strideV = p.HV * p.V, strideK = p.HV * p.K;  // elements between token rows
+    const int strideV = p.HV * bp.Vmem, strideK = p.HV * p.K;  // elements between token rows
     const __amdgpu_buffer_rsrc_t rDv =
-        make_rsrc(static_cast<char *>(bp.dv) + (row0 * p.HV + chv) * p.V * ES, ((int64_t)(L - 1) * strideV + p.V) * ES);
+        make_rsrc(static_cast<char *>(bp.dv) + (row0 * p.HV + chv) * bp.Vmem * ES, ((int64_t)(L - 1) * strideV + p.V) * ES);
     const int64_t qk0 = (row0 * p.HV + chv) * p.K, qkBytes = ((int64_t)(L - 1) * strideK + p.K) * ESQ;
     const __amdgpu_buffer_rsrc_t rDq =
         make_rsrc(part ? static_cast<char *>(static_cast<void *>(bp.dq_part)) + qk0 * 4 : static_cast<char *>(bp.dq) + qk0 * ES, qkBytes);
@@ -1298,7 +1303,7 @@ __global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
   }
   for (int e = threadIdx.x; e < 64 * VD; e += 256) {
     const int i = e / VD, c = e % VD;
-    sV[e] = (i < L && c < p.V) ? ld_el<BF>(p.v, ((row0 + i) * p.HV + hv) * p.V + c) : 0.f;
+    sV[e] = (i < L && c < p.V) ? ld_el<BF>(p.v, ((row0 + i) * p.HV + hv) * bp.Vmem + c) : 0.f;
   }
   if (GH && threadIdx.x < 64) sRow[threadIdx.x] = 0.f;
   __syncthreads();
@@ -1307,7 +1312,7 @@ __global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
   const float *Ec = bp.dstate + ((int64_t)(ca.si.first + ca.c) * p.HV + hv) * p.K * p.V;
   auto dout = [&](int i, int j) -> float {  // do at token i, column col0 + j
     const int col = col0 + j;
-    return col < p.V ? ld_el<BF>(bp.dout, ((row0 + i) * p.HV + hv) * p.V + col) : 0.f;
+    return col < p.V ? ld_el<BF>(bp.dout, ((row0 + i) * p.HV + hv) * bp.Vmem + col) : 0.f;
   };
   auto reduce = [&](float x) {
 #pragma unroll
@@ -1396,7 +1401,7 @@ __global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
     }
     for (int col = threadIdx.x; col < p.V; col += 256) {
       const float sv = sRed[col] + sRed[VD + col] + sRed[2 * VD + col] + sRed[3 * VD + col];
-      st_el<BF>(bp.dv, ((row0 + i) * p.HV + hv) * p.V + col, sv);
+      st_el<BF>(bp.dv, ((row0 + i) * p.HV + hv) * bp.Vmem + col, sv);
     }
 #pragma unroll
     for (int j = 0; j < NC; ++j) U[j] *= a;
@@ -1406,10 +1411,12 @@ __global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
 }
 
 // ---------------------------------------------------------------- gla_bwd_group_sum
-// dq, dk of key head h = the sum of the fp32 shares of its G value heads,
-// rounded once to the output dtype.  One thread per 4 keys of a token row.
+// dq, dk of key head h = the sum of the fp32 shares of its G value heads over
+// every value slice (slices `slice_stride` floats apart), rounded once to the
+// output dtype.  One thread per 4 keys of a token row.
 template <bool BF>
-__global__ __launch_bounds__(256) void gla_bwd_group_sum(BwdParams bp, int64_t quads) {
+__global__ __launch_bounds__(256) void gla_bwd_group_sum(BwdParams bp, int64_t quads, int slices,
+                                                         int64_t slice_stride) {
   const WalkParams &p = bp.w;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= quads) return;
@@ -1419,17 +1426,27 @@ __global__ __launch_bounds__(256) void gla_bwd_group_sum(BwdParams bp, int64_t q
   const int64_t row = rowh / p.H;
   const int h = (int)(rowh - row * p.H);
   f32x4_t dq = zero4(), dk = zero4();
-  for (int gi = 0; gi < p.G; ++gi) {
-    const int64_t off = (row * p.HV + h * p.G + gi) * p.K + k;
-    dq += *reinterpret_cast<const f32x4_t *>(bp.dq_part + off);
-    dk += *reinterpret_cast<const f32x4_t *>(bp.dk_part + off);
-  }
+  for (int sl = 0; sl < slices; ++sl)
+    for (int gi = 0; gi < p.G; ++gi) {
+      const int64_t off = sl * slice_stride + (row * p.HV + h * p.G + gi) * p.K + k;
+      dq += *reinterpret_cast<const f32x4_t *>(bp.dq_part + off);
+      dk += *reinterpret_cast<const f32x4_t *>(bp.dk_part + off);
+    }
   const int64_t off = rowh * p.K + k;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     st_el<BF>(bp.dq, off + r, dq[r]);
     st_el<BF>(bp.dk, off + r, dk[r]);
   }
+}
+
+// dg with several value slices: out[e] = the sum of the slices' fp32 shares.
+__global__ __launch_bounds__(256) void gla_bwd_slice_sum(float *out, const float *parts, int64_t n, int slices) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  float x = 0.f;
+  for (int sl = 0; sl < slices; ++sl) x += parts[sl * n + e];
+  out[e] = x;
 }
 
 template <bool BF, int KD, int VD, bool GH>
@@ -1471,16 +1488,38 @@ hipError_t launch_bwd_local(bool bf16, const BwdParams &bp, hipStream_t s) { ret
 hipError_t launch_bwd_chunk(bool bf16, const BwdParams &bp, hipStream_t s) {
   hipError_t e = launch_bwd_kernel(1, bf16, bp, s);
   if (e != hipSuccess) return e;
-  e = launch_bwd_kernel(2, bf16, bp, s);
-  if (e != hipSuccess || bp.w.G == 1) return e;
+  return launch_bwd_kernel(2, bf16, bp, s);
+}
+
+hipError_t launch_bwd_finish(bool bf16, const BwdParams &bp, int slices, const float *dg_parts, float *dg,
+                             hipStream_t s) {
   const long long rows = (bp.w.cu ? 1LL : (long long)bp.w.N) * bp.w.T;  // token rows of [B,T]
-  const long long quads = rows * bp.w.H * (bp.w.K / 4);
-  if (quads <= 0) return hipSuccess;
-  const long long blocks = (quads + 255) / 256;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (bf16) hipLaunchKernelGGL(gla_bwd_group_sum<true>, dim3((unsigned)blocks), dim3(256), 0, s, bp, (int64_t)quads);
-  else hipLaunchKernelGGL(gla_bwd_group_sum<false>, dim3((unsigned)blocks), dim3(256), 0, s, bp, (int64_t)quads);
-  return hipGetLastError();
+  if (bp.dq_part != nullptr) {
+    const long long quads = rows * bp.w.H * (bp.w.K / 4);
+    const long long blocks = (quads + 255) / 256;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    const int64_t stride = rows * bp.w.HV * bp.w.K;
+    if (blocks > 0) {
+      if (bf16)
+        hipLaunchKernelGGL(gla_bwd_group_sum<true>, dim3((unsigned)blocks), dim3(256), 0, s, bp, (int64_t)quads, slices,
+                           stride);
+      else
+        hipLaunchKernelGGL(gla_bwd_group_sum<false>, dim3((unsigned)blocks), dim3(256), 0, s, bp, (int64_t)quads,
+                           slices, stride);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  if (slices > 1) {
+    const long long n = rows * bp.w.HV * (bp.w.gate_head ? 1 : bp.w.K);
+    const long long blocks = (n + 255) / 256;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (blocks > 0) {
+      hipLaunchKernelGGL(gla_bwd_slice_sum, dim3((unsigned)blocks), dim3(256), 0, s, dg, dg_parts, (int64_t)n, slices);
+      return hipGetLastError();
+    }
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_bwd_scan(const BwdParams &bp, hipStream_t s) {

@@ -289,10 +289,14 @@ gla_status run_forward(const gla_problem *p, const Plan &pl, const void *q, cons
 }
 
 // Backward: one chunk per slot (the forward's segment numbering with R = 1),
-// and the backward's tables.  K and V of at most 128.
+// and the backward's tables.  K of at most 128; V is cut into value slices of
+// at most 128 columns, run one after another over the same state tables.
+constexpr int kBwdSlice = 128;
+int bwd_slices(int V) { return (V + kBwdSlice - 1) / kBwdSlice; }
+
 struct BwdPlan {
   Plan fwd;  // slot numbering only (R = 1)
-  size_t off_base, off_fstate, off_dstate, off_ddecay, off_flags, off_dq_part, off_dk_part, total;
+  size_t off_base, off_fstate, off_dstate, off_ddecay, off_flags, off_dq_part, off_dk_part, off_dg_part, total;
   bool ok;
 };
 
@@ -305,25 +309,32 @@ BwdPlan make_bwd_plan(const gla_problem *p, bool varlen) {
   const long long HV = p->HV == 0 ? p->H : p->HV;
   const long long G = HV / p->H;
   const long long slots = pl.seg_slots;
+  const int slices = bwd_slices(p->V);
+  const long long Vs = p->V < kBwdSlice ? p->V : kBwdSlice;  // widest slice
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t cur = kHeaderBytes;
   b.off_base = cur;
   cur += up(varlen ? (size_t)(pl.N + 1 + slots) * sizeof(int32_t) : 0);
   b.off_fstate = cur;
-  cur += up((size_t)slots * HV * p->K * p->V * sizeof(float));
+  cur += up((size_t)slots * HV * p->K * Vs * sizeof(float));
   b.off_dstate = cur;
-  cur += up((size_t)slots * HV * p->K * p->V * sizeof(float));
+  cur += up((size_t)slots * HV * p->K * Vs * sizeof(float));
   b.off_ddecay = cur;
   cur += up((size_t)slots * HV * p->K * sizeof(float));
   b.off_flags = cur;
   cur += up((size_t)slots * HV * sizeof(int32_t));
-  const size_t part = G > 1 ? up((size_t)p->B * p->T * HV * p->K * sizeof(float)) : 0;
+  // fp32 shares of dq, dk per value head and slice, and of dg per slice
+  const size_t rows = (size_t)p->B * p->T;
+  const size_t part = (G > 1 || slices > 1) ? up(slices * rows * HV * p->K * sizeof(float)) : 0;
   b.off_dq_part = cur;
   cur += part;
   b.off_dk_part = cur;
   cur += part;
+  b.off_dg_part = cur;
+  const size_t kg = p->gate == GLA_GATE_PER_HEAD ? 1 : p->K;
+  cur += slices > 1 ? up(slices * rows * HV * kg * sizeof(float)) : 0;
   b.total = cur;
-  const long long scan_blocks = 2LL * pl.N * HV * ((p->K * p->V / 4 + 255) / 256);
+  const long long scan_blocks = 2LL * pl.N * HV * ((p->K * Vs / 4 + 255) / 256);
   const long long rows_quads = (long long)p->B * p->T * p->H * (p->K / 4);
   // the chunk kernel addresses a chunk's 64 token rows of an output with
   // 32-bit byte offsets
@@ -345,7 +356,7 @@ bool bwd_chain_pays(long long N, long long HV) { return 4 * N * HV >= device_cu_
 gla_status validate_bwd(const gla_problem *p) {
   const gla_status st = validate(p);
   if (st != GLA_OK) return st;
-  if (p->K > gla::kMaxKeyBlock || p->V > 128) return GLA_ERR_UNSUPPORTED;
+  if (p->K > gla::kMaxKeyBlock) return GLA_ERR_UNSUPPORTED;
   return GLA_OK;
 }
 
@@ -379,31 +390,58 @@ gla_status run_backward(const gla_problem *p, const BwdPlan &bpl, const void *q,
   gla::BwdParams b{};
   b.w = w;  // seg_order stays null: the backward's kernels take slots in plain order
   b.persistent_blocks = 2 * device_cu_count();
-  b.dout = dout; b.dht = dht;
-  b.dq = dq; b.dk = dk; b.dv = dv; b.dg = dg; b.dh0 = dh0;
+  b.dq = dq; b.dk = dk;
+  b.Vmem = p->V;
   b.fstate = reinterpret_cast<float *>(ws + bpl.off_fstate);
   b.dstate = reinterpret_cast<float *>(ws + bpl.off_dstate);
   b.ddecay = reinterpret_cast<float *>(ws + bpl.off_ddecay);
   b.flags = reinterpret_cast<int32_t *>(ws + bpl.off_flags);
-  if (w.G > 1) {
-    b.dq_part = reinterpret_cast<float *>(ws + bpl.off_dq_part);
-    b.dk_part = reinterpret_cast<float *>(ws + bpl.off_dk_part);
+  const int slices = bwd_slices(p->V);
+  const long long rows = (long long)p->B * p->T;
+  float *dq_part = nullptr, *dk_part = nullptr;
+  if (w.G > 1 || slices > 1) {
+    dq_part = reinterpret_cast<float *>(ws + bpl.off_dq_part);
+    dk_part = reinterpret_cast<float *>(ws + bpl.off_dk_part);
   }
+  float *dg_parts = slices > 1 ? reinterpret_cast<float *>(ws + bpl.off_dg_part) : nullptr;
+  const long long dg_slice = rows * w.HV * (w.gate_head ? 1 : p->K);
   // Fixed-length sequences can chain the scan into the summary kernel (one
   // chain per sequence, value head and direction): it saves the scan's pass
   // over both state tables, but a chain advances one chunk per link.
   const long long tasks = 2LL * pl.seg_slots * w.HV;
-  const bool chained = !varlen && tokens && tasks + b.persistent_blocks <= INT_MAX &&
+  const bool chained = !varlen && tokens && slices == 1 && tasks + b.persistent_blocks <= INT_MAX &&
                        (p->schedule == 2 || (p->schedule == 0 && bwd_chain_pays(N, w.HV)));
-  if (chained) {
-    // the decay table is only read by gla_bwd_scan, which this schedule does
-    // not launch: it holds the chains' counter and flags instead
-    b.chain = reinterpret_cast<int32_t *>(ws + bpl.off_ddecay);
-    if (gla::launch_clear(b.chain, 1 + tasks, s) != hipSuccess) return GLA_ERR_HIP;
+  const size_t es = bf ? 2 : 4;
+  // Each value slice runs the whole sequence of launches over the same state
+  // tables (stream order keeps a slice's tables until its chunk kernel is done).
+  for (int sl = 0; sl < slices; ++sl) {
+    const int voff = sl * kBwdSlice;
+    b.w.V = p->V - voff < kBwdSlice ? p->V - voff : kBwdSlice;
+    b.w.v = static_cast<const char *>(v) + voff * es;
+    b.w.h0 = h0 ? h0 + voff : nullptr;
+    b.dout = static_cast<const char *>(dout) + voff * es;
+    b.dv = static_cast<char *>(dv) + voff * es;
+    b.dht = dht ? dht + voff : nullptr;
+    b.dh0 = dh0 ? dh0 + voff : nullptr;
+    b.dq_part = dq_part ? dq_part + sl * rows * w.HV * p->K : nullptr;
+    b.dk_part = dk_part ? dk_part + sl * rows * w.HV * p->K : nullptr;
+    b.dg = dg_parts ? dg_parts + sl * dg_slice : dg;
+    b.chain = nullptr;
+    if (chained) {
+      // the decay table is only read by gla_bwd_scan, which this schedule does
+      // not launch: it holds the chains' counter and flags instead
+      b.chain = reinterpret_cast<int32_t *>(ws + bpl.off_ddecay);
+      if (gla::launch_clear(b.chain, 1 + tasks, s) != hipSuccess) return GLA_ERR_HIP;
+    }
+    if (tokens && gla::launch_bwd_local(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
+    if (!chained && gla::launch_bwd_scan(b, s) != hipSuccess) return GLA_ERR_HIP;
+    if (tokens && gla::launch_bwd_chunk(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
   }
-  if (tokens && gla::launch_bwd_local(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
-  if (!chained && gla::launch_bwd_scan(b, s) != hipSuccess) return GLA_ERR_HIP;
-  if (tokens && gla::launch_bwd_chunk(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
+  if (tokens) {
+    b.dq_part = dq_part;
+    b.dk_part = dk_part;
+    if (gla::launch_bwd_finish(bf, b, slices, dg_parts, dg, s) != hipSuccess) return GLA_ERR_HIP;
+  }
   return GLA_OK;
 }
 

@@ -81,7 +81,10 @@ hipError_t launch_clear(int32_t *words, long long n, hipStream_t s);
 // Backward (gla_bwd.hip).  The state tables hold one chunk per slot: chunk c
 // of sequence n is slot first(n) + c, with first(n) = n P (fixed length) or
 // seg_base[n] (packed), as the forward kernels number segments of one chunk
-// (gla_segment_plan with R = 1 fills seg_base).  K and V are at most 128.
+// (gla_segment_plan with R = 1 fills seg_base).  K is at most 128; wider V is
+// cut into value slices of at most 128 columns, each launched on its own
+// (w.V = the slice's width, v, do, dv, h0, dht, dh0 offset to its first
+// column, Vmem = the full width, the row stride of those six).
 struct BwdParams {
   WalkParams w;          // problem sizes, q, k, v, g, h0, cu, seg_base (seg_order null), scale
   const void *dout;      // [B,T,HV,V] dtype: gradient of o
@@ -93,18 +96,23 @@ struct BwdParams {
   float *fstate;         // [slots][HV][K][V]: chunk summaries of the state, then S_c (state before chunk c)
   float *dstate;         // [slots][HV][K][V]: chunk summaries of the state gradient, then E_c
   float *ddecay;         // [slots][HV][K]: e^{G_last} of each chunk
-  int32_t *chain;        // fixed-length sequences, or null: gla_bwd_local also walks the chains of S_c and
-                         // E_c ([0] task counter, then flags [2][slots][HV]; zeroed before the launch) and
-                         // gla_bwd_scan is not launched
+  int32_t *chain;        // fixed-length sequences with one value slice, or null: gla_bwd_local
+                         // also walks the chains of S_c and E_c ([0] task counter, then flags
+                         // [2][slots][HV]; zeroed before the launch) and gla_bwd_scan is not launched
   int32_t *flags;        // [slots][HV]: 1 when the chunk is left to the token-by-token kernel
-  float *dq_part, *dk_part;  // [B,T,HV,K] fp32 shares of dq, dk per value head (G > 1), else null
+  float *dq_part, *dk_part;  // [B,T,HV,K] fp32 shares of dq, dk of this value slice (G > 1 or several slices), else null
+  int32_t Vmem;              // value columns per row of v, do, dv, h0, dht, dh0
   int32_t persistent_blocks; // workgroups of the persistent kernels (a few per compute unit)
 };
 hipError_t launch_bwd_local(bool bf16, const BwdParams &bp, hipStream_t s);
 hipError_t launch_bwd_scan(const BwdParams &bp, hipStream_t s);
-// the fast chunk kernel, the token-by-token kernel for flagged chunks, and
-// (G > 1) the sum of dq, dk over each key head's value heads
+// the fast chunk kernel and the token-by-token kernel for flagged chunks
 hipError_t launch_bwd_chunk(bool bf16, const BwdParams &bp, hipStream_t s);
+// After every value slice: with dq_part, dq and dk as the sums of the shares
+// over value heads and `slices` slices (bp.dq_part / dk_part at slice 0); with
+// several slices, dg as the sum of the slices' shares dg_parts.
+hipError_t launch_bwd_finish(bool bf16, const BwdParams &bp, int slices, const float *dg_parts, float *dg,
+                             hipStream_t s);
 
 // WY-representation forward (gla_wy.hip): one chunk per slot as in the backward.
 struct WyParams {

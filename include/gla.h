@@ -110,8 +110,8 @@ typedef struct gla_problem {
                       /* states (bf16 with K <= 128, else three passes).  A tuning    */
                       /* choice: results agree to rounding.  gla_bwd: 0 automatic;    */
                       /* 1 a separate scan over the chunk summaries; 2 the scan       */
-                      /* chained into the summary kernel (fixed-length sequences;     */
-                      /* packed ones always take 1).  Results are the same.           */
+                      /* chained into the summary kernel (fixed-length sequences with */
+                      /* V <= 128; others take 1).  Results are the same.             */
 } gla_problem;
 
 /*
@@ -197,8 +197,10 @@ size_t gla_bwd_workspace_bytes(const gla_problem *p);
  *            word as for gla_fwd (GLA_STATUS_WAIT_EXHAUSTED when a wait of the
  *            chained scan, see schedule, ran out).  It holds the state before
  *            every chunk and the state gradient reaching every chunk:
- *            2 * chunks * HV * K * V * 4 bytes and more.
- * Supported: K and V multiples of 16 up to 128 (else GLA_ERR_UNSUPPORTED),
+ *            2 * chunks * HV * K * min(V, 128) * 4 bytes and more.
+ * Supported: K a multiple of 16 up to 128, V a multiple of 16 up to 256 (else
+ * GLA_ERR_UNSUPPORTED; V past 128 runs as value slices of 128 columns, whose
+ * shares of dq, dk and dg are summed in fp32 before rounding),
  * both dtypes, both gate layouts, HV a multiple of H, packed sequences.  Every
  * output row of a token is written; rows of other tokens are untouched.
  * Gates are exact as in the forward: a chunk in which some key decays by more

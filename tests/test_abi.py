@@ -209,9 +209,9 @@ def call_bwd(lib, p, ws=FAKE, ws_bytes=1 << 40, cu=None, dq=FAKE, do=FAKE):
     (dict(scale=0.0), BAD_SCALE),
     (dict(chunk=32), UNSUPPORTED),
     (dict(K=24), UNSUPPORTED),
-    (dict(K=144), UNSUPPORTED),         # the backward takes K, V up to 128
-    (dict(V=144), UNSUPPORTED),
+    (dict(K=144), UNSUPPORTED),         # the backward takes K up to 128, V up to 256
     (dict(K=256, V=256), UNSUPPORTED),
+    (dict(V=272), UNSUPPORTED),
     (dict(n_seqs=3), BAD_SHAPE),
     (dict(HV=4), BAD_SHAPE),
     (dict(gate=2), UNSUPPORTED),
@@ -233,8 +233,8 @@ def test_backward_null_arguments(lib):
 
 @pytest.mark.parametrize("dtype", [gla.GLA_BF16, gla.GLA_F32])
 @pytest.mark.parametrize("K", [16, 48, 64, 128])
-@pytest.mark.parametrize("V", [16, 96, 128])
-def test_backward_accepts_widths_up_to_128(lib, dtype, K, V):
+@pytest.mark.parametrize("V", [16, 96, 128, 144, 256])
+def test_backward_accepts_its_widths(lib, dtype, K, V):
     p = prob(dtype=dtype, K=K, V=V)
     assert lib.gla_bwd_workspace_bytes(ctypes.byref(p)) != ctypes.c_size_t(-1).value
 
@@ -262,6 +262,16 @@ def test_backward_workspace_size_and_check(lib):
     sv, dv_ = up(slots_v * H * K * V * 4), up(slots_v * H * K * 4)
     assert lib.gla_bwd_workspace_bytes(ctypes.byref(pv)) == (WS_HEADER + up((6 + slots_v) * 4) + 2 * sv + dv_
                                                              + up(slots_v * H * 4))
+    # V = 256: two value slices of 128 columns run one after the other over
+    # state tables of 128 columns, with fp32 shares of dq, dk and dg per slice
+    pw = prob(B=B, T=T, H=H, K=K, V=256)
+    sw = up(slots * H * K * 128 * 4)
+    shares = up(2 * B * T * H * K * 4)
+    assert lib.gla_bwd_workspace_bytes(ctypes.byref(pw)) == (WS_HEADER + 2 * sw + decays + up(slots * H * 4)
+                                                             + 3 * shares)
+    pwh = prob(B=B, T=T, H=H, K=K, V=256, gate=gla.GATE_PER_HEAD)
+    assert lib.gla_bwd_workspace_bytes(ctypes.byref(pwh)) == (WS_HEADER + 2 * sw + decays + up(slots * H * 4)
+                                                              + 2 * shares + up(2 * B * T * H * 4))
 
 
 # ---------------------------------------------------------------- WY-representation forward

@@ -122,6 +122,28 @@ def test_ragged_lengths(dtype, T, schedule):
     check_bwd(d, dtype, seed=9, label=f"T={T}", schedule=schedule)
 
 
+# V past 128 runs as value slices of 128 columns; dq, dk and dg are summed
+# over the slices' fp32 shares, dv and dh0 are written per slice
+@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("K,V", [(64, 144), (128, 256), (32, 192)])
+def test_value_slices(dtype, K, V, schedule):
+    d = gi.draw(350 + K + V, 2, 150, 2, K, V, dtype=dtype, h0=True)
+    check_bwd(d, dtype, seed=24, label=f"K={K} V={V}", schedule=schedule)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_value_slices_variants(dtype):
+    # value-head groups and a per-head gate; packed sequences; strong gates
+    # (chunks in the token-by-token kernel), each with two value slices
+    d = gi.draw(360, 2, 140, 2, 64, 256, dtype=dtype, h0=True, HV=4, gate="head")
+    check_bwd(d, dtype, seed=25, label="V=256 HV=4 gate=head")
+    d = gi.draw(361, 1, 0, 2, 64, 160, dtype=dtype, h0=True, lengths=[70, 0, 190, 5])
+    check_bwd(d, dtype, seed=26, label="V=160 packed")
+    d = gi.draw(362, 2, 200, 2, 64, 256, dtype=dtype, h0=True, gate_scale=40.0)
+    check_bwd(d, dtype, seed=27, label="V=256 gates x40")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_packed(dtype):
     d = gi.draw(401, 1, 0, 2, 64, 128, dtype=dtype, h0=True, lengths=[0, 1, 64, 65, 200, 3, 128])
@@ -203,7 +225,7 @@ def head_slice(d, heads):
     return out
 
 
-@pytest.mark.parametrize("name", ["c2048", "varlen"])
+@pytest.mark.parametrize("name", ["c2048", "varlen", "c4096"])
 def test_workload_sampled_heads(name):
     """A full-size workload on the GPU; the oracle on two of its heads."""
     w = gi.WORKLOADS[name]
