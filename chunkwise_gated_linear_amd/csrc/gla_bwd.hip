@@ -1440,6 +1440,19 @@ __global__ __launch_bounds__(256) void gla_bwd_group_sum(BwdParams bp, int64_t q
   }
 }
 
+// Columns [0, cols) of `rows` fp32 rows, src row r at src + r src_stride to
+// dst row r at dst + r dst_stride; one thread per float4 (cols, both strides
+// and both bases multiples of 4 floats).
+__global__ __launch_bounds__(256) void gla_bwd_copy_rows(float *dst, int64_t dst_stride, const float *src,
+                                                         int64_t src_stride, int64_t quads, int cols) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= quads) return;
+  const int q = cols / 4;
+  const int64_t r = e / q;
+  const int c = (int)(e - r * q) * 4;
+  *reinterpret_cast<f32x4_t *>(dst + r * dst_stride + c) = *reinterpret_cast<const f32x4_t *>(src + r * src_stride + c);
+}
+
 // dg with several value slices: out[e] = the sum of the slices' fp32 shares.
 __global__ __launch_bounds__(256) void gla_bwd_slice_sum(float *out, const float *parts, int64_t n, int slices) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1489,6 +1502,17 @@ hipError_t launch_bwd_chunk(bool bf16, const BwdParams &bp, hipStream_t s) {
   hipError_t e = launch_bwd_kernel(1, bf16, bp, s);
   if (e != hipSuccess) return e;
   return launch_bwd_kernel(2, bf16, bp, s);
+}
+
+hipError_t launch_copy_rows(float *dst, int64_t dst_stride, const float *src, int64_t src_stride, int64_t rows,
+                            int cols, hipStream_t s) {
+  const long long quads = rows * (cols / 4);
+  const long long blocks = (quads + 255) / 256;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL || cols % 4 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gla_bwd_copy_rows, dim3((unsigned)blocks), dim3(256), 0, s, dst, dst_stride, src, src_stride,
+                     (int64_t)quads, cols);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_finish(bool bf16, const BwdParams &bp, int slices, const float *dg_parts, float *dg,

@@ -296,7 +296,8 @@ int bwd_slices(int V) { return (V + kBwdSlice - 1) / kBwdSlice; }
 
 struct BwdPlan {
   Plan fwd;  // slot numbering only (R = 1)
-  size_t off_base, off_fstate, off_dstate, off_ddecay, off_flags, off_dq_part, off_dk_part, off_dg_part, total;
+  size_t off_base, off_fstate, off_dstate, off_ddecay, off_flags, off_dq_part, off_dk_part, off_dg_part,
+      off_bound, total;
   bool ok;
 };
 
@@ -333,6 +334,10 @@ BwdPlan make_bwd_plan(const gla_problem *p, bool varlen) {
   b.off_dg_part = cur;
   const size_t kg = p->gate == GLA_GATE_PER_HEAD ? 1 : p->K;
   cur += slices > 1 ? up(slices * rows * HV * kg * sizeof(float)) : 0;
+  // with several slices, the chained scan's h0, dht and dh0 columns of one
+  // slice, staged compactly [N][HV][K][Vs]
+  b.off_bound = cur;
+  cur += (slices > 1 && !varlen) ? 3 * up((size_t)pl.N * HV * p->K * Vs * sizeof(float)) : 0;
   b.total = cur;
   const long long scan_blocks = 2LL * pl.N * HV * ((p->K * Vs / 4 + 255) / 256);
   const long long rows_quads = (long long)p->B * p->T * p->H * (p->K / 4);
@@ -409,8 +414,16 @@ gla_status run_backward(const gla_problem *p, const BwdPlan &bpl, const void *q,
   // chain per sequence, value head and direction): it saves the scan's pass
   // over both state tables, but a chain advances one chunk per link.
   const long long tasks = 2LL * pl.seg_slots * w.HV;
-  const bool chained = !varlen && tokens && slices == 1 && tasks + b.persistent_blocks <= INT_MAX &&
+  const bool chained = !varlen && tokens && tasks + b.persistent_blocks <= INT_MAX &&
                        (p->schedule == 2 || (p->schedule == 0 && bwd_chain_pays(N, w.HV)));
+  // the chained scan's link takes h0, dht and dh0 with the slice's own width:
+  // with several slices their columns are staged through the workspace
+  const long long brows = (long long)N * w.HV * p->K;  // state rows of h0, dht, dh0
+  const size_t bbytes = ((size_t)brows * kBwdSlice * sizeof(float) + 255) & ~(size_t)255;
+  float *stage_h0 = reinterpret_cast<float *>(ws + bpl.off_bound);
+  float *stage_dht = reinterpret_cast<float *>(ws + bpl.off_bound + bbytes);
+  float *stage_dh0 = reinterpret_cast<float *>(ws + bpl.off_bound + 2 * bbytes);
+  const bool stage = chained && slices > 1;
   const size_t es = bf ? 2 : 4;
   // Each value slice runs the whole sequence of launches over the same state
   // tables (stream order keeps a slice's tables until its chunk kernel is done).
@@ -433,7 +446,21 @@ gla_status run_backward(const gla_problem *p, const BwdPlan &bpl, const void *q,
       b.chain = reinterpret_cast<int32_t *>(ws + bpl.off_ddecay);
       if (gla::launch_clear(b.chain, 1 + tasks, s) != hipSuccess) return GLA_ERR_HIP;
     }
+    if (stage) {
+      if (h0) {
+        if (gla::launch_copy_rows(stage_h0, b.w.V, h0 + voff, p->V, brows, b.w.V, s) != hipSuccess) return GLA_ERR_HIP;
+        b.w.h0 = stage_h0;
+      }
+      if (dht) {
+        if (gla::launch_copy_rows(stage_dht, b.w.V, dht + voff, p->V, brows, b.w.V, s) != hipSuccess) return GLA_ERR_HIP;
+        b.dht = stage_dht;
+      }
+      if (dh0) b.dh0 = stage_dh0;
+    }
     if (tokens && gla::launch_bwd_local(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
+    if (stage && dh0 &&
+        gla::launch_copy_rows(dh0 + voff, p->V, stage_dh0, b.w.V, brows, b.w.V, s) != hipSuccess)
+      return GLA_ERR_HIP;
     if (!chained && gla::launch_bwd_scan(b, s) != hipSuccess) return GLA_ERR_HIP;
     if (tokens && gla::launch_bwd_chunk(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
   }

@@ -96,9 +96,10 @@ struct BwdParams {
   float *fstate;         // [slots][HV][K][V]: chunk summaries of the state, then S_c (state before chunk c)
   float *dstate;         // [slots][HV][K][V]: chunk summaries of the state gradient, then E_c
   float *ddecay;         // [slots][HV][K]: e^{G_last} of each chunk
-  int32_t *chain;        // fixed-length sequences with one value slice, or null: gla_bwd_local
-                         // also walks the chains of S_c and E_c ([0] task counter, then flags
-                         // [2][slots][HV]; zeroed before the launch) and gla_bwd_scan is not launched
+  int32_t *chain;        // fixed-length sequences, or null: gla_bwd_local also walks the chains
+                         // of S_c and E_c ([0] task counter, then flags [2][slots][HV]; zeroed
+                         // before the launch) and gla_bwd_scan is not launched.  Its h0, dht and
+                         // dh0 are [N][HV][K][V] (a value slice's columns staged compactly)
   int32_t *flags;        // [slots][HV]: 1 when the chunk is left to the token-by-token kernel
   float *dq_part, *dk_part;  // [B,T,HV,K] fp32 shares of dq, dk of this value slice (G > 1 or several slices), else null
   int32_t Vmem;              // value columns per row of v, do, dv, h0, dht, dh0
@@ -113,6 +114,10 @@ hipError_t launch_bwd_chunk(bool bf16, const BwdParams &bp, hipStream_t s);
 // several slices, dg as the sum of the slices' shares dg_parts.
 hipError_t launch_bwd_finish(bool bf16, const BwdParams &bp, int slices, const float *dg_parts, float *dg,
                              hipStream_t s);
+// Columns [0, cols) of `rows` fp32 rows from src (row stride src_stride) to dst
+// (row stride dst_stride); cols and both strides multiples of 4.
+hipError_t launch_copy_rows(float *dst, int64_t dst_stride, const float *src, int64_t src_stride, int64_t rows,
+                            int cols, hipStream_t s);
 
 // WY-representation forward (gla_wy.hip): one chunk per slot as in the backward.
 struct WyParams {

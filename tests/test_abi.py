@@ -263,15 +263,17 @@ def test_backward_workspace_size_and_check(lib):
     assert lib.gla_bwd_workspace_bytes(ctypes.byref(pv)) == (WS_HEADER + up((6 + slots_v) * 4) + 2 * sv + dv_
                                                              + up(slots_v * H * 4))
     # V = 256: two value slices of 128 columns run one after the other over
-    # state tables of 128 columns, with fp32 shares of dq, dk and dg per slice
+    # state tables of 128 columns, with fp32 shares of dq, dk and dg per slice,
+    # and one slice's columns of h0, dht and dh0 staged for the chained scan
     pw = prob(B=B, T=T, H=H, K=K, V=256)
     sw = up(slots * H * K * 128 * 4)
     shares = up(2 * B * T * H * K * 4)
+    staged = 3 * up(B * H * K * 128 * 4)
     assert lib.gla_bwd_workspace_bytes(ctypes.byref(pw)) == (WS_HEADER + 2 * sw + decays + up(slots * H * 4)
-                                                             + 3 * shares)
+                                                             + 3 * shares + staged)
     pwh = prob(B=B, T=T, H=H, K=K, V=256, gate=gla.GATE_PER_HEAD)
     assert lib.gla_bwd_workspace_bytes(ctypes.byref(pwh)) == (WS_HEADER + 2 * sw + decays + up(slots * H * 4)
-                                                              + 2 * shares + up(2 * B * T * H * 4))
+                                                              + 2 * shares + up(2 * B * T * H * 4) + staged)
 
 
 # ---------------------------------------------------------------- WY-representation forward

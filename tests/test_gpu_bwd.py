@@ -246,15 +246,17 @@ def test_workload_sampled_heads(name):
     say("   max|err|/rms: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
-@pytest.mark.parametrize("dtype,gate", [("bf16", "key"), ("fp32", "key"), ("bf16", "head")])
-def test_chained_scan_matches_separate_scan(dtype, gate):
+@pytest.mark.parametrize("dtype,gate,V", [("bf16", "key", 128), ("fp32", "key", 128), ("bf16", "head", 128),
+                                           ("bf16", "key", 256)])
+def test_chained_scan_matches_separate_scan(dtype, gate, V):
     """The chained scan applies the separate scan's recurrences in the same
     order and precision to the same summaries: every output agrees bit for bit.
     Many chains of many chunks (B=4, H=16, T=1000: 64 chains of 16 chunks per
-    direction) cross workgroups on different dies; the oracle checks two heads."""
-    d = gi.draw(920, 4, 1000, 16, 128, 128, dtype=dtype, h0=True, gate=gate)
+    direction) cross workgroups on different dies; the oracle checks two heads.
+    With V = 256 each value slice's h0, dht and dh0 columns are staged."""
+    d = gi.draw(920, 4, 1000, 16, 128, V, dtype=dtype, h0=True, gate=gate)
     do, dht = grads_in(d, dtype, 21)
-    say(f"bwd chained vs separate scan: B=4 T=1000 H=16 K=V=128 {dtype} gate={gate}")
+    say(f"bwd chained vs separate scan: B=4 T=1000 H=16 K=128 V={V} {dtype} gate={gate}")
     a = run_bwd_gpu(d, do, dht, dtype, schedule=1)
     b = run_bwd_gpu(d, do, dht, dtype, schedule=2)
     for name, x, y in zip(("dq", "dk", "dv", "dg", "dh0"), a, b):
