@@ -11,7 +11,7 @@ importing the binding still works but every call raises.
     dq, dk, dv, dg, dh0 = gla_bwd(q, k, v, g, do, h0=None, dht=None,
                                   cu_seqlens=None, scale=None)
 
-K and V are multiples of 16 in [16, 256] (the backward: K up to 128).
+K and V are multiples of 16 in [16, 256], for the forward and the backward.
 
 Shapes are time-major: q, k [B, T, H, K]; v [B, T, HV, V]; g [B, T, HV, K]
 (a decay per key) or [B, T, HV] (one per value head); h0, ht [N, HV, K, V]

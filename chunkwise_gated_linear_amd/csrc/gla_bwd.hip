@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "gla.h"
 #include "gla_device.h"
@@ -201,7 +202,7 @@ __device__ __forceinline__ void gate_load(const WalkParams &p, const ChunkAt &ca
   if constexpr (GH) {
     gr.gh = threadIdx.x < ca.L ? p.g[(ca.row0 + threadIdx.x) * p.HV + hv] : 0.f;
   } else {
-    const ChunkRowsRsrc rg = chunk_rows<false>(p.g, (ca.row0 * p.HV + hv) * p.K, p.HV * p.K, p.K, ca.L);
+    const ChunkRowsRsrc rg = chunk_rows<false>(p.g, (ca.row0 * p.HV + hv) * p.Kmem, p.HV * p.Kmem, p.K, ca.L);
 #pragma unroll
     for (int t = 0; t < GateRows<KD, GH, NT>::TG; ++t) {
       const int e = threadIdx.x + NT * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
@@ -317,29 +318,32 @@ struct LocalTask {
   bool grad, work;
 };
 
+// Task numbers are below 2 slots HV, which the host keeps within int range
+// (32-bit arithmetic: the task decode runs on the scalar unit, where 64-bit
+// division costs many registers).
 // Task t of the three-launch schedule.
-__device__ __forceinline__ bool local_task(const BwdParams &bp, long long t, LocalTask &lt) {
+__device__ __forceinline__ bool local_task(const BwdParams &bp, int t, LocalTask &lt) {
   const WalkParams &p = bp.w;
-  const long long half = (long long)p.seg_slots * p.HV;
+  const int half = p.seg_slots * p.HV;
   lt.grad = t >= half;
-  const long long blk = lt.grad ? t - half : t;
-  lt.hv = (int)(blk % p.HV);
-  lt.slot = (int)(blk / p.HV);
+  const int blk = lt.grad ? t - half : t;
+  lt.slot = blk / p.HV;
+  lt.hv = blk - lt.slot * p.HV;
   lt.work = true;
   return chunk_at(p, lt.slot, lt.ca);
 }
 
 // Task t of the chained schedule (fixed-length sequences, P chunks each).
-__device__ __forceinline__ bool chained_task(const BwdParams &bp, long long t, LocalTask &lt) {
+__device__ __forceinline__ bool chained_task(const BwdParams &bp, int t, LocalTask &lt) {
   const WalkParams &p = bp.w;
-  const long long pairs = (long long)p.N * p.HV;
-  const long long step = t / (2 * pairs);
-  long long rem = t - step * 2 * pairs;
+  const int pairs = p.N * p.HV;
+  const int step = t / (2 * pairs);
+  int rem = t - step * 2 * pairs;
   lt.grad = rem >= pairs;
   if (lt.grad) rem -= pairs;
-  const int n = (int)(rem / p.HV);
-  lt.hv = (int)(rem - (long long)n * p.HV);
-  const int c = lt.grad ? p.P - 1 - (int)step : (int)step;
+  const int n = rem / p.HV;
+  lt.hv = rem - n * p.HV;
+  const int c = lt.grad ? p.P - 1 - step : step;
   lt.slot = n * p.P + c;
   lt.work = lt.grad ? (c > 0 || bp.dh0 != nullptr) : c < p.P - 1;
   return chunk_at(p, lt.slot, lt.ca);
@@ -351,7 +355,7 @@ __device__ __forceinline__ void local_load(const BwdParams &bp, const LocalTask 
   const WalkParams &p = bp.w;
   const ChunkAt &ca = lt.ca;
   const int h = lt.hv / p.G;
-  const ChunkRowsRsrc rx = chunk_rows<BF>(lt.grad ? p.q : p.k, (ca.row0 * p.H + h) * p.K, p.H * p.K, p.K, ca.L);
+  const ChunkRowsRsrc rx = chunk_rows<BF>(lt.grad ? p.q : p.k, (ca.row0 * p.H + h) * p.Kmem, p.H * p.Kmem, p.K, ca.L);
   const ChunkRowsRsrc ry =
       chunk_rows<BF>(lt.grad ? bp.dout : p.v, (ca.row0 * p.HV + lt.hv) * bp.Vmem, p.HV * bp.Vmem, p.V, ca.L);
 #pragma unroll
@@ -491,19 +495,19 @@ __global__ __launch_bounds__(256, 2) void gla_bwd_local(BwdParams bp) {
   __shared__ float sdec[KD];  // a_c per key
   __shared__ int sclaim;      // chained schedule: the task number taken from the counter
   const bool chained = bp.chain != nullptr;
-  const long long ntask = 2LL * p.seg_slots * p.HV;
+  const unsigned ntask = 2u * p.seg_slots * p.HV;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
 
   // the next task: from the counter (chained; sclaim was written before a
   // barrier), else the next one with a chunk on the grid stride
-  long long task = (long long)blockIdx.x - gridDim.x;
+  unsigned task = blockIdx.x - gridDim.x;  // wraps; the first step adds gridDim.x back
   auto advance = [&](LocalTask &lt) -> bool {
     if (chained) {
-      const long long t = __builtin_amdgcn_readfirstlane(sclaim);
-      return t < ntask && chained_task(bp, t, lt);
+      const unsigned t = (unsigned)__builtin_amdgcn_readfirstlane(sclaim);
+      return t < ntask && chained_task(bp, (int)t, lt);
     }
     for (task += gridDim.x; task < ntask; task += gridDim.x)
-      if (local_task(bp, task, lt)) return true;
+      if (local_task(bp, (int)task, lt)) return true;
     return false;
   };
   auto claim = [&]() {
@@ -674,7 +678,7 @@ __global__ __launch_bounds__(256) void gla_bwd_scan(BwdParams bp, int per_state)
   }
   const int nc = min((len + kChunk - 1) / kChunk, nseg);
   const int krow = (4 * e4) / p.V, col = 4 * e4 - krow * p.V;
-  const int64_t sidx = (((int64_t)n * p.HV + hv) * p.K + krow) * bp.Vmem + col;  // h0, dht, dh0 element
+  const int64_t sidx = (((int64_t)n * p.HV + hv) * p.Kmem + krow) * bp.Vmem + col;  // h0, dht, dh0 element
   constexpr int BATCH = 16;
   auto cell = [&](float *base, int c) {
     return reinterpret_cast<f32x4_t *>(base + ((int64_t)(first + c) * p.HV + hv) * p.K * p.V) + e4;
@@ -731,11 +735,11 @@ template <bool BF>
 __device__ __forceinline__ void store_dqk(const BwdParams &bp, int64_t row, int hv, int k, float dqv, float dkv) {
   const WalkParams &p = bp.w;
   if (bp.dq_part == nullptr) {
-    const int64_t off = (row * p.H + hv) * p.K + k;
+    const int64_t off = (row * p.H + hv) * p.Kmem + k;
     st_el<BF>(bp.dq, off, dqv);
     st_el<BF>(bp.dk, off, dkv);
   } else {
-    const int64_t off = (row * p.HV + hv) * p.K + k;
+    const int64_t off = (row * p.HV + hv) * p.Kmem + k;
     bp.dq_part[off] = dqv;
     bp.dk_part[off] = dkv;
   }
@@ -777,9 +781,9 @@ __device__ __forceinline__ void chunk_load(const BwdParams &bp, const ChunkAt &c
   using R = ChunkRows<BF, KD, VD, GH>;
   const WalkParams &p = bp.w;
   const int h = hv / p.G;
-  const int64_t fk = (ca.row0 * p.H + h) * p.K, fv = (ca.row0 * p.HV + hv) * bp.Vmem;
-  const ChunkRowsRsrc rq = chunk_rows<BF>(p.q, fk, p.H * p.K, p.K, ca.L);
-  const ChunkRowsRsrc rk = chunk_rows<BF>(p.k, fk, p.H * p.K, p.K, ca.L);
+  const int64_t fk = (ca.row0 * p.H + h) * p.Kmem, fv = (ca.row0 * p.HV + hv) * bp.Vmem;
+  const ChunkRowsRsrc rq = chunk_rows<BF>(p.q, fk, p.H * p.Kmem, p.K, ca.L);
+  const ChunkRowsRsrc rk = chunk_rows<BF>(p.k, fk, p.H * p.Kmem, p.K, ca.L);
   const ChunkRowsRsrc ro = chunk_rows<BF>(bp.dout, fv, p.HV * bp.Vmem, p.V, ca.L);
   const ChunkRowsRsrc rv = chunk_rows<BF>(p.v, fv, p.HV * bp.Vmem, p.V, ca.L);
 #pragma unroll
@@ -838,16 +842,21 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
     // rows: rows past its last token lie outside the range, so their stores
     // are dropped without a branch, and the offsets are 32-bit.  (K and V are
     // multiples of 16, so a key or value block is wholly inside or outside.)
-    // dq, dk: [B,T,H,K] in the input dtype with one value head per key head
+    // dq, dk: [B,T,H,Kmem] in the input dtype with one value head per key head
     // (then H = HV) and one value slice, else this value head's and slice's
-    // fp32 share [B,T,HV,K].  dv: [B,T,HV,Vmem], this launch's columns.
+    // fp32 share [B,T,HV,Kmem]; this launch's keys.  dv: [B,T,HV,Vmem], this
+    // launch's columns, or with several key blocks this block's fp32 share.
     constexpr int ES = BF ? 2 : 4;
     const bool part = bp.dq_part != nullptr;
     const int ESQ = part ? 4 : ES;
-    const int strideV = p.HV * bp.Vmem, strideK = p.HV * p.K;  // elements between token rows
+    const bool dvpart = bp.dv_part != nullptr;  // dv is this key block's fp32 share
+    const int ESV = dvpart ? 4 : ES;
+    const int strideV = p.HV * bp.Vmem, strideK = p.HV * p.Kmem;  // elements between token rows
     const __amdgpu_buffer_rsrc_t rDv =
-        make_rsrc(static_cast<char *>(bp.dv) + (row0 * p.HV + chv) * bp.Vmem * ES, ((int64_t)(L - 1) * strideV + p.V) * ES);
-    const int64_t qk0 = (row0 * p.HV + chv) * p.K, qkBytes = ((int64_t)(L - 1) * strideK + p.K) * ESQ;
+        make_rsrc(dvpart ? static_cast<char *>(static_cast<void *>(bp.dv_part)) + (row0 * p.HV + chv) * bp.Vmem * 4
+                         : static_cast<char *>(bp.dv) + (row0 * p.HV + chv) * bp.Vmem * ES,
+                  ((int64_t)(L - 1) * strideV + p.V) * ESV);
+    const int64_t qk0 = (row0 * p.HV + chv) * p.Kmem, qkBytes = ((int64_t)(L - 1) * strideK + p.K) * ESQ;
     const __amdgpu_buffer_rsrc_t rDq =
         make_rsrc(part ? static_cast<char *>(static_cast<void *>(bp.dq_part)) + qk0 * 4 : static_cast<char *>(bp.dq) + qk0 * ES, qkBytes);
     const __amdgpu_buffer_rsrc_t rDk =
@@ -1125,17 +1134,23 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
         }
       }
     }
+    auto store_dv = [&](auto es_tag) {
+      constexpr bool F32 = decltype(es_tag)::value;  // the fp32 share of a key block
 #pragma unroll
-    for (int b = 0; b < NVB; ++b) {
-      if (vb0 + b * 16 >= p.V) continue;  // uniform over the wave
+      for (int b = 0; b < NVB; ++b) {
+        if (vb0 + b * 16 >= p.V) continue;  // uniform over the wave
 #pragma unroll
-      for (int j = 0; j < NJB; ++j)
+        for (int j = 0; j < NJB; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = (jb0 + j) * 16 + 4 * lg + r, col = vb0 + b * 16 + l16;
-          bst_el<BF>(rDv, (row * strideV + col) * ES, dv[b][j][r]);
-        }
-    }
+          for (int r = 0; r < 4; ++r) {
+            const int row = (jb0 + j) * 16 + 4 * lg + r, col = vb0 + b * 16 + l16;
+            if constexpr (F32) bst_el<false>(rDv, (row * strideV + col) * 4, dv[b][j][r]);
+            else bst_el<BF>(rDv, (row * strideV + col) * ES, dv[b][j][r]);
+          }
+      }
+    };
+    if (dvpart) store_dv(std::true_type{});
+    else store_dv(std::false_type{});
 
     // ---- dq = scale (do S_c^T) + dA' (k e^-G)
 #pragma unroll
@@ -1296,9 +1311,9 @@ __global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
   for (int e = threadIdx.x; e < 64 * KD; e += 256) {
     const int i = e / KD, kk = e % KD;
     const bool in = i < L && kk < p.K;
-    sK[e] = in ? ld_el<BF>(p.k, (row0 + i) * p.H * p.K + h * p.K + kk) : 0.f;
+    sK[e] = in ? ld_el<BF>(p.k, (row0 + i) * p.H * p.Kmem + h * p.Kmem + kk) : 0.f;
     float gv = 0.f;
-    if (in) gv = GH ? p.g[(row0 + i) * p.HV + hv] : p.g[((row0 + i) * p.HV + hv) * p.K + kk];
+    if (in) gv = GH ? p.g[(row0 + i) * p.HV + hv] : p.g[((row0 + i) * p.HV + hv) * p.Kmem + kk];
     sA[e] = __expf(gv);
   }
   for (int e = threadIdx.x; e < 64 * VD; e += 256) {
@@ -1345,7 +1360,7 @@ __global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
     U[j] = (kin && col < p.V) ? Ec[(int64_t)key * p.V + col] : 0.f;
   }
   for (int i = L - 1; i >= 0; --i) {
-    const int64_t qoff = (row0 + i) * p.H * p.K + h * p.K + key;
+    const int64_t qoff = (row0 + i) * p.H * p.Kmem + h * p.Kmem + key;
     const float qv = kin ? ld_el<BF>(p.q, qoff) : 0.f;
     const float kv = sK[i * KD + key];
     float dkp = 0.f;
@@ -1388,7 +1403,7 @@ __global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
       const int64_t row = row0 + i;
       const float dgi = a * acc;
       store_dqk<BF>(bp, row, hv, key, sDq[i * KD + key], dkp);
-      if (!GH) bp.dg[(row * p.HV + hv) * p.K + key] = dgi;
+      if (!GH) bp.dg[(row * p.HV + hv) * p.Kmem + key] = dgi;
     }
     if (GH && cp == 0) sKeyDg[key] = kin ? a * acc : 0.f;
     __syncthreads();
@@ -1401,7 +1416,9 @@ __global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
     }
     for (int col = threadIdx.x; col < p.V; col += 256) {
       const float sv = sRed[col] + sRed[VD + col] + sRed[2 * VD + col] + sRed[3 * VD + col];
-      st_el<BF>(bp.dv, ((row0 + i) * p.HV + hv) * bp.Vmem + col, sv);
+      const int64_t dvo = ((row0 + i) * p.HV + hv) * bp.Vmem + col;
+      if (bp.dv_part != nullptr) bp.dv_part[dvo] = sv;
+      else st_el<BF>(bp.dv, dvo, sv);
     }
 #pragma unroll
     for (int j = 0; j < NC; ++j) U[j] *= a;
@@ -1440,20 +1457,36 @@ __global__ __launch_bounds__(256) void gla_bwd_group_sum(BwdParams bp, int64_t q
   }
 }
 
-// Columns [0, cols) of `rows` fp32 rows, src row r at src + r src_stride to
-// dst row r at dst + r dst_stride; one thread per float4 (cols, both strides
-// and both bases multiples of 4 floats).
-__global__ __launch_bounds__(256) void gla_bwd_copy_rows(float *dst, int64_t dst_stride, const float *src,
-                                                         int64_t src_stride, int64_t quads, int cols) {
+// Columns [0, cols) of `groups` x `rows` fp32 rows: row r of group gi from
+// src + gi src.group + r src.row to dst + gi dst.group + r dst.row; one thread
+// per float4 (cols, strides and bases multiples of 4 floats).
+struct RowsLayout {
+  int64_t group, row;
+};
+__global__ __launch_bounds__(256) void gla_bwd_copy_rows(float *dst, RowsLayout dl, const float *src, RowsLayout sl,
+                                                         int rows, int64_t quads, int cols) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= quads) return;
   const int q = cols / 4;
-  const int64_t r = e / q;
-  const int c = (int)(e - r * q) * 4;
-  *reinterpret_cast<f32x4_t *>(dst + r * dst_stride + c) = *reinterpret_cast<const f32x4_t *>(src + r * src_stride + c);
+  const int64_t gr = e / q;  // gi rows + r
+  const int c = (int)(e - gr * q) * 4;
+  const int64_t gi = gr / rows, r = gr - gi * rows;
+  *reinterpret_cast<f32x4_t *>(dst + gi * dl.group + r * dl.row + c) =
+      *reinterpret_cast<const f32x4_t *>(src + gi * sl.group + r * sl.row + c);
 }
 
-// dg with several value slices: out[e] = the sum of the slices' fp32 shares.
+// dv with several key blocks: the blocks' fp32 shares summed and rounded once.
+template <bool BF>
+__global__ __launch_bounds__(256) void gla_bwd_dv_sum(void *dv, const float *parts, int64_t n, int blocks) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  float x = 0.f;
+  for (int b = 0; b < blocks; ++b) x += parts[b * n + e];
+  st_el<BF>(dv, e, x);
+}
+
+// dg with several value slices (or, with a per-head gate, key blocks): out[e]
+// = the sum of the fp32 shares.
 __global__ __launch_bounds__(256) void gla_bwd_slice_sum(float *out, const float *parts, int64_t n, int slices) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= n) return;
@@ -1504,19 +1537,28 @@ hipError_t launch_bwd_chunk(bool bf16, const BwdParams &bp, hipStream_t s) {
   return launch_bwd_kernel(2, bf16, bp, s);
 }
 
-hipError_t launch_copy_rows(float *dst, int64_t dst_stride, const float *src, int64_t src_stride, int64_t rows,
-                            int cols, hipStream_t s) {
-  const long long quads = rows * (cols / 4);
+hipError_t launch_copy_rows(float *dst, int64_t dst_group, int64_t dst_row, const float *src, int64_t src_group,
+                            int64_t src_row, long long groups, int rows, int cols, hipStream_t s) {
+  const long long quads = groups * rows * (cols / 4);
   const long long blocks = (quads + 255) / 256;
   if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffffLL || cols % 4 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gla_bwd_copy_rows, dim3((unsigned)blocks), dim3(256), 0, s, dst, dst_stride, src, src_stride,
-                     (int64_t)quads, cols);
+  if (blocks > 0x7fffffffLL || cols % 4 != 0 || rows <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gla_bwd_copy_rows, dim3((unsigned)blocks), dim3(256), 0, s, dst, RowsLayout{dst_group, dst_row},
+                     src, RowsLayout{src_group, src_row}, rows, (int64_t)quads, cols);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_finish(bool bf16, const BwdParams &bp, int slices, const float *dg_parts, float *dg,
-                             hipStream_t s) {
+hipError_t launch_dv_sum(bool bf16, void *dv, const float *parts, long long n, int blocks, hipStream_t s) {
+  const long long grid = (n + 255) / 256;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (bf16) hipLaunchKernelGGL(gla_bwd_dv_sum<true>, dim3((unsigned)grid), dim3(256), 0, s, dv, parts, (int64_t)n, blocks);
+  else hipLaunchKernelGGL(gla_bwd_dv_sum<false>, dim3((unsigned)grid), dim3(256), 0, s, dv, parts, (int64_t)n, blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_finish(bool bf16, const BwdParams &bp, int slices, const float *dg_parts, int dg_nparts,
+                             float *dg, hipStream_t s) {
   const long long rows = (bp.w.cu ? 1LL : (long long)bp.w.N) * bp.w.T;  // token rows of [B,T]
   if (bp.dq_part != nullptr) {
     const long long quads = rows * bp.w.H * (bp.w.K / 4);
@@ -1534,12 +1576,13 @@ hipError_t launch_bwd_finish(bool bf16, const BwdParams &bp, int slices, const f
       if (e != hipSuccess) return e;
     }
   }
-  if (slices > 1) {
+  if (dg_nparts > 1) {
     const long long n = rows * bp.w.HV * (bp.w.gate_head ? 1 : bp.w.K);
     const long long blocks = (n + 255) / 256;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     if (blocks > 0) {
-      hipLaunchKernelGGL(gla_bwd_slice_sum, dim3((unsigned)blocks), dim3(256), 0, s, dg, dg_parts, (int64_t)n, slices);
+      hipLaunchKernelGGL(gla_bwd_slice_sum, dim3((unsigned)blocks), dim3(256), 0, s, dg, dg_parts, (int64_t)n,
+                         dg_nparts);
       return hipGetLastError();
     }
   }

@@ -289,15 +289,17 @@ gla_status run_forward(const gla_problem *p, const Plan &pl, const void *q, cons
 }
 
 // Backward: one chunk per slot (the forward's segment numbering with R = 1),
-// and the backward's tables.  K of at most 128; V is cut into value slices of
-// at most 128 columns, run one after another over the same state tables.
+// and the backward's tables.  K past 128 is cut into two key blocks (as the
+// forward's) and V into value slices of at most 128 columns; every (block,
+// slice) runs one after another over the same state tables.
 constexpr int kBwdSlice = 128;
 int bwd_slices(int V) { return (V + kBwdSlice - 1) / kBwdSlice; }
 
 struct BwdPlan {
   Plan fwd;  // slot numbering only (R = 1)
-  size_t off_base, off_fstate, off_dstate, off_ddecay, off_flags, off_dq_part, off_dk_part, off_dg_part,
-      off_bound, total;
+  int nkb, kb[2], slices;
+  size_t off_base, off_fstate, off_dstate, off_ddecay, off_flags, off_dq_part, off_dk_part, off_dg_part, off_dv_part,
+      off_bound, bound_bytes, total;
   bool ok;
 };
 
@@ -310,36 +312,43 @@ BwdPlan make_bwd_plan(const gla_problem *p, bool varlen) {
   const long long HV = p->HV == 0 ? p->H : p->HV;
   const long long G = HV / p->H;
   const long long slots = pl.seg_slots;
-  const int slices = bwd_slices(p->V);
+  b.nkb = key_blocks(p->K, b.kb);
+  b.slices = bwd_slices(p->V);
+  const long long Kb = b.kb[0];                               // widest key block
   const long long Vs = p->V < kBwdSlice ? p->V : kBwdSlice;  // widest slice
+  const bool gh = p->gate == GLA_GATE_PER_HEAD;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t cur = kHeaderBytes;
   b.off_base = cur;
   cur += up(varlen ? (size_t)(pl.N + 1 + slots) * sizeof(int32_t) : 0);
   b.off_fstate = cur;
-  cur += up((size_t)slots * HV * p->K * Vs * sizeof(float));
+  cur += up((size_t)slots * HV * Kb * Vs * sizeof(float));
   b.off_dstate = cur;
-  cur += up((size_t)slots * HV * p->K * Vs * sizeof(float));
+  cur += up((size_t)slots * HV * Kb * Vs * sizeof(float));
   b.off_ddecay = cur;
-  cur += up((size_t)slots * HV * p->K * sizeof(float));
+  cur += up((size_t)slots * HV * Kb * sizeof(float));
   b.off_flags = cur;
   cur += up((size_t)slots * HV * sizeof(int32_t));
-  // fp32 shares of dq, dk per value head and slice, and of dg per slice
+  // fp32 shares: dq, dk per value head and slice; dg per slice (and key block,
+  // with a per-head gate); dv per key block
   const size_t rows = (size_t)p->B * p->T;
-  const size_t part = (G > 1 || slices > 1) ? up(slices * rows * HV * p->K * sizeof(float)) : 0;
+  const size_t part = (G > 1 || b.slices > 1) ? up(b.slices * rows * HV * p->K * sizeof(float)) : 0;
   b.off_dq_part = cur;
   cur += part;
   b.off_dk_part = cur;
   cur += part;
   b.off_dg_part = cur;
-  const size_t kg = p->gate == GLA_GATE_PER_HEAD ? 1 : p->K;
-  cur += slices > 1 ? up(slices * rows * HV * kg * sizeof(float)) : 0;
-  // with several slices, the chained scan's h0, dht and dh0 columns of one
-  // slice, staged compactly [N][HV][K][Vs]
+  const int dg_parts = b.slices * (gh ? b.nkb : 1);
+  cur += dg_parts > 1 ? up(dg_parts * rows * HV * (gh ? 1 : p->K) * sizeof(float)) : 0;
+  b.off_dv_part = cur;
+  cur += b.nkb > 1 ? up(b.nkb * rows * HV * p->V * sizeof(float)) : 0;
+  // with several blocks or slices, the chained scan's h0, dht and dh0 rows and
+  // columns of one (block, slice), staged compactly [N][HV][Kb][Vs]
   b.off_bound = cur;
-  cur += (slices > 1 && !varlen) ? 3 * up((size_t)pl.N * HV * p->K * Vs * sizeof(float)) : 0;
+  b.bound_bytes = up((size_t)pl.N * HV * Kb * Vs * sizeof(float));
+  cur += ((b.slices > 1 || b.nkb > 1) && !varlen) ? 3 * b.bound_bytes : 0;
   b.total = cur;
-  const long long scan_blocks = 2LL * pl.N * HV * ((p->K * Vs / 4 + 255) / 256);
+  const long long scan_blocks = 2LL * pl.N * HV * ((Kb * Vs / 4 + 255) / 256);
   const long long rows_quads = (long long)p->B * p->T * p->H * (p->K / 4);
   // the chunk kernel addresses a chunk's 64 token rows of an output with
   // 32-bit byte offsets
@@ -361,7 +370,6 @@ bool bwd_chain_pays(long long N, long long HV) { return 4 * N * HV >= device_cu_
 gla_status validate_bwd(const gla_problem *p) {
   const gla_status st = validate(p);
   if (st != GLA_OK) return st;
-  if (p->K > gla::kMaxKeyBlock) return GLA_ERR_UNSUPPORTED;
   return GLA_OK;
 }
 
@@ -395,79 +403,106 @@ gla_status run_backward(const gla_problem *p, const BwdPlan &bpl, const void *q,
   gla::BwdParams b{};
   b.w = w;  // seg_order stays null: the backward's kernels take slots in plain order
   b.persistent_blocks = 2 * device_cu_count();
-  b.dq = dq; b.dk = dk;
   b.Vmem = p->V;
   b.fstate = reinterpret_cast<float *>(ws + bpl.off_fstate);
   b.dstate = reinterpret_cast<float *>(ws + bpl.off_dstate);
   b.ddecay = reinterpret_cast<float *>(ws + bpl.off_ddecay);
   b.flags = reinterpret_cast<int32_t *>(ws + bpl.off_flags);
-  const int slices = bwd_slices(p->V);
+  const int slices = bpl.slices, nkb = bpl.nkb;
+  const bool gh = w.gate_head != 0;
   const long long rows = (long long)p->B * p->T;
   float *dq_part = nullptr, *dk_part = nullptr;
   if (w.G > 1 || slices > 1) {
     dq_part = reinterpret_cast<float *>(ws + bpl.off_dq_part);
     dk_part = reinterpret_cast<float *>(ws + bpl.off_dk_part);
   }
-  float *dg_parts = slices > 1 ? reinterpret_cast<float *>(ws + bpl.off_dg_part) : nullptr;
-  const long long dg_slice = rows * w.HV * (w.gate_head ? 1 : p->K);
+  const int dg_nparts = slices * (gh ? nkb : 1);
+  float *dg_parts = dg_nparts > 1 ? reinterpret_cast<float *>(ws + bpl.off_dg_part) : nullptr;
+  float *dv_parts = nkb > 1 ? reinterpret_cast<float *>(ws + bpl.off_dv_part) : nullptr;
+  const long long dg_share = rows * w.HV * (gh ? 1 : p->K), dv_share = rows * w.HV * p->V;
   // Fixed-length sequences can chain the scan into the summary kernel (one
   // chain per sequence, value head and direction): it saves the scan's pass
   // over both state tables, but a chain advances one chunk per link.
   const long long tasks = 2LL * pl.seg_slots * w.HV;
   const bool chained = !varlen && tokens && tasks + b.persistent_blocks <= INT_MAX &&
                        (p->schedule == 2 || (p->schedule == 0 && bwd_chain_pays(N, w.HV)));
-  // the chained scan's link takes h0, dht and dh0 with the slice's own width:
-  // with several slices their columns are staged through the workspace
-  const long long brows = (long long)N * w.HV * p->K;  // state rows of h0, dht, dh0
-  const size_t bbytes = ((size_t)brows * kBwdSlice * sizeof(float) + 255) & ~(size_t)255;
+  // the chained scan's link takes h0, dht and dh0 as [N][HV][Kb][Vs] of its
+  // block and slice: with several of either they are staged through the
+  // workspace (groups of Kb rows, one group per sequence and value head)
+  const bool stage = chained && (slices > 1 || nkb > 1);
   float *stage_h0 = reinterpret_cast<float *>(ws + bpl.off_bound);
-  float *stage_dht = reinterpret_cast<float *>(ws + bpl.off_bound + bbytes);
-  float *stage_dh0 = reinterpret_cast<float *>(ws + bpl.off_bound + 2 * bbytes);
-  const bool stage = chained && slices > 1;
+  float *stage_dht = reinterpret_cast<float *>(ws + bpl.off_bound + bpl.bound_bytes);
+  float *stage_dh0 = reinterpret_cast<float *>(ws + bpl.off_bound + 2 * bpl.bound_bytes);
+  const long long groups = (long long)N * w.HV;
+  const long long full_group = (long long)p->K * p->V;  // one state of h0, dht, dh0
   const size_t es = bf ? 2 : 4;
-  // Each value slice runs the whole sequence of launches over the same state
-  // tables (stream order keeps a slice's tables until its chunk kernel is done).
-  for (int sl = 0; sl < slices; ++sl) {
-    const int voff = sl * kBwdSlice;
-    b.w.V = p->V - voff < kBwdSlice ? p->V - voff : kBwdSlice;
-    b.w.v = static_cast<const char *>(v) + voff * es;
-    b.w.h0 = h0 ? h0 + voff : nullptr;
-    b.dout = static_cast<const char *>(dout) + voff * es;
-    b.dv = static_cast<char *>(dv) + voff * es;
-    b.dht = dht ? dht + voff : nullptr;
-    b.dh0 = dh0 ? dh0 + voff : nullptr;
-    b.dq_part = dq_part ? dq_part + sl * rows * w.HV * p->K : nullptr;
-    b.dk_part = dk_part ? dk_part + sl * rows * w.HV * p->K : nullptr;
-    b.dg = dg_parts ? dg_parts + sl * dg_slice : dg;
-    b.chain = nullptr;
-    if (chained) {
-      // the decay table is only read by gla_bwd_scan, which this schedule does
-      // not launch: it holds the chains' counter and flags instead
-      b.chain = reinterpret_cast<int32_t *>(ws + bpl.off_ddecay);
-      if (gla::launch_clear(b.chain, 1 + tasks, s) != hipSuccess) return GLA_ERR_HIP;
-    }
-    if (stage) {
-      if (h0) {
-        if (gla::launch_copy_rows(stage_h0, b.w.V, h0 + voff, p->V, brows, b.w.V, s) != hipSuccess) return GLA_ERR_HIP;
-        b.w.h0 = stage_h0;
+  // Each (key block, value slice) runs the whole sequence of launches over the
+  // same state tables (stream order keeps one's tables until its chunk kernel
+  // is done).
+  for (int kbi = 0; kbi < nkb; ++kbi) {
+    const int koff = kbi == 0 ? 0 : bpl.kb[0];
+    b.w.K = bpl.kb[kbi];
+    b.w.Kmem = p->K;
+    b.w.q = static_cast<const char *>(q) + koff * es;
+    b.w.k = static_cast<const char *>(k) + koff * es;
+    b.w.g = gh ? g : g + koff;
+    b.dq = static_cast<char *>(dq) + koff * es;
+    b.dk = static_cast<char *>(dk) + koff * es;
+    for (int sl = 0; sl < slices; ++sl) {
+      const int voff = sl * kBwdSlice;
+      b.w.V = p->V - voff < kBwdSlice ? p->V - voff : kBwdSlice;
+      const long long boff = (long long)koff * p->V + voff;  // first element of h0, dht, dh0
+      b.w.v = static_cast<const char *>(v) + voff * es;
+      b.w.h0 = h0 ? h0 + boff : nullptr;
+      b.dout = static_cast<const char *>(dout) + voff * es;
+      b.dv = static_cast<char *>(dv) + voff * es;
+      b.dv_part = dv_parts ? dv_parts + kbi * dv_share + voff : nullptr;
+      b.dht = dht ? dht + boff : nullptr;
+      b.dh0 = dh0 ? dh0 + boff : nullptr;
+      b.dq_part = dq_part ? dq_part + sl * rows * w.HV * p->K + koff : nullptr;
+      b.dk_part = dk_part ? dk_part + sl * rows * w.HV * p->K + koff : nullptr;
+      if (dg_parts) b.dg = dg_parts + (gh ? (long long)(kbi * slices + sl) : sl) * dg_share + (gh ? 0 : koff);
+      else b.dg = gh ? dg : dg + koff;
+      b.chain = nullptr;
+      if (chained) {
+        // the decay table is only read by gla_bwd_scan, which this schedule
+        // does not launch: it holds the chains' counter and flags instead
+        b.chain = reinterpret_cast<int32_t *>(ws + bpl.off_ddecay);
+        if (gla::launch_clear(b.chain, 1 + tasks, s) != hipSuccess) return GLA_ERR_HIP;
       }
-      if (dht) {
-        if (gla::launch_copy_rows(stage_dht, b.w.V, dht + voff, p->V, brows, b.w.V, s) != hipSuccess) return GLA_ERR_HIP;
-        b.dht = stage_dht;
+      const long long cg = (long long)b.w.K * b.w.V;  // one compact state
+      if (stage) {
+        if (h0) {
+          if (gla::launch_copy_rows(stage_h0, cg, b.w.V, b.w.h0, full_group, p->V, groups, b.w.K, b.w.V, s) !=
+              hipSuccess)
+            return GLA_ERR_HIP;
+          b.w.h0 = stage_h0;
+        }
+        if (dht) {
+          if (gla::launch_copy_rows(stage_dht, cg, b.w.V, b.dht, full_group, p->V, groups, b.w.K, b.w.V, s) !=
+              hipSuccess)
+            return GLA_ERR_HIP;
+          b.dht = stage_dht;
+        }
+        if (dh0) b.dh0 = stage_dh0;
       }
-      if (dh0) b.dh0 = stage_dh0;
+      if (tokens && gla::launch_bwd_local(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
+      if (stage && dh0 &&
+          gla::launch_copy_rows(dh0 + boff, full_group, p->V, stage_dh0, cg, b.w.V, groups, b.w.K, b.w.V, s) !=
+              hipSuccess)
+        return GLA_ERR_HIP;
+      if (!chained && gla::launch_bwd_scan(b, s) != hipSuccess) return GLA_ERR_HIP;
+      if (tokens && gla::launch_bwd_chunk(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
     }
-    if (tokens && gla::launch_bwd_local(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
-    if (stage && dh0 &&
-        gla::launch_copy_rows(dh0 + voff, p->V, stage_dh0, b.w.V, brows, b.w.V, s) != hipSuccess)
-      return GLA_ERR_HIP;
-    if (!chained && gla::launch_bwd_scan(b, s) != hipSuccess) return GLA_ERR_HIP;
-    if (tokens && gla::launch_bwd_chunk(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
   }
   if (tokens) {
+    b.w.K = p->K;  // the shares hold rows of all keys
+    b.dq = dq;
+    b.dk = dk;
     b.dq_part = dq_part;
     b.dk_part = dk_part;
-    if (gla::launch_bwd_finish(bf, b, slices, dg_parts, dg, s) != hipSuccess) return GLA_ERR_HIP;
+    if (gla::launch_bwd_finish(bf, b, slices, dg_parts, dg_nparts, dg, s) != hipSuccess) return GLA_ERR_HIP;
+    if (dv_parts && gla::launch_dv_sum(bf, dv, dv_parts, dv_share, nkb, s) != hipSuccess) return GLA_ERR_HIP;
   }
   return GLA_OK;
 }

@@ -81,10 +81,11 @@ hipError_t launch_clear(int32_t *words, long long n, hipStream_t s);
 // Backward (gla_bwd.hip).  The state tables hold one chunk per slot: chunk c
 // of sequence n is slot first(n) + c, with first(n) = n P (fixed length) or
 // seg_base[n] (packed), as the forward kernels number segments of one chunk
-// (gla_segment_plan with R = 1 fills seg_base).  K is at most 128; wider V is
-// cut into value slices of at most 128 columns, each launched on its own
-// (w.V = the slice's width, v, do, dv, h0, dht, dh0 offset to its first
-// column, Vmem = the full width, the row stride of those six).
+// (gla_segment_plan with R = 1 fills seg_base).  K past 128 is cut into two
+// key blocks and V past 128 into value slices of at most 128 columns; each
+// (block, slice) is launched on its own: w.K / w.V the block's keys and the
+// slice's columns, the tensors offset to their first key and column, w.Kmem
+// and Vmem the full widths (the row strides).
 struct BwdParams {
   WalkParams w;          // problem sizes, q, k, v, g, h0, cu, seg_base (seg_order null), scale
   const void *dout;      // [B,T,HV,V] dtype: gradient of o
@@ -101,7 +102,8 @@ struct BwdParams {
                          // before the launch) and gla_bwd_scan is not launched.  Its h0, dht and
                          // dh0 are [N][HV][K][V] (a value slice's columns staged compactly)
   int32_t *flags;        // [slots][HV]: 1 when the chunk is left to the token-by-token kernel
-  float *dq_part, *dk_part;  // [B,T,HV,K] fp32 shares of dq, dk of this value slice (G > 1 or several slices), else null
+  float *dq_part, *dk_part;  // [B,T,HV,Kmem] fp32 shares of dq, dk of this value slice (G > 1 or several slices), else null
+  float *dv_part;            // [B,T,HV,Vmem] fp32 share of dv of this key block (several key blocks), else null
   int32_t Vmem;              // value columns per row of v, do, dv, h0, dht, dh0
   int32_t persistent_blocks; // workgroups of the persistent kernels (a few per compute unit)
 };
@@ -109,15 +111,19 @@ hipError_t launch_bwd_local(bool bf16, const BwdParams &bp, hipStream_t s);
 hipError_t launch_bwd_scan(const BwdParams &bp, hipStream_t s);
 // the fast chunk kernel and the token-by-token kernel for flagged chunks
 hipError_t launch_bwd_chunk(bool bf16, const BwdParams &bp, hipStream_t s);
-// After every value slice: with dq_part, dq and dk as the sums of the shares
-// over value heads and `slices` slices (bp.dq_part / dk_part at slice 0); with
-// several slices, dg as the sum of the slices' shares dg_parts.
-hipError_t launch_bwd_finish(bool bf16, const BwdParams &bp, int slices, const float *dg_parts, float *dg,
-                             hipStream_t s);
-// Columns [0, cols) of `rows` fp32 rows from src (row stride src_stride) to dst
-// (row stride dst_stride); cols and both strides multiples of 4.
-hipError_t launch_copy_rows(float *dst, int64_t dst_stride, const float *src, int64_t src_stride, int64_t rows,
-                            int cols, hipStream_t s);
+// After every key block and value slice: with dq_part, dq and dk as the sums
+// of the shares over value heads and `slices` slices (bp.dq_part / dk_part at
+// slice 0, rows of bp.w.K keys); with dg_nparts > 1, dg as the sum of the
+// shares dg_parts.
+hipError_t launch_bwd_finish(bool bf16, const BwdParams &bp, int slices, const float *dg_parts, int dg_nparts,
+                             float *dg, hipStream_t s);
+// Columns [0, cols) of groups x rows fp32 rows: row r of group gi from src +
+// gi src_group + r src_row to dst + gi dst_group + r dst_row; cols, strides
+// and bases multiples of 4 floats.
+hipError_t launch_copy_rows(float *dst, int64_t dst_group, int64_t dst_row, const float *src, int64_t src_group,
+                            int64_t src_row, long long groups, int rows, int cols, hipStream_t s);
+// dv (n elements, input dtype) = the sum of `blocks` fp32 shares n apart.
+hipError_t launch_dv_sum(bool bf16, void *dv, const float *parts, long long n, int blocks, hipStream_t s);
 
 // WY-representation forward (gla_wy.hip): one chunk per slot as in the backward.
 struct WyParams {

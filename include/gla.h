@@ -198,9 +198,9 @@ size_t gla_bwd_workspace_bytes(const gla_problem *p);
  *            chained scan, see schedule, ran out).  It holds the state before
  *            every chunk and the state gradient reaching every chunk:
  *            2 * chunks * HV * K * min(V, 128) * 4 bytes and more.
- * Supported: K a multiple of 16 up to 128, V a multiple of 16 up to 256 (else
- * GLA_ERR_UNSUPPORTED; V past 128 runs as value slices of 128 columns, whose
- * shares of dq, dk and dg are summed in fp32 before rounding),
+ * Supported: K and V as for gla_fwd (K past 128 runs as two key blocks, whose
+ * shares of dv are summed in fp32 before rounding; V past 128 as value slices
+ * of 128 columns, whose shares of dq, dk and dg are summed the same way),
  * both dtypes, both gate layouts, HV a multiple of H, packed sequences.  Every
  * output row of a token is written; rows of other tokens are untouched.
  * Gates are exact as in the forward: a chunk in which some key decays by more

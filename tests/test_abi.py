@@ -209,8 +209,7 @@ def call_bwd(lib, p, ws=FAKE, ws_bytes=1 << 40, cu=None, dq=FAKE, do=FAKE):
     (dict(scale=0.0), BAD_SCALE),
     (dict(chunk=32), UNSUPPORTED),
     (dict(K=24), UNSUPPORTED),
-    (dict(K=144), UNSUPPORTED),         # the backward takes K up to 128, V up to 256
-    (dict(K=256, V=256), UNSUPPORTED),
+    (dict(K=272), UNSUPPORTED),         # the backward takes what the forward takes
     (dict(V=272), UNSUPPORTED),
     (dict(n_seqs=3), BAD_SHAPE),
     (dict(HV=4), BAD_SHAPE),
@@ -232,7 +231,7 @@ def test_backward_null_arguments(lib):
 
 
 @pytest.mark.parametrize("dtype", [gla.GLA_BF16, gla.GLA_F32])
-@pytest.mark.parametrize("K", [16, 48, 64, 128])
+@pytest.mark.parametrize("K", [16, 48, 64, 128, 144, 256])
 @pytest.mark.parametrize("V", [16, 96, 128, 144, 256])
 def test_backward_accepts_its_widths(lib, dtype, K, V):
     p = prob(dtype=dtype, K=K, V=V)
@@ -274,6 +273,13 @@ def test_backward_workspace_size_and_check(lib):
     pwh = prob(B=B, T=T, H=H, K=K, V=256, gate=gla.GATE_PER_HEAD)
     assert lib.gla_bwd_workspace_bytes(ctypes.byref(pwh)) == (WS_HEADER + 2 * sw + decays + up(slots * H * 4)
                                                               + 2 * shares + up(2 * B * T * H * 4) + staged)
+    # K = 192: two key blocks of 96 keys over state tables of 96 keys, dv as
+    # fp32 shares per block, and the staged boundary rows of one block
+    pk = prob(B=B, T=T, H=H, K=192, V=V)
+    sk = up(slots * H * 96 * V * 4)
+    assert lib.gla_bwd_workspace_bytes(ctypes.byref(pk)) == (WS_HEADER + 2 * sk + up(slots * H * 96 * 4)
+                                                             + up(slots * H * 4) + up(2 * B * T * H * V * 4)
+                                                             + 3 * up(B * H * 96 * V * 4))
 
 
 # ---------------------------------------------------------------- WY-representation forward

@@ -132,6 +132,26 @@ def test_value_slices(dtype, K, V, schedule):
     check_bwd(d, dtype, seed=24, label=f"K={K} V={V}", schedule=schedule)
 
 
+# K past 128 runs as two key blocks; dv (and a per-head gate's dg) are summed
+# over the blocks' fp32 shares
+@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("K,V", [(144, 64), (256, 128), (192, 256)])
+def test_key_blocks(dtype, K, V, schedule):
+    d = gi.draw(370 + K + V, 2, 150, 2, K, V, dtype=dtype, h0=True)
+    check_bwd(d, dtype, seed=28, label=f"K={K} V={V}", schedule=schedule)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_key_blocks_variants(dtype):
+    d = gi.draw(380, 2, 140, 2, 256, 64, dtype=dtype, h0=True, HV=4, gate="head")
+    check_bwd(d, dtype, seed=29, label="K=256 HV=4 gate=head")
+    d = gi.draw(381, 1, 0, 2, 160, 160, dtype=dtype, h0=True, lengths=[70, 0, 190, 5])
+    check_bwd(d, dtype, seed=30, label="K=V=160 packed")
+    d = gi.draw(382, 2, 200, 2, 256, 128, dtype=dtype, h0=True, gate_scale=40.0)
+    check_bwd(d, dtype, seed=31, label="K=256 gates x40")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_value_slices_variants(dtype):
     # value-head groups and a per-head gate; packed sequences; strong gates
@@ -246,17 +266,19 @@ def test_workload_sampled_heads(name):
     say("   max|err|/rms: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
-@pytest.mark.parametrize("dtype,gate,V", [("bf16", "key", 128), ("fp32", "key", 128), ("bf16", "head", 128),
-                                           ("bf16", "key", 256)])
-def test_chained_scan_matches_separate_scan(dtype, gate, V):
+@pytest.mark.parametrize("dtype,gate,K,V", [("bf16", "key", 128, 128), ("fp32", "key", 128, 128),
+                                             ("bf16", "head", 128, 128), ("bf16", "key", 128, 256),
+                                             ("bf16", "head", 256, 128)])
+def test_chained_scan_matches_separate_scan(dtype, gate, K, V):
     """The chained scan applies the separate scan's recurrences in the same
     order and precision to the same summaries: every output agrees bit for bit.
     Many chains of many chunks (B=4, H=16, T=1000: 64 chains of 16 chunks per
     direction) cross workgroups on different dies; the oracle checks two heads.
-    With V = 256 each value slice's h0, dht and dh0 columns are staged."""
-    d = gi.draw(920, 4, 1000, 16, 128, V, dtype=dtype, h0=True, gate=gate)
+    With V = 256 or K = 256 each value slice's or key block's h0, dht and dh0
+    rows and columns are staged."""
+    d = gi.draw(920, 4, 1000, 16, K, V, dtype=dtype, h0=True, gate=gate)
     do, dht = grads_in(d, dtype, 21)
-    say(f"bwd chained vs separate scan: B=4 T=1000 H=16 K=128 V={V} {dtype} gate={gate}")
+    say(f"bwd chained vs separate scan: B=4 T=1000 H=16 K={K} V={V} {dtype} gate={gate}")
     a = run_bwd_gpu(d, do, dht, dtype, schedule=1)
     b = run_bwd_gpu(d, do, dht, dtype, schedule=2)
     for name, x, y in zip(("dq", "dk", "dv", "dg", "dh0"), a, b):
