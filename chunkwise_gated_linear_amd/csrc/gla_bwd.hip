@@ -31,8 +31,10 @@
 // Kernels (launched by the host in this order):
 //   gla_bwd_local       per (chunk, value head): the chunk's summaries
 //                       sum_j k_j e^{G_last - G_j} v_j^T and scale (q e^G)^T do, and a;
-//                       for fixed-length sequences it can also chain them into
-//                       S_c, E_c and dh0 itself (then gla_bwd_scan is not launched)
+//                       it can also chain them into S_c, E_c and dh0 itself (then
+//                       gla_bwd_scan is not launched; packed sequences first get a
+//                       task table from gla_bwd_chain_plan, and those without
+//                       chunks their dh0 from gla_bwd_empty_dh0)
 //   gla_bwd_scan        per state element: S_c forward, E_c in reverse, dh0
 //   gla_bwd_chunk       per (chunk, value head): dq, dk, dv, dg (bf16 MFMA on split
 //                       operands for the bf16 products named below, fp32 MFMA otherwise)
@@ -279,9 +281,9 @@ __device__ __forceinline__ u32x4_t pack8(const float (&x)[8]) {
 // Two schedules.  Without bp.chain, task t < 2 slots HV forms Sigma (first
 // half) or D (second half) of slot t / HV and head t % HV, stores it in
 // fstate / dstate (and a_c in ddecay), and gla_bwd_scan then walks the
-// tables.  With bp.chain (fixed-length sequences) the walks run inside this
-// kernel: every (sequence, value head) has a state chain over chunks
-// 0, 1, .., P-1 and a gradient chain over P-1, .., 0, and each task applies
+// tables.  With bp.chain the walks run inside this kernel: every (sequence,
+// value head) with P chunks has a state chain over chunks 0, 1, .., P-1 and a
+// gradient chain over P-1, .., 0, and each task applies
 // one step of the scan's recurrences to the state its predecessor published:
 //   state:    slot c holds S_c;  S_{c+1} = a_c S_c + Sigma_c goes to slot c + 1
 //   gradient: slot c holds E_c;  E_{c-1} = D_c + a_c E_c goes to slot c - 1,
@@ -315,6 +317,7 @@ struct LocalRows {
 struct LocalTask {
   ChunkAt ca;
   int hv, slot;
+  int nc;  // chunks of the task's sequence (the length of its chains)
   bool grad, work;
 };
 
@@ -329,6 +332,7 @@ __device__ __forceinline__ bool local_task(const BwdParams &bp, int t, LocalTask
   const int blk = lt.grad ? t - half : t;
   lt.slot = blk / p.HV;
   lt.hv = blk - lt.slot * p.HV;
+  lt.nc = 0;  // no chains in this schedule
   lt.work = true;
   return chunk_at(p, lt.slot, lt.ca);
 }
@@ -345,8 +349,43 @@ __device__ __forceinline__ bool chained_task(const BwdParams &bp, int t, LocalTa
   lt.hv = rem - n * p.HV;
   const int c = lt.grad ? p.P - 1 - step : step;
   lt.slot = n * p.P + c;
+  lt.nc = p.P;
   lt.work = lt.grad ? (c > 0 || bp.dh0 != nullptr) : c < p.P - 1;
   return chunk_at(p, lt.slot, lt.ca);
+}
+
+// Task t of the chained schedule for packed sequences.  The chain plan lists
+// u = 0 .. (total chunks - 1) as (step s, sequence n): the steps in order and,
+// within step s, the sequences with more than s chunks.  Task t is u = t / 2HV,
+// direction (t / HV) % 2 and value head t % HV, so that a chain's task at step
+// s - 1 has a lower number than its task at step s.
+__device__ __forceinline__ bool packed_chained_task(const BwdParams &bp, int t, LocalTask &lt) {
+  const WalkParams &p = bp.w;
+  const int u = t / (2 * p.HV);
+  const int rem = t - u * 2 * p.HV;
+  lt.grad = rem >= p.HV;
+  lt.hv = lt.grad ? rem - p.HV : rem;
+  const int2 sn = reinterpret_cast<const int2 *>(bp.chain_plan + kChainPlanTable)[u];
+  const int step = __builtin_amdgcn_readfirstlane(sn.x), n = __builtin_amdgcn_readfirstlane(sn.y);
+  ChunkAt &ca = lt.ca;
+  SegInfo &si = ca.si;
+  int bos, len;
+  seq_extent(p.cu, n, p.T, bos, len);
+  lt.nc = (len + kChunk - 1) / kChunk;
+  const int c = lt.grad ? lt.nc - 1 - step : step;
+  si.n = n;
+  si.first = p.seg_base[n];
+  si.nseg = p.seg_base[n + 1] - si.first;
+  si.s = c;
+  si.bos = bos;
+  si.len = len;
+  if (c < 0 || c >= lt.nc || c >= si.nseg) return false;  // a plan that does not match its sequence
+  ca.c = c;
+  ca.L = min(kChunk, len - kChunk * c);
+  ca.row0 = si.bos + (int64_t)kChunk * c;
+  lt.slot = si.first + c;
+  lt.work = lt.grad ? (c > 0 || bp.dh0 != nullptr) : c < lt.nc - 1;
+  return true;
 }
 
 template <bool BF, int KD, int VD, bool GH>
@@ -387,8 +426,8 @@ __device__ __forceinline__ void chain_step(const BwdParams &bp, const LocalTask 
   constexpr int kOutside = 0x40000000;  // a byte offset past any state
   const WalkParams &p = bp.w;
   const int c = lt.ca.c, n = lt.ca.si.n;
-  const bool first = lt.grad ? c == p.P - 1 : c == 0;
-  const bool publish = lt.grad ? c > 0 : c < p.P - 1;
+  const bool first = lt.grad ? c == lt.nc - 1 : c == 0;
+  const bool publish = lt.grad ? c > 0 : c < lt.nc - 1;
   if (!first && !lt.work) return;  // a summary nobody needs, and a slot its predecessor filled
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // the lane through an opaque copy: the offsets below would otherwise be
@@ -484,7 +523,9 @@ __device__ __forceinline__ void chain_step(const BwdParams &bp, const LocalTask 
   }
 }
 
-template <bool BF, int KD, int VD, bool GH>
+// PC: the chained schedule for packed sequences (its own instantiation, so
+// that the table decode adds nothing to the registers of the others).
+template <bool BF, int KD, int VD, bool GH, bool PC>
 __global__ __launch_bounds__(256, 2) void gla_bwd_local(BwdParams bp) {
   const WalkParams &p = bp.w;
   using R = LocalRows<BF, KD, VD, GH>;
@@ -495,7 +536,10 @@ __global__ __launch_bounds__(256, 2) void gla_bwd_local(BwdParams bp) {
   __shared__ float sdec[KD];  // a_c per key
   __shared__ int sclaim;      // chained schedule: the task number taken from the counter
   const bool chained = bp.chain != nullptr;
-  const unsigned ntask = 2u * p.seg_slots * p.HV;
+  // packed sequences: the chain plan holds the task count and table
+  constexpr bool packed_chain = PC;
+  const unsigned ntask = packed_chain ? (unsigned)__builtin_amdgcn_readfirstlane(bp.chain_plan[kChainPlanTasks])
+                                      : 2u * p.seg_slots * p.HV;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
 
   // the next task: from the counter (chained; sclaim was written before a
@@ -504,7 +548,8 @@ __global__ __launch_bounds__(256, 2) void gla_bwd_local(BwdParams bp) {
   auto advance = [&](LocalTask &lt) -> bool {
     if (chained) {
       const unsigned t = (unsigned)__builtin_amdgcn_readfirstlane(sclaim);
-      return t < ntask && chained_task(bp, (int)t, lt);
+      if constexpr (PC) return t < ntask && packed_chained_task(bp, (int)t, lt);
+      else return t < ntask && chained_task(bp, (int)t, lt);
     }
     for (task += gridDim.x; task < ntask; task += gridDim.x)
       if (local_task(bp, (int)task, lt)) return true;
@@ -642,6 +687,100 @@ __global__ __launch_bounds__(256, 2) void gla_bwd_local(BwdParams bp) {
     }
     __syncthreads();  // LDS is refilled for the next task
   }
+}
+
+// ---------------------------------------------------------------- chain plan (packed)
+// Inclusive prefix sums of in[0, n) into out (in may equal out), by one
+// workgroup of 1024 threads in tiles of 1024.
+__device__ __forceinline__ void block_scan_1024(const int32_t *in, int32_t *out, int n, int32_t *part,
+                                                int32_t &carry) {
+  const int tid = threadIdx.x;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < n; base += 1024) {
+    part[tid] = base + tid < n ? in[base + tid] : 0;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+      const int add = tid >= d ? part[tid - d] : 0;
+      __syncthreads();
+      part[tid] += add;
+      __syncthreads();
+    }
+    if (base + tid < n) out[base + tid] = carry + part[tid];
+    __syncthreads();
+    if (tid == 1023) carry += part[1023];
+    __syncthreads();
+  }
+}
+
+// The chained scan's task table for packed sequences (one workgroup).  With
+// nc_n the chunks of sequence n (at most cmax) and cnt[s] the sequences with
+// more than s chunks: order lists the sequences by nc descending, so that the
+// first cnt[s] of them are those with a chunk s, and table[u] for u = pbase[s]
+// + rank (pbase the exclusive sums of cnt) is (s, order[rank]).  plan[0]
+// receives the task count 2 HV (total chunks).
+__global__ __launch_bounds__(1024) void gla_bwd_chain_plan(const int32_t *cu, int N, int T, int HV, int cmax,
+                                                           int slots, int32_t *plan, int32_t *hist, int32_t *cnt,
+                                                           int32_t *pbase, int32_t *order) {
+  __shared__ int32_t part[1024];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x;
+  for (int c = tid; c <= cmax; c += 1024) hist[c] = 0;
+  __syncthreads();
+  for (int n = tid; n < N; n += 1024) {
+    int bos, len;
+    seq_extent(cu, n, T, bos, len);
+    atomicAdd(&hist[min((len + kChunk - 1) / kChunk, cmax)], 1);
+  }
+  __syncthreads();
+  block_scan_1024(hist, cnt, cmax + 1, part, carry);  // sequences with at most s chunks
+  for (int c = tid; c <= cmax; c += 1024) {
+    cnt[c] = N - cnt[c];
+    hist[c] = 0;  // from here: the next free place of each chunk count
+  }
+  __syncthreads();
+  for (int n = tid; n < N; n += 1024) {
+    int bos, len;
+    seq_extent(cu, n, T, bos, len);
+    const int nc = min((len + kChunk - 1) / kChunk, cmax);
+    order[cnt[nc] + atomicAdd(&hist[nc], 1)] = n;
+  }
+  // pbase[s + 1] = cnt[0] + .. + cnt[s], pbase[0] = 0
+  if (tid == 0) pbase[0] = 0;
+  block_scan_1024(cnt, pbase + 1, cmax + 1, part, carry);
+  const int total = min(pbase[cmax + 1], slots);
+  int2 *table = reinterpret_cast<int2 *>(plan + kChainPlanTable);
+  for (int u = tid; u < total; u += 1024) {
+    int lo = 0, hi = cmax;  // the last s with pbase[s] <= u
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pbase[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    table[u] = int2{lo, order[u - pbase[lo]]};
+  }
+  if (tid == 0) plan[kChainPlanTasks] = 2 * HV * total;
+}
+
+// dh0 of the packed sequences without chunks (the chained scan has no task
+// for them): dht, or zero.  One thread per float4 of a (sequence, value head)
+// state of `rows` keys and V columns, rows Kmem apart per head and Vmem
+// floats apart, from the (block and slice offset) dh0 / dht.
+__global__ __launch_bounds__(256) void gla_bwd_empty_dh0(BwdParams bp, int rows, int64_t quads) {
+  const WalkParams &p = bp.w;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= quads) return;
+  const int q = p.V / 4;
+  const int64_t hr = e / q;  // (n, hv, row)
+  const int col = (int)(e - hr * q) * 4;
+  const int64_t nh = hr / rows;
+  const int row = (int)(hr - nh * rows);
+  const int n = (int)(nh / p.HV);
+  int bos, len;
+  seq_extent(p.cu, n, p.T, bos, len);
+  if (len > 0) return;
+  const int64_t off = (nh * p.Kmem + row) * bp.Vmem + col;
+  const f32x4_t x = bp.dht ? *reinterpret_cast<const f32x4_t *>(bp.dht + off) : zero4();
+  *reinterpret_cast<f32x4_t *>(bp.dh0 + off) = x;
 }
 
 // ---------------------------------------------------------------- gla_bwd_scan
@@ -1499,7 +1638,12 @@ template <bool BF, int KD, int VD, bool GH>
 hipError_t launch_bwd_t(int which, const BwdParams &bp, long long blocks, hipStream_t s) {
   const dim3 grid((unsigned)blocks), block(256);
   switch (which) {
-    case 0: hipLaunchKernelGGL((gla_bwd_local<BF, KD, VD, GH>), grid, block, 0, s, bp); break;
+    case 0:
+      if (bp.chain != nullptr && bp.w.seg_base != nullptr)
+        hipLaunchKernelGGL((gla_bwd_local<BF, KD, VD, GH, true>), grid, block, 0, s, bp);
+      else
+        hipLaunchKernelGGL((gla_bwd_local<BF, KD, VD, GH, false>), grid, block, 0, s, bp);
+      break;
     case 1:
       hipLaunchKernelGGL((gla_bwd_chunk<BF, KD, VD, GH>), grid, dim3(64 * chunk_waves<KD>()), 0, s, bp);
       break;
@@ -1545,6 +1689,23 @@ hipError_t launch_copy_rows(float *dst, int64_t dst_group, int64_t dst_row, cons
   if (blocks > 0x7fffffffLL || cols % 4 != 0 || rows <= 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gla_bwd_copy_rows, dim3((unsigned)blocks), dim3(256), 0, s, dst, RowsLayout{dst_group, dst_row},
                      src, RowsLayout{src_group, src_row}, rows, (int64_t)quads, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_chain_plan(const BwdParams &bp, int cmax, int32_t *scratch, hipStream_t s) {
+  const WalkParams &p = bp.w;
+  int32_t *hist = scratch, *cnt = hist + cmax + 1, *pbase = cnt + cmax + 1, *order = pbase + cmax + 2;
+  hipLaunchKernelGGL(gla_bwd_chain_plan, dim3(1), dim3(1024), 0, s, p.cu, p.N, p.T, p.HV, cmax, p.seg_slots,
+                     bp.chain_plan, hist, cnt, pbase, order);
+  return hipGetLastError();
+}
+
+hipError_t launch_empty_dh0(const BwdParams &bp, hipStream_t s) {
+  const long long quads = (long long)bp.w.N * bp.w.HV * bp.w.K * (bp.w.V / 4);
+  const long long blocks = (quads + 255) / 256;
+  if (blocks <= 0 || bp.dh0 == nullptr) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gla_bwd_empty_dh0, dim3((unsigned)blocks), dim3(256), 0, s, bp, bp.w.K, (int64_t)quads);
   return hipGetLastError();
 }
 

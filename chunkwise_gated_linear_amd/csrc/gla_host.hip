@@ -299,7 +299,8 @@ struct BwdPlan {
   Plan fwd;  // slot numbering only (R = 1)
   int nkb, kb[2], slices;
   size_t off_base, off_fstate, off_dstate, off_ddecay, off_flags, off_dq_part, off_dk_part, off_dg_part, off_dv_part,
-      off_bound, bound_bytes, total;
+      off_bound, bound_bytes, off_chain_plan, off_plan_scratch, total;
+  int cmax;  // packed: chunks of the longest possible sequence
   bool ok;
 };
 
@@ -346,7 +347,13 @@ BwdPlan make_bwd_plan(const gla_problem *p, bool varlen) {
   // columns of one (block, slice), staged compactly [N][HV][Kb][Vs]
   b.off_bound = cur;
   b.bound_bytes = up((size_t)pl.N * HV * Kb * Vs * sizeof(float));
-  cur += ((b.slices > 1 || b.nkb > 1) && !varlen) ? 3 * b.bound_bytes : 0;
+  cur += (b.slices > 1 || b.nkb > 1) ? 3 * b.bound_bytes : 0;
+  // packed: the chained scan's task table and its plan's scratch
+  b.cmax = (int)(((long long)p->T + gla::kChunk - 1) / gla::kChunk);
+  b.off_chain_plan = cur;
+  cur += varlen ? up((size_t)gla::chain_plan_words(pl.seg_slots) * sizeof(int32_t)) : 0;
+  b.off_plan_scratch = cur;
+  cur += varlen ? up((size_t)gla::chain_plan_scratch_words(b.cmax, pl.N) * sizeof(int32_t)) : 0;
   b.total = cur;
   const long long scan_blocks = 2LL * pl.N * HV * ((Kb * Vs / 4 + 255) / 256);
   const long long rows_quads = (long long)p->B * p->T * p->H * (p->K / 4);
@@ -420,12 +427,19 @@ gla_status run_backward(const gla_problem *p, const BwdPlan &bpl, const void *q,
   float *dg_parts = dg_nparts > 1 ? reinterpret_cast<float *>(ws + bpl.off_dg_part) : nullptr;
   float *dv_parts = nkb > 1 ? reinterpret_cast<float *>(ws + bpl.off_dv_part) : nullptr;
   const long long dg_share = rows * w.HV * (gh ? 1 : p->K), dv_share = rows * w.HV * p->V;
-  // Fixed-length sequences can chain the scan into the summary kernel (one
-  // chain per sequence, value head and direction): it saves the scan's pass
-  // over both state tables, but a chain advances one chunk per link.
+  // The scan can be chained into the summary kernel (one chain per sequence,
+  // value head and direction): it saves the scan's pass over both state
+  // tables, but a chain advances one chunk per link.
   const long long tasks = 2LL * pl.seg_slots * w.HV;
-  const bool chained = !varlen && tokens && tasks + b.persistent_blocks <= INT_MAX &&
+  const bool chained = tokens && tasks + b.persistent_blocks <= INT_MAX &&
                        (p->schedule == 2 || (p->schedule == 0 && bwd_chain_pays(N, w.HV)));
+  if (chained && varlen) {
+    // packed: the task table orders each step's chains by sequence length
+    b.chain_plan = reinterpret_cast<int32_t *>(ws + bpl.off_chain_plan);
+    if (gla::launch_chain_plan(b, bpl.cmax, reinterpret_cast<int32_t *>(ws + bpl.off_plan_scratch), s) !=
+        hipSuccess)
+      return GLA_ERR_HIP;
+  }
   // the chained scan's link takes h0, dht and dh0 as [N][HV][Kb][Vs] of its
   // block and slice: with several of either they are staged through the
   // workspace (groups of Kb rows, one group per sequence and value head)
@@ -491,6 +505,13 @@ gla_status run_backward(const gla_problem *p, const BwdPlan &bpl, const void *q,
           gla::launch_copy_rows(dh0 + boff, full_group, p->V, stage_dh0, cg, b.w.V, groups, b.w.K, b.w.V, s) !=
               hipSuccess)
         return GLA_ERR_HIP;
+      if (chained && varlen && dh0) {
+        // sequences without chunks have no chain: their dh0 is dht (or zero)
+        gla::BwdParams e = b;
+        e.dh0 = dh0 + boff;
+        e.dht = dht ? dht + boff : nullptr;
+        if (gla::launch_empty_dh0(e, s) != hipSuccess) return GLA_ERR_HIP;
+      }
       if (!chained && gla::launch_bwd_scan(b, s) != hipSuccess) return GLA_ERR_HIP;
       if (tokens && gla::launch_bwd_chunk(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
     }

@@ -86,6 +86,11 @@ hipError_t launch_clear(int32_t *words, long long n, hipStream_t s);
 // (block, slice) is launched on its own: w.K / w.V the block's keys and the
 // slice's columns, the tensors offset to their first key and column, w.Kmem
 // and Vmem the full widths (the row strides).
+constexpr int kChainPlanTasks = 0, kChainPlanTable = 2;  // words of the chain plan
+constexpr int chain_plan_words(int slots) { return kChainPlanTable + 2 * slots; }
+// scratch words of launch_chain_plan for sequences of at most cmax chunks
+constexpr long long chain_plan_scratch_words(int cmax, int N) { return 3LL * cmax + 4 + N; }
+
 struct BwdParams {
   WalkParams w;          // problem sizes, q, k, v, g, h0, cu, seg_base (seg_order null), scale
   const void *dout;      // [B,T,HV,V] dtype: gradient of o
@@ -97,10 +102,12 @@ struct BwdParams {
   float *fstate;         // [slots][HV][K][V]: chunk summaries of the state, then S_c (state before chunk c)
   float *dstate;         // [slots][HV][K][V]: chunk summaries of the state gradient, then E_c
   float *ddecay;         // [slots][HV][K]: e^{G_last} of each chunk
-  int32_t *chain;        // fixed-length sequences, or null: gla_bwd_local also walks the chains
+  int32_t *chain;        // the chained schedule, or null: gla_bwd_local also walks the chains
                          // of S_c and E_c ([0] task counter, then flags [2][slots][HV]; zeroed
                          // before the launch) and gla_bwd_scan is not launched.  Its h0, dht and
                          // dh0 are [N][HV][K][V] (a value slice's columns staged compactly)
+  int32_t *chain_plan;   // packed sequences with the chain: [kChainPlanTasks] task count, from word
+                         // kChainPlanTable the (step, sequence) int2 table (launch_chain_plan)
   int32_t *flags;        // [slots][HV]: 1 when the chunk is left to the token-by-token kernel
   float *dq_part, *dk_part;  // [B,T,HV,Kmem] fp32 shares of dq, dk of this value slice (G > 1 or several slices), else null
   float *dv_part;            // [B,T,HV,Vmem] fp32 share of dv of this key block (several key blocks), else null
@@ -122,6 +129,12 @@ hipError_t launch_bwd_finish(bool bf16, const BwdParams &bp, int slices, const f
 // and bases multiples of 4 floats.
 hipError_t launch_copy_rows(float *dst, int64_t dst_group, int64_t dst_row, const float *src, int64_t src_group,
                             int64_t src_row, long long groups, int rows, int cols, hipStream_t s);
+// The chained scan's task table for packed sequences (bp.chain_plan, from
+// cu_seqlens; sequences of at most cmax chunks; scratch of
+// chain_plan_scratch_words(cmax, N) words).
+hipError_t launch_chain_plan(const BwdParams &bp, int cmax, int32_t *scratch, hipStream_t s);
+// dh0 = dht (or zero) for the packed sequences without chunks.
+hipError_t launch_empty_dh0(const BwdParams &bp, hipStream_t s);
 // dv (n elements, input dtype) = the sum of `blocks` fp32 shares n apart.
 hipError_t launch_dv_sum(bool bf16, void *dv, const float *parts, long long n, int blocks, hipStream_t s);
 

@@ -259,8 +259,11 @@ def test_backward_workspace_size_and_check(lib):
     pv = prob(B=1, T=1000, n_seqs=5, packed=1, H=H, K=K, V=V)
     slots_v = 5 + 16 + 5
     sv, dv_ = up(slots_v * H * K * V * 4), up(slots_v * H * K * 4)
+    # ... and the chained scan's task table (a count and an int pair per slot)
+    # with its plan's scratch (3 cmax + 4 + N words, cmax = ceil(T / 64))
+    plan_v = up((2 + 2 * slots_v) * 4) + up((3 * 16 + 4 + 5) * 4)
     assert lib.gla_bwd_workspace_bytes(ctypes.byref(pv)) == (WS_HEADER + up((6 + slots_v) * 4) + 2 * sv + dv_
-                                                             + up(slots_v * H * 4))
+                                                             + up(slots_v * H * 4) + plan_v)
     # V = 256: two value slices of 128 columns run one after the other over
     # state tables of 128 columns, with fp32 shares of dq, dk and dg per slice,
     # and one slice's columns of h0, dht and dh0 staged for the chained scan

@@ -148,6 +148,7 @@ def test_key_blocks_variants(dtype):
     check_bwd(d, dtype, seed=29, label="K=256 HV=4 gate=head")
     d = gi.draw(381, 1, 0, 2, 160, 160, dtype=dtype, h0=True, lengths=[70, 0, 190, 5])
     check_bwd(d, dtype, seed=30, label="K=V=160 packed")
+    check_bwd(d, dtype, seed=30, label="K=V=160 packed, chained scan", schedule=2)
     d = gi.draw(382, 2, 200, 2, 256, 128, dtype=dtype, h0=True, gate_scale=40.0)
     check_bwd(d, dtype, seed=31, label="K=256 gates x40")
 
@@ -160,14 +161,16 @@ def test_value_slices_variants(dtype):
     check_bwd(d, dtype, seed=25, label="V=256 HV=4 gate=head")
     d = gi.draw(361, 1, 0, 2, 64, 160, dtype=dtype, h0=True, lengths=[70, 0, 190, 5])
     check_bwd(d, dtype, seed=26, label="V=160 packed")
+    check_bwd(d, dtype, seed=26, label="V=160 packed, chained scan", schedule=2)
     d = gi.draw(362, 2, 200, 2, 64, 256, dtype=dtype, h0=True, gate_scale=40.0)
     check_bwd(d, dtype, seed=27, label="V=256 gates x40")
 
 
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_packed(dtype):
+def test_packed(dtype, schedule):
     d = gi.draw(401, 1, 0, 2, 64, 128, dtype=dtype, h0=True, lengths=[0, 1, 64, 65, 200, 3, 128])
-    check_bwd(d, dtype, seed=10, label="packed")
+    check_bwd(d, dtype, seed=10, label="packed", schedule=schedule)
 
 
 @pytest.mark.parametrize("schedule", SCHEDULES)
@@ -188,10 +191,11 @@ def test_head_and_gate_variants(dtype, HV, gate, schedule):
     check_bwd(d, dtype, seed=12, label=f"HV={H * HV} gate={gate}", schedule=schedule)
 
 
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_head_variants_packed(dtype):
+def test_head_variants_packed(dtype, schedule):
     d = gi.draw(650, 1, 0, 2, 64, 128, dtype=dtype, h0=True, lengths=[70, 0, 190, 5], HV=4, gate="head")
-    check_bwd(d, dtype, seed=13, label="packed heads")
+    check_bwd(d, dtype, seed=13, label="packed heads", schedule=schedule)
 
 
 @pytest.mark.parametrize("schedule", SCHEDULES)
@@ -287,6 +291,32 @@ def test_chained_scan_matches_separate_scan(dtype, gate, K, V):
     ds = head_slice(d, heads)
     ref = oracle.gla_reference_bwd(ds["q"], ds["k"], ds["v"], ds["g"], np.ascontiguousarray(do[:, :, heads]),
                                    h0=ds["h0"], dht=np.ascontiguousarray(dht[:, heads]))
+    for name, x, r in zip(("dq", "dk", "dv", "dg", "dh0"), b, ref):
+        x = x[:, heads] if name == "dh0" else x[:, :, heads]
+        check_close(name, x, r, TOL_HT if name in ("dg", "dh0") else TOL[dtype],
+                    out_dtype="fp32" if name in ("dg", "dh0") else dtype)
+
+
+@pytest.mark.parametrize("dtype,K,V", [("bf16", 64, 64), ("fp32", 64, 64), ("bf16", 160, 192)])
+def test_chained_scan_packed_matches_separate_scan(dtype, K, V):
+    """Packed sequences: the chain plan orders each step's chains by sequence
+    length; sequences without chunks keep dh0 = dht.  Every output agrees bit
+    for bit with the separate scan; the oracle checks two heads."""
+    rng = np.random.default_rng(945)
+    lengths = [int(x) for x in rng.integers(0, 700, size=40)]
+    lengths[3] = lengths[17] = 0
+    lengths[5], lengths[8], lengths[9], lengths[30] = 1, 64, 65, 1500
+    d = gi.draw(946, 1, 0, 8, K, V, dtype=dtype, h0=True, lengths=lengths)
+    do, dht = grads_in(d, dtype, 32)
+    say(f"bwd packed chained vs separate scan: 40 sequences H=8 K={K} V={V} {dtype}")
+    a = run_bwd_gpu(d, do, dht, dtype, schedule=1)
+    b = run_bwd_gpu(d, do, dht, dtype, schedule=2)
+    for name, x, y in zip(("dq", "dk", "dv", "dg", "dh0"), a, b):
+        assert np.array_equal(x, y), f"{name}: max|diff| {np.max(np.abs(x - y)):.3e}"
+    heads = [2, 7]
+    ds = head_slice(d, heads)
+    ref = oracle.gla_reference_bwd(ds["q"], ds["k"], ds["v"], ds["g"], np.ascontiguousarray(do[:, :, heads]),
+                                   h0=ds["h0"], dht=np.ascontiguousarray(dht[:, heads]), cu_seqlens=d["cu_seqlens"])
     for name, x, r in zip(("dq", "dk", "dv", "dg", "dh0"), b, ref):
         x = x[:, heads] if name == "dh0" else x[:, :, heads]
         check_close(name, x, r, TOL_HT if name in ("dg", "dh0") else TOL[dtype],
