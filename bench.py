@@ -31,7 +31,7 @@ Also reported:
                 MFMA peak, whichever bound gives the longer ideal time; `traffic`
                 is the HBM bytes one forward moves (FETCH_SIZE + WRITE_SIZE of all
                 its kernels, from rocprofv3 counter runs of the current device
-                sources), null when no matching measurement exists.
+                code), null when no matching measurement exists.
   cpu_baseline  the fp64 CPU oracle (test infrastructure) on the host cores, on a
                 bounded sample of the same workload (whole sequences of the first
                 heads), in tokens/s of the full workload's head count.
@@ -81,12 +81,40 @@ def cpu_model() -> str:
     return "unknown CPU"
 
 
+def code_only(text: str) -> str:
+    """C++ source without its comments, blank lines and indentation: what the
+    compiler sees of it (string and character literals are kept whole)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (line.strip() for line in "".join(out).split("\n"))
+    return "\n".join(line for line in lines if line)
+
+
 def kernel_source_hash(which: str = "fwd") -> str:
-    """Hash of the device and launch sources of one pass: counters measured on other code are not reused."""
+    """Hash of the code (comments aside) of the device and launch sources of one
+    pass: counters measured on other code are not reused."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS[which]:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
+            h.update(b"\0")
     return h.hexdigest()[:16]
 
 

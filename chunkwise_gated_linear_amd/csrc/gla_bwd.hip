@@ -41,7 +41,15 @@
 //   gla_bwd_chunk_exact per (chunk, value head) whose decay leaves the fp32 range
 //                       of the factors e^-G (some key below e^-80 within the
 //                       chunk): the same gradients token by token
-//   gla_bwd_group_sum   with several value heads per key head: dq, dk summed
+//   gla_bwd_group_sum   with several value heads per key head or several value
+//                       slices: dq, dk summed over their fp32 shares
+//   gla_bwd_slice_sum   with several value slices (or, per-head gate, key
+//                       blocks): dg summed over the shares
+//   gla_bwd_dv_sum      with several key blocks: dv summed over the shares
+// K past 128 runs as two key blocks and V past 128 as value slices of 128
+// columns; each (block, slice) runs the per-chunk launches above on its own
+// (gla_bwd_copy_rows stages its rows and columns of h0, dht and dh0 for the
+// chained scan), and the sums follow the last of them.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

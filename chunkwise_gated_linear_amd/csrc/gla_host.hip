@@ -10,11 +10,18 @@
 //
 // Backward (page "fla/ops/gla/fused_chunk.py", FusedChunkGLAFunction.backward):
 //   [packed input]                       gla_segment_plan (one chunk per segment)
-//   [tokens]                             gla_bwd_local: chunk summaries of the state
-//                                        and of its gradient
-//   [tokens, or dh0 wanted]              gla_bwd_scan: S_c and E_c per chunk, dh0
-//   [tokens]                             gla_bwd_chunk, gla_bwd_chunk_exact
-//                                        (+ gla_bwd_group_sum with HV > H)
+//   [packed input, chained scan]         gla_bwd_chain_plan: chains ordered by length
+//   per key block (K > 128: two) and value slice (V > 128: 128 columns each):
+//     [chained, several blocks/slices]   gla_bwd_copy_rows: stage h0 and dht
+//     [tokens]                           gla_bwd_local: chunk summaries of the state
+//                                        and of its gradient (chained schedule: and
+//                                        the scan itself, S_c, E_c and dh0)
+//     [chained, staged dh0]              gla_bwd_copy_rows: dh0 back into place
+//     [chained, packed, dh0 wanted]      gla_bwd_empty_dh0 for sequences without chunks
+//     [separate scan: tokens or dh0]     gla_bwd_scan: S_c and E_c per chunk, dh0
+//     [tokens]                           gla_bwd_chunk, gla_bwd_chunk_exact
+//   [tokens, several shares]             gla_bwd_group_sum, gla_bwd_slice_sum,
+//                                        gla_bwd_dv_sum
 #include <hip/hip_runtime.h>
 
 #include <climits>
