@@ -439,9 +439,10 @@ def main():
     ap.add_argument("--single", type=int, default=11,
                     help="launches timed one by one after the timed steps, warm and with L2/MALL evicted")
     ap.add_argument("--segment-chunks", type=int, default=0)
-    ap.add_argument("--schedule", type=int, default=0, choices=[0, 1, 2],
+    ap.add_argument("--schedule", type=int, default=0, choices=[0, 1, 2, 3],
                     help="segmented sequences: 0 automatic, 1 three passes, 2 one pass; with --pass bwd: "
-                         "0 automatic, 1 a separate scan launch, 2 the scan chained into the summary kernel")
+                         "0 automatic, 1 a separate scan launch, 2 the scan chained into the summary kernel, "
+                         "3 the summary kernel walking whole chains")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the forward, run a plain 512 MiB device copy "
                          "(used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")

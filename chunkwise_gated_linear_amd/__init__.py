@@ -232,8 +232,9 @@ def gla_bwd(q, k, v, g, do, h0=None, dht=None, cu_seqlens=None, scale: Optional[
     ``need_dh0`` (default: h0 was given) else None.  Asynchronous on torch's
     current stream; a given ``workspace`` (uint8, zeroed before its first use) is
     used when large enough.  ``schedule``: 0 automatic, 1 a separate scan
-    launch, 2 the scan chained into the summary kernel; ``wait_limit`` bounds
-    the chained scan's waits as for gla_fwd.
+    launch, 2 the scan chained into the summary kernel, 3 the summary kernel
+    walking whole chains; ``wait_limit`` bounds the chained scan's waits as
+    for gla_fwd.
     """
     import torch
 

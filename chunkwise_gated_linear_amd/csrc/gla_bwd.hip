@@ -144,25 +144,32 @@ __device__ __forceinline__ bool chunk_at(const WalkParams &p, int slot, ChunkAt 
 // afterwards buf[swz<KD>(row, key)] = G for every row and key (keys past K
 // get 0).  Thread t of NT sums key t % KD over rows [part RP, part RP + RP),
 // part = t / KD; part totals go through tot[NT].  Starts after a barrier that
-// made buf visible and ends with one.
-template <int KD, bool GH, int NT>
+// made buf visible and ends with one.  GUARD: the workgroup has more than NT
+// threads, and the others only meet the barriers (the sums, and so their
+// rounding, depend on NT alone).
+template <int KD, bool GH, int NT, bool GUARD = false>
 __device__ __forceinline__ void gate_cumsum_lds(int K, float *buf, float *tot) {
   constexpr int PARTS = NT / KD, RP = 64 / PARTS;
   const int kk = threadIdx.x % KD, part = threadIdx.x / KD;
+  const bool in = !GUARD || threadIdx.x < NT;
   float G[RP];
   float x = 0.f;
+  if (in) {
 #pragma unroll
-  for (int r = 0; r < RP; ++r) {
-    const int i = part * RP + r;
-    x += (kk < K) ? (GH ? buf[i] : buf[swz<KD>(i, kk)]) : 0.f;
-    G[r] = x;
+    for (int r = 0; r < RP; ++r) {
+      const int i = part * RP + r;
+      x += (kk < K) ? (GH ? buf[i] : buf[swz<KD>(i, kk)]) : 0.f;
+      G[r] = x;
+    }
+    tot[threadIdx.x] = x;
   }
-  tot[threadIdx.x] = x;
   __syncthreads();
-  float off = 0.f;
-  for (int q = 0; q < part; ++q) off += tot[q * KD + kk];
+  if (in) {
+    float off = 0.f;
+    for (int q = 0; q < part; ++q) off += tot[q * KD + kk];
 #pragma unroll
-  for (int r = 0; r < RP; ++r) buf[swz<KD>(part * RP + r, kk)] = G[r] + off;
+    for (int r = 0; r < RP; ++r) buf[swz<KD>(part * RP + r, kk)] = G[r] + off;
+  }
   __syncthreads();
 }
 
@@ -313,11 +320,11 @@ __device__ __forceinline__ u32x4_t pack8(const float (&x)[8]) {
 //
 // Persistent workgroups (two per compute unit); the rows of a workgroup's
 // next task are loaded into registers while it forms the current one.
-template <bool BF, int KD, int VD, bool GH>
+template <bool BF, int KD, int VD, bool GH, int NT>
 struct LocalRows {
-  static constexpr int TK = 64 * KD / 4 / 256, TV = 64 * VD / 4 / 256;  // row quads per thread
+  static constexpr int TK = 64 * KD / 4 / NT, TV = 64 * VD / 4 / NT;  // row quads per thread
   typename RawQuad<BF>::type x[TK], y[TV];
-  GateRows<KD, GH, 256> gate;
+  GateRows<KD, GH, NT> gate;
 };
 
 // A task: chunk ca of value head hv, the state summary (grad false) or the
@@ -396,9 +403,52 @@ __device__ __forceinline__ bool packed_chained_task(const BwdParams &bp, int t, 
   return true;
 }
 
-template <bool BF, int KD, int VD, bool GH>
-__device__ __forceinline__ void local_load(const BwdParams &bp, const LocalTask &lt, LocalRows<BF, KD, VD, GH> &rw) {
-  using R = LocalRows<BF, KD, VD, GH>;
+// Step `step` of chain j of the walk schedule.  Chains 0 .. N HV - 1 are the
+// state chains of (sequence, value head) = (j / HV, j % HV), chains N HV ..
+// 2 N HV - 1 the gradient chains in the same order; a state chain takes its
+// sequence's chunks in order, a gradient chain in reverse.  False past the
+// chain's last chunk.
+__device__ __forceinline__ bool walk_task(const BwdParams &bp, int j, int step, LocalTask &lt) {
+  const WalkParams &p = bp.w;
+  const int pairs = p.N * p.HV;
+  lt.grad = j >= pairs;
+  const int rem = lt.grad ? j - pairs : j;
+  const int n = rem / p.HV;
+  lt.hv = rem - n * p.HV;
+  if (p.seg_base == nullptr) {
+    if (step >= p.P) return false;
+    const int c = lt.grad ? p.P - 1 - step : step;
+    lt.nc = p.P;
+    lt.slot = n * p.P + c;
+    lt.work = lt.grad ? (c > 0 || bp.dh0 != nullptr) : c < p.P - 1;
+    return chunk_at(p, lt.slot, lt.ca);
+  }
+  ChunkAt &ca = lt.ca;
+  SegInfo &si = ca.si;
+  int bos, len;
+  seq_extent(p.cu, n, p.T, bos, len);
+  lt.nc = (len + kChunk - 1) / kChunk;
+  if (step >= lt.nc) return false;
+  const int c = lt.grad ? lt.nc - 1 - step : step;
+  si.n = n;
+  si.first = p.seg_base[n];
+  si.nseg = p.seg_base[n + 1] - si.first;
+  si.s = c;
+  si.bos = bos;
+  si.len = len;
+  if (c >= si.nseg) return false;  // a segment table that does not match its sequence
+  ca.c = c;
+  ca.L = min(kChunk, len - kChunk * c);
+  ca.row0 = si.bos + (int64_t)kChunk * c;
+  lt.slot = si.first + c;
+  lt.work = lt.grad ? (c > 0 || bp.dh0 != nullptr) : c < lt.nc - 1;
+  return true;
+}
+
+template <bool BF, int KD, int VD, bool GH, int NT>
+__device__ __forceinline__ void local_load(const BwdParams &bp, const LocalTask &lt,
+                                           LocalRows<BF, KD, VD, GH, NT> &rw) {
+  using R = LocalRows<BF, KD, VD, GH, NT>;
   const WalkParams &p = bp.w;
   const ChunkAt &ca = lt.ca;
   const int h = lt.hv / p.G;
@@ -407,13 +457,13 @@ __device__ __forceinline__ void local_load(const BwdParams &bp, const LocalTask 
       chunk_rows<BF>(lt.grad ? bp.dout : p.v, (ca.row0 * p.HV + lt.hv) * bp.Vmem, p.HV * bp.Vmem, p.V, ca.L);
 #pragma unroll
   for (int t = 0; t < R::TK; ++t) {
-    const int e = threadIdx.x + 256 * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
+    const int e = threadIdx.x + NT * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
     rw.x[t] = ld_row4<BF>(rx, i, c4);  // key-side rows: k, or q for the gradient
   }
-  gate_load<KD, GH, 256>(p, ca, lt.hv, rw.gate);
+  gate_load<KD, GH, NT>(p, ca, lt.hv, rw.gate);
 #pragma unroll
   for (int t = 0; t < R::TV; ++t) {
-    const int e = threadIdx.x + 256 * t, i = e / (VD / 4), c4 = (e % (VD / 4)) * 4;
+    const int e = threadIdx.x + NT * t, i = e / (VD / 4), c4 = (e % (VD / 4)) * 4;
     rw.y[t] = ld_row4<BF>(ry, i, c4);  // value-side rows: v, or do
   }
 }
@@ -531,29 +581,117 @@ __device__ __forceinline__ void chain_step(const BwdParams &bp, const LocalTask 
   }
 }
 
-// PC: the chained schedule for packed sequences (its own instantiation, so
-// that the table decode adds nothing to the registers of the others).
-template <bool BF, int KD, int VD, bool GH, bool PC>
-__global__ __launch_bounds__(256, 2) void gla_bwd_local(BwdParams bp) {
+// One step of a walk (walk schedule, eight waves) for task lt, whose summary
+// is in acc and decays in dec.  Wave w holds rows ((w % 4) NKB + a) 16 +
+// lane % 16 and the NVW column blocks from (w / 4) NVW, as chain_step's waves
+// hold all of theirs.  The workgroup carries its chain's state in x, in the
+// layout of acc, from one chunk to the next, so a step waits for nothing: the
+// chain's first chunk loads h0 / dht (or zero) into x and stores it in its own
+// slot for the chunk kernel, and every step that publishes stores x = a_c x +
+// Sigma_c (or D_c) in the next slot (after the gradient's chunk 0: in dh0).
+// Offsets as in chain_step.
+template <int KD, int NVW>
+__device__ __forceinline__ void walk_step(const BwdParams &bp, const LocalTask &lt, const f32x4_t (&acc)[KD / 64][NVW],
+                                          const float *dec, f32x4_t (&x)[KD / 64][NVW]) {
+  constexpr int NKB = KD / 64;
   const WalkParams &p = bp.w;
-  using R = LocalRows<BF, KD, VD, GH>;
-  constexpr int NKB = KD / 64, NVB = VD / 16;
+  const int c = lt.ca.c, n = lt.ca.si.n;
+  const bool first = lt.grad ? c == lt.nc - 1 : c == 0;
+  const bool publish = lt.grad ? c > 0 : c < lt.nc - 1;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rw = wave & 3, cb0 = (wave >> 2) * NVW;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
+  const int64_t KV = (int64_t)p.K * p.V;
+  float *tab = lt.grad ? bp.dstate : bp.fstate;
+  int off[NKB][NVW];
+#pragma unroll
+  for (int a = 0; a < NKB; ++a)
+#pragma unroll
+    for (int b = 0; b < NVW; ++b) {
+      const int rb = rw * NKB + a, cb = cb0 + b;  // 16-row and 16-column blocks
+      const bool in = rb * 16 < p.K && cb * 16 < p.V;
+      off[a][b] = in ? ((rb * 16 + l16) * p.V + cb * 16 + 4 * lg) * 4 : kOutsideRange;
+    }
+  if (first) {
+    const float *bound = lt.grad ? bp.dht : p.h0;
+    if (bound != nullptr) {
+      const __amdgpu_buffer_rsrc_t rB = make_rsrc(bound + ((int64_t)n * p.HV + lt.hv) * KV, KV * 4);
+#pragma unroll
+      for (int a = 0; a < NKB; ++a)
+#pragma unroll
+        for (int b = 0; b < NVW; ++b) x[a][b] = buf_ldf4<0>(rB, off[a][b]);
+    } else {
+#pragma unroll
+      for (int a = 0; a < NKB; ++a)
+#pragma unroll
+        for (int b = 0; b < NVW; ++b) x[a][b] = zero4();
+    }
+    const __amdgpu_buffer_rsrc_t rHere = make_rsrc(tab + ((int64_t)lt.slot * p.HV + lt.hv) * KV, KV * 4);
+#pragma unroll
+    for (int a = 0; a < NKB; ++a)
+#pragma unroll
+      for (int b = 0; b < NVW; ++b) buf_stf4<0>(rHere, off[a][b], x[a][b]);
+  }
+  if (!publish && !lt.work) return;
+  float *out = publish ? tab + ((int64_t)(lt.grad ? lt.slot - 1 : lt.slot + 1) * p.HV + lt.hv) * KV
+                       : bp.dh0 + ((int64_t)n * p.HV + lt.hv) * KV;
+  const __amdgpu_buffer_rsrc_t rOut = make_rsrc(out, KV * 4);
+#pragma unroll
+  for (int a = 0; a < NKB; ++a) {
+    const float ak = dec[(rw * NKB + a) * 16 + l16];  // rows past K: stores dropped
+#pragma unroll
+    for (int b = 0; b < NVW; ++b) {
+      x[a][b] = ak * x[a][b] + acc[a][b];
+      buf_stf4<0>(rOut, off[a][b], x[a][b]);
+    }
+  }
+}
+
+// MODE: kLocalTasks (the three-launch schedule, or the chained schedule for
+// fixed-length sequences), kLocalPackedChain (the chained schedule for packed
+// sequences: its own instantiation, so that the table decode adds nothing to
+// the registers of the others) or kLocalWalk (the walk schedule: one chain per
+// workgroup at a time).  The walk runs eight waves, the others four: waves w
+// and w + 4 form the same rows of a summary, each half of its columns (so
+// that the registers that carry the state leave room for a second wave per
+// SIMD).
+constexpr int kLocalTasks = 0, kLocalPackedChain = 1, kLocalWalk = 2;
+constexpr int local_threads(int mode) { return mode == kLocalWalk ? 512 : 256; }
+template <bool BF, int KD, int VD, bool GH, int MODE>
+__global__ __launch_bounds__(local_threads(MODE), MODE == kLocalWalk ? 1 : 2) void gla_bwd_local(BwdParams bp) {
+  constexpr bool PC = MODE == kLocalPackedChain, WALK = MODE == kLocalWalk;
+  constexpr int NT = local_threads(MODE);
+  const WalkParams &p = bp.w;
+  using R = LocalRows<BF, KD, VD, GH, NT>;
+  // each wave: NKB 16-row blocks from row (wave % 4) 16 NKB, NVW 16-column
+  // blocks from column (wave / 4) 16 NVW
+  constexpr int NKB = KD / 64, NVW = VD / 16 / (NT / 256);
   __shared__ __attribute__((aligned(16))) float sA[64 * KD];  // G, then k e^{G_last - G} or scale q e^G
   __shared__ __attribute__((aligned(16))) float sB[64 * VD];  // v or do
-  __shared__ float tot[256];
+  __shared__ float tot[NT];
   __shared__ float sdec[KD];  // a_c per key
   __shared__ int sclaim;      // chained schedule: the task number taken from the counter
-  const bool chained = bp.chain != nullptr;
-  // packed sequences: the chain plan holds the task count and table
-  constexpr bool packed_chain = PC;
-  const unsigned ntask = packed_chain ? (unsigned)__builtin_amdgcn_readfirstlane(bp.chain_plan[kChainPlanTasks])
-                                      : 2u * p.seg_slots * p.HV;
+  const bool chained = !WALK && bp.chain != nullptr;
+  // packed sequences: the chain plan holds the task count and table; walk:
+  // the tasks are the chains
+  const unsigned ntask = PC     ? (unsigned)__builtin_amdgcn_readfirstlane(bp.chain_plan[kChainPlanTasks])
+                         : WALK ? 2u * p.N * p.HV
+                                : 2u * p.seg_slots * p.HV;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
+  // the wave's first row block / NKB and first column block
+  const int rw = NT == 256 ? wave : wave & 3, cb0 = NT == 256 ? 0 : (wave >> 2) * NVW;
 
-  // the next task: from the counter (chained; sclaim was written before a
-  // barrier), else the next one with a chunk on the grid stride
-  unsigned task = blockIdx.x - gridDim.x;  // wraps; the first step adds gridDim.x back
+  // the next task: walk, the next step of the chain (or the first of the
+  // next chain on the grid stride); chained, from the counter (sclaim was
+  // written before a barrier); else the next one with a chunk on the grid stride
+  unsigned task = WALK ? blockIdx.x : blockIdx.x - gridDim.x;  // wraps; the first step adds gridDim.x back
+  int step = -1;                                                // walk: the step within chain `task`
   auto advance = [&](LocalTask &lt) -> bool {
+    if constexpr (WALK) {
+      for (++step; task < ntask; task += gridDim.x, step = 0)
+        if (walk_task(bp, (int)task, step, lt)) return true;
+      return false;
+    }
     if (chained) {
       const unsigned t = (unsigned)__builtin_amdgcn_readfirstlane(sclaim);
       if constexpr (PC) return t < ntask && packed_chained_task(bp, (int)t, lt);
@@ -568,27 +706,30 @@ __global__ __launch_bounds__(256, 2) void gla_bwd_local(BwdParams bp) {
       sclaim = __hip_atomic_fetch_add(bp.chain, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 
-  R rw;
+  R rows;
   LocalTask nxt;
+  f32x4_t wx[NKB][NVW];  // walk: the chain's state
   claim();
   __syncthreads();
   bool have = advance(nxt);
   __syncthreads();  // sclaim is read before the loop's first claim overwrites it
-  if (have && nxt.work) local_load<BF, KD, VD, GH>(bp, nxt, rw);
+  if (have && nxt.work) local_load<BF, KD, VD, GH, NT>(bp, nxt, rows);
   while (have) {
     const LocalTask cur = nxt;
     claim();
     if (cur.work) {
       // gate rows -> LDS, cumsum down each key column (G in sA)
-      gate_stage<KD, GH, 256>(rw.gate, sA);
+      gate_stage<KD, GH, NT>(rows.gate, sA);
       __syncthreads();
-      gate_cumsum_lds<KD, GH, 256>(p.K, sA, tot);
+      // the cumsum in the four-wave order whatever NT: every schedule forms
+      // the same summaries, bit for bit
+      gate_cumsum_lds<KD, GH, 256, (NT > 256)>(p.K, sA, tot);
       f32x4_t xg[R::TK];
 #pragma unroll
       for (int t = 0; t < R::TK; ++t) {
-        const int e = threadIdx.x + 256 * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
+        const int e = threadIdx.x + NT * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
         const f32x4_t G4 = lds4<KD>(sA, i, c4), Gl4 = lds4<KD>(sA, 63, c4);
-        f32x4_t xt = unpack4<BF>(rw.x[t]);
+        f32x4_t xt = unpack4<BF>(rows.x[t]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) xt[r] *= cur.grad ? p.scale * __expf(G4[r]) : __expf(Gl4[r] - G4[r]);
         xg[t] = xt;
@@ -597,34 +738,34 @@ __global__ __launch_bounds__(256, 2) void gla_bwd_local(BwdParams bp) {
           for (int r = 0; r < 4; ++r) {
             const float a = __expf(Gl4[r]);
             sdec[c4 + r] = a;
-            if (!chained && !cur.grad) bp.ddecay[((int64_t)cur.slot * p.HV + cur.hv) * p.K + c4 + r] = a;
+            if (!WALK && !chained && !cur.grad) bp.ddecay[((int64_t)cur.slot * p.HV + cur.hv) * p.K + c4 + r] = a;
           }
         }
       }
 #pragma unroll
       for (int t = 0; t < R::TV; ++t) {
-        const int e = threadIdx.x + 256 * t, i = e / (VD / 4), c4 = (e % (VD / 4)) * 4;
-        lds4_st<VD>(sB, i, c4, unpack4<BF>(rw.y[t]));
+        const int e = threadIdx.x + NT * t, i = e / (VD / 4), c4 = (e % (VD / 4)) * 4;
+        lds4_st<VD>(sB, i, c4, unpack4<BF>(rows.y[t]));
       }
       __syncthreads();  // G read by every thread
 #pragma unroll
       for (int t = 0; t < R::TK; ++t) {
-        const int e = threadIdx.x + 256 * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
+        const int e = threadIdx.x + NT * t, i = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
         lds4_st<KD>(sA, i, c4, xg[t]);
       }
     }
     __syncthreads();
     // the next task's rows travel while this one's products are formed
     have = advance(nxt);
-    if (have && nxt.work) local_load<BF, KD, VD, GH>(bp, nxt, rw);
+    if (have && nxt.work) local_load<BF, KD, VD, GH, NT>(bp, nxt, rows);
 
     // transposed product (rows v, columns k): each lane then holds 4
     // consecutive values of one state row and stores them as one float4
-    f32x4_t acc[NKB][NVB];
+    f32x4_t acc[NKB][NVW];
 #pragma unroll
     for (int a = 0; a < NKB; ++a)
 #pragma unroll
-      for (int b = 0; b < NVB; ++b) acc[a][b] = zero4();
+      for (int b = 0; b < NVW; ++b) acc[a][b] = zero4();
     if (!cur.work) {
     } else if constexpr (BF) {
       // bf16 inputs: the value-side rows (v or do) are exact in bf16, the gated
@@ -644,14 +785,14 @@ __global__ __launch_bounds__(256, 2) void gla_bwd_local(BwdParams bp) {
         for (int a = 0; a < NKB; ++a) {
           float x8[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x8[e] = sA[swz<KD>(tb * 32 + 8 * mg + e, (wave * NKB + a) * 16 + m16)];
+          for (int e = 0; e < 8; ++e) x8[e] = sA[swz<KD>(tb * 32 + 8 * mg + e, (rw * NKB + a) * 16 + m16)];
           split8_3(x8, xh[a], xm[a], xl[a]);
         }
 #pragma unroll
-        for (int b = 0; b < NVB; ++b) {
+        for (int b = 0; b < NVW; ++b) {
           float y8[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) y8[e] = sB[swz<VD>(tb * 32 + 8 * mg + e, b * 16 + m16)];
+          for (int e = 0; e < 8; ++e) y8[e] = sB[swz<VD>(tb * 32 + 8 * mg + e, (cb0 + b) * 16 + m16)];
           const u32x4_t yv = pack8(y8);
 #pragma unroll
           for (int a = 0; a < NKB; ++a) {
@@ -664,32 +805,34 @@ __global__ __launch_bounds__(256, 2) void gla_bwd_local(BwdParams bp) {
     } else {
 #pragma unroll 1
       for (int ib = 0; ib < 4; ++ib) {  // not unrolled: keeps the operand registers of one row block
-        float xa[NKB][4], yb[NVB][4];
+        float xa[NKB][4], yb[NVW][4];
 #pragma unroll
         for (int a = 0; a < NKB; ++a)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) xa[a][r] = sA[swz<KD>(ib * 16 + 4 * lg + r, (wave * NKB + a) * 16 + l16)];
+          for (int r = 0; r < 4; ++r) xa[a][r] = sA[swz<KD>(ib * 16 + 4 * lg + r, (rw * NKB + a) * 16 + l16)];
 #pragma unroll
-        for (int b = 0; b < NVB; ++b)
+        for (int b = 0; b < NVW; ++b)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) yb[b][r] = sB[swz<VD>(ib * 16 + 4 * lg + r, b * 16 + l16)];
+          for (int r = 0; r < 4; ++r) yb[b][r] = sB[swz<VD>(ib * 16 + 4 * lg + r, (cb0 + b) * 16 + l16)];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
           for (int a = 0; a < NKB; ++a)
 #pragma unroll
-            for (int b = 0; b < NVB; ++b) acc[a][b] = mfma_f32(yb[b][r], xa[a][r], acc[a][b]);
+            for (int b = 0; b < NVW; ++b) acc[a][b] = mfma_f32(yb[b][r], xa[a][r], acc[a][b]);
       }
     }
-    if (chained) {
+    if constexpr (WALK) {
+      walk_step<KD, NVW>(bp, cur, acc, sdec, wx);
+    } else if (chained) {
       chain_step<KD, VD>(bp, cur, acc, sdec);
     } else {
       float *dst = (cur.grad ? bp.dstate : bp.fstate) + ((int64_t)cur.slot * p.HV + cur.hv) * p.K * p.V;
 #pragma unroll
       for (int a = 0; a < NKB; ++a)
 #pragma unroll
-        for (int b = 0; b < NVB; ++b) {
-          const int krow = (wave * NKB + a) * 16 + l16, col = b * 16 + 4 * lg;
+        for (int b = 0; b < NVW; ++b) {
+          const int krow = (rw * NKB + a) * 16 + l16, col = (cb0 + b) * 16 + 4 * lg;
           if (krow < p.K && col < p.V) *reinterpret_cast<f32x4_t *>(dst + (int64_t)krow * p.V + col) = acc[a][b];
         }
     }
@@ -1647,10 +1790,13 @@ hipError_t launch_bwd_t(int which, const BwdParams &bp, long long blocks, hipStr
   const dim3 grid((unsigned)blocks), block(256);
   switch (which) {
     case 0:
-      if (bp.chain != nullptr && bp.w.seg_base != nullptr)
-        hipLaunchKernelGGL((gla_bwd_local<BF, KD, VD, GH, true>), grid, block, 0, s, bp);
+      if (bp.walk)
+        hipLaunchKernelGGL((gla_bwd_local<BF, KD, VD, GH, kLocalWalk>), grid, dim3(local_threads(kLocalWalk)), 0, s,
+                           bp);
+      else if (bp.chain != nullptr && bp.w.seg_base != nullptr)
+        hipLaunchKernelGGL((gla_bwd_local<BF, KD, VD, GH, kLocalPackedChain>), grid, block, 0, s, bp);
       else
-        hipLaunchKernelGGL((gla_bwd_local<BF, KD, VD, GH, false>), grid, block, 0, s, bp);
+        hipLaunchKernelGGL((gla_bwd_local<BF, KD, VD, GH, kLocalTasks>), grid, block, 0, s, bp);
       break;
     case 1:
       hipLaunchKernelGGL((gla_bwd_chunk<BF, KD, VD, GH>), grid, dim3(64 * chunk_waves<KD>()), 0, s, bp);
@@ -1671,7 +1817,8 @@ hipError_t launch_bwd_kv(int which, const BwdParams &bp, long long blocks, hipSt
 // Per-chunk kernels: one workgroup per (chunk slot, value head).
 hipError_t launch_bwd_kernel(int which, bool bf16, const BwdParams &bp, hipStream_t s) {
   long long blocks = (long long)bp.w.seg_slots * bp.w.HV;
-  if (which == 0) blocks = std::min<long long>(bp.persistent_blocks, 2 * blocks);  // two per compute unit
+  if (which == 0)  // two per compute unit; walk: at most one per chain
+    blocks = std::min<long long>(bp.persistent_blocks, bp.walk ? 2LL * bp.w.N * bp.w.HV : 2 * blocks);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL || bp.w.K > 128 || bp.w.V > 128) return hipErrorInvalidValue;
   const bool gh = bp.w.gate_head != 0;

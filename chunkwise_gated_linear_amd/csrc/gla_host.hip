@@ -91,7 +91,7 @@ gla_status validate(const gla_problem *p) {
   if (p->packed ? p->B != 1 : p->n_seqs != p->B) return GLA_ERR_BAD_SHAPE;
   if (p->HV < 0 || (p->HV != 0 && p->HV % p->H != 0)) return GLA_ERR_BAD_SHAPE;
   if (p->gate != GLA_GATE_PER_KEY && p->gate != GLA_GATE_PER_HEAD) return GLA_ERR_UNSUPPORTED;
-  if (p->schedule < 0 || p->schedule > 2) return GLA_ERR_UNSUPPORTED;
+  if (p->schedule < 0 || p->schedule > 3) return GLA_ERR_UNSUPPORTED;  // 3: the backward's walk
   // token-head rows and state elements must stay addressable with 64-bit
   // offsets; one chunk's byte range of any tensor (64 token rows of H heads)
   // must stay below 2^30, where the kernels put lanes with nothing to load
@@ -100,6 +100,12 @@ gla_status validate(const gla_problem *p) {
   if (rows * (p->K > p->V ? p->K : p->V) > 4.0e15) return GLA_ERR_BAD_SHAPE;
   if (HV * (p->K > p->V ? p->K : p->V) > (1LL << 22)) return GLA_ERR_BAD_SHAPE;
   return GLA_OK;
+}
+
+gla_status validate_fwd(const gla_problem *p) {
+  const gla_status st = validate(p);
+  if (st != GLA_OK) return st;
+  return p->schedule == 3 ? GLA_ERR_UNSUPPORTED : GLA_OK;
 }
 
 // How the sequence axis is cut into state segments, and the workspace layout.
@@ -381,6 +387,10 @@ BwdPlan make_bwd_plan(const gla_problem *p, bool varlen) {
 // faster, 32 chains 18-23% slower.
 bool bwd_chain_pays(long long N, long long HV) { return 4 * N * HV >= device_cu_count(); }
 
+// Whether the backward walks its chains (schedule 0): fixed-length sequences
+// with at least one chain (of 2 N HV) per compute unit.
+bool bwd_walk_pays(bool varlen, long long N, long long HV) { return !varlen && 2 * N * HV >= device_cu_count(); }
+
 gla_status validate_bwd(const gla_problem *p) {
   const gla_status st = validate(p);
   if (st != GLA_OK) return st;
@@ -437,9 +447,13 @@ gla_status run_backward(const gla_problem *p, const BwdPlan &bpl, const void *q,
   // The scan can be chained into the summary kernel (one chain per sequence,
   // value head and direction): it saves the scan's pass over both state
   // tables, but a chain advances one chunk per link.
+  // The walk (one workgroup per chain at a time, carrying the state) has no
+  // links at all, but runs only as many workgroups as there are chains.
   const long long tasks = 2LL * pl.seg_slots * w.HV;
-  const bool chained = tokens && tasks + b.persistent_blocks <= INT_MAX &&
+  const bool walk = tokens && (p->schedule == 3 || (p->schedule == 0 && bwd_walk_pays(varlen, N, w.HV)));
+  const bool chained = tokens && !walk && tasks + b.persistent_blocks <= INT_MAX &&
                        (p->schedule == 2 || (p->schedule == 0 && bwd_chain_pays(N, w.HV)));
+  b.walk = walk ? 1 : 0;
   if (chained && varlen) {
     // packed: the task table orders each step's chains by sequence length
     b.chain_plan = reinterpret_cast<int32_t *>(ws + bpl.off_chain_plan);
@@ -450,7 +464,7 @@ gla_status run_backward(const gla_problem *p, const BwdPlan &bpl, const void *q,
   // the chained scan's link takes h0, dht and dh0 as [N][HV][Kb][Vs] of its
   // block and slice: with several of either they are staged through the
   // workspace (groups of Kb rows, one group per sequence and value head)
-  const bool stage = chained && (slices > 1 || nkb > 1);
+  const bool stage = (chained || walk) && (slices > 1 || nkb > 1);
   float *stage_h0 = reinterpret_cast<float *>(ws + bpl.off_bound);
   float *stage_dht = reinterpret_cast<float *>(ws + bpl.off_bound + bpl.bound_bytes);
   float *stage_dh0 = reinterpret_cast<float *>(ws + bpl.off_bound + 2 * bpl.bound_bytes);
@@ -512,14 +526,14 @@ gla_status run_backward(const gla_problem *p, const BwdPlan &bpl, const void *q,
           gla::launch_copy_rows(dh0 + boff, full_group, p->V, stage_dh0, cg, b.w.V, groups, b.w.K, b.w.V, s) !=
               hipSuccess)
         return GLA_ERR_HIP;
-      if (chained && varlen && dh0) {
+      if ((chained || walk) && varlen && dh0) {
         // sequences without chunks have no chain: their dh0 is dht (or zero)
         gla::BwdParams e = b;
         e.dh0 = dh0 + boff;
         e.dht = dht ? dht + boff : nullptr;
         if (gla::launch_empty_dh0(e, s) != hipSuccess) return GLA_ERR_HIP;
       }
-      if (!chained && gla::launch_bwd_scan(b, s) != hipSuccess) return GLA_ERR_HIP;
+      if (!chained && !walk && gla::launch_bwd_scan(b, s) != hipSuccess) return GLA_ERR_HIP;
       if (tokens && gla::launch_bwd_chunk(bf, b, s) != hipSuccess) return GLA_ERR_HIP;
     }
   }
@@ -571,7 +585,7 @@ WyPlan make_wy_plan(const gla_wy_problem *p) {
 // Host-side checks of a call (same for both entry points).
 gla_status check_call(const gla_problem *p, const void *q, const void *k, const void *v, const float *g,
                       const void *o, const int32_t *cu_seqlens, Plan &pl) {
-  gla_status st = validate(p);
+  gla_status st = validate_fwd(p);
   if (st != GLA_OK) return st;
   const bool varlen = p->packed == 1;
   if (varlen != (cu_seqlens != nullptr)) return GLA_ERR_NULL_ARG;
@@ -622,7 +636,7 @@ const char *gla_status_str(gla_status s) {
 }
 
 size_t gla_fwd_workspace_bytes(const gla_problem *p) {
-  if (validate(p) != GLA_OK) return (size_t)-1;
+  if (validate_fwd(p) != GLA_OK) return (size_t)-1;
   const Plan pl = make_plan(p, p->packed == 1);
   if (!pl.ok) return (size_t)-1;
   return pl.ws_total;

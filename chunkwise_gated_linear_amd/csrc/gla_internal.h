@@ -113,6 +113,10 @@ struct BwdParams {
   float *dv_part;            // [B,T,HV,Vmem] fp32 share of dv of this key block (several key blocks), else null
   int32_t Vmem;              // value columns per row of v, do, dv, h0, dht, dh0
   int32_t persistent_blocks; // workgroups of the persistent kernels (a few per compute unit)
+  int32_t walk;              // 1: the walk schedule (read by the launcher only): each workgroup of
+                             // gla_bwd_local walks whole chains of S_c / E_c, carrying the state
+                             // (h0, dht, dh0 laid out as for the chained schedule; no counter
+                             // or flags), and gla_bwd_scan is not launched
 };
 hipError_t launch_bwd_local(bool bf16, const BwdParams &bp, hipStream_t s);
 hipError_t launch_bwd_scan(const BwdParams &bp, hipStream_t s);

@@ -110,7 +110,9 @@ typedef struct gla_problem {
                       /* states (bf16 with K <= 128, else three passes).  A tuning    */
                       /* choice: results agree to rounding.  gla_bwd: 0 automatic;    */
                       /* 1 a separate scan over the chunk summaries; 2 the scan       */
-                      /* chained into the summary kernel.  Results are the same.      */
+                      /* chained into the summary kernel; 3 the summary kernel walks  */
+                      /* whole chains (gla_bwd only: gla_fwd rejects 3).  Results are */
+                      /* the same.                                                    */
 } gla_problem;
 
 /*

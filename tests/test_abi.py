@@ -89,7 +89,8 @@ def call_noalloc(lib, p, q=FAKE, k=FAKE, v=FAKE, g=FAKE, cu=None, o=FAKE):
     (dict(HV=4), BAD_SHAPE),            # value heads must be a multiple of the key heads
     (dict(HV=-3), BAD_SHAPE),
     (dict(gate=2), UNSUPPORTED),
-    (dict(schedule=3), UNSUPPORTED),
+    (dict(schedule=3), UNSUPPORTED),    # the backward's walk
+    (dict(schedule=4), UNSUPPORTED),
     (dict(schedule=-1), UNSUPPORTED),
 ])
 def test_invalid_problems_are_rejected(lib, kw, code):
@@ -214,13 +215,20 @@ def call_bwd(lib, p, ws=FAKE, ws_bytes=1 << 40, cu=None, dq=FAKE, do=FAKE):
     (dict(n_seqs=3), BAD_SHAPE),
     (dict(HV=4), BAD_SHAPE),
     (dict(gate=2), UNSUPPORTED),
-    (dict(schedule=3), UNSUPPORTED),
+    (dict(schedule=4), UNSUPPORTED),    # 3, the walk, is the backward's own
     (dict(schedule=-1), UNSUPPORTED),
 ])
 def test_backward_rejects_invalid_problems(lib, kw, code):
     p = prob(**kw)
     assert call_bwd(lib, p) == code
     assert lib.gla_bwd_workspace_bytes(ctypes.byref(p)) == ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("schedule", [0, 1, 2, 3])
+def test_backward_schedules_share_one_workspace(lib, schedule):
+    # every schedule runs in the workspace the size query gives for schedule 0
+    p0, p = prob(B=2, T=1000, H=3), prob(B=2, T=1000, H=3, schedule=schedule)
+    assert lib.gla_bwd_workspace_bytes(ctypes.byref(p)) == lib.gla_bwd_workspace_bytes(ctypes.byref(p0))
 
 
 def test_backward_null_arguments(lib):

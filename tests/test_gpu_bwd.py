@@ -90,8 +90,8 @@ def check_bwd(d, dtype, seed, scale=None, use_dht=True, need_dh0=True, label="",
 
 
 # schedule 1: summaries, a separate scan launch, chunk kernel; 2: the scan
-# chained into the summary kernel (fixed-length sequences)
-SCHEDULES = [1, 2]
+# chained into the summary kernel; 3: the summary kernel walks whole chains
+SCHEDULES = [1, 2, 3]
 
 
 @pytest.mark.parametrize("schedule", SCHEDULES)
@@ -270,21 +270,22 @@ def test_workload_sampled_heads(name):
     say("   max|err|/rms: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
+@pytest.mark.parametrize("schedule", [2, 3])
 @pytest.mark.parametrize("dtype,gate,K,V", [("bf16", "key", 128, 128), ("fp32", "key", 128, 128),
                                              ("bf16", "head", 128, 128), ("bf16", "key", 128, 256),
                                              ("bf16", "head", 256, 128)])
-def test_chained_scan_matches_separate_scan(dtype, gate, K, V):
-    """The chained scan applies the separate scan's recurrences in the same
-    order and precision to the same summaries: every output agrees bit for bit.
-    Many chains of many chunks (B=4, H=16, T=1000: 64 chains of 16 chunks per
-    direction) cross workgroups on different dies; the oracle checks two heads.
-    With V = 256 or K = 256 each value slice's or key block's h0, dht and dh0
-    rows and columns are staged."""
+def test_chained_scan_matches_separate_scan(dtype, gate, K, V, schedule):
+    """The chained scan (schedule 2) and the walk (3) apply the separate scan's
+    recurrences in the same order and precision to the same summaries: every
+    output agrees bit for bit.  Many chains of many chunks (B=4, H=16, T=1000:
+    64 chains of 16 chunks per direction; chained, they cross workgroups on
+    different dies); the oracle checks two heads.  With V = 256 or K = 256 each
+    value slice's or key block's h0, dht and dh0 rows and columns are staged."""
     d = gi.draw(920, 4, 1000, 16, K, V, dtype=dtype, h0=True, gate=gate)
     do, dht = grads_in(d, dtype, 21)
-    say(f"bwd chained vs separate scan: B=4 T=1000 H=16 K={K} V={V} {dtype} gate={gate}")
+    say(f"bwd schedule {schedule} vs separate scan: B=4 T=1000 H=16 K={K} V={V} {dtype} gate={gate}")
     a = run_bwd_gpu(d, do, dht, dtype, schedule=1)
-    b = run_bwd_gpu(d, do, dht, dtype, schedule=2)
+    b = run_bwd_gpu(d, do, dht, dtype, schedule=schedule)
     for name, x, y in zip(("dq", "dk", "dv", "dg", "dh0"), a, b):
         assert np.array_equal(x, y), f"{name}: max|diff| {np.max(np.abs(x - y)):.3e}"
     heads = [3, 14]
@@ -297,20 +298,45 @@ def test_chained_scan_matches_separate_scan(dtype, gate, K, V):
                     out_dtype="fp32" if name in ("dg", "dh0") else dtype)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_walk_more_chains_than_workgroups(dtype):
+    """The walk with 1024 chains (B=64, H=8, three chunks each) on at most two
+    workgroups per compute unit: each workgroup walks several chains in turn,
+    carrying each from its own first chunk.  Bit for bit against the separate
+    scan; the oracle checks two heads."""
+    d = gi.draw(960, 64, 130, 8, 64, 64, dtype=dtype, h0=True)
+    do, dht = grads_in(d, dtype, 34)
+    say(f"bwd walk, 1024 chains: B=64 T=130 H=8 K=V=64 {dtype}")
+    a = run_bwd_gpu(d, do, dht, dtype, schedule=1)
+    b = run_bwd_gpu(d, do, dht, dtype, schedule=3)
+    for name, x, y in zip(("dq", "dk", "dv", "dg", "dh0"), a, b):
+        assert np.array_equal(x, y), f"{name}: max|diff| {np.max(np.abs(x - y)):.3e}"
+    heads = [0, 5]
+    ds = head_slice(d, heads)
+    ref = oracle.gla_reference_bwd(ds["q"], ds["k"], ds["v"], ds["g"], np.ascontiguousarray(do[:, :, heads]),
+                                   h0=ds["h0"], dht=np.ascontiguousarray(dht[:, heads]))
+    for name, x, r in zip(("dq", "dk", "dv", "dg", "dh0"), b, ref):
+        x = x[:, heads] if name == "dh0" else x[:, :, heads]
+        check_close(name, x, r, TOL_HT if name in ("dg", "dh0") else TOL[dtype],
+                    out_dtype="fp32" if name in ("dg", "dh0") else dtype)
+
+
+@pytest.mark.parametrize("schedule", [2, 3])
 @pytest.mark.parametrize("dtype,K,V", [("bf16", 64, 64), ("fp32", 64, 64), ("bf16", 160, 192)])
-def test_chained_scan_packed_matches_separate_scan(dtype, K, V):
+def test_chained_scan_packed_matches_separate_scan(dtype, K, V, schedule):
     """Packed sequences: the chain plan orders each step's chains by sequence
-    length; sequences without chunks keep dh0 = dht.  Every output agrees bit
-    for bit with the separate scan; the oracle checks two heads."""
+    length (chained), each workgroup walks the chains of its sequences (walk);
+    sequences without chunks keep dh0 = dht.  Every output agrees bit for bit
+    with the separate scan; the oracle checks two heads."""
     rng = np.random.default_rng(945)
     lengths = [int(x) for x in rng.integers(0, 700, size=40)]
     lengths[3] = lengths[17] = 0
     lengths[5], lengths[8], lengths[9], lengths[30] = 1, 64, 65, 1500
     d = gi.draw(946, 1, 0, 8, K, V, dtype=dtype, h0=True, lengths=lengths)
     do, dht = grads_in(d, dtype, 32)
-    say(f"bwd packed chained vs separate scan: 40 sequences H=8 K={K} V={V} {dtype}")
+    say(f"bwd packed schedule {schedule} vs separate scan: 40 sequences H=8 K={K} V={V} {dtype}")
     a = run_bwd_gpu(d, do, dht, dtype, schedule=1)
-    b = run_bwd_gpu(d, do, dht, dtype, schedule=2)
+    b = run_bwd_gpu(d, do, dht, dtype, schedule=schedule)
     for name, x, y in zip(("dq", "dk", "dv", "dg", "dh0"), a, b):
         assert np.array_equal(x, y), f"{name}: max|diff| {np.max(np.abs(x - y)):.3e}"
     heads = [2, 7]
@@ -323,19 +349,21 @@ def test_chained_scan_packed_matches_separate_scan(dtype, K, V):
                     out_dtype="fp32" if name in ("dg", "dh0") else dtype)
 
 
-def test_chained_scan_many_packed_sequences():
+@pytest.mark.parametrize("schedule", [2, 3])
+def test_chained_scan_many_packed_sequences(schedule):
     """1500 short packed sequences (empty, one token, up to three chunks):
     the chain plan's loops over sequences and steps run several rounds of its
-    1024 threads; bit for bit against the separate scan, the oracle on one head."""
+    1024 threads (chained), each workgroup walks several chains (walk: 6000
+    chains); bit for bit against the separate scan, the oracle on one head."""
     rng = np.random.default_rng(950)
     lengths = [int(x) for x in rng.integers(0, 190, size=1500)]
     lengths[0] = lengths[700] = lengths[1499] = 0
     lengths[1] = 1
     d = gi.draw(951, 1, 0, 2, 64, 64, dtype="bf16", h0=True, lengths=lengths)
     do, dht = grads_in(d, "bf16", 33)
-    say("bwd packed chained vs separate scan: 1500 sequences H=2 K=V=64 bf16")
+    say(f"bwd packed schedule {schedule} vs separate scan: 1500 sequences H=2 K=V=64 bf16")
     a = run_bwd_gpu(d, do, dht, "bf16", schedule=1)
-    b = run_bwd_gpu(d, do, dht, "bf16", schedule=2)
+    b = run_bwd_gpu(d, do, dht, "bf16", schedule=schedule)
     for name, x, y in zip(("dq", "dk", "dv", "dg", "dh0"), a, b):
         assert np.array_equal(x, y), f"{name}: max|diff| {np.max(np.abs(x - y)):.3e}"
     ds = head_slice(d, [1])
