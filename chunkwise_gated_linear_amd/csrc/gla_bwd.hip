@@ -403,19 +403,23 @@ __device__ __forceinline__ bool packed_chained_task(const BwdParams &bp, int t, 
   return true;
 }
 
-// Step `step` of chain j of the walk schedule.  Chains 0 .. N HV - 1 are the
-// state chains of (sequence, value head) = (j / HV, j % HV), chains N HV ..
-// 2 N HV - 1 the gradient chains in the same order; a state chain takes its
-// sequence's chunks in order, a gradient chain in reverse.  False past the
-// chain's last chunk.
+// Step `step` of chain j of the walk schedule; a state chain takes its
+// sequence's chunks in order, a gradient chain in reverse.  Fixed-length
+// sequences: chains 0 .. N HV - 1 are the state chains of (sequence, value
+// head) = (j / HV, j % HV), chains N HV .. 2 N HV - 1 the gradient chains in
+// the same order.  Packed sequences: chain j is the state (j / HV even) or
+// gradient chain of value head j % HV of the sequence in place j / 2HV of the
+// chain plan's step 0, which lists the sequences with chunks longest first
+// (workgroups start in about the order of their numbers, so the longest
+// chains start first).  False past the chain's last chunk.
 __device__ __forceinline__ bool walk_task(const BwdParams &bp, int j, int step, LocalTask &lt) {
   const WalkParams &p = bp.w;
-  const int pairs = p.N * p.HV;
-  lt.grad = j >= pairs;
-  const int rem = lt.grad ? j - pairs : j;
-  const int n = rem / p.HV;
-  lt.hv = rem - n * p.HV;
   if (p.seg_base == nullptr) {
+    const int pairs = p.N * p.HV;
+    lt.grad = j >= pairs;
+    const int rem = lt.grad ? j - pairs : j;
+    const int n = rem / p.HV;
+    lt.hv = rem - n * p.HV;
     if (step >= p.P) return false;
     const int c = lt.grad ? p.P - 1 - step : step;
     lt.nc = p.P;
@@ -423,6 +427,11 @@ __device__ __forceinline__ bool walk_task(const BwdParams &bp, int j, int step, 
     lt.work = lt.grad ? (c > 0 || bp.dh0 != nullptr) : c < p.P - 1;
     return chunk_at(p, lt.slot, lt.ca);
   }
+  const int u = j / (2 * p.HV);
+  const int rem = j - u * 2 * p.HV;
+  lt.grad = rem >= p.HV;
+  lt.hv = lt.grad ? rem - p.HV : rem;
+  const int n = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int2 *>(bp.chain_plan + kChainPlanTable)[u].y);
   ChunkAt &ca = lt.ca;
   SegInfo &si = ca.si;
   int bos, len;
@@ -674,9 +683,11 @@ __global__ __launch_bounds__(local_threads(MODE), MODE == kLocalWalk ? 1 : 2) vo
   const bool chained = !WALK && bp.chain != nullptr;
   // packed sequences: the chain plan holds the task count and table; walk:
   // the tasks are the chains
-  const unsigned ntask = PC     ? (unsigned)__builtin_amdgcn_readfirstlane(bp.chain_plan[kChainPlanTasks])
-                         : WALK ? 2u * p.N * p.HV
-                                : 2u * p.seg_slots * p.HV;
+  unsigned ntask = 2u * p.seg_slots * p.HV;
+  if (PC) ntask = (unsigned)__builtin_amdgcn_readfirstlane(bp.chain_plan[kChainPlanTasks]);
+  if (WALK)
+    ntask = p.seg_base ? 2u * p.HV * (unsigned)__builtin_amdgcn_readfirstlane(bp.chain_plan[kChainPlanSeqs])
+                       : 2u * p.N * p.HV;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
   // the wave's first row block / NKB and first column block
   const int rw = NT == 256 ? wave : wave & 3, cb0 = NT == 256 ? 0 : (wave >> 2) * NVW;
@@ -869,7 +880,8 @@ __device__ __forceinline__ void block_scan_1024(const int32_t *in, int32_t *out,
 // more than s chunks: order lists the sequences by nc descending, so that the
 // first cnt[s] of them are those with a chunk s, and table[u] for u = pbase[s]
 // + rank (pbase the exclusive sums of cnt) is (s, order[rank]).  plan[0]
-// receives the task count 2 HV (total chunks).
+// receives the task count 2 HV (total chunks) and plan[1] the number of
+// sequences with a chunk.
 __global__ __launch_bounds__(1024) void gla_bwd_chain_plan(const int32_t *cu, int N, int T, int HV, int cmax,
                                                            int slots, int32_t *plan, int32_t *hist, int32_t *cnt,
                                                            int32_t *pbase, int32_t *order) {
@@ -909,7 +921,10 @@ __global__ __launch_bounds__(1024) void gla_bwd_chain_plan(const int32_t *cu, in
     }
     table[u] = int2{lo, order[u - pbase[lo]]};
   }
-  if (tid == 0) plan[kChainPlanTasks] = 2 * HV * total;
+  if (tid == 0) {
+    plan[kChainPlanTasks] = 2 * HV * total;
+    plan[kChainPlanSeqs] = min(cnt[0], total);  // table[0, cnt[0]): step 0, the sequences by length
+  }
 }
 
 // dh0 of the packed sequences without chunks (the chained scan has no task
@@ -1817,8 +1832,8 @@ hipError_t launch_bwd_kv(int which, const BwdParams &bp, long long blocks, hipSt
 // Per-chunk kernels: one workgroup per (chunk slot, value head).
 hipError_t launch_bwd_kernel(int which, bool bf16, const BwdParams &bp, hipStream_t s) {
   long long blocks = (long long)bp.w.seg_slots * bp.w.HV;
-  if (which == 0)  // two per compute unit; walk: at most one per chain
-    blocks = std::min<long long>(bp.persistent_blocks, bp.walk ? 2LL * bp.w.N * bp.w.HV : 2 * blocks);
+  if (which == 0)  // two per compute unit; walk: one per chain
+    blocks = bp.walk ? 2LL * bp.w.N * bp.w.HV : std::min<long long>(bp.persistent_blocks, 2 * blocks);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL || bp.w.K > 128 || bp.w.V > 128) return hipErrorInvalidValue;
   const bool gh = bp.w.gate_head != 0;

@@ -378,18 +378,17 @@ BwdPlan make_bwd_plan(const gla_problem *p, bool varlen) {
   return b;
 }
 
-// Whether the backward of N fixed-length sequences with HV value heads chains
-// its scan into the summary kernel (schedule 0).  Each link of a chain costs
-// a few memory round trips (a few microseconds); with at least one chain per
-// four compute units the links of the many chains overlap the summaries, and
-// with fewer the chains set the pace.  Measured on MI355X, K = V = 128 bf16:
-// 128 chains per direction of 32 chunks 916 against 1073 us, 64 chains 4-6%
-// faster, 32 chains 18-23% slower.
-bool bwd_chain_pays(long long N, long long HV) { return 4 * N * HV >= device_cu_count(); }
-
-// Whether the backward walks its chains (schedule 0): fixed-length sequences
-// with at least one chain (of 2 N HV) per compute unit.
-bool bwd_walk_pays(bool varlen, long long N, long long HV) { return !varlen && 2 * N * HV >= device_cu_count(); }
+// Whether the backward walks its chains (schedule 0), for N sequences with HV
+// value heads; else it runs the separate scan.  The walk takes one workgroup
+// per chain (2 N HV of them) and moves no state but the stores; with fewer
+// chains than half the compute units the chains, one chunk at a time, set the
+// pace.  Measured on MI355X, K = V = 128 bf16, us for the separate scan /
+// chained scan / walk (N HV pairs, chunks per sequence):
+//   128 pairs, 32 chunks  1011 / 861 / 709      512 pairs, 8 chunks  972 / 824 / 724
+//    64 pairs, 64 chunks   991 / 966 / 920       64 pairs, 32 chunks 511 / 514 / 478
+//    32 pairs, 32 chunks   246 / 339 / 348       16 pairs, 128 chunks 520 / 935 / 1130
+// The chained scan is never faster than both others; it stays as schedule 2.
+bool bwd_walk_pays(long long N, long long HV) { return 4 * N * HV >= device_cu_count(); }
 
 gla_status validate_bwd(const gla_problem *p) {
   const gla_status st = validate(p);
@@ -444,17 +443,16 @@ gla_status run_backward(const gla_problem *p, const BwdPlan &bpl, const void *q,
   float *dg_parts = dg_nparts > 1 ? reinterpret_cast<float *>(ws + bpl.off_dg_part) : nullptr;
   float *dv_parts = nkb > 1 ? reinterpret_cast<float *>(ws + bpl.off_dv_part) : nullptr;
   const long long dg_share = rows * w.HV * (gh ? 1 : p->K), dv_share = rows * w.HV * p->V;
-  // The scan can be chained into the summary kernel (one chain per sequence,
-  // value head and direction): it saves the scan's pass over both state
-  // tables, but a chain advances one chunk per link.
-  // The walk (one workgroup per chain at a time, carrying the state) has no
-  // links at all, but runs only as many workgroups as there are chains.
+  // The scan can run inside the summary kernel (one chain per sequence, value
+  // head and direction): chained, the chains' tasks spread over all
+  // workgroups and meet through links in memory; walked, each workgroup
+  // carries one chain's state from chunk to chunk.  Both save the scan's pass
+  // over both state tables.
   const long long tasks = 2LL * pl.seg_slots * w.HV;
-  const bool walk = tokens && (p->schedule == 3 || (p->schedule == 0 && bwd_walk_pays(varlen, N, w.HV)));
-  const bool chained = tokens && !walk && tasks + b.persistent_blocks <= INT_MAX &&
-                       (p->schedule == 2 || (p->schedule == 0 && bwd_chain_pays(N, w.HV)));
+  const bool walk = tokens && (p->schedule == 3 || (p->schedule == 0 && bwd_walk_pays(N, w.HV)));
+  const bool chained = tokens && !walk && p->schedule == 2 && tasks + b.persistent_blocks <= INT_MAX;
   b.walk = walk ? 1 : 0;
-  if (chained && varlen) {
+  if ((chained || walk) && varlen) {
     // packed: the task table orders each step's chains by sequence length
     b.chain_plan = reinterpret_cast<int32_t *>(ws + bpl.off_chain_plan);
     if (gla::launch_chain_plan(b, bpl.cmax, reinterpret_cast<int32_t *>(ws + bpl.off_plan_scratch), s) !=

@@ -86,7 +86,9 @@ hipError_t launch_clear(int32_t *words, long long n, hipStream_t s);
 // (block, slice) is launched on its own: w.K / w.V the block's keys and the
 // slice's columns, the tensors offset to their first key and column, w.Kmem
 // and Vmem the full widths (the row strides).
-constexpr int kChainPlanTasks = 0, kChainPlanTable = 2;  // words of the chain plan
+// words of the chain plan: the chained schedule's task count, the number of
+// sequences with chunks, the table
+constexpr int kChainPlanTasks = 0, kChainPlanSeqs = 1, kChainPlanTable = 2;
 constexpr int chain_plan_words(int slots) { return kChainPlanTable + 2 * slots; }
 // scratch words of launch_chain_plan for sequences of at most cmax chunks
 constexpr long long chain_plan_scratch_words(int cmax, int N) { return 3LL * cmax + 4 + N; }
@@ -106,8 +108,9 @@ struct BwdParams {
                          // of S_c and E_c ([0] task counter, then flags [2][slots][HV]; zeroed
                          // before the launch) and gla_bwd_scan is not launched.  Its h0, dht and
                          // dh0 are [N][HV][K][V] (a value slice's columns staged compactly)
-  int32_t *chain_plan;   // packed sequences with the chain: [kChainPlanTasks] task count, from word
-                         // kChainPlanTable the (step, sequence) int2 table (launch_chain_plan)
+  int32_t *chain_plan;   // packed sequences, chained or walk: [kChainPlanTasks] task count,
+                         // [kChainPlanSeqs] sequences with chunks, from word kChainPlanTable
+                         // the (step, sequence) int2 table (launch_chain_plan)
   int32_t *flags;        // [slots][HV]: 1 when the chunk is left to the token-by-token kernel
   float *dq_part, *dk_part;  // [B,T,HV,Kmem] fp32 shares of dq, dk of this value slice (G > 1 or several slices), else null
   float *dv_part;            // [B,T,HV,Vmem] fp32 share of dv of this key block (several key blocks), else null
