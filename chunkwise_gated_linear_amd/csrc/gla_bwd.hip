@@ -1588,23 +1588,13 @@ __global__ __launch_bounds__(64 * chunk_waves<KD>(), 1) void gla_bwd_chunk(BwdPa
 //   staged rows, S_{i-1} = sum_{j<i} w_j k_j v_j^T + w_{-1} S_c with w the
 //   products of the decays in between (O(64^2) per chunk: this kernel only
 //   runs for chunks whose decay is beyond the fast kernel's range).
+// The token-by-token gradients of one flagged chunk ca of value head hv (the
+// body of gla_bwd_chunk_exact; the LDS arrays are the kernel's).
 template <bool BF, int KD, int VD, bool GH>
-__global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
+__device__ __forceinline__ void chunk_exact_task(const BwdParams &bp, int hv, const ChunkAt &ca, float *sV, float *sK,
+                                                 float *sA, float *sDq, float *sRed, float *sRow, float *sKeyDg) {
   const WalkParams &p = bp.w;
   constexpr int PARTS = 256 / KD, NC = VD / PARTS;
-  __shared__ __attribute__((aligned(16))) float sV[64 * VD];  // v rows
-  __shared__ float sK[64 * KD];    // k rows
-  __shared__ float sA[64 * KD];    // e^{g} per token and key
-  __shared__ float sDq[64 * KD];   // dq
-  __shared__ float sRed[4 * VD];   // per-wave partial dv of one token
-  __shared__ float sRow[64];       // per-head gate: dg of each token
-  __shared__ float sKeyDg[KD];     // per-head gate: each key's share of one token's dg
-
-  const int hv = (int)(blockIdx.x % (unsigned)p.HV);
-  const int slot = (int)(blockIdx.x / (unsigned)p.HV);
-  ChunkAt ca;
-  if (!chunk_at(p, slot, ca)) return;
-  if (bp.flags[(int64_t)slot * p.HV + hv] == 0) return;
   const int h = hv / p.G;
   const int L = ca.L;
   const int64_t row0 = ca.row0;
@@ -1732,6 +1722,47 @@ __global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
   if (GH && threadIdx.x < L) bp.dg[(row0 + threadIdx.x) * p.HV + hv] = sRow[threadIdx.x];
 }
 
+// The kernel: a few workgroups per compute unit, each over a fixed share of
+// the (slot, value head) tasks; a launch with no flagged chunk reads the
+// flags and ends.
+template <bool BF, int KD, int VD, bool GH>
+__global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
+  const WalkParams &p = bp.w;
+  __shared__ __attribute__((aligned(16))) float sV[64 * VD];  // v rows
+  __shared__ float sK[64 * KD];    // k rows
+  __shared__ float sA[64 * KD];    // e^{g} per token and key
+  __shared__ float sDq[64 * KD];   // dq
+  __shared__ float sRed[4 * VD];   // per-wave partial dv of one token
+  __shared__ float sRow[64];       // per-head gate: dg of each token
+  __shared__ float sKeyDg[KD];     // per-head gate: each key's share of one token's dg
+
+  __shared__ int sTodo[256];  // flagged tasks of one round
+  __shared__ int sCount;
+  // Tasks blockIdx.x + gridDim.x i (task = slot HV + hv, the flags' order):
+  // one round reads 256 of their flags at once and runs the flagged ones.
+  const unsigned ntask = (unsigned)p.seg_slots * (unsigned)p.HV;
+  const unsigned mine = (ntask - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  for (unsigned base = 0; base < mine; base += 256) {
+    if (threadIdx.x == 0) sCount = 0;
+    __syncthreads();
+    if (base + threadIdx.x < mine) {
+      const unsigned t = blockIdx.x + gridDim.x * (base + threadIdx.x);
+      if (bp.flags[t] != 0) sTodo[atomicAdd(&sCount, 1)] = (int)t;
+    }
+    __syncthreads();
+    const int todo = sCount;
+    for (int u = 0; u < todo; ++u) {
+      const unsigned task = (unsigned)sTodo[u];
+      const int hv = (int)(task % (unsigned)p.HV);
+      const int slot = (int)(task / (unsigned)p.HV);
+      ChunkAt ca;
+      if (chunk_at(p, slot, ca)) chunk_exact_task<BF, KD, VD, GH>(bp, hv, ca, sV, sK, sA, sDq, sRed, sRow, sKeyDg);
+      __syncthreads();  // LDS is reused by the next task
+    }
+    __syncthreads();  // sTodo and sCount are reused by the next round
+  }
+}
+
 // ---------------------------------------------------------------- gla_bwd_group_sum
 // dq, dk of key head h = the sum of the fp32 shares of its G value heads over
 // every value slice (slices `slice_stride` floats apart), rounded once to the
@@ -1834,6 +1865,7 @@ hipError_t launch_bwd_kernel(int which, bool bf16, const BwdParams &bp, hipStrea
   long long blocks = (long long)bp.w.seg_slots * bp.w.HV;
   if (which == 0)  // two per compute unit; walk: one per chain
     blocks = bp.walk ? 2LL * bp.w.N * bp.w.HV : std::min<long long>(bp.persistent_blocks, 2 * blocks);
+  if (which == 2) blocks = std::min<long long>(bp.persistent_blocks, blocks);  // over the flags
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL || bp.w.K > 128 || bp.w.V > 128) return hipErrorInvalidValue;
   const bool gh = bp.w.gate_head != 0;
