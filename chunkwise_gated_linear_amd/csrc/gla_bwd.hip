@@ -31,10 +31,12 @@
 // Kernels (launched by the host in this order):
 //   gla_bwd_local       per (chunk, value head): the chunk's summaries
 //                       sum_j k_j e^{G_last - G_j} v_j^T and scale (q e^G)^T do, and a;
-//                       it can also chain them into S_c, E_c and dh0 itself (then
-//                       gla_bwd_scan is not launched; packed sequences first get a
-//                       task table from gla_bwd_chain_plan, and those without
-//                       chunks their dh0 from gla_bwd_empty_dh0)
+//                       it can also turn them into S_c, E_c and dh0 itself, walking
+//                       each chain in one workgroup or chaining its steps across
+//                       workgroups (then gla_bwd_scan is not launched; packed
+//                       sequences first get a table of their chains from
+//                       gla_bwd_chain_plan, and those without chunks their dh0
+//                       from gla_bwd_empty_dh0)
 //   gla_bwd_scan        per state element: S_c forward, E_c in reverse, dh0
 //   gla_bwd_chunk       per (chunk, value head): dq, dk, dv, dg (bf16 MFMA on split
 //                       operands for the bf16 products named below, fp32 MFMA otherwise)
@@ -293,17 +295,25 @@ __device__ __forceinline__ u32x4_t pack8(const float (&x)[8]) {
 //   a_c     = e^{G_last}                             (K)
 // Every factor is a decay (at most 1), so any gate is exact here.
 //
-// Two schedules.  Without bp.chain, task t < 2 slots HV forms Sigma (first
-// half) or D (second half) of slot t / HV and head t % HV, stores it in
-// fstate / dstate (and a_c in ddecay), and gla_bwd_scan then walks the
-// tables.  With bp.chain the walks run inside this kernel: every (sequence,
-// value head) with P chunks has a state chain over chunks 0, 1, .., P-1 and a
-// gradient chain over P-1, .., 0, and each task applies
-// one step of the scan's recurrences to the state its predecessor published:
+// Three schedules.  Without bp.chain or bp.walk, task t < 2 slots HV forms
+// Sigma (first half) or D (second half) of slot t / HV and head t % HV, stores
+// it in fstate / dstate (and a_c in ddecay), and gla_bwd_scan then walks the
+// tables.  Otherwise the walks run inside this kernel: every (sequence, value
+// head) with P chunks has a state chain over chunks 0, 1, .., P-1 and a
+// gradient chain over P-1, .., 0, and each step of a chain applies the scan's
+// recurrences:
 //   state:    slot c holds S_c;  S_{c+1} = a_c S_c + Sigma_c goes to slot c + 1
 //   gradient: slot c holds E_c;  E_{c-1} = D_c + a_c E_c goes to slot c - 1,
 //             after chunk 0 to dh0
-// (S_0 = h0 and E_{P-1} = dht, or zero).  Tasks are taken from a counter in
+// (S_0 = h0 and E_{P-1} = dht, or zero).
+//
+// Walk (bp.walk, eight waves): one workgroup per chain takes the chain's
+// chunks in order and carries the state in registers (walk_step), so no step
+// waits for another workgroup; it pays off when the chains fill the compute
+// units.
+//
+// Chained (bp.chain): each task applies one step to the state its predecessor
+// published, in whichever workgroup that ran.  Tasks are taken from a counter in
 // step order (step s: chunk s of every state chain, chunk P-1-s of every
 // gradient chain), so a task's predecessor always has a lower number and has
 // been taken by a running workgroup: the chains always move.  A published
@@ -318,8 +328,9 @@ __device__ __forceinline__ u32x4_t pack8(const float (&x)[8]) {
 // summary of the last chunk and, without dh0, the gradient summary of chunk
 // 0 feed nothing and are not formed.
 //
-// Persistent workgroups (two per compute unit); the rows of a workgroup's
-// next task are loaded into registers while it forms the current one.
+// Persistent workgroups (two per compute unit; walk: one per chain); the rows
+// of a workgroup's next task are loaded into registers while it forms the
+// current one.
 template <bool BF, int KD, int VD, bool GH, int NT>
 struct LocalRows {
   static constexpr int TK = 64 * KD / 4 / NT, TV = 64 * VD / 4 / NT;  // row quads per thread
