@@ -103,6 +103,21 @@ __device__ __forceinline__ void st_el(void *base, int64_t i, float x) {
   if constexpr (BF) reinterpret_cast<__bf16 *>(base)[i] = (__bf16)x;
   else reinterpret_cast<float *>(base)[i] = x;
 }
+// Four consecutive elements from i (a multiple of 4), rounded as st_el rounds
+// each, in one store.
+template <bool BF>
+__device__ __forceinline__ void st_el4(void *base, int64_t i, f32x4_t x) {
+  if constexpr (BF) {
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      w[h] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x[2 * h]) |
+             (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x[2 * h + 1]) << 16;
+    *reinterpret_cast<u32x2_t *>(reinterpret_cast<uint16_t *>(base) + i) = u32x2_t{w[0], w[1]};
+  } else {
+    *reinterpret_cast<f32x4_t *>(reinterpret_cast<float *>(base) + i) = x;
+  }
+}
 // One element through a buffer descriptor (byte offset; past the range:
 // dropped / zero), as bf16 (rounded to nearest even) or fp32.
 template <bool BF>
@@ -1797,11 +1812,8 @@ __global__ __launch_bounds__(256) void gla_bwd_group_sum(BwdParams bp, int64_t q
       dk += *reinterpret_cast<const f32x4_t *>(bp.dk_part + off);
     }
   const int64_t off = rowh * p.K + k;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    st_el<BF>(bp.dq, off + r, dq[r]);
-    st_el<BF>(bp.dk, off + r, dk[r]);
-  }
+  st_el4<BF>(bp.dq, off, dq);
+  st_el4<BF>(bp.dk, off, dk);
 }
 
 // Columns [0, cols) of `groups` x `rows` fp32 rows: row r of group gi from
@@ -1840,6 +1852,14 @@ __global__ __launch_bounds__(256) void gla_bwd_slice_sum(float *out, const float
   float x = 0.f;
   for (int sl = 0; sl < slices; ++sl) x += parts[sl * n + e];
   out[e] = x;
+}
+// The same for n a multiple of 4, a float4 per thread (n4 = n / 4).
+__global__ __launch_bounds__(256) void gla_bwd_slice_sum4(float *out, const float *parts, int64_t n4, int slices) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n4) return;
+  f32x4_t x = zero4();
+  for (int sl = 0; sl < slices; ++sl) x += reinterpret_cast<const f32x4_t *>(parts + sl * 4 * n4)[e];
+  reinterpret_cast<f32x4_t *>(out)[e] = x;
 }
 
 template <bool BF, int KD, int VD, bool GH>
@@ -1952,11 +1972,16 @@ hipError_t launch_bwd_finish(bool bf16, const BwdParams &bp, int slices, const f
   }
   if (dg_nparts > 1) {
     const long long n = rows * bp.w.HV * (bp.w.gate_head ? 1 : bp.w.K);
-    const long long blocks = (n + 255) / 256;
+    const bool quads = n % 4 == 0;  // dg and the shares are 16-byte aligned
+    const long long blocks = ((quads ? n / 4 : n) + 255) / 256;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     if (blocks > 0) {
-      hipLaunchKernelGGL(gla_bwd_slice_sum, dim3((unsigned)blocks), dim3(256), 0, s, dg, dg_parts, (int64_t)n,
-                         dg_nparts);
+      if (quads)
+        hipLaunchKernelGGL(gla_bwd_slice_sum4, dim3((unsigned)blocks), dim3(256), 0, s, dg, dg_parts, (int64_t)(n / 4),
+                           dg_nparts);
+      else
+        hipLaunchKernelGGL(gla_bwd_slice_sum, dim3((unsigned)blocks), dim3(256), 0, s, dg, dg_parts, (int64_t)n,
+                           dg_nparts);
       return hipGetLastError();
     }
   }
