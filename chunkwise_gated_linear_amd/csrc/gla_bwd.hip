@@ -1836,12 +1836,12 @@ __global__ __launch_bounds__(256) void gla_bwd_copy_rows(float *dst, RowsLayout 
 
 // dv with several key blocks: the blocks' fp32 shares summed and rounded once.
 template <bool BF>
-__global__ __launch_bounds__(256) void gla_bwd_dv_sum(void *dv, const float *parts, int64_t n, int blocks) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= n) return;
-  float x = 0.f;
-  for (int b = 0; b < blocks; ++b) x += parts[b * n + e];
-  st_el<BF>(dv, e, x);
+__global__ __launch_bounds__(256) void gla_bwd_dv_sum(void *dv, const float *parts, int64_t n4, int blocks) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // a float4 of dv (n = 4 n4 elements)
+  if (e >= n4) return;
+  f32x4_t x = zero4();
+  for (int b = 0; b < blocks; ++b) x += reinterpret_cast<const f32x4_t *>(parts + b * 4 * n4)[e];
+  st_el4<BF>(dv, 4 * e, x);
 }
 
 // dg with several value slices (or, with a per-head gate, key blocks): out[e]
@@ -1943,11 +1943,12 @@ hipError_t launch_empty_dh0(const BwdParams &bp, hipStream_t s) {
 }
 
 hipError_t launch_dv_sum(bool bf16, void *dv, const float *parts, long long n, int blocks, hipStream_t s) {
-  const long long grid = (n + 255) / 256;
+  if (n % 4 != 0) return hipErrorInvalidValue;  // rows of V columns, V a multiple of 16
+  const long long n4 = n / 4, grid = (n4 + 255) / 256;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (bf16) hipLaunchKernelGGL(gla_bwd_dv_sum<true>, dim3((unsigned)grid), dim3(256), 0, s, dv, parts, (int64_t)n, blocks);
-  else hipLaunchKernelGGL(gla_bwd_dv_sum<false>, dim3((unsigned)grid), dim3(256), 0, s, dv, parts, (int64_t)n, blocks);
+  if (bf16) hipLaunchKernelGGL(gla_bwd_dv_sum<true>, dim3((unsigned)grid), dim3(256), 0, s, dv, parts, (int64_t)n4, blocks);
+  else hipLaunchKernelGGL(gla_bwd_dv_sum<false>, dim3((unsigned)grid), dim3(256), 0, s, dv, parts, (int64_t)n4, blocks);
   return hipGetLastError();
 }
 
