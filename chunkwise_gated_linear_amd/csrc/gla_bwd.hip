@@ -1748,9 +1748,9 @@ __device__ __forceinline__ void chunk_exact_task(const BwdParams &bp, int hv, co
   if (GH && threadIdx.x < L) bp.dg[(row0 + threadIdx.x) * p.HV + hv] = sRow[threadIdx.x];
 }
 
-// The kernel: a few workgroups per compute unit, each over a fixed share of
-// the (slot, value head) tasks; a launch with no flagged chunk reads the
-// flags and ends.
+// The kernel: one workgroup per compute unit, each over a fixed share of the
+// (slot, value head) tasks; a launch with no flagged chunk reads the flags and
+// ends.
 template <bool BF, int KD, int VD, bool GH>
 __global__ __launch_bounds__(256, 1) void gla_bwd_chunk_exact(BwdParams bp) {
   const WalkParams &p = bp.w;
@@ -1896,7 +1896,8 @@ hipError_t launch_bwd_kernel(int which, bool bf16, const BwdParams &bp, hipStrea
   long long blocks = (long long)bp.w.seg_slots * bp.w.HV;
   if (which == 0)  // two per compute unit; walk: one per chain
     blocks = bp.walk ? 2LL * bp.w.N * bp.w.HV : std::min<long long>(bp.persistent_blocks, 2 * blocks);
-  if (which == 2) blocks = std::min<long long>(bp.persistent_blocks, blocks);  // over the flags
+  // over the flags: one per compute unit (its LDS leaves room for no second)
+  if (which == 2) blocks = std::min<long long>(std::max(bp.persistent_blocks / 2, 1), blocks);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL || bp.w.K > 128 || bp.w.V > 128) return hipErrorInvalidValue;
   const bool gh = bp.w.gate_head != 0;
