@@ -203,9 +203,11 @@ __global__ __launch_bounds__(256) void gla_wy_fwd_kernel_bf16(WyParams wp) {
     const void *src = which == 0 ? p.v : p.k;
     const int64_t srow = which == 0 ? (int64_t)p.HV * p.V : (int64_t)p.H * p.K;  // source row stride
     const int64_t soff = which == 0 ? (int64_t)hv * p.V : (int64_t)h * p.K;      // source head offset
+    // thread: tokens 2 m + t % 2 + 32 (t / 2) (m = threadIdx.x / 16), columns
+    // c4 .. c4 + 3, so that its two tokens of a pair are staged as one word
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int e = threadIdx.x + 256 * t, j = e >> 4, c4 = (e & 15) * 4;
+      const int j = 2 * (threadIdx.x >> 4) + (t & 1) + 32 * (t >> 1), c4 = (threadIdx.x & 15) * 4;
       xr[t] = u32x2_t{0u, 0u};
       if (j < L && c0 + c4 < W)
         xr[t] = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(src) +
@@ -219,17 +221,27 @@ __global__ __launch_bounds__(256) void gla_wy_fwd_kernel_bf16(WyParams wp) {
     block(b, which, c0, W);
     __syncthreads();  // sS / sA ready (first block); sX free (later blocks)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int e = threadIdx.x + 256 * t, j = e >> 4, c4 = (e & 15) * 4;
-      const float sc = sS[which][j];
-      const float x[4] = {bf_lo(xr[t][0]) * sc, bf_hi(xr[t][0]) * sc, bf_lo(xr[t][1]) * sc,
-                          bf_hi(xr[t][1]) * sc};
+    for (int q = 0; q < 2; ++q) {  // the token pair j, j + 1 (j even: one 4-byte word of X^T)
+      const int j = 2 * (threadIdx.x >> 4) + 32 * q, c4 = (threadIdx.x & 15) * 4;
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32x2_t xw = xr[2 * q + u];
+        const float sc = sS[which][j + u];
+        const float x[4] = {bf_lo(xw[0]) * sc, bf_hi(xw[0]) * sc, bf_lo(xw[1]) * sc, bf_hi(xw[1]) * sc};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const __bf16 hi = (__bf16)x[r];
+          const __bf16 lo = (__bf16)(x[r] - (float)hi);
+          const uint32_t h16 = __builtin_bit_cast(uint16_t, hi), l16w = __builtin_bit_cast(uint16_t, lo);
+          hw[r] = u == 0 ? h16 : hw[r] | h16 << 16;
+          lw[r] = u == 0 ? l16w : lw[r] | l16w << 16;
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const __bf16 hi = (__bf16)x[r];
-        const __bf16 lo = (__bf16)(x[r] - (float)hi);
-        sXh[bswz(c4 + r, j)] = __builtin_bit_cast(uint16_t, hi);
-        sXl[bswz(c4 + r, j)] = __builtin_bit_cast(uint16_t, lo);
+        *reinterpret_cast<uint32_t *>(sXh + bswz(c4 + r, j)) = hw[r];
+        *reinterpret_cast<uint32_t *>(sXl + bswz(c4 + r, j)) = lw[r];
       }
     }
     if (b + 1 < nb) load_rows(b + 1, xr);
